@@ -1,0 +1,351 @@
+// oracle.cpp — TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.
+//
+// A plain, slow, fp64 CPU reference ("the oracle") for the forward pass of
+// sparse long-sequence self-attention. Only the tests, the smoke check and the
+// benchmark's CPU-baseline leg load it. It shares no code, header, helper or
+// constant with the HIP library in sparse_long_sequence_amd/, and it never
+// reads anything that library produced.
+//
+// Sparse attention is exact masked softmax attention, so the oracle is that
+// definition written out (LongNet page, §3.4 "Standard Self-Attention and
+// Sparse Attention (Preliminaries)", Eq. 2: entries outside the mask S are set
+// to -inf before the softmax):
+//
+//   s_ij   = (q_i . k_j) / sqrt(D) + bias_ij
+//   M_i    = max over allowed j of s_ij
+//   Z_i    = sum_j c_ij exp(s_ij - M_i)
+//   O_i    = sum_j c_ij exp(s_ij - M_i) v_j / Z_i,   lse_i = M_i + ln Z_i
+//
+// where c_ij is the explicit mask (0/1) or, for the LongNet mixture, an integer
+// key multiplicity. The mask is evaluated by its predicate for every key j of
+// every requested row; the n x n matrix is materialised one row at a time (a
+// full n x n byte matrix for n = 32768 would be 1 GiB per head).
+//
+// Readings of points the pages leave open (each is listed in the design doc):
+//   * scale 1/sqrt(D) everywhere, LongNet included;
+//   * masked pairs are excluded (-inf), not given ETC's -10000;
+//   * the window is inclusive, |j-i| <= d*R, and keys outside [0,N) are dropped;
+//   * causal means j <= i for every pair, band, global row and global column;
+//   * a global key inside the band counts once (set union);
+//   * the scalar relative bias applies only to pairs of the same kind (both
+//     global or both non-global), indexed by clamp(j-i, -k, k);
+//   * with separate global projections, a global row i uses qg_i, kg_j, vg_j
+//     for every key j; non-global rows use q, k, v, also for global columns;
+//   * LongNet head h keeps, in each segment, the positions whose offset from
+//     the segment start is congruent to h mod r; the last segment is truncated
+//     to N; attention inside a segment is causal in position when causal != 0;
+//     a row that no pattern covers gets O = 0 and lse = -inf.
+//
+// Threads: rows are split over std::threads; each row is summed sequentially
+// in fp64, so the result does not depend on the thread count.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <limits>
+#include <thread>
+#include <vector>
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Pattern predicates
+// ---------------------------------------------------------------------------
+
+// Membership of position p in the strictly increasing global index set G.
+bool in_global(const int32_t* gidx, int32_t n_global, int32_t p) {
+  return std::binary_search(gidx, gidx + n_global, p);
+}
+
+// Dilated sliding window, one side of the union that forms the mask.
+// Longformer page, §3.4 "Sliding Window Attention" (w/2 keys per side plus the
+// token itself, Fig. 2b) and "Dilated Sliding Window Attention" (keys at
+// i + d*m for |m| <= w/2, Fig. 2c); causal: "Autoregressive Language Modeling
+// Configuration" (only keys to the left). Here R = w/2.
+bool band_allows(int32_t i, int32_t j, int32_t radius, int32_t dil, int32_t causal) {
+  const int64_t delta = (int64_t)j - (int64_t)i;
+  if (causal && delta > 0) return false;
+  if (delta % dil != 0) return false;
+  const int64_t steps = delta / dil;
+  return steps >= -(int64_t)radius && steps <= (int64_t)radius;
+}
+
+// The full mask entry c_ij in {0,1}. Global tokens attend to every key and
+// every query attends to them (Longformer page, §3.4 "Global Attention",
+// Fig. 2d; ETC page, §3.4 "Global-Local Attention": g2g, g2l and l2g pieces are
+// full, l2l is banded with radius r). Causal restricts all of them to j <= i.
+uint8_t mask_entry(int32_t i, int32_t j, bool i_glob, bool j_glob, int32_t radius,
+                   int32_t dil, int32_t causal) {
+  if (causal && j > i) return 0;
+  if (i_glob || j_glob) return 1;
+  return band_allows(i, j, radius, dil, causal) ? 1 : 0;
+}
+
+// LongNet sparsification membership: position p is kept by pattern (w, r) for
+// head h iff (p - segment_start) mod r == h mod r. LongNet page, §3.4
+// "Dilated Attention: Core Mechanism" (Eqs. 3-5) and "Multi-Head Dilated
+// Attention: Offset Mechanism" (Eqs. 13-15, offset s_j = j mod r).
+bool longnet_kept(int32_t p, int32_t w, int32_t r, int32_t head) {
+  const int32_t seg_start = (p / w) * w;
+  return ((p - seg_start) % r) == (head % r);
+}
+
+// Integer multiplicity of key j for query i under the mixture of patterns:
+// the number of patterns whose sparsified segment holds both i and j. By the
+// page's equivalence statement ("Mixture of Dilated Attentions": mixing with
+// alpha_i = s_i / sum_j s_j equals one softmax over the gathered keys of all
+// patterns), this multiplicity weights one joint softmax.
+int32_t longnet_mult(int32_t i, int32_t j, int32_t head, const int32_t* w, const int32_t* r,
+                     int32_t n_pairs, int32_t causal) {
+  if (causal && j > i) return 0;
+  int32_t m = 0;
+  for (int32_t k = 0; k < n_pairs; ++k) {
+    if (i / w[k] != j / w[k]) continue;  // same segment
+    if (longnet_kept(i, w[k], r[k], head) && longnet_kept(j, w[k], r[k], head)) ++m;
+  }
+  return m;
+}
+
+// ---------------------------------------------------------------------------
+// Masked dense softmax attention of one query row (the definition above).
+// weight[j] is c_ij (0 excludes the key). bias(j) adds to the scaled logit.
+// ---------------------------------------------------------------------------
+template <class Bias>
+void attend_row(int32_t N, int32_t D, const double* qi, const double* kbase, const double* vbase,
+                const std::vector<double>& weight, Bias bias, double* out, double* lse) {
+  const double scale = 1.0 / std::sqrt((double)D);
+  std::vector<double> logit(N, 0.0);
+  double M = -std::numeric_limits<double>::infinity();
+  for (int32_t j = 0; j < N; ++j) {
+    if (weight[j] == 0.0) continue;  // excluded keys carry weight exactly 0
+    const double* kj = kbase + (size_t)j * D;
+    double dot = 0.0;
+    for (int32_t c = 0; c < D; ++c) dot += qi[c] * kj[c];
+    logit[j] = dot * scale + bias(j);
+    M = std::max(M, logit[j]);
+  }
+  for (int32_t c = 0; c < D; ++c) out[c] = 0.0;
+  if (M == -std::numeric_limits<double>::infinity()) {  // no allowed key
+    *lse = M;
+    return;
+  }
+  double Z = 0.0;
+  for (int32_t j = 0; j < N; ++j) {
+    if (weight[j] == 0.0) continue;
+    const double p = weight[j] * std::exp(logit[j] - M);
+    Z += p;
+    const double* vj = vbase + (size_t)j * D;
+    for (int32_t c = 0; c < D; ++c) out[c] += p * vj[c];
+  }
+  for (int32_t c = 0; c < D; ++c) out[c] /= Z;
+  *lse = M + std::log(Z);
+}
+
+// Run fn(row_index) for row_index in [0, n) over n_threads threads.
+template <class Fn>
+void parallel_rows(int64_t n, int32_t n_threads, Fn fn) {
+  int32_t T = n_threads > 0 ? n_threads : (int32_t)std::thread::hardware_concurrency();
+  if (T < 1) T = 1;
+  if ((int64_t)T > n) T = (int32_t)std::max<int64_t>(n, 1);
+  std::vector<std::thread> pool;
+  for (int32_t t = 0; t < T; ++t) {
+    pool.emplace_back([=, &fn]() {
+      for (int64_t x = t; x < n; x += T) fn(x);
+    });
+  }
+  for (auto& th : pool) th.join();
+}
+
+// Decode the (b, h, i) of the x-th requested row: `sel` holds triples, or is
+// null for all rows in [B, H, N] order.
+inline void decode_row(const int32_t* sel, int64_t x, int32_t H, int32_t N, int32_t& b, int32_t& h,
+                       int32_t& i) {
+  if (sel) {
+    b = sel[3 * x];
+    h = sel[3 * x + 1];
+    i = sel[3 * x + 2];
+  } else {
+    i = (int32_t)(x % N);
+    h = (int32_t)((x / N) % H);
+    b = (int32_t)(x / ((int64_t)N * H));
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lo_version(void) { return 1; }
+
+// Explicit 0/1 mask rows of the band + global pattern for one head.
+// mask is [n_rows][N]; rows == null means every row 0..N-1 (the n x n matrix).
+int32_t lo_mask_rows(int32_t N, const int32_t* gidx, int32_t n_global, int32_t radius,
+                     int32_t dilation, int32_t causal, const int32_t* rows, int32_t n_rows,
+                     uint8_t* mask) {
+  if (N <= 0 || radius < 0 || dilation < 1 || n_global < 0 || (n_global > 0 && !gidx)) return -1;
+  const int32_t nr = rows ? n_rows : N;
+  for (int32_t x = 0; x < nr; ++x) {
+    const int32_t i = rows ? rows[x] : x;
+    const bool ig = in_global(gidx, n_global, i);
+    for (int32_t j = 0; j < N; ++j)
+      mask[(size_t)x * N + j] = mask_entry(i, j, ig, in_global(gidx, n_global, j), radius, dilation, causal);
+  }
+  return 0;
+}
+
+// LongNet key multiplicity rows for one head; mult is [n_rows][N].
+int32_t lo_longnet_mult_rows(int32_t N, int32_t head, const int32_t* w, const int32_t* r,
+                             int32_t n_pairs, int32_t causal, const int32_t* rows, int32_t n_rows,
+                             int32_t* mult) {
+  if (N <= 0 || n_pairs < 1) return -1;
+  for (int32_t k = 0; k < n_pairs; ++k)
+    if (w[k] < 1 || r[k] < 1) return -1;
+  const int32_t nr = rows ? n_rows : N;
+  for (int32_t x = 0; x < nr; ++x) {
+    const int32_t i = rows ? rows[x] : x;
+    for (int32_t j = 0; j < N; ++j)
+      mult[(size_t)x * N + j] = longnet_mult(i, j, head, w, r, n_pairs, causal);
+  }
+  return 0;
+}
+
+// Band + global attention (Longformer / ETC), fp64.
+// q, k, v: [B,H,N,D]; qg, kg, vg: all null (shared projections) or all
+// [B,H,N,D] (Longformer page, §3.4 "Separate Linear Projections for Local vs.
+// Global Attention"). dilation: [H] (null = all 1). rel_bias: [H][2*rel_k+1]
+// or null (ETC page, §3.4 "Relative Position Encoding", clipping at k; here
+// the scalar form of the per-label term). sel: n_sel (b,h,i) triples or null
+// for all B*H*N rows. out: [n_sel][D]; lse: [n_sel].
+int32_t lo_attn_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q, const double* k,
+                     const double* v, const double* qg, const double* kg, const double* vg,
+                     const int32_t* gidx, int32_t n_global, int32_t radius, const int32_t* dilation,
+                     int32_t causal, const double* rel_bias, int32_t rel_k, const int32_t* sel,
+                     int64_t n_sel, double* out, double* lse, int32_t n_threads) {
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || radius < 0 || n_global < 0) return -1;
+  if (!q || !k || !v || !out || !lse) return -1;
+  if ((qg || kg || vg) && !(qg && kg && vg)) return -1;
+  if (n_global > 0 && !gidx) return -1;
+  if (rel_bias && rel_k < 0) return -1;
+  if (dilation)
+    for (int32_t h = 0; h < H; ++h)
+      if (dilation[h] < 1) return -1;
+  const int64_t rows = sel ? n_sel : (int64_t)B * H * N;
+  std::vector<uint8_t> is_glob(N, 0);
+  for (int32_t g = 0; g < n_global; ++g)
+    if (gidx[g] >= 0 && gidx[g] < N) is_glob[gidx[g]] = 1;
+  parallel_rows(rows, n_threads, [&](int64_t x) {
+    int32_t b, h, i;
+    decode_row(sel, x, H, N, b, h, i);
+    const int32_t dil = dilation ? dilation[h] : 1;
+    const bool ig = is_glob[i] != 0;
+    const size_t head_off = ((size_t)b * H + h) * (size_t)N * D;
+    // Global rows with separate projections use qg_i, kg_j, vg_j.
+    const bool sep = ig && qg;
+    const double* qi = (sep ? qg : q) + head_off + (size_t)i * D;
+    const double* kb = (sep ? kg : k) + head_off;
+    const double* vb = (sep ? vg : v) + head_off;
+    std::vector<double> weight(N);
+    for (int32_t j = 0; j < N; ++j)  // the explicit mask row c_i,:
+      weight[j] = mask_entry(i, j, ig, is_glob[j] != 0, radius, dil, causal);
+    const double* tab = rel_bias ? rel_bias + (size_t)h * (2 * rel_k + 1) : nullptr;
+    auto bias = [&](int32_t j) -> double {
+      if (!tab) return 0.0;
+      if ((is_glob[j] != 0) != ig) return 0.0;  // mixed global/non-global pair
+      int64_t dlt = (int64_t)j - i;
+      dlt = std::max<int64_t>(-rel_k, std::min<int64_t>(rel_k, dlt));
+      return tab[dlt + rel_k];
+    };
+    attend_row(N, D, qi, kb, vb, weight, bias, out + (size_t)x * D, lse + x);
+  });
+  return 0;
+}
+
+// LongNet mixture of dilated attentions, path 1: one softmax per row over the
+// integer key multiplicity (the page's equivalence statement).
+int32_t lo_longnet_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q, const double* k,
+                        const double* v, const int32_t* w, const int32_t* r, int32_t n_pairs,
+                        int32_t causal, const int32_t* sel, int64_t n_sel, double* out, double* lse,
+                        int32_t n_threads) {
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || n_pairs < 1 || !q || !k || !v || !out || !lse) return -1;
+  for (int32_t p = 0; p < n_pairs; ++p)
+    if (w[p] < 1 || r[p] < 1) return -1;
+  const int64_t rows = sel ? n_sel : (int64_t)B * H * N;
+  parallel_rows(rows, n_threads, [&](int64_t x) {
+    int32_t b, h, i;
+    decode_row(sel, x, H, N, b, h, i);
+    const size_t head_off = ((size_t)b * H + h) * (size_t)N * D;
+    std::vector<double> weight(N);
+    for (int32_t j = 0; j < N; ++j) weight[j] = longnet_mult(i, j, h, w, r, n_pairs, causal);
+    attend_row(N, D, q + head_off + (size_t)i * D, k + head_off, v + head_off, weight,
+               [](int32_t) { return 0.0; }, out + (size_t)x * D, lse + x);
+  });
+  return 0;
+}
+
+// LongNet mixture of dilated attentions, path 2, in the page's order:
+// for each pattern (w_k, r_k): sparsify the row's segment (Eqs. 3-5 with the
+// head offset of Eqs. 13-15), dense softmax attention on the sparsified
+// segment (Eq. 6), scatter back with zeros for rows the pattern skips
+// (Eqs. 7-8); then mix O = sum_k alpha_k O_k with alpha_k = s_k / sum_j s_j,
+// s_k the softmax denominator sum exp(s) of pattern k (Eqs. 9-10; "Mixture of
+// Dilated Attentions"). s_k is carried as lse_k = ln s_k.
+// Optional per-pattern outputs: out_k [n_pairs][n_sel][D], lse_k [n_pairs][n_sel]
+// (lse_k = -inf where pattern k skips the row).
+int32_t lo_longnet_mixture_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q,
+                                const double* k, const double* v, const int32_t* w, const int32_t* r,
+                                int32_t n_pairs, int32_t causal, const int32_t* sel, int64_t n_sel,
+                                double* out, double* lse, double* out_k, double* lse_k,
+                                int32_t n_threads) {
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || n_pairs < 1 || !q || !k || !v || !out || !lse) return -1;
+  for (int32_t p = 0; p < n_pairs; ++p)
+    if (w[p] < 1 || r[p] < 1) return -1;
+  const int64_t rows = sel ? n_sel : (int64_t)B * H * N;
+  const double NEG_INF = -std::numeric_limits<double>::infinity();
+  parallel_rows(rows, n_threads, [&](int64_t x) {
+    int32_t b, h, i;
+    decode_row(sel, x, H, N, b, h, i);
+    const size_t head_off = ((size_t)b * H + h) * (size_t)N * D;
+    const double* qi = q + head_off + (size_t)i * D;
+    std::vector<double> Ok((size_t)n_pairs * D, 0.0), Lk(n_pairs, NEG_INF);
+    for (int32_t p = 0; p < n_pairs; ++p) {
+      const int32_t seg_start = (i / w[p]) * w[p];
+      const int32_t seg_end = std::min<int64_t>((int64_t)seg_start + w[p], N);
+      const int32_t off = h % r[p];
+      if ((i - seg_start) % r[p] != off) continue;  // scattered zero row
+      // Gather the sparsified keys of this segment: seg_start + off + m*r.
+      std::vector<double> weight(N, 0.0);
+      for (int64_t j = (int64_t)seg_start + off; j < seg_end; j += r[p])
+        if (!causal || j <= i) weight[j] = 1.0;
+      attend_row(N, D, qi, k + head_off, v + head_off, weight, [](int32_t) { return 0.0; },
+                 &Ok[(size_t)p * D], &Lk[p]);
+    }
+    // alpha_k = s_k / sum_j s_j with s_k = exp(lse_k); evaluated stably.
+    double Lmax = NEG_INF;
+    for (int32_t p = 0; p < n_pairs; ++p) Lmax = std::max(Lmax, Lk[p]);
+    double* o = out + (size_t)x * D;
+    for (int32_t c = 0; c < D; ++c) o[c] = 0.0;
+    if (Lmax == NEG_INF) {
+      lse[x] = NEG_INF;
+    } else {
+      double S = 0.0;
+      for (int32_t p = 0; p < n_pairs; ++p)
+        if (Lk[p] != NEG_INF) S += std::exp(Lk[p] - Lmax);
+      for (int32_t p = 0; p < n_pairs; ++p) {
+        if (Lk[p] == NEG_INF) continue;
+        const double alpha = std::exp(Lk[p] - Lmax) / S;
+        for (int32_t c = 0; c < D; ++c) o[c] += alpha * Ok[(size_t)p * D + c];
+      }
+      lse[x] = Lmax + std::log(S);
+    }
+    if (out_k && lse_k) {
+      for (int32_t p = 0; p < n_pairs; ++p) {
+        for (int32_t c = 0; c < D; ++c) out_k[((size_t)p * rows + x) * D + c] = Ok[(size_t)p * D + c];
+        lse_k[(size_t)p * rows + x] = Lk[p];
+      }
+    }
+  });
+  return 0;
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+"""Seeded synthetic workloads for sparse long-sequence attention.
+
+This module holds only workload descriptions (shapes, pattern parameters) and
+seeded random inputs. It contains none of the attention arithmetic, so both the
+HIP path and the CPU oracle may draw their inputs from it.
+
+The five named workloads stand in for the pages' data (document QA at 4,096
+tokens, ETC long inputs with one global summary token per sentence, character
+language modelling at 16,384 tokens, LongNet's 32K sequences); no dataset is
+read. Recipe: ``torch.Generator('cpu').manual_seed(seed)``; draw order q, k, v,
+then qg, kg, vg (when the workload has separate global projections), then the
+relative-bias table as 0.1 * N(0,1); values iid N(0,1) in fp32, then rounded to
+bf16 (round-to-nearest-even) for bf16 workloads.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Dict, List, Optional, Tuple
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One attention call: shapes, dtype and pattern parameters."""
+
+    name: str
+    B: int
+    H: int
+    N: int
+    D: int = 64
+    dtype: str = "bf16"                     # "bf16" or "f32"
+    kind: str = "band"                      # "band" (la_attn_forward) or "dilated" (la_dilated_forward)
+    radius: int = 0
+    global_idx: Tuple[int, ...] = ()
+    dilation: Optional[Tuple[int, ...]] = None  # per head; None = all 1
+    causal: bool = False
+    rel_k: int = 0                          # >0: scalar relative bias table [H][2k+1]
+    separate_global: bool = False
+    pairs: Tuple[Tuple[int, int], ...] = ()  # LongNet (segment length w, dilation r)
+    seed: int = 0
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workloads of the hot path. Seeds are 1000 + index.
+TINY = Workload("tiny-local-global", B=1, H=1, N=512, dtype="f32", radius=32,
+                global_idx=(0, 1), seed=1001)
+LONGFORMER_BASE = Workload("longformer-base-n4096-r256-g64", B=2, H=12, N=4096, radius=256,
+                           global_idx=tuple(range(64)), separate_global=True, seed=1002)
+ETC_SHAPE = Workload("etc-ng256-nl4096-r84-relk12", B=1, H=12, N=256 + 4096, radius=84,
+                     global_idx=tuple(range(256)), rel_k=12, seed=1003)
+CHARLM_DILATED = Workload("charlm-causal-n16384-w512-dil", B=1, H=8, N=16384, radius=512,
+                          dilation=(1, 1, 1, 1, 1, 1, 2, 2), causal=True, seed=1004)
+LONGNET_SHARE = Workload("longnet-n32768-5pairs", B=1, H=12, N=32768, kind="dilated", causal=True,
+                         pairs=((2048, 1), (4096, 2), (8192, 4), (16384, 6), (32768, 12)),
+                         seed=1005)
+
+WORKLOADS: Dict[str, Workload] = {w.name: w for w in
+                                  (TINY, LONGFORMER_BASE, ETC_SHAPE, CHARLM_DILATED, LONGNET_SHARE)}
+ORDERED: List[Workload] = [TINY, LONGFORMER_BASE, ETC_SHAPE, CHARLM_DILATED, LONGNET_SHARE]
+
+
+@dataclass
+class Inputs:
+    """CPU tensors for one call (dtype as the workload; rel_bias fp32)."""
+
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    qg: Optional[torch.Tensor] = None
+    kg: Optional[torch.Tensor] = None
+    vg: Optional[torch.Tensor] = None
+    rel_bias: Optional[torch.Tensor] = None
+    extra: dict = field(default_factory=dict)
+
+
+def make_inputs(w: Workload, seed: Optional[int] = None) -> Inputs:
+    """Draw the workload's inputs on the CPU from ``seed`` (default ``w.seed``)."""
+    g = torch.Generator("cpu").manual_seed(w.seed if seed is None else seed)
+    shape = (w.B, w.H, w.N, w.D)
+
+    def draw(sz):
+        return torch.randn(sz, generator=g, dtype=torch.float32)
+
+    q, k, v = draw(shape), draw(shape), draw(shape)
+    qg = kg = vg = None
+    if w.separate_global:
+        qg, kg, vg = draw(shape), draw(shape), draw(shape)
+    rb = None
+    if w.rel_k > 0:
+        rb = 0.1 * draw((w.H, 2 * w.rel_k + 1))
+    dt = w.torch_dtype
+    cast = (lambda t: None if t is None else t.to(dt).contiguous())
+    return Inputs(cast(q), cast(k), cast(v), cast(qg), cast(kg), cast(vg),
+                  None if rb is None else rb.contiguous())
+
+
+def sample_rows(w: Workload, n: int, seed: int = 7, must_include=()) -> torch.Tensor:
+    """``[n, 3]`` int32 (b, h, i) rows: edges, pattern boundaries and random rows."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    rows = []
+    edge = sorted({0, 1, w.N - 1, w.N - 2, w.N // 2} | set(i for i in must_include if 0 <= i < w.N))
+    for b in range(w.B):
+        for h in range(w.H):
+            for i in edge:
+                rows.append((b, h, i))
+    extra = max(0, n - len(rows))
+    if extra:
+        bb = torch.randint(0, w.B, (extra,), generator=g)
+        hh = torch.randint(0, w.H, (extra,), generator=g)
+        ii = torch.randint(0, w.N, (extra,), generator=g)
+        rows += list(zip(bb.tolist(), hh.tolist(), ii.tolist()))
+    return torch.tensor(rows, dtype=torch.int32)

@@ -1,0 +1,534 @@
+"""Pins of the fp64 CPU oracle against what the pages and mathematics fix.
+
+Nothing here re-types the oracle's own predicate or re-calls its routines to
+check themselves. Each pin uses another route to the same fact:
+
+* constructive key enumeration from the pages' wording (keys i + d*m,
+  |m| <= w/2; global rows and columns) against the oracle's mask predicate;
+* closed-form pair counts (w+1 keys per interior row; the ETC cost formula
+  n_g(n_g+n_l) + n_l(n_g+2r+1) less the window's edge loss; LongNet's
+  per-segment triangle counts) read through exp(lse) with Q = 0;
+* the LongNet page's worked sparsification example (golden fixture);
+* special cases that reduce to library dense attention (torch SDPA in fp64);
+* plain-Python brute force on tiny inputs, including ETC's four-piece
+  formulation with its two unified softmaxes and LongNet's literal
+  sparsify -> attend -> scatter -> weighted-sum procedure;
+* algebraic identities (mixture == joint softmax; duplicate patterns; rows
+  of P sum to one).
+
+``test_planted_mistakes_are_caught`` plants plausible mistakes in a copy of the
+oracle's source, rebuilds it, and checks that every mistake fails some pin.
+"""
+from __future__ import annotations
+
+import math
+import os
+import random
+import shutil
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------
+# closed forms and brute force (independent of oracle.cpp)
+# ---------------------------------------------------------------------------
+
+def count_1d(n: int, R: int, causal: bool) -> int:
+    """Allowed pairs of a radius-R window on a length-n sequence."""
+    if n <= 0:
+        return 0
+    if causal:
+        if n <= R + 1:
+            return n * (n + 1) // 2
+        return (R + 1) * (R + 2) // 2 + (n - R - 1) * (R + 1)
+    if n <= R + 1:
+        return n * n
+    return n * (2 * R + 1) - R * (R + 1)
+
+
+def count_dilated(N: int, R: int, d: int, causal: bool) -> int:
+    """Residue class c of a dilation-d window is a length ceil((N-c)/d) band."""
+    return sum(count_1d((N - c + d - 1) // d, R, causal) for c in range(min(d, N)))
+
+
+def count_prefix_globals(N: int, R: int, g: int) -> int:
+    """Non-causal, d=1, G = {0..g-1}: global rows see N keys; a row i >= g sees
+    its window plus the globals left of the window, min(g, max(0, i-R))."""
+    tot = g * N
+    for i in range(g, N):
+        lo, hi = max(0, i - R), min(N - 1, i + R)
+        tot += (hi - lo + 1) + min(g, lo)
+    return tot
+
+
+def longnet_row_count(N: int, pairs, h: int, i: int, causal: bool) -> int:
+    tot = 0
+    for (w, r) in pairs:
+        s = h % r
+        seg = (i // w) * w
+        L = min(w, N - seg)
+        if (i - seg) % r != s:
+            continue
+        n_seg = (L - s + r - 1) // r
+        m = (i - seg - s) // r
+        tot += (m + 1) if causal else n_seg
+    return tot
+
+
+def longnet_count(N: int, pairs, h: int, causal: bool) -> int:
+    tot = 0
+    for (w, r) in pairs:
+        s = h % r
+        for seg in range(0, N, w):
+            L = min(w, N - seg)
+            n = (L - s + r - 1) // r if s < L else 0
+            tot += n * (n + 1) // 2 if causal else n * n
+    return tot
+
+
+def _dot(a, b):
+    return sum(x * y for x, y in zip(a, b))
+
+
+def bf_attend(qi, keys, K, V, bias=None):
+    """Softmax attention of one query over an explicit key list (Python floats)."""
+    D = len(qi)
+    sc = 1.0 / math.sqrt(D)
+    logits = [sc * _dot(qi, K[j]) + (bias(j) if bias else 0.0) for j in keys]
+    M = max(logits)
+    e = [math.exp(x - M) for x in logits]
+    Z = sum(e)
+    out = [sum(e[t] * V[j][c] for t, j in enumerate(keys)) / Z for c in range(D)]
+    return out, M + math.log(Z)
+
+
+def bf_band_head(q, k, v, G, R, d, causal, qg=None, kg=None, vg=None, relb=None):
+    """Longformer pattern by enumeration: keys i + d*m, m in [-R, R] (causal:
+    [-R, 0]), inside [0, N); plus the global columns; global rows see all."""
+    N = len(q)
+    Gs = set(G)
+    outs, lses = [], []
+    for i in range(N):
+        if i in Gs:
+            keys = [j for j in range(N) if (not causal or j <= i)]
+            Q, K, V = (qg, kg, vg) if qg is not None else (q, k, v)
+        else:
+            steps = range(-R, 1) if causal else range(-R, R + 1)
+            ks = {i + d * m for m in steps if 0 <= i + d * m < N}
+            ks |= {g for g in Gs if (not causal or g <= i)}
+            keys = sorted(ks)
+            Q, K, V = q, k, v
+        bias = None
+        if relb is not None:
+            kk = (len(relb) - 1) // 2
+
+            def bias(j, i=i, kk=kk):
+                if (j in Gs) != (i in Gs):
+                    return 0.0
+                return relb[max(-kk, min(kk, j - i)) + kk]
+        o, l = bf_attend(Q[i], keys, K, V, bias)
+        outs.append(o)
+        lses.append(l)
+    return np.array(outs), np.array(lses)
+
+
+def bf_etc_four_pieces(qg_, kg_, vg_, ql, kl, vl, r, relb):
+    """ETC global-local attention from its four pieces: a global query takes one
+    softmax over [g2g ; g2l], a long query one over [l2g ; l2l within radius r].
+    Relative labels (clipped distance) apply within g2g and l2l."""
+    ng, nl = len(qg_), len(ql)
+    kk = (len(relb) - 1) // 2
+    D = len(ql[0])
+    sc = 1.0 / math.sqrt(D)
+    lab = lambda dlt: relb[max(-kk, min(kk, dlt)) + kk]
+    out, lse = [], []
+    for i in range(ng):
+        e = [sc * _dot(qg_[i], kg_[j]) + lab(j - i) for j in range(ng)]
+        e += [sc * _dot(qg_[i], kl[j]) for j in range(nl)]
+        vals = list(vg_) + list(vl)
+        M = max(e)
+        p = [math.exp(x - M) for x in e]
+        Z = sum(p)
+        out.append([sum(p[t] * vals[t][c] for t in range(len(p))) / Z for c in range(D)])
+        lse.append(M + math.log(Z))
+    for i in range(nl):
+        keys = [j for j in range(max(0, i - r), min(nl, i + r + 1))]
+        e = [sc * _dot(ql[i], kg_[j]) for j in range(ng)]
+        e += [sc * _dot(ql[i], kl[j]) + lab(j - i) for j in keys]
+        vals = list(vg_) + [vl[j] for j in keys]
+        M = max(e)
+        p = [math.exp(x - M) for x in e]
+        Z = sum(p)
+        out.append([sum(p[t] * vals[t][c] for t in range(len(p))) / Z for c in range(D)])
+        lse.append(M + math.log(Z))
+    return np.array(out), np.array(lse)
+
+
+def bf_longnet_head(q, k, v, pairs, h, causal):
+    """LongNet's procedure as the page orders it: per pattern, sparsify each
+    segment with head offset h mod r, attend densely on the sparsified rows,
+    scatter back (zeros elsewhere), then mix with alpha_i = s_i / sum_j s_j."""
+    N, D = len(q), len(q[0])
+    sc = 1.0 / math.sqrt(D)
+    Os, Ss = [], []
+    for (w, r) in pairs:
+        s = h % r
+        Oh = [[0.0] * D for _ in range(N)]
+        den = [0.0] * N
+        for seg in range(0, N, w):
+            L = min(w, N - seg)
+            idx = list(range(seg + s, seg + L, r))
+            for a, i in enumerate(idx):
+                keys = idx[: a + 1] if causal else idx
+                e = [math.exp(sc * _dot(q[i], k[j])) for j in keys]
+                Z = sum(e)
+                Oh[i] = [sum(e[t] * v[j][c] for t, j in enumerate(keys)) / Z for c in range(D)]
+                den[i] = Z
+        Os.append(Oh)
+        Ss.append(den)
+    out, lse = [], []
+    for i in range(N):
+        S = sum(Ss[p][i] for p in range(len(pairs)))
+        if S == 0.0:
+            out.append([0.0] * D)
+            lse.append(-math.inf)
+            continue
+        out.append([sum(Ss[p][i] * Os[p][i][c] for p in range(len(pairs))) / S for c in range(D)])
+        lse.append(math.log(S))
+    return np.array(out), np.array(lse)
+
+
+def rand_qkv(rng: np.random.Generator, B, H, N, D):
+    return [rng.standard_normal((B, H, N, D)) for _ in range(3)]
+
+
+def sdpa(q, k, v, causal=False):
+    t = [torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v)]
+    o = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=causal)
+    D = q.shape[-1]
+    s = torch.matmul(t[0], t[1].transpose(-1, -2).contiguous()) / math.sqrt(D)
+    if causal:
+        N = q.shape[-2]
+        s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), -math.inf)
+    return o.numpy(), torch.logsumexp(s, dim=-1).numpy()
+
+
+# ---------------------------------------------------------------------------
+# pins (each takes the oracle library so the planted-mistake test can reuse it)
+# ---------------------------------------------------------------------------
+
+def pin_mask_matches_enumeration(lib):
+    rnd = random.Random(11)
+    for _ in range(60):
+        N = rnd.randint(1, 40)
+        R = rnd.randint(0, N + 2)
+        d = rnd.randint(1, 4)
+        causal = rnd.random() < 0.5
+        G = sorted(rnd.sample(range(N), rnd.randint(0, min(4, N))))
+        m = oracle.mask_rows(N, G, R, d, causal, lib=lib)
+        for i in range(N):
+            if i in G:
+                ks = {j for j in range(N) if not causal or j <= i}
+            else:
+                steps = range(-R, 1) if causal else range(-R, R + 1)
+                ks = {i + d * s for s in steps if 0 <= i + d * s < N}
+                ks |= {g for g in G if not causal or g <= i}
+            assert set(np.nonzero(m[i])[0].tolist()) == ks, (N, R, d, causal, G, i)
+
+
+def _count_via_lse(lib, N, G, R, dil, causal, H=1):
+    z = np.zeros((1, H, N, 8))
+    _, lse = oracle.attn_rows(z, z, z, G, R, dil, causal, lib=lib)
+    return np.exp(lse)
+
+
+def pin_counts_closed_form(lib):
+    # Interior rows of a radius-R window see w+1 = 2R+1 keys (R+1 causal).
+    c = _count_via_lse(lib, 200, (), 20, None, False)[0, 0]
+    assert np.allclose(c[20:180], 41, rtol=0, atol=1e-9)
+    assert abs(c.sum() - count_1d(200, 20, False)) < 1e-6
+    c = _count_via_lse(lib, 200, (), 20, None, True)[0, 0]
+    assert np.allclose(c[20:], 21, rtol=0, atol=1e-9)
+    assert abs(c.sum() - count_1d(200, 20, True)) < 1e-6
+    # Dilation: every residue class is an undilated band of its own length.
+    for d, causal in ((2, False), (3, True), (5, False)):
+        c = _count_via_lse(lib, 157, (), 7, [d], causal)
+        assert abs(c.sum() - count_dilated(157, 7, d, causal)) < 1e-6
+    # Prefix globals, non-causal.
+    c = _count_via_lse(lib, 300, tuple(range(9)), 25, None, False)
+    assert abs(c.sum() - count_prefix_globals(300, 25, 9)) < 1e-6
+
+
+def pin_counts_full_workloads(lib):
+    # Longformer-base workload: N=4096, R=256, G = first 64 positions.
+    m = oracle.mask_rows(4096, range(64), 256, 1, False, lib=lib)
+    assert int(m.sum(dtype=np.int64)) == count_prefix_globals(4096, 256, 64) == 2_522_816
+    # ETC workload as one concatenated sequence: the cost formula
+    # n_g(n_g+n_l) + n_l(n_g+2r+1) counts 2r+1 keys for every long row; the
+    # window loses r(r+1) keys at the two ends of the long input.
+    ng, nl, r = 256, 4096, 84
+    m = oracle.mask_rows(ng + nl, range(ng), r, 1, False, lib=lib)
+    assert int(m.sum(dtype=np.int64)) == ng * (ng + nl) + nl * (ng + 2 * r + 1) - r * (r + 1) \
+        == 2_847_772
+    # Char-LM workload: causal R=512, dilation 2 on a head.
+    rows = [0, 1, 600, 1023, 1024, 1025, 16383]
+    m = oracle.mask_rows(16384, (), 512, 2, True, rows=rows, lib=lib)
+    for x, i in enumerate(rows):
+        assert int(m[x].sum()) == min(i // 2, 512) + 1
+
+
+def pin_longnet_counts(lib):
+    pairs = ((16, 1), (32, 2), (64, 4), (96, 6))
+    for N in (96, 100):
+        for causal in (True, False):
+            for h in range(7):
+                mlt = oracle.longnet_mult_rows(N, h, pairs, causal, lib=lib)
+                assert int(mlt.sum()) == longnet_count(N, pairs, h, causal)
+                for i in range(N):
+                    assert int(mlt[i].sum()) == longnet_row_count(N, pairs, h, i, causal)
+    # The 32K-token workload, on sampled rows, and its total by closed form.
+    big = ((2048, 1), (4096, 2), (8192, 4), (16384, 6), (32768, 12))
+    assert sum(longnet_count(32768, big, h, True) for h in range(12)) == 839_254_020
+    rows = [0, 5, 2047, 2048, 2730, 5461, 16383, 16384, 27305, 32767]
+    for h in (0, 5, 11):
+        mlt = oracle.longnet_mult_rows(32768, h, big, True, rows=rows, lib=lib)
+        for x, i in enumerate(rows):
+            assert int(mlt[x].sum()) == longnet_row_count(32768, big, h, i, True)
+
+
+def pin_longnet_worked_example(lib):
+    with open(os.path.join(GOLDEN, "longnet_sparsify_w16_r4.txt")) as f:
+        lines = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    assert len(lines) >= 5
+    for ln in lines:
+        N, w, r, head, seg = map(int, ln[:5])
+        kept = [int(x) for x in ln[5:]]
+        mlt = oracle.longnet_mult_rows(N, head, [(w, r)], False, lib=lib)
+        for i in range(seg * w, seg * w + w):
+            keys = np.nonzero(mlt[i])[0].tolist()
+            assert keys == (kept if i in kept else []), (ln, i)
+
+
+def pin_longnet_offsets_partition(lib):
+    # Across heads 0..r-1 every position of every segment is kept exactly once.
+    for (N, w, r) in ((64, 16, 4), (100, 24, 6), (50, 50, 12)):
+        cover = np.zeros(N, dtype=np.int64)
+        for h in range(r):
+            mlt = oracle.longnet_mult_rows(N, h, [(w, r)], True, lib=lib)
+            cover += np.diag(mlt)
+        assert (cover == 1).all()
+
+
+def pin_dense_special_cases(lib):
+    rng = np.random.default_rng(5)
+    q, k, v = rand_qkv(rng, 2, 3, 37, 16)
+    o_ref, l_ref = sdpa(q, k, v)
+    oc_ref, lc_ref = sdpa(q, k, v, causal=True)
+    # A window that covers the sequence is full attention (ETC lifting; Longformer).
+    for R in (36, 100):
+        o, l = oracle.attn_rows(q, k, v, (), R, lib=lib)
+        assert np.abs(o - o_ref).max() < 1e-12 and np.abs(l - l_ref).max() < 1e-12
+        o, l = oracle.attn_rows(q, k, v, (), R, None, True, lib=lib)
+        assert np.abs(o - oc_ref).max() < 1e-12 and np.abs(l - lc_ref).max() < 1e-12
+    # Every position global is full attention too.
+    o, l = oracle.attn_rows(q, k, v, range(37), 0, lib=lib)
+    assert np.abs(o - o_ref).max() < 1e-12
+    # One LongNet pattern with w = N, r = 1 is dense (causal) attention.
+    for causal, (orf, lrf) in ((True, (oc_ref, lc_ref)), (False, (o_ref, l_ref))):
+        for fn in (oracle.longnet_rows, oracle.longnet_mixture_rows):
+            o, l = fn(q, k, v, [(37, 1)], causal, lib=lib)
+            assert np.abs(o - orf).max() < 1e-12 and np.abs(l - lrf).max() < 1e-12
+
+
+def pin_global_rows_are_full_rows(lib):
+    rng = np.random.default_rng(6)
+    q, k, v = rand_qkv(rng, 1, 2, 45, 8)
+    qg, kg, vg = rand_qkv(rng, 1, 2, 45, 8)
+    G = (0, 3, 17, 44)
+    o, l = oracle.attn_rows(q, k, v, G, 2, lib=lib)
+    o_ref, l_ref = sdpa(q, k, v)
+    assert np.abs(o[:, :, G] - o_ref[:, :, G]).max() < 1e-12
+    o, l = oracle.attn_rows(q, k, v, G, 2, qg=qg, kg=kg, vg=vg, lib=lib)
+    og_ref, lg_ref = sdpa(qg, kg, vg)
+    assert np.abs(o[:, :, G] - og_ref[:, :, G]).max() < 1e-12
+    assert np.abs(l[:, :, G] - lg_ref[:, :, G]).max() < 1e-12
+    o2, _ = oracle.attn_rows(q, k, v, G, 2, lib=lib)  # non-global rows ignore qg, kg, vg
+    ng = [i for i in range(45) if i not in G]
+    assert np.abs(o[:, :, ng] - o2[:, :, ng]).max() < 1e-15
+
+
+def pin_brute_force_band(lib):
+    rnd = random.Random(3)
+    rng = np.random.default_rng(3)
+    for t in range(14):
+        N = rnd.randint(1, 22)
+        H = 2
+        D = 4
+        R = rnd.randint(0, 6)
+        dil = [rnd.randint(1, 3) for _ in range(H)]
+        causal = t % 2 == 1
+        G = sorted(rnd.sample(range(N), rnd.randint(0, min(3, N))))
+        sep = t % 3 == 0
+        q, k, v = rand_qkv(rng, 1, H, N, D)
+        qg, kg, vg = rand_qkv(rng, 1, H, N, D) if sep else (None, None, None)
+        relb = rng.standard_normal((H, 7)) if t % 4 == 2 else None
+        o, l = oracle.attn_rows(q, k, v, G, R, dil, causal, relb, qg, kg, vg, lib=lib)
+        for h in range(H):
+            ob, lb = bf_band_head(q[0, h].tolist(), k[0, h].tolist(), v[0, h].tolist(), G, R,
+                                  dil[h], causal,
+                                  *(x[0, h].tolist() for x in (qg, kg, vg)) if sep else (None,) * 3,
+                                  relb=None if relb is None else relb[h].tolist())
+            assert np.abs(o[0, h] - ob).max() < 1e-12, (t, h)
+            assert np.abs(l[0, h] - lb).max() < 1e-12, (t, h)
+
+
+def pin_etc_four_pieces(lib):
+    rng = np.random.default_rng(8)
+    ng, nl, D, r = 5, 23, 4, 3
+    for _ in range(3):
+        xg = [rng.standard_normal((ng, D)) for _ in range(3)]
+        xl = [rng.standard_normal((nl, D)) for _ in range(3)]
+        relb = rng.standard_normal(2 * 2 + 1)
+        ob, lb = bf_etc_four_pieces(*(x.tolist() for x in xg), *(x.tolist() for x in xl), r,
+                                    relb.tolist())
+        cat = [np.concatenate([a, b])[None, None] for a, b in zip(xg, xl)]
+        o, l = oracle.attn_rows(*cat, range(ng), r, rel_bias=relb[None], lib=lib)
+        assert np.abs(o[0, 0] - ob).max() < 1e-12
+        assert np.abs(l[0, 0] - lb).max() < 1e-12
+
+
+def pin_brute_force_longnet(lib):
+    rng = np.random.default_rng(9)
+    cases = [(24, ((4, 1), (8, 2), (24, 4)), True), (21, ((6, 1), (12, 3)), True),
+             (20, ((8, 2), (20, 5)), False), (16, ((16, 4),), True)]
+    for N, pairs, causal in cases:
+        H, D = 6, 4
+        q, k, v = [x * 0.5 for x in rand_qkv(rng, 1, H, N, D)]
+        o1, l1 = oracle.longnet_rows(q, k, v, pairs, causal, lib=lib)
+        o2, l2 = oracle.longnet_mixture_rows(q, k, v, pairs, causal, lib=lib)
+        for h in range(H):
+            ob, lb = bf_longnet_head(q[0, h].tolist(), k[0, h].tolist(), v[0, h].tolist(),
+                                     pairs, h, causal)
+            fin = np.isfinite(lb)
+            for o, l in ((o1, l1), (o2, l2)):
+                assert np.abs(o[0, h] - ob).max() < 1e-12, (N, pairs, h)
+                assert np.array_equal(np.isfinite(l[0, h]), fin)
+                assert np.abs(l[0, h][fin] - lb[fin]).max() < 1e-12
+
+
+def pin_longnet_paths_agree(lib):
+    rng = np.random.default_rng(10)
+    pairs = ((32, 1), (64, 2), (128, 4), (192, 6), (200, 12))
+    q, k, v = rand_qkv(rng, 1, 12, 200, 16)
+    for causal in (True, False):
+        o1, l1 = oracle.longnet_rows(q, k, v, pairs, causal, lib=lib)
+        o2, l2 = oracle.longnet_mixture_rows(q, k, v, pairs, causal, lib=lib)
+        assert np.abs(o1 - o2).max() < 1e-12 and np.abs(l1 - l2).max() < 1e-12
+    # A pattern listed twice changes no output; lse rises by ln 2.
+    o3, l3 = oracle.longnet_rows(q, k, v, pairs[:2] + pairs[:2], True, lib=lib)
+    o4, l4 = oracle.longnet_rows(q, k, v, pairs[:2], True, lib=lib)
+    assert np.abs(o3 - o4).max() < 1e-12 and np.abs(l3 - l4 - math.log(2)).max() < 1e-12
+    o5, _ = oracle.longnet_mixture_rows(q, k, v, pairs[:2] + pairs[:2], True, lib=lib)
+    assert np.abs(o5 - o4).max() < 1e-12
+
+
+def pin_rows_sum_to_one(lib):
+    rng = np.random.default_rng(12)
+    q, k, _ = rand_qkv(rng, 1, 2, 60, 8)
+    ones = np.ones_like(q)
+    o, _ = oracle.attn_rows(q, k, ones, (1, 30), 5, [1, 3], True, lib=lib)
+    assert np.abs(o - 1).max() < 1e-13
+    o, _ = oracle.longnet_rows(q, k, ones, ((8, 1), (16, 2)), True, lib=lib)
+    assert np.abs(o - 1).max() < 1e-13
+
+
+def pin_uncovered_rows(lib):
+    # A single r=2 pattern leaves odd rows of head 0 uncovered: O = 0, lse = -inf.
+    rng = np.random.default_rng(13)
+    q, k, v = rand_qkv(rng, 1, 2, 16, 4)
+    for fn in (oracle.longnet_rows, oracle.longnet_mixture_rows):
+        o, l = fn(q, k, v, [(8, 2)], True, lib=lib)
+        assert np.isneginf(l[0, 0, 1::2]).all() and (o[0, 0, 1::2] == 0).all()
+        assert np.isfinite(l[0, 0, 0::2]).all() and np.isfinite(l[0, 1, 1::2]).all()
+
+
+def pin_sampled_rows_match_full(lib):
+    rng = np.random.default_rng(14)
+    q, k, v = rand_qkv(rng, 2, 3, 50, 8)
+    o, l = oracle.attn_rows(q, k, v, (4,), 3, [1, 2, 1], True, lib=lib)
+    sel = np.array([[1, 2, 49], [0, 0, 0], [1, 1, 4], [0, 1, 17]])
+    os_, ls_ = oracle.attn_rows(q, k, v, (4,), 3, [1, 2, 1], True, sel=sel, lib=lib)
+    for x, (b, h, i) in enumerate(sel):
+        assert np.array_equal(os_[x], o[b, h, i]) and ls_[x] == l[b, h, i]
+
+
+PINS = [pin_mask_matches_enumeration, pin_counts_closed_form, pin_counts_full_workloads,
+        pin_longnet_counts, pin_longnet_worked_example, pin_longnet_offsets_partition,
+        pin_dense_special_cases, pin_global_rows_are_full_rows, pin_brute_force_band,
+        pin_etc_four_pieces, pin_brute_force_longnet, pin_longnet_paths_agree,
+        pin_rows_sum_to_one, pin_uncovered_rows, pin_sampled_rows_match_full]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin(oracle.load())
+
+
+# Plausible mistakes, planted in a copy of oracle.cpp: (name, original, replacement).
+MUTANTS = [
+    ("causal-direction", "const int64_t delta = (int64_t)j - (int64_t)i;",
+     "const int64_t delta = (int64_t)i - (int64_t)j;"),
+    ("exclusive-window-end", "return steps >= -(int64_t)radius && steps <= (int64_t)radius;",
+     "return steps >= -(int64_t)radius && steps < (int64_t)radius;"),
+    ("dropped-scale", "logit[j] = dot * scale + bias(j);", "logit[j] = dot + bias(j);"),
+    ("bias-index-sign", "return tab[dlt + rel_k];", "return tab[rel_k - dlt];"),
+    ("bias-on-mixed-pairs", "if ((is_glob[j] != 0) != ig) return 0.0;", ""),
+    ("shared-keys-for-global-rows", "const double* kb = (sep ? kg : k) + head_off;",
+     "const double* kb = (sep ? k : k) + head_off;"),
+    ("keys-as-values", "const double* vj = vbase + (size_t)j * D;",
+     "const double* vj = kbase + (size_t)j * D;"),
+    ("lse-without-max", "*lse = M + std::log(Z);", "*lse = std::log(Z);"),
+    ("global-ignores-causal", "  if (causal && j > i) return 0;\n  if (i_glob || j_glob) return 1;",
+     "  if (i_glob || j_glob) return 1;"),
+    ("no-head-offset", "return ((p - seg_start) % r) == (head % r);",
+     "return ((p - seg_start) % r) == 0;"),
+    ("no-segment-check", "if (i / w[k] != j / w[k]) continue;  // same segment", ""),
+    ("equal-mixture-weights", "const double alpha = std::exp(Lk[p] - Lmax) / S;",
+     "const double alpha = 1.0 / n_pairs;"),
+    ("mixture-excludes-self", "if (!causal || j <= i) weight[j] = 1.0;",
+     "if (!causal || j < i) weight[j] = 1.0;"),
+    ("mixture-no-scatter", "if ((i - seg_start) % r[p] != off) continue;  // scattered zero row", ""),
+]
+
+
+def test_planted_mistakes_are_caught():
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.cpp")).read()
+    tmp = tempfile.mkdtemp(prefix="oracle_mut_")
+    try:
+        missed = []
+        for name, old, new in MUTANTS:
+            assert src.count(old) == 1, f"mutation {name!r} does not match oracle.cpp exactly once"
+            path = os.path.join(tmp, f"{name}.cpp")
+            with open(path, "w") as f:
+                f.write(src.replace(old, new))
+            so = oracle.build(path, os.path.join(tmp, f"lib{name}.so"), strict=False)
+            lib = oracle.load(so)
+            caught = False
+            for pin in PINS:
+                try:
+                    pin(lib)
+                except (AssertionError, ValueError):
+                    caught = True
+                    break
+            if not caught:
+                missed.append(name)
+        assert not missed, f"planted mistakes no pin catches: {missed}"
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
