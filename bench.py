@@ -1,0 +1,225 @@
+"""Benchmark of the sparse long-sequence attention forward pass on one MI355X.
+
+A step is one la_attn_forward call on the Longformer-base workload (B=2, H=12,
+N=4096, D=64, bf16, window radius 256, 64 global tokens with separate global
+projections): band tiles, global-column fold, online softmax, PV, epilogue and
+the global-row pass with its merge, all in one kernel launch. Inputs are seeded
+synthetic N(0,1) tensors already resident in device memory.
+
+Prints one JSON line. `value` is useful TFLOP/s (4*D FLOPs per allowed
+(query, key) pair) on that workload; `roofline` relates the kernel's average
+launch duration, timed with HIP events on the stream the kernel runs on, to the
+bf16 MFMA peak; `workloads` times the other four workloads the same way;
+`cpu_baseline` times the fp64 CPU oracle on a bounded row sample of the same
+workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X fp32 matrix
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+METRIC = "effective TFLOP/s & ms/call, window+global attn n=4096 r=256 (frac of MFMA peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Call:
+    """Device-resident inputs and preallocated outputs of one workload."""
+
+    def __init__(self, w, dev):
+        import torch
+        import sparse_long_sequence_amd as la
+        from sparse_long_sequence_amd import workloads as W
+
+        self.w = w
+        inp = W.make_inputs(w)
+        d = lambda t: None if t is None else t.to(dev).contiguous()
+        self.q, self.k, self.v = d(inp.q), d(inp.k), d(inp.v)
+        self.qg, self.kg, self.vg = d(inp.qg), d(inp.kg), d(inp.vg)
+        self.rb = d(inp.rel_bias)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:3], dtype=torch.float32, device=dev)
+        self.g = (torch.tensor(w.global_idx, dtype=torch.int32, device=dev)
+                  if w.global_idx else None)
+        dims = la.LaDims(w.B, w.H, w.N, w.D, la.LA_BF16 if w.dtype == "bf16" else la.LA_F32)
+        if w.kind == "dilated":
+            nb = la.la_dilated_workspace_size(dims, [p[0] for p in w.pairs], [p[1] for p in w.pairs])
+        else:
+            nb = la.la_attn_workspace_size(dims, len(w.global_idx), w.separate_global)
+        self.ws = torch.zeros(max(nb, 1), dtype=torch.uint8, device=dev)
+        self.la = la
+
+    def __call__(self):
+        w = self.w
+        if w.kind == "dilated":
+            self.la.la_dilated_forward(self.q, self.k, self.v, [p[0] for p in w.pairs],
+                                       [p[1] for p in w.pairs], w.causal, out=self.out,
+                                       lse=self.lse, workspace=self.ws)
+        else:
+            self.la.la_attn_forward(self.q, self.k, self.v, self.g, w.radius, w.dilation, w.causal,
+                                    self.rb, out=self.out, lse=self.lse, qg=self.qg, kg=self.kg,
+                                    vg=self.vg, workspace=self.ws)
+
+
+def time_calls(call, steps, warmup):
+    """(ms per step over the timed region, mean per-launch ms from event pairs)."""
+    import torch
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    # region timing: K back-to-back calls
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    region_ms = t0.elapsed_time(t1) / steps
+    # per-launch timing: an event pair around every call (same stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    return region_ms, sum(per) / len(per), per[len(per) // 2]
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """Time the fp64 oracle on a bounded sample of the workload's rows."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_long_sequence_amd import flops as F
+    from sparse_long_sequence_amd import workloads as W
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    inp = W.make_inputs(w)
+    f = lambda t: None if t is None else t.to(torch.float64).numpy()
+    q, k, v, qg, kg, vg, rb = (f(x) for x in (inp.q, inp.k, inp.v, inp.qg, inp.kg, inp.vg,
+                                              inp.rel_bias))
+    total_rows = w.B * w.H * w.N
+    n = min(total_rows, 2048)
+    elapsed = 0.0
+    while True:
+        sel = None if n >= total_rows else W.sample_rows(w, n, seed=3).numpy()[:n]
+        t = time.perf_counter()
+        if w.kind == "dilated":
+            oracle.longnet_rows(q, k, v, w.pairs, w.causal, sel=sel, n_threads=cores)
+        else:
+            oracle.attn_rows(q, k, v, w.global_idx, w.radius, w.dilation, w.causal, rb, qg, kg, vg,
+                             sel=sel, n_threads=cores)
+        elapsed = time.perf_counter() - t
+        if elapsed >= budget_s / 4 or n >= total_rows:
+            break
+        n = min(total_rows, int(n * max(2.0, budget_s / 2 / max(elapsed, 1e-3))))
+    # useful FLOPs of the sampled rows: the per-row share of the whole call
+    flops_per_row = F.useful_flops(w) / total_rows
+    value = flops_per_row * n / elapsed / 1e12
+    return {"value": round(value, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {total_rows} rows of {w.name} (fp64, masked dense softmax per row)",
+            "seconds": round(elapsed, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default=None, help="time only this workload name")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_long_sequence_amd import flops as F
+    from sparse_long_sequence_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    head = W.LONGFORMER_BASE
+    results = {}
+    for w in W.ORDERED:
+        if args.only and w.name != args.only and w is not head:
+            continue
+        log(f"bench: {w.name} (B={w.B} H={w.H} N={w.N} {w.dtype})")
+        call = Call(w, dev)
+        steps = args.steps
+        region_ms, mean_ms, med_ms = time_calls(call, steps, args.warmup)
+        fl = F.useful_flops(w)
+        by = F.algorithmic_bytes(w)
+        peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        results[w.name] = {
+            "ms_per_call": round(region_ms, 5), "ms_per_launch_mean": round(mean_ms, 5),
+            "ms_per_launch_median": round(med_ms, 5),
+            "useful_tflops": round(fl / (mean_ms * 1e-3) / 1e12, 3),
+            "frac_mfma_peak": round(fl / (mean_ms * 1e-3) / 1e12 / peak, 4),
+            "hbm_gbs_algorithmic": round(by / (mean_ms * 1e-3) / 1e9, 1),
+            "useful_flop": fl, "algorithmic_bytes": by,
+        }
+        log(f"  {results[w.name]}")
+        del call
+        torch.cuda.empty_cache()
+
+    r = results[head.name]
+    fl = F.useful_flops(head)
+    by = F.algorithmic_bytes(head)
+    achieved = fl / (r["ms_per_launch_mean"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(fl / (r["ms_per_call"] * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_call"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1) Q/K/V, cast to bf16)",
+        "config": {"workload": head.name, "B": head.B, "H": head.H, "N": head.N, "D": head.D,
+                   "radius": head.radius, "n_global": len(head.global_idx),
+                   "separate_global": head.separate_global, "causal": head.causal},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_fwd_kernel<bf16>",
+                     "hbm_gbs_algorithmic": round(by / (r["ms_per_launch_mean"] * 1e-3) / 1e9, 1),
+                     "hbm_peak_gbs": HBM_PEAK_GBS},
+        "workloads": results,
+    }
+    if not args.no_cpu:
+        log("bench: cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(head)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

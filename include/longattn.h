@@ -1,0 +1,156 @@
+/* longattn.h — C ABI of the sparse long-sequence attention forward pass (gfx950).
+ *
+ * Two operations, both exact masked softmax attention (LongNet page, §3.4
+ * "Standard Self-Attention and Sparse Attention (Preliminaries)", Eq. 2):
+ *
+ *   la_attn_forward     sliding-window attention of radius R (optionally dilated
+ *                       per head and causal), unioned with a set G of global
+ *                       tokens that attend to every key and that every query
+ *                       attends to, with optional separate projections for the
+ *                       global rows and an optional per-head scalar relative-
+ *                       position bias.
+ *                       Longformer page, §3.4 "Sliding Window Attention"
+ *                       (Fig. 2b), "Dilated Sliding Window Attention" (Fig. 2c,
+ *                       head-specific dilation), "Global Attention" (Fig. 2d),
+ *                       "Separate Linear Projections for Local vs. Global
+ *                       Attention", "Autoregressive Language Modeling
+ *                       Configuration" (causal window). ETC page, §3.4
+ *                       "Global-Local Attention" (g2g/g2l/l2g full, l2l within
+ *                       radius r, two unified softmaxes) and "Relative Position
+ *                       Encoding" (labels clipped at distance k).
+ *
+ *   la_dilated_forward  LongNet dilated attention: for every (segment length w,
+ *                       dilation r) pattern, each length-w segment keeps the
+ *                       positions whose offset from the segment start is
+ *                       congruent to (head mod r), attends densely among them,
+ *                       and the per-pattern outputs are mixed with weights
+ *                       proportional to their softmax denominators.
+ *                       LongNet page, §3.4 "Dilated Attention: Core Mechanism"
+ *                       (Eqs. 3-8), "Mixture of Dilated Attentions" (Eqs. 9-10),
+ *                       "Multi-Head Dilated Attention: Offset Mechanism"
+ *                       (Eqs. 13-15).
+ *
+ * Conventions for every call:
+ *   - B, H, N >= 0; a call with B, H or N equal to 0 does nothing and returns
+ *     LA_OK (after the remaining argument checks that need no pointer).
+ *   - q, k, v, out (and qg, kg, vg) are device tensors, contiguous [B,H,N,D]
+ *     row-major, 16-byte aligned, of the dtype in la_dims (bf16 or fp32);
+ *     D must be 64 and la_attn_forward takes H <= 64 (LA_EUNSUPPORTED above).
+ *   - logits are (q_i . k_j) / sqrt(D) + bias_ij in fp32; softmax and both
+ *     products accumulate in fp32; out is rounded to its dtype (RNE).
+ *   - lse (optional) is device fp32 [B,H,N]: the natural-log softmax
+ *     denominator, lse_i = ln sum_j c_ij exp(s_ij).
+ *   - Ownership: the caller owns every buffer. The library allocates nothing,
+ *     keeps no pointer after returning, never writes its inputs, and fully
+ *     overwrites out and lse. out must not alias an input. Workspace rules
+ *     are given with each call's extras below.
+ *   - All work is enqueued on `stream` (0 = the null stream); the call returns
+ *     without synchronising and issues no device-to-host copy.
+ *   - Errors: host-detectable argument errors return LA_EINVAL and enqueue
+ *     nothing; valid but unbuilt combinations return LA_EUNSUPPORTED; a failed
+ *     launch returns LA_EHIP. la_last_error() then describes the failure.
+ *     Facts that live in device memory (global_idx sorted and in range) are
+ *     the caller's contract; la_check_global_idx() verifies them synchronously.
+ *   - Thread safety: calls may come from several host threads; the only state
+ *     is the thread-local error message.
+ */
+#ifndef LONGATTN_H
+#define LONGATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LA_OK = 0, LA_EINVAL = -1, LA_EUNSUPPORTED = -2, LA_EHIP = -3 } la_status;
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+/* Shape and element type shared by q, k, v, out: [B,H,N,D]. */
+typedef struct {
+  int32_t B, H, N, D;
+  int32_t dtype; /* la_dtype */
+} la_dims;
+
+/* Optional extras of la_attn_forward; pass NULL for none. */
+typedef struct {
+  /* rel_bias holds H*(2*rel_k+1) fp32 entries; entry [h][clamp(j-i,-rel_k,rel_k)+rel_k]
+   * is added to the logit of every pair (i,j) whose members are of the same kind
+   * (both global or both non-global). Required (> 0) iff rel_bias != NULL. */
+  int32_t rel_k;
+  /* Separate projections for the global rows: all three or none, dims as q.
+   * A global row i then uses qg_i, kg_j, vg_j for every key j; non-global rows
+   * keep q, k, v (for their global columns too). */
+  const void *qg, *kg, *vg;
+  /* Device scratch of at least la_attn_workspace_size() bytes, 256-byte aligned;
+   * required when n_global > 0. Its last block holds completion counters: the
+   * workspace must be zero-filled once before its first use (e.g. at
+   * allocation); every call returns the counters to zero, so later calls need
+   * no clearing. Calls that share a workspace must not overlap in time. */
+  void *workspace;
+  size_t workspace_bytes;
+} la_attn_ext;
+
+/* Optional extras of la_dilated_forward; pass NULL for none. */
+typedef struct {
+  float *lse;      /* device fp32 [B,H,N] or NULL; -inf where no pattern covers a row */
+  void *workspace; /* device scratch of la_dilated_workspace_size() bytes, 256-byte aligned */
+  size_t workspace_bytes;
+} la_dilated_ext;
+
+/* Band + global attention.
+ *  global_idx  device int32[n_global], strictly increasing, each in [0,N); NULL iff n_global == 0.
+ *  radius      R >= 0, counted in dilation steps: row i sees keys i + d*m for |m| <= R
+ *              (causal: -R <= m <= 0), inside [0,N).
+ *  dilation    host int32[H], each >= 1; NULL means 1 for every head.
+ *  causal      0 or 1; when 1, every pair (band, global row, global column) needs j <= i.
+ *  rel_bias    device fp32 [H][2*rel_k+1] or NULL (see la_attn_ext.rel_k).
+ *  out         device [B,H,N,D], dtype as q.   lse: device fp32 [B,H,N] or NULL.
+ * Requires ext->workspace when n_global > 0 (ext may be NULL otherwise). */
+la_status la_attn_forward(const la_dims *dims, const void *q, const void *k, const void *v,
+                          const int32_t *global_idx, int32_t n_global, int32_t radius,
+                          const int32_t *dilation, int32_t causal, const float *rel_bias,
+                          void *out, float *lse, hipStream_t stream, const la_attn_ext *ext);
+
+/* LongNet dilated attention mixture (bf16 only).
+ *  seg_lens, dil_rates  host int32[n_pairs]: segment length w_k >= 1 and dilation r_k >= 1.
+ *                       1 <= n_pairs <= 16. The last segment of a pattern is
+ *                       truncated at N. Head h uses offset h mod r_k.
+ *  causal               0 or 1: within a segment, key position <= query position.
+ *  out                  device bf16 [B,H,N,D]; rows no pattern covers are 0.
+ * Requires ext->workspace of la_dilated_workspace_size() bytes. */
+la_status la_dilated_forward(const la_dims *dims, const void *q, const void *k, const void *v,
+                             const int32_t *seg_lens, const int32_t *dil_rates, int32_t n_pairs,
+                             int32_t causal, void *out, hipStream_t stream,
+                             const la_dilated_ext *ext);
+
+/* Bytes of workspace la_attn_forward needs for these dims and n_global
+ * (0 when n_global == 0). has_separate_global is accepted for symmetry and
+ * does not change the size. Returns 0 for invalid dims. */
+size_t la_attn_workspace_size(const la_dims *dims, int32_t n_global, int32_t has_separate_global);
+
+/* Bytes of workspace la_dilated_forward needs for these dims and patterns
+ * (host arrays as in la_dilated_forward). Returns 0 for invalid arguments. */
+size_t la_dilated_workspace_size(const la_dims *dims, const int32_t *seg_lens,
+                                 const int32_t *dil_rates, int32_t n_pairs);
+
+/* Synchronous test helper: LA_OK iff global_idx (device int32[n_global]) is
+ * strictly increasing and inside [0,N). Copies the array to the host on `stream`
+ * and waits for it. */
+la_status la_check_global_idx(const int32_t *global_idx, int32_t n_global, int32_t N,
+                              hipStream_t stream);
+
+/* Message of the last non-OK status on this thread ("" if none). */
+const char *la_last_error(void);
+
+/* ABI version of this library. */
+int32_t la_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LONGATTN_H */

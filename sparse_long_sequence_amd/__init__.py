@@ -1,0 +1,261 @@
+"""sparse_long_sequence_amd — sparse long-sequence attention forward for MI355X (gfx950).
+
+A thin ctypes binding over ``liblongattn.so``, whose C ABI is declared in
+``include/longattn.h``. The functions here only marshal arguments: every step
+of the attention runs in the library's HIP kernels. PyTorch supplies device
+memory and streams. If the library is missing, every call raises
+:class:`LaError`; nothing falls back to another implementation.
+
+Entry points (same names as the C ABI):
+
+* :func:`la_attn_forward` — sliding-window (optionally dilated, causal) plus
+  global-token attention, with optional separate global projections and a
+  per-head scalar relative-position bias (Longformer, ETC).
+* :func:`la_dilated_forward` — LongNet's mixture of dilated attentions.
+* :func:`la_attn_workspace_size`, :func:`la_dilated_workspace_size`,
+  :func:`la_check_global_idx`, :func:`la_last_error`, :func:`la_version`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblongattn.so")
+
+LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EHIP = 0, -1, -2, -3
+LA_F32, LA_BF16 = 0, 1
+
+
+class LaError(RuntimeError):
+    """A non-OK status from the library (``status`` holds the code)."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"longattn status {status}: {msg}")
+        self.status = status
+
+
+class LaDims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class LaAttnExt(ctypes.Structure):
+    _fields_ = [("rel_k", ctypes.c_int32), ("qg", ctypes.c_void_p), ("kg", ctypes.c_void_p),
+                ("vg", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class LaDilatedExt(ctypes.Structure):
+    _fields_ = [("lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_lib: Optional[ctypes.CDLL] = None
+
+# Every symbol include/longattn.h declares.
+EXPORTS = ("la_attn_forward", "la_dilated_forward", "la_attn_workspace_size",
+           "la_dilated_workspace_size", "la_check_global_idx", "la_last_error", "la_version")
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LaError(LA_EHIP, f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(or python -m sparse_long_sequence_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.la_version.restype = ctypes.c_int32
+    L.la_last_error.restype = ctypes.c_char_p
+    L.la_attn_forward.restype = ctypes.c_int32
+    L.la_attn_forward.argtypes = [ctypes.POINTER(LaDims), ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                  _i32p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(LaAttnExt)]
+    L.la_dilated_forward.restype = ctypes.c_int32
+    L.la_dilated_forward.argtypes = [ctypes.POINTER(LaDims), ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(LaDilatedExt)]
+    L.la_attn_workspace_size.restype = ctypes.c_size_t
+    L.la_attn_workspace_size.argtypes = [ctypes.POINTER(LaDims), ctypes.c_int32, ctypes.c_int32]
+    L.la_dilated_workspace_size.restype = ctypes.c_size_t
+    L.la_dilated_workspace_size.argtypes = [ctypes.POINTER(LaDims), _i32p, _i32p, ctypes.c_int32]
+    L.la_check_global_idx.restype = ctypes.c_int32
+    L.la_check_global_idx.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p]
+    _lib = L
+    return L
+
+
+def la_version() -> int:
+    return int(lib().la_version())
+
+
+def la_last_error() -> str:
+    return lib().la_last_error().decode()
+
+
+def _check(status: int):
+    if status != LA_OK:
+        raise LaError(status, la_last_error())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_F32
+    raise LaError(LA_EINVAL, f"unsupported dtype {t.dtype}")
+
+
+def _dims(q: torch.Tensor) -> LaDims:
+    if q.dim() != 4:
+        raise LaError(LA_EINVAL, "tensors must be [B, H, N, D]")
+    B, H, N, D = q.shape
+    return LaDims(B, H, N, D, _dtype_code(q))
+
+
+def _dev(t: Optional[torch.Tensor], like: torch.Tensor, name: str) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda or not t.is_contiguous() or t.shape != like.shape or t.dtype != like.dtype:
+        raise LaError(LA_EINVAL, f"{name} must be a contiguous device tensor shaped and typed like q")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _host_i32(vals: Sequence[int]):
+    arr = (ctypes.c_int32 * len(vals))(*[int(x) for x in vals])
+    return arr
+
+
+def la_attn_workspace_size(dims: LaDims, n_global: int, has_separate_global: bool = False) -> int:
+    return int(lib().la_attn_workspace_size(ctypes.byref(dims), int(n_global),
+                                            int(bool(has_separate_global))))
+
+
+def la_dilated_workspace_size(dims: LaDims, seg_lens: Sequence[int], dil_rates: Sequence[int]) -> int:
+    return int(lib().la_dilated_workspace_size(ctypes.byref(dims), _host_i32(seg_lens),
+                                               _host_i32(dil_rates), len(seg_lens)))
+
+
+def _workspace(nbytes: int, device, given: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    if given is not None:
+        if given.numel() * given.element_size() < nbytes or not given.is_cuda:
+            raise LaError(LA_EINVAL, "workspace tensor too small")
+        return given
+    # torch's caching allocator returns 512-byte aligned blocks; zero-filled
+    # once, as la_attn_forward's completion counters require
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def la_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    global_idx: Optional[torch.Tensor] = None, radius: int = 0,
+                    dilation: Optional[Sequence[int]] = None, causal: bool = False,
+                    rel_bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, qg: Optional[torch.Tensor] = None,
+                    kg: Optional[torch.Tensor] = None, vg: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None,
+                    want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Band + global attention; returns ``(out, lse)``.
+
+    ``global_idx`` is a device int32 tensor of strictly increasing positions.
+    ``rel_bias`` is a device fp32 ``[H, 2k+1]`` table. ``out``, ``lse`` and the
+    workspace are allocated with torch when not given.
+    """
+    dims = _dims(q)
+    for name, t in (("k", k), ("v", v)):
+        _dev(t, q, name)
+    qptr = _dev(q, q, "q")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, q, "out")
+    if want_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != tuple(q.shape[:3])):
+        raise LaError(LA_EINVAL, "lse must be a contiguous fp32 [B, H, N] tensor")
+    n_global = 0
+    gptr = 0
+    if global_idx is not None:
+        if global_idx.dtype != torch.int32 or not global_idx.is_cuda or global_idx.dim() != 1:
+            raise LaError(LA_EINVAL, "global_idx must be a 1-D device int32 tensor")
+        n_global = global_idx.numel()
+        gptr = global_idx.data_ptr() if n_global else 0
+    dil = None if dilation is None else _host_i32(dilation)
+    if dilation is not None and len(dilation) != dims.H:
+        raise LaError(LA_EINVAL, "dilation needs one entry per head")
+    rk = 0
+    rptr = 0
+    if rel_bias is not None:
+        if rel_bias.dtype != torch.float32 or not rel_bias.is_cuda or rel_bias.dim() != 2 \
+                or rel_bias.shape[0] != dims.H or rel_bias.shape[1] % 2 != 1:
+            raise LaError(LA_EINVAL, "rel_bias must be a device fp32 [H, 2k+1] tensor")
+        rk = (rel_bias.shape[1] - 1) // 2
+        rel_bias = rel_bias.contiguous()
+        rptr = rel_bias.data_ptr()
+    sep = qg is not None
+    ws = _workspace(la_attn_workspace_size(dims, n_global, sep), q.device, workspace)
+    ext = LaAttnExt(rk, _dev(qg, q, "qg") or None, _dev(kg, q, "kg") or None,
+                    _dev(vg, q, "vg") or None, ws.data_ptr() if ws is not None else None,
+                    ws.numel() if ws is not None else 0)
+    st = lib().la_attn_forward(ctypes.byref(dims), qptr, k.data_ptr(), v.data_ptr(), gptr or None,
+                               n_global, int(radius), dil, int(bool(causal)), rptr or None,
+                               out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                               _stream(q, stream), ctypes.byref(ext))
+    _check(st)
+    return out, lse
+
+
+def la_dilated_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       seg_lens: Sequence[int], dil_rates: Sequence[int], causal: bool = True,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None,
+                       want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """LongNet dilated attention mixture; returns ``(out, lse)``."""
+    dims = _dims(q)
+    for name, t in (("k", k), ("v", v)):
+        _dev(t, q, name)
+    qptr = _dev(q, q, "q")
+    if len(seg_lens) != len(dil_rates):
+        raise LaError(LA_EINVAL, "seg_lens and dil_rates differ in length")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, q, "out")
+    if want_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    nbytes = la_dilated_workspace_size(dims, seg_lens, dil_rates) if len(seg_lens) else 0
+    ws = _workspace(nbytes, q.device, workspace)
+    ext = LaDilatedExt(lse.data_ptr() if lse is not None else None,
+                       ws.data_ptr() if ws is not None else None,
+                       ws.numel() if ws is not None else 0)
+    st = lib().la_dilated_forward(ctypes.byref(dims), qptr, k.data_ptr(), v.data_ptr(),
+                                  _host_i32(seg_lens), _host_i32(dil_rates), len(seg_lens),
+                                  int(bool(causal)), out.data_ptr(), _stream(q, stream),
+                                  ctypes.byref(ext))
+    _check(st)
+    return out, lse
+
+
+def la_check_global_idx(global_idx: torch.Tensor, N: int, stream=None) -> bool:
+    """Synchronous check that ``global_idx`` is strictly increasing in [0, N)."""
+    n = global_idx.numel()
+    st = lib().la_check_global_idx(global_idx.data_ptr() if n else None, n, int(N),
+                                   _stream(global_idx, stream))
+    if st == LA_EINVAL:
+        return False
+    _check(st)
+    return True

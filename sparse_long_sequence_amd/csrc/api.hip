@@ -1,0 +1,275 @@
+// api.hip — the C ABI declared in include/longattn.h: argument checks,
+// workspace sizing and launches. No allocation, no host synchronisation
+// (except la_check_global_idx, a synchronous test helper).
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "longattn.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+la_status fail(la_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+constexpr int32_t kDHead = 64;
+constexpr int32_t kQTile = 64;
+constexpr int32_t kChunk = 512;  // keys per global-row partial
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+la_status check_dims(const la_dims* d, bool need_bf16) {
+  if (!d) return fail(LA_EINVAL, "dims is NULL");
+  if (d->B < 0 || d->H < 0 || d->N < 0 || d->D < 1)
+    return fail(LA_EINVAL, "dims must be non-negative (B, H, N) and D positive");
+  if (d->dtype != LA_F32 && d->dtype != LA_BF16) return fail(LA_EINVAL, "unknown dtype");
+  if (d->D != kDHead) return fail(LA_EUNSUPPORTED, "only D == 64 is built");
+  if (need_bf16 && d->dtype != LA_BF16) return fail(LA_EUNSUPPORTED, "this call is built for bf16 only");
+  const int64_t total = (int64_t)d->B * d->H * d->N;
+  if (total > (int64_t)1 << 31) return fail(LA_EUNSUPPORTED, "B*H*N above 2^31 rows");
+  return LA_OK;
+}
+
+bool is_empty(const la_dims* d) { return d->B == 0 || d->H == 0 || d->N == 0; }
+
+int32_t n_chunks_of(int32_t N) { return (N + kChunk - 1) / kChunk; }
+
+// Workspace of la_attn_forward: global-row partials (fp32 O, fp32 lse), then
+// one int32 counter per (batch, head, 64-row global tile).
+struct AttnWs {
+  size_t o_off, lse_off, cnt_off, bytes;
+};
+
+AttnWs attn_ws_layout(const la_dims* d, int32_t n_global) {
+  AttnWs w = {0, 0, 0, 0};
+  if (n_global <= 0) return w;
+  const size_t parts = (size_t)d->B * d->H * n_global * n_chunks_of(d->N);
+  const size_t tiles = (size_t)d->B * d->H * ((n_global + kQTile - 1) / kQTile);
+  w.lse_off = align_up(parts * kDHead * sizeof(float));
+  w.cnt_off = w.lse_off + align_up(parts * sizeof(float));
+  w.bytes = w.cnt_off + align_up(tiles * sizeof(int32_t));
+  return w;
+}
+
+size_t attn_ws_bytes(const la_dims* d, int32_t n_global) { return attn_ws_layout(d, n_global).bytes; }
+
+struct DilPlan {
+  la::DilArgs a;
+  size_t ws_bytes;
+};
+
+la_status plan_dilated(const la_dims* d, const int32_t* w, const int32_t* r, int32_t n_pairs,
+                       DilPlan& p) {
+  if (!w || !r) return fail(LA_EINVAL, "seg_lens and dil_rates are required");
+  if (n_pairs < 1) return fail(LA_EINVAL, "n_pairs must be >= 1");
+  if (n_pairs > la::kMaxPairs) return fail(LA_EUNSUPPORTED, "more than 16 (w, r) pairs");
+  memset(&p.a, 0, sizeof(p.a));
+  la::DilArgs& a = p.a;
+  a.B = d->B;
+  a.H = d->H;
+  a.N = d->N;
+  a.n_pairs = n_pairs;
+  int64_t rows = 0;
+  for (int32_t k = 0; k < n_pairs; ++k) {
+    if (w[k] < 1 || r[k] < 1) return fail(LA_EINVAL, "every w and r must be >= 1");
+    a.w[k] = w[k];
+    a.r[k] = r[k];
+    a.nseg[k] = (d->N + w[k] - 1) / w[k];
+    a.seg_rows[k] = (w[k] + r[k] - 1) / r[k];
+    a.qtiles[k] = (a.seg_rows[k] + kQTile - 1) / kQTile;
+    a.row_off[k] = rows;
+    rows += (int64_t)d->B * d->H * a.nseg[k] * a.seg_rows[k];
+  }
+  a.rows_total = rows;
+  // Patterns with more query tiles per segment carry the longest workgroups:
+  // launch them first.
+  std::vector<int32_t> ord(n_pairs);
+  for (int32_t k = 0; k < n_pairs; ++k) ord[k] = k;
+  std::stable_sort(ord.begin(), ord.end(),
+                   [&](int32_t x, int32_t y) { return a.qtiles[x] > a.qtiles[y]; });
+  int64_t wg = 0;
+  for (int32_t i = 0; i < n_pairs; ++i) {
+    const int32_t k = ord[i];
+    a.order[i] = k;
+    a.wg_start[i] = wg;
+    wg += (int64_t)d->B * d->H * a.nseg[k] * a.qtiles[k];
+  }
+  a.wg_start[n_pairs] = wg;
+  if (wg > 0x7fffffffLL) return fail(LA_EUNSUPPORTED, "launch grid too large");
+  p.ws_bytes = align_up((size_t)rows * kDHead * sizeof(float)) + align_up((size_t)rows * sizeof(float));
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t la_version(void) { return 1; }
+
+const char* la_last_error(void) { return g_err.c_str(); }
+
+size_t la_attn_workspace_size(const la_dims* dims, int32_t n_global, int32_t has_separate_global) {
+  (void)has_separate_global;
+  if (check_dims(dims, false) != LA_OK || n_global < 0 || n_global > dims->N) return 0;
+  return attn_ws_bytes(dims, n_global);
+}
+
+size_t la_dilated_workspace_size(const la_dims* dims, const int32_t* seg_lens,
+                                 const int32_t* dil_rates, int32_t n_pairs) {
+  if (check_dims(dims, true) != LA_OK) return 0;
+  DilPlan p;
+  if (plan_dilated(dims, seg_lens, dil_rates, n_pairs, p) != LA_OK) return 0;
+  return p.ws_bytes;
+}
+
+la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, const void* v,
+                          const int32_t* global_idx, int32_t n_global, int32_t radius,
+                          const int32_t* dilation, int32_t causal, const float* rel_bias,
+                          void* out, float* lse, hipStream_t stream, const la_attn_ext* ext) {
+  la_status st = check_dims(dims, false);
+  if (st != LA_OK) return st;
+  if (is_empty(dims)) return LA_OK;  // nothing to compute
+  if (!q || !k || !v || !out) return fail(LA_EINVAL, "q, k, v and out are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(LA_EINVAL, "q, k, v and out must be 16-byte aligned");
+  if (n_global < 0 || n_global > dims->N) return fail(LA_EINVAL, "n_global must be in [0, N]");
+  if ((n_global > 0) != (global_idx != nullptr))
+    return fail(LA_EINVAL, "global_idx must be non-NULL exactly when n_global > 0");
+  if (radius < 0) return fail(LA_EINVAL, "radius must be >= 0");
+  if (causal != 0 && causal != 1) return fail(LA_EINVAL, "causal must be 0 or 1");
+  la::AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  if (dilation) {
+    for (int32_t h = 0; h < dims->H; ++h)
+      if (dilation[h] < 1) return fail(LA_EINVAL, "dilation entries must be >= 1");
+  }
+  if (dims->H > la::kMaxHeadsDil) return fail(LA_EUNSUPPORTED, "H above 64");
+  for (int32_t h = 0; h < dims->H; ++h) a.dil[h] = dilation ? dilation[h] : 1;
+  const int32_t rel_k = ext ? ext->rel_k : 0;
+  if (rel_bias && rel_k < 1) return fail(LA_EINVAL, "rel_bias needs ext->rel_k >= 1");
+  if (!rel_bias && rel_k != 0) return fail(LA_EINVAL, "ext->rel_k set without rel_bias");
+  if (rel_k > la::kMaxRelK) return fail(LA_EUNSUPPORTED, "rel_k above 31");
+  const void *qg = q, *kg = k, *vg = v;
+  if (ext && (ext->qg || ext->kg || ext->vg)) {
+    if (!(ext->qg && ext->kg && ext->vg)) return fail(LA_EINVAL, "qg, kg, vg: all three or none");
+    if (!aligned16(ext->qg) || !aligned16(ext->kg) || !aligned16(ext->vg))
+      return fail(LA_EINVAL, "qg, kg, vg must be 16-byte aligned");
+    qg = ext->qg;
+    kg = ext->kg;
+    vg = ext->vg;
+  }
+  const size_t need = attn_ws_bytes(dims, n_global);
+  if (need > 0) {
+    if (!ext || !ext->workspace || ext->workspace_bytes < need)
+      return fail(LA_EINVAL, "workspace missing or smaller than la_attn_workspace_size()");
+    if (((uintptr_t)ext->workspace & (kAlign - 1)) != 0)
+      return fail(LA_EINVAL, "workspace must be 256-byte aligned");
+  }
+
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.qg = qg;
+  a.kg = kg;
+  a.vg = vg;
+  a.gidx = global_idx;
+  a.n_global = n_global;
+  a.B = dims->B;
+  a.H = dims->H;
+  a.N = dims->N;
+  a.radius = radius;
+  a.causal = causal;
+  a.rel_bias = rel_bias;
+  a.rel_k = rel_k;
+  a.out = out;
+  a.lse = lse;
+  if (need > 0) {
+    const AttnWs lay = attn_ws_layout(dims, n_global);
+    char* base = reinterpret_cast<char*>(ext->workspace);
+    a.ws_o = reinterpret_cast<float*>(base + lay.o_off);
+    a.ws_lse = reinterpret_cast<float*>(base + lay.lse_off);
+    a.ws_cnt = reinterpret_cast<int32_t*>(base + lay.cnt_off);
+  }
+  a.chunk_len = kChunk;
+  a.n_chunks = n_chunks_of(dims->N);
+  int32_t tiles = 0;
+  for (int32_t h = 0; h < dims->H; ++h)
+    tiles = std::max(tiles, la::host_band_tiles_of_head(dims->N, a.dil[h]));
+  a.band_tiles_per_head = tiles;
+  const int64_t band_wg = (int64_t)dims->B * dims->H * tiles;
+  a.n_gq_tiles = (n_global + kQTile - 1) / kQTile;
+  const int64_t glob_wg = (int64_t)dims->B * dims->H * a.n_gq_tiles * a.n_chunks;
+  if (band_wg + glob_wg > 0x7fffffffLL) return fail(LA_EUNSUPPORTED, "launch grid too large");
+  a.n_band_wg = (int32_t)band_wg;
+  a.n_glob_wg = (int32_t)glob_wg;
+  a.scale_log2 = (float)(1.0 / sqrt((double)kDHead) * 1.4426950408889634);
+  hipError_t e = la::launch_attn(a, dims->dtype, stream);
+  if (e != hipSuccess) return fail(LA_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(e));
+  return LA_OK;
+}
+
+la_status la_dilated_forward(const la_dims* dims, const void* q, const void* k, const void* v,
+                             const int32_t* seg_lens, const int32_t* dil_rates, int32_t n_pairs,
+                             int32_t causal, void* out, hipStream_t stream,
+                             const la_dilated_ext* ext) {
+  la_status st = check_dims(dims, true);
+  if (st != LA_OK) return st;
+  if (n_pairs < 1) return fail(LA_EINVAL, "n_pairs must be >= 1");
+  if (is_empty(dims)) return LA_OK;  // nothing to compute
+  if (!q || !k || !v || !out) return fail(LA_EINVAL, "q, k, v and out are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(LA_EINVAL, "q, k, v and out must be 16-byte aligned");
+  if (causal != 0 && causal != 1) return fail(LA_EINVAL, "causal must be 0 or 1");
+  DilPlan p;
+  st = plan_dilated(dims, seg_lens, dil_rates, n_pairs, p);
+  if (st != LA_OK) return st;
+  if (!ext || !ext->workspace || ext->workspace_bytes < p.ws_bytes)
+    return fail(LA_EINVAL, "workspace missing or smaller than la_dilated_workspace_size()");
+  if (((uintptr_t)ext->workspace & (kAlign - 1)) != 0)
+    return fail(LA_EINVAL, "workspace must be 256-byte aligned");
+  la::DilArgs& a = p.a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.causal = causal;
+  a.out = out;
+  a.lse = ext->lse;
+  a.ws_o = reinterpret_cast<float*>(ext->workspace);
+  a.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ext->workspace) +
+                                      align_up((size_t)a.rows_total * kDHead * sizeof(float)));
+  a.scale_log2 = (float)(1.0 / sqrt((double)kDHead) * 1.4426950408889634);
+  hipError_t e = la::launch_dilated(a, stream);
+  if (e != hipSuccess) return fail(LA_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(e));
+  return LA_OK;
+}
+
+la_status la_check_global_idx(const int32_t* global_idx, int32_t n_global, int32_t N,
+                              hipStream_t stream) {
+  if (n_global < 0 || n_global > N) return fail(LA_EINVAL, "n_global must be in [0, N]");
+  if (n_global == 0) return global_idx ? fail(LA_EINVAL, "global_idx given with n_global == 0") : LA_OK;
+  if (!global_idx) return fail(LA_EINVAL, "global_idx is NULL");
+  std::vector<int32_t> h(n_global);
+  hipError_t e = hipMemcpyAsync(h.data(), global_idx, sizeof(int32_t) * n_global,
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(LA_EHIP, std::string("copy failed: ") + hipGetErrorString(e));
+  for (int32_t i = 0; i < n_global; ++i) {
+    if (h[i] < 0 || h[i] >= N) return fail(LA_EINVAL, "global_idx entry outside [0, N)");
+    if (i > 0 && h[i] <= h[i - 1]) return fail(LA_EINVAL, "global_idx not strictly increasing");
+  }
+  return LA_OK;
+}
+
+}  // extern "C"

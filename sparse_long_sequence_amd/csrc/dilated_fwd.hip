@@ -1,0 +1,122 @@
+// dilated_fwd.hip — LongNet dilated attention on gfx950.
+//
+// For each (segment length w, dilation r) pattern and head h, every segment of
+// w positions keeps the rows whose offset from the segment start is congruent
+// to h mod r (LongNet page, §3.4 "Dilated Attention: Core Mechanism", Eqs. 3-5,
+// and "Multi-Head Dilated Attention: Offset Mechanism", Eqs. 13-15). Those rows
+// are read straight from Q, K, V as a strided view (row stride r*D): no gather
+// copy is made. Dense attention runs among them (Eq. 6), causal in position
+// when requested, and each pattern writes a partial (normalised O, lse) per
+// kept row. A second launch scatters and mixes: a row's output is the sum of
+// the partials of the patterns that kept it, weighted by exp(lse_k), i.e. by
+// the softmax denominators (Eqs. 7-10, "Mixture of Dilated Attentions");
+// rows a pattern skipped receive nothing from it.
+#include "tile_core.h"
+#include "kernels.h"
+
+namespace la {
+
+__global__ __launch_bounds__(kThreads) void dilated_pair_kernel(DilArgs a) {
+  using TT = TileTraits<bf16>;
+  __shared__ TT::Smem sm;
+  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t wg = blockIdx.x;
+  int32_t oi = 0;
+  while (oi + 1 < a.n_pairs && wg >= a.wg_start[oi + 1]) ++oi;
+  const int32_t k = a.order[oi];
+  const int64_t local = wg - a.wg_start[oi];
+  const int32_t w = a.w[k], r = a.r[k], nseg = a.nseg[k], qtiles = a.qtiles[k];
+  // heaviest (last) query tiles of every segment first
+  const int64_t per_rank = (int64_t)a.B * a.H * nseg;
+  const int32_t qt = qtiles - 1 - (int32_t)(local / per_rank);
+  const int64_t rest = local % per_rank;
+  const int32_t seg = (int32_t)(rest % nseg);
+  const int32_t bh = (int32_t)(rest / nseg);
+  const int32_t h = bh % a.H;
+  const int32_t sigma = seg * w;
+  const int32_t L = min(w, a.N - sigma);
+  const int32_t s = h % r;
+  const int32_t n_rows = L > s ? (L - s + r - 1) / r : 0;
+  const int32_t t0 = qt * kTQ;
+  if (t0 >= n_rows) return;
+  const int32_t qcount = min(kTQ, n_rows - t0);
+  const size_t head_elems = (size_t)a.N * kD;
+  const bf16* qb = reinterpret_cast<const bf16*>(a.q) + bh * head_elems;
+  const bf16* kb = reinterpret_cast<const bf16*>(a.k) + bh * head_elems;
+  const bf16* vb = reinterpret_cast<const bf16*>(a.v) + bh * head_elems;
+  const int32_t base = sigma + s;
+  const RowMap qm = {nullptr, base + r * t0, r, qcount};
+  TT::Wave wv;
+  TT::load_q(wv, qb, qm, wave, lane);
+  const int32_t qi = 16 * wave + (lane & 15);
+  const int32_t qpos = base + r * (t0 + qi);
+  const int32_t hi = a.causal ? t0 + qcount - 1 : n_rows - 1;
+  const int32_t n_tiles = (hi + kTK) / kTK;
+
+  auto desc = [&](int32_t n, RowMap& kmo, MaskRule& mro) {
+    const int32_t u0 = n * kTK;
+    const int32_t kcount = min(kTK, hi - u0 + 1);
+    kmo = {nullptr, base + r * u0, r, kcount};
+    const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= t0);
+    mro = {kSeg, full ? 0 : 1, a.causal, 0, r, t0 - u0};
+  };
+  const BiasRule br = {nullptr, 0, 0};
+  run_tiles<bf16>(sm, wv, kb, vb, n_tiles, desc, br, false, nullptr, 0, qi, qpos, a.scale_log2);
+  const float l_tot = wave_sum_xor16_32(wv.l);
+  if (qi < qcount) {
+    const int64_t prow = a.row_off[k] + ((int64_t)bh * nseg + seg) * a.seg_rows[k] + t0 + qi;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    TileTraits<float>::store_row(a.ws_o + prow * kD, wv.o, inv, lane);
+    if ((lane >> 4) == 0) a.ws_lse[prow] = l_tot > 0.f ? (wv.m + __log2f(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+// Scatter + mixture. 4 rows per 256-thread block, thread = d.
+__global__ __launch_bounds__(256) void dilated_combine_kernel(DilArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int32_t dd = threadIdx.x & 63;
+  const int64_t total = (int64_t)a.B * a.H * a.N;
+  if (row >= total) return;
+  const int32_t i = (int32_t)(row % a.N);
+  const int32_t bh = (int32_t)(row / a.N);
+  const int32_t h = bh % a.H;
+  int64_t prow[kMaxPairs];
+  float lk[kMaxPairs];
+  float L = kNegInf;
+  for (int32_t k = 0; k < a.n_pairs; ++k) {
+    const int32_t w = a.w[k], r = a.r[k];
+    const int32_t seg = i / w, off = i - seg * w;
+    prow[k] = -1;
+    lk[k] = kNegInf;
+    if (off % r != h % r) continue;
+    prow[k] = a.row_off[k] + ((int64_t)bh * a.nseg[k] + seg) * a.seg_rows[k] + off / r;
+    lk[k] = a.ws_lse[prow[k]];
+    L = fmaxf(L, lk[k]);
+  }
+  float acc = 0.f, S = 0.f;
+  if (L != kNegInf) {
+    for (int32_t k = 0; k < a.n_pairs; ++k) {
+      if (prow[k] < 0 || lk[k] == kNegInf) continue;
+      const float wgt = __expf(lk[k] - L);
+      S += wgt;
+      acc += wgt * a.ws_o[prow[k] * kD + dd];
+    }
+  }
+  const float val = S > 0.f ? acc / S : 0.f;
+  reinterpret_cast<uint16_t*>(a.out)[row * kD + dd] = (uint16_t)f32_to_bf16_bits(val);
+  if (a.lse && dd == 0) a.lse[row] = S > 0.f ? L + __logf(S) : kNegInf;
+}
+
+hipError_t launch_dilated(const DilArgs& a, hipStream_t stream) {
+  const int64_t grid = a.wg_start[a.n_pairs];
+  if (grid > 0) {
+    hipLaunchKernelGGL(dilated_pair_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  hipLaunchKernelGGL(dilated_combine_kernel, dim3((uint32_t)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace la

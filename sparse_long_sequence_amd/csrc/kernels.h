@@ -1,0 +1,58 @@
+// kernels.h — argument blocks and launchers shared by the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+constexpr int32_t kMaxHeadsDil = 64;  // per-head dilation table size
+constexpr int32_t kMaxPairs = 16;     // LongNet patterns per call
+constexpr int32_t kMaxRelK = 31;      // 2k+1 <= 63 bias entries per head
+
+struct AttnArgs {
+  const void *q, *k, *v;
+  const void *qg, *kg, *vg;  // the global rows' projections (== q, k, v when shared)
+  const int32_t* gidx;
+  int32_t n_global;
+  int32_t B, H, N;
+  int32_t radius, causal;
+  int32_t dil[kMaxHeadsDil];
+  const float* rel_bias;
+  int32_t rel_k;
+  void* out;
+  float* lse;
+  float* ws_o;      // [B*H][n_global][n_chunks][D] global-row partials
+  float* ws_lse;    // [B*H][n_global][n_chunks]
+  int32_t* ws_cnt;  // [B*H][n_gq_tiles] finished-chunk counters, zero between calls
+  int32_t chunk_len, n_chunks;
+  int32_t band_tiles_per_head;
+  int32_t n_band_wg;
+  int32_t n_glob_wg;  // B*H*n_gq_tiles*n_chunks, placed first in the grid
+  int32_t n_gq_tiles;
+  float scale_log2;
+};
+
+struct DilArgs {
+  const void *q, *k, *v;
+  int32_t B, H, N, causal, n_pairs;
+  int32_t w[kMaxPairs], r[kMaxPairs];
+  int32_t nseg[kMaxPairs];      // segments of pattern k: ceil(N / w)
+  int32_t seg_rows[kMaxPairs];  // partial rows reserved per segment: ceil(w / r)
+  int32_t qtiles[kMaxPairs];    // query tiles per segment: ceil(seg_rows / 64)
+  int32_t order[kMaxPairs];     // launch order of the patterns (heaviest first)
+  int64_t wg_start[kMaxPairs + 1];  // first workgroup of the i-th pattern in launch order
+  int64_t row_off[kMaxPairs];   // first partial row of pattern k
+  int64_t rows_total;           // partial rows of all patterns
+  float* ws_o;                  // [rows_total][D]
+  float* ws_lse;                // [rows_total]
+  void* out;
+  float* lse;
+  float scale_log2;
+};
+
+hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream);
+hipError_t launch_dilated(const DilArgs& a, hipStream_t stream);
+int32_t host_band_tiles_of_head(int32_t N, int32_t d);
+
+}  // namespace la

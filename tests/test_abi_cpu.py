@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every symbol include/longattn.h declares, sizes its workspaces, and rejects bad
+arguments before touching the device."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_long_sequence_amd as la
+from sparse_long_sequence_amd import LaAttnExt, LaDilatedExt, LaDims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "longattn.h")
+FAKE = 0x10000  # a non-null, 256-byte aligned address; never dereferenced by these calls
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(la.LIB_PATH):
+        from sparse_long_sequence_amd import build
+        build.build()
+    return la.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_symbols() == sorted(la.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    assert la.la_version() == 1
+
+
+def _attn(L, dims, q=FAKE, k=FAKE, v=FAKE, gidx=None, n_global=0, radius=0, dil=None,
+          causal=0, rel_bias=None, out=FAKE, lse=None, ext=None):
+    return L.la_attn_forward(ctypes.byref(dims) if dims is not None else None, q, k, v, gidx,
+                             n_global, radius, dil, causal, rel_bias, out, lse, None,
+                             ctypes.byref(ext) if ext is not None else None)
+
+
+def test_attn_argument_errors(L):
+    d = LaDims(1, 2, 128, 64, la.LA_BF16)
+    assert _attn(L, None) == la.LA_EINVAL
+    assert _attn(L, LaDims(-1, 2, 128, 64, la.LA_BF16)) == la.LA_EINVAL
+    assert _attn(L, LaDims(1, 2, 128, 64, 7)) == la.LA_EINVAL
+    assert "dtype" in la.la_last_error()
+    assert _attn(L, LaDims(1, 2, 128, 32, la.LA_BF16)) == la.LA_EUNSUPPORTED
+    assert _attn(L, d, q=None) == la.LA_EINVAL
+    assert _attn(L, d, q=FAKE + 2) == la.LA_EINVAL          # misaligned
+    assert _attn(L, d, radius=-1) == la.LA_EINVAL
+    assert _attn(L, d, causal=2) == la.LA_EINVAL
+    assert _attn(L, d, n_global=3) == la.LA_EINVAL           # count without indices
+    assert _attn(L, d, gidx=FAKE, n_global=0) == la.LA_EINVAL
+    assert _attn(L, d, gidx=FAKE, n_global=129) == la.LA_EINVAL
+    bad_dil = (ctypes.c_int32 * 2)(1, 0)
+    assert _attn(L, d, dil=bad_dil) == la.LA_EINVAL
+    assert _attn(L, d, rel_bias=FAKE) == la.LA_EINVAL        # rel_bias without rel_k
+    assert _attn(L, d, ext=LaAttnExt(3, None, None, None, None, 0)) == la.LA_EINVAL
+    assert _attn(L, d, rel_bias=FAKE, ext=LaAttnExt(40, None, None, None, None, 0)) == \
+        la.LA_EUNSUPPORTED
+    assert _attn(L, d, ext=LaAttnExt(0, FAKE, None, None, None, 0)) == la.LA_EINVAL
+    # globals need a large enough workspace
+    assert _attn(L, d, gidx=FAKE, n_global=4) == la.LA_EINVAL
+    need = la.la_attn_workspace_size(d, 4)
+    assert _attn(L, d, gidx=FAKE, n_global=4,
+                 ext=LaAttnExt(0, None, None, None, FAKE, need - 1)) == la.LA_EINVAL
+    assert _attn(L, LaDims(1, 65, 128, 64, la.LA_BF16)) == la.LA_EUNSUPPORTED
+    # empty tensors are a no-op
+    assert _attn(L, LaDims(0, 2, 128, 64, la.LA_BF16), q=None, k=None, v=None, out=None) == la.LA_OK
+
+
+def test_dilated_argument_errors(L):
+    d = LaDims(1, 2, 256, 64, la.LA_BF16)
+    w = (ctypes.c_int32 * 2)(64, 128)
+    r = (ctypes.c_int32 * 2)(1, 2)
+
+    def call(dims=d, w=w, r=r, n=2, causal=1, ext=None, q=FAKE):
+        return L.la_dilated_forward(ctypes.byref(dims), q, FAKE, FAKE, w, r, n, causal, FAKE, None,
+                                    ctypes.byref(ext) if ext is not None else None)
+    assert call(dims=LaDims(1, 2, 256, 64, la.LA_F32)) == la.LA_EUNSUPPORTED
+    assert call(n=0) == la.LA_EINVAL
+    assert call(w=None) == la.LA_EINVAL
+    assert call(r=(ctypes.c_int32 * 2)(1, 0)) == la.LA_EINVAL
+    big = (ctypes.c_int32 * 17)(*([64] * 17))
+    assert call(w=big, r=(ctypes.c_int32 * 17)(*([1] * 17)), n=17) == la.LA_EUNSUPPORTED
+    assert call(causal=3) == la.LA_EINVAL
+    assert call(q=None) == la.LA_EINVAL
+    assert call() == la.LA_EINVAL  # no workspace
+    need = la.la_dilated_workspace_size(d, [64, 128], [1, 2])
+    assert call(ext=LaDilatedExt(None, FAKE, need - 1)) == la.LA_EINVAL
+
+
+def test_workspace_sizes(L):
+    d = LaDims(2, 12, 4096, 64, la.LA_BF16)
+    assert la.la_attn_workspace_size(d, 0) == 0
+    # 64 global rows x 8 key chunks of 512 per (b, h): fp32 O plus fp32 lse,
+    # then one int32 counter per (b, h, 64-row global tile), 256-byte aligned
+    parts = 2 * 12 * 64 * 8
+    assert la.la_attn_workspace_size(d, 64) == parts * 64 * 4 + parts * 4 + 256
+    assert la.la_attn_workspace_size(LaDims(1, 1, 10, 64, la.LA_BF16), 11) == 0  # n_global > N
+    d5 = LaDims(1, 12, 32768, 64, la.LA_BF16)
+    ws = la.la_dilated_workspace_size(d5, [2048, 4096, 8192, 16384, 32768], [1, 2, 4, 6, 12])
+    rows = 12 * (16 * 2048 + 8 * 2048 + 4 * 2048 + 2 * 2731 + 1 * 2731)
+    assert ws >= rows * 65 * 4 and ws < rows * 65 * 4 + 1024

@@ -1,0 +1,299 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Tolerances: max |O_gpu - O_oracle| <= 1e-4 for fp32 inputs and <= 2e-2 for bf16
+inputs (fp32 accumulation); lse within 1e-4 (it never passes through bf16).
+Mask and global-index handling are checked exactly: with Q = 0 every logit is
+0, so exp(lse_i) is the number of allowed keys of row i (the multiplicity sum
+for LongNet); with V = one-hot(j mod 64), O_i[c] * count_i is the number of
+allowed keys congruent to c mod 64.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_long_sequence_amd as la
+from sparse_long_sequence_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+LSE_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    la.lib()
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to64(t):
+    return None if t is None else t.detach().to("cpu", torch.float64).numpy()
+
+
+def gpu_attn(w: W.Workload, inp: W.Inputs, dev, **kw):
+    g = torch.tensor(w.global_idx, dtype=torch.int32, device=dev) if w.global_idx else None
+    d = lambda t: None if t is None else t.to(dev)
+    out, lse = la.la_attn_forward(d(inp.q), d(inp.k), d(inp.v), g, w.radius, w.dilation, w.causal,
+                                  d(inp.rel_bias), qg=d(inp.qg), kg=d(inp.kg), vg=d(inp.vg), **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def gpu_dilated(w: W.Workload, inp: W.Inputs, dev):
+    out, lse = la.la_dilated_forward(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev),
+                                     [p[0] for p in w.pairs], [p[1] for p in w.pairs], w.causal)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_attn(w: W.Workload, inp: W.Inputs, sel=None):
+    return oracle.attn_rows(to64(inp.q), to64(inp.k), to64(inp.v), w.global_idx, w.radius,
+                            w.dilation, w.causal, to64(inp.rel_bias), to64(inp.qg), to64(inp.kg),
+                            to64(inp.vg), sel=sel)
+
+
+def oracle_dilated(w: W.Workload, inp: W.Inputs, sel=None):
+    return oracle.longnet_rows(to64(inp.q), to64(inp.k), to64(inp.v), w.pairs, w.causal, sel=sel)
+
+
+def compare(w, out, lse, o_ref, l_ref, sel=None, tag=""):
+    o = to64(out)
+    l = to64(lse)
+    if sel is not None:
+        s = np.asarray(sel)
+        o = o[s[:, 0], s[:, 1], s[:, 2]]
+        l = l[s[:, 0], s[:, 1], s[:, 2]]
+    err = np.abs(o - o_ref).max()
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(l), fin), f"{tag}: lse finiteness differs"
+    lerr = np.abs(l[fin] - l_ref[fin]).max() if fin.any() else 0.0
+    say(f"{tag}: max|dO| = {err:.3e}  max|dlse| = {lerr:.3e}")
+    assert err <= TOL[w.dtype], f"{tag}: max|dO| {err} > {TOL[w.dtype]}"
+    assert lerr <= LSE_TOL, f"{tag}: max|dlse| {lerr} > {LSE_TOL}"
+
+
+# --------------------------------------------------------------------------
+# small cases: several tiles, ragged tails, every feature; all rows compared
+# --------------------------------------------------------------------------
+SMALL = [
+    # name, N, H, R, dilation, causal, G, rel_k, separate, dtype
+    ("band-ragged", 300, 2, 37, None, False, (), 0, False, "bf16"),
+    ("band-f32", 300, 2, 37, None, False, (), 0, False, "f32"),
+    ("band-R0", 130, 1, 0, None, False, (), 0, False, "bf16"),
+    ("band-R>=N", 100, 2, 150, None, False, (), 0, False, "bf16"),
+    ("band-N1", 1, 1, 3, None, False, (), 0, False, "bf16"),
+    ("band-N<64", 45, 2, 7, None, True, (), 0, False, "f32"),
+    ("global-scatter", 333, 3, 20, None, False, (0, 5, 64, 65, 200, 332), 0, False, "bf16"),
+    ("global-sep-f32", 257, 2, 30, None, False, (1, 2, 3, 100, 256), 0, True, "f32"),
+    ("global-sep-bf16", 257, 2, 30, None, False, tuple(range(70)), 0, True, "bf16"),
+    ("causal-global", 200, 2, 25, None, True, (0, 63, 64, 150), 0, False, "bf16"),
+    ("dilated-mix", 301, 4, 19, (1, 2, 3, 5), False, (), 0, False, "bf16"),
+    ("dilated-causal-global", 301, 4, 19, (1, 2, 3, 5), True, (7, 90, 91), 0, False, "bf16"),
+    ("dilated-global-f32", 150, 2, 9, (3, 1), False, (0, 149), 0, False, "f32"),
+    ("relbias", 400, 3, 21, None, False, tuple(range(30)), 5, False, "bf16"),
+    ("relbias-f32-causal", 260, 2, 40, (1, 2), True, (3, 77, 200), 12, False, "f32"),
+    ("relbias-sep", 300, 2, 33, None, False, (0, 1, 2, 150, 299), 3, True, "bf16"),
+    ("all-global", 96, 1, 2, None, False, tuple(range(96)), 0, False, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_band_global(dev, case):
+    name, N, H, R, dil, causal, G, rk, sep, dt = case
+    w = W.Workload(name, B=2, H=H, N=N, dtype=dt, radius=R, global_idx=G, dilation=dil,
+                   causal=causal, rel_k=rk, separate_global=sep, seed=77)
+    inp = W.make_inputs(w)
+    say(f"case {name}: N={N} H={H} R={R} dil={dil} causal={causal} |G|={len(G)} rel_k={rk} "
+        f"sep={sep} {dt}")
+    out, lse = gpu_attn(w, inp, dev)
+    o_ref, l_ref = oracle_attn(w, inp)
+    compare(w, out, lse, o_ref, l_ref, tag=name)
+
+
+SMALL_DIL = [
+    ("longnet-small", 256, 7, ((16, 1), (32, 2), (64, 4), (96, 6)), True),
+    ("longnet-ragged", 300, 5, ((64, 1), (128, 3), (300, 12)), True),
+    ("longnet-noncausal", 200, 3, ((50, 1), (100, 4)), False),
+    ("longnet-uncovered", 128, 2, ((64, 2),), True),
+    ("longnet-dense", 190, 2, ((190, 1),), True),
+    ("longnet-multitile", 1000, 3, ((400, 1), (1000, 2)), True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_DIL, ids=[c[0] for c in SMALL_DIL])
+def test_small_dilated(dev, case):
+    name, N, H, pairs, causal = case
+    w = W.Workload(name, B=2, H=H, N=N, kind="dilated", causal=causal, pairs=pairs, seed=78)
+    inp = W.make_inputs(w)
+    say(f"case {name}: N={N} H={H} pairs={pairs} causal={causal}")
+    out, lse = gpu_dilated(w, inp, dev)
+    o_ref, l_ref = oracle_dilated(w, inp)
+    compare(w, out, lse, o_ref, l_ref, tag=name)
+
+
+# --------------------------------------------------------------------------
+# exact mask and global-index handling (Q = 0, V = one-hot(j mod 64))
+# --------------------------------------------------------------------------
+def _mask_inputs(w, dev):
+    B, H, N, D = w.B, w.H, w.N, w.D
+    dt = w.torch_dtype
+    q = torch.zeros(B, H, N, D, dtype=dt)
+    k = torch.randn(B, H, N, D, generator=torch.Generator().manual_seed(5)).to(dt)
+    v = torch.zeros(B, H, N, D, dtype=dt)
+    v[:, :, torch.arange(N), torch.arange(N) % D] = 1
+    sep = None
+    if w.separate_global:
+        sep = (torch.zeros_like(q), k.flip(2).contiguous(), v.clone())
+    return W.Inputs(q, k, v, *(sep or (None, None, None)))
+
+
+MASK_CASES = [
+    W.Workload("mask-longformer", B=1, H=2, N=1000, radius=100, global_idx=(0, 1, 2, 500, 999),
+               separate_global=True),
+    W.Workload("mask-dilated-causal", B=1, H=3, N=777, radius=40, dilation=(1, 2, 4), causal=True,
+               global_idx=(3, 400)),
+    W.Workload("mask-f32", B=1, H=1, N=300, dtype="f32", radius=31, global_idx=(150,)),
+    W.Workload("mask-etc", B=1, H=2, N=256 + 700, radius=84, global_idx=tuple(range(256))),
+]
+
+
+def _counts(mask):
+    cnt = mask.sum(axis=1).astype(np.int64)
+    N = mask.shape[1]
+    res = np.stack([mask[:, c::64].sum(axis=1) for c in range(64)], axis=1).astype(np.int64)
+    return cnt, res
+
+
+@pytest.mark.parametrize("w", MASK_CASES, ids=[w.name for w in MASK_CASES])
+def test_mask_exact(dev, w):
+    say(f"case {w.name}")
+    inp = _mask_inputs(w, dev)
+    out, lse = gpu_attn(w, inp, dev)
+    o = to64(out)
+    l = to64(lse)
+    for h in range(w.H):
+        d = w.dilation[h] if w.dilation else 1
+        m = oracle.mask_rows(w.N, w.global_idx, w.radius, d, w.causal)
+        cnt, res = _counts(m)
+        got_cnt = np.rint(np.exp(l[0, h])).astype(np.int64)
+        assert np.array_equal(got_cnt, cnt), f"{w.name} h={h}: key counts differ"
+        got_res = np.rint(o[0, h] * cnt[:, None]).astype(np.int64)
+        assert np.array_equal(got_res, res), f"{w.name} h={h}: allowed key sets differ"
+
+
+def test_mask_exact_longnet(dev):
+    w = W.Workload("mask-longnet", B=1, H=6, N=700, kind="dilated", causal=True,
+                   pairs=((64, 1), (128, 2), (256, 4), (700, 6)))
+    inp = _mask_inputs(w, dev)
+    out, lse = gpu_dilated(w, inp, dev)
+    o, l = to64(out), to64(lse)
+    for h in range(w.H):
+        m = oracle.longnet_mult_rows(w.N, h, w.pairs, True)
+        cnt, res = _counts(m)
+        assert np.array_equal(np.rint(np.exp(l[0, h])).astype(np.int64), cnt), f"h={h}"
+        assert np.array_equal(np.rint(o[0, h] * cnt[:, None]).astype(np.int64), res), f"h={h}"
+
+
+# --------------------------------------------------------------------------
+# the five workloads at full size, in the launch configuration the bench times
+# --------------------------------------------------------------------------
+def _sel_rows(w, n):
+    must = set()
+    for t in range(0, w.N, 64):
+        must |= {t - 1, t, t + 1}
+    must = sorted(i for i in must if 0 <= i < w.N)[:64]
+    rows = W.sample_rows(w, n, seed=11, must_include=must).numpy()
+    if w.global_idx:  # every global row of two heads (the separate pass)
+        g = np.array(w.global_idx)
+        for (b, h) in ((0, 0), (w.B - 1, w.H - 1)):
+            rows = np.concatenate([rows, np.stack([np.full_like(g, b), np.full_like(g, h), g], 1)])
+    return rows.astype(np.int32)
+
+
+@pytest.mark.parametrize("w", W.ORDERED, ids=[w.name for w in W.ORDERED])
+def test_workload_parity(dev, w):
+    say(f"workload {w.name}: B={w.B} H={w.H} N={w.N} {w.dtype}")
+    inp = W.make_inputs(w)
+    if w.kind == "dilated":
+        out, lse = gpu_dilated(w, inp, dev)
+        sel = _sel_rows(w, 1500)
+        o_ref, l_ref = oracle_dilated(w, inp, sel)
+        compare(w, out, lse, o_ref, l_ref, sel, tag=w.name)
+        return
+    out, lse = gpu_attn(w, inp, dev)
+    if w.B * w.H * w.N <= 1 << 14:
+        o_ref, l_ref = oracle_attn(w, inp)
+        compare(w, out, lse, o_ref, l_ref, tag=w.name)
+    else:
+        sel = _sel_rows(w, 3000)
+        o_ref, l_ref = oracle_attn(w, inp, sel)
+        compare(w, out, lse, o_ref, l_ref, sel, tag=w.name)
+
+
+# --------------------------------------------------------------------------
+# determinism, streams, graph capture
+# --------------------------------------------------------------------------
+def test_deterministic(dev):
+    w = W.LONGFORMER_BASE
+    inp = W.make_inputs(w)
+    a = [gpu_attn(w, inp, dev) for _ in range(3)]
+    for o, l in a[1:]:
+        assert torch.equal(o, a[0][0]) and torch.equal(l, a[0][1])
+    w5 = W.Workload("det-longnet", B=1, H=4, N=4096, kind="dilated", causal=True,
+                    pairs=((512, 1), (1024, 2), (4096, 8)))
+    inp5 = W.make_inputs(w5)
+    b = [gpu_dilated(w5, inp5, dev) for _ in range(3)]
+    for o, l in b[1:]:
+        assert torch.equal(o, b[0][0]) and torch.equal(l, b[0][1])
+
+
+def test_nondefault_stream(dev):
+    w = W.Workload("stream", B=1, H=2, N=1024, radius=64, global_idx=(0, 10), seed=3)
+    inp = W.make_inputs(w)
+    ref, _ = gpu_attn(w, inp, dev)
+    s = torch.cuda.Stream()
+    g = torch.tensor(w.global_idx, dtype=torch.int32, device=dev)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        out, _ = la.la_attn_forward(q, k, v, g, w.radius, stream=s)
+    s.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_graph_capture(dev):
+    w = W.Workload("graph", B=1, H=2, N=2048, radius=128, global_idx=tuple(range(16)), seed=4)
+    inp = W.make_inputs(w)
+    g = torch.tensor(w.global_idx, dtype=torch.int32, device=dev)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    ref, ref_lse = la.la_attn_forward(q, k, v, g, w.radius)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = torch.zeros(la.la_attn_workspace_size(la.LaDims(1, 2, 2048, 64, la.LA_BF16), 16),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            la.la_attn_forward(q, k, v, g, w.radius, out=out, lse=lse, workspace=ws, stream=s)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        lse.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(lse, ref_lse), f"replay {rep}"
+        _ = (q.float() * 2).sum().item()  # unrelated eager work between replays
