@@ -42,8 +42,7 @@
  *     denominator, lse_i = ln sum_j c_ij exp(s_ij).
  *   - Ownership: the caller owns every buffer. The library allocates nothing,
  *     keeps no pointer after returning, never writes its inputs, and fully
- *     overwrites out and lse. out must not alias an input. Workspace rules
- *     are given with each call's extras below.
+ *     overwrites out, lse and the workspace. out must not alias an input.
  *   - All work is enqueued on `stream` (0 = the null stream); the call returns
  *     without synchronising and issues no device-to-host copy.
  *   - Errors: host-detectable argument errors return LA_EINVAL and enqueue
@@ -86,10 +85,8 @@ typedef struct {
    * keep q, k, v (for their global columns too). */
   const void *qg, *kg, *vg;
   /* Device scratch of at least la_attn_workspace_size() bytes, 256-byte aligned;
-   * required when n_global > 0. Its last block holds completion counters: the
-   * workspace must be zero-filled once before its first use (e.g. at
-   * allocation); every call returns the counters to zero, so later calls need
-   * no clearing. Calls that share a workspace must not overlap in time. */
+   * required when n_global > 0. Its contents need no initialisation and are
+   * overwritten. Calls that share a workspace must not overlap in time. */
   void *workspace;
   size_t workspace_bytes;
 } la_attn_ext;

@@ -157,9 +157,8 @@ def _workspace(nbytes: int, device, given: Optional[torch.Tensor]) -> Optional[t
         if given.numel() * given.element_size() < nbytes or not given.is_cuda:
             raise LaError(LA_EINVAL, "workspace tensor too small")
         return given
-    # torch's caching allocator returns 512-byte aligned blocks; zero-filled
-    # once, as la_attn_forward's completion counters require
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def la_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

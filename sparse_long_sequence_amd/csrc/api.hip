@@ -46,20 +46,17 @@ bool is_empty(const la_dims* d) { return d->B == 0 || d->H == 0 || d->N == 0; }
 
 int32_t n_chunks_of(int32_t N) { return (N + kChunk - 1) / kChunk; }
 
-// Workspace of la_attn_forward: global-row partials (fp32 O, fp32 lse), then
-// one int32 counter per (batch, head, 64-row global tile).
+// Workspace of la_attn_forward: global-row partials, fp32 O then fp32 lse.
 struct AttnWs {
-  size_t o_off, lse_off, cnt_off, bytes;
+  size_t o_off, lse_off, bytes;
 };
 
 AttnWs attn_ws_layout(const la_dims* d, int32_t n_global) {
-  AttnWs w = {0, 0, 0, 0};
+  AttnWs w = {0, 0, 0};
   if (n_global <= 0) return w;
   const size_t parts = (size_t)d->B * d->H * n_global * n_chunks_of(d->N);
-  const size_t tiles = (size_t)d->B * d->H * ((n_global + kQTile - 1) / kQTile);
   w.lse_off = align_up(parts * kDHead * sizeof(float));
-  w.cnt_off = w.lse_off + align_up(parts * sizeof(float));
-  w.bytes = w.cnt_off + align_up(tiles * sizeof(int32_t));
+  w.bytes = w.lse_off + align_up(parts * sizeof(float));
   return w;
 }
 
@@ -200,7 +197,6 @@ la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, con
     char* base = reinterpret_cast<char*>(ext->workspace);
     a.ws_o = reinterpret_cast<float*>(base + lay.o_off);
     a.ws_lse = reinterpret_cast<float*>(base + lay.lse_off);
-    a.ws_cnt = reinterpret_cast<int32_t*>(base + lay.cnt_off);
   }
   a.chunk_len = kChunk;
   a.n_chunks = n_chunks_of(dims->N);

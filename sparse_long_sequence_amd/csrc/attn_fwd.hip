@@ -3,8 +3,8 @@
 // One launch holds two kinds of workgroups:
 //   * global-row workgroups (first in the grid), one per (batch, head, 64
 //     global rows, key chunk): each global row against a chunk of all keys,
-//     written as a partial (normalised O, lse) to the workspace; the last
-//     workgroup of a row tile to finish merges the chunk partials;
+//     written as a partial (normalised O, lse) to the workspace, merged by a
+//     second, small launch;
 //   * band workgroups, one per 64-row query tile of one residue class of one
 //     (batch, head): the sliding-window key tiles (strided by the head's
 //     dilation), then the global-column tiles (keys of G outside the window).
@@ -27,14 +27,18 @@ __host__ __device__ inline int32_t band_tiles_of_head(int32_t N, int32_t d) {
   return t;
 }
 
-// Number of entries of the sorted array g[0..n) that are < p.
-__device__ __forceinline__ int32_t lower_bound(const int32_t* g, int32_t n, int32_t p) {
-  int32_t lo = 0, hi = n;
-  while (lo < hi) {
-    int32_t mid = (lo + hi) >> 1;
-    if (g[mid] < p) lo = mid + 1; else hi = mid;
+// Entries of the sorted array g[0..n) below p0 and below p1, counted by the
+// whole wave at once (one round of loads instead of a chain of dependent ones).
+__device__ __forceinline__ void count_below(const int32_t* g, int32_t n, int32_t p0, int32_t p1,
+                                            int32_t lane, int32_t& c0, int32_t& c1) {
+  c0 = 0;
+  c1 = 0;
+  for (int32_t x0 = 0; x0 < n; x0 += 64) {
+    const int32_t x = x0 + lane;
+    const int32_t v = x < n ? g[x] : 0x7fffffff;
+    c0 += __builtin_popcountll(__ballot(v < p0));
+    c1 += __builtin_popcountll(__ballot(v < p1));
   }
-  return lo;
 }
 
 template <typename T>
@@ -45,127 +49,149 @@ template <>
 struct OutT<float> { typedef float type; };
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
+__device__ __forceinline__ void load_bias_table(typename TileTraits<T>::Smem& sm, const AttnArgs& a,
+                                                int32_t h, int32_t tid) {
+  if (a.rel_bias && tid < 2 * a.rel_k + 1)
+    sm.bias[tid] = a.rel_bias[h * (2 * a.rel_k + 1) + tid] * kInvScale;
+}
+
+// ---------------------------------------------------------------------------
+// band workgroup: 64 query rows of one residue class (positions c + d*t)
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileTraits<T>::Smem& sm,
+                                               int32_t bw) {
   using TT = TileTraits<T>;
   using O = typename OutT<T>::type;
-  __shared__ typename TT::Smem sm;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t wg = (int32_t)blockIdx.x;
   const int32_t N = a.N;
   const size_t head_elems = (size_t)N * kD;
+  const int32_t bh = bw / a.band_tiles_per_head;
+  int32_t tile = bw % a.band_tiles_per_head;
+  const int32_t h = bh % a.H;
+  const int32_t d = a.dil[h];
+  int32_t c = 0, n_c = 0;
+  for (; c < d && c < N; ++c) {
+    n_c = (N - c + d - 1) / d;
+    const int32_t tc = (n_c + kTQ - 1) / kTQ;
+    if (tile < tc) break;
+    tile -= tc;
+  }
+  if (c >= d || c >= N) return;  // padding workgroup of a less-dilated head
+  const int32_t t0 = tile * kTQ;
+  const int32_t qcount = min(kTQ, n_c - t0);
+  const int32_t qbase = c + d * t0;
+  const int32_t i_lo = qbase, i_hi = qbase + d * (qcount - 1);
 
-  if (wg >= a.n_glob_wg) {
-    // ---------------- band workgroup ----------------
-    const int32_t bw = wg - a.n_glob_wg;
-    const int32_t bh = bw / a.band_tiles_per_head;
-    int32_t tile = bw % a.band_tiles_per_head;
-    const int32_t h = bh % a.H;
-    const int32_t d = a.dil[h];
-    int32_t c = 0, n_c = 0;
-    for (; c < d && c < N; ++c) {
-      n_c = (N - c + d - 1) / d;
-      const int32_t tc = (n_c + kTQ - 1) / kTQ;
-      if (tile < tc) break;
-      tile -= tc;
+  // Global rows inside this tile: G[g0, g1) holds every global position in [i_lo, i_hi].
+  int32_t g0 = 0, g1 = 0;
+  if (a.n_global > 0) {
+    count_below(a.gidx, a.n_global, i_lo, i_hi + 1, lane, g0, g1);
+    // a tile made only of global rows belongs to the global-row pass
+    if (d == 1 && g1 - g0 == qcount) return;
+  }
+  load_bias_table<T>(sm, a, h, tid);
+
+  const T* qb = reinterpret_cast<const T*>(a.q) + bh * head_elems;
+  const T* kb = reinterpret_cast<const T*>(a.k) + bh * head_elems;
+  const T* vb = reinterpret_cast<const T*>(a.v) + bh * head_elems;
+  const int32_t qi = 16 * wave + (lane & 15);
+  const int32_t qpos = qbase + d * min(qi, qcount - 1);
+  typename TT::Wave w;
+  TT::load_q(w, qb, qpos, lane);
+
+  // window keys in strided index space [lo, hi]
+  const int32_t R = a.radius;
+  const int32_t lo = max(0, t0 - R);
+  const int32_t hi = a.causal ? (t0 + qcount - 1) : min(n_c - 1, t0 + qcount - 1 + R);
+  const int32_t n_band = (hi - lo + 1 + kTK - 1) / kTK;
+  const bool want_bias = a.rel_bias != nullptr;
+  GlobInfo gi = {kGlobNone, a.gidx, a.n_global};
+  if (want_bias && a.n_global > 0) {
+    if (hi - lo + 1 <= 32 * kGMaskWords) {
+      build_gmask<T>(sm, a.gidx, a.n_global, c + d * lo, d, hi - lo + 1, tid);
+      gi.mode = kGlobBitmap;
+    } else {
+      gi.mode = kGlobSearch;
     }
-    if (c >= d || c >= N) return;  // padding workgroup of a less-dilated head
-    const int32_t t0 = tile * kTQ;
-    const int32_t qcount = min(kTQ, n_c - t0);
-    const int32_t qbase = c + d * t0;
-    // A tile made only of global rows belongs to the global-row pass.
-    if (a.n_global > 0 && d == 1) {
-      const int32_t ng = lower_bound(a.gidx, a.n_global, qbase + qcount) -
-                         lower_bound(a.gidx, a.n_global, qbase);
-      if (ng == qcount) return;
-    }
-    if (a.rel_bias && tid < 2 * a.rel_k + 1) sm.bias[tid] = a.rel_bias[h * (2 * a.rel_k + 1) + tid];
+  }
+  const BiasRule br = {want_bias ? sm.bias : nullptr, a.rel_k, 0};
 
-    const T* qb = reinterpret_cast<const T*>(a.q) + bh * head_elems;
-    const T* kb = reinterpret_cast<const T*>(a.k) + bh * head_elems;
-    const T* vb = reinterpret_cast<const T*>(a.v) + bh * head_elems;
-    const RowMap qm = {nullptr, qbase, d, qcount};
-    typename TT::Wave w;
-    TT::load_q(w, qb, qm, wave, lane);
-    const int32_t qi = 16 * wave + (lane & 15);
-    const int32_t qpos = qbase + d * qi;
+  auto band_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+    const int32_t u0 = lo + n * kTK;
+    const int32_t kcount = min(kTK, hi - u0 + 1);
+    kt = {nullptr, c + d * u0, d, kcount, u0 - lo};
+    // strided index difference key - query = kj - qi - (t0 - u0)
+    const int32_t dmin = u0 - t0 - (qcount - 1);
+    const int32_t dmax = u0 + kcount - 1 - t0;
+    const int32_t hib = a.causal ? 0 : R;
+    const bool full = kcount == kTK && dmin >= -R && dmax <= hib;
+    mr = {kRange, full ? 0 : 1, 0, t0 - u0, -R, hib, 0, 0, 1};
+  };
+  run_tiles<T, false>(sm, w, kb, vb, n_band, band_desc, br, gi, qi, qpos, a.scale_log2);
 
-    // window keys in strided index space [lo, hi]
-    const int32_t R = a.radius;
-    const int32_t lo = max(0, t0 - R);
-    const int32_t hi = a.causal ? (t0 + qcount - 1) : min(n_c - 1, t0 + qcount - 1 + R);
-    const int32_t n_band = (hi - lo + 1 + kTK - 1) / kTK;
-
+  if (a.n_global > 0) {
     // global-column tiles that can hold an allowed pair (bit set = keep)
     const int32_t n_gt = (a.n_global + kTK - 1) / kTK;
     uint64_t keep = ~0ull;
-    const int32_t i_lo = qbase, i_hi = qbase + d * (qcount - 1);
     if (n_gt <= 64) {
       keep = 0;
       for (int32_t gt = 0; gt < n_gt; ++gt) {
         const int32_t cnt = min(kTK, a.n_global - gt * kTK);
-        const int32_t g_lo = a.gidx[gt * kTK], g_hi = a.gidx[gt * kTK + cnt - 1];
+        const int32_t gl = a.gidx[gt * kTK], gh = a.gidx[gt * kTK + cnt - 1];
         bool all_in_band = false;
-        if (d == 1) {
-          all_in_band = a.causal ? (g_lo >= i_hi - R && g_hi <= i_lo)
-                                 : (g_lo >= i_hi - R && g_hi <= i_lo + R);
-        }
-        const bool none_allowed_causal = a.causal && g_lo > i_hi;
-        if (!all_in_band && !none_allowed_causal) keep |= (1ull << gt);
+        if (d == 1)
+          all_in_band = a.causal ? (gl >= i_hi - R && gh <= i_lo) : (gl >= i_hi - R && gh <= i_lo + R);
+        const bool none_causal = a.causal && gl > i_hi;
+        if (!all_in_band && !none_causal) keep |= (1ull << gt);
       }
     }
     const int32_t n_glob = n_gt <= 64 ? __builtin_popcountll(keep) : n_gt;
-
-    auto desc = [&](int32_t n, RowMap& km, MaskRule& mr) {
-      if (n < n_band) {
-        const int32_t u0 = lo + n * kTK;
-        const int32_t kcount = min(kTK, hi - u0 + 1);
-        km = {nullptr, c + d * u0, d, kcount};
-        const int32_t dmin = u0 - t0 - (qcount - 1);
-        const int32_t dmax = u0 + kcount - 1 - t0;
-        const bool full = kcount == kTK && dmin >= -R && dmax <= (a.causal ? 0 : R);
-        mr = {kBand, full ? 0 : 1, a.causal, R, d, t0 - u0};
-      } else {
-        int32_t x = n - n_band, gt = x;
-        if (n_gt <= 64) {
-          uint64_t m = keep;
-          for (int32_t s = 0; s < x; ++s) m &= m - 1;
-          gt = __builtin_ctzll(m);
-        }
-        const int32_t kcount = min(kTK, a.n_global - gt * kTK);
-        km = {a.gidx + gt * kTK, 0, 1, kcount};
-        const int32_t g_lo = a.gidx[gt * kTK], g_hi = a.gidx[gt * kTK + kcount - 1];
-        const bool outside = (g_hi < i_lo - d * R) || (g_lo > i_hi + d * R);
-        const bool causal_ok = !a.causal || g_hi <= i_lo;
-        const bool full = kcount == kTK && outside && causal_ok;
-        mr = {kGlobCol, full ? 0 : 1, a.causal, R, d, 0};
+    auto glob_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+      int32_t gt = n;
+      if (n_gt <= 64) {
+        uint64_t m = keep;
+        for (int32_t s = 0; s < n; ++s) m &= m - 1;
+        gt = __builtin_ctzll(m);
       }
+      const int32_t kcount = min(kTK, a.n_global - gt * kTK);
+      kt = {a.gidx + gt * kTK, 0, 1, kcount, 0};
+      const int32_t gl = a.gidx[gt * kTK], gh = a.gidx[gt * kTK + kcount - 1];
+      const bool outside = (gh < i_lo - d * R) || (gl > i_hi + d * R);
+      const bool causal_ok = !a.causal || gh <= i_lo;
+      const bool full = kcount == kTK && outside && causal_ok;
+      mr = {kGlobCol, full ? 0 : 1, 0, 0, 0, 0, a.causal, R, d};
     };
-    const BiasRule br = {a.rel_bias ? sm.bias : nullptr, a.rel_k, 0};
-    const bool need_glob = a.rel_bias != nullptr && a.n_global > 0;
-    run_tiles<T>(sm, w, kb, vb, n_band + n_glob, desc, br, need_glob, a.gidx, a.n_global, qi, qpos,
-                 a.scale_log2);
-
-    // epilogue: rows outside G (the global-row pass owns the rest)
-    const float l_tot = wave_sum_xor16_32(w.l);
-    if (qi < qcount) {
-      const bool is_g = a.n_global > 0 && sorted_contains(a.gidx, a.n_global, qpos);
-      if (!is_g) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        O* dst = reinterpret_cast<O*>(a.out) + bh * head_elems + (size_t)qpos * kD;
-        TT::store_row(dst, w.o, inv, lane);
-        if (a.lse && (lane >> 4) == 0)
-          a.lse[(size_t)bh * N + qpos] = l_tot > 0.f ? (w.m + __log2f(l_tot)) * kLn2 : kNegInf;
-      }
-    }
-    return;
+    const GlobInfo gall = {want_bias ? kGlobAll : kGlobNone, a.gidx, a.n_global};
+    run_tiles<T, true>(sm, w, kb, vb, n_glob, glob_desc, br, gall, qi, qpos, a.scale_log2);
   }
 
-  // ---------------- global-row workgroup ----------------
-  // global-row workgroups come first in the grid so their merges are not the tail
-  const int32_t gw = wg;
+  // epilogue: rows outside G (the global-row pass owns the rest)
+  const float l_tot = wave_sum_xor16_32(w.l);
+  if (qi < qcount) {
+    const bool is_g = g1 > g0 && sorted_contains(a.gidx + g0, g1 - g0, qpos);
+    if (!is_g) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      O* dst = reinterpret_cast<O*>(a.out) + bh * head_elems + (size_t)qpos * kD;
+      TT::store_row(dst, w.o, inv, lane);
+      if (a.lse && (lane >> 4) == 0)
+        a.lse[(size_t)bh * N + qpos] = l_tot > 0.f ? (w.m + __log2f(l_tot)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// global-row workgroup: 64 global rows against one chunk of keys
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void global_workgroup(const AttnArgs& a,
+                                                 typename TileTraits<T>::Smem& sm, int32_t gw) {
+  using TT = TileTraits<T>;
+  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t N = a.N;
+  const size_t head_elems = (size_t)N * kD;
   const int32_t per_bh = a.n_gq_tiles * a.n_chunks;
   const int32_t bh = gw / per_bh;
-  if (bh >= a.B * a.H) return;
   const int32_t rem = gw % per_bh;
   const int32_t gq = rem / a.n_chunks, chunk = rem % a.n_chunks;
   const int32_t h = bh % a.H;
@@ -176,27 +202,31 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   int32_t j1 = min(N, j0 + a.chunk_len);
   if (a.causal) j1 = min(j1, i_max + 1);
   const int32_t n_tiles = j1 > j0 ? (j1 - j0 + kTK - 1) / kTK : 0;
-  if (a.rel_bias && tid < 2 * a.rel_k + 1) sm.bias[tid] = a.rel_bias[h * (2 * a.rel_k + 1) + tid];
+  load_bias_table<T>(sm, a, h, tid);
+  const bool want_bias = a.rel_bias != nullptr;
+  GlobInfo gi = {kGlobNone, a.gidx, a.n_global};
+  if (want_bias && n_tiles > 0) {
+    build_gmask<T>(sm, a.gidx, a.n_global, j0, 1, j1 - j0, tid);  // j1 - j0 <= chunk_len
+    gi.mode = kGlobBitmap;
+  }
 
   const T* qb = reinterpret_cast<const T*>(a.qg) + bh * head_elems;
   const T* kb = reinterpret_cast<const T*>(a.kg) + bh * head_elems;
   const T* vb = reinterpret_cast<const T*>(a.vg) + bh * head_elems;
-  const RowMap qm = {qidx, 0, 1, qcount};
-  typename TT::Wave w;
-  TT::load_q(w, qb, qm, wave, lane);
   const int32_t qi = 16 * wave + (lane & 15);
-  const int32_t qpos = qi < qcount ? qidx[qi] : i_max;
-  auto desc = [&](int32_t n, RowMap& km, MaskRule& mr) {
+  const int32_t qpos = qidx[min(qi, qcount - 1)];
+  typename TT::Wave w;
+  TT::load_q(w, qb, qpos, lane);
+  auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = j0 + n * kTK;
     const int32_t kcount = min(kTK, j1 - u0);
-    km = {nullptr, u0, 1, kcount};
+    kt = {nullptr, u0, 1, kcount, u0 - j0};
+    // key position u0 + kj <= qpos  <=>  kj - (qpos - u0) <= 0
     const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= i_min);
-    mr = {kAll, full ? 0 : 1, a.causal, 0, 1, 0};
+    mr = {kRange, full ? 0 : 1, 1, -u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
   };
-  const BiasRule br = {a.rel_bias ? sm.bias : nullptr, a.rel_k, 1};
-  const bool need_glob = a.rel_bias != nullptr;
-  run_tiles<T>(sm, w, kb, vb, n_tiles, desc, br, need_glob, a.gidx, a.n_global, qi, qpos,
-               a.scale_log2);
+  const BiasRule br = {want_bias ? sm.bias : nullptr, a.rel_k, 1};
+  run_tiles<T, false>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, a.scale_log2);
   const float l_tot = wave_sum_xor16_32(w.l);
   if (qi < qcount) {
     const size_t prow = ((size_t)bh * a.n_global + gq * kTQ + qi) * a.n_chunks + chunk;
@@ -204,48 +234,51 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
     TileTraits<float>::store_row(a.ws_o + prow * kD, w.o, inv, lane);
     if ((lane >> 4) == 0) a.ws_lse[prow] = l_tot > 0.f ? (w.m + __log2f(l_tot)) * kLn2 : kNegInf;
   }
+}
 
-  // The last of the n_chunks workgroups of this row tile to finish merges the
-  // partials: lse = ln sum_c e^{lse_c}, O = sum_c e^{lse_c - lse} O_c, in chunk
-  // order (so the result does not depend on which workgroup merges). It then
-  // returns the tile's counter to zero for the next call.
-  __shared__ int32_t s_last;
-  __threadfence();  // publish this workgroup's partial before counting it
-  __syncthreads();
-  if (tid == 0) {
-    const int32_t prev = atomicAdd(&a.ws_cnt[bh * a.n_gq_tiles + gq], 1);
-    s_last = prev == a.n_chunks - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();  // see every other workgroup's partial
-  // 256 threads: 4 rows at a time, thread = d
-  for (int32_t r = tid >> 6; r < qcount; r += kThreads / 64) {
-    const int32_t dd = tid & 63;
-    const size_t p0 = ((size_t)bh * a.n_global + gq * kTQ + r) * a.n_chunks;
-    float L = kNegInf;
-    for (int32_t c = 0; c < a.n_chunks; ++c) L = fmaxf(L, a.ws_lse[p0 + c]);
-    float acc = 0.f, S = 0.f;
-    if (L != kNegInf) {
-      for (int32_t c = 0; c < a.n_chunks; ++c) {
-        const float lc = a.ws_lse[p0 + c];
-        if (lc == kNegInf) continue;
-        const float wgt = __expf(lc - L);
-        S += wgt;
-        acc += wgt * a.ws_o[(p0 + c) * kD + dd];
-      }
+template <typename T>
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
+  __shared__ typename TileTraits<T>::Smem sm;
+  const int32_t wg = (int32_t)blockIdx.x;
+  // global-row workgroups come first in the grid so they are not the tail
+  if (wg < a.n_glob_wg) global_workgroup<T>(a, sm, wg);
+  else band_workgroup<T>(a, sm, wg - a.n_glob_wg);
+}
+
+// Merge the key-chunk partials of every global row: lse = ln sum_c e^{lse_c},
+// O = sum_c e^{lse_c - lse} O_c, in chunk order. A separate launch: merging
+// inside the first one would need device-scope fences, which on a multi-XCD
+// part write back and invalidate a whole L2 each time.
+// 256 threads = 4 rows, thread = d.
+template <typename T>
+__global__ __launch_bounds__(256) void global_merge_kernel(AttnArgs a) {
+  using O = typename OutT<T>::type;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // over B*H*n_global
+  if (row >= (int64_t)a.B * a.H * a.n_global) return;
+  const int32_t bh = (int32_t)(row / a.n_global), r = (int32_t)(row % a.n_global);
+  const int32_t dd = threadIdx.x & 63;
+  const size_t p0 = (size_t)row * a.n_chunks;
+  float L = kNegInf;
+  for (int32_t c = 0; c < a.n_chunks; ++c) L = fmaxf(L, a.ws_lse[p0 + c]);
+  float acc = 0.f, S = 0.f;
+  if (L != kNegInf) {
+    for (int32_t c = 0; c < a.n_chunks; ++c) {
+      const float lc = a.ws_lse[p0 + c];
+      if (lc == kNegInf) continue;
+      const float wgt = __expf(lc - L);
+      S += wgt;
+      acc += wgt * a.ws_o[(p0 + c) * kD + dd];
     }
-    const int32_t pos = qidx[r];
-    O* dst = reinterpret_cast<O*>(a.out) + bh * head_elems + (size_t)pos * kD;
-    const float val = S > 0.f ? acc / S : 0.f;
-    if constexpr (sizeof(O) == 2) {
-      reinterpret_cast<uint16_t*>(dst)[dd] = (uint16_t)f32_to_bf16_bits(val);
-    } else {
-      dst[dd] = val;
-    }
-    if (a.lse && dd == 0) a.lse[(size_t)bh * N + pos] = S > 0.f ? L + __logf(S) : kNegInf;
   }
-  if (tid == 0) atomicExch(&a.ws_cnt[bh * a.n_gq_tiles + gq], 0);
+  const int32_t pos = a.gidx[r];
+  O* dst = reinterpret_cast<O*>(a.out) + ((size_t)bh * a.N + pos) * kD;
+  const float val = S > 0.f ? acc / S : 0.f;
+  if constexpr (sizeof(O) == 2) {
+    reinterpret_cast<__bf16*>(dst)[dd] = (__bf16)val;
+  } else {
+    dst[dd] = val;
+  }
+  if (a.lse && dd == 0) a.lse[(size_t)bh * a.N + pos] = S > 0.f ? L + __logf(S) : kNegInf;
 }
 
 hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
@@ -255,6 +288,13 @@ hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
     hipLaunchKernelGGL(attn_fwd_kernel<bf16>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(attn_fwd_kernel<float>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_global == 0) return e;
+  const uint32_t blocks = (uint32_t)(((int64_t)a.B * a.H * a.n_global + 3) / 4);
+  if (dtype == 1)
+    hipLaunchKernelGGL(global_merge_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(global_merge_kernel<float>, dim3(blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -45,23 +45,24 @@ __global__ __launch_bounds__(kThreads) void dilated_pair_kernel(DilArgs a) {
   const bf16* kb = reinterpret_cast<const bf16*>(a.k) + bh * head_elems;
   const bf16* vb = reinterpret_cast<const bf16*>(a.v) + bh * head_elems;
   const int32_t base = sigma + s;
-  const RowMap qm = {nullptr, base + r * t0, r, qcount};
-  TT::Wave wv;
-  TT::load_q(wv, qb, qm, wave, lane);
   const int32_t qi = 16 * wave + (lane & 15);
-  const int32_t qpos = base + r * (t0 + qi);
+  const int32_t qpos = base + r * (t0 + min(qi, qcount - 1));
+  TT::Wave wv;
+  TT::load_q(wv, qb, qpos, lane);
   const int32_t hi = a.causal ? t0 + qcount - 1 : n_rows - 1;
   const int32_t n_tiles = (hi + kTK) / kTK;
 
-  auto desc = [&](int32_t n, RowMap& kmo, MaskRule& mro) {
+  auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = n * kTK;
     const int32_t kcount = min(kTK, hi - u0 + 1);
-    kmo = {nullptr, base + r * u0, r, kcount};
+    kt = {nullptr, base + r * u0, r, kcount, 0};
+    // gathered index difference key - query = kj - qi - (t0 - u0) <= 0 when causal
     const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= t0);
-    mro = {kSeg, full ? 0 : 1, a.causal, 0, r, t0 - u0};
+    mr = {kRange, full ? 0 : 1, 0, t0 - u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
   };
   const BiasRule br = {nullptr, 0, 0};
-  run_tiles<bf16>(sm, wv, kb, vb, n_tiles, desc, br, false, nullptr, 0, qi, qpos, a.scale_log2);
+  const GlobInfo gi = {kGlobNone, nullptr, 0};
+  run_tiles<bf16, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, a.scale_log2);
   const float l_tot = wave_sum_xor16_32(wv.l);
   if (qi < qcount) {
     const int64_t prow = a.row_off[k] + ((int64_t)bh * nseg + seg) * a.seg_rows[k] + t0 + qi;
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256) void dilated_combine_kernel(DilArgs a) {
     }
   }
   const float val = S > 0.f ? acc / S : 0.f;
-  reinterpret_cast<uint16_t*>(a.out)[row * kD + dd] = (uint16_t)f32_to_bf16_bits(val);
+  reinterpret_cast<__bf16*>(a.out)[row * kD + dd] = (__bf16)val;
   if (a.lse && dd == 0) a.lse[row] = S > 0.f ? L + __logf(S) : kNegInf;
 }
 

@@ -32,7 +32,7 @@ namespace la {
 
 typedef __bf16 bf16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
@@ -41,9 +41,10 @@ constexpr int kTQ = 64;       // query rows per workgroup
 constexpr int kTK = 64;       // keys per key tile
 constexpr int kD = 64;        // head dimension
 constexpr int kThreads = 256; // 4 waves
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kInvScale = 8.0f;  // sqrt(kD): the bias table is stored in q.k units
+constexpr int kGMaskWords = 256;   // LDS bitmap of global positions: 8192 key rows
 
 // LDS row pitches (elements). Padding keeps the MFMA operand reads free of
 // most bank conflicts.
@@ -51,45 +52,12 @@ constexpr int kKPitchBf16 = 72;  // K tile [key][d], 144 B rows
 constexpr int kVPitchBf16 = 68;  // V^T tile [d][key], 136 B rows
 constexpr int kPitchF32 = 68;    // fp32 K and V tiles [key][d], 272 B rows
 
-// A sequence of rows of one [N, D] matrix: either positions base + stride*x
-// for x < count, or positions idx[x] for x < count (a gather).
-struct RowMap {
-  const int32_t* idx;  // non-null for a gather
-  int32_t base;
-  int32_t stride;
-  int32_t count;
-  __device__ __forceinline__ int32_t pos(int32_t x) const {
-    return idx ? idx[x] : base + stride * x;
-  }
-};
-
-// Per-element mask/bias rules of one key tile (positions are sequence
-// positions of the query row i and key row j).
-enum TileKind : int32_t {
-  kBand = 0,    // sliding-window tile in strided index space
-  kGlobCol = 1, // global-column tile: keys are global tokens outside the band
-  kAll = 2,     // plain range of keys (global rows): causal only
-  kSeg = 3,     // LongNet gathered segment: causal in gathered index
-};
-
-struct MaskRule {
-  int32_t kind;
-  int32_t need_mask;  // 0: every (query, key) of the tile is allowed
-  int32_t causal;
-  int32_t radius;     // band half-width in dilation steps
-  int32_t dil;        // dilation of the head
-  int32_t qoff;       // kBand / kSeg: strided index of query row 0 minus that of key row 0
-};
-
-// fp32 -> bf16 with round-to-nearest-even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// fp32 -> bf16, round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float wave_max_xor16_32(float x) {
@@ -115,38 +83,55 @@ __device__ __forceinline__ bool sorted_contains(const int32_t* g, int32_t n, int
   return false;
 }
 
-// Is (query position i, key position j) allowed by the rule? kq/kk are the
-// row indices inside the tiles.
-__device__ __forceinline__ bool allowed(const MaskRule& r, int32_t qi, int32_t kj, int32_t i,
-                                        int32_t j, int32_t kcount) {
-  if (kj >= kcount) return false;
-  switch (r.kind) {
-    case kBand: {
-      // strided index difference key - query
-      const int32_t dlt = kj - qi - r.qoff;
-      if (r.causal) return dlt <= 0 && dlt >= -r.radius;
-      return dlt >= -r.radius && dlt <= r.radius;
-    }
-    case kGlobCol: {
-      if (r.causal && j > i) return false;
-      const int32_t dl = j - i;
-      const bool in_band = (dl % r.dil == 0) && (dl / r.dil <= r.radius) &&
-                           (dl / r.dil >= -r.radius) && (!r.causal || dl <= 0);
-      return !in_band;  // the band tile already counted it
-    }
-    case kAll:
-      return !r.causal || j <= i;
-    default: {  // kSeg
-      const int32_t dlt = kj - qi - r.qoff;
-      return !r.causal || dlt <= 0;
-    }
+// Number of entries of the sorted array g[0..n) that are < p.
+__device__ __forceinline__ int32_t lower_bound(const int32_t* g, int32_t n, int32_t p) {
+  int32_t lo = 0, hi = n;
+  while (lo < hi) {
+    int32_t mid = (lo + hi) >> 1;
+    if (g[mid] < p) lo = mid + 1; else hi = mid;
   }
+  return lo;
 }
+
+// Key rows of one tile: positions base + stride*x (strided view) or idx[x]
+// (gather through the global index list), for x < count (count >= 1).
+struct KeyTile {
+  const int32_t* idx;
+  int32_t base, stride, count;
+  int32_t gbit0;  // bit of row 0 in the workgroup's global bitmap (strided tiles)
+};
+
+// Which (query, key) pairs of a tile are allowed.
+//   kRange:   key row kj of the tile, reference ref = (use_qpos ? qpos : qi) + ref_off;
+//             allowed iff kj < count and lo <= kj - ref <= hi.
+//   kGlobCol: key j = global position outside the query's window (j <= i if causal).
+enum MaskKind : int32_t { kRange = 0, kGlobCol = 1 };
+
+struct MaskRule {
+  int32_t kind;
+  int32_t need_mask;  // 0: every (query, key) of the tile is allowed
+  int32_t use_qpos;
+  int32_t ref_off;
+  int32_t lo, hi;
+  // kGlobCol only
+  int32_t causal, radius, dil;
+};
+
+constexpr int32_t kFar = 0x3fffffff;
+
+// How the per-key "is global" flags of a tile are found (needed by the bias).
+enum GlobMode : int32_t { kGlobNone = 0, kGlobBitmap = 1, kGlobSearch = 2, kGlobAll = 3 };
+
+struct GlobInfo {
+  int32_t mode;
+  const int32_t* gidx;
+  int32_t n_global;
+};
 
 // Bias source: the scalar relative-position table of one head (ETC page,
 // §3.4 "Relative Position Encoding": labels clip j - i to [-k, k]).
 struct BiasRule {
-  const float* tab;   // LDS copy of the head's 2k+1 entries, or null
+  const float* tab;   // LDS copy of the head's 2k+1 entries (times sqrt(D)), or null
   int32_t k;
   int32_t key_global_is_same_kind;  // 1: pair is same-kind iff the key is global
 };
@@ -154,22 +139,36 @@ struct BiasRule {
 template <typename T>
 struct TileTraits;
 
+// Position of key row x of a tile (x clamped into [0, count) by the caller).
+template <bool GATHER>
+__device__ __forceinline__ int32_t key_pos(const KeyTile& kt, int32_t x) {
+  if constexpr (GATHER) return kt.idx[x];
+  else return kt.base + kt.stride * x;
+}
+
+// Per-key metadata shared by both engines: position and global flag.
+struct KeyMeta {
+  int32_t pos;
+  int32_t gbit;
+};
+
 // ---------------------------------------------------------------------------
 // bf16 engine
 // ---------------------------------------------------------------------------
 template <>
 struct TileTraits<bf16> {
-  struct Smem {
-    bf16 k[2][kTK][kKPitchBf16];
-    bf16 vt[2][kD][kVPitchBf16];
-    int32_t kpos[2][kTK];
-    uint8_t kglob[2][kTK];
-    float bias[64];
+  // 16-byte alignment lets the operand reads use ds_read_b128 / ds_read_b64.
+  struct __attribute__((aligned(16))) Smem {
+    alignas(16) bf16 k[2][kTK][kKPitchBf16];
+    alignas(16) bf16 vt[2][kD][kVPitchBf16];
+    alignas(16) int32_t kpos[2][kTK];
+    alignas(16) float bias[64];
+    alignas(16) uint32_t gmask[kGMaskWords];
+    alignas(16) uint8_t kglob[2][kTK];
   };
   struct Prefetch {
     u32x4 k0, k1, v0, v1;
-    int32_t pos;
-    uint8_t glob;
+    KeyMeta meta;
   };
   struct Wave {
     bf16x8 qf[2];
@@ -178,27 +177,24 @@ struct TileTraits<bf16> {
     float l;  // this lane's share of the running sum
   };
 
-  // Issue the global loads of one key tile into registers.
+  // Issue the global loads of one key tile into registers. Rows past the
+  // tile's end re-read its last row: those keys are masked, and a valid row
+  // keeps every value finite.
+  template <bool GATHER>
   static __device__ __forceinline__ void fetch(Prefetch& pf, const bf16* kb, const bf16* vb,
-                                               const RowMap& km, int32_t tid, bool need_glob,
-                                               const int32_t* gidx, int32_t n_global) {
-    const int32_t kk = tid >> 2, ck = tid & 3;
-    const int32_t vp = tid >> 3, cv = tid & 7;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    if (kk < km.count) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(kb + (size_t)km.pos(kk) * kD + 16 * ck);
-      pf.k0 = src[0];
-      pf.k1 = src[1];
-    } else {
-      pf.k0 = z;
-      pf.k1 = z;
-    }
-    const int32_t ka = 2 * vp, kb2 = 2 * vp + 1;
-    pf.v0 = ka < km.count ? *reinterpret_cast<const u32x4*>(vb + (size_t)km.pos(ka) * kD + 8 * cv) : z;
-    pf.v1 = kb2 < km.count ? *reinterpret_cast<const u32x4*>(vb + (size_t)km.pos(kb2) * kD + 8 * cv) : z;
+                                               const KeyTile& kt, int32_t tid) {
+    const int32_t last = kt.count - 1;
+    const int32_t pk = key_pos<GATHER>(kt, min(tid >> 2, last));
+    const int32_t pa = key_pos<GATHER>(kt, min(2 * (tid >> 3), last));
+    const int32_t pb = key_pos<GATHER>(kt, min(2 * (tid >> 3) + 1, last));
+    const u32x4* ks = reinterpret_cast<const u32x4*>(kb + (size_t)pk * kD + 16 * (tid & 3));
+    pf.k0 = ks[0];
+    pf.k1 = ks[1];
+    pf.v0 = *reinterpret_cast<const u32x4*>(vb + (size_t)pa * kD + 8 * (tid & 7));
+    pf.v1 = *reinterpret_cast<const u32x4*>(vb + (size_t)pb * kD + 8 * (tid & 7));
     if (tid < kTK) {
-      pf.pos = tid < km.count ? km.pos(tid) : 0;
-      pf.glob = (need_glob && tid < km.count) ? (uint8_t)sorted_contains(gidx, n_global, pf.pos) : 0;
+      pf.meta.pos = key_pos<GATHER>(kt, min(tid, last));
+      pf.meta.gbit = kt.gbit0 + min(tid, last);
     }
   }
 
@@ -213,29 +209,18 @@ struct TileTraits<bf16> {
     for (int e = 0; e < 4; ++e) {
       // two bf16 of one key share a dword; pair keys 2vp and 2vp+1
       const uint32_t a = pf.v0[e], b = pf.v1[e];
-      const uint32_t lo = (a & 0xffffu) | (b << 16);
-      const uint32_t hi = (a >> 16) | (b & 0xffff0000u);
-      *reinterpret_cast<uint32_t*>(&sm.vt[buf][8 * cv + 2 * e][2 * vp]) = lo;
-      *reinterpret_cast<uint32_t*>(&sm.vt[buf][8 * cv + 2 * e + 1][2 * vp]) = hi;
-    }
-    if (tid < kTK) {
-      sm.kpos[buf][tid] = pf.pos;
-      sm.kglob[buf][tid] = pf.glob;
+      *reinterpret_cast<uint32_t*>(&sm.vt[buf][8 * cv + 2 * e][2 * vp]) =
+          __builtin_amdgcn_perm(b, a, 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&sm.vt[buf][8 * cv + 2 * e + 1][2 * vp]) =
+          __builtin_amdgcn_perm(b, a, 0x07060302u);
     }
   }
 
-  static __device__ __forceinline__ void load_q(Wave& w, const bf16* qb, const RowMap& qm,
-                                                int32_t wave, int32_t lane) {
-    const int32_t qq = 16 * wave + (lane & 15), g = lane >> 4;
-    if (qq < qm.count) {
-      const bf16x8* src = reinterpret_cast<const bf16x8*>(qb + (size_t)qm.pos(qq) * kD + 8 * g);
-      w.qf[0] = src[0];
-      w.qf[1] = src[4];
-    } else {
-      const bf16x8 z = {};
-      w.qf[0] = z;
-      w.qf[1] = z;
-    }
+  static __device__ __forceinline__ void load_q(Wave& w, const bf16* qb, int32_t qrow_pos,
+                                                int32_t lane) {
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(qb + (size_t)qrow_pos * kD + 8 * (lane >> 4));
+    w.qf[0] = src[0];
+    w.qf[1] = src[4];
     const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < 4; ++i) w.o[i] = zf;
     w.m = kNegInf;
@@ -304,17 +289,17 @@ struct TileTraits<bf16> {
 // ---------------------------------------------------------------------------
 template <>
 struct TileTraits<float> {
-  struct Smem {
-    float k[2][kTK][kPitchF32];
-    float v[2][kTK][kPitchF32];
-    int32_t kpos[2][kTK];
-    uint8_t kglob[2][kTK];
-    float bias[64];
+  struct __attribute__((aligned(16))) Smem {
+    alignas(16) float k[2][kTK][kPitchF32];
+    alignas(16) float v[2][kTK][kPitchF32];
+    alignas(16) int32_t kpos[2][kTK];
+    alignas(16) float bias[64];
+    alignas(16) uint32_t gmask[kGMaskWords];
+    alignas(16) uint8_t kglob[2][kTK];
   };
   struct Prefetch {
     u32x4 k[4], v[4];
-    int32_t pos;
-    uint8_t glob;
+    KeyMeta meta;
   };
   struct Wave {
     float qf[16];
@@ -323,30 +308,21 @@ struct TileTraits<float> {
     float l;
   };
 
+  template <bool GATHER>
   static __device__ __forceinline__ void fetch(Prefetch& pf, const float* kb, const float* vb,
-                                               const RowMap& km, int32_t tid, bool need_glob,
-                                               const int32_t* gidx, int32_t n_global) {
-    const int32_t kk = tid >> 2, c = tid & 3;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    if (kk < km.count) {
-      const size_t row = (size_t)km.pos(kk) * kD + 16 * c;
-      const u32x4* ks = reinterpret_cast<const u32x4*>(kb + row);
-      const u32x4* vs = reinterpret_cast<const u32x4*>(vb + row);
+                                               const KeyTile& kt, int32_t tid) {
+    const int32_t last = kt.count - 1;
+    const size_t row = (size_t)key_pos<GATHER>(kt, min(tid >> 2, last)) * kD + 16 * (tid & 3);
+    const u32x4* ks = reinterpret_cast<const u32x4*>(kb + row);
+    const u32x4* vs = reinterpret_cast<const u32x4*>(vb + row);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        pf.k[x] = ks[x];
-        pf.v[x] = vs[x];
-      }
-    } else {
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        pf.k[x] = z;
-        pf.v[x] = z;
-      }
+    for (int x = 0; x < 4; ++x) {
+      pf.k[x] = ks[x];
+      pf.v[x] = vs[x];
     }
     if (tid < kTK) {
-      pf.pos = tid < km.count ? km.pos(tid) : 0;
-      pf.glob = (need_glob && tid < km.count) ? (uint8_t)sorted_contains(gidx, n_global, pf.pos) : 0;
+      pf.meta.pos = key_pos<GATHER>(kt, min(tid, last));
+      pf.meta.gbit = kt.gbit0 + min(tid, last);
     }
   }
 
@@ -358,25 +334,15 @@ struct TileTraits<float> {
       *reinterpret_cast<u32x4*>(&sm.k[buf][kk][16 * c + 4 * x]) = pf.k[x];
       *reinterpret_cast<u32x4*>(&sm.v[buf][kk][16 * c + 4 * x]) = pf.v[x];
     }
-    if (tid < kTK) {
-      sm.kpos[buf][tid] = pf.pos;
-      sm.kglob[buf][tid] = pf.glob;
-    }
   }
 
   // The contraction over d runs in the order d = 16g + step, so each lane
   // reads 16 contiguous floats of its Q row and of each K row.
-  static __device__ __forceinline__ void load_q(Wave& w, const float* qb, const RowMap& qm,
-                                                int32_t wave, int32_t lane) {
-    const int32_t qq = 16 * wave + (lane & 15), g = lane >> 4;
-    if (qq < qm.count) {
-      const float* src = qb + (size_t)qm.pos(qq) * kD + 16 * g;
+  static __device__ __forceinline__ void load_q(Wave& w, const float* qb, int32_t qrow_pos,
+                                                int32_t lane) {
+    const float* src = qb + (size_t)qrow_pos * kD + 16 * (lane >> 4);
 #pragma unroll
-      for (int x = 0; x < 16; ++x) w.qf[x] = src[x];
-    } else {
-#pragma unroll
-      for (int x = 0; x < 16; ++x) w.qf[x] = 0.f;
-    }
+    for (int x = 0; x < 16; ++x) w.qf[x] = src[x];
     const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < 4; ++i) w.o[i] = zf;
     w.m = kNegInf;
@@ -424,10 +390,100 @@ struct TileTraits<float> {
   }
 };
 
-// ---------------------------------------------------------------------------
+// Per-key position and global flag of a staged tile (tid < 64 write them).
+template <typename T>
+__device__ __forceinline__ void stage_meta(typename TileTraits<T>::Smem& sm, int32_t buf,
+                                           const KeyMeta& mt, const GlobInfo& gi, int32_t tid) {
+  if (tid < kTK) {
+    sm.kpos[buf][tid] = mt.pos;
+    uint8_t f = 0;
+    if (gi.mode == kGlobBitmap)
+      f = (uint8_t)((sm.gmask[mt.gbit >> 5] >> (mt.gbit & 31)) & 1u);
+    else if (gi.mode == kGlobSearch)
+      f = (uint8_t)sorted_contains(gi.gidx, gi.n_global, mt.pos);
+    else if (gi.mode == kGlobAll)
+      f = 1;
+    sm.kglob[buf][tid] = f;
+  }
+}
+
+// Mark in sm.gmask the rows u in [0, count) whose position base + stride*u is
+// global. Needs count <= 32 * kGMaskWords. Ends with a barrier.
+template <typename T>
+__device__ __forceinline__ void build_gmask(typename TileTraits<T>::Smem& sm, const int32_t* gidx,
+                                            int32_t n_global, int32_t base, int32_t stride,
+                                            int32_t count, int32_t tid) {
+  for (int32_t x = tid; x < kGMaskWords; x += kThreads) sm.gmask[x] = 0u;
+  __syncthreads();
+  for (int32_t x = tid; x < n_global; x += kThreads) {
+    const int32_t dl = gidx[x] - base;
+    if (dl >= 0 && dl % stride == 0 && dl / stride < count) {
+      const int32_t u = dl / stride;
+      atomicOr(&sm.gmask[u >> 5], 1u << (u & 31));
+    }
+  }
+  __syncthreads();
+}
+
+// Scores stay raw dot products q.k until the exponent; the bias table in LDS
+// is pre-multiplied by sqrt(D) so that it adds in the same units.
+template <typename T>
+__device__ __forceinline__ void add_bias(f32x4 s[4], const typename TileTraits<T>::Smem& sm,
+                                         int32_t buf, const BiasRule& br, int32_t qpos, int32_t g) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t kj = 16 * kb + 4 * g + i;
+      const bool same = (sm.kglob[buf][kj] != 0) == (br.key_global_is_same_kind != 0);
+      const int32_t dl = min(max(sm.kpos[buf][kj] - qpos, -br.k), br.k);
+      const float b = br.tab[dl + br.k];  // always read: keeps the loop branch-free
+      s[kb][i] += same ? b : 0.f;
+    }
+  }
+}
+
+// Set excluded (query, key) pairs of a partial tile to -inf. One uniform
+// branch per tile; the per-element tests are a few integer ops.
+template <typename T>
+__device__ __forceinline__ void mask_tile(f32x4 s[4], const typename TileTraits<T>::Smem& sm,
+                                          int32_t buf, const MaskRule& mr, int32_t kcount,
+                                          int32_t qi, int32_t qpos, int32_t g) {
+  if (mr.kind == kRange) {
+    const int32_t base = 4 * g - (mr.use_qpos ? qpos : qi) - mr.ref_off;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t kj = 16 * kb + 4 * g + i;
+        const int32_t dlt = base + 16 * kb + i;
+        const bool ok = (kj < kcount) & (dlt >= mr.lo) & (dlt <= mr.hi);
+        s[kb][i] = ok ? s[kb][i] : kNegInf;
+      }
+    }
+  } else {  // kGlobCol
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t kj = 16 * kb + 4 * g + i;
+        const int32_t dl = sm.kpos[buf][kj] - qpos;
+        const bool in_band = (dl % mr.dil == 0) & (dl >= -mr.radius * mr.dil) &
+                             (dl <= mr.radius * mr.dil) & (!mr.causal | (dl <= 0));
+        const bool ok = (kj < kcount) & (!mr.causal | (dl <= 0)) & !in_band;
+        s[kb][i] = ok ? s[kb][i] : kNegInf;
+      }
+    }
+  }
+}
+
+// The running max moves only when a row's tile max exceeds it by more than
+// this many log2 units; p = 2^(t - m) then stays below 2^8, and the final
+// O = sum p v / sum p is unchanged, so most tiles skip the O rescale.
+constexpr float kRescaleSlack = 8.0f;
+
 // One key tile through the online softmax (shared by both engines).
 // qpos: this lane's query position; qi: its row index in the query tile.
-// ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem& sm, int32_t buf,
                                              typename TileTraits<T>::Wave& w, int32_t lane,
@@ -437,80 +493,71 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
   f32x4 s[4];
   TT::scores(sm, buf, w, lane, s);
   const int32_t g = lane >> 4;
-  float mx = kNegInf;
+  if (br.tab) add_bias<T>(s, sm, buf, br, qpos, g);
+  if (mr.need_mask) mask_tile<T>(s, sm, buf, mr, kcount, qi, qpos, g);
+  float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int32_t kj = 16 * kb + 4 * g + i;
-      float t = s[kb][i] * scale_log2;
-      if (br.tab) {
-        const int32_t j = sm.kpos[buf][kj];
-        const bool kglob = sm.kglob[buf][kj] != 0;
-        if (kglob == (br.key_global_is_same_kind != 0)) {
-          int32_t dl = j - qpos;
-          dl = dl < -br.k ? -br.k : (dl > br.k ? br.k : dl);
-          t += br.tab[dl + br.k] * kLog2e;
-        }
-      }
-      if (mr.need_mask && !allowed(mr, qi, kj, qpos, sm.kpos[buf][kj], kcount)) t = kNegInf;
-      s[kb][i] = t;
-      mx = fmaxf(mx, t);
-    }
-  }
+  for (int kb = 1; kb < 4; ++kb)
+    mx = fmaxf(fmaxf(mx, fmaxf(s[kb][0], s[kb][1])), fmaxf(s[kb][2], s[kb][3]));
   mx = wave_max_xor16_32(mx);
-  const float m_new = fmaxf(w.m, mx);
+  const float mt = mx * scale_log2;  // tile max in log2 units (-inf if all masked)
+  const bool up = mt > w.m + kRescaleSlack;
+  if (__ballot(up) != 0ull) {
+    const float alpha = !up ? 1.f : (w.m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(w.m - mt));
+    w.m = up ? mt : w.m;
+    w.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) w.o[db] *= alpha;
+  }
   // A row with every key masked so far keeps m = -inf; shift by 0 then.
-  const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(w.m - m_use);
+  const float nm = (w.m == kNegInf) ? 0.f : -w.m;
   float rs = 0.f;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f(s[kb][i] - m_use);
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], scale_log2, nm));
       s[kb][i] = p;
       rs += p;
     }
   }
-  w.m = m_new;
-  w.l = w.l * alpha + rs;
-#pragma unroll
-  for (int db = 0; db < 4; ++db) w.o[db] *= alpha;
+  w.l += rs;
   TT::accumulate(sm, buf, w, lane, s);
 }
 
-// The key-tile loop: tiles 0..n_tiles-1 described by desc(n, RowMap&, MaskRule&).
-template <typename T, typename Desc>
+// The key-tile loop: tiles 0..n_tiles-1 described by desc(n, KeyTile&, MaskRule&),
+// all strided or all gathered (GATHER).
+template <typename T, bool GATHER, typename Desc>
 __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
                                           typename TileTraits<T>::Wave& w, const T* kb,
                                           const T* vb, int32_t n_tiles, Desc desc,
-                                          const BiasRule& br, bool need_glob,
-                                          const int32_t* gidx, int32_t n_global, int32_t qi,
+                                          const BiasRule& br, const GlobInfo& gi, int32_t qi,
                                           int32_t qpos, float scale_log2) {
   using TT = TileTraits<T>;
   const int32_t tid = threadIdx.x, lane = tid & 63;
   if (n_tiles <= 0) return;
   typename TT::Prefetch pf;
-  RowMap km;
+  KeyTile kt;
   MaskRule mr;
-  desc(0, km, mr);
-  TT::fetch(pf, kb, vb, km, tid, need_glob, gidx, n_global);
+  desc(0, kt, mr);
+  TT::template fetch<GATHER>(pf, kb, vb, kt, tid);
   TT::stage(sm, 0, pf, tid);
+  stage_meta<T>(sm, 0, pf.meta, gi, tid);
   __syncthreads();
   for (int32_t n = 0; n < n_tiles; ++n) {
     const int32_t buf = n & 1;
-    RowMap km_next;
+    KeyTile kt_next;
     MaskRule mr_next;
     const bool more = n + 1 < n_tiles;
     if (more) {
-      desc(n + 1, km_next, mr_next);
-      TT::fetch(pf, kb, vb, km_next, tid, need_glob, gidx, n_global);
+      desc(n + 1, kt_next, mr_next);
+      TT::template fetch<GATHER>(pf, kb, vb, kt_next, tid);
     }
-    process_tile<T>(sm, buf, w, lane, mr, br, km.count, qi, qpos, scale_log2);
+    process_tile<T>(sm, buf, w, lane, mr, br, kt.count, qi, qpos, scale_log2);
     if (more) {
       TT::stage(sm, buf ^ 1, pf, tid);
-      km = km_next;
+      stage_meta<T>(sm, buf ^ 1, pf.meta, gi, tid);
+      kt = kt_next;
       mr = mr_next;
     }
     __syncthreads();
