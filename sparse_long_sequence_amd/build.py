@@ -16,8 +16,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU ops are kept out of the generated code (they are avoided on
 # the test machines); hipcc's host pass warns that it does not know the feature.
+# -fno-honor-nans: inputs are finite, so fmax needs no NaN canonicalisation
+# (infinities, which the masks use, keep their meaning).
+# -amdgpu-mfma-vgpr-form: MFMA results stay in VGPRs (no AGPR round trips).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
 
 

@@ -22,7 +22,6 @@ la_status fail(la_status s, const std::string& msg) {
 }
 
 constexpr int32_t kDHead = 64;
-constexpr int32_t kQTile = 64;
 constexpr int32_t kChunk = 512;  // keys per global-row partial
 constexpr size_t kAlign = 256;
 
@@ -85,7 +84,7 @@ la_status plan_dilated(const la_dims* d, const int32_t* w, const int32_t* r, int
     a.r[k] = r[k];
     a.nseg[k] = (d->N + w[k] - 1) / w[k];
     a.seg_rows[k] = (w[k] + r[k] - 1) / r[k];
-    a.qtiles[k] = (a.seg_rows[k] + kQTile - 1) / kQTile;
+    a.qtiles[k] = (a.seg_rows[k] + la::kDilatedQueryTile - 1) / la::kDilatedQueryTile;
     a.row_off[k] = rows;
     rows += (int64_t)d->B * d->H * a.nseg[k] * a.seg_rows[k];
   }
@@ -200,12 +199,13 @@ la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, con
   }
   a.chunk_len = kChunk;
   a.n_chunks = n_chunks_of(dims->N);
+  const int32_t tq = la::host_query_tile(dims->dtype);
   int32_t tiles = 0;
   for (int32_t h = 0; h < dims->H; ++h)
-    tiles = std::max(tiles, la::host_band_tiles_of_head(dims->N, a.dil[h]));
+    tiles = std::max(tiles, la::host_band_tiles_of_head(dims->N, a.dil[h], tq));
   a.band_tiles_per_head = tiles;
   const int64_t band_wg = (int64_t)dims->B * dims->H * tiles;
-  a.n_gq_tiles = (n_global + kQTile - 1) / kQTile;
+  a.n_gq_tiles = (n_global + tq - 1) / tq;
   const int64_t glob_wg = (int64_t)dims->B * dims->H * a.n_gq_tiles * a.n_chunks;
   if (band_wg + glob_wg > 0x7fffffffLL) return fail(LA_EUNSUPPORTED, "launch grid too large");
   a.n_band_wg = (int32_t)band_wg;

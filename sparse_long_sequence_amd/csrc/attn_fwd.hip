@@ -20,10 +20,10 @@
 
 namespace la {
 
-// Number of residue-class query tiles of a head of dilation d.
-__host__ __device__ inline int32_t band_tiles_of_head(int32_t N, int32_t d) {
+// Number of residue-class query tiles (of tq rows) of a head of dilation d.
+__host__ __device__ inline int32_t band_tiles_of_head(int32_t N, int32_t d, int32_t tq) {
   int32_t t = 0;
-  for (int32_t c = 0; c < d && c < N; ++c) t += ((N - c + d - 1) / d + kTQ - 1) / kTQ;
+  for (int32_t c = 0; c < d && c < N; ++c) t += ((N - c + d - 1) / d + tq - 1) / tq;
   return t;
 }
 
@@ -63,6 +63,7 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
                                                int32_t bw) {
   using TT = TileTraits<T>;
   using O = typename OutT<T>::type;
+  constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t N = a.N;
   const size_t head_elems = (size_t)N * kD;
@@ -95,7 +96,7 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   const T* qb = reinterpret_cast<const T*>(a.q) + bh * head_elems;
   const T* kb = reinterpret_cast<const T*>(a.k) + bh * head_elems;
   const T* vb = reinterpret_cast<const T*>(a.v) + bh * head_elems;
-  const int32_t qi = 16 * wave + (lane & 15);
+  const int32_t qi = TT::qrow(wave, lane);
   const int32_t qpos = qbase + d * min(qi, qcount - 1);
   typename TT::Wave w;
   TT::load_q(w, qb, qpos, lane);
@@ -167,14 +168,14 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   }
 
   // epilogue: rows outside G (the global-row pass owns the rest)
-  const float l_tot = wave_sum_xor16_32(w.l);
+  const float l_tot = TT::row_sum(w.l);
   if (qi < qcount) {
     const bool is_g = g1 > g0 && sorted_contains(a.gidx + g0, g1 - g0, qpos);
     if (!is_g) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       O* dst = reinterpret_cast<O*>(a.out) + bh * head_elems + (size_t)qpos * kD;
-      TT::store_row(dst, w.o, inv, lane);
-      if (a.lse && (lane >> 4) == 0)
+      TT::store_row(dst, w, inv, lane);
+      if (a.lse && TT::row_leader(lane))
         a.lse[(size_t)bh * N + qpos] = l_tot > 0.f ? (w.m + __log2f(l_tot)) * kLn2 : kNegInf;
     }
   }
@@ -187,6 +188,7 @@ template <typename T>
 __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
                                                  typename TileTraits<T>::Smem& sm, int32_t gw) {
   using TT = TileTraits<T>;
+  constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t N = a.N;
   const size_t head_elems = (size_t)N * kD;
@@ -213,7 +215,7 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   const T* qb = reinterpret_cast<const T*>(a.qg) + bh * head_elems;
   const T* kb = reinterpret_cast<const T*>(a.kg) + bh * head_elems;
   const T* vb = reinterpret_cast<const T*>(a.vg) + bh * head_elems;
-  const int32_t qi = 16 * wave + (lane & 15);
+  const int32_t qi = TT::qrow(wave, lane);
   const int32_t qpos = qidx[min(qi, qcount - 1)];
   typename TT::Wave w;
   TT::load_q(w, qb, qpos, lane);
@@ -227,19 +229,20 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   };
   const BiasRule br = {want_bias ? sm.bias : nullptr, a.rel_k, 1};
   run_tiles<T, false>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, a.scale_log2);
-  const float l_tot = wave_sum_xor16_32(w.l);
+  const float l_tot = TT::row_sum(w.l);
   if (qi < qcount) {
     const size_t prow = ((size_t)bh * a.n_global + gq * kTQ + qi) * a.n_chunks + chunk;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    TileTraits<float>::store_row(a.ws_o + prow * kD, w.o, inv, lane);
-    if ((lane >> 4) == 0) a.ws_lse[prow] = l_tot > 0.f ? (w.m + __log2f(l_tot)) * kLn2 : kNegInf;
+    TT::store_row_f32(a.ws_o + prow * kD, w, inv, lane);
+    if (TT::row_leader(lane)) a.ws_lse[prow] = l_tot > 0.f ? (w.m + __log2f(l_tot)) * kLn2 : kNegInf;
   }
 }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   __shared__ typename TileTraits<T>::Smem sm;
-  const int32_t wg = (int32_t)blockIdx.x;
+  const int32_t wg = xcd_logical_block((int32_t)blockIdx.x, a.n_glob_wg + a.n_band_wg);
+  if (wg < 0) return;
   // global-row workgroups come first in the grid so they are not the tail
   if (wg < a.n_glob_wg) global_workgroup<T>(a, sm, wg);
   else band_workgroup<T>(a, sm, wg - a.n_glob_wg);
@@ -282,8 +285,9 @@ __global__ __launch_bounds__(256) void global_merge_kernel(AttnArgs a) {
 }
 
 hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
-  const int64_t grid = (int64_t)a.n_band_wg + (int64_t)a.n_glob_wg;
+  int64_t grid = (int64_t)a.n_band_wg + (int64_t)a.n_glob_wg;
   if (grid <= 0) return hipSuccess;
+  grid = (grid + kXcds - 1) / kXcds * kXcds;  // padded for the XCD remap
   if (dtype == 1)
     hipLaunchKernelGGL(attn_fwd_kernel<bf16>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);
   else
@@ -298,6 +302,11 @@ hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int32_t host_band_tiles_of_head(int32_t N, int32_t d) { return band_tiles_of_head(N, d); }
+int32_t host_band_tiles_of_head(int32_t N, int32_t d, int32_t tq) {
+  return band_tiles_of_head(N, d, tq);
+}
+int32_t host_query_tile(int32_t dtype) {
+  return dtype == 1 ? TileTraits<bf16>::kTQ : TileTraits<float>::kTQ;
+}
 
 }  // namespace la

@@ -19,8 +19,10 @@ namespace la {
 __global__ __launch_bounds__(kThreads) void dilated_pair_kernel(DilArgs a) {
   using TT = TileTraits<bf16>;
   __shared__ TT::Smem sm;
+  constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t wg = blockIdx.x;
+  const int64_t wg = xcd_logical_block((int32_t)blockIdx.x, (int32_t)a.wg_start[a.n_pairs]);
+  if (wg < 0) return;
   int32_t oi = 0;
   while (oi + 1 < a.n_pairs && wg >= a.wg_start[oi + 1]) ++oi;
   const int32_t k = a.order[oi];
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void dilated_pair_kernel(DilArgs a) {
   const bf16* kb = reinterpret_cast<const bf16*>(a.k) + bh * head_elems;
   const bf16* vb = reinterpret_cast<const bf16*>(a.v) + bh * head_elems;
   const int32_t base = sigma + s;
-  const int32_t qi = 16 * wave + (lane & 15);
+  const int32_t qi = TT::qrow(wave, lane);
   const int32_t qpos = base + r * (t0 + min(qi, qcount - 1));
   TT::Wave wv;
   TT::load_q(wv, qb, qpos, lane);
@@ -63,12 +65,12 @@ __global__ __launch_bounds__(kThreads) void dilated_pair_kernel(DilArgs a) {
   const BiasRule br = {nullptr, 0, 0};
   const GlobInfo gi = {kGlobNone, nullptr, 0};
   run_tiles<bf16, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, a.scale_log2);
-  const float l_tot = wave_sum_xor16_32(wv.l);
+  const float l_tot = TT::row_sum(wv.l);
   if (qi < qcount) {
     const int64_t prow = a.row_off[k] + ((int64_t)bh * nseg + seg) * a.seg_rows[k] + t0 + qi;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    TileTraits<float>::store_row(a.ws_o + prow * kD, wv.o, inv, lane);
-    if ((lane >> 4) == 0) a.ws_lse[prow] = l_tot > 0.f ? (wv.m + __log2f(l_tot)) * kLn2 : kNegInf;
+    TT::store_row_f32(a.ws_o + prow * kD, wv, inv, lane);
+    if (TT::row_leader(lane)) a.ws_lse[prow] = l_tot > 0.f ? (wv.m + __log2f(l_tot)) * kLn2 : kNegInf;
   }
 }
 
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(256) void dilated_combine_kernel(DilArgs a) {
 }
 
 hipError_t launch_dilated(const DilArgs& a, hipStream_t stream) {
-  const int64_t grid = a.wg_start[a.n_pairs];
+  const int64_t grid = (a.wg_start[a.n_pairs] + kXcds - 1) / kXcds * kXcds;  // XCD remap padding
   if (grid > 0) {
     hipLaunchKernelGGL(dilated_pair_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();

@@ -52,6 +52,8 @@ struct DilArgs {
 
 hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream);
 hipError_t launch_dilated(const DilArgs& a, hipStream_t stream);
-int32_t host_band_tiles_of_head(int32_t N, int32_t d);
+int32_t host_band_tiles_of_head(int32_t N, int32_t d, int32_t tq);
+int32_t host_query_tile(int32_t dtype);  // query rows per workgroup
+constexpr int32_t kDilatedQueryTile = 128;  // bf16 workgroup rows of the LongNet kernel
 
 }  // namespace la
