@@ -3,21 +3,30 @@
 A step is one la_attn_forward call on the Longformer-base workload (B=2, H=12,
 N=4096, D=64, bf16, window radius 256, 64 global tokens with separate global
 projections): band tiles, global-column fold, online softmax, PV, epilogue and
-the global-row pass with its merge, all in one kernel launch. Inputs are seeded
-synthetic N(0,1) tensors already resident in device memory.
+the global-row pass (one launch), then the merge of the global rows' key-chunk
+partials (a second, small launch). Inputs are seeded synthetic N(0,1) tensors
+already resident in device memory.
 
 Prints one JSON line. `value` is useful TFLOP/s (4*D FLOPs per allowed
-(query, key) pair) on that workload; `roofline` relates the kernel's average
-launch duration, timed with HIP events on the stream the kernel runs on, to the
-bf16 MFMA peak; `workloads` times the other four workloads the same way;
-`cpu_baseline` times the fp64 CPU oracle on a bounded row sample of the same
-workload on the host cores.
+(query, key) pair) on that workload; `roofline` relates the call's average
+duration, timed with HIP events on the stream its kernels run on, to the bf16
+MFMA peak, and reports the HBM traffic that rocprofv3's FETCH_SIZE/WRITE_SIZE
+counters measured for the same kernels (read from profiles/, and null when the
+kernel sources changed since); `workloads` times the other four workloads the
+same way; `cpu_baseline` times the fp64 CPU oracle on a bounded row sample of
+the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only NAME]
+                       [--copy-probe]
+
+--copy-probe also runs a plain device copy of 256 MiB (torch.neg, fp32) a few
+times: under rocprofv3 --pmc its FETCH_SIZE and WRITE_SIZE give the factor that
+turns those counters into bytes.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -61,18 +70,17 @@ class Call:
         else:
             nb = la.la_attn_workspace_size(dims, len(w.global_idx), w.separate_global)
         self.ws = torch.zeros(max(nb, 1), dtype=torch.uint8, device=dev)
-        self.la = la
+        if w.kind == "dilated":
+            self.bound = la.bind_dilated(self.q, self.k, self.v, [p[0] for p in w.pairs],
+                                         [p[1] for p in w.pairs], w.causal, out=self.out,
+                                         lse=self.lse, workspace=self.ws)
+        else:
+            self.bound = la.bind_attn(self.q, self.k, self.v, self.g, w.radius, w.dilation,
+                                      w.causal, self.rb, out=self.out, lse=self.lse, qg=self.qg,
+                                      kg=self.kg, vg=self.vg, workspace=self.ws)
 
     def __call__(self):
-        w = self.w
-        if w.kind == "dilated":
-            self.la.la_dilated_forward(self.q, self.k, self.v, [p[0] for p in w.pairs],
-                                       [p[1] for p in w.pairs], w.causal, out=self.out,
-                                       lse=self.lse, workspace=self.ws)
-        else:
-            self.la.la_attn_forward(self.q, self.k, self.v, self.g, w.radius, w.dilation, w.causal,
-                                    self.rb, out=self.out, lse=self.lse, qg=self.qg, kg=self.kg,
-                                    vg=self.vg, workspace=self.ws)
+        self.bound()
 
 
 def time_calls(call, steps, warmup):
@@ -144,6 +152,58 @@ def cpu_baseline(w, budget_s=20.0):
             "seconds": round(elapsed, 3)}
 
 
+COPY_PROBE_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_longformer_base_traffic.txt")
+
+
+def kernel_sources_digest() -> str:
+    """sha256 over the sources the HIP library is built from (and its build flags)."""
+    import glob
+
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "sparse_long_sequence_amd")
+    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + \
+        sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))) + [os.path.join(pkg, "build.py")]
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per call from the committed counter summary, or None.
+
+    The summary holds `key = value` lines: sources_sha256, fetch_kib and
+    write_kib (average per call, all kernels of the call) and copy_fetch_kib /
+    copy_write_kib of the copy probe. Counters are scaled by known/measured of
+    the probe. None if the file is missing or the kernel sources changed.
+    """
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(ln.split("=", 1) for ln in fh.read().splitlines()
+                      if "=" in ln and not ln.lstrip().startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("sources_sha256") != kernel_sources_digest():
+        return None
+    known_kib = COPY_PROBE_BYTES / 1024
+    f_fetch = known_kib / float(kv["copy_fetch_kib"])
+    f_write = known_kib / float(kv["copy_write_kib"])
+    return (float(kv["fetch_kib"]) * f_fetch + float(kv["write_kib"]) * f_write) * 1024
+
+
+def copy_probe(dev, reps=3):
+    import torch
+
+    x = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +211,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="time only this workload name")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 256 MiB device copy (counter scaling under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -163,6 +225,9 @@ def main():
     from sparse_long_sequence_amd import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        log("bench: copy probe (torch.neg, 256 MiB fp32)")
+        copy_probe(dev)
     head = W.LONGFORMER_BASE
     results = {}
     for w in W.ORDERED:
@@ -191,6 +256,7 @@ def main():
     fl = F.useful_flops(head)
     by = F.algorithmic_bytes(head)
     achieved = fl / (r["ms_per_launch_mean"] * 1e-3) / 1e12
+    traffic = measured_traffic()
     line = {
         "metric": METRIC,
         "value": round(fl / (r["ms_per_call"] * 1e-3) / 1e12, 3),
@@ -209,8 +275,11 @@ def main():
                    "separate_global": head.separate_global, "causal": head.causal},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "attn_fwd_kernel<bf16>",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None if traffic is None else int(traffic),
+                     "traffic_unit": "HBM bytes per call (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+                     "algorithmic_bytes": by,
+                     "kernel": "attn_fwd_kernel<bf16> + global_merge_kernel<bf16> (one call)",
                      "hbm_gbs_algorithmic": round(by / (r["ms_per_launch_mean"] * 1e-3) / 1e9, 1),
                      "hbm_peak_gbs": HBM_PEAK_GBS},
         "workloads": results,

@@ -14,6 +14,10 @@ Entry points (same names as the C ABI):
 * :func:`la_dilated_forward` — LongNet's mixture of dilated attentions.
 * :func:`la_attn_workspace_size`, :func:`la_dilated_workspace_size`,
   :func:`la_check_global_idx`, :func:`la_last_error`, :func:`la_version`.
+
+:func:`bind_attn` and :func:`bind_dilated` marshal a call once and return a
+:class:`BoundCall` that re-issues it cheaply (the host cost of argument
+checking is otherwise comparable to the kernels' own time).
 """
 from __future__ import annotations
 
@@ -161,20 +165,35 @@ def _workspace(nbytes: int, device, given: Optional[torch.Tensor]) -> Optional[t
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def la_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                    global_idx: Optional[torch.Tensor] = None, radius: int = 0,
-                    dilation: Optional[Sequence[int]] = None, causal: bool = False,
-                    rel_bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                    lse: Optional[torch.Tensor] = None, qg: Optional[torch.Tensor] = None,
-                    kg: Optional[torch.Tensor] = None, vg: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, stream=None,
-                    want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Band + global attention; returns ``(out, lse)``.
+class BoundCall:
+    """One forward call with its arguments already marshalled.
 
-    ``global_idx`` is a device int32 tensor of strictly increasing positions.
-    ``rel_bias`` is a device fp32 ``[H, 2k+1]`` table. ``out``, ``lse`` and the
-    workspace are allocated with torch when not given.
+    Built by :func:`bind_attn` / :func:`bind_dilated`; calling it re-issues the
+    same C call (same tensors, workspace and stream) with no Python-side
+    checks, for loops that repeat one call. The tensors it refers to are kept
+    alive by the object.
     """
+
+    def __init__(self, fn, args, keep, out, lse):
+        self._fn, self._args, self._keep = fn, args, keep
+        self.out, self.lse = out, lse
+
+    def __call__(self) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        st = self._fn(*self._args)
+        if st != LA_OK:
+            _check(st)
+        return self.out, self.lse
+
+
+def bind_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+              global_idx: Optional[torch.Tensor] = None, radius: int = 0,
+              dilation: Optional[Sequence[int]] = None, causal: bool = False,
+              rel_bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None, qg: Optional[torch.Tensor] = None,
+              kg: Optional[torch.Tensor] = None, vg: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, stream=None,
+              want_lse: bool = True) -> BoundCall:
+    """Validate and marshal a :func:`la_attn_forward` call without issuing it."""
     dims = _dims(q)
     for name, t in (("k", k), ("v", v)):
         _dev(t, q, name)
@@ -211,20 +230,37 @@ def la_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     ext = LaAttnExt(rk, _dev(qg, q, "qg") or None, _dev(kg, q, "kg") or None,
                     _dev(vg, q, "vg") or None, ws.data_ptr() if ws is not None else None,
                     ws.numel() if ws is not None else 0)
-    st = lib().la_attn_forward(ctypes.byref(dims), qptr, k.data_ptr(), v.data_ptr(), gptr or None,
-                               n_global, int(radius), dil, int(bool(causal)), rptr or None,
-                               out.data_ptr(), lse.data_ptr() if lse is not None else None,
-                               _stream(q, stream), ctypes.byref(ext))
-    _check(st)
-    return out, lse
+    args = (ctypes.byref(dims), qptr, k.data_ptr(), v.data_ptr(), gptr or None, n_global,
+            int(radius), dil, int(bool(causal)), rptr or None, out.data_ptr(),
+            lse.data_ptr() if lse is not None else None, _stream(q, stream), ctypes.byref(ext))
+    keep = (dims, ext, dil, q, k, v, global_idx, rel_bias, qg, kg, vg, ws)
+    return BoundCall(lib().la_attn_forward, args, keep, out, lse)
 
 
-def la_dilated_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                       seg_lens: Sequence[int], dil_rates: Sequence[int], causal: bool = True,
-                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None, stream=None,
-                       want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """LongNet dilated attention mixture; returns ``(out, lse)``."""
+def la_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    global_idx: Optional[torch.Tensor] = None, radius: int = 0,
+                    dilation: Optional[Sequence[int]] = None, causal: bool = False,
+                    rel_bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, qg: Optional[torch.Tensor] = None,
+                    kg: Optional[torch.Tensor] = None, vg: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None,
+                    want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Band + global attention; returns ``(out, lse)``.
+
+    ``global_idx`` is a device int32 tensor of strictly increasing positions.
+    ``rel_bias`` is a device fp32 ``[H, 2k+1]`` table. ``out``, ``lse`` and the
+    workspace are allocated with torch when not given.
+    """
+    return bind_attn(q, k, v, global_idx, radius, dilation, causal, rel_bias, out, lse, qg, kg,
+                     vg, workspace, stream, want_lse)()
+
+
+def bind_dilated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 seg_lens: Sequence[int], dil_rates: Sequence[int], causal: bool = True,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None,
+                 want_lse: bool = True) -> BoundCall:
+    """Validate and marshal a :func:`la_dilated_forward` call without issuing it."""
     dims = _dims(q)
     for name, t in (("k", k), ("v", v)):
         _dev(t, q, name)
@@ -241,12 +277,21 @@ def la_dilated_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     ext = LaDilatedExt(lse.data_ptr() if lse is not None else None,
                        ws.data_ptr() if ws is not None else None,
                        ws.numel() if ws is not None else 0)
-    st = lib().la_dilated_forward(ctypes.byref(dims), qptr, k.data_ptr(), v.data_ptr(),
-                                  _host_i32(seg_lens), _host_i32(dil_rates), len(seg_lens),
-                                  int(bool(causal)), out.data_ptr(), _stream(q, stream),
-                                  ctypes.byref(ext))
-    _check(st)
-    return out, lse
+    w_arr, r_arr = _host_i32(seg_lens), _host_i32(dil_rates)
+    args = (ctypes.byref(dims), qptr, k.data_ptr(), v.data_ptr(), w_arr, r_arr, len(seg_lens),
+            int(bool(causal)), out.data_ptr(), _stream(q, stream), ctypes.byref(ext))
+    keep = (dims, ext, w_arr, r_arr, q, k, v, ws)
+    return BoundCall(lib().la_dilated_forward, args, keep, out, lse)
+
+
+def la_dilated_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       seg_lens: Sequence[int], dil_rates: Sequence[int], causal: bool = True,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None,
+                       want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """LongNet dilated attention mixture; returns ``(out, lse)``."""
+    return bind_dilated(q, k, v, seg_lens, dil_rates, causal, out, lse, workspace, stream,
+                        want_lse)()
 
 
 def la_check_global_idx(global_idx: torch.Tensor, N: int, stream=None) -> bool:

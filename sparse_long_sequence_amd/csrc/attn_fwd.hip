@@ -1,11 +1,11 @@
 // attn_fwd.hip — band + global attention (Longformer / ETC) on gfx950.
 //
 // One launch holds two kinds of workgroups:
-//   * global-row workgroups (first in the grid), one per (batch, head, 64
-//     global rows, key chunk): each global row against a chunk of all keys,
+//   * global-row workgroups (first in the grid), one per (batch, head, query
+//     tile of global rows, key chunk): each global row against a chunk of all keys,
 //     written as a partial (normalised O, lse) to the workspace, merged by a
 //     second, small launch;
-//   * band workgroups, one per 64-row query tile of one residue class of one
+//   * band workgroups, one per query tile of one residue class of one
 //     (batch, head): the sliding-window key tiles (strided by the head's
 //     dilation), then the global-column tiles (keys of G outside the window).
 //
@@ -56,7 +56,7 @@ __device__ __forceinline__ void load_bias_table(typename TileTraits<T>::Smem& sm
 }
 
 // ---------------------------------------------------------------------------
-// band workgroup: 64 query rows of one residue class (positions c + d*t)
+// band workgroup: one query tile of one residue class (positions c + d*t)
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileTraits<T>::Smem& sm,
@@ -96,8 +96,12 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   const T* qb = reinterpret_cast<const T*>(a.q) + bh * head_elems;
   const T* kb = reinterpret_cast<const T*>(a.k) + bh * head_elems;
   const T* vb = reinterpret_cast<const T*>(a.v) + bh * head_elems;
-  const int32_t qi = TT::qrow(wave, lane);
-  const int32_t qpos = qbase + d * min(qi, qcount - 1);
+  int32_t qi[TT::kQB], qpos[TT::kQB];
+#pragma unroll
+  for (int b = 0; b < TT::kQB; ++b) {
+    qi[b] = TT::qrow(wave, lane, b);
+    qpos[b] = qbase + d * min(qi[b], qcount - 1);
+  }
   typename TT::Wave w;
   TT::load_q(w, qb, qpos, lane);
 
@@ -168,21 +172,24 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   }
 
   // epilogue: rows outside G (the global-row pass owns the rest)
-  const float l_tot = TT::row_sum(w.l);
-  if (qi < qcount) {
-    const bool is_g = g1 > g0 && sorted_contains(a.gidx + g0, g1 - g0, qpos);
-    if (!is_g) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      O* dst = reinterpret_cast<O*>(a.out) + bh * head_elems + (size_t)qpos * kD;
-      TT::store_row(dst, w, inv, lane);
-      if (a.lse && TT::row_leader(lane))
-        a.lse[(size_t)bh * N + qpos] = l_tot > 0.f ? (w.m + __log2f(l_tot)) * kLn2 : kNegInf;
+#pragma unroll
+  for (int b = 0; b < TT::kQB; ++b) {
+    const float l_tot = TT::row_sum(w.l[b]);
+    if (qi[b] < qcount) {
+      const bool is_g = g1 > g0 && sorted_contains(a.gidx + g0, g1 - g0, qpos[b]);
+      if (!is_g) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        O* dst = reinterpret_cast<O*>(a.out) + bh * head_elems + (size_t)qpos[b] * kD;
+        TT::store_row(dst, w, b, inv, lane);
+        if (a.lse && TT::row_leader(lane))
+          a.lse[(size_t)bh * N + qpos[b]] = l_tot > 0.f ? (w.m[b] + __log2f(l_tot)) * kLn2 : kNegInf;
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// global-row workgroup: 64 global rows against one chunk of keys
+// global-row workgroup: one tile of global rows against one chunk of keys
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
@@ -215,8 +222,12 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   const T* qb = reinterpret_cast<const T*>(a.qg) + bh * head_elems;
   const T* kb = reinterpret_cast<const T*>(a.kg) + bh * head_elems;
   const T* vb = reinterpret_cast<const T*>(a.vg) + bh * head_elems;
-  const int32_t qi = TT::qrow(wave, lane);
-  const int32_t qpos = qidx[min(qi, qcount - 1)];
+  int32_t qi[TT::kQB], qpos[TT::kQB];
+#pragma unroll
+  for (int b = 0; b < TT::kQB; ++b) {
+    qi[b] = TT::qrow(wave, lane, b);
+    qpos[b] = qidx[min(qi[b], qcount - 1)];
+  }
   typename TT::Wave w;
   TT::load_q(w, qb, qpos, lane);
   auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
@@ -229,17 +240,23 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   };
   const BiasRule br = {want_bias ? sm.bias : nullptr, a.rel_k, 1};
   run_tiles<T, false>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, a.scale_log2);
-  const float l_tot = TT::row_sum(w.l);
-  if (qi < qcount) {
-    const size_t prow = ((size_t)bh * a.n_global + gq * kTQ + qi) * a.n_chunks + chunk;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    TT::store_row_f32(a.ws_o + prow * kD, w, inv, lane);
-    if (TT::row_leader(lane)) a.ws_lse[prow] = l_tot > 0.f ? (w.m + __log2f(l_tot)) * kLn2 : kNegInf;
+#pragma unroll
+  for (int b = 0; b < TT::kQB; ++b) {
+    const float l_tot = TT::row_sum(w.l[b]);
+    if (qi[b] < qcount) {
+      const size_t prow = ((size_t)bh * a.n_global + gq * kTQ + qi[b]) * a.n_chunks + chunk;
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      TT::store_row_f32(a.ws_o + prow * kD, w, b, inv, lane);
+      if (TT::row_leader(lane))
+        a.ws_lse[prow] = l_tot > 0.f ? (w.m[b] + __log2f(l_tot)) * kLn2 : kNegInf;
+    }
   }
 }
 
+// Two waves per SIMD: the register budget is 256 per lane (VGPR + AGPR).
 template <typename T>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(TileTraits<T>::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fwd_kernel(AttnArgs a) {
   __shared__ typename TileTraits<T>::Smem sm;
   const int32_t wg = xcd_logical_block((int32_t)blockIdx.x, a.n_glob_wg + a.n_band_wg);
   if (wg < 0) return;
@@ -289,9 +306,11 @@ hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   grid = (grid + kXcds - 1) / kXcds * kXcds;  // padded for the XCD remap
   if (dtype == 1)
-    hipLaunchKernelGGL(attn_fwd_kernel<bf16>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_fwd_kernel<bf16>, dim3((uint32_t)grid),
+                       dim3(TileTraits<bf16>::kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<float>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_fwd_kernel<float>, dim3((uint32_t)grid),
+                       dim3(TileTraits<float>::kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_global == 0) return e;
   const uint32_t blocks = (uint32_t)(((int64_t)a.B * a.H * a.n_global + 3) / 4);

@@ -16,7 +16,8 @@
 
 namespace la {
 
-__global__ __launch_bounds__(kThreads) void dilated_pair_kernel(DilArgs a) {
+__global__ __launch_bounds__(TileTraits<bf16>::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void dilated_pair_kernel(DilArgs a) {
   using TT = TileTraits<bf16>;
   __shared__ TT::Smem sm;
   constexpr int32_t kTQ = TT::kTQ;
@@ -47,8 +48,12 @@ __global__ __launch_bounds__(kThreads) void dilated_pair_kernel(DilArgs a) {
   const bf16* kb = reinterpret_cast<const bf16*>(a.k) + bh * head_elems;
   const bf16* vb = reinterpret_cast<const bf16*>(a.v) + bh * head_elems;
   const int32_t base = sigma + s;
-  const int32_t qi = TT::qrow(wave, lane);
-  const int32_t qpos = base + r * (t0 + min(qi, qcount - 1));
+  int32_t qi[TT::kQB], qpos[TT::kQB];
+#pragma unroll
+  for (int b = 0; b < TT::kQB; ++b) {
+    qi[b] = TT::qrow(wave, lane, b);
+    qpos[b] = base + r * (t0 + min(qi[b], qcount - 1));
+  }
   TT::Wave wv;
   TT::load_q(wv, qb, qpos, lane);
   const int32_t hi = a.causal ? t0 + qcount - 1 : n_rows - 1;
@@ -65,12 +70,16 @@ __global__ __launch_bounds__(kThreads) void dilated_pair_kernel(DilArgs a) {
   const BiasRule br = {nullptr, 0, 0};
   const GlobInfo gi = {kGlobNone, nullptr, 0};
   run_tiles<bf16, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, a.scale_log2);
-  const float l_tot = TT::row_sum(wv.l);
-  if (qi < qcount) {
-    const int64_t prow = a.row_off[k] + ((int64_t)bh * nseg + seg) * a.seg_rows[k] + t0 + qi;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    TT::store_row_f32(a.ws_o + prow * kD, wv, inv, lane);
-    if (TT::row_leader(lane)) a.ws_lse[prow] = l_tot > 0.f ? (wv.m + __log2f(l_tot)) * kLn2 : kNegInf;
+#pragma unroll
+  for (int b = 0; b < TT::kQB; ++b) {
+    const float l_tot = TT::row_sum(wv.l[b]);
+    if (qi[b] < qcount) {
+      const int64_t prow = a.row_off[k] + ((int64_t)bh * nseg + seg) * a.seg_rows[k] + t0 + qi[b];
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      TT::store_row_f32(a.ws_o + prow * kD, wv, b, inv, lane);
+      if (TT::row_leader(lane))
+        a.ws_lse[prow] = l_tot > 0.f ? (wv.m[b] + __log2f(l_tot)) * kLn2 : kNegInf;
+    }
   }
 }
 
@@ -113,7 +122,7 @@ __global__ __launch_bounds__(256) void dilated_combine_kernel(DilArgs a) {
 hipError_t launch_dilated(const DilArgs& a, hipStream_t stream) {
   const int64_t grid = (a.wg_start[a.n_pairs] + kXcds - 1) / kXcds * kXcds;  // XCD remap padding
   if (grid > 0) {
-    hipLaunchKernelGGL(dilated_pair_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(dilated_pair_kernel, dim3((uint32_t)grid), dim3(TileTraits<bf16>::kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -1,19 +1,21 @@
 // tile_core.h — the attention tile engine shared by every kernel of the library.
 //
-// One workgroup = 4 wave64s = one tile of query rows (128 for bf16, 64 for
-// fp32). Keys arrive in tiles of 64 rows staged through LDS (double-buffered,
-// register prefetch of the next tile). Each wave owns kQW query rows and
-// computes, per key tile,
+// One workgroup = one tile of query rows (128 for bf16, 64 for fp32). Keys
+// arrive in tiles of 64 rows staged through LDS (double-buffered, register
+// prefetch of the next tile). Each wave owns kQW query rows, held as kQB
+// blocks of 32 (bf16) or 16 (fp32) rows, and computes, per key sub-tile,
 //
-//   S^T (64 keys x kQW queries) = K_tile . Q^T      (MFMA, fp32 accumulate)
-//   online softmax on S^T in the log2 domain        (registers, fp32)
-//   O^T (64 d x kQW queries)   += V_tile^T . P^T    (MFMA, fp32 accumulate)
+//   S^T (keys x queries) = K_sub . Q^T                (MFMA, fp32 accumulate)
+//   online softmax on S^T in the log2 domain          (registers, fp32)
+//   O^T (64 d x queries) += V_sub^T . P^T             (MFMA, fp32 accumulate)
 //
 // The S^T orientation puts one query column per lane (its other keys sit in
 // the lane 32 apart for bf16, in the lanes 16/32/48 apart for fp32), so the
 // row max needs one (bf16) or two (fp32) cross-lane swaps and the row sum none
 // until the end. The same lane layout is exactly the B operand of the PV
 // product (after a fixed permutation of the key order, applied to V^T too).
+// In the bf16 engine every K and V^T fragment read from LDS feeds the MFMAs of
+// both query blocks of the wave.
 //
 // MFMA operand layouts used here (lane l; measured on gfx950):
 //   v_mfma_f32_32x32x16_bf16: A[m = l%32][k = 8h..8h+7], B[k = 8h..8h+7][n = l%32],
@@ -42,18 +44,16 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
 constexpr int kTK = 64;       // keys per key tile
 constexpr int kD = 64;        // head dimension
-constexpr int kThreads = 256; // 4 waves
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kInvScale = 8.0f;  // sqrt(kD): the bias table is stored in q.k units
 constexpr int kGMaskWords = 256;   // LDS bitmap of global positions: 8192 key rows
 constexpr int32_t kFar = 0x3fffffff;
 
-// LDS row pitches (elements). Padding keeps the MFMA operand reads free of
-// most bank conflicts.
-constexpr int kKPitchBf16 = 72;  // K tile [key][d], 144 B rows
-constexpr int kVPitchBf16 = 68;  // V^T tile [d][key], 136 B rows
-constexpr int kPitchF32 = 68;    // fp32 K and V tiles [key][d], 272 B rows
+// LDS row pitches (elements). 144-byte rows put the 16-byte operand reads of
+// 8 consecutive rows on disjoint banks.
+constexpr int kPitchBf16 = 72;  // K tile [key][d] and V^T tile [d][key]
+constexpr int kPitchF32 = 68;   // fp32 K and V tiles [key][d], 272 B rows
 
 // fp32 -> bf16, round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -61,6 +61,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   v[0] = (__bf16)lo;
   v[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc + lo + hi of a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t pk, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, acc, false);
 }
 
 // max / sum with the lane 32 (resp. 16) apart: gfx950 v_permlane32_swap and
@@ -164,47 +170,62 @@ struct KeyMeta {
 
 // Per-thread element offsets of a full strided tile (stride fixed per loop).
 struct FetchPlan {
-  int32_t ok, oa, ob;  // K row chunk, V row chunks of the key pair
+  int32_t ok;  // this thread's K chunk
+  int32_t ov;  // this thread's first V chunk
+  int32_t rs;  // elements between consecutive key rows
 };
 
 template <typename T>
 struct TileTraits;
 
 // ---------------------------------------------------------------------------
-// bf16 engine: 32 queries per wave, v_mfma_f32_32x32x16_bf16
+// bf16 engine: 2 waves x 64 queries, v_mfma_f32_32x32x16_bf16
 // ---------------------------------------------------------------------------
 template <>
 struct TileTraits<bf16> {
-  static constexpr int kQW = 32;        // query rows per wave
-  static constexpr int kTQ = 4 * kQW;   // query rows per workgroup
-  static constexpr int kNS = 32;        // scores per lane per key tile
+  static constexpr int kWaves = 2;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kQB = 2;              // 32-row query blocks per wave
+  static constexpr int kQW = 32 * kQB;       // query rows per wave
+  static constexpr int kTQ = kWaves * kQW;   // query rows per workgroup
+  static constexpr int kSub = 2;             // key sub-tiles of 32 keys
+  static constexpr int kSubKeys = kTK / kSub;
+  static constexpr int kNS = 16;             // scores per lane, query block and sub-tile
+  static constexpr int kRowsPerBlock = 32;   // lanes 0..31 hold the block's rows in order
 
-  // 16-byte alignment lets the operand reads use ds_read_b128 / ds_read_b64.
+  // V^T rows hold each group of 16 keys in the order 0-3, 8-11, 4-7, 12-15,
+  // so that the 8 keys one lane feeds to a PV MFMA step are one 16-byte read.
+  // 16-byte alignment lets the operand reads use ds_read_b128.
   struct __attribute__((aligned(16))) Smem {
-    alignas(16) bf16 k[2][kTK][kKPitchBf16];
-    alignas(16) bf16 vt[2][kD][kVPitchBf16];
+    alignas(16) bf16 k[2][kTK][kPitchBf16];
+    alignas(16) bf16 vt[2][kD][kPitchBf16];
     alignas(16) int32_t kpos[2][kTK];
     alignas(16) float bias[64];
     alignas(16) uint32_t gmask[kGMaskWords];
     alignas(16) uint8_t kglob[2][kTK];
   };
   struct Prefetch {
-    u32x4 k0, k1, v0, v1;
+    u32x4 k[4];  // half a K row (32 d)
+    u32x4 v[4];  // 8 d of 4 consecutive V rows
     KeyMeta meta;
   };
   struct Wave {
-    bf16x8 qf[4];
-    f32x16 o[2];
-    float m;  // running max, log2 domain
-    float l;  // this lane's share of the running sum
+    bf16x8 qf[kQB][4];
+    f32x16 o[kQB][2];
+    float m[kQB];  // running max, log2 domain
+    float l[kQB];  // this lane's share of the running sum
+  };
+  // P of one sub-tile as bf16, the B operands of the two PV MFMA steps.
+  struct PTile {
+    u32x4 p[kQB][2];
   };
 
-  static __device__ __forceinline__ int32_t qrow(int32_t wave, int32_t lane) {
-    return kQW * wave + (lane & 31);
+  static __device__ __forceinline__ int32_t qrow(int32_t wave, int32_t lane, int qb) {
+    return kQW * wave + 32 * qb + (lane & 31);
   }
-  // Key row of score element r: a constant part and a lane part.
-  static __device__ __forceinline__ constexpr int32_t key_const(int r) {
-    return 32 * (r >> 4) + 8 * ((r >> 2) & 3) + (r & 3);
+  // Key row of score element r of sub-tile sb: a constant part and a lane part.
+  static __device__ __forceinline__ constexpr int32_t key_const(int sb, int r) {
+    return 32 * sb + 8 * (r >> 2) + (r & 3);
   }
   static __device__ __forceinline__ int32_t key_lane(int32_t lane) { return 4 * (lane >> 5); }
   static __device__ __forceinline__ float row_max(float x) { return xor32_max(x); }
@@ -212,11 +233,13 @@ struct TileTraits<bf16> {
   // one lane per query row writes the row's scalars
   static __device__ __forceinline__ bool row_leader(int32_t lane) { return lane < 32; }
 
+  // K: thread t loads half (t & 1) of key row t >> 1.
+  // V: thread t loads d chunk t >> 4 (8 d) of the key rows 4(t & 15) + 0..3.
   static __device__ __forceinline__ FetchPlan plan(int32_t stride, int32_t tid) {
     FetchPlan p;
-    p.ok = (tid >> 2) * stride * kD + 16 * (tid & 3);
-    p.oa = 2 * (tid >> 3) * stride * kD + 8 * (tid & 7);
-    p.ob = p.oa + stride * kD;
+    p.rs = stride * kD;
+    p.ok = (tid >> 1) * p.rs + 32 * (tid & 1);
+    p.ov = 4 * (tid & 15) * p.rs + 8 * (tid >> 4);
     return p;
   }
 
@@ -228,22 +251,24 @@ struct TileTraits<bf16> {
                                                const KeyTile& kt, const FetchPlan& fp,
                                                int32_t tid) {
     const int32_t last = kt.count - 1;
-    const bf16 *pk, *pa, *pb;
+    const bf16* pk;
+    const bf16* pv[4];
     if (!GATHER && kt.count == kTK) {
       const size_t b0 = (size_t)kt.base * kD;
       pk = kb + b0 + fp.ok;
-      pa = vb + b0 + fp.oa;
-      pb = vb + b0 + fp.ob;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) pv[x] = vb + b0 + fp.ov + x * fp.rs;
     } else {
-      pk = kb + (size_t)key_pos<GATHER>(kt, min(tid >> 2, last)) * kD + 16 * (tid & 3);
-      pa = vb + (size_t)key_pos<GATHER>(kt, min(2 * (tid >> 3), last)) * kD + 8 * (tid & 7);
-      pb = vb + (size_t)key_pos<GATHER>(kt, min(2 * (tid >> 3) + 1, last)) * kD + 8 * (tid & 7);
+      pk = kb + (size_t)key_pos<GATHER>(kt, min(tid >> 1, last)) * kD + 32 * (tid & 1);
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        pv[x] = vb + (size_t)key_pos<GATHER>(kt, min(4 * (tid & 15) + x, last)) * kD + 8 * (tid >> 4);
     }
     const u32x4* ks = reinterpret_cast<const u32x4*>(pk);
-    pf.k0 = ks[0];
-    pf.k1 = ks[1];
-    pf.v0 = *reinterpret_cast<const u32x4*>(pa);
-    pf.v1 = *reinterpret_cast<const u32x4*>(pb);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) pf.k[x] = ks[x];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) pf.v[x] = *reinterpret_cast<const u32x4*>(pv[x]);
     if (tid < kTK) {
       pf.meta.pos = key_pos<GATHER>(kt, min(tid, last));
       pf.meta.gbit = kt.gbit0 + min(tid, last);
@@ -253,85 +278,116 @@ struct TileTraits<bf16> {
   // Move a prefetched tile into LDS buffer `buf` (V transposed to [d][key]).
   static __device__ __forceinline__ void stage(Smem& sm, int32_t buf, const Prefetch& pf,
                                                int32_t tid) {
-    const int32_t kk = tid >> 2, ck = tid & 3;
-    *reinterpret_cast<u32x4*>(&sm.k[buf][kk][16 * ck]) = pf.k0;
-    *reinterpret_cast<u32x4*>(&sm.k[buf][kk][16 * ck + 8]) = pf.k1;
-    const int32_t vp = tid >> 3, cv = tid & 7;
+    const int32_t kk = tid >> 1, hk = tid & 1;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      *reinterpret_cast<u32x4*>(&sm.k[buf][kk][32 * hk + 8 * x]) = pf.k[x];
+    // key quad kq = keys 4kq..4kq+3 = local quad lq of 16-key group g
+    const int32_t kq = tid & 15, dc = tid >> 4;
+    const int32_t lq = kq & 3;
+    const int32_t col = 16 * (kq >> 2) + 4 * (((lq & 1) << 1) | (lq >> 1));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      // two bf16 of one key share a dword; pair keys 2vp and 2vp+1
-      const uint32_t a = pf.v0[e], b = pf.v1[e];
-      *reinterpret_cast<uint32_t*>(&sm.vt[buf][8 * cv + 2 * e][2 * vp]) =
-          __builtin_amdgcn_perm(b, a, 0x05040100u);
-      *reinterpret_cast<uint32_t*>(&sm.vt[buf][8 * cv + 2 * e + 1][2 * vp]) =
-          __builtin_amdgcn_perm(b, a, 0x07060302u);
+      // dword e of each row holds d = 8dc + 2e (low half) and 8dc + 2e + 1 (high half)
+      u32x2 lo, hi;
+      lo[0] = __builtin_amdgcn_perm(pf.v[1][e], pf.v[0][e], 0x05040100u);
+      lo[1] = __builtin_amdgcn_perm(pf.v[3][e], pf.v[2][e], 0x05040100u);
+      hi[0] = __builtin_amdgcn_perm(pf.v[1][e], pf.v[0][e], 0x07060302u);
+      hi[1] = __builtin_amdgcn_perm(pf.v[3][e], pf.v[2][e], 0x07060302u);
+      *reinterpret_cast<u32x2*>(&sm.vt[buf][8 * dc + 2 * e][col]) = lo;
+      *reinterpret_cast<u32x2*>(&sm.vt[buf][8 * dc + 2 * e + 1][col]) = hi;
     }
   }
 
-  static __device__ __forceinline__ void load_q(Wave& w, const bf16* qb, int32_t qrow_pos,
+  static __device__ __forceinline__ void load_q(Wave& w, const bf16* qb, const int32_t* qpos,
                                                 int32_t lane) {
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(qb + (size_t)qrow_pos * kD + 8 * (lane >> 5));
-#pragma unroll
-    for (int st = 0; st < 4; ++st) w.qf[st] = src[2 * st];
     const f32x16 zf = {};
-    w.o[0] = zf;
-    w.o[1] = zf;
-    w.m = kNegInf;
-    w.l = 0.f;
+#pragma unroll
+    for (int b = 0; b < kQB; ++b) {
+      const bf16x8* src =
+          reinterpret_cast<const bf16x8*>(qb + (size_t)qpos[b] * kD + 8 * (lane >> 5));
+#pragma unroll
+      for (int st = 0; st < 4; ++st) w.qf[b][st] = src[2 * st];
+      w.o[b][0] = zf;
+      w.o[b][1] = zf;
+      w.m[b] = kNegInf;
+      w.l[b] = 0.f;
+    }
   }
 
-  // S^T for this wave: s[16kb + e] = K[key_const(16kb+e) + key_lane] . Q[qrow].
+  // S^T of sub-tile sb for the query blocks in LIVE (bit b = block b):
+  // s[b][e] = K[key_const(sb, e) + key_lane] . Q[qrow(b)].
+  template <int LIVE>
+  static __device__ __forceinline__ void scores_of(const Smem& sm, int32_t buf, const Wave& w,
+                                                   int32_t lane, int sb, float s[kQB][kNS]) {
+    const int32_t r = lane & 31, h = lane >> 5;
+    f32x16 acc[kQB];
+#pragma unroll
+    for (int b = 0; b < kQB; ++b) acc[b] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * sb + r][16 * st + 8 * h]);
+      static_assert(kQB == 2, "two query blocks per wave");
+      if constexpr ((LIVE & 1) != 0)
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[0][st], acc[0], 0, 0, 0);
+      if constexpr ((LIVE & 2) != 0)
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[1][st], acc[1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < kQB; ++b)
+#pragma unroll
+      for (int e = 0; e < kNS; ++e) s[b][e] = acc[b][e];
+  }
   static __device__ __forceinline__ void scores(const Smem& sm, int32_t buf, const Wave& w,
-                                                int32_t lane, float s[kNS]) {
-    const int32_t r = lane & 31, h = lane >> 5;
+                                                int32_t lane, int sb, float s[kQB][kNS],
+                                                int32_t live) {
+    if (live == 3) scores_of<3>(sm, buf, w, lane, sb, s);
+    else if (live == 1) scores_of<1>(sm, buf, w, lane, sb, s);
+    else scores_of<2>(sm, buf, w, lane, sb, s);
+  }
+
+  // Query block b: p = 2^(s * c + nm) rounded to bf16; the row sum adds exactly
+  // these values.
+  static __device__ __forceinline__ void softmax_p(const float s[kNS], float nm, float c,
+                                                   PTile& P, int b, float& l) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 acc = {};
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * kb + r][16 * st + 8 * h]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[st], acc, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * t + 2 * i], c, nm));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * t + 2 * i + 1], c, nm));
+        const uint32_t pk = pack_bf16x2(p0, p1);
+        P.p[b][t][i] = pk;
+        l = add_bf16x2(pk, l);
       }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[16 * kb + e] = acc[e];
     }
   }
 
-  // O^T += V^T . P^T with P in p[] (already exponentiated). MFMA step (kb, t)
-  // takes the 16 keys 32kb + 16t + [0, 16): this lane's p[16kb + 8t + 0..7].
+  // O^T += V^T . P^T over sub-tile sb for query block b. MFMA step t takes the
+  // keys 32sb + 16t + [0, 16): in k-slot 8h + e the key
+  // 32sb + 16t + 8(e >> 2) + 4h + (e & 3), i.e. this lane's score elements 8t + e.
   static __device__ __forceinline__ void accumulate(const Smem& sm, int32_t buf, Wave& w,
-                                                    int32_t lane, const float p[kNS]) {
+                                                    int32_t lane, int sb, const PTile& P, int b) {
     const int32_t r = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int t = 0; t < 2; ++t) {
+      const int c0 = 16 * (2 * sb + t) + 8 * h;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int e0 = 16 * kb + 8 * t;
-        u32x4 pb;
-        pb[0] = pack_bf16x2(p[e0 + 0], p[e0 + 1]);
-        pb[1] = pack_bf16x2(p[e0 + 2], p[e0 + 3]);
-        pb[2] = pack_bf16x2(p[e0 + 4], p[e0 + 5]);
-        pb[3] = pack_bf16x2(p[e0 + 6], p[e0 + 7]);
-        const bf16x8 b = __builtin_bit_cast(bf16x8, pb);
-        const int c0 = 32 * kb + 16 * t + 4 * h;
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const u32x2 v0 = *reinterpret_cast<const u32x2*>(&sm.vt[buf][32 * db + r][c0]);
-          const u32x2 v1 = *reinterpret_cast<const u32x2*>(&sm.vt[buf][32 * db + r][c0 + 8]);
-          u32x4 av;
-          av[0] = v0[0];
-          av[1] = v0[1];
-          av[2] = v1[0];
-          av[3] = v1[1];
-          w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), b,
-                                                             w.o[db], 0, 0, 0);
-        }
+      for (int db = 0; db < 2; ++db) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[buf][32 * db + r][c0]);
+        w.o[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, __builtin_bit_cast(bf16x8, P.p[b][t]), w.o[b][db], 0, 0, 0);
       }
     }
   }
 
-  // Output row of this lane's query; the lane holds d = 32db + 8j + 4h + i.
-  static __device__ __forceinline__ void store_row(bf16* dst, const Wave& w, float inv,
+  static __device__ __forceinline__ void scale_acc(Wave& w, int b, float alpha) {
+    w.o[b][0] *= alpha;
+    w.o[b][1] *= alpha;
+  }
+
+  // Output row of query block b; the lane holds d = 32db + 8j + 4h + i.
+  static __device__ __forceinline__ void store_row(bf16* dst, const Wave& w, int b, float inv,
                                                    int32_t lane) {
     const int32_t h = lane >> 5;
 #pragma unroll
@@ -339,14 +395,14 @@ struct TileTraits<bf16> {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         u32x2 pk;
-        pk[0] = pack_bf16x2(w.o[db][4 * j + 0] * inv, w.o[db][4 * j + 1] * inv);
-        pk[1] = pack_bf16x2(w.o[db][4 * j + 2] * inv, w.o[db][4 * j + 3] * inv);
+        pk[0] = pack_bf16x2(w.o[b][db][4 * j + 0] * inv, w.o[b][db][4 * j + 1] * inv);
+        pk[1] = pack_bf16x2(w.o[b][db][4 * j + 2] * inv, w.o[b][db][4 * j + 3] * inv);
         *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * j + 4 * h) = pk;
       }
     }
   }
   // Same, fp32 (partials of split computations).
-  static __device__ __forceinline__ void store_row_f32(float* dst, const Wave& w, float inv,
+  static __device__ __forceinline__ void store_row_f32(float* dst, const Wave& w, int b, float inv,
                                                        int32_t lane) {
     const int32_t h = lane >> 5;
 #pragma unroll
@@ -354,7 +410,7 @@ struct TileTraits<bf16> {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f32x4 x;
-        for (int i = 0; i < 4; ++i) x[i] = w.o[db][4 * j + i] * inv;
+        for (int i = 0; i < 4; ++i) x[i] = w.o[b][db][4 * j + i] * inv;
         *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * j + 4 * h) = x;
       }
     }
@@ -362,13 +418,19 @@ struct TileTraits<bf16> {
 };
 
 // ---------------------------------------------------------------------------
-// fp32 engine: 16 queries per wave, fp32 MFMA; P kept in fp32
+// fp32 engine: 4 waves x 16 queries, fp32 MFMA; P kept in fp32
 // ---------------------------------------------------------------------------
 template <>
 struct TileTraits<float> {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kQB = 1;
   static constexpr int kQW = 16;
-  static constexpr int kTQ = 4 * kQW;
+  static constexpr int kTQ = kWaves * kQW;
+  static constexpr int kSub = 1;
+  static constexpr int kSubKeys = kTK / kSub;
   static constexpr int kNS = 16;
+  static constexpr int kRowsPerBlock = 16;
 
   struct __attribute__((aligned(16))) Smem {
     alignas(16) float k[2][kTK][kPitchF32];
@@ -385,14 +447,17 @@ struct TileTraits<float> {
   struct Wave {
     float qf[16];
     f32x4 o[4];
-    float m;
-    float l;
+    float m[kQB];
+    float l[kQB];
+  };
+  struct PTile {
+    float p[kNS];
   };
 
-  static __device__ __forceinline__ int32_t qrow(int32_t wave, int32_t lane) {
+  static __device__ __forceinline__ int32_t qrow(int32_t wave, int32_t lane, int) {
     return kQW * wave + (lane & 15);
   }
-  static __device__ __forceinline__ constexpr int32_t key_const(int r) {
+  static __device__ __forceinline__ constexpr int32_t key_const(int, int r) {
     return 16 * (r >> 2) + (r & 3);
   }
   static __device__ __forceinline__ int32_t key_lane(int32_t lane) { return 4 * (lane >> 4); }
@@ -402,9 +467,9 @@ struct TileTraits<float> {
 
   static __device__ __forceinline__ FetchPlan plan(int32_t stride, int32_t tid) {
     FetchPlan p;
-    p.ok = (tid >> 2) * stride * kD + 16 * (tid & 3);
-    p.oa = p.ok;
-    p.ob = p.ok;
+    p.rs = stride * kD;
+    p.ok = (tid >> 2) * p.rs + 16 * (tid & 3);
+    p.ov = p.ok;
     return p;
   }
 
@@ -443,19 +508,19 @@ struct TileTraits<float> {
 
   // The contraction over d runs in the order d = 16g + step, so each lane
   // reads 16 contiguous floats of its Q row and of each K row.
-  static __device__ __forceinline__ void load_q(Wave& w, const float* qb, int32_t qrow_pos,
+  static __device__ __forceinline__ void load_q(Wave& w, const float* qb, const int32_t* qpos,
                                                 int32_t lane) {
-    const float* src = qb + (size_t)qrow_pos * kD + 16 * (lane >> 4);
+    const float* src = qb + (size_t)qpos[0] * kD + 16 * (lane >> 4);
 #pragma unroll
     for (int x = 0; x < 16; ++x) w.qf[x] = src[x];
     const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < 4; ++i) w.o[i] = zf;
-    w.m = kNegInf;
-    w.l = 0.f;
+    w.m[0] = kNegInf;
+    w.l[0] = 0.f;
   }
 
   static __device__ __forceinline__ void scores(const Smem& sm, int32_t buf, const Wave& w,
-                                                int32_t lane, float s[kNS]) {
+                                                int32_t lane, int, float s[kQB][kNS], int32_t) {
     const int32_t r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -465,13 +530,24 @@ struct TileTraits<float> {
       for (int st = 0; st < 16; ++st)
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(krow[st], w.qf[st], acc, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[4 * kb + i] = acc[i];
+      for (int i = 0; i < 4; ++i) s[0][4 * kb + i] = acc[i];
     }
+  }
+
+  static __device__ __forceinline__ void softmax_p(const float s[kNS], float nm, float c,
+                                                   PTile& P, int, float& l) {
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < kNS; ++r) {
+      P.p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, nm));
+      rs += P.p[r];
+    }
+    l += rs;
   }
 
   // k-slot g of step (kb, i) is key 16kb + 4g + i: A = V[key][d = 16db + r].
   static __device__ __forceinline__ void accumulate(const Smem& sm, int32_t buf, Wave& w,
-                                                    int32_t lane, const float p[kNS]) {
+                                                    int32_t lane, int, const PTile& P, int) {
     const int32_t r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -480,12 +556,17 @@ struct TileTraits<float> {
         const float* vrow = &sm.v[buf][16 * kb + 4 * g + i][r];
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-          w.o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[16 * db], p[4 * kb + i], w.o[db], 0, 0, 0);
+          w.o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[16 * db], P.p[4 * kb + i], w.o[db], 0, 0, 0);
       }
     }
   }
 
-  static __device__ __forceinline__ void store_row(float* dst, const Wave& w, float inv,
+  static __device__ __forceinline__ void scale_acc(Wave& w, int, float alpha) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) w.o[db] *= alpha;
+  }
+
+  static __device__ __forceinline__ void store_row(float* dst, const Wave& w, int, float inv,
                                                    int32_t lane) {
     const int32_t g = lane >> 4;
 #pragma unroll
@@ -494,9 +575,9 @@ struct TileTraits<float> {
       *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = x;
     }
   }
-  static __device__ __forceinline__ void store_row_f32(float* dst, const Wave& w, float inv,
+  static __device__ __forceinline__ void store_row_f32(float* dst, const Wave& w, int b, float inv,
                                                        int32_t lane) {
-    store_row(dst, w, inv, lane);
+    store_row(dst, w, b, inv, lane);
   }
 };
 
@@ -523,9 +604,10 @@ template <typename T>
 __device__ __forceinline__ void build_gmask(typename TileTraits<T>::Smem& sm, const int32_t* gidx,
                                             int32_t n_global, int32_t base, int32_t stride,
                                             int32_t count, int32_t tid) {
-  for (int32_t x = tid; x < kGMaskWords; x += kThreads) sm.gmask[x] = 0u;
+  constexpr int32_t nt = TileTraits<T>::kThreads;
+  for (int32_t x = tid; x < kGMaskWords; x += nt) sm.gmask[x] = 0u;
   __syncthreads();
-  for (int32_t x = tid; x < n_global; x += kThreads) {
+  for (int32_t x = tid; x < n_global; x += nt) {
     const int32_t dl = gidx[x] - base;
     if (dl >= 0 && dl % stride == 0 && dl / stride < count) {
       const int32_t u = dl / stride;
@@ -539,13 +621,13 @@ __device__ __forceinline__ void build_gmask(typename TileTraits<T>::Smem& sm, co
 // is pre-multiplied by sqrt(D) so that it adds in the same units.
 template <typename T>
 __device__ __forceinline__ void add_bias(float* s, const typename TileTraits<T>::Smem& sm,
-                                         int32_t buf, const BiasRule& br, int32_t qpos,
+                                         int32_t buf, const BiasRule& br, int sb, int32_t qpos,
                                          int32_t lane) {
   using TT = TileTraits<T>;
   const int32_t kl = TT::key_lane(lane);
 #pragma unroll
   for (int r = 0; r < TT::kNS; ++r) {
-    const int32_t kj = TT::key_const(r) + kl;
+    const int32_t kj = TT::key_const(sb, r) + kl;
     const bool same = (sm.kglob[buf][kj] != 0) == (br.key_global_is_same_kind != 0);
     const int32_t dl = min(max(sm.kpos[buf][kj] - qpos, -br.k), br.k);
     const float b = br.tab[dl + br.k];  // always read: keeps the loop branch-free
@@ -557,7 +639,7 @@ __device__ __forceinline__ void add_bias(float* s, const typename TileTraits<T>:
 // branch per tile; the per-element tests are a few integer ops.
 template <typename T>
 __device__ __forceinline__ void mask_tile(float* s, const typename TileTraits<T>::Smem& sm,
-                                          int32_t buf, const MaskRule& mr, int32_t kcount,
+                                          int32_t buf, const MaskRule& mr, int sb, int32_t kcount,
                                           int32_t qi, int32_t qpos, int32_t lane) {
   using TT = TileTraits<T>;
   const int32_t kl = TT::key_lane(lane);
@@ -565,15 +647,15 @@ __device__ __forceinline__ void mask_tile(float* s, const typename TileTraits<T>
     const int32_t base = kl - (mr.use_qpos ? qpos : qi) - mr.ref_off;
 #pragma unroll
     for (int r = 0; r < TT::kNS; ++r) {
-      const int32_t kj = TT::key_const(r) + kl;
-      const int32_t dlt = base + TT::key_const(r);
+      const int32_t kj = TT::key_const(sb, r) + kl;
+      const int32_t dlt = base + TT::key_const(sb, r);
       const bool ok = (kj < kcount) & (dlt >= mr.lo) & (dlt <= mr.hi);
       s[r] = ok ? s[r] : kNegInf;
     }
   } else {  // kGlobCol
 #pragma unroll
     for (int r = 0; r < TT::kNS; ++r) {
-      const int32_t kj = TT::key_const(r) + kl;
+      const int32_t kj = TT::key_const(sb, r) + kl;
       const int32_t dl = sm.kpos[buf][kj] - qpos;
       const bool in_band = (dl % mr.dil == 0) & (dl >= -mr.radius * mr.dil) &
                            (dl <= mr.radius * mr.dil) & (!mr.causal | (dl <= 0));
@@ -583,59 +665,87 @@ __device__ __forceinline__ void mask_tile(float* s, const typename TileTraits<T>
   }
 }
 
-// The running max moves only when a row's tile max exceeds it by more than
-// this many log2 units; p = 2^(t - m) then stays below 2^8, and the final
-// O = sum p v / sum p is unchanged, so most tiles skip the O rescale.
+// The running max moves only when a row's sub-tile max exceeds it by more
+// than this many log2 units; p = 2^(t - m) then stays below 2^8, and the final
+// O = sum p v / sum p is unchanged, so most sub-tiles skip the O rescale.
 constexpr float kRescaleSlack = 8.0f;
 
-template <typename W>
-__device__ __forceinline__ void scale_acc(W& w, float alpha);
-template <>
-__device__ __forceinline__ void scale_acc(TileTraits<bf16>::Wave& w, float alpha) {
-  w.o[0] *= alpha;
-  w.o[1] *= alpha;
-}
-template <>
-__device__ __forceinline__ void scale_acc(TileTraits<float>::Wave& w, float alpha) {
-#pragma unroll
-  for (int db = 0; db < 4; ++db) w.o[db] *= alpha;
+// Which pairs of (query block, key sub-tile sb) a rule allows: 0 none,
+// 1 all, 2 some. ref0 <= ref1 bound the block's reference values (the rule's
+// query index or position plus ref_off, non-decreasing along the block).
+enum BlockClass : int32_t { kEmpty = 0, kFull = 1, kPartial = 2 };
+
+template <typename T>
+__device__ __forceinline__ int32_t classify(const MaskRule& mr, int32_t kcount, int sb,
+                                            int32_t ref0, int32_t ref1) {
+  constexpr int32_t SK = TileTraits<T>::kSubKeys;
+  const int32_t k0 = SK * sb, k1 = k0 + SK - 1;
+  if (k0 >= kcount) return kEmpty;
+  if (mr.kind != kRange) return mr.need_mask ? kPartial : kFull;
+  const int32_t dmin = k0 - ref1, dmax = k1 - ref0;
+  if (dmax < mr.lo || dmin > mr.hi) return kEmpty;
+  return (k1 < kcount && dmin >= mr.lo && dmax <= mr.hi) ? kFull : kPartial;
 }
 
-// One key tile through the online softmax (shared by both engines).
-// qpos: this lane's query position; qi: its row index in the query tile.
+// One key tile through the online softmax (shared by both engines), one key
+// sub-tile at a time. qpos[b]: this lane's query position in query block b;
+// qi[b]: its row index in the query tile. The scores of all query blocks come
+// first; then each block's softmax (VALU) is followed by its PV product
+// (MFMA), so that the MFMAs of one block run while the next block's softmax
+// is issued.
 template <typename T>
 __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem& sm, int32_t buf,
                                              typename TileTraits<T>::Wave& w, int32_t lane,
                                              const MaskRule& mr, const BiasRule& br, int32_t kcount,
-                                             int32_t qi, int32_t qpos, float scale_log2) {
+                                             const int32_t* qi, const int32_t* qpos,
+                                             float scale_log2) {
   using TT = TileTraits<T>;
-  float s[TT::kNS];
-  TT::scores(sm, buf, w, lane, s);
-  if (br.tab) add_bias<T>(s, sm, buf, br, qpos, lane);
-  if (mr.need_mask) mask_tile<T>(s, sm, buf, mr, kcount, qi, qpos, lane);
-  float mx = s[0];
+  constexpr int QB = TT::kQB;
+  // reference range of each query block (uniform across the wave)
+  int32_t r0[QB], r1[QB];
 #pragma unroll
-  for (int r = 1; r < TT::kNS; ++r) mx = fmaxf(mx, s[r]);
-  mx = TT::row_max(mx);
-  const float mt = mx * scale_log2;  // tile max in log2 units (-inf if all masked)
-  const bool up = mt > w.m + kRescaleSlack;
-  if (__ballot(up) != 0ull) {
-    const float alpha = !up ? 1.f : (w.m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(w.m - mt));
-    w.m = up ? mt : w.m;
-    w.l *= alpha;
-    scale_acc(w, alpha);
+  for (int b = 0; b < QB; ++b) {
+    const int32_t ref = (mr.use_qpos ? qpos[b] : qi[b]) + mr.ref_off;
+    r0[b] = __builtin_amdgcn_readlane(ref, 0);
+    r1[b] = __builtin_amdgcn_readlane(ref, TT::kRowsPerBlock - 1);
   }
-  // A row with every key masked so far keeps m = -inf; shift by 0 then.
-  const float nm = (w.m == kNegInf) ? 0.f : -w.m;
-  float rs = 0.f;
 #pragma unroll
-  for (int r = 0; r < TT::kNS; ++r) {
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, nm));
-    s[r] = p;
-    rs += p;
+  for (int sb = 0; sb < TT::kSub; ++sb) {
+    int32_t cls[QB];
+    int32_t live = 0;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      cls[b] = classify<T>(mr, kcount, sb, r0[b], r1[b]);
+      live |= (cls[b] != kEmpty ? 1 : 0) << b;
+    }
+    if (live == 0) continue;  // no allowed pair: no scores, no softmax, no PV
+    float s[QB][TT::kNS];
+    TT::scores(sm, buf, w, lane, sb, s, live);
+    typename TT::PTile P;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      if (cls[b] == kEmpty) continue;
+      if (br.tab) add_bias<T>(s[b], sm, buf, br, sb, qpos[b], lane);
+      if (cls[b] == kPartial) mask_tile<T>(s[b], sm, buf, mr, sb, kcount, qi[b], qpos[b], lane);
+      float mx = s[b][0];
+#pragma unroll
+      for (int r = 1; r < TT::kNS; ++r) mx = fmaxf(mx, s[b][r]);
+      const float mt = TT::row_max(mx) * scale_log2;  // sub-tile max, log2 units (-inf if all masked)
+      const float m_old = w.m[b];
+      const bool up = mt > m_old + kRescaleSlack;
+      if (__ballot(up) != 0ull) {
+        const float alpha = !up ? 1.f : (m_old == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_old - mt));
+        w.m[b] = up ? mt : m_old;
+        w.l[b] *= alpha;
+        TT::scale_acc(w, b, alpha);
+      }
+      // A row with every key masked so far keeps m = -inf; shift by 0 then.
+      const float m_cur = w.m[b];
+      const float nm = (m_cur == kNegInf) ? 0.f : -m_cur;
+      TT::softmax_p(s[b], nm, scale_log2, P, b, w.l[b]);
+      TT::accumulate(sm, buf, w, lane, sb, P, b);
+    }
   }
-  w.l += rs;
-  TT::accumulate(sm, buf, w, lane, s);
 }
 
 // The key-tile loop: tiles 0..n_tiles-1 described by desc(n, KeyTile&, MaskRule&),
@@ -644,8 +754,9 @@ template <typename T, bool GATHER, typename Desc>
 __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
                                           typename TileTraits<T>::Wave& w, const T* kb,
                                           const T* vb, int32_t n_tiles, Desc desc,
-                                          const BiasRule& br, const GlobInfo& gi, int32_t qi,
-                                          int32_t qpos, float scale_log2) {
+                                          const BiasRule& br, const GlobInfo& gi,
+                                          const int32_t* qi, const int32_t* qpos,
+                                          float scale_log2) {
   using TT = TileTraits<T>;
   const int32_t tid = threadIdx.x, lane = tid & 63;
   if (n_tiles <= 0) return;

@@ -1,7 +1,12 @@
 """GPU parity of the HIP path against the fp64 oracle, through the C ABI.
 
 Tolerances: max |O_gpu - O_oracle| <= 1e-4 for fp32 inputs and <= 2e-2 for bf16
-inputs (fp32 accumulation); lse within 1e-4 (it never passes through bf16).
+inputs (fp32 accumulation). lse within 1e-4 for fp32 inputs. For bf16 inputs the
+kernel rounds each probability p to bf16 (the operand of the PV product) and
+normalises by the sum of the rounded values, so the row sum carries a relative
+error of at most 2^-8 (bf16 unit roundoff: 8 significant bits, round to nearest)
+and lse an absolute error of at most ln(1 + 2^-8) < 2^-8: lse within 2^-8 + 1e-4
+for bf16 (the second term is the fp32 allowance).
 Mask and global-index handling are checked exactly: with Q = 0 every logit is
 0, so exp(lse_i) is the number of allowed keys of row i (the multiplicity sum
 for LongNet); with V = one-hot(j mod 64), O_i[c] * count_i is the number of
@@ -23,7 +28,7 @@ from sparse_long_sequence_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
-LSE_TOL = 1e-4
+LSE_TOL = {"f32": 1e-4, "bf16": 2.0 ** -8 + 1e-4}
 
 
 @pytest.fixture(scope="module")
@@ -81,7 +86,7 @@ def compare(w, out, lse, o_ref, l_ref, sel=None, tag=""):
     lerr = np.abs(l[fin] - l_ref[fin]).max() if fin.any() else 0.0
     say(f"{tag}: max|dO| = {err:.3e}  max|dlse| = {lerr:.3e}")
     assert err <= TOL[w.dtype], f"{tag}: max|dO| {err} > {TOL[w.dtype]}"
-    assert lerr <= LSE_TOL, f"{tag}: max|dlse| {lerr} > {LSE_TOL}"
+    assert lerr <= LSE_TOL[w.dtype], f"{tag}: max|dlse| {lerr} > {LSE_TOL[w.dtype]}"
 
 
 # --------------------------------------------------------------------------
