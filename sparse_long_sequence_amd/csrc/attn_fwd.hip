@@ -96,14 +96,11 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   const T* qb = reinterpret_cast<const T*>(a.q) + bh * head_elems;
   const T* kb = reinterpret_cast<const T*>(a.k) + bh * head_elems;
   const T* vb = reinterpret_cast<const T*>(a.v) + bh * head_elems;
-  int32_t qi[TT::kQB], qpos[TT::kQB];
-#pragma unroll
-  for (int b = 0; b < TT::kQB; ++b) {
-    qi[b] = TT::qrow(wave, lane, b);
-    qpos[b] = qbase + d * min(qi[b], qcount - 1);
-  }
+  const int32_t qi = TT::qrow(wave, lane, 0);
+  const int32_t qpos = qbase + d * min(qi, qcount - 1);
+  const bool dead = TT::kQW * wave >= qcount;  // no valid row in this wave
   typename TT::Wave w;
-  TT::load_q(w, qb, qpos, lane);
+  TT::load_q(w, qb, &qpos, lane);
 
   // window keys in strided index space [lo, hi]
   const int32_t R = a.radius;
@@ -133,7 +130,7 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
     const bool full = kcount == kTK && dmin >= -R && dmax <= hib;
     mr = {kRange, full ? 0 : 1, 0, t0 - u0, -R, hib, 0, 0, 1};
   };
-  run_tiles<T, false>(sm, w, kb, vb, n_band, band_desc, br, gi, qi, qpos, a.scale_log2);
+  run_tiles<T, false>(sm, w, kb, vb, n_band, band_desc, br, gi, qi, qpos, dead, a.scale_log2);
 
   if (a.n_global > 0) {
     // global-column tiles that can hold an allowed pair (bit set = keep)
@@ -168,22 +165,19 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
       mr = {kGlobCol, full ? 0 : 1, 0, 0, 0, 0, a.causal, R, d};
     };
     const GlobInfo gall = {want_bias ? kGlobAll : kGlobNone, a.gidx, a.n_global};
-    run_tiles<T, true>(sm, w, kb, vb, n_glob, glob_desc, br, gall, qi, qpos, a.scale_log2);
+    run_tiles<T, true>(sm, w, kb, vb, n_glob, glob_desc, br, gall, qi, qpos, dead, a.scale_log2);
   }
 
   // epilogue: rows outside G (the global-row pass owns the rest)
-#pragma unroll
-  for (int b = 0; b < TT::kQB; ++b) {
-    const float l_tot = TT::row_sum(w.l[b]);
-    if (qi[b] < qcount) {
-      const bool is_g = g1 > g0 && sorted_contains(a.gidx + g0, g1 - g0, qpos[b]);
-      if (!is_g) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        O* dst = reinterpret_cast<O*>(a.out) + bh * head_elems + (size_t)qpos[b] * kD;
-        TT::store_row(dst, w, b, inv, lane);
-        if (a.lse && TT::row_leader(lane))
-          a.lse[(size_t)bh * N + qpos[b]] = l_tot > 0.f ? (w.m[b] + __log2f(l_tot)) * kLn2 : kNegInf;
-      }
+  const float l_tot = TT::row_sum(w.l[0]);
+  if (qi < qcount) {
+    const bool is_g = g1 > g0 && sorted_contains(a.gidx + g0, g1 - g0, qpos);
+    if (!is_g) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      O* dst = reinterpret_cast<O*>(a.out) + bh * head_elems + (size_t)qpos * kD;
+      TT::store_row(dst, w, 0, inv, lane);
+      if (a.lse && TT::row_leader(lane))
+        a.lse[(size_t)bh * N + qpos] = l_tot > 0.f ? (w.m[0] + __log2f(l_tot)) * kLn2 : kNegInf;
     }
   }
 }
@@ -222,14 +216,11 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   const T* qb = reinterpret_cast<const T*>(a.qg) + bh * head_elems;
   const T* kb = reinterpret_cast<const T*>(a.kg) + bh * head_elems;
   const T* vb = reinterpret_cast<const T*>(a.vg) + bh * head_elems;
-  int32_t qi[TT::kQB], qpos[TT::kQB];
-#pragma unroll
-  for (int b = 0; b < TT::kQB; ++b) {
-    qi[b] = TT::qrow(wave, lane, b);
-    qpos[b] = qidx[min(qi[b], qcount - 1)];
-  }
+  const int32_t qi = TT::qrow(wave, lane, 0);
+  const int32_t qpos = qidx[min(qi, qcount - 1)];
+  const bool dead = TT::kQW * wave >= qcount;  // no valid row in this wave
   typename TT::Wave w;
-  TT::load_q(w, qb, qpos, lane);
+  TT::load_q(w, qb, &qpos, lane);
   auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = j0 + n * kTK;
     const int32_t kcount = min(kTK, j1 - u0);
@@ -239,23 +230,21 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
     mr = {kRange, full ? 0 : 1, 1, -u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
   };
   const BiasRule br = {want_bias ? sm.bias : nullptr, a.rel_k, 1};
-  run_tiles<T, false>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, a.scale_log2);
-#pragma unroll
-  for (int b = 0; b < TT::kQB; ++b) {
-    const float l_tot = TT::row_sum(w.l[b]);
-    if (qi[b] < qcount) {
-      const size_t prow = ((size_t)bh * a.n_global + gq * kTQ + qi[b]) * a.n_chunks + chunk;
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      TT::store_row_f32(a.ws_o + prow * kD, w, b, inv, lane);
-      if (TT::row_leader(lane))
-        a.ws_lse[prow] = l_tot > 0.f ? (w.m[b] + __log2f(l_tot)) * kLn2 : kNegInf;
-    }
+  run_tiles<T, false>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2);
+  const float l_tot = TT::row_sum(w.l[0]);
+  if (qi < qcount) {
+    const size_t prow = ((size_t)bh * a.n_global + gq * kTQ + qi) * a.n_chunks + chunk;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    TT::store_row_f32(a.ws_o + prow * kD, w, 0, inv, lane);
+    if (TT::row_leader(lane))
+      a.ws_lse[prow] = l_tot > 0.f ? (w.m[0] + __log2f(l_tot)) * kLn2 : kNegInf;
   }
 }
 
-// Two waves per SIMD: the register budget is 256 per lane (VGPR + AGPR).
+// At least kMinWavesPerEU waves per SIMD: that bounds each wave's registers.
 template <typename T>
-__global__ __launch_bounds__(TileTraits<T>::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(TileTraits<T>::kThreads)
+__attribute__((amdgpu_waves_per_eu(TileTraits<T>::kMinWavesPerEU)))
 void attn_fwd_kernel(AttnArgs a) {
   __shared__ typename TileTraits<T>::Smem sm;
   const int32_t wg = xcd_logical_block((int32_t)blockIdx.x, a.n_glob_wg + a.n_band_wg);

@@ -16,7 +16,8 @@
 
 namespace la {
 
-__global__ __launch_bounds__(TileTraits<bf16>::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(TileTraits<bf16>::kThreads)
+__attribute__((amdgpu_waves_per_eu(TileTraits<bf16>::kMinWavesPerEU)))
 void dilated_pair_kernel(DilArgs a) {
   using TT = TileTraits<bf16>;
   __shared__ TT::Smem sm;
@@ -48,14 +49,11 @@ void dilated_pair_kernel(DilArgs a) {
   const bf16* kb = reinterpret_cast<const bf16*>(a.k) + bh * head_elems;
   const bf16* vb = reinterpret_cast<const bf16*>(a.v) + bh * head_elems;
   const int32_t base = sigma + s;
-  int32_t qi[TT::kQB], qpos[TT::kQB];
-#pragma unroll
-  for (int b = 0; b < TT::kQB; ++b) {
-    qi[b] = TT::qrow(wave, lane, b);
-    qpos[b] = base + r * (t0 + min(qi[b], qcount - 1));
-  }
+  const int32_t qi = TT::qrow(wave, lane, 0);
+  const int32_t qpos = base + r * (t0 + min(qi, qcount - 1));
+  const bool dead = TT::kQW * wave >= qcount;  // no valid row in this wave
   TT::Wave wv;
-  TT::load_q(wv, qb, qpos, lane);
+  TT::load_q(wv, qb, &qpos, lane);
   const int32_t hi = a.causal ? t0 + qcount - 1 : n_rows - 1;
   const int32_t n_tiles = (hi + kTK) / kTK;
 
@@ -69,17 +67,14 @@ void dilated_pair_kernel(DilArgs a) {
   };
   const BiasRule br = {nullptr, 0, 0};
   const GlobInfo gi = {kGlobNone, nullptr, 0};
-  run_tiles<bf16, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, a.scale_log2);
-#pragma unroll
-  for (int b = 0; b < TT::kQB; ++b) {
-    const float l_tot = TT::row_sum(wv.l[b]);
-    if (qi[b] < qcount) {
-      const int64_t prow = a.row_off[k] + ((int64_t)bh * nseg + seg) * a.seg_rows[k] + t0 + qi[b];
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      TT::store_row_f32(a.ws_o + prow * kD, wv, b, inv, lane);
-      if (TT::row_leader(lane))
-        a.ws_lse[prow] = l_tot > 0.f ? (wv.m[b] + __log2f(l_tot)) * kLn2 : kNegInf;
-    }
+  run_tiles<bf16, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2);
+  const float l_tot = TT::row_sum(wv.l[0]);
+  if (qi < qcount) {
+    const int64_t prow = a.row_off[k] + ((int64_t)bh * nseg + seg) * a.seg_rows[k] + t0 + qi;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    TT::store_row_f32(a.ws_o + prow * kD, wv, 0, inv, lane);
+    if (TT::row_leader(lane))
+      a.ws_lse[prow] = l_tot > 0.f ? (wv.m[0] + __log2f(l_tot)) * kLn2 : kNegInf;
   }
 }
 

@@ -55,6 +55,30 @@ constexpr int32_t kFar = 0x3fffffff;
 constexpr int kPitchBf16 = 72;  // K tile [key][d] and V^T tile [d][key]
 constexpr int kPitchF32 = 68;   // fp32 K and V tiles [key][d], 272 B rows
 
+// 16-byte load from global memory. The explicit address space makes it a
+// global_load: through a generic pointer the compiler may emit a flat_load,
+// which also counts against the LDS wait counter, so every later wait for an
+// LDS read would wait for this load as well.
+typedef const u32x4 __attribute__((address_space(1)))* gptr_u32x4;
+typedef const u32x2 __attribute__((address_space(1)))* gptr_u32x2;
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *(gptr_u32x4)(p); }
+__device__ __forceinline__ u32x2 ldg8(const void* p) { return *(gptr_u32x2)(p); }
+
+// Buffer loads: a 128-bit resource (base address, size, format) held in
+// scalar registers, a per-lane 32-bit byte offset and a uniform 32-bit byte
+// offset. Per-lane address state is one register per load instead of a 64-bit
+// pointer. Word 3 selects 32-bit data format for untyped loads.
+constexpr int32_t kBufWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, kBufWord3);
+}
+__device__ __forceinline__ u32x4 ldb16(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x2 ldb8(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
 // fp32 -> bf16, round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v;
@@ -179,19 +203,20 @@ template <typename T>
 struct TileTraits;
 
 // ---------------------------------------------------------------------------
-// bf16 engine: 2 waves x 64 queries, v_mfma_f32_32x32x16_bf16
+// bf16 engine: 4 waves x 32 queries, v_mfma_f32_32x32x16_bf16
 // ---------------------------------------------------------------------------
 template <>
 struct TileTraits<bf16> {
-  static constexpr int kWaves = 2;
+  static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kQB = 2;              // 32-row query blocks per wave
-  static constexpr int kQW = 32 * kQB;       // query rows per wave
+  static constexpr int kQB = 1;              // one 32-row query block per wave
+  static constexpr int kQW = 32;             // query rows per wave
   static constexpr int kTQ = kWaves * kQW;   // query rows per workgroup
   static constexpr int kSub = 2;             // key sub-tiles of 32 keys
   static constexpr int kSubKeys = kTK / kSub;
-  static constexpr int kNS = 16;             // scores per lane, query block and sub-tile
+  static constexpr int kNS = 16;             // scores per lane and sub-tile
   static constexpr int kRowsPerBlock = 32;   // lanes 0..31 hold the block's rows in order
+  static constexpr int kMinWavesPerEU = 4;
 
   // V^T rows hold each group of 16 keys in the order 0-3, 8-11, 4-7, 12-15,
   // so that the 8 keys one lane feeds to a PV MFMA step are one 16-byte read.
@@ -205,23 +230,23 @@ struct TileTraits<bf16> {
     alignas(16) uint8_t kglob[2][kTK];
   };
   struct Prefetch {
-    u32x4 k[4];  // half a K row (32 d)
-    u32x4 v[4];  // 8 d of 4 consecutive V rows
+    u32x4 k[2];  // d 16c..16c+15 of one K row
+    u32x2 v[4];  // d 4dc..4dc+3 of 4 consecutive V rows
     KeyMeta meta;
   };
   struct Wave {
-    bf16x8 qf[kQB][4];
-    f32x16 o[kQB][2];
+    bf16x8 qf[4];
+    f32x16 o[2];
     float m[kQB];  // running max, log2 domain
     float l[kQB];  // this lane's share of the running sum
   };
-  // P of one sub-tile as bf16, the B operands of the two PV MFMA steps.
+  // P of one sub-tile as bf16: the B operands of its two PV MFMA steps.
   struct PTile {
-    u32x4 p[kQB][2];
+    u32x4 p[2];
   };
 
-  static __device__ __forceinline__ int32_t qrow(int32_t wave, int32_t lane, int qb) {
-    return kQW * wave + 32 * qb + (lane & 31);
+  static __device__ __forceinline__ int32_t qrow(int32_t wave, int32_t lane, int) {
+    return kQW * wave + (lane & 31);
   }
   // Key row of score element r of sub-tile sb: a constant part and a lane part.
   static __device__ __forceinline__ constexpr int32_t key_const(int sb, int r) {
@@ -233,42 +258,42 @@ struct TileTraits<bf16> {
   // one lane per query row writes the row's scalars
   static __device__ __forceinline__ bool row_leader(int32_t lane) { return lane < 32; }
 
-  // K: thread t loads half (t & 1) of key row t >> 1.
-  // V: thread t loads d chunk t >> 4 (8 d) of the key rows 4(t & 15) + 0..3.
+  // K: thread t loads d chunk 16(t & 3) of key row t >> 2.
+  // V: thread t loads d 4(t >> 4)..+3 of the key rows 4(t & 15) + 0..3.
   static __device__ __forceinline__ FetchPlan plan(int32_t stride, int32_t tid) {
     FetchPlan p;
     p.rs = stride * kD;
-    p.ok = (tid >> 1) * p.rs + 32 * (tid & 1);
-    p.ov = 4 * (tid & 15) * p.rs + 8 * (tid >> 4);
+    p.ok = (tid >> 2) * p.rs + 16 * (tid & 3);
+    p.ov = 4 * (tid & 15) * p.rs + 4 * (tid >> 4);
     return p;
   }
 
-  // Issue the global loads of one key tile into registers. Rows past the
-  // tile's end re-read its last row: those keys are masked, and a valid row
-  // keeps every value finite.
+  // Issue the loads of one key tile into registers (buffer loads relative to
+  // the head's K and V; byte offsets fit in 32 bits for N < 2^24). Rows past
+  // the tile's end re-read its last row: those keys are masked, and a valid
+  // row keeps every value finite.
   template <bool GATHER>
   static __device__ __forceinline__ void fetch(Prefetch& pf, const bf16* kb, const bf16* vb,
                                                const KeyTile& kt, const FetchPlan& fp,
                                                int32_t tid) {
+    if (kt.count <= 0) return;
+    const __amdgpu_buffer_rsrc_t rk = buffer_of(kb), rv = buffer_of(vb);
     const int32_t last = kt.count - 1;
-    const bf16* pk;
-    const bf16* pv[4];
     if (!GATHER && kt.count == kTK) {
-      const size_t b0 = (size_t)kt.base * kD;
-      pk = kb + b0 + fp.ok;
+      const int32_t sb = kt.base * (kD * 2);  // tile base, bytes (uniform)
+      const int32_t rb = fp.rs * 2;           // bytes between key rows (uniform)
+      pf.k[0] = ldb16(rk, fp.ok * 2, sb);
+      pf.k[1] = ldb16(rk, fp.ok * 2 + 16, sb);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) pv[x] = vb + b0 + fp.ov + x * fp.rs;
+      for (int x = 0; x < 4; ++x) pf.v[x] = ldb8(rv, fp.ov * 2, sb + x * rb);
     } else {
-      pk = kb + (size_t)key_pos<GATHER>(kt, min(tid >> 1, last)) * kD + 32 * (tid & 1);
+      const int32_t ok = (key_pos<GATHER>(kt, min(tid >> 2, last)) * kD + 16 * (tid & 3)) * 2;
+      pf.k[0] = ldb16(rk, ok, 0);
+      pf.k[1] = ldb16(rk, ok + 16, 0);
 #pragma unroll
       for (int x = 0; x < 4; ++x)
-        pv[x] = vb + (size_t)key_pos<GATHER>(kt, min(4 * (tid & 15) + x, last)) * kD + 8 * (tid >> 4);
+        pf.v[x] = ldb8(rv, (key_pos<GATHER>(kt, min(4 * (tid & 15) + x, last)) * kD + 4 * (tid >> 4)) * 2, 0);
     }
-    const u32x4* ks = reinterpret_cast<const u32x4*>(pk);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) pf.k[x] = ks[x];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) pf.v[x] = *reinterpret_cast<const u32x4*>(pv[x]);
     if (tid < kTK) {
       pf.meta.pos = key_pos<GATHER>(kt, min(tid, last));
       pf.meta.gbit = kt.gbit0 + min(tid, last);
@@ -278,78 +303,55 @@ struct TileTraits<bf16> {
   // Move a prefetched tile into LDS buffer `buf` (V transposed to [d][key]).
   static __device__ __forceinline__ void stage(Smem& sm, int32_t buf, const Prefetch& pf,
                                                int32_t tid) {
-    const int32_t kk = tid >> 1, hk = tid & 1;
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-      *reinterpret_cast<u32x4*>(&sm.k[buf][kk][32 * hk + 8 * x]) = pf.k[x];
-    // key quad kq = keys 4kq..4kq+3 = local quad lq of 16-key group g
+    const int32_t kk = tid >> 2, ck = tid & 3;
+    *reinterpret_cast<u32x4*>(&sm.k[buf][kk][16 * ck]) = pf.k[0];
+    *reinterpret_cast<u32x4*>(&sm.k[buf][kk][16 * ck + 8]) = pf.k[1];
+    // key quad kq = keys 4kq..4kq+3 = local quad lq of 16-key group kq >> 2
     const int32_t kq = tid & 15, dc = tid >> 4;
     const int32_t lq = kq & 3;
     const int32_t col = 16 * (kq >> 2) + 4 * (((lq & 1) << 1) | (lq >> 1));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // dword e of each row holds d = 8dc + 2e (low half) and 8dc + 2e + 1 (high half)
+    for (int e = 0; e < 2; ++e) {
+      // dword e of each row holds d = 4dc + 2e (low half) and 4dc + 2e + 1 (high half)
       u32x2 lo, hi;
       lo[0] = __builtin_amdgcn_perm(pf.v[1][e], pf.v[0][e], 0x05040100u);
       lo[1] = __builtin_amdgcn_perm(pf.v[3][e], pf.v[2][e], 0x05040100u);
       hi[0] = __builtin_amdgcn_perm(pf.v[1][e], pf.v[0][e], 0x07060302u);
       hi[1] = __builtin_amdgcn_perm(pf.v[3][e], pf.v[2][e], 0x07060302u);
-      *reinterpret_cast<u32x2*>(&sm.vt[buf][8 * dc + 2 * e][col]) = lo;
-      *reinterpret_cast<u32x2*>(&sm.vt[buf][8 * dc + 2 * e + 1][col]) = hi;
+      *reinterpret_cast<u32x2*>(&sm.vt[buf][4 * dc + 2 * e][col]) = lo;
+      *reinterpret_cast<u32x2*>(&sm.vt[buf][4 * dc + 2 * e + 1][col]) = hi;
     }
   }
 
   static __device__ __forceinline__ void load_q(Wave& w, const bf16* qb, const int32_t* qpos,
                                                 int32_t lane) {
+    const bf16* src = qb + (size_t)qpos[0] * kD + 8 * (lane >> 5);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) w.qf[st] = __builtin_bit_cast(bf16x8, ldg16(src + 16 * st));
     const f32x16 zf = {};
-#pragma unroll
-    for (int b = 0; b < kQB; ++b) {
-      const bf16x8* src =
-          reinterpret_cast<const bf16x8*>(qb + (size_t)qpos[b] * kD + 8 * (lane >> 5));
-#pragma unroll
-      for (int st = 0; st < 4; ++st) w.qf[b][st] = src[2 * st];
-      w.o[b][0] = zf;
-      w.o[b][1] = zf;
-      w.m[b] = kNegInf;
-      w.l[b] = 0.f;
-    }
+    w.o[0] = zf;
+    w.o[1] = zf;
+    w.m[0] = kNegInf;
+    w.l[0] = 0.f;
   }
 
-  // S^T of sub-tile sb for the query blocks in LIVE (bit b = block b):
-  // s[b][e] = K[key_const(sb, e) + key_lane] . Q[qrow(b)].
-  template <int LIVE>
-  static __device__ __forceinline__ void scores_of(const Smem& sm, int32_t buf, const Wave& w,
-                                                   int32_t lane, int sb, float s[kQB][kNS]) {
+  // S^T of sub-tile sb: s[e] = K[key_const(sb, e) + key_lane] . Q[qrow].
+  static __device__ __forceinline__ void scores(const Smem& sm, int32_t buf, const Wave& w,
+                                                int32_t lane, int sb, float s[kNS]) {
     const int32_t r = lane & 31, h = lane >> 5;
-    f32x16 acc[kQB];
-#pragma unroll
-    for (int b = 0; b < kQB; ++b) acc[b] = f32x16{};
+    f32x16 acc = {};
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * sb + r][16 * st + 8 * h]);
-      static_assert(kQB == 2, "two query blocks per wave");
-      if constexpr ((LIVE & 1) != 0)
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[0][st], acc[0], 0, 0, 0);
-      if constexpr ((LIVE & 2) != 0)
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[1][st], acc[1], 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[st], acc, 0, 0, 0);
     }
 #pragma unroll
-    for (int b = 0; b < kQB; ++b)
-#pragma unroll
-      for (int e = 0; e < kNS; ++e) s[b][e] = acc[b][e];
-  }
-  static __device__ __forceinline__ void scores(const Smem& sm, int32_t buf, const Wave& w,
-                                                int32_t lane, int sb, float s[kQB][kNS],
-                                                int32_t live) {
-    if (live == 3) scores_of<3>(sm, buf, w, lane, sb, s);
-    else if (live == 1) scores_of<1>(sm, buf, w, lane, sb, s);
-    else scores_of<2>(sm, buf, w, lane, sb, s);
+    for (int e = 0; e < kNS; ++e) s[e] = acc[e];
   }
 
-  // Query block b: p = 2^(s * c + nm) rounded to bf16; the row sum adds exactly
-  // these values.
+  // p = 2^(s * c + nm) rounded to bf16; the row sum adds exactly these values.
   static __device__ __forceinline__ void softmax_p(const float s[kNS], float nm, float c,
-                                                   PTile& P, int b, float& l) {
+                                                   PTile& P, float& l) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -357,17 +359,17 @@ struct TileTraits<bf16> {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * t + 2 * i], c, nm));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * t + 2 * i + 1], c, nm));
         const uint32_t pk = pack_bf16x2(p0, p1);
-        P.p[b][t][i] = pk;
+        P.p[t][i] = pk;
         l = add_bf16x2(pk, l);
       }
     }
   }
 
-  // O^T += V^T . P^T over sub-tile sb for query block b. MFMA step t takes the
-  // keys 32sb + 16t + [0, 16): in k-slot 8h + e the key
-  // 32sb + 16t + 8(e >> 2) + 4h + (e & 3), i.e. this lane's score elements 8t + e.
+  // O^T += V^T . P^T over sub-tile sb. MFMA step t takes the keys
+  // 32sb + 16t + [0, 16): in k-slot 8h + e the key 32sb + 16t + 8(e >> 2) + 4h + (e & 3),
+  // i.e. this lane's score elements 8t + e.
   static __device__ __forceinline__ void accumulate(const Smem& sm, int32_t buf, Wave& w,
-                                                    int32_t lane, int sb, const PTile& P, int b) {
+                                                    int32_t lane, int sb, const PTile& P) {
     const int32_t r = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -375,19 +377,19 @@ struct TileTraits<bf16> {
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[buf][32 * db + r][c0]);
-        w.o[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            a, __builtin_bit_cast(bf16x8, P.p[b][t]), w.o[b][db], 0, 0, 0);
+        w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, P.p[t]),
+                                                          w.o[db], 0, 0, 0);
       }
     }
   }
 
-  static __device__ __forceinline__ void scale_acc(Wave& w, int b, float alpha) {
-    w.o[b][0] *= alpha;
-    w.o[b][1] *= alpha;
+  static __device__ __forceinline__ void scale_acc(Wave& w, float alpha) {
+    w.o[0] *= alpha;
+    w.o[1] *= alpha;
   }
 
-  // Output row of query block b; the lane holds d = 32db + 8j + 4h + i.
-  static __device__ __forceinline__ void store_row(bf16* dst, const Wave& w, int b, float inv,
+  // Output row of this lane's query; the lane holds d = 32db + 8j + 4h + i.
+  static __device__ __forceinline__ void store_row(bf16* dst, const Wave& w, int, float inv,
                                                    int32_t lane) {
     const int32_t h = lane >> 5;
 #pragma unroll
@@ -395,14 +397,14 @@ struct TileTraits<bf16> {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         u32x2 pk;
-        pk[0] = pack_bf16x2(w.o[b][db][4 * j + 0] * inv, w.o[b][db][4 * j + 1] * inv);
-        pk[1] = pack_bf16x2(w.o[b][db][4 * j + 2] * inv, w.o[b][db][4 * j + 3] * inv);
+        pk[0] = pack_bf16x2(w.o[db][4 * j + 0] * inv, w.o[db][4 * j + 1] * inv);
+        pk[1] = pack_bf16x2(w.o[db][4 * j + 2] * inv, w.o[db][4 * j + 3] * inv);
         *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * j + 4 * h) = pk;
       }
     }
   }
   // Same, fp32 (partials of split computations).
-  static __device__ __forceinline__ void store_row_f32(float* dst, const Wave& w, int b, float inv,
+  static __device__ __forceinline__ void store_row_f32(float* dst, const Wave& w, int, float inv,
                                                        int32_t lane) {
     const int32_t h = lane >> 5;
 #pragma unroll
@@ -410,7 +412,7 @@ struct TileTraits<bf16> {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f32x4 x;
-        for (int i = 0; i < 4; ++i) x[i] = w.o[b][db][4 * j + i] * inv;
+        for (int i = 0; i < 4; ++i) x[i] = w.o[db][4 * j + i] * inv;
         *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * j + 4 * h) = x;
       }
     }
@@ -431,6 +433,7 @@ struct TileTraits<float> {
   static constexpr int kSubKeys = kTK / kSub;
   static constexpr int kNS = 16;
   static constexpr int kRowsPerBlock = 16;
+  static constexpr int kMinWavesPerEU = 2;
 
   struct __attribute__((aligned(16))) Smem {
     alignas(16) float k[2][kTK][kPitchF32];
@@ -483,12 +486,10 @@ struct TileTraits<float> {
       row = (size_t)kt.base * kD + fp.ok;
     else
       row = (size_t)key_pos<GATHER>(kt, min(tid >> 2, last)) * kD + 16 * (tid & 3);
-    const u32x4* ks = reinterpret_cast<const u32x4*>(kb + row);
-    const u32x4* vs = reinterpret_cast<const u32x4*>(vb + row);
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      pf.k[x] = ks[x];
-      pf.v[x] = vs[x];
+      pf.k[x] = ldg16(kb + row + 4 * x);
+      pf.v[x] = ldg16(vb + row + 4 * x);
     }
     if (tid < kTK) {
       pf.meta.pos = key_pos<GATHER>(kt, min(tid, last));
@@ -520,7 +521,7 @@ struct TileTraits<float> {
   }
 
   static __device__ __forceinline__ void scores(const Smem& sm, int32_t buf, const Wave& w,
-                                                int32_t lane, int, float s[kQB][kNS], int32_t) {
+                                                int32_t lane, int, float s[kNS]) {
     const int32_t r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -530,12 +531,12 @@ struct TileTraits<float> {
       for (int st = 0; st < 16; ++st)
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(krow[st], w.qf[st], acc, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[0][4 * kb + i] = acc[i];
+      for (int i = 0; i < 4; ++i) s[4 * kb + i] = acc[i];
     }
   }
 
   static __device__ __forceinline__ void softmax_p(const float s[kNS], float nm, float c,
-                                                   PTile& P, int, float& l) {
+                                                   PTile& P, float& l) {
     float rs = 0.f;
 #pragma unroll
     for (int r = 0; r < kNS; ++r) {
@@ -547,7 +548,7 @@ struct TileTraits<float> {
 
   // k-slot g of step (kb, i) is key 16kb + 4g + i: A = V[key][d = 16db + r].
   static __device__ __forceinline__ void accumulate(const Smem& sm, int32_t buf, Wave& w,
-                                                    int32_t lane, int, const PTile& P, int) {
+                                                    int32_t lane, int, const PTile& P) {
     const int32_t r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -561,7 +562,7 @@ struct TileTraits<float> {
     }
   }
 
-  static __device__ __forceinline__ void scale_acc(Wave& w, int, float alpha) {
+  static __device__ __forceinline__ void scale_acc(Wave& w, float alpha) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) w.o[db] *= alpha;
   }
@@ -624,7 +625,8 @@ __device__ __forceinline__ void add_bias(float* s, const typename TileTraits<T>:
                                          int32_t buf, const BiasRule& br, int sb, int32_t qpos,
                                          int32_t lane) {
   using TT = TileTraits<T>;
-  const int32_t kl = TT::key_lane(lane);
+  int32_t kl = TT::key_lane(lane);
+  asm("" : "+v"(kl));  // opaque per call: keeps kl-derived per-element values out of loop-invariant hoisting
 #pragma unroll
   for (int r = 0; r < TT::kNS; ++r) {
     const int32_t kj = TT::key_const(sb, r) + kl;
@@ -642,7 +644,8 @@ __device__ __forceinline__ void mask_tile(float* s, const typename TileTraits<T>
                                           int32_t buf, const MaskRule& mr, int sb, int32_t kcount,
                                           int32_t qi, int32_t qpos, int32_t lane) {
   using TT = TileTraits<T>;
-  const int32_t kl = TT::key_lane(lane);
+  int32_t kl = TT::key_lane(lane);
+  asm("" : "+v"(kl));  // opaque per call: keeps kl-derived per-element values out of loop-invariant hoisting
   if (mr.kind == kRange) {
     const int32_t base = kl - (mr.use_qpos ? qpos : qi) - mr.ref_off;
 #pragma unroll
@@ -687,64 +690,78 @@ __device__ __forceinline__ int32_t classify(const MaskRule& mr, int32_t kcount, 
   return (k1 < kcount && dmin >= mr.lo && dmax <= mr.hi) ? kFull : kPartial;
 }
 
-// One key tile through the online softmax (shared by both engines), one key
-// sub-tile at a time. qpos[b]: this lane's query position in query block b;
-// qi[b]: its row index in the query tile. The scores of all query blocks come
-// first; then each block's softmax (VALU) is followed by its PV product
-// (MFMA), so that the MFMAs of one block run while the next block's softmax
-// is issued.
+// Online softmax and PV of key sub-tile sb given its final logits s (raw
+// q.k, with bias, -inf where excluded).
+template <typename T>
+__device__ __forceinline__ void sub_update(const typename TileTraits<T>::Smem& sm, int32_t buf,
+                                           typename TileTraits<T>::Wave& w, int32_t lane, int sb,
+                                           const float* s, float scale_log2) {
+  using TT = TileTraits<T>;
+  float mx = s[0];
+#pragma unroll
+  for (int r = 1; r < TT::kNS; ++r) mx = fmaxf(mx, s[r]);
+  const float mt = TT::row_max(mx) * scale_log2;  // sub-tile max, log2 units (-inf if all masked)
+  const float m_old = w.m[0];
+  const bool up = mt > m_old + kRescaleSlack;
+  if (__ballot(up) != 0ull) {
+    const float alpha = !up ? 1.f : (m_old == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_old - mt));
+    w.m[0] = up ? mt : m_old;
+    w.l[0] *= alpha;
+    TT::scale_acc(w, alpha);
+  }
+  // A row with every key masked so far keeps m = -inf; shift by 0 then.
+  const float m_cur = w.m[0];
+  const float nm = (m_cur == kNegInf) ? 0.f : -m_cur;
+  typename TT::PTile P;
+  TT::softmax_p(s, nm, scale_log2, P, w.l[0]);
+  TT::accumulate(sm, buf, w, lane, sb, P);
+}
+
+// One staged key tile through the online softmax (shared by both engines).
+// qpos: this lane's query position; qi: its row index in the query tile;
+// dead: the wave holds no valid query row (it only helps stage tiles).
+//
+// Each (wave's query block, key sub-tile) is classified from the block's row
+// range. When every sub-tile is full and there is no bias, the fast path
+// issues the score MFMAs of all sub-tiles before the first softmax, so that
+// the later sub-tiles' MFMAs run while the earlier softmax is issued, and it
+// carries no mask code. Otherwise each sub-tile is skipped (no allowed pair),
+// or biased and masked as needed, one at a time.
 template <typename T>
 __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem& sm, int32_t buf,
                                              typename TileTraits<T>::Wave& w, int32_t lane,
                                              const MaskRule& mr, const BiasRule& br, int32_t kcount,
-                                             const int32_t* qi, const int32_t* qpos,
+                                             int32_t qi, int32_t qpos, bool dead,
                                              float scale_log2) {
   using TT = TileTraits<T>;
-  constexpr int QB = TT::kQB;
-  // reference range of each query block (uniform across the wave)
-  int32_t r0[QB], r1[QB];
+  constexpr int SB = TT::kSub;
+  const int32_t ref = (mr.use_qpos ? qpos : qi) + mr.ref_off;
+  const int32_t r0 = __builtin_amdgcn_readlane(ref, 0);
+  const int32_t r1 = __builtin_amdgcn_readlane(ref, TT::kRowsPerBlock - 1);
+  int32_t cls[SB];
+  bool fast = br.tab == nullptr;
 #pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    const int32_t ref = (mr.use_qpos ? qpos[b] : qi[b]) + mr.ref_off;
-    r0[b] = __builtin_amdgcn_readlane(ref, 0);
-    r1[b] = __builtin_amdgcn_readlane(ref, TT::kRowsPerBlock - 1);
+  for (int sb = 0; sb < SB; ++sb) {
+    cls[sb] = dead ? kEmpty : classify<T>(mr, kcount, sb, r0, r1);
+    fast = fast && cls[sb] == kFull;
+  }
+  if (fast) {
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      float s[TT::kNS];
+      TT::scores(sm, buf, w, lane, sb, s);
+      sub_update<T>(sm, buf, w, lane, sb, s, scale_log2);
+    }
+    return;
   }
 #pragma unroll
-  for (int sb = 0; sb < TT::kSub; ++sb) {
-    int32_t cls[QB];
-    int32_t live = 0;
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      cls[b] = classify<T>(mr, kcount, sb, r0[b], r1[b]);
-      live |= (cls[b] != kEmpty ? 1 : 0) << b;
-    }
-    if (live == 0) continue;  // no allowed pair: no scores, no softmax, no PV
-    float s[QB][TT::kNS];
-    TT::scores(sm, buf, w, lane, sb, s, live);
-    typename TT::PTile P;
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      if (cls[b] == kEmpty) continue;
-      if (br.tab) add_bias<T>(s[b], sm, buf, br, sb, qpos[b], lane);
-      if (cls[b] == kPartial) mask_tile<T>(s[b], sm, buf, mr, sb, kcount, qi[b], qpos[b], lane);
-      float mx = s[b][0];
-#pragma unroll
-      for (int r = 1; r < TT::kNS; ++r) mx = fmaxf(mx, s[b][r]);
-      const float mt = TT::row_max(mx) * scale_log2;  // sub-tile max, log2 units (-inf if all masked)
-      const float m_old = w.m[b];
-      const bool up = mt > m_old + kRescaleSlack;
-      if (__ballot(up) != 0ull) {
-        const float alpha = !up ? 1.f : (m_old == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_old - mt));
-        w.m[b] = up ? mt : m_old;
-        w.l[b] *= alpha;
-        TT::scale_acc(w, b, alpha);
-      }
-      // A row with every key masked so far keeps m = -inf; shift by 0 then.
-      const float m_cur = w.m[b];
-      const float nm = (m_cur == kNegInf) ? 0.f : -m_cur;
-      TT::softmax_p(s[b], nm, scale_log2, P, b, w.l[b]);
-      TT::accumulate(sm, buf, w, lane, sb, P, b);
-    }
+  for (int sb = 0; sb < SB; ++sb) {
+    if (cls[sb] == kEmpty) continue;  // no allowed pair: no scores, no softmax, no PV
+    float s[TT::kNS];
+    TT::scores(sm, buf, w, lane, sb, s);
+    if (br.tab) add_bias<T>(s, sm, buf, br, sb, qpos, lane);
+    if (cls[sb] == kPartial) mask_tile<T>(s, sm, buf, mr, sb, kcount, qi, qpos, lane);
+    sub_update<T>(sm, buf, w, lane, sb, s, scale_log2);
   }
 }
 
@@ -754,9 +771,8 @@ template <typename T, bool GATHER, typename Desc>
 __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
                                           typename TileTraits<T>::Wave& w, const T* kb,
                                           const T* vb, int32_t n_tiles, Desc desc,
-                                          const BiasRule& br, const GlobInfo& gi,
-                                          const int32_t* qi, const int32_t* qpos,
-                                          float scale_log2) {
+                                          const BiasRule& br, const GlobInfo& gi, int32_t qi,
+                                          int32_t qpos, bool dead, float scale_log2) {
   using TT = TileTraits<T>;
   const int32_t tid = threadIdx.x, lane = tid & 63;
   if (n_tiles <= 0) return;
@@ -778,7 +794,7 @@ __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
       desc(n + 1, kt_next, mr_next);
       TT::template fetch<GATHER>(pf, kb, vb, kt_next, fp, tid);
     }
-    process_tile<T>(sm, buf, w, lane, mr, br, kt.count, qi, qpos, scale_log2);
+    process_tile<T>(sm, buf, w, lane, mr, br, kt.count, qi, qpos, dead, scale_log2);
     if (more) {
       TT::stage(sm, buf ^ 1, pf, tid);
       stage_meta<T>(sm, buf ^ 1, pf.meta, gi, tid);
