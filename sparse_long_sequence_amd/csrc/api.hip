@@ -82,6 +82,8 @@ la_status plan_dilated(const la_dims* d, const int32_t* w, const int32_t* r, int
     if (w[k] < 1 || r[k] < 1) return fail(LA_EINVAL, "every w and r must be >= 1");
     a.w[k] = w[k];
     a.r[k] = r[k];
+    a.inv_w[k] = 1.0f / (float)w[k];
+    a.inv_r[k] = 1.0f / (float)r[k];
     a.nseg[k] = (d->N + w[k] - 1) / w[k];
     a.seg_rows[k] = (w[k] + r[k] - 1) / r[k];
     a.qtiles[k] = (a.seg_rows[k] + la::kDilatedQueryTile - 1) / la::kDilatedQueryTile;

@@ -255,39 +255,61 @@ void attn_fwd_kernel(AttnArgs a) {
 }
 
 // Merge the key-chunk partials of every global row: lse = ln sum_c e^{lse_c},
-// O = sum_c e^{lse_c - lse} O_c, in chunk order. A separate launch: merging
-// inside the first one would need device-scope fences, which on a multi-XCD
-// part write back and invalidate a whole L2 each time.
-// 256 threads = 4 rows, thread = d.
+// O = sum_c e^{lse_c - lse} O_c. A separate launch: merging inside the first
+// one would need device-scope fences, which on a multi-XCD part write back
+// and invalidate a whole L2 each time. 16 lanes per row, 4 consecutive d per
+// lane, 16 rows per 256-thread block; chunks are taken kMergeGroup at a time
+// with all their loads issued together (a running max keeps the sums
+// bounded).
+constexpr int32_t kMergeGroup = 8;
+constexpr int32_t kMergeRows = 16;
+
 template <typename T>
 __global__ __launch_bounds__(256) void global_merge_kernel(AttnArgs a) {
   using O = typename OutT<T>::type;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // over B*H*n_global
+  const int64_t row = (int64_t)blockIdx.x * kMergeRows + (threadIdx.x >> 4);  // over B*H*n_global
   if (row >= (int64_t)a.B * a.H * a.n_global) return;
   const int32_t bh = (int32_t)(row / a.n_global), r = (int32_t)(row % a.n_global);
-  const int32_t dd = threadIdx.x & 63;
+  const int32_t d4 = 4 * (threadIdx.x & 15);
   const size_t p0 = (size_t)row * a.n_chunks;
-  float L = kNegInf;
-  for (int32_t c = 0; c < a.n_chunks; ++c) L = fmaxf(L, a.ws_lse[p0 + c]);
-  float acc = 0.f, S = 0.f;
-  if (L != kNegInf) {
-    for (int32_t c = 0; c < a.n_chunks; ++c) {
-      const float lc = a.ws_lse[p0 + c];
-      if (lc == kNegInf) continue;
-      const float wgt = __expf(lc - L);
-      S += wgt;
-      acc += wgt * a.ws_o[(p0 + c) * kD + dd];
+  float L = kNegInf, S = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int32_t c0 = 0; c0 < a.n_chunks; c0 += kMergeGroup) {
+    float lc[kMergeGroup];
+    f32x4 oc[kMergeGroup];
+#pragma unroll
+    for (int j = 0; j < kMergeGroup; ++j) {
+      const size_t p = p0 + min(c0 + j, a.n_chunks - 1);  // always a valid partial
+      lc[j] = c0 + j < a.n_chunks ? a.ws_lse[p] : kNegInf;
+      oc[j] = *reinterpret_cast<const f32x4*>(a.ws_o + p * kD + d4);
     }
+    float Lg = L;
+#pragma unroll
+    for (int j = 0; j < kMergeGroup; ++j) Lg = fmaxf(Lg, lc[j]);
+    if (Lg == kNegInf) continue;
+    const float sc = L == kNegInf ? 0.f : __expf(L - Lg);
+    S *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int j = 0; j < kMergeGroup; ++j) {
+      const float wgt = lc[j] == kNegInf ? 0.f : __expf(lc[j] - Lg);
+      S += wgt;
+      acc += wgt * oc[j];
+    }
+    L = Lg;
   }
   const int32_t pos = a.gidx[r];
-  O* dst = reinterpret_cast<O*>(a.out) + ((size_t)bh * a.N + pos) * kD;
-  const float val = S > 0.f ? acc / S : 0.f;
+  O* dst = reinterpret_cast<O*>(a.out) + ((size_t)bh * a.N + pos) * kD + d4;
+  const float inv = S > 0.f ? 1.f / S : 0.f;
   if constexpr (sizeof(O) == 2) {
-    reinterpret_cast<__bf16*>(dst)[dd] = (__bf16)val;
+    u32x2 pk;
+    pk[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    pk[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<u32x2*>(dst) = pk;
   } else {
-    dst[dd] = val;
+    *reinterpret_cast<f32x4*>(dst) = acc * inv;
   }
-  if (a.lse && dd == 0) a.lse[(size_t)bh * a.N + pos] = S > 0.f ? L + __logf(S) : kNegInf;
+  if (a.lse && d4 == 0) a.lse[(size_t)bh * a.N + pos] = S > 0.f ? L + __logf(S) : kNegInf;
 }
 
 hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
@@ -302,7 +324,7 @@ hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
                        dim3(TileTraits<float>::kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_global == 0) return e;
-  const uint32_t blocks = (uint32_t)(((int64_t)a.B * a.H * a.n_global + 3) / 4);
+  const uint32_t blocks = (uint32_t)(((int64_t)a.B * a.H * a.n_global + kMergeRows - 1) / kMergeRows);
   if (dtype == 1)
     hipLaunchKernelGGL(global_merge_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, a);
   else

@@ -78,40 +78,74 @@ void dilated_pair_kernel(DilArgs a) {
   }
 }
 
-// Scatter + mixture. 4 rows per 256-thread block, thread = d.
+// x / d for 0 <= x < 2^24 and d >= 1 with a precomputed fp32 1/d: the
+// estimate is within 2 of the quotient, and two exact integer corrections
+// fix it (integer division would be a long emulated sequence per lane).
+__device__ __forceinline__ int32_t div_small(int32_t x, int32_t d, float inv_d) {
+  int32_t q = (int32_t)((float)x * inv_d);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int32_t rem = x - q * d;
+    q += rem < 0 ? -1 : (rem >= d ? 1 : 0);
+  }
+  return q;
+}
+
+// Scatter + mixture. 16 lanes per output row, 4 consecutive d per lane
+// (16-byte loads), 16 rows per 256-thread block. Patterns are taken
+// kCombineGroup at a time with all their loads issued together (a running
+// max keeps the sums bounded).
+constexpr int32_t kCombineGroup = 8;
+constexpr int32_t kCombineRows = 16;
+
 __global__ __launch_bounds__(256) void dilated_combine_kernel(DilArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int32_t dd = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kCombineRows + (threadIdx.x >> 4);
+  const int32_t d4 = 4 * (threadIdx.x & 15);
   const int64_t total = (int64_t)a.B * a.H * a.N;
   if (row >= total) return;
   const int32_t i = (int32_t)(row % a.N);
   const int32_t bh = (int32_t)(row / a.N);
   const int32_t h = bh % a.H;
-  int64_t prow[kMaxPairs];
-  float lk[kMaxPairs];
-  float L = kNegInf;
-  for (int32_t k = 0; k < a.n_pairs; ++k) {
-    const int32_t w = a.w[k], r = a.r[k];
-    const int32_t seg = i / w, off = i - seg * w;
-    prow[k] = -1;
-    lk[k] = kNegInf;
-    if (off % r != h % r) continue;
-    prow[k] = a.row_off[k] + ((int64_t)bh * a.nseg[k] + seg) * a.seg_rows[k] + off / r;
-    lk[k] = a.ws_lse[prow[k]];
-    L = fmaxf(L, lk[k]);
-  }
-  float acc = 0.f, S = 0.f;
-  if (L != kNegInf) {
-    for (int32_t k = 0; k < a.n_pairs; ++k) {
-      if (prow[k] < 0 || lk[k] == kNegInf) continue;
-      const float wgt = __expf(lk[k] - L);
-      S += wgt;
-      acc += wgt * a.ws_o[prow[k] * kD + dd];
+  float L = kNegInf, S = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int32_t k0 = 0; k0 < a.n_pairs; k0 += kCombineGroup) {
+    float lk[kCombineGroup];
+    f32x4 ok[kCombineGroup];
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) {
+      const int32_t k = min(k0 + j, a.n_pairs - 1);
+      const int32_t w = a.w[k], r = a.r[k];
+      const int32_t seg = div_small(i, w, a.inv_w[k]), off = i - seg * w;
+      const int32_t m = div_small(off, r, a.inv_r[k]);       // off = m r + (off mod r)
+      const int32_t hs = h - div_small(h, r, a.inv_r[k]) * r;  // h mod r
+      // pattern k covers row i iff its offset in the segment is congruent to h mod r
+      const bool cov = k0 + j < a.n_pairs && off - m * r == hs;
+      const int64_t prow =
+          a.row_off[k] + ((int64_t)bh * a.nseg[k] + seg) * a.seg_rows[k] + (cov ? m : 0);
+      lk[j] = cov ? a.ws_lse[prow] : kNegInf;
+      ok[j] = *reinterpret_cast<const f32x4*>(a.ws_o + prow * kD + d4);
     }
+    float Lg = L;
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) Lg = fmaxf(Lg, lk[j]);
+    if (Lg == kNegInf) continue;
+    const float sc = L == kNegInf ? 0.f : __expf(L - Lg);
+    S *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) {
+      const float wgt = lk[j] == kNegInf ? 0.f : __expf(lk[j] - Lg);
+      S += wgt;
+      acc += wgt * ok[j];
+    }
+    L = Lg;
   }
-  const float val = S > 0.f ? acc / S : 0.f;
-  reinterpret_cast<__bf16*>(a.out)[row * kD + dd] = (__bf16)val;
-  if (a.lse && dd == 0) a.lse[row] = S > 0.f ? L + __logf(S) : kNegInf;
+  const float inv = S > 0.f ? 1.f / S : 0.f;
+  u32x2 pk;
+  pk[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pk[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(a.out) + row * kD + d4) = pk;
+  if (a.lse && d4 == 0) a.lse[row] = S > 0.f ? L + __logf(S) : kNegInf;
 }
 
 hipError_t launch_dilated(const DilArgs& a, hipStream_t stream) {
@@ -122,7 +156,8 @@ hipError_t launch_dilated(const DilArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const int64_t rows = (int64_t)a.B * a.H * a.N;
-  hipLaunchKernelGGL(dilated_combine_kernel, dim3((uint32_t)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(dilated_combine_kernel, dim3((uint32_t)((rows + kCombineRows - 1) / kCombineRows)),
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -36,9 +36,10 @@ struct DilArgs {
   const void *q, *k, *v;
   int32_t B, H, N, causal, n_pairs;
   int32_t w[kMaxPairs], r[kMaxPairs];
+  float inv_w[kMaxPairs], inv_r[kMaxPairs];  // 1/w, 1/r (fp32) for division without divides
   int32_t nseg[kMaxPairs];      // segments of pattern k: ceil(N / w)
   int32_t seg_rows[kMaxPairs];  // partial rows reserved per segment: ceil(w / r)
-  int32_t qtiles[kMaxPairs];    // query tiles per segment: ceil(seg_rows / 64)
+  int32_t qtiles[kMaxPairs];    // query tiles per segment: ceil(seg_rows / query tile)
   int32_t order[kMaxPairs];     // launch order of the patterns (heaviest first)
   int64_t wg_start[kMaxPairs + 1];  // first workgroup of the i-th pattern in launch order
   int64_t row_off[kMaxPairs];   // first partial row of pattern k
