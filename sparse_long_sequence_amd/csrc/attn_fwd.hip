@@ -27,20 +27,6 @@ __host__ __device__ inline int32_t band_tiles_of_head(int32_t N, int32_t d, int3
   return t;
 }
 
-// Entries of the sorted array g[0..n) below p0 and below p1, counted by the
-// whole wave at once (one round of loads instead of a chain of dependent ones).
-__device__ __forceinline__ void count_below(const int32_t* g, int32_t n, int32_t p0, int32_t p1,
-                                            int32_t lane, int32_t& c0, int32_t& c1) {
-  c0 = 0;
-  c1 = 0;
-  for (int32_t x0 = 0; x0 < n; x0 += 64) {
-    const int32_t x = x0 + lane;
-    const int32_t v = x < n ? g[x] : 0x7fffffff;
-    c0 += __builtin_popcountll(__ballot(v < p0));
-    c1 += __builtin_popcountll(__ballot(v < p1));
-  }
-}
-
 template <typename T>
 struct OutT;
 template <>
@@ -84,13 +70,14 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   const int32_t qbase = c + d * t0;
   const int32_t i_lo = qbase, i_hi = qbase + d * (qcount - 1);
 
-  // Global rows inside this tile: G[g0, g1) holds every global position in [i_lo, i_hi].
-  int32_t g0 = 0, g1 = 0;
-  if (a.n_global > 0) {
-    count_below(a.gidx, a.n_global, i_lo, i_hi + 1, lane, g0, g1);
-    // a tile made only of global rows belongs to the global-row pass
-    if (d == 1 && g1 - g0 == qcount) return;
-  }
+  // Bounds of the global index list (uniform scalar loads, consumed late):
+  // only a tile whose rows meet [G first, G last] can hold global rows.
+  const int32_t ng = a.n_global;
+  const int32_t g_first = ng > 0 ? a.gidx[0] : 0;
+  const int32_t g_last = ng > 0 ? a.gidx[ng - 1] : -1;
+  // a tile made only of global rows belongs to the global-row pass (detected
+  // here when G is one run of consecutive positions)
+  if (d == 1 && g_last - g_first == ng - 1 && g_first <= i_lo && g_last >= i_hi) return;
   load_bias_table<T>(sm, a, h, tid);
 
   const T* qb = reinterpret_cast<const T*>(a.q) + bh * head_elems;
@@ -171,7 +158,7 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   // epilogue: rows outside G (the global-row pass owns the rest)
   const float l_tot = TT::row_sum(w.l[0]);
   if (qi < qcount) {
-    const bool is_g = g1 > g0 && sorted_contains(a.gidx + g0, g1 - g0, qpos);
+    const bool is_g = g_first <= i_hi && g_last >= i_lo && sorted_contains(a.gidx, ng, qpos);
     if (!is_g) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       O* dst = reinterpret_cast<O*>(a.out) + bh * head_elems + (size_t)qpos * kD;
@@ -247,11 +234,17 @@ __global__ __launch_bounds__(TileTraits<T>::kThreads)
 __attribute__((amdgpu_waves_per_eu(TileTraits<T>::kMinWavesPerEU)))
 void attn_fwd_kernel(AttnArgs a) {
   __shared__ typename TileTraits<T>::Smem sm;
-  const int32_t wg = xcd_logical_block((int32_t)blockIdx.x, a.n_glob_wg + a.n_band_wg);
-  if (wg < 0) return;
-  // global-row workgroups come first in the grid so they are not the tail
-  if (wg < a.n_glob_wg) global_workgroup<T>(a, sm, wg);
-  else band_workgroup<T>(a, sm, wg - a.n_glob_wg);
+  // Block b runs on XCD b % 8. Each XCD takes an equal share of the global-row
+  // workgroups, then an equal share of the band workgroups, each share a
+  // contiguous range (workgroups of one head then share K/V in that XCD's L2,
+  // and no XCD is left with only the shorter global-row work).
+  const int32_t x = (int32_t)blockIdx.x % kXcds, j = (int32_t)blockIdx.x / kXcds;
+  const int32_t gper = (a.n_glob_wg + kXcds - 1) / kXcds;
+  const int32_t bper = (a.n_band_wg + kXcds - 1) / kXcds;
+  const int32_t gcnt = min(gper, max(0, a.n_glob_wg - x * gper));
+  const int32_t bcnt = min(bper, max(0, a.n_band_wg - x * bper));
+  if (j < gcnt) global_workgroup<T>(a, sm, x * gper + j);
+  else if (j - gcnt < bcnt) band_workgroup<T>(a, sm, x * bper + (j - gcnt));
 }
 
 // Merge the key-chunk partials of every global row: lse = ln sum_c e^{lse_c},
@@ -313,9 +306,10 @@ __global__ __launch_bounds__(256) void global_merge_kernel(AttnArgs a) {
 }
 
 hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
-  int64_t grid = (int64_t)a.n_band_wg + (int64_t)a.n_glob_wg;
-  if (grid <= 0) return hipSuccess;
-  grid = (grid + kXcds - 1) / kXcds * kXcds;  // padded for the XCD remap
+  if ((int64_t)a.n_band_wg + a.n_glob_wg <= 0) return hipSuccess;
+  // per-XCD shares of each kind (see attn_fwd_kernel)
+  const int64_t grid = (int64_t)kXcds * ((a.n_glob_wg + kXcds - 1) / kXcds +
+                                         (a.n_band_wg + kXcds - 1) / kXcds);
   if (dtype == 1)
     hipLaunchKernelGGL(attn_fwd_kernel<bf16>, dim3((uint32_t)grid),
                        dim3(TileTraits<bf16>::kThreads), 0, stream, a);
