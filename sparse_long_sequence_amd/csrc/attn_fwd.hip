@@ -251,19 +251,20 @@ void attn_fwd_kernel(AttnArgs a) {
 // O = sum_c e^{lse_c - lse} O_c. A separate launch: merging inside the first
 // one would need device-scope fences, which on a multi-XCD part write back
 // and invalidate a whole L2 each time. 16 lanes per row, 4 consecutive d per
-// lane, 16 rows per 256-thread block; chunks are taken kMergeGroup at a time
-// with all their loads issued together (a running max keeps the sums
-// bounded).
+// lane, 4 rows per 64-thread block (many small blocks spread the few rows
+// over the CUs); chunks are taken kMergeGroup at a time with all their loads
+// issued together (a running max keeps the sums bounded).
 constexpr int32_t kMergeGroup = 8;
-constexpr int32_t kMergeRows = 16;
+constexpr int32_t kMergeRows = 4;
 
 template <typename T>
-__global__ __launch_bounds__(256) void global_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) void global_merge_kernel(AttnArgs a) {
   using O = typename OutT<T>::type;
   const int64_t row = (int64_t)blockIdx.x * kMergeRows + (threadIdx.x >> 4);  // over B*H*n_global
   if (row >= (int64_t)a.B * a.H * a.n_global) return;
   const int32_t bh = (int32_t)(row / a.n_global), r = (int32_t)(row % a.n_global);
   const int32_t d4 = 4 * (threadIdx.x & 15);
+  const int32_t pos = a.gidx[r];  // issued with the partial loads, used at the end
   const size_t p0 = (size_t)row * a.n_chunks;
   float L = kNegInf, S = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -291,7 +292,6 @@ __global__ __launch_bounds__(256) void global_merge_kernel(AttnArgs a) {
     }
     L = Lg;
   }
-  const int32_t pos = a.gidx[r];
   O* dst = reinterpret_cast<O*>(a.out) + ((size_t)bh * a.N + pos) * kD + d4;
   const float inv = S > 0.f ? 1.f / S : 0.f;
   if constexpr (sizeof(O) == 2) {
@@ -320,9 +320,9 @@ hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
   if (e != hipSuccess || a.n_global == 0) return e;
   const uint32_t blocks = (uint32_t)(((int64_t)a.B * a.H * a.n_global + kMergeRows - 1) / kMergeRows);
   if (dtype == 1)
-    hipLaunchKernelGGL(global_merge_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(global_merge_kernel<bf16>, dim3(blocks), dim3(64), 0, stream, a);
   else
-    hipLaunchKernelGGL(global_merge_kernel<float>, dim3(blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(global_merge_kernel<float>, dim3(blocks), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
