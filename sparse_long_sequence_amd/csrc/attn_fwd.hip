@@ -109,7 +109,7 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   auto band_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = lo + n * kTK;
     const int32_t kcount = min(kTK, hi - u0 + 1);
-    kt = {nullptr, c + d * u0, d, kcount, u0 - lo};
+    kt = {nullptr, c + d * u0, d, kcount, u0 - lo, gi.mode};
     // strided index difference key - query = kj - qi - (t0 - u0)
     const int32_t dmin = u0 - t0 - (qcount - 1);
     const int32_t dmax = u0 + kcount - 1 - t0;
@@ -117,9 +117,40 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
     const bool full = kcount == kTK && dmin >= -R && dmax <= hib;
     mr = {kRange, full ? 0 : 1, 0, t0 - u0, -R, hib, 0, 0, 1};
   };
-  run_tiles<T, false>(sm, w, kb, vb, n_band, band_desc, br, gi, qi, qpos, dead, a.scale_log2);
+  // When d = 1 and G is one run of consecutive positions, its key tiles are
+  // strided views too: they follow the window tiles in the same loop (their
+  // first loads overlap the last window tile). Otherwise they are gathered
+  // through G in a second loop.
+  const bool g_run = ng > 0 && d == 1 && g_last - g_first == ng - 1;
+  if (g_run) {
+    const int32_t n_gt = (ng + kTK - 1) / kTK;
+    const int32_t glob_mode = want_bias ? kGlobAll : kGlobNone;
+    auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+      if (n < n_band) {
+        band_desc(n, kt, mr);
+        return;
+      }
+      // keys of G outside the window (a global key in the window is counted
+      // there); a tile that cannot hold an allowed pair gets count 0
+      const int32_t gt = n - n_band;
+      const int32_t cnt = min(kTK, ng - gt * kTK);
+      const int32_t gl = g_first + gt * kTK, gh = gl + cnt - 1;
+      const bool all_in_band =
+          a.causal ? (gl >= i_hi - R && gh <= i_lo) : (gl >= i_hi - R && gh <= i_lo + R);
+      const bool none_causal = a.causal && gl > i_hi;
+      const bool keep = !all_in_band && !none_causal;
+      kt = {nullptr, gl, 1, keep ? cnt : 0, 0, glob_mode};
+      // key gl + kj is allowed iff its distance kj - (qpos - gl) to the query
+      // lies outside the window [-R, R] (causal: [-R, inf), so also j <= i)
+      mr = {kOutside, 1, 1, -gl, -R, a.causal ? kFar : R, 0, 0, 1};
+    };
+    run_tiles<T, false>(sm, w, kb, vb, n_band + n_gt, desc, br, gi, qi, qpos, dead,
+                        a.scale_log2);
+  } else {
+    run_tiles<T, false>(sm, w, kb, vb, n_band, band_desc, br, gi, qi, qpos, dead, a.scale_log2);
+  }
 
-  if (a.n_global > 0) {
+  if (a.n_global > 0 && !g_run) {
     // global-column tiles that can hold an allowed pair (bit set = keep)
     const int32_t n_gt = (a.n_global + kTK - 1) / kTK;
     uint64_t keep = ~0ull;
@@ -144,7 +175,7 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
         gt = __builtin_ctzll(m);
       }
       const int32_t kcount = min(kTK, a.n_global - gt * kTK);
-      kt = {a.gidx + gt * kTK, 0, 1, kcount, 0};
+      kt = {a.gidx + gt * kTK, 0, 1, kcount, 0, want_bias ? kGlobAll : kGlobNone};
       const int32_t gl = a.gidx[gt * kTK], gh = a.gidx[gt * kTK + kcount - 1];
       const bool outside = (gh < i_lo - d * R) || (gl > i_hi + d * R);
       const bool causal_ok = !a.causal || gh <= i_lo;
@@ -211,7 +242,7 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = j0 + n * kTK;
     const int32_t kcount = min(kTK, j1 - u0);
-    kt = {nullptr, u0, 1, kcount, u0 - j0};
+    kt = {nullptr, u0, 1, kcount, u0 - j0, gi.mode};
     // key position u0 + kj <= qpos  <=>  kj - (qpos - u0) <= 0
     const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= i_min);
     mr = {kRange, full ? 0 : 1, 1, -u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};

@@ -60,7 +60,7 @@ void dilated_pair_kernel(DilArgs a) {
   auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = n * kTK;
     const int32_t kcount = min(kTK, hi - u0 + 1);
-    kt = {nullptr, base + r * u0, r, kcount, 0};
+    kt = {nullptr, base + r * u0, r, kcount, 0, kGlobNone};
     // gathered index difference key - query = kj - qi - (t0 - u0) <= 0 when causal
     const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= t0);
     mr = {kRange, full ? 0 : 1, 0, t0 - u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};

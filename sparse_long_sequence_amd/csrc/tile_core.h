@@ -142,15 +142,18 @@ __device__ __forceinline__ bool sorted_contains(const int32_t* g, int32_t n, int
 // (gather through the global index list), for x < count (count >= 1).
 struct KeyTile {
   const int32_t* idx;
-  int32_t base, stride, count;
+  int32_t base, stride, count;  // count 0: nothing to load, every query block is empty
   int32_t gbit0;  // bit of row 0 in the workgroup's global bitmap (strided tiles)
+  int32_t gmode;  // how the keys' "is global" flags are found (GlobMode)
 };
 
 // Which (query, key) pairs of a tile are allowed.
 //   kRange:   key row kj of the tile, reference ref = (use_qpos ? qpos : qi) + ref_off;
 //             allowed iff kj < count and lo <= kj - ref <= hi.
 //   kGlobCol: key j = global position outside the query's window (j <= i if causal).
-enum MaskKind : int32_t { kRange = 0, kGlobCol = 1 };
+//   kOutside: as kRange with the interval's complement: kj < count and
+//             kj - ref < lo or kj - ref > hi.
+enum MaskKind : int32_t { kRange = 0, kGlobCol = 1, kOutside = 2 };
 
 struct MaskRule {
   int32_t kind;
@@ -480,6 +483,7 @@ struct TileTraits<float> {
   static __device__ __forceinline__ void fetch(Prefetch& pf, const float* kb, const float* vb,
                                                const KeyTile& kt, const FetchPlan& fp,
                                                int32_t tid) {
+    if (kt.count <= 0) return;
     const int32_t last = kt.count - 1;
     size_t row;
     if (!GATHER && kt.count == kTK)
@@ -585,15 +589,16 @@ struct TileTraits<float> {
 // Per-key position and global flag of a staged tile (tid < 64 write them).
 template <typename T>
 __device__ __forceinline__ void stage_meta(typename TileTraits<T>::Smem& sm, int32_t buf,
-                                           const KeyMeta& mt, const GlobInfo& gi, int32_t tid) {
+                                           const KeyMeta& mt, const GlobInfo& gi, int32_t mode,
+                                           int32_t tid) {
   if (tid < kTK) {
     sm.kpos[buf][tid] = mt.pos;
     uint8_t f = 0;
-    if (gi.mode == kGlobBitmap)
+    if (mode == kGlobBitmap)
       f = (uint8_t)((sm.gmask[mt.gbit >> 5] >> (mt.gbit & 31)) & 1u);
-    else if (gi.mode == kGlobSearch)
+    else if (mode == kGlobSearch)
       f = (uint8_t)sorted_contains(gi.gidx, gi.n_global, mt.pos);
-    else if (gi.mode == kGlobAll)
+    else if (mode == kGlobAll)
       f = 1;
     sm.kglob[buf][tid] = f;
   }
@@ -646,13 +651,15 @@ __device__ __forceinline__ void mask_tile(float* s, const typename TileTraits<T>
   using TT = TileTraits<T>;
   int32_t kl = TT::key_lane(lane);
   asm("" : "+v"(kl));  // opaque per call: keeps kl-derived per-element values out of loop-invariant hoisting
-  if (mr.kind == kRange) {
+  if (mr.kind != kGlobCol) {
     const int32_t base = kl - (mr.use_qpos ? qpos : qi) - mr.ref_off;
+    const bool outside = mr.kind == kOutside;
 #pragma unroll
     for (int r = 0; r < TT::kNS; ++r) {
       const int32_t kj = TT::key_const(sb, r) + kl;
       const int32_t dlt = base + TT::key_const(sb, r);
-      const bool ok = (kj < kcount) & (dlt >= mr.lo) & (dlt <= mr.hi);
+      const bool in = (dlt >= mr.lo) & (dlt <= mr.hi);
+      const bool ok = (kj < kcount) & (in != outside);
       s[r] = ok ? s[r] : kNegInf;
     }
   } else {  // kGlobCol
@@ -684,10 +691,16 @@ __device__ __forceinline__ int32_t classify(const MaskRule& mr, int32_t kcount, 
   constexpr int32_t SK = TileTraits<T>::kSubKeys;
   const int32_t k0 = SK * sb, k1 = k0 + SK - 1;
   if (k0 >= kcount) return kEmpty;
-  if (mr.kind != kRange) return mr.need_mask ? kPartial : kFull;
+  if (mr.kind == kGlobCol) return mr.need_mask ? kPartial : kFull;
   const int32_t dmin = k0 - ref1, dmax = k1 - ref0;
-  if (dmax < mr.lo || dmin > mr.hi) return kEmpty;
-  return (k1 < kcount && dmin >= mr.lo && dmax <= mr.hi) ? kFull : kPartial;
+  const bool inside = dmin >= mr.lo && dmax <= mr.hi;  // every pair in [lo, hi]
+  const bool apart = dmax < mr.lo || dmin > mr.hi;     // no pair in [lo, hi]
+  if (mr.kind == kOutside) {
+    if (inside) return kEmpty;
+    return (k1 < kcount && apart) ? kFull : kPartial;
+  }
+  if (apart) return kEmpty;
+  return (k1 < kcount && inside) ? kFull : kPartial;
 }
 
 // Online softmax and PV of key sub-tile sb given its final logits s (raw
@@ -783,7 +796,7 @@ __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
   const FetchPlan fp = TT::plan(kt.stride, tid);
   TT::template fetch<GATHER>(pf, kb, vb, kt, fp, tid);
   TT::stage(sm, 0, pf, tid);
-  stage_meta<T>(sm, 0, pf.meta, gi, tid);
+  stage_meta<T>(sm, 0, pf.meta, gi, kt.gmode, tid);
   __syncthreads();
   for (int32_t n = 0; n < n_tiles; ++n) {
     const int32_t buf = n & 1;
@@ -797,7 +810,7 @@ __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
     process_tile<T>(sm, buf, w, lane, mr, br, kt.count, qi, qpos, dead, scale_log2);
     if (more) {
       TT::stage(sm, buf ^ 1, pf, tid);
-      stage_meta<T>(sm, buf ^ 1, pf.meta, gi, tid);
+      stage_meta<T>(sm, buf ^ 1, pf.meta, gi, kt_next.gmode, tid);
       kt = kt_next;
       mr = mr_next;
     }
