@@ -221,20 +221,20 @@ struct TileTraits<bf16> {
   static constexpr int kRowsPerBlock = 32;   // lanes 0..31 hold the block's rows in order
   static constexpr int kMinWavesPerEU = 4;
 
-  // V^T rows hold each group of 16 keys in the order 0-3, 8-11, 4-7, 12-15,
-  // so that the 8 keys one lane feeds to a PV MFMA step are one 16-byte read.
-  // 16-byte alignment lets the operand reads use ds_read_b128.
+  // K and V tiles are kept as loaded, [key][d] in 128-byte rows, and go from
+  // global memory straight into LDS (no register staging). The 16-byte chunk
+  // c of row k sits at chunk position c ^ swz(k), so that both the K operand
+  // reads (one chunk of 16 consecutive rows) and the transposing V reads (two
+  // chunks of 4 consecutive rows) fall on distinct banks.
   struct __attribute__((aligned(16))) Smem {
-    alignas(16) bf16 k[2][kTK][kPitchBf16];
-    alignas(16) bf16 vt[2][kD][kPitchBf16];
+    alignas(16) bf16 k[2][kTK * kD];
+    alignas(16) bf16 v[2][kTK * kD];
     alignas(16) int32_t kpos[2][kTK];
     alignas(16) float bias[64];
     alignas(16) uint32_t gmask[kGMaskWords];
     alignas(16) uint8_t kglob[2][kTK];
   };
   struct Prefetch {
-    u32x4 k[2];  // d 16c..16c+15 of one K row
-    u32x2 v[4];  // d 4dc..4dc+3 of 4 consecutive V rows
     KeyMeta meta;
   };
   struct Wave {
@@ -247,6 +247,14 @@ struct TileTraits<bf16> {
   struct PTile {
     u32x4 p[2];
   };
+
+  // Chunk-position swizzle of row k (depends on k mod 16): within 8 aligned
+  // rows it is a permutation of 0..7, the 8 even (odd) rows of 16 aligned rows
+  // take distinct values, and for 4 aligned rows bits 1-2 are distinct while
+  // bit 2 differs between rows k and k + 2.
+  static __device__ __forceinline__ int32_t swz(int32_t k) {
+    return (((k & 3) << 1) | ((k >> 2) & 1)) ^ ((k >> 2) & 2);
+  }
 
   static __device__ __forceinline__ int32_t qrow(int32_t wave, int32_t lane, int) {
     return kQW * wave + (lane & 31);
@@ -261,41 +269,60 @@ struct TileTraits<bf16> {
   // one lane per query row writes the row's scalars
   static __device__ __forceinline__ bool row_leader(int32_t lane) { return lane < 32; }
 
-  // K: thread t loads d chunk 16(t & 3) of key row t >> 2.
-  // V: thread t loads d 4(t >> 4)..+3 of the key rows 4(t & 15) + 0..3.
+  // Wave w loads the key rows 16w + 8i + (lane >> 3), i = 0, 1, of both K and
+  // V; lane l writes chunk position l & 7 of its row, so it reads the chunk
+  // (l & 7) ^ swz(row). ok / ov: byte offsets of the two reads from the start
+  // of a full strided tile.
+  static __device__ __forceinline__ int32_t load_row(int32_t tid, int i) {
+    return 16 * (tid >> 6) + 8 * i + ((tid & 63) >> 3);
+  }
+  static __device__ __forceinline__ int32_t load_chunk(int32_t tid, int i) {
+    return (tid & 7) ^ swz(load_row(tid, i));
+  }
   static __device__ __forceinline__ FetchPlan plan(int32_t stride, int32_t tid) {
     FetchPlan p;
     p.rs = stride * kD;
-    p.ok = (tid >> 2) * p.rs + 16 * (tid & 3);
-    p.ov = 4 * (tid & 15) * p.rs + 4 * (tid >> 4);
+    p.ok = (load_row(tid, 0) * p.rs + 8 * load_chunk(tid, 0)) * 2;
+    p.ov = (load_row(tid, 1) * p.rs + 8 * load_chunk(tid, 1)) * 2;
     return p;
   }
 
-  // Issue the loads of one key tile into registers (buffer loads relative to
-  // the head's K and V; byte offsets fit in 32 bits for N < 2^24). Rows past
-  // the tile's end re-read its last row: those keys are masked, and a valid
-  // row keeps every value finite.
+  // 16 bytes per lane from a buffer into LDS at dst + 16 * lane (dst uniform).
+  static __device__ __forceinline__ void to_lds(__amdgpu_buffer_rsrc_t r, bf16* dst, int32_t voff,
+                                                int32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                             voff, soff, 0, 0);
+  }
+
+  // Issue the loads of one key tile into LDS buffer `buf` (buffer loads
+  // relative to the head's K and V; byte offsets fit in 32 bits for N < 2^24).
+  // Rows past the tile's end re-read its last row: those keys are masked, and
+  // a valid row keeps every value finite. `buf` must not be read until
+  // stage() and a barrier have followed.
   template <bool GATHER>
-  static __device__ __forceinline__ void fetch(Prefetch& pf, const bf16* kb, const bf16* vb,
+  static __device__ __forceinline__ void fetch(Prefetch& pf, Smem& sm, int32_t buf,
+                                               const bf16* kb, const bf16* vb,
                                                const KeyTile& kt, const FetchPlan& fp,
                                                int32_t tid) {
     if (kt.count <= 0) return;
     const __amdgpu_buffer_rsrc_t rk = buffer_of(kb), rv = buffer_of(vb);
     const int32_t last = kt.count - 1;
+    bf16* kd = &sm.k[buf][16 * (tid >> 6) * kD];
+    bf16* vd = &sm.v[buf][16 * (tid >> 6) * kD];
     if (!GATHER && kt.count == kTK) {
       const int32_t sb = kt.base * (kD * 2);  // tile base, bytes (uniform)
-      const int32_t rb = fp.rs * 2;           // bytes between key rows (uniform)
-      pf.k[0] = ldb16(rk, fp.ok * 2, sb);
-      pf.k[1] = ldb16(rk, fp.ok * 2 + 16, sb);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) pf.v[x] = ldb8(rv, fp.ov * 2, sb + x * rb);
+      to_lds(rk, kd, fp.ok, sb);
+      to_lds(rk, kd + 8 * kD, fp.ov, sb);
+      to_lds(rv, vd, fp.ok, sb);
+      to_lds(rv, vd + 8 * kD, fp.ov, sb);
     } else {
-      const int32_t ok = (key_pos<GATHER>(kt, min(tid >> 2, last)) * kD + 16 * (tid & 3)) * 2;
-      pf.k[0] = ldb16(rk, ok, 0);
-      pf.k[1] = ldb16(rk, ok + 16, 0);
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
-        pf.v[x] = ldb8(rv, (key_pos<GATHER>(kt, min(4 * (tid & 15) + x, last)) * kD + 4 * (tid >> 4)) * 2, 0);
+      for (int i = 0; i < 2; ++i) {
+        const int32_t off =
+            (key_pos<GATHER>(kt, min(load_row(tid, i), last)) * kD + 8 * load_chunk(tid, i)) * 2;
+        to_lds(rk, kd + 8 * i * kD, off, 0);
+        to_lds(rv, vd + 8 * i * kD, off, 0);
+      }
     }
     if (tid < kTK) {
       pf.meta.pos = key_pos<GATHER>(kt, min(tid, last));
@@ -303,27 +330,10 @@ struct TileTraits<bf16> {
     }
   }
 
-  // Move a prefetched tile into LDS buffer `buf` (V transposed to [d][key]).
-  static __device__ __forceinline__ void stage(Smem& sm, int32_t buf, const Prefetch& pf,
-                                               int32_t tid) {
-    const int32_t kk = tid >> 2, ck = tid & 3;
-    *reinterpret_cast<u32x4*>(&sm.k[buf][kk][16 * ck]) = pf.k[0];
-    *reinterpret_cast<u32x4*>(&sm.k[buf][kk][16 * ck + 8]) = pf.k[1];
-    // key quad kq = keys 4kq..4kq+3 = local quad lq of 16-key group kq >> 2
-    const int32_t kq = tid & 15, dc = tid >> 4;
-    const int32_t lq = kq & 3;
-    const int32_t col = 16 * (kq >> 2) + 4 * (((lq & 1) << 1) | (lq >> 1));
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      // dword e of each row holds d = 4dc + 2e (low half) and 4dc + 2e + 1 (high half)
-      u32x2 lo, hi;
-      lo[0] = __builtin_amdgcn_perm(pf.v[1][e], pf.v[0][e], 0x05040100u);
-      lo[1] = __builtin_amdgcn_perm(pf.v[3][e], pf.v[2][e], 0x05040100u);
-      hi[0] = __builtin_amdgcn_perm(pf.v[1][e], pf.v[0][e], 0x07060302u);
-      hi[1] = __builtin_amdgcn_perm(pf.v[3][e], pf.v[2][e], 0x07060302u);
-      *reinterpret_cast<u32x2*>(&sm.vt[buf][4 * dc + 2 * e][col]) = lo;
-      *reinterpret_cast<u32x2*>(&sm.vt[buf][4 * dc + 2 * e + 1][col]) = hi;
-    }
+  // The tile's loads have landed in LDS for this wave (a barrier must follow
+  // before other waves read them).
+  static __device__ __forceinline__ void stage(Smem&, int32_t, const Prefetch&, int32_t) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
 
   static __device__ __forceinline__ void load_q(Wave& w, const bf16* qb, const int32_t* qpos,
@@ -342,10 +352,12 @@ struct TileTraits<bf16> {
   static __device__ __forceinline__ void scores(const Smem& sm, int32_t buf, const Wave& w,
                                                 int32_t lane, int sb, float s[kNS]) {
     const int32_t r = lane & 31, h = lane >> 5;
+    const int32_t y = h ^ swz(r);  // chunk 2st + h of row r sits at position 2st ^ y
+    const bf16* row = &sm.k[buf][(32 * sb + r) * kD];
     f32x16 acc = {};
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * sb + r][16 * st + 8 * h]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(row + 8 * ((2 * st) ^ y));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[st], acc, 0, 0, 0);
     }
 #pragma unroll
@@ -370,16 +382,27 @@ struct TileTraits<bf16> {
 
   // O^T += V^T . P^T over sub-tile sb. MFMA step t takes the keys
   // 32sb + 16t + [0, 16): in k-slot 8h + e the key 32sb + 16t + 8(e >> 2) + 4h + (e & 3),
-  // i.e. this lane's score elements 8t + e.
+  // i.e. this lane's score elements 8t + e. The A operand (V^T, d = 32db + l % 32)
+  // comes from two ds_read_b64_tr_b16: in each group of 16 lanes, lane L
+  // addresses d 4(L & 3)..+3 of key K0 + L / 4 and receives keys K0..K0+3 of
+  // its own d.
   static __device__ __forceinline__ void accumulate(const Smem& sm, int32_t buf, Wave& w,
                                                     int32_t lane, int sb, const PTile& P) {
-    const int32_t r = lane & 31, h = lane >> 5;
+    typedef short __attribute__((__vector_size__(4 * sizeof(short)))) s16x4;
+    typedef s16x4 __attribute__((address_space(3)))* lptr;
+    const int32_t L = lane & 15, g = (lane >> 4) & 1, h = lane >> 5;
+    const int32_t kr = 4 * h + (L >> 2);  // key row mod 16 of the first read; +8 for the second
+    const int32_t u = (2 * g + ((L & 3) >> 1)) ^ swz(kr);
+    const bf16* base = &sm.v[buf][kr * kD + 4 * (L & 1)];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int c0 = 16 * (2 * sb + t) + 8 * h;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[buf][32 * db + r][c0]);
+        const bf16* p0 = base + (32 * sb + 16 * t) * kD + 8 * ((4 * db) ^ u);
+        const bf16* p1 = base + (32 * sb + 16 * t + 8) * kD + 8 * ((4 * db) ^ u ^ 2);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)const_cast<bf16*>(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)const_cast<bf16*>(p1));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, P.p[t]),
                                                           w.o[db], 0, 0, 0);
       }
@@ -480,7 +503,8 @@ struct TileTraits<float> {
   }
 
   template <bool GATHER>
-  static __device__ __forceinline__ void fetch(Prefetch& pf, const float* kb, const float* vb,
+  static __device__ __forceinline__ void fetch(Prefetch& pf, Smem&, int32_t, const float* kb,
+                                               const float* vb,
                                                const KeyTile& kt, const FetchPlan& fp,
                                                int32_t tid) {
     if (kt.count <= 0) return;
@@ -794,7 +818,7 @@ __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
   MaskRule mr;
   desc(0, kt, mr);
   const FetchPlan fp = TT::plan(kt.stride, tid);
-  TT::template fetch<GATHER>(pf, kb, vb, kt, fp, tid);
+  TT::template fetch<GATHER>(pf, sm, 0, kb, vb, kt, fp, tid);
   TT::stage(sm, 0, pf, tid);
   stage_meta<T>(sm, 0, pf.meta, gi, kt.gmode, tid);
   __syncthreads();
@@ -805,7 +829,7 @@ __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
     const bool more = n + 1 < n_tiles;
     if (more) {
       desc(n + 1, kt_next, mr_next);
-      TT::template fetch<GATHER>(pf, kb, vb, kt_next, fp, tid);
+      TT::template fetch<GATHER>(pf, sm, buf ^ 1, kb, vb, kt_next, fp, tid);
     }
     process_tile<T>(sm, buf, w, lane, mr, br, kt.count, qi, qpos, dead, scale_log2);
     if (more) {
