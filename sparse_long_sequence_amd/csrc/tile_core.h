@@ -1,9 +1,11 @@
 // tile_core.h — the attention tile engine shared by every kernel of the library.
 //
 // One workgroup = one tile of query rows (128 for bf16, 64 for fp32). Keys
-// arrive in tiles of 64 rows staged through LDS (double-buffered, register
-// prefetch of the next tile). Each wave owns kQW query rows, held as kQB
-// blocks of 32 (bf16) or 16 (fp32) rows, and computes, per key sub-tile,
+// arrive in tiles of 64 rows, double-buffered in LDS; the next tile's loads
+// are issued while the current one computes (bf16: straight from global
+// memory into LDS; fp32: through registers). Each wave owns kQW query rows,
+// held as kQB blocks of 32 (bf16) or 16 (fp32) rows, and computes, per key
+// sub-tile,
 //
 //   S^T (keys x queries) = K_sub . Q^T                (MFMA, fp32 accumulate)
 //   online softmax on S^T in the log2 domain          (registers, fp32)
@@ -13,9 +15,7 @@
 // the lane 32 apart for bf16, in the lanes 16/32/48 apart for fp32), so the
 // row max needs one (bf16) or two (fp32) cross-lane swaps and the row sum none
 // until the end. The same lane layout is exactly the B operand of the PV
-// product (after a fixed permutation of the key order, applied to V^T too).
-// In the bf16 engine every K and V^T fragment read from LDS feeds the MFMAs of
-// both query blocks of the wave.
+// product, once the A operand (V^T) takes its keys in the matching order.
 //
 // MFMA operand layouts used here (lane l; measured on gfx950):
 //   v_mfma_f32_32x32x16_bf16: A[m = l%32][k = 8h..8h+7], B[k = 8h..8h+7][n = l%32],
@@ -50,10 +50,9 @@ constexpr float kInvScale = 8.0f;  // sqrt(kD): the bias table is stored in q.k 
 constexpr int kGMaskWords = 256;   // LDS bitmap of global positions: 8192 key rows
 constexpr int32_t kFar = 0x3fffffff;
 
-// LDS row pitches (elements). 144-byte rows put the 16-byte operand reads of
-// 8 consecutive rows on disjoint banks.
-constexpr int kPitchBf16 = 72;  // K tile [key][d] and V^T tile [d][key]
-constexpr int kPitchF32 = 68;   // fp32 K and V tiles [key][d], 272 B rows
+// LDS row pitch of the fp32 K and V tiles [key][d] (elements): 272-byte rows
+// put the operand reads of consecutive rows on disjoint banks.
+constexpr int kPitchF32 = 68;
 
 // 16-byte load from global memory. The explicit address space makes it a
 // global_load: through a generic pointer the compiler may emit a flat_load,
