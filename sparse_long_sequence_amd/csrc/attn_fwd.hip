@@ -234,9 +234,15 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   const T* qb = reinterpret_cast<const T*>(a.qg) + bh * head_elems;
   const T* kb = reinterpret_cast<const T*>(a.kg) + bh * head_elems;
   const T* vb = reinterpret_cast<const T*>(a.vg) + bh * head_elems;
-  const int32_t qi = TT::qrow(wave, lane, 0);
+  // A tile of at most half the workgroup's rows (bf16: two key sub-tiles per
+  // tile) keeps every wave busy: waves w and w + 2 take the same rows, wave w
+  // the first 32 keys of each tile and wave w + 2 the last 32, and their
+  // running states are folded together at the end.
+  const bool split = TT::kSub == 2 && qcount <= 2 * TT::kQW;
+  const int32_t wrow = split ? (wave & 1) : wave;
+  const int32_t qi = TT::qrow(wrow, lane, 0);
   const int32_t qpos = qidx[min(qi, qcount - 1)];
-  const bool dead = TT::kQW * wave >= qcount;  // no valid row in this wave
+  const bool dead = TT::kQW * wrow >= qcount;  // no valid row in this wave
   typename TT::Wave w;
   TT::load_q(w, qb, &qpos, lane);
   auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
@@ -248,7 +254,14 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
     mr = {kRange, full ? 0 : 1, 1, -u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
   };
   const BiasRule br = {want_bias ? sm.bias : nullptr, a.rel_k, 1};
-  run_tiles<T, false>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2);
+  run_tiles<T, false>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2,
+                      split ? (wave >> 1) : -1);
+  if constexpr (TT::kSub == 2) {
+    if (split) {
+      TT::fold_pairs(sm, w, wave, lane);
+      if (wave >= 2) return;
+    }
+  }
   const float l_tot = TT::row_sum(w.l[0]);
   if (qi < qcount) {
     const size_t prow = ((size_t)bh * a.n_global + gq * kTQ + qi) * a.n_chunks + chunk;

@@ -413,6 +413,38 @@ struct TileTraits<bf16> {
     w.o[1] *= alpha;
   }
 
+  // Waves w and w + 2 (w = 0, 1) held the same query rows over different key
+  // sub-tiles: fold the running state of wave w + 2 into wave w through LDS
+  // (reusing the K/V buffers). Each side's O and l are relative to its own
+  // reference max; both are rescaled to the larger one. Call from all waves
+  // after the tile loop; waves 2 and 3 are spent afterwards.
+  static __device__ __forceinline__ void fold_pairs(Smem& sm, Wave& w, int32_t wave,
+                                                    int32_t lane) {
+    float* xo = reinterpret_cast<float*>(&sm.k[0][0]);  // [2][32][64]: 16 KB
+    float* xs = reinterpret_cast<float*>(&sm.v[0][0]);  // [2][2][64]
+    __syncthreads();  // every wave is done with the last staged tile
+    if (wave >= 2) {
+      const int32_t p = wave - 2;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) xo[(p * 32 + e) * 64 + lane] = w.o[e >> 4][e & 15];
+      xs[(p * 2 + 0) * 64 + lane] = w.m[0];
+      xs[(p * 2 + 1) * 64 + lane] = w.l[0];
+    }
+    __syncthreads();
+    if (wave < 2) {
+      const float mb = xs[(wave * 2 + 0) * 64 + lane], lb = xs[(wave * 2 + 1) * 64 + lane];
+      const float ma = w.m[0];
+      const float m = fmaxf(ma, mb);
+      const float sa = ma == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ma - m);
+      const float sb = mb == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mb - m);
+#pragma unroll
+      for (int e = 0; e < 32; ++e)
+        w.o[e >> 4][e & 15] = w.o[e >> 4][e & 15] * sa + xo[(wave * 32 + e) * 64 + lane] * sb;
+      w.l[0] = w.l[0] * sa + lb * sb;
+      w.m[0] = m;
+    }
+  }
+
   // Output row of this lane's query; the lane holds d = 32db + 8j + 4h + i.
   static __device__ __forceinline__ void store_row(bf16* dst, const Wave& w, int, float inv,
                                                    int32_t lane) {
@@ -768,7 +800,7 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
                                              typename TileTraits<T>::Wave& w, int32_t lane,
                                              const MaskRule& mr, const BiasRule& br, int32_t kcount,
                                              int32_t qi, int32_t qpos, bool dead,
-                                             float scale_log2) {
+                                             float scale_log2, int32_t only_sb) {
   using TT = TileTraits<T>;
   constexpr int SB = TT::kSub;
   const int32_t ref = (mr.use_qpos ? qpos : qi) + mr.ref_off;
@@ -778,7 +810,7 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
   bool fast = br.tab == nullptr;
 #pragma unroll
   for (int sb = 0; sb < SB; ++sb) {
-    cls[sb] = dead ? kEmpty : classify<T>(mr, kcount, sb, r0, r1);
+    cls[sb] = (dead || (only_sb >= 0 && sb != only_sb)) ? kEmpty : classify<T>(mr, kcount, sb, r0, r1);
     fast = fast && cls[sb] == kFull;
   }
   if (fast) {
@@ -802,13 +834,16 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
 }
 
 // The key-tile loop: tiles 0..n_tiles-1 described by desc(n, KeyTile&, MaskRule&),
-// all strided with one stride or all gathered (GATHER).
+// all strided with one stride or all gathered (GATHER). only_sb >= 0: this
+// wave computes only that key sub-tile of every tile (the others are left to
+// other waves holding the same rows).
 template <typename T, bool GATHER, typename Desc>
 __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
                                           typename TileTraits<T>::Wave& w, const T* kb,
                                           const T* vb, int32_t n_tiles, Desc desc,
                                           const BiasRule& br, const GlobInfo& gi, int32_t qi,
-                                          int32_t qpos, bool dead, float scale_log2) {
+                                          int32_t qpos, bool dead, float scale_log2,
+                                          int32_t only_sb = -1) {
   using TT = TileTraits<T>;
   const int32_t tid = threadIdx.x, lane = tid & 63;
   if (n_tiles <= 0) return;
@@ -830,7 +865,7 @@ __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
       desc(n + 1, kt_next, mr_next);
       TT::template fetch<GATHER>(pf, sm, buf ^ 1, kb, vb, kt_next, fp, tid);
     }
-    process_tile<T>(sm, buf, w, lane, mr, br, kt.count, qi, qpos, dead, scale_log2);
+    process_tile<T>(sm, buf, w, lane, mr, br, kt.count, qi, qpos, dead, scale_log2, only_sb);
     if (more) {
       TT::stage(sm, buf ^ 1, pf, tid);
       stage_meta<T>(sm, buf ^ 1, pf.meta, gi, kt_next.gmode, tid);
