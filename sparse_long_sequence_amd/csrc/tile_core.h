@@ -707,15 +707,31 @@ __device__ __forceinline__ void mask_tile(float* s, const typename TileTraits<T>
   int32_t kl = TT::key_lane(lane);
   asm("" : "+v"(kl));  // opaque per call: keeps kl-derived per-element values out of loop-invariant hoisting
   if (mr.kind != kGlobCol) {
-    const int32_t base = kl - (mr.use_qpos ? qpos : qi) - mr.ref_off;
-    const bool outside = mr.kind == kOutside;
+    // The lane's allowed key rows (kRange) or excluded ones (kOutside) form
+    // one interval [a, a + span]; element r's row kj = key_const(sb, r) + kl
+    // is inside iff (unsigned)(kj - a) <= (unsigned)span: one add, one compare.
+    const int32_t ref = (mr.use_qpos ? qpos : qi) + mr.ref_off;
+    int32_t a = ref + mr.lo, span = mr.hi - mr.lo;
+    if (mr.kind == kRange) {
+      span = min(ref + mr.hi, kcount - 1) - a;  // rows past the tile's end are excluded too
+      // nothing allowed: an interval no row reaches
+      a = span < 0 ? 0x40000000 : a;
+      span = max(span, 0);
+    }
+    const int32_t c = kl - a;
+    if (mr.kind == kRange) {
 #pragma unroll
-    for (int r = 0; r < TT::kNS; ++r) {
-      const int32_t kj = TT::key_const(sb, r) + kl;
-      const int32_t dlt = base + TT::key_const(sb, r);
-      const bool in = (dlt >= mr.lo) & (dlt <= mr.hi);
-      const bool ok = (kj < kcount) & (in != outside);
-      s[r] = ok ? s[r] : kNegInf;
+      for (int r = 0; r < TT::kNS; ++r) {
+        const bool in = (uint32_t)(TT::key_const(sb, r) + c) <= (uint32_t)span;
+        s[r] = in ? s[r] : kNegInf;
+      }
+    } else {
+      const int32_t lim = kcount - kl;  // rows past the tile's end stay excluded
+#pragma unroll
+      for (int r = 0; r < TT::kNS; ++r) {
+        const bool in = (uint32_t)(TT::key_const(sb, r) + c) <= (uint32_t)span;
+        s[r] = (!in & (TT::key_const(sb, r) < lim)) ? s[r] : kNegInf;
+      }
     }
   } else {  // kGlobCol
 #pragma unroll
