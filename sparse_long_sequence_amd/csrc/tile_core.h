@@ -315,10 +315,15 @@ struct TileTraits<bf16> {
       to_lds(rv, vd, fp.ok, sb);
       to_lds(rv, vd + 8 * kD, fp.ov, sb);
     } else {
+      // lane values recomputed here from an opaque copy of tid: kept across the
+      // loop they would be spilled, and a spill reload waits for the loads
+      // just issued
+      int32_t t = tid;
+      asm volatile("" : "+v"(t));
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int32_t off =
-            (key_pos<GATHER>(kt, min(load_row(tid, i), last)) * kD + 8 * load_chunk(tid, i)) * 2;
+            (key_pos<GATHER>(kt, min(load_row(t, i), last)) * kD + 8 * load_chunk(t, i)) * 2;
         to_lds(rk, kd + 8 * i * kD, off, 0);
         to_lds(rv, vd + 8 * i * kD, off, 0);
       }
@@ -849,6 +854,12 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
   }
 }
 
+// A compile-time LDS buffer index.
+template <int32_t B>
+struct BufTag {
+  static constexpr int32_t value = B;
+};
+
 // The key-tile loop: tiles 0..n_tiles-1 described by desc(n, KeyTile&, MaskRule&),
 // all strided with one stride or all gathered (GATHER). only_sb >= 0: this
 // wave computes only that key sub-tile of every tile (the others are left to
@@ -872,8 +883,11 @@ __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
   TT::stage(sm, 0, pf, tid);
   stage_meta<T>(sm, 0, pf.meta, gi, kt.gmode, tid);
   __syncthreads();
-  for (int32_t n = 0; n < n_tiles; ++n) {
-    const int32_t buf = n & 1;
+  // Tile n computes from LDS buffer n & 1 while tile n + 1 loads into the
+  // other. The loop is unrolled by two so that the buffer of each step is a
+  // compile-time constant: LDS addresses then fold into instruction offsets.
+  auto step = [&](auto buf_tag, int32_t n) {
+    constexpr int32_t buf = decltype(buf_tag)::value;
     KeyTile kt_next;
     MaskRule mr_next;
     const bool more = n + 1 < n_tiles;
@@ -889,6 +903,10 @@ __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
       mr = mr_next;
     }
     __syncthreads();
+  };
+  for (int32_t n = 0; n < n_tiles; n += 2) {
+    step(BufTag<0>{}, n);
+    if (n + 1 < n_tiles) step(BufTag<1>{}, n + 1);
   }
 }
 
