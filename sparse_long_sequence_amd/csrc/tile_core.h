@@ -306,8 +306,10 @@ struct TileTraits<bf16> {
     if (kt.count <= 0) return;
     const __amdgpu_buffer_rsrc_t rk = buffer_of(kb), rv = buffer_of(vb);
     const int32_t last = kt.count - 1;
-    bf16* kd = &sm.k[buf][16 * (tid >> 6) * kD];
-    bf16* vd = &sm.v[buf][16 * (tid >> 6) * kD];
+    // the destination is per wave: uniform, so it is formed in scalar registers
+    const int32_t wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    bf16* kd = &sm.k[buf][16 * wv * kD];
+    bf16* vd = &sm.v[buf][16 * wv * kD];
     if (!GATHER && kt.count == kTK) {
       const int32_t sb = kt.base * (kD * 2);  // tile base, bytes (uniform)
       to_lds(rk, kd, fp.ok, sb);
@@ -824,9 +826,12 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
                                              float scale_log2, int32_t only_sb) {
   using TT = TileTraits<T>;
   constexpr int SB = TT::kSub;
-  const int32_t ref = (mr.use_qpos ? qpos : qi) + mr.ref_off;
-  const int32_t r0 = __builtin_amdgcn_readlane(ref, 0);
-  const int32_t r1 = __builtin_amdgcn_readlane(ref, TT::kRowsPerBlock - 1);
+  // the block's first and last reference values (loop-invariant lane reads,
+  // plus the tile's scalar offset)
+  const int32_t r0 = (mr.use_qpos ? __builtin_amdgcn_readlane(qpos, 0)
+                                  : __builtin_amdgcn_readlane(qi, 0)) + mr.ref_off;
+  const int32_t r1 = (mr.use_qpos ? __builtin_amdgcn_readlane(qpos, TT::kRowsPerBlock - 1)
+                                  : __builtin_amdgcn_readlane(qi, TT::kRowsPerBlock - 1)) + mr.ref_off;
   int32_t cls[SB];
   bool fast = br.tab == nullptr;
 #pragma unroll
