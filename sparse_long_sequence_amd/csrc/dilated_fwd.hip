@@ -91,54 +91,57 @@ __device__ __forceinline__ int32_t div_small(int32_t x, int32_t d, float inv_d) 
   return q;
 }
 
-// Scatter + mixture. 16 lanes per output row, 4 consecutive d per lane
-// (16-byte loads), 16 rows per 256-thread block. Patterns are taken
-// kCombineGroup at a time with all their loads issued together (a running
-// max keeps the sums bounded).
-constexpr int32_t kCombineGroup = 8;
+// Scatter + mixture. 16 output rows per 256-thread block. First one thread
+// per (row, pattern) finds whether the pattern covers the row, and if so its
+// partial row and lse (into LDS); then 16 lanes per row, 4 consecutive d per
+// lane (16-byte loads), read the covering partials and mix them (a running max
+// keeps the sums bounded).
 constexpr int32_t kCombineRows = 16;
 
 __global__ __launch_bounds__(256) void dilated_combine_kernel(DilArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * kCombineRows + (threadIdx.x >> 4);
-  const int32_t d4 = 4 * (threadIdx.x & 15);
+  __shared__ int64_t s_prow[kCombineRows][kMaxPairs];
+  __shared__ float s_lse[kCombineRows][kMaxPairs];
+  const int32_t tid = threadIdx.x;
   const int64_t total = (int64_t)a.B * a.H * a.N;
-  if (row >= total) return;
-  const int32_t i = (int32_t)(row % a.N);
-  const int32_t bh = (int32_t)(row / a.N);
-  const int32_t h = bh % a.H;
-  float L = kNegInf, S = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int32_t k0 = 0; k0 < a.n_pairs; k0 += kCombineGroup) {
-    float lk[kCombineGroup];
-    f32x4 ok[kCombineGroup];
-#pragma unroll
-    for (int j = 0; j < kCombineGroup; ++j) {
-      const int32_t k = min(k0 + j, a.n_pairs - 1);
+  const int64_t row0 = (int64_t)blockIdx.x * kCombineRows;
+  {
+    const int32_t rr = tid >> 4, k = tid & 15;  // kMaxPairs == 16
+    const int64_t row = row0 + rr;
+    float lse = kNegInf;
+    int64_t prow = 0;
+    if (k < a.n_pairs && row < total) {
+      const int32_t i = (int32_t)(row % a.N);
+      const int32_t bh = (int32_t)(row / a.N);
+      const int32_t h = bh % a.H;
       const int32_t w = a.w[k], r = a.r[k];
       const int32_t seg = div_small(i, w, a.inv_w[k]), off = i - seg * w;
       const int32_t m = div_small(off, r, a.inv_r[k]);       // off = m r + (off mod r)
       const int32_t hs = h - div_small(h, r, a.inv_r[k]) * r;  // h mod r
       // pattern k covers row i iff its offset in the segment is congruent to h mod r
-      const bool cov = k0 + j < a.n_pairs && off - m * r == hs;
-      const int64_t prow =
-          a.row_off[k] + ((int64_t)bh * a.nseg[k] + seg) * a.seg_rows[k] + (cov ? m : 0);
-      lk[j] = cov ? a.ws_lse[prow] : kNegInf;
-      ok[j] = *reinterpret_cast<const f32x4*>(a.ws_o + prow * kD + d4);
+      if (off - m * r == hs) {
+        prow = a.row_off[k] + ((int64_t)bh * a.nseg[k] + seg) * a.seg_rows[k] + m;
+        lse = a.ws_lse[prow];
+      }
     }
-    float Lg = L;
-#pragma unroll
-    for (int j = 0; j < kCombineGroup; ++j) Lg = fmaxf(Lg, lk[j]);
-    if (Lg == kNegInf) continue;
-    const float sc = L == kNegInf ? 0.f : __expf(L - Lg);
-    S *= sc;
-    acc *= sc;
-#pragma unroll
-    for (int j = 0; j < kCombineGroup; ++j) {
-      const float wgt = lk[j] == kNegInf ? 0.f : __expf(lk[j] - Lg);
+    s_prow[rr][k] = prow;
+    s_lse[rr][k] = lse;
+  }
+  __syncthreads();
+  const int32_t rr = tid >> 4, d4 = 4 * (tid & 15);
+  const int64_t row = row0 + rr;
+  if (row >= total) return;
+  float L = kNegInf;
+  for (int32_t k = 0; k < a.n_pairs; ++k) L = fmaxf(L, s_lse[rr][k]);
+  float S = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (L != kNegInf) {
+    for (int32_t k = 0; k < a.n_pairs; ++k) {
+      const float lk = s_lse[rr][k];
+      if (lk == kNegInf) continue;  // not covering (or an empty partial)
+      const float wgt = __expf(lk - L);
       S += wgt;
-      acc += wgt * ok[j];
+      acc += wgt * *reinterpret_cast<const f32x4*>(a.ws_o + s_prow[rr][k] * kD + d4);
     }
-    L = Lg;
   }
   const float inv = S > 0.f ? 1.f / S : 0.f;
   u32x2 pk;
@@ -147,6 +150,8 @@ __global__ __launch_bounds__(256) void dilated_combine_kernel(DilArgs a) {
   *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(a.out) + row * kD + d4) = pk;
   if (a.lse && d4 == 0) a.lse[row] = S > 0.f ? L + __logf(S) : kNegInf;
 }
+
+static_assert(kMaxPairs == 16, "one thread per (row, pattern) in a 256-thread block");
 
 hipError_t launch_dilated(const DilArgs& a, hipStream_t stream) {
   const int64_t grid = (a.wg_start[a.n_pairs] + kXcds - 1) / kXcds * kXcds;  // XCD remap padding
