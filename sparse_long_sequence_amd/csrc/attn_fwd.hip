@@ -44,7 +44,9 @@ __device__ __forceinline__ void load_bias_table(typename TileTraits<T>::Smem& sm
 // ---------------------------------------------------------------------------
 // band workgroup: one query tile of one residue class (positions c + d*t)
 // ---------------------------------------------------------------------------
-template <typename T>
+// BIAS: a relative-position bias table is given (the no-bias loops are
+// compiled without its code).
+template <typename T, bool BIAS>
 __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileTraits<T>::Smem& sm,
                                                int32_t bw) {
   using TT = TileTraits<T>;
@@ -144,10 +146,10 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
       // lies outside the window [-R, R] (causal: [-R, inf), so also j <= i)
       mr = {kOutside, 1, 1, -gl, -R, a.causal ? kFar : R, 0, 0, 1};
     };
-    run_tiles<T, false>(sm, w, kb, vb, n_band + n_gt, desc, br, gi, qi, qpos, dead,
+    run_tiles<T, false, BIAS>(sm, w, kb, vb, n_band + n_gt, desc, br, gi, qi, qpos, dead,
                         a.scale_log2);
   } else {
-    run_tiles<T, false>(sm, w, kb, vb, n_band, band_desc, br, gi, qi, qpos, dead, a.scale_log2);
+    run_tiles<T, false, BIAS>(sm, w, kb, vb, n_band, band_desc, br, gi, qi, qpos, dead, a.scale_log2);
   }
 
   if (a.n_global > 0 && !g_run) {
@@ -183,7 +185,7 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
       mr = {kGlobCol, full ? 0 : 1, 0, 0, 0, 0, a.causal, R, d};
     };
     const GlobInfo gall = {want_bias ? kGlobAll : kGlobNone, a.gidx, a.n_global};
-    run_tiles<T, true>(sm, w, kb, vb, n_glob, glob_desc, br, gall, qi, qpos, dead, a.scale_log2);
+    run_tiles<T, true, BIAS>(sm, w, kb, vb, n_glob, glob_desc, br, gall, qi, qpos, dead, a.scale_log2);
   }
 
   // epilogue: rows outside G (the global-row pass owns the rest)
@@ -203,7 +205,7 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
 // ---------------------------------------------------------------------------
 // global-row workgroup: one tile of global rows against one chunk of keys
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool BIAS>
 __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
                                                  typename TileTraits<T>::Smem& sm, int32_t gw) {
   using TT = TileTraits<T>;
@@ -254,7 +256,7 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
     mr = {kRange, full ? 0 : 1, 1, -u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
   };
   const BiasRule br = {want_bias ? sm.bias : nullptr, a.rel_k, 1};
-  run_tiles<T, false>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2,
+  run_tiles<T, false, BIAS>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2,
                       split ? (wave >> 1) : -1);
   if constexpr (TT::kSub == 2) {
     if (split) {
@@ -287,8 +289,14 @@ void attn_fwd_kernel(AttnArgs a) {
   const int32_t bper = (a.n_band_wg + kXcds - 1) / kXcds;
   const int32_t gcnt = min(gper, max(0, a.n_glob_wg - x * gper));
   const int32_t bcnt = min(bper, max(0, a.n_band_wg - x * bper));
-  if (j < gcnt) global_workgroup<T>(a, sm, x * gper + j);
-  else if (j - gcnt < bcnt) band_workgroup<T>(a, sm, x * bper + (j - gcnt));
+  const bool bias = a.rel_bias != nullptr;
+  if (j < gcnt) {
+    if (bias) global_workgroup<T, true>(a, sm, x * gper + j);
+    else global_workgroup<T, false>(a, sm, x * gper + j);
+  } else if (j - gcnt < bcnt) {
+    if (bias) band_workgroup<T, true>(a, sm, x * bper + (j - gcnt));
+    else band_workgroup<T, false>(a, sm, x * bper + (j - gcnt));
+  }
 }
 
 // Merge the key-chunk partials of every global row: lse = ln sum_c e^{lse_c},

@@ -67,7 +67,7 @@ void dilated_pair_kernel(DilArgs a) {
   };
   const BiasRule br = {nullptr, 0, 0};
   const GlobInfo gi = {kGlobNone, nullptr, 0};
-  run_tiles<bf16, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2);
+  run_tiles<bf16, false, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2);
   const float l_tot = TT::row_sum(wv.l[0]);
   if (qi < qcount) {
     const int64_t prow = a.row_off[k] + ((int64_t)bh * nseg + seg) * a.seg_rows[k] + t0 + qi;

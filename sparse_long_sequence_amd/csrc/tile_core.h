@@ -232,6 +232,7 @@ struct TileTraits<bf16> {
     alignas(16) float bias[64];
     alignas(16) uint32_t gmask[kGMaskWords];
     alignas(16) uint8_t kglob[2][kTK];
+    int32_t gcls[2];  // per staged tile: bit 0 some key is global, bit 1 every key is
   };
   struct Prefetch {
     KeyMeta meta;
@@ -506,6 +507,7 @@ struct TileTraits<float> {
     alignas(16) float bias[64];
     alignas(16) uint32_t gmask[kGMaskWords];
     alignas(16) uint8_t kglob[2][kTK];
+    int32_t gcls[2];  // per staged tile: bit 0 some key is global, bit 1 every key is
   };
   struct Prefetch {
     u32x4 k[4], v[4];
@@ -663,6 +665,12 @@ __device__ __forceinline__ void stage_meta(typename TileTraits<T>::Smem& sm, int
     else if (mode == kGlobAll)
       f = 1;
     sm.kglob[buf][tid] = f;
+    if (mode != kGlobNone) {
+      // the rows past the tile's end repeat its last key, so the whole wave
+      // (tid < 64) gives the tile's any / all
+      const uint64_t g = __ballot(f != 0);
+      if (tid == 0) sm.gcls[buf] = (g != 0ull ? 1 : 0) | (g == ~0ull ? 2 : 0);
+    }
   }
 }
 
@@ -687,13 +695,23 @@ __device__ __forceinline__ void build_gmask(typename TileTraits<T>::Smem& sm, co
 
 // Scores stay raw dot products q.k until the exponent; the bias table in LDS
 // is pre-multiplied by sqrt(D) so that it adds in the same units.
+// all_same: every key of the tile is of the query's kind (no per-key test).
 template <typename T>
 __device__ __forceinline__ void add_bias(float* s, const typename TileTraits<T>::Smem& sm,
                                          int32_t buf, const BiasRule& br, int sb, int32_t qpos,
-                                         int32_t lane) {
+                                         int32_t lane, bool all_same) {
   using TT = TileTraits<T>;
   int32_t kl = TT::key_lane(lane);
   asm("" : "+v"(kl));  // opaque per call: keeps kl-derived per-element values out of loop-invariant hoisting
+  if (all_same) {
+#pragma unroll
+    for (int r = 0; r < TT::kNS; ++r) {
+      const int32_t kj = TT::key_const(sb, r) + kl;
+      const int32_t dl = min(max(sm.kpos[buf][kj] - qpos, -br.k), br.k);
+      s[r] += br.tab[dl + br.k];
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < TT::kNS; ++r) {
     const int32_t kj = TT::key_const(sb, r) + kl;
@@ -818,22 +836,35 @@ __device__ __forceinline__ void sub_update(const typename TileTraits<T>::Smem& s
 // the later sub-tiles' MFMAs run while the earlier softmax is issued, and it
 // carries no mask code. Otherwise each sub-tile is skipped (no allowed pair),
 // or biased and masked as needed, one at a time.
-template <typename T>
+template <typename T, bool BIAS>
 __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem& sm, int32_t buf,
                                              typename TileTraits<T>::Wave& w, int32_t lane,
-                                             const MaskRule& mr, const BiasRule& br, int32_t kcount,
-                                             int32_t qi, int32_t qpos, bool dead,
-                                             float scale_log2, int32_t only_sb) {
+                                             const MaskRule& mr, const BiasRule& br,
+                                             const KeyTile& kt, bool strided, int32_t qi,
+                                             int32_t qpos, bool dead, float scale_log2,
+                                             int32_t only_sb) {
   using TT = TileTraits<T>;
   constexpr int SB = TT::kSub;
+  const int32_t kcount = kt.count;
   // the block's first and last reference values (loop-invariant lane reads,
   // plus the tile's scalar offset)
   const int32_t r0 = (mr.use_qpos ? __builtin_amdgcn_readlane(qpos, 0)
                                   : __builtin_amdgcn_readlane(qi, 0)) + mr.ref_off;
   const int32_t r1 = (mr.use_qpos ? __builtin_amdgcn_readlane(qpos, TT::kRowsPerBlock - 1)
                                   : __builtin_amdgcn_readlane(qi, TT::kRowsPerBlock - 1)) + mr.ref_off;
+  // Bias (ETC page, §3.4 "Relative Position Encoding": same-kind pairs only).
+  // From the staged tile's global flags: no key of the query's kind means no
+  // bias at all; every key of its kind means no per-key kind test.
+  bool bias_on = false, all_same = false;
+  if constexpr (BIAS) {
+    // (kGlobNone: no key is global, and the class word was not written)
+    const int32_t gc = kt.gmode == kGlobNone ? 0 : __builtin_amdgcn_readfirstlane(sm.gcls[buf]);
+    const bool any_g = (gc & 1) != 0, all_g = (gc & 2) != 0;
+    bias_on = br.key_global_is_same_kind ? any_g : !all_g;
+    all_same = br.key_global_is_same_kind ? all_g : !any_g;
+  }
   int32_t cls[SB];
-  bool fast = br.tab == nullptr;
+  bool fast = !bias_on;
 #pragma unroll
   for (int sb = 0; sb < SB; ++sb) {
     cls[sb] = (dead || (only_sb >= 0 && sb != only_sb)) ? kEmpty : classify<T>(mr, kcount, sb, r0, r1);
@@ -853,7 +884,28 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
     if (cls[sb] == kEmpty) continue;  // no allowed pair: no scores, no softmax, no PV
     float s[TT::kNS];
     TT::scores(sm, buf, w, lane, sb, s);
-    if (br.tab) add_bias<T>(s, sm, buf, br, sb, qpos, lane);
+    if (BIAS && bias_on) {
+      // A strided sub-tile whose clipped distances are all +k (or all -k) for
+      // the block's rows takes one table entry for every pair.
+      bool uniform = false;
+      int32_t ue = 0;
+      if (strided && all_same) {
+        constexpr int32_t SK = TT::kSubKeys;
+        const int32_t q0 = __builtin_amdgcn_readlane(qpos, 0);
+        const int32_t q1 = __builtin_amdgcn_readlane(qpos, TT::kRowsPerBlock - 1);
+        const int32_t k0 = kt.base + kt.stride * (SK * sb);
+        const int32_t k1 = kt.base + kt.stride * min(SK * sb + SK - 1, kcount - 1);
+        if (k0 - q1 >= br.k) { uniform = true; ue = 2 * br.k; }
+        else if (k1 - q0 <= -br.k) { uniform = true; ue = 0; }
+      }
+      if (uniform) {
+        const float b = br.tab[ue];
+#pragma unroll
+        for (int r = 0; r < TT::kNS; ++r) s[r] += b;
+      } else {
+        add_bias<T>(s, sm, buf, br, sb, qpos, lane, all_same);
+      }
+    }
     if (cls[sb] == kPartial) mask_tile<T>(s, sm, buf, mr, sb, kcount, qi, qpos, lane);
     sub_update<T>(sm, buf, w, lane, sb, s, scale_log2);
   }
@@ -866,10 +918,11 @@ struct BufTag {
 };
 
 // The key-tile loop: tiles 0..n_tiles-1 described by desc(n, KeyTile&, MaskRule&),
-// all strided with one stride or all gathered (GATHER). only_sb >= 0: this
+// all strided with one stride or all gathered (GATHER); BIAS: br holds a bias
+// table (compiled out otherwise). only_sb >= 0: this
 // wave computes only that key sub-tile of every tile (the others are left to
 // other waves holding the same rows).
-template <typename T, bool GATHER, typename Desc>
+template <typename T, bool GATHER, bool BIAS, typename Desc>
 __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
                                           typename TileTraits<T>::Wave& w, const T* kb,
                                           const T* vb, int32_t n_tiles, Desc desc,
@@ -900,7 +953,8 @@ __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
       desc(n + 1, kt_next, mr_next);
       TT::template fetch<GATHER>(pf, sm, buf ^ 1, kb, vb, kt_next, fp, tid);
     }
-    process_tile<T>(sm, buf, w, lane, mr, br, kt.count, qi, qpos, dead, scale_log2, only_sb);
+    process_tile<T, BIAS>(sm, buf, w, lane, mr, br, kt, !GATHER, qi, qpos, dead, scale_log2,
+                          only_sb);
     if (more) {
       TT::stage(sm, buf ^ 1, pf, tid);
       stage_meta<T>(sm, buf ^ 1, pf.meta, gi, kt_next.gmode, tid);
