@@ -110,6 +110,7 @@ SMALL = [
     ("relbias", 400, 3, 21, None, False, tuple(range(30)), 5, False, "bf16"),
     ("relbias-f32-causal", 260, 2, 40, (1, 2), True, (3, 77, 200), 12, False, "f32"),
     ("relbias-sep", 300, 2, 33, None, False, (0, 1, 2, 150, 299), 3, True, "bf16"),
+    ("relbias-dil-causal", 350, 4, 17, (1, 2, 3, 4), True, (5, 64, 65, 200, 349), 7, False, "bf16"),
     ("all-global", 96, 1, 2, None, False, tuple(range(96)), 0, False, "bf16"),
 ]
 
