@@ -91,20 +91,28 @@ la_status plan_dilated(const la_dims* d, const int32_t* w, const int32_t* r, int
     rows += (int64_t)d->B * d->H * a.nseg[k] * a.seg_rows[k];
   }
   a.rows_total = rows;
-  // Patterns with more query tiles per segment carry the longest workgroups:
-  // launch them first.
+  // Workgroups in decreasing query-tile index (the key tiles of a workgroup
+  // grow with it), across all patterns, so that the longest start first.
+  // With the patterns sorted by qtiles, the levels split into bands over which
+  // the set of patterns having that tile index is fixed.
   std::vector<int32_t> ord(n_pairs);
   for (int32_t k = 0; k < n_pairs; ++k) ord[k] = k;
   std::stable_sort(ord.begin(), ord.end(),
                    [&](int32_t x, int32_t y) { return a.qtiles[x] > a.qtiles[y]; });
-  int64_t wg = 0;
+  a.pre[0] = 0;
   for (int32_t i = 0; i < n_pairs; ++i) {
-    const int32_t k = ord[i];
-    a.order[i] = k;
-    a.wg_start[i] = wg;
-    wg += (int64_t)d->B * d->H * a.nseg[k] * a.qtiles[k];
+    a.order[i] = ord[i];
+    a.pre[i + 1] = a.pre[i] + (int64_t)d->B * d->H * a.nseg[ord[i]];
   }
-  a.wg_start[n_pairs] = wg;
+  int64_t wg = 0;
+  for (int32_t j = 0; j < n_pairs; ++j) {
+    const int32_t lo = j + 1 < n_pairs ? a.qtiles[ord[j + 1]] : 0;
+    a.band_top[j] = a.qtiles[ord[j]] - 1;
+    a.band_per[j] = a.pre[j + 1];
+    a.band_start[j] = wg;
+    wg += (int64_t)(a.qtiles[ord[j]] - lo) * a.band_per[j];
+  }
+  a.band_start[n_pairs] = wg;
   if (wg > 0x7fffffffLL) return fail(LA_EUNSUPPORTED, "launch grid too large");
   p.ws_bytes = align_up((size_t)rows * kDHead * sizeof(float)) + align_up((size_t)rows * sizeof(float));
   return LA_OK;

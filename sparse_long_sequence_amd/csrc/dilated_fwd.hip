@@ -23,17 +23,20 @@ void dilated_pair_kernel(DilArgs a) {
   __shared__ TT::Smem sm;
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t wg = xcd_logical_block((int32_t)blockIdx.x, (int32_t)a.wg_start[a.n_pairs]);
-  if (wg < 0) return;
+  // Blocks in launch order (no XCD remap: that would give one XCD all the
+  // longest workgroups): query-tile level descending across all patterns.
+  const int64_t wg = blockIdx.x;
+  if (wg >= a.band_start[a.n_pairs]) return;
+  int32_t j = 0;
+  while (j + 1 < a.n_pairs && wg >= a.band_start[j + 1]) ++j;
+  const int64_t off = wg - a.band_start[j];
+  const int32_t qt = a.band_top[j] - (int32_t)(off / a.band_per[j]);
+  const int64_t rem = off % a.band_per[j];
   int32_t oi = 0;
-  while (oi + 1 < a.n_pairs && wg >= a.wg_start[oi + 1]) ++oi;
+  while (oi < j && rem >= a.pre[oi + 1]) ++oi;
   const int32_t k = a.order[oi];
-  const int64_t local = wg - a.wg_start[oi];
-  const int32_t w = a.w[k], r = a.r[k], nseg = a.nseg[k], qtiles = a.qtiles[k];
-  // heaviest (last) query tiles of every segment first
-  const int64_t per_rank = (int64_t)a.B * a.H * nseg;
-  const int32_t qt = qtiles - 1 - (int32_t)(local / per_rank);
-  const int64_t rest = local % per_rank;
+  const int32_t w = a.w[k], r = a.r[k], nseg = a.nseg[k];
+  const int64_t rest = rem - a.pre[oi];
   const int32_t seg = (int32_t)(rest % nseg);
   const int32_t bh = (int32_t)(rest / nseg);
   const int32_t h = bh % a.H;
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(256) void dilated_combine_kernel(DilArgs a) {
 static_assert(kMaxPairs == 16, "one thread per (row, pattern) in a 256-thread block");
 
 hipError_t launch_dilated(const DilArgs& a, hipStream_t stream) {
-  const int64_t grid = (a.wg_start[a.n_pairs] + kXcds - 1) / kXcds * kXcds;  // XCD remap padding
+  const int64_t grid = a.band_start[a.n_pairs];
   if (grid > 0) {
     hipLaunchKernelGGL(dilated_pair_kernel, dim3((uint32_t)grid), dim3(TileTraits<bf16>::kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();

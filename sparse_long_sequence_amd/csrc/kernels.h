@@ -40,8 +40,17 @@ struct DilArgs {
   int32_t nseg[kMaxPairs];      // segments of pattern k: ceil(N / w)
   int32_t seg_rows[kMaxPairs];  // partial rows reserved per segment: ceil(w / r)
   int32_t qtiles[kMaxPairs];    // query tiles per segment: ceil(seg_rows / query tile)
-  int32_t order[kMaxPairs];     // launch order of the patterns (heaviest first)
-  int64_t wg_start[kMaxPairs + 1];  // first workgroup of the i-th pattern in launch order
+  // Launch order: by query-tile index t descending (a workgroup's key tiles
+  // grow with t), all patterns together. order[] lists the patterns by qtiles
+  // descending; band j holds the levels t in [qtiles[order[j+1]], band_top[j]]
+  // (the last band down to 0), where exactly patterns order[0..j] have a tile
+  // t, band_per[j] workgroups per level. pre[i]: workgroups of one level that
+  // belong to order[0..i-1].
+  int32_t order[kMaxPairs];
+  int32_t band_top[kMaxPairs];
+  int64_t band_per[kMaxPairs];
+  int64_t pre[kMaxPairs + 1];
+  int64_t band_start[kMaxPairs + 1];  // first workgroup of band j; [n_pairs]: total
   int64_t row_off[kMaxPairs];   // first partial row of pattern k
   int64_t rows_total;           // partial rows of all patterns
   float* ws_o;                  // [rows_total][D]
