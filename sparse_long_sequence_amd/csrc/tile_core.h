@@ -831,11 +831,9 @@ __device__ __forceinline__ void sub_update(const typename TileTraits<T>::Smem& s
 // dead: the wave holds no valid query row (it only helps stage tiles).
 //
 // Each (wave's query block, key sub-tile) is classified from the block's row
-// range. When every sub-tile is full and there is no bias, the fast path
-// issues the score MFMAs of all sub-tiles before the first softmax, so that
-// the later sub-tiles' MFMAs run while the earlier softmax is issued, and it
-// carries no mask code. Otherwise each sub-tile is skipped (no allowed pair),
-// or biased and masked as needed, one at a time.
+// range. When every sub-tile is full and no bias applies, the fast path runs
+// the sub-tiles one after the other with no mask or bias code. Otherwise each
+// sub-tile is skipped (no allowed pair), or biased and masked as needed.
 template <typename T, bool BIAS>
 __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem& sm, int32_t buf,
                                              typename TileTraits<T>::Wave& w, int32_t lane,
