@@ -800,15 +800,18 @@ __device__ __forceinline__ int32_t classify(const MaskRule& mr, int32_t kcount, 
 }
 
 // Online softmax and PV of key sub-tile sb given its final logits s (raw
-// q.k, with bias, -inf where excluded).
-template <typename T>
+// q.k, with bias, -inf where excluded). ADD: the logits are s + badd, badd
+// the same for every pair of the sub-tile (folded into the row max and the
+// exponent's shift instead of added to each score).
+template <typename T, bool ADD = false>
 __device__ __forceinline__ void sub_update(const typename TileTraits<T>::Smem& sm, int32_t buf,
                                            typename TileTraits<T>::Wave& w, int32_t lane, int sb,
-                                           const float* s, float scale_log2) {
+                                           const float* s, float scale_log2, float badd = 0.f) {
   using TT = TileTraits<T>;
   float mx = s[0];
 #pragma unroll
   for (int r = 1; r < TT::kNS; ++r) mx = fmaxf(mx, s[r]);
+  if constexpr (ADD) mx += badd;
   const float mt = TT::row_max(mx) * scale_log2;  // sub-tile max, log2 units (-inf if all masked)
   const float m_old = w.m[0];
   const bool up = mt > m_old + kRescaleSlack;
@@ -820,7 +823,8 @@ __device__ __forceinline__ void sub_update(const typename TileTraits<T>::Smem& s
   }
   // A row with every key masked so far keeps m = -inf; shift by 0 then.
   const float m_cur = w.m[0];
-  const float nm = (m_cur == kNegInf) ? 0.f : -m_cur;
+  float nm = (m_cur == kNegInf) ? 0.f : -m_cur;
+  if constexpr (ADD) nm += badd * scale_log2;
   typename TT::PTile P;
   TT::softmax_p(s, nm, scale_log2, P, w.l[0]);
   TT::accumulate(sm, buf, w, lane, sb, P);
@@ -882,6 +886,7 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
     if (cls[sb] == kEmpty) continue;  // no allowed pair: no scores, no softmax, no PV
     float s[TT::kNS];
     TT::scores(sm, buf, w, lane, sb, s);
+    float badd = 0.f;  // a bias shared by every pair of the sub-tile
     if (BIAS && bias_on) {
       // A strided sub-tile whose clipped distances are all +k (or all -k) for
       // the block's rows takes one table entry for every pair.
@@ -896,16 +901,11 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
         if (k0 - q1 >= br.k) { uniform = true; ue = 2 * br.k; }
         else if (k1 - q0 <= -br.k) { uniform = true; ue = 0; }
       }
-      if (uniform) {
-        const float b = br.tab[ue];
-#pragma unroll
-        for (int r = 0; r < TT::kNS; ++r) s[r] += b;
-      } else {
-        add_bias<T>(s, sm, buf, br, sb, qpos, lane, all_same);
-      }
+      if (uniform) badd = br.tab[ue];
+      else add_bias<T>(s, sm, buf, br, sb, qpos, lane, all_same);
     }
     if (cls[sb] == kPartial) mask_tile<T>(s, sm, buf, mr, sb, kcount, qi, qpos, lane);
-    sub_update<T>(sm, buf, w, lane, sb, s, scale_log2);
+    sub_update<T, BIAS>(sm, buf, w, lane, sb, s, scale_log2, badd);
   }
 }
 
