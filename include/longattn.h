@@ -85,8 +85,9 @@ typedef struct {
    * keep q, k, v (for their global columns too). */
   const void *qg, *kg, *vg;
   /* Device scratch of at least la_attn_workspace_size() bytes, 256-byte aligned;
-   * required when n_global > 0. Its contents need no initialisation and are
-   * overwritten. Calls that share a workspace must not overlap in time. */
+   * required when n_global > 0. It must be zero-filled before its first use
+   * (it holds arrival counters that every call leaves at zero again); the rest
+   * is overwritten. Calls that share a workspace must not overlap in time. */
   void *workspace;
   size_t workspace_bytes;
 } la_attn_ext;

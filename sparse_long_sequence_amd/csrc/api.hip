@@ -45,17 +45,21 @@ bool is_empty(const la_dims* d) { return d->B == 0 || d->H == 0 || d->N == 0; }
 
 int32_t n_chunks_of(int32_t N) { return (N + kChunk - 1) / kChunk; }
 
-// Workspace of la_attn_forward: global-row partials, fp32 O then fp32 lse.
+// Workspace of la_attn_forward: global-row partials, fp32 O then fp32 lse,
+// then one uint32 arrival counter per tile of global rows (zero between calls).
 struct AttnWs {
-  size_t o_off, lse_off, bytes;
+  size_t o_off, lse_off, cnt_off, bytes;
 };
 
 AttnWs attn_ws_layout(const la_dims* d, int32_t n_global) {
-  AttnWs w = {0, 0, 0};
+  AttnWs w = {0, 0, 0, 0};
   if (n_global <= 0) return w;
   const size_t parts = (size_t)d->B * d->H * n_global * n_chunks_of(d->N);
+  const int32_t tq = la::host_query_tile(d->dtype);
+  const size_t tiles = (size_t)d->B * d->H * ((n_global + tq - 1) / tq);
   w.lse_off = align_up(parts * kDHead * sizeof(float));
-  w.bytes = w.lse_off + align_up(parts * sizeof(float));
+  w.cnt_off = w.lse_off + align_up(parts * sizeof(float));
+  w.bytes = w.cnt_off + align_up(tiles * sizeof(uint32_t));
   return w;
 }
 
@@ -206,6 +210,9 @@ la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, con
     char* base = reinterpret_cast<char*>(ext->workspace);
     a.ws_o = reinterpret_cast<float*>(base + lay.o_off);
     a.ws_lse = reinterpret_cast<float*>(base + lay.lse_off);
+    a.ws_cnt = reinterpret_cast<uint32_t*>(base + lay.cnt_off);
+    // partials are addressed with 32-bit byte offsets
+    if (lay.cnt_off > (size_t)0x7fffffff) return fail(LA_EUNSUPPORTED, "global-row partials above 2 GiB");
   }
   a.chunk_len = kChunk;
   a.n_chunks = n_chunks_of(dims->N);

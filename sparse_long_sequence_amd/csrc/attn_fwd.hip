@@ -3,8 +3,8 @@
 // One launch holds two kinds of workgroups:
 //   * global-row workgroups (first in the grid), one per (batch, head, query
 //     tile of global rows, key chunk): each global row against a chunk of all keys,
-//     written as a partial (normalised O, lse) to the workspace, merged by a
-//     second, small launch;
+//     written as a partial (normalised O, lse) to the workspace; the last
+//     chunk workgroup of a tile to finish merges the tile's partials;
 //   * band workgroups, one per query tile of one residue class of one
 //     (batch, head): the sliding-window key tiles (strided by the head's
 //     dilation), then the global-column tiles (keys of G outside the window).
@@ -203,6 +203,79 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
 }
 
 // ---------------------------------------------------------------------------
+// merge of the key-chunk partials of one tile of global rows
+// ---------------------------------------------------------------------------
+// lse = ln sum_c e^{lse_c}, O = sum_c e^{lse_c - lse} O_c over the n_chunks
+// partials of each row (all complete and written through to memory). 8 lanes
+// per row with 8 consecutive d each, 32 rows per pass; chunks are taken
+// kMergeGroup at a time with all their loads issued together (a running max
+// keeps the sums bounded).
+constexpr int32_t kMergeGroup = 8;
+
+template <typename T>
+__device__ __forceinline__ void merge_global_tile(float* ws_o, float* ws_lse, const int32_t* gidx,
+                                                  void* out, float* lse, int32_t n_global,
+                                                  int32_t nc, int32_t N, int32_t bh,
+                                                  int32_t r_first, int32_t qcount) {
+  using O = typename OutT<T>::type;
+  constexpr int32_t nt = TileTraits<T>::kThreads;
+  constexpr int32_t kRowsPerPass = nt / 8;
+  const int32_t tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t ro = buffer_of(ws_o), rl = buffer_of(ws_lse);
+  const int32_t d8 = 8 * (tid & 7);
+  for (int32_t r0 = 0; r0 < qcount; r0 += kRowsPerPass) {
+    const int32_t r = r0 + tid / 8;
+    if (r >= qcount) break;
+    const int32_t p0 = (bh * n_global + r_first + r) * nc;
+    const int32_t pos = gidx[r_first + r];
+    float L = kNegInf, S = 0.f;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    for (int32_t c0 = 0; c0 < nc; c0 += kMergeGroup) {
+      float lc[kMergeGroup];
+      f32x4 oa[kMergeGroup], ob[kMergeGroup];
+#pragma unroll
+      for (int j = 0; j < kMergeGroup; ++j) {
+        const int32_t p = p0 + min(c0 + j, nc - 1);  // always a valid partial
+        const float lj = ld_coh4(rl, p * 4);
+        lc[j] = c0 + j < nc ? lj : kNegInf;
+        oa[j] = ld_coh16(ro, (p * kD + d8) * 4);
+        ob[j] = ld_coh16(ro, (p * kD + d8 + 4) * 4);
+      }
+      float Lg = L;
+#pragma unroll
+      for (int j = 0; j < kMergeGroup; ++j) Lg = fmaxf(Lg, lc[j]);
+      if (Lg == kNegInf) continue;
+      const float sc = L == kNegInf ? 0.f : __expf(L - Lg);
+      S *= sc;
+      acc0 *= sc;
+      acc1 *= sc;
+#pragma unroll
+      for (int j = 0; j < kMergeGroup; ++j) {
+        const float wgt = lc[j] == kNegInf ? 0.f : __expf(lc[j] - Lg);
+        S += wgt;
+        acc0 += wgt * oa[j];
+        acc1 += wgt * ob[j];
+      }
+      L = Lg;
+    }
+    O* dst = reinterpret_cast<O*>(out) + ((size_t)bh * N + pos) * kD + d8;
+    const float inv = S > 0.f ? 1.f / S : 0.f;
+    if constexpr (sizeof(O) == 2) {
+      u32x4 pk;
+      pk[0] = pack_bf16x2(acc0[0] * inv, acc0[1] * inv);
+      pk[1] = pack_bf16x2(acc0[2] * inv, acc0[3] * inv);
+      pk[2] = pack_bf16x2(acc1[0] * inv, acc1[1] * inv);
+      pk[3] = pack_bf16x2(acc1[2] * inv, acc1[3] * inv);
+      *reinterpret_cast<u32x4*>(dst) = pk;
+    } else {
+      *reinterpret_cast<f32x4*>(dst) = acc0 * inv;
+      *reinterpret_cast<f32x4*>(dst + 4) = acc1 * inv;
+    }
+    if (lse && d8 == 0) lse[(size_t)bh * N + pos] = S > 0.f ? L + __logf(S) : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // global-row workgroup: one tile of global rows against one chunk of keys
 // ---------------------------------------------------------------------------
 template <typename T, bool BIAS>
@@ -258,23 +331,42 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   const BiasRule br = {want_bias ? sm.bias : nullptr, a.rel_k, 1};
   run_tiles<T, false, BIAS>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2,
                       split ? (wave >> 1) : -1);
+  bool holds_rows = true;  // this wave holds a final running state
   if constexpr (TT::kSub == 2) {
     if (split) {
       TT::fold_pairs(sm, w, wave, lane);
-      if (wave >= 2) return;
+      holds_rows = wave < 2;
     }
   }
+  // The chunk's partial (normalised O, lse) of each row, written through to
+  // memory so that the workgroup merging the chunks may run on another XCD.
+  const __amdgpu_buffer_rsrc_t ro = buffer_of(a.ws_o), rl = buffer_of(a.ws_lse);
   const float l_tot = TT::row_sum(w.l[0]);
-  if (qi < qcount) {
-    const size_t prow = ((size_t)bh * a.n_global + gq * kTQ + qi) * a.n_chunks + chunk;
+  if (holds_rows && qi < qcount) {
+    const int32_t prow = ((bh * a.n_global + gq * kTQ + qi) * a.n_chunks + chunk);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    TT::store_row_f32(a.ws_o + prow * kD, w, 0, inv, lane);
+    TT::store_row_coh(ro, prow * (kD * 4), w, inv, lane);
     if (TT::row_leader(lane))
-      a.ws_lse[prow] = l_tot > 0.f ? (w.m[0] + __log2f(l_tot)) * kLn2 : kNegInf;
+      st_coh4(rl, prow * 4, l_tot > 0.f ? (w.m[0] + __log2f(l_tot)) * kLn2 : kNegInf);
   }
+  // Arrival: the last chunk workgroup of this tile merges all its chunks.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
+  __syncthreads();
+  int32_t* flag = reinterpret_cast<int32_t*>(&sm.gcls[0]);
+  uint32_t* cnt = a.ws_cnt + (bh * a.n_gq_tiles + gq);
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old + 1u == (uint32_t)a.n_chunks;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (*flag == 0) return;
+  merge_global_tile<T>(a.ws_o, a.ws_lse, a.gidx, a.out, a.lse, a.n_global, a.n_chunks, N, bh,
+                       gq * kTQ, qcount);
 }
 
-// At least kMinWavesPerEU waves per SIMD: that bounds each wave's registers.
+// At least kMinWavesPerEU waves per SIMD// At least kMinWavesPerEU waves per SIMD: that bounds each wave's registers.
 template <typename T>
 __global__ __launch_bounds__(TileTraits<T>::kThreads)
 __attribute__((amdgpu_waves_per_eu(TileTraits<T>::kMinWavesPerEU)))
@@ -299,64 +391,6 @@ void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-// Merge the key-chunk partials of every global row: lse = ln sum_c e^{lse_c},
-// O = sum_c e^{lse_c - lse} O_c. A separate launch: merging inside the first
-// one would need device-scope fences, which on a multi-XCD part write back
-// and invalidate a whole L2 each time. 16 lanes per row, 4 consecutive d per
-// lane, 4 rows per 64-thread block (many small blocks spread the few rows
-// over the CUs); chunks are taken kMergeGroup at a time with all their loads
-// issued together (a running max keeps the sums bounded).
-constexpr int32_t kMergeGroup = 8;
-constexpr int32_t kMergeRows = 4;
-
-template <typename T>
-__global__ __launch_bounds__(64) void global_merge_kernel(AttnArgs a) {
-  using O = typename OutT<T>::type;
-  const int64_t row = (int64_t)blockIdx.x * kMergeRows + (threadIdx.x >> 4);  // over B*H*n_global
-  if (row >= (int64_t)a.B * a.H * a.n_global) return;
-  const int32_t bh = (int32_t)(row / a.n_global), r = (int32_t)(row % a.n_global);
-  const int32_t d4 = 4 * (threadIdx.x & 15);
-  const int32_t pos = a.gidx[r];  // issued with the partial loads, used at the end
-  const size_t p0 = (size_t)row * a.n_chunks;
-  float L = kNegInf, S = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int32_t c0 = 0; c0 < a.n_chunks; c0 += kMergeGroup) {
-    float lc[kMergeGroup];
-    f32x4 oc[kMergeGroup];
-#pragma unroll
-    for (int j = 0; j < kMergeGroup; ++j) {
-      const size_t p = p0 + min(c0 + j, a.n_chunks - 1);  // always a valid partial
-      lc[j] = c0 + j < a.n_chunks ? a.ws_lse[p] : kNegInf;
-      oc[j] = *reinterpret_cast<const f32x4*>(a.ws_o + p * kD + d4);
-    }
-    float Lg = L;
-#pragma unroll
-    for (int j = 0; j < kMergeGroup; ++j) Lg = fmaxf(Lg, lc[j]);
-    if (Lg == kNegInf) continue;
-    const float sc = L == kNegInf ? 0.f : __expf(L - Lg);
-    S *= sc;
-    acc *= sc;
-#pragma unroll
-    for (int j = 0; j < kMergeGroup; ++j) {
-      const float wgt = lc[j] == kNegInf ? 0.f : __expf(lc[j] - Lg);
-      S += wgt;
-      acc += wgt * oc[j];
-    }
-    L = Lg;
-  }
-  O* dst = reinterpret_cast<O*>(a.out) + ((size_t)bh * a.N + pos) * kD + d4;
-  const float inv = S > 0.f ? 1.f / S : 0.f;
-  if constexpr (sizeof(O) == 2) {
-    u32x2 pk;
-    pk[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    pk[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    *reinterpret_cast<u32x2*>(dst) = pk;
-  } else {
-    *reinterpret_cast<f32x4*>(dst) = acc * inv;
-  }
-  if (a.lse && d4 == 0) a.lse[(size_t)bh * a.N + pos] = S > 0.f ? L + __logf(S) : kNegInf;
-}
-
 hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
   if ((int64_t)a.n_band_wg + a.n_glob_wg <= 0) return hipSuccess;
   // per-XCD shares of each kind (see attn_fwd_kernel)
@@ -368,13 +402,6 @@ hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
   else
     hipLaunchKernelGGL(attn_fwd_kernel<float>, dim3((uint32_t)grid),
                        dim3(TileTraits<float>::kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_global == 0) return e;
-  const uint32_t blocks = (uint32_t)(((int64_t)a.B * a.H * a.n_global + kMergeRows - 1) / kMergeRows);
-  if (dtype == 1)
-    hipLaunchKernelGGL(global_merge_kernel<bf16>, dim3(blocks), dim3(64), 0, stream, a);
-  else
-    hipLaunchKernelGGL(global_merge_kernel<float>, dim3(blocks), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ struct AttnArgs {
   float* lse;
   float* ws_o;      // [B*H][n_global][n_chunks][D] global-row partials
   float* ws_lse;    // [B*H][n_global][n_chunks]
+  uint32_t* ws_cnt; // [B*H][n_gq_tiles] chunk arrivals per global-row tile (0 between calls)
   int32_t chunk_len, n_chunks;
   int32_t band_tiles_per_head;
   int32_t n_band_wg;

@@ -78,6 +78,25 @@ __device__ __forceinline__ u32x2 ldb8(__amdgpu_buffer_rsrc_t r, int32_t voff, in
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
+// Device-coherent buffer stores and loads (cache policy sc1): a store is
+// written through to memory, a load does not return a line another XCD's
+// writes may have made stale. Workgroups on different XCDs can then hand data
+// to each other through an atomic counter without writing back or
+// invalidating a whole L2.
+constexpr int32_t kCoherent = 16;  // sc1
+__device__ __forceinline__ void st_coh16(__amdgpu_buffer_rsrc_t r, int32_t voff, u32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, 0, kCoherent);
+}
+__device__ __forceinline__ void st_coh4(__amdgpu_buffer_rsrc_t r, int32_t voff, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, 0, kCoherent);
+}
+__device__ __forceinline__ f32x4 ld_coh16(__amdgpu_buffer_rsrc_t r, int32_t voff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCoherent));
+}
+__device__ __forceinline__ float ld_coh4(__amdgpu_buffer_rsrc_t r, int32_t voff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kCoherent));
+}
+
 // fp32 -> bf16, round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v;
@@ -482,6 +501,21 @@ struct TileTraits<bf16> {
       }
     }
   }
+  // Same, device-coherent: the row at byte offset voff of buffer r.
+  // byte offset voff of buffer r.
+  static __device__ __forceinline__ void store_row_coh(__amdgpu_buffer_rsrc_t r, int32_t voff,
+                                                       const Wave& w, float inv, int32_t lane) {
+    const int32_t h = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 x;
+        for (int i = 0; i < 4; ++i) x[i] = w.o[db][4 * j + i] * inv;
+        st_coh16(r, voff + 4 * (32 * db + 8 * j + 4 * h), __builtin_bit_cast(u32x4, x));
+      }
+    }
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -644,9 +678,14 @@ struct TileTraits<float> {
       *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = x;
     }
   }
-  static __device__ __forceinline__ void store_row_f32(float* dst, const Wave& w, int b, float inv,
-                                                       int32_t lane) {
-    store_row(dst, w, b, inv, lane);
+  static __device__ __forceinline__ void store_row_coh(__amdgpu_buffer_rsrc_t r, int32_t voff,
+                                                       const Wave& w, float inv, int32_t lane) {
+    const int32_t g = lane >> 4;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      f32x4 x = w.o[db] * inv;
+      st_coh16(r, voff + 4 * (16 * db + 4 * g), __builtin_bit_cast(u32x4, x));
+    }
   }
 };
 
