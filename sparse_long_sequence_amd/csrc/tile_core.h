@@ -412,26 +412,44 @@ struct TileTraits<bf16> {
   // comes from two ds_read_b64_tr_b16: in each group of 16 lanes, lane L
   // addresses d 4(L & 3)..+3 of key K0 + L / 4 and receives keys K0..K0+3 of
   // its own d.
+  //
+  // The reads are issued through inline asm that also waits for them: for the
+  // builtin, the compiler cannot tell that the read does not touch the LDS
+  // buffer the next tile is being loaded into, and waits for those loads
+  // first, which leaves the prefetch only part of a tile to land.
+  static __device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+  }
   static __device__ __forceinline__ void accumulate(const Smem& sm, int32_t buf, Wave& w,
                                                     int32_t lane, int sb, const PTile& P) {
     typedef short __attribute__((__vector_size__(4 * sizeof(short)))) s16x4;
-    typedef s16x4 __attribute__((address_space(3)))* lptr;
     const int32_t L = lane & 15, g = (lane >> 4) & 1, h = lane >> 5;
     const int32_t kr = 4 * h + (L >> 2);  // key row mod 16 of the first read; +8 for the second
     const int32_t u = (2 * g + ((L & 3) >> 1)) ^ swz(kr);
-    const bf16* base = &sm.v[buf][kr * kD + 4 * (L & 1)];
+    const bf16* base = &sm.v[0][kr * kD + 4 * (L & 1)];
+    // lane addresses of the (d block, key half) reads; buffer, sub-tile and
+    // step go into the instruction's offset
+    const uint32_t a00 = lds_addr(base + 8 * (0 ^ u));
+    const uint32_t a01 = lds_addr(base + 8 * kD + 8 * (0 ^ u ^ 2));
+    const uint32_t a10 = lds_addr(base + 8 * (4 ^ u));
+    const uint32_t a11 = lds_addr(base + 8 * kD + 8 * (4 ^ u ^ 2));
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const bf16* p0 = base + (32 * sb + 16 * t) * kD + 8 * ((4 * db) ^ u);
-        const bf16* p1 = base + (32 * sb + 16 * t + 8) * kD + 8 * ((4 * db) ^ u ^ 2);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)const_cast<bf16*>(p0));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)const_cast<bf16*>(p1));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, P.p[t]),
-                                                          w.o[db], 0, 0, 0);
-      }
+      const int32_t off = (buf * kTK * kD + (32 * sb + 16 * t) * kD) * 2;  // bytes
+      s16x4 lo0, hi0, lo1, hi1;
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
+          "ds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
+          "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
+          "ds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(lo0), "=&v"(hi0), "=&v"(lo1), "=&v"(hi1)
+          : "v"(a00), "v"(a01), "v"(a10), "v"(a11), "i"(off));
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo0, hi0, 0, 1, 2, 3, 4, 5, 6, 7));
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo1, hi1, 0, 1, 2, 3, 4, 5, 6, 7));
+      const bf16x8 b = __builtin_bit_cast(bf16x8, P.p[t]);
+      w.o[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, w.o[0], 0, 0, 0);
+      w.o[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, w.o[1], 0, 0, 0);
     }
   }
 
@@ -912,12 +930,13 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
     fast = fast && cls[sb] == kFull;
   }
   if (fast) {
+    // Every sub-tile's scores first: the later sub-tiles' score MFMAs then
+    // run on the matrix core while this wave does the earlier ones' softmax.
+    float s[SB][TT::kNS];
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      float s[TT::kNS];
-      TT::scores(sm, buf, w, lane, sb, s);
-      sub_update<T>(sm, buf, w, lane, sb, s, scale_log2);
-    }
+    for (int sb = 0; sb < SB; ++sb) TT::scores(sm, buf, w, lane, sb, s[sb]);
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) sub_update<T>(sm, buf, w, lane, sb, s[sb], scale_log2);
     return;
   }
 #pragma unroll
