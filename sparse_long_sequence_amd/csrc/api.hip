@@ -22,7 +22,7 @@ la_status fail(la_status s, const std::string& msg) {
 }
 
 constexpr int32_t kDHead = 64;
-constexpr int32_t kChunk = 512;  // keys per global-row partial
+constexpr int32_t kChunk = 640;  // keys per global-row partial (10 key tiles)
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -81,9 +81,13 @@ la_status plan_dilated(const la_dims* d, const int32_t* w, const int32_t* r, int
   a.H = d->H;
   a.N = d->N;
   a.n_pairs = n_pairs;
-  int64_t rows = 0;
+  a.fin = -1;
   for (int32_t k = 0; k < n_pairs; ++k) {
     if (w[k] < 1 || r[k] < 1) return fail(LA_EINVAL, "every w and r must be >= 1");
+    if (r[k] == 1 && a.fin < 0) a.fin = k;
+  }
+  int64_t rows = 0;
+  for (int32_t k = 0; k < n_pairs; ++k) {
     a.w[k] = w[k];
     a.r[k] = r[k];
     a.inv_w[k] = 1.0f / (float)w[k];
@@ -92,33 +96,43 @@ la_status plan_dilated(const la_dims* d, const int32_t* w, const int32_t* r, int
     a.seg_rows[k] = (w[k] + r[k] - 1) / r[k];
     a.qtiles[k] = (a.seg_rows[k] + la::kDilatedQueryTile - 1) / la::kDilatedQueryTile;
     a.row_off[k] = rows;
-    rows += (int64_t)d->B * d->H * a.nseg[k] * a.seg_rows[k];
+    if (k != a.fin) rows += (int64_t)d->B * d->H * a.nseg[k] * a.seg_rows[k];
   }
   a.rows_total = rows;
-  // Workgroups in decreasing query-tile index (the key tiles of a workgroup
-  // grow with it), across all patterns, so that the longest start first.
-  // With the patterns sorted by qtiles, the levels split into bands over which
-  // the set of patterns having that tile index is fixed.
-  std::vector<int32_t> ord(n_pairs);
-  for (int32_t k = 0; k < n_pairs; ++k) ord[k] = k;
+  // Workgroups of the pair launch (every pattern but the finisher) in
+  // decreasing query-tile index (the key tiles of a workgroup grow with it),
+  // across all patterns, so that the longest start first. With the patterns
+  // sorted by qtiles, the levels split into bands over which the set of
+  // patterns having that tile index is fixed.
+  std::vector<int32_t> ord;
+  for (int32_t k = 0; k < n_pairs; ++k)
+    if (k != a.fin) ord.push_back(k);
+  const int32_t np = (int32_t)ord.size();
+  a.n_part = np;
   std::stable_sort(ord.begin(), ord.end(),
                    [&](int32_t x, int32_t y) { return a.qtiles[x] > a.qtiles[y]; });
   a.pre[0] = 0;
-  for (int32_t i = 0; i < n_pairs; ++i) {
+  for (int32_t i = 0; i < np; ++i) {
     a.order[i] = ord[i];
     a.pre[i + 1] = a.pre[i] + (int64_t)d->B * d->H * a.nseg[ord[i]];
   }
   int64_t wg = 0;
-  for (int32_t j = 0; j < n_pairs; ++j) {
-    const int32_t lo = j + 1 < n_pairs ? a.qtiles[ord[j + 1]] : 0;
+  for (int32_t j = 0; j < np; ++j) {
+    const int32_t lo = j + 1 < np ? a.qtiles[ord[j + 1]] : 0;
     a.band_top[j] = a.qtiles[ord[j]] - 1;
     a.band_per[j] = a.pre[j + 1];
     a.band_start[j] = wg;
     wg += (int64_t)(a.qtiles[ord[j]] - lo) * a.band_per[j];
   }
-  a.band_start[n_pairs] = wg;
+  a.band_start[np] = wg;
   if (wg > 0x7fffffffLL) return fail(LA_EUNSUPPORTED, "launch grid too large");
-  p.ws_bytes = align_up((size_t)rows * kDHead * sizeof(float)) + align_up((size_t)rows * sizeof(float));
+  if (a.fin >= 0 &&
+      (int64_t)d->B * d->H * a.nseg[a.fin] * a.qtiles[a.fin] > 0x7fffffffLL)
+    return fail(LA_EUNSUPPORTED, "launch grid too large");
+  // (a call whose only pattern is the finisher needs no workspace)
+  p.ws_bytes = rows == 0 ? 0
+                         : align_up((size_t)rows * kDHead * sizeof(float)) +
+                               align_up((size_t)rows * sizeof(float));
   return LA_OK;
 }
 
@@ -248,20 +262,24 @@ la_status la_dilated_forward(const la_dims* dims, const void* q, const void* k, 
   DilPlan p;
   st = plan_dilated(dims, seg_lens, dil_rates, n_pairs, p);
   if (st != LA_OK) return st;
-  if (!ext || !ext->workspace || ext->workspace_bytes < p.ws_bytes)
-    return fail(LA_EINVAL, "workspace missing or smaller than la_dilated_workspace_size()");
-  if (((uintptr_t)ext->workspace & (kAlign - 1)) != 0)
-    return fail(LA_EINVAL, "workspace must be 256-byte aligned");
+  if (p.ws_bytes > 0) {
+    if (!ext || !ext->workspace || ext->workspace_bytes < p.ws_bytes)
+      return fail(LA_EINVAL, "workspace missing or smaller than la_dilated_workspace_size()");
+    if (((uintptr_t)ext->workspace & (kAlign - 1)) != 0)
+      return fail(LA_EINVAL, "workspace must be 256-byte aligned");
+  }
   la::DilArgs& a = p.a;
   a.q = q;
   a.k = k;
   a.v = v;
   a.causal = causal;
   a.out = out;
-  a.lse = ext->lse;
-  a.ws_o = reinterpret_cast<float*>(ext->workspace);
-  a.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ext->workspace) +
-                                      align_up((size_t)a.rows_total * kDHead * sizeof(float)));
+  a.lse = ext ? ext->lse : nullptr;
+  if (p.ws_bytes > 0) {
+    a.ws_o = reinterpret_cast<float*>(ext->workspace);
+    a.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ext->workspace) +
+                                        align_up((size_t)a.rows_total * kDHead * sizeof(float)));
+  }
   a.scale_log2 = (float)(1.0 / sqrt((double)kDHead) * 1.4426950408889634);
   hipError_t e = la::launch_dilated(a, stream);
   if (e != hipSuccess) return fail(LA_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(e));

@@ -7,45 +7,39 @@
 // are read straight from Q, K, V as a strided view (row stride r*D): no gather
 // copy is made. Dense attention runs among them (Eq. 6), causal in position
 // when requested, and each pattern writes a partial (normalised O, lse) per
-// kept row. A second launch scatters and mixes: a row's output is the sum of
-// the partials of the patterns that kept it, weighted by exp(lse_k), i.e. by
-// the softmax denominators (Eqs. 7-10, "Mixture of Dilated Attentions");
-// rows a pattern skipped receive nothing from it.
+// kept row. A row's output is the sum of the partials of the patterns that
+// kept it, weighted by exp(lse_k), i.e. by the softmax denominators (Eqs.
+// 7-10, "Mixture of Dilated Attentions"); rows a pattern skipped receive
+// nothing from it. When a pattern has dilation 1 it keeps every row: it runs
+// last, in a launch of its own, and its workgroups mix the other patterns'
+// partials into their rows. Otherwise a combine launch scatters and mixes.
 #include "tile_core.h"
 #include "kernels.h"
 
 namespace la {
 
-__global__ __launch_bounds__(TileTraits<bf16>::kThreads)
-__attribute__((amdgpu_waves_per_eu(TileTraits<bf16>::kMinWavesPerEU)))
-void dilated_pair_kernel(DilArgs a) {
+// One query tile (128 kept rows from t0) of pattern k, segment seg, head bh:
+// dense attention (causal in position when requested) among the segment's
+// kept rows, run through the tile engine. Leaves each wave's running state in
+// wv; returns false if the tile holds no row.
+struct DilTile {
+  int32_t base, r, t0, qcount, qi, qpos;
+};
+
+__device__ __forceinline__ bool dilated_tile(const DilArgs& a, TileTraits<bf16>::Smem& sm,
+                                             TileTraits<bf16>::Wave& wv, int32_t k, int32_t seg,
+                                             int32_t bh, int32_t qt, DilTile& dt) {
   using TT = TileTraits<bf16>;
-  __shared__ TT::Smem sm;
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Blocks in launch order (no XCD remap: that would give one XCD all the
-  // longest workgroups): query-tile level descending across all patterns.
-  const int64_t wg = blockIdx.x;
-  if (wg >= a.band_start[a.n_pairs]) return;
-  int32_t j = 0;
-  while (j + 1 < a.n_pairs && wg >= a.band_start[j + 1]) ++j;
-  const int64_t off = wg - a.band_start[j];
-  const int32_t qt = a.band_top[j] - (int32_t)(off / a.band_per[j]);
-  const int64_t rem = off % a.band_per[j];
-  int32_t oi = 0;
-  while (oi < j && rem >= a.pre[oi + 1]) ++oi;
-  const int32_t k = a.order[oi];
-  const int32_t w = a.w[k], r = a.r[k], nseg = a.nseg[k];
-  const int64_t rest = rem - a.pre[oi];
-  const int32_t seg = (int32_t)(rest % nseg);
-  const int32_t bh = (int32_t)(rest / nseg);
+  const int32_t w = a.w[k], r = a.r[k];
   const int32_t h = bh % a.H;
   const int32_t sigma = seg * w;
   const int32_t L = min(w, a.N - sigma);
   const int32_t s = h % r;
   const int32_t n_rows = L > s ? (L - s + r - 1) / r : 0;
   const int32_t t0 = qt * kTQ;
-  if (t0 >= n_rows) return;
+  if (t0 >= n_rows) return false;
   const int32_t qcount = min(kTQ, n_rows - t0);
   const size_t head_elems = (size_t)a.N * kD;
   const bf16* qb = reinterpret_cast<const bf16*>(a.q) + bh * head_elems;
@@ -55,7 +49,6 @@ void dilated_pair_kernel(DilArgs a) {
   const int32_t qi = TT::qrow(wave, lane, 0);
   const int32_t qpos = base + r * (t0 + min(qi, qcount - 1));
   const bool dead = TT::kQW * wave >= qcount;  // no valid row in this wave
-  TT::Wave wv;
   TT::load_q(wv, qb, &qpos, lane);
   const int32_t hi = a.causal ? t0 + qcount - 1 : n_rows - 1;
   const int32_t n_tiles = (hi + kTK) / kTK;
@@ -71,9 +64,39 @@ void dilated_pair_kernel(DilArgs a) {
   const BiasRule br = {nullptr, 0, 0};
   const GlobInfo gi = {kGlobNone, nullptr, 0};
   run_tiles<bf16, false, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2);
+  dt = {base, r, t0, qcount, qi, qpos};
+  return true;
+}
+
+// Every pattern but the finisher: a partial (normalised O, lse) per kept row.
+__global__ __launch_bounds__(TileTraits<bf16>::kThreads)
+__attribute__((amdgpu_waves_per_eu(TileTraits<bf16>::kMinWavesPerEU)))
+void dilated_pair_kernel(DilArgs a) {
+  using TT = TileTraits<bf16>;
+  __shared__ TT::Smem sm;
+  const int32_t lane = threadIdx.x & 63;
+  // Blocks in launch order (no XCD remap: that would give one XCD all the
+  // longest workgroups): query-tile level descending across all patterns.
+  const int64_t wg = blockIdx.x;
+  if (wg >= a.band_start[a.n_part]) return;
+  int32_t j = 0;
+  while (j + 1 < a.n_part && wg >= a.band_start[j + 1]) ++j;
+  const int64_t off = wg - a.band_start[j];
+  const int32_t qt = a.band_top[j] - (int32_t)(off / a.band_per[j]);
+  const int64_t rem = off % a.band_per[j];
+  int32_t oi = 0;
+  while (oi < j && rem >= a.pre[oi + 1]) ++oi;
+  const int32_t k = a.order[oi];
+  const int32_t nseg = a.nseg[k];
+  const int64_t rest = rem - a.pre[oi];
+  const int32_t seg = (int32_t)(rest % nseg);
+  const int32_t bh = (int32_t)(rest / nseg);
+  TT::Wave wv;
+  DilTile dt;
+  if (!dilated_tile(a, sm, wv, k, seg, bh, qt, dt)) return;
   const float l_tot = TT::row_sum(wv.l[0]);
-  if (qi < qcount) {
-    const int64_t prow = a.row_off[k] + ((int64_t)bh * nseg + seg) * a.seg_rows[k] + t0 + qi;
+  if (dt.qi < dt.qcount) {
+    const int64_t prow = a.row_off[k] + ((int64_t)bh * nseg + seg) * a.seg_rows[k] + dt.t0 + dt.qi;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     TT::store_row_f32(a.ws_o + prow * kD, wv, 0, inv, lane);
     if (TT::row_leader(lane))
@@ -154,14 +177,92 @@ __global__ __launch_bounds__(256) void dilated_combine_kernel(DilArgs a) {
   if (a.lse && d4 == 0) a.lse[row] = S > 0.f ? L + __logf(S) : kNegInf;
 }
 
+// The finisher pattern (dilation 1: it keeps every row of its segments),
+// whose workgroups, after their own tile, mix the partials of the patterns
+// that also cover their rows with weights exp(lse_k) (LongNet page, §3.4
+// "Mixture of Dilated Attentions", Eqs. 7-10) and write the final rows. The
+// pair launch before it has written every partial. Workgroups in decreasing
+// query-tile index (the longest first).
+__global__ __launch_bounds__(TileTraits<bf16>::kThreads)
+__attribute__((amdgpu_waves_per_eu(TileTraits<bf16>::kMinWavesPerEU)))
+void dilated_finish_kernel(DilArgs a) {
+  using TT = TileTraits<bf16>;
+  __shared__ TT::Smem sm;
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t kf = a.fin;
+  const int32_t nseg = a.nseg[kf];
+  const int64_t per = (int64_t)a.B * a.H * nseg;
+  const int64_t wg = blockIdx.x;
+  if (wg >= per * a.qtiles[kf]) return;
+  const int32_t qt = a.qtiles[kf] - 1 - (int32_t)(wg / per);
+  const int64_t rest = wg % per;
+  const int32_t seg = (int32_t)(rest % nseg);
+  const int32_t bh = (int32_t)(rest / nseg);
+  TT::Wave wv;
+  DilTile dt;
+  if (!dilated_tile(a, sm, wv, kf, seg, bh, qt, dt)) return;
+  const bool valid = dt.qi < dt.qcount;
+  const float l_tot = TT::row_sum(wv.l[0]);
+  // running mixture: M = max lse, S = sum e^{lse - M}, wv.o = sum e^{lse - M} O
+  float M = l_tot > 0.f ? (wv.m[0] + __log2f(l_tot)) * kLn2 : kNegInf;
+  float S = M == kNegInf ? 0.f : 1.f;
+  TT::scale_acc(wv, l_tot > 0.f ? 1.f / l_tot : 0.f);
+  const int32_t i = dt.qpos;  // this lane's row position (the finisher keeps every row)
+  const int32_t h = bh % a.H;
+  const int32_t d0 = 4 * (lane >> 5);  // this lane holds d = 32db + 8j + d0 + [0, 4)
+  for (int32_t k = 0; k < a.n_pairs; ++k) {
+    if (k == kf) continue;
+    const int32_t w = a.w[k], r = a.r[k];
+    const int32_t sg = div_small(i, w, a.inv_w[k]), off = i - sg * w;
+    const int32_t m = div_small(off, r, a.inv_r[k]);
+    const int32_t hs = h - div_small(h, r, a.inv_r[k]) * r;  // h mod r
+    // pattern k covers row i iff its offset in the segment is congruent to h mod r
+    const bool cov = valid && off - m * r == hs;
+    const int64_t prow = a.row_off[k] + ((int64_t)bh * a.nseg[k] + sg) * a.seg_rows[k] + m;
+    const float lk = cov ? a.ws_lse[prow] : kNegInf;
+    const bool use = lk != kNegInf;
+    if (__ballot(use) == 0ull) continue;
+    if (use) {
+      const float Mn = fmaxf(M, lk);
+      const float sc = M == kNegInf ? 0.f : __expf(M - Mn);
+      const float wk = __expf(lk - Mn);
+      const float* src = a.ws_o + prow * kD + d0;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(src + 32 * db + 8 * jj);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            wv.o[db][4 * jj + e] = wv.o[db][4 * jj + e] * sc + wk * x[e];
+        }
+      }
+      S = S * sc + wk;
+      M = Mn;
+    }
+  }
+  if (valid) {
+    const float inv = S > 0.f ? 1.f / S : 0.f;
+    bf16* dst = reinterpret_cast<bf16*>(a.out) + ((size_t)bh * a.N + i) * kD;
+    TT::store_row(dst, wv, 0, inv, lane);
+    if (a.lse && TT::row_leader(lane))
+      a.lse[(size_t)bh * a.N + i] = S > 0.f ? M + __logf(S) : kNegInf;
+  }
+}
+
 static_assert(kMaxPairs == 16, "one thread per (row, pattern) in a 256-thread block");
 
 hipError_t launch_dilated(const DilArgs& a, hipStream_t stream) {
-  const int64_t grid = a.band_start[a.n_pairs];
+  const int64_t grid = a.band_start[a.n_part];
   if (grid > 0) {
     hipLaunchKernelGGL(dilated_pair_kernel, dim3((uint32_t)grid), dim3(TileTraits<bf16>::kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (a.fin >= 0) {
+    const int64_t g = (int64_t)a.B * a.H * a.nseg[a.fin] * a.qtiles[a.fin];
+    hipLaunchKernelGGL(dilated_finish_kernel, dim3((uint32_t)g), dim3(TileTraits<bf16>::kThreads), 0, stream, a);
+    return hipGetLastError();
   }
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   hipLaunchKernelGGL(dilated_combine_kernel, dim3((uint32_t)((rows + kCombineRows - 1) / kCombineRows)),

@@ -47,12 +47,17 @@ struct DilArgs {
   // (the last band down to 0), where exactly patterns order[0..j] have a tile
   // t, band_per[j] workgroups per level. pre[i]: workgroups of one level that
   // belong to order[0..i-1].
+  // Finisher: a pattern of dilation 1 (it covers every row), or -1. When
+  // there is one, the pair launch runs the other n_part patterns, and the
+  // finisher's own launch mixes their partials into its rows; otherwise all
+  // patterns write partials (n_part == n_pairs) and a combine launch mixes.
+  int32_t fin, n_part;
   int32_t order[kMaxPairs];
   int32_t band_top[kMaxPairs];
   int64_t band_per[kMaxPairs];
   int64_t pre[kMaxPairs + 1];
   int64_t band_start[kMaxPairs + 1];  // first workgroup of band j; [n_pairs]: total
-  int64_t row_off[kMaxPairs];   // first partial row of pattern k
+  int64_t row_off[kMaxPairs];   // first partial row of pattern k (not the finisher's)
   int64_t rows_total;           // partial rows of all patterns
   float* ws_o;                  // [rows_total][D]
   float* ws_lse;                // [rows_total]

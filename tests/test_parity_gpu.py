@@ -135,6 +135,10 @@ SMALL_DIL = [
     ("longnet-uncovered", 128, 2, ((64, 2),), True),
     ("longnet-dense", 190, 2, ((190, 1),), True),
     ("longnet-multitile", 1000, 3, ((400, 1), (1000, 2)), True),
+    # no dilation-1 pattern: every pattern writes partials, a combine launch mixes
+    ("longnet-no-finisher", 333, 5, ((64, 2), (128, 3), (333, 5)), True),
+    # the dilation-1 pattern listed after others, and a second one among the partials
+    ("longnet-finisher-order", 400, 4, ((128, 2), (64, 1), (200, 1), (400, 4)), True),
 ]
 
 
