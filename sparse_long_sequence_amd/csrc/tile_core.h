@@ -922,12 +922,21 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
     bias_on = br.key_global_is_same_kind ? any_g : !all_g;
     all_same = br.key_global_is_same_kind ? all_g : !any_g;
   }
+  // A tile every pair of which is allowed for all of the workgroup's rows
+  // (the rule needs no mask) and that takes no bias is full for every wave
+  // holding rows: a uniform test instead of the per-wave classification.
   int32_t cls[SB];
   bool fast = !bias_on;
+  if (!bias_on && mr.need_mask == 0 && only_sb < 0) {
 #pragma unroll
-  for (int sb = 0; sb < SB; ++sb) {
-    cls[sb] = (dead || (only_sb >= 0 && sb != only_sb)) ? kEmpty : classify<T>(mr, kcount, sb, r0, r1);
-    fast = fast && cls[sb] == kFull;
+    for (int sb = 0; sb < SB; ++sb) cls[sb] = dead ? kEmpty : kFull;
+    fast = !dead;
+  } else {
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      cls[sb] = (dead || (only_sb >= 0 && sb != only_sb)) ? kEmpty : classify<T>(mr, kcount, sb, r0, r1);
+      fast = fast && cls[sb] == kFull;
+    }
   }
   if (fast) {
     // Every sub-tile's scores first: the later sub-tiles' score MFMAs then
