@@ -42,7 +42,8 @@
  *     denominator, lse_i = ln sum_j c_ij exp(s_ij).
  *   - Ownership: the caller owns every buffer. The library allocates nothing,
  *     keeps no pointer after returning, never writes its inputs, and fully
- *     overwrites out, lse and the workspace. out must not alias an input.
+ *     overwrites out and lse. The workspace is scratch (see la_attn_ext for the
+ *     part of it that must start at zero). out must not alias an input.
  *   - All work is enqueued on `stream` (0 = the null stream); the call returns
  *     without synchronising and issues no device-to-host copy.
  *   - Errors: host-detectable argument errors return LA_EINVAL and enqueue
@@ -95,7 +96,8 @@ typedef struct {
 /* Optional extras of la_dilated_forward; pass NULL for none. */
 typedef struct {
   float *lse;      /* device fp32 [B,H,N] or NULL; -inf where no pattern covers a row */
-  void *workspace; /* device scratch of la_dilated_workspace_size() bytes, 256-byte aligned */
+  void *workspace; /* device scratch of la_dilated_workspace_size() bytes, 256-byte aligned
+                    * (NULL when that size is 0) */
   size_t workspace_bytes;
 } la_dilated_ext;
 
@@ -119,7 +121,10 @@ la_status la_attn_forward(const la_dims *dims, const void *q, const void *k, con
  *                       truncated at N. Head h uses offset h mod r_k.
  *  causal               0 or 1: within a segment, key position <= query position.
  *  out                  device bf16 [B,H,N,D]; rows no pattern covers are 0.
- * Requires ext->workspace of la_dilated_workspace_size() bytes. */
+ * The first pattern with r_k == 1 (it keeps every row) runs last and mixes the
+ * other patterns' partials into its rows, so it needs no workspace of its own.
+ * Requires ext->workspace of la_dilated_workspace_size() bytes when that size is
+ * non-zero (it needs no initialisation); ext may be NULL when it is zero. */
 la_status la_dilated_forward(const la_dims *dims, const void *q, const void *k, const void *v,
                              const int32_t *seg_lens, const int32_t *dil_rates, int32_t n_pairs,
                              int32_t causal, void *out, hipStream_t stream,
