@@ -27,8 +27,9 @@
 //   * the window is inclusive, |j-i| <= d*R, and keys outside [0,N) are dropped;
 //   * causal means j <= i for every pair, band, global row and global column;
 //   * a global key inside the band counts once (set union);
-//   * the scalar relative bias applies only to pairs of the same kind (both
-//     global or both non-global), indexed by clamp(j-i, -k, k);
+//   * the scalar relative bias and the relative key vectors apply only to
+//     pairs of the same kind (both global or both non-global), indexed by the
+//     label clamp(j-i, -k, k); mixed pairs get neither;
 //   * with separate global projections, a global row i uses qg_i, kg_j, vg_j
 //     for every key j; non-global rows use q, k, v, also for global columns;
 //   * LongNet head h keeps, in each segment, the positions whose offset from
@@ -214,19 +215,23 @@ int32_t lo_longnet_mult_rows(int32_t N, int32_t head, const int32_t* w, const in
 // q, k, v: [B,H,N,D]; qg, kg, vg: all null (shared projections) or all
 // [B,H,N,D] (Longformer page, §3.4 "Separate Linear Projections for Local vs.
 // Global Attention"). dilation: [H] (null = all 1). rel_bias: [H][2*rel_k+1]
-// or null (ETC page, §3.4 "Relative Position Encoding", clipping at k; here
-// the scalar form of the per-label term). sel: n_sel (b,h,i) triples or null
-// for all B*H*N rows. out: [n_sel][D]; lse: [n_sel].
+// or null, a scalar added to the scaled logit per label. rel_vec:
+// [H][2*rel_k+1][D] or null, the learned key-side vector a_l of each label:
+// the logit becomes q_i . (k_j + a_l) / sqrt(D) (ETC page, §3.4 "Relative
+// Position Encoding", Steps 1-3: labels clip j - i at k; one vector per label
+// and head). Either, both or neither may be given. sel: n_sel (b,h,i) triples
+// or null for all B*H*N rows. out: [n_sel][D]; lse: [n_sel].
 int32_t lo_attn_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q, const double* k,
                      const double* v, const double* qg, const double* kg, const double* vg,
                      const int32_t* gidx, int32_t n_global, int32_t radius, const int32_t* dilation,
-                     int32_t causal, const double* rel_bias, int32_t rel_k, const int32_t* sel,
-                     int64_t n_sel, double* out, double* lse, int32_t n_threads) {
+                     int32_t causal, const double* rel_bias, const double* rel_vec, int32_t rel_k,
+                     const int32_t* sel, int64_t n_sel, double* out, double* lse,
+                     int32_t n_threads) {
   if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || radius < 0 || n_global < 0) return -1;
   if (!q || !k || !v || !out || !lse) return -1;
   if ((qg || kg || vg) && !(qg && kg && vg)) return -1;
   if (n_global > 0 && !gidx) return -1;
-  if (rel_bias && rel_k < 0) return -1;
+  if ((rel_bias || rel_vec) && rel_k < 0) return -1;
   if (dilation)
     for (int32_t h = 0; h < H; ++h)
       if (dilation[h] < 1) return -1;
@@ -249,12 +254,21 @@ int32_t lo_attn_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q
     for (int32_t j = 0; j < N; ++j)  // the explicit mask row c_i,:
       weight[j] = mask_entry(i, j, ig, is_glob[j] != 0, radius, dil, causal);
     const double* tab = rel_bias ? rel_bias + (size_t)h * (2 * rel_k + 1) : nullptr;
+    const double* vec = rel_vec ? rel_vec + (size_t)h * (2 * rel_k + 1) * D : nullptr;
+    const double scale = 1.0 / std::sqrt((double)D);
     auto bias = [&](int32_t j) -> double {
-      if (!tab) return 0.0;
+      if (!tab && !vec) return 0.0;
       if ((is_glob[j] != 0) != ig) return 0.0;  // mixed global/non-global pair
       int64_t dlt = (int64_t)j - i;
       dlt = std::max<int64_t>(-rel_k, std::min<int64_t>(rel_k, dlt));
-      return tab[dlt + rel_k];
+      double b = tab ? tab[dlt + rel_k] : 0.0;
+      if (vec) {  // q_i . a_l / sqrt(D): the key-side vector's share of the logit
+        const double* al = vec + (size_t)(dlt + rel_k) * D;
+        double dot = 0.0;
+        for (int32_t d = 0; d < D; ++d) dot += qi[d] * al[d];
+        b += dot * scale;
+      }
+      return b;
     };
     attend_row(N, D, qi, kb, vb, weight, bias, out + (size_t)x * D, lse + x);
   });

@@ -109,9 +109,12 @@ def bf_attend(qi, keys, K, V, bias=None):
     return out, M + math.log(Z)
 
 
-def bf_band_head(q, k, v, G, R, d, causal, qg=None, kg=None, vg=None, relb=None):
+def bf_band_head(q, k, v, G, R, d, causal, qg=None, kg=None, vg=None, relb=None, relv=None):
     """Longformer pattern by enumeration: keys i + d*m, m in [-R, R] (causal:
-    [-R, 0]), inside [0, N); plus the global columns; global rows see all."""
+    [-R, 0]), inside [0, N); plus the global columns; global rows see all.
+    relv ([2k+1][D]): ETC's key-side label vectors, the logit written out as
+    q_i . (k_j + a_l) / sqrt(D) for same-kind pairs (bf_attend adds the
+    q_i . k_j / sqrt(D) part, so the bias is the remaining q_i . a_l / sqrt(D))."""
     N = len(q)
     Gs = set(G)
     outs, lses = [], []
@@ -126,13 +129,17 @@ def bf_band_head(q, k, v, G, R, d, causal, qg=None, kg=None, vg=None, relb=None)
             keys = sorted(ks)
             Q, K, V = q, k, v
         bias = None
-        if relb is not None:
-            kk = (len(relb) - 1) // 2
+        if relb is not None or relv is not None:
+            kk = (len((relb if relb is not None else relv)) - 1) // 2
 
-            def bias(j, i=i, kk=kk):
+            def bias(j, i=i, kk=kk, Qi=Q[i]):
                 if (j in Gs) != (i in Gs):
                     return 0.0
-                return relb[max(-kk, min(kk, j - i)) + kk]
+                lab = max(-kk, min(kk, j - i)) + kk
+                b = relb[lab] if relb is not None else 0.0
+                if relv is not None:
+                    b += sum(a * x for a, x in zip(Qi, relv[lab])) / math.sqrt(len(Qi))
+                return b
         o, l = bf_attend(Q[i], keys, K, V, bias)
         outs.append(o)
         lses.append(l)
@@ -379,12 +386,15 @@ def pin_brute_force_band(lib):
         q, k, v = rand_qkv(rng, 1, H, N, D)
         qg, kg, vg = rand_qkv(rng, 1, H, N, D) if sep else (None, None, None)
         relb = rng.standard_normal((H, 7)) if t % 4 == 2 else None
-        o, l = oracle.attn_rows(q, k, v, G, R, dil, causal, relb, qg, kg, vg, lib=lib)
+        relv = rng.standard_normal((H, 7, D)) if t % 4 in (1, 2) else None
+        o, l = oracle.attn_rows(q, k, v, G, R, dil, causal, relb, qg, kg, vg, lib=lib,
+                                rel_vec=relv)
         for h in range(H):
             ob, lb = bf_band_head(q[0, h].tolist(), k[0, h].tolist(), v[0, h].tolist(), G, R,
                                   dil[h], causal,
                                   *(x[0, h].tolist() for x in (qg, kg, vg)) if sep else (None,) * 3,
-                                  relb=None if relb is None else relb[h].tolist())
+                                  relb=None if relb is None else relb[h].tolist(),
+                                  relv=None if relv is None else relv[h].tolist())
             assert np.abs(o[0, h] - ob).max() < 1e-12, (t, h)
             assert np.abs(l[0, h] - lb).max() < 1e-12, (t, h)
 
@@ -402,6 +412,36 @@ def pin_etc_four_pieces(lib):
         o, l = oracle.attn_rows(*cat, range(ng), r, rel_bias=relb[None], lib=lib)
         assert np.abs(o[0, 0] - ob).max() < 1e-12
         assert np.abs(l[0, 0] - lb).max() < 1e-12
+
+
+def pin_relvec_reduces_to_scalar(lib):
+    """With every query's component 0 equal to sqrt(D) and a_l = b_l e_0, the
+    vector term q_i . a_l / sqrt(D) is exactly the scalar b_l: the vector path
+    must then equal the (separately pinned) scalar-table path. Separate global
+    projections and causal windows included."""
+    rng = np.random.default_rng(12)
+    B, H, N, D, k = 1, 3, 37, 4, 5
+    for t in range(4):
+        q, kk, v = rand_qkv(rng, B, H, N, D)
+        qg, kg, vg = rand_qkv(rng, B, H, N, D) if t % 2 else (None, None, None)
+        q[..., 0] = math.sqrt(D)
+        if qg is not None:
+            qg[..., 0] = math.sqrt(D)
+        b = rng.standard_normal((H, 2 * k + 1))
+        a = np.zeros((H, 2 * k + 1, D))
+        a[..., 0] = b
+        G, R, causal = (0, 3, 17, 36), 4, t >= 2
+        o1, l1 = oracle.attn_rows(q, kk, v, G, R, [1, 2, 1], causal, b, qg, kg, vg, lib=lib)
+        o2, l2 = oracle.attn_rows(q, kk, v, G, R, [1, 2, 1], causal, None, qg, kg, vg, lib=lib,
+                                  rel_vec=a)
+        assert np.abs(o1 - o2).max() < 1e-12, t
+        assert np.abs(l1 - l2).max() < 1e-12, t
+        # both together add up: scalar b plus the vector's b again gives 2b
+        o3, l3 = oracle.attn_rows(q, kk, v, G, R, [1, 2, 1], causal, b, qg, kg, vg, lib=lib,
+                                  rel_vec=a)
+        o4, l4 = oracle.attn_rows(q, kk, v, G, R, [1, 2, 1], causal, 2 * b, qg, kg, vg, lib=lib)
+        assert np.abs(o3 - o4).max() < 1e-12, t
+        assert np.abs(l3 - l4).max() < 1e-12, t
 
 
 def pin_brute_force_longnet(lib):
@@ -472,7 +512,8 @@ def pin_sampled_rows_match_full(lib):
 PINS = [pin_mask_matches_enumeration, pin_counts_closed_form, pin_counts_full_workloads,
         pin_longnet_counts, pin_longnet_worked_example, pin_longnet_offsets_partition,
         pin_dense_special_cases, pin_global_rows_are_full_rows, pin_brute_force_band,
-        pin_etc_four_pieces, pin_brute_force_longnet, pin_longnet_paths_agree,
+        pin_etc_four_pieces, pin_relvec_reduces_to_scalar, pin_brute_force_longnet,
+        pin_longnet_paths_agree,
         pin_rows_sum_to_one, pin_uncovered_rows, pin_sampled_rows_match_full]
 
 
@@ -488,7 +529,13 @@ MUTANTS = [
     ("exclusive-window-end", "return steps >= -(int64_t)radius && steps <= (int64_t)radius;",
      "return steps >= -(int64_t)radius && steps < (int64_t)radius;"),
     ("dropped-scale", "logit[j] = dot * scale + bias(j);", "logit[j] = dot + bias(j);"),
-    ("bias-index-sign", "return tab[dlt + rel_k];", "return tab[rel_k - dlt];"),
+    ("bias-index-sign", "double b = tab ? tab[dlt + rel_k] : 0.0;",
+     "double b = tab ? tab[rel_k - dlt] : 0.0;"),
+    ("relvec-label-sign", "const double* al = vec + (size_t)(dlt + rel_k) * D;",
+     "const double* al = vec + (size_t)(rel_k - dlt) * D;"),
+    ("relvec-unscaled", "b += dot * scale;", "b += dot;"),
+    ("relvec-against-key", "for (int32_t d = 0; d < D; ++d) dot += qi[d] * al[d];",
+     "for (int32_t d = 0; d < D; ++d) dot += kb[(size_t)j * D + d] * al[d];"),
     ("bias-on-mixed-pairs", "if ((is_glob[j] != 0) != ig) return 0.0;", ""),
     ("shared-keys-for-global-rows", "const double* kb = (sep ? kg : k) + head_off;",
      "const double* kb = (sep ? k : k) + head_off;"),
