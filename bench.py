@@ -60,6 +60,7 @@ class Call:
         self.q, self.k, self.v = d(inp.q), d(inp.k), d(inp.v)
         self.qg, self.kg, self.vg = d(inp.qg), d(inp.kg), d(inp.vg)
         self.rb = d(inp.rel_bias)
+        self.rv = d(inp.rel_vec)
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty(self.q.shape[:3], dtype=torch.float32, device=dev)
         self.g = (torch.tensor(w.global_idx, dtype=torch.int32, device=dev)
@@ -77,6 +78,7 @@ class Call:
         else:
             self.bound = la.bind_attn(self.q, self.k, self.v, self.g, w.radius, w.dilation,
                                       w.causal, self.rb, out=self.out, lse=self.lse, qg=self.qg,
+                                      rel_vec=self.rv,
                                       kg=self.kg, vg=self.vg, workspace=self.ws)
 
     def __call__(self):
@@ -127,8 +129,8 @@ def cpu_baseline(w, budget_s=20.0):
     cores = max(1, min(cores, 16))
     inp = W.make_inputs(w)
     f = lambda t: None if t is None else t.to(torch.float64).numpy()
-    q, k, v, qg, kg, vg, rb = (f(x) for x in (inp.q, inp.k, inp.v, inp.qg, inp.kg, inp.vg,
-                                              inp.rel_bias))
+    q, k, v, qg, kg, vg, rb, rv = (f(x) for x in (inp.q, inp.k, inp.v, inp.qg, inp.kg, inp.vg,
+                                                  inp.rel_bias, inp.rel_vec))
     total_rows = w.B * w.H * w.N
     n = min(total_rows, 2048)
     elapsed = 0.0
@@ -139,7 +141,7 @@ def cpu_baseline(w, budget_s=20.0):
             oracle.longnet_rows(q, k, v, w.pairs, w.causal, sel=sel, n_threads=cores)
         else:
             oracle.attn_rows(q, k, v, w.global_idx, w.radius, w.dilation, w.causal, rb, qg, kg, vg,
-                             sel=sel, n_threads=cores)
+                             sel=sel, n_threads=cores, rel_vec=rv)
         elapsed = time.perf_counter() - t
         if elapsed >= budget_s / 4 or n >= total_rows:
             break

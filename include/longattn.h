@@ -79,7 +79,8 @@ typedef struct {
 typedef struct {
   /* rel_bias holds H*(2*rel_k+1) fp32 entries; entry [h][clamp(j-i,-rel_k,rel_k)+rel_k]
    * is added to the logit of every pair (i,j) whose members are of the same kind
-   * (both global or both non-global). Required (> 0) iff rel_bias != NULL. */
+   * (both global or both non-global). Required (> 0) iff rel_bias != NULL or
+   * rel_vec != NULL. */
   int32_t rel_k;
   /* Separate projections for the global rows: all three or none, dims as q.
    * A global row i then uses qg_i, kg_j, vg_j for every key j; non-global rows
@@ -91,6 +92,14 @@ typedef struct {
    * is overwritten. Calls that share a workspace must not overlap in time. */
   void *workspace;
   size_t workspace_bytes;
+  /* Key-side relative-position vectors (ETC page, §3.4 "Relative Position
+   * Encoding", Steps 2-3): device fp32 [H][2*rel_k+1][D], 16-byte aligned, or
+   * NULL. For a same-kind pair (i,j) with label l = clamp(j-i,-rel_k,rel_k) the
+   * logit becomes q_i . (k_j + a_{h,l}) / sqrt(D) (plus rel_bias when both are
+   * given). The kernels precompute q_i . a_{h,l} per query row and label, as the
+   * page's implementation note describes; such calls use 2*rel_k+1 fp32 of LDS
+   * per query row of a workgroup beyond the usual. */
+  const float *rel_vec;
 } la_attn_ext;
 
 /* Optional extras of la_dilated_forward; pass NULL for none. */

@@ -182,8 +182,12 @@ la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, con
   if (dims->H > la::kMaxHeadsDil) return fail(LA_EUNSUPPORTED, "H above 64");
   for (int32_t h = 0; h < dims->H; ++h) a.dil[h] = dilation ? dilation[h] : 1;
   const int32_t rel_k = ext ? ext->rel_k : 0;
-  if (rel_bias && rel_k < 1) return fail(LA_EINVAL, "rel_bias needs ext->rel_k >= 1");
-  if (!rel_bias && rel_k != 0) return fail(LA_EINVAL, "ext->rel_k set without rel_bias");
+  const float* rel_vec = ext ? ext->rel_vec : nullptr;
+  if ((rel_bias || rel_vec) && rel_k < 1)
+    return fail(LA_EINVAL, "rel_bias / ext->rel_vec need ext->rel_k >= 1");
+  if (!rel_bias && !rel_vec && rel_k != 0)
+    return fail(LA_EINVAL, "ext->rel_k set without rel_bias or ext->rel_vec");
+  if (rel_vec && !aligned16(rel_vec)) return fail(LA_EINVAL, "ext->rel_vec must be 16-byte aligned");
   if (rel_k > la::kMaxRelK) return fail(LA_EUNSUPPORTED, "rel_k above 31");
   const void *qg = q, *kg = k, *vg = v;
   if (ext && (ext->qg || ext->kg || ext->vg)) {
@@ -216,6 +220,7 @@ la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, con
   a.radius = radius;
   a.causal = causal;
   a.rel_bias = rel_bias;
+  a.rel_vec = rel_vec;
   a.rel_k = rel_k;
   a.out = out;
   a.lse = lse;

@@ -41,6 +41,82 @@ __device__ __forceinline__ void load_bias_table(typename TileTraits<T>::Smem& sm
     sm.bias[tid] = a.rel_bias[h * (2 * a.rel_k + 1) + tid] * kInvScale;
 }
 
+// With key-side label vectors a_l (ETC page, §3.4 "Relative Position
+// Encoding", Step 3 and its implementation note): the workgroup's table of
+// q_i . a_l for each of its query rows and each label, in q.k units, plus the
+// scalar label bias (times sqrt(D)) when one is given too. Row r's query is
+// q[pos(r)]; rt holds kTQ rows of 2k+1 entries. The head's label vectors are
+// staged in `stage` (an LDS buffer not yet in use, at least (2k+1) * D fp32);
+// each thread holds a half row of its query in registers and sums one label
+// in kTPR. Ends with a barrier.
+static_assert(sizeof(TileTraits<bf16>::Smem::v) >= (2 * kMaxRelK + 1) * kD * sizeof(float) &&
+                  sizeof(TileTraits<float>::Smem::v) >= (2 * kMaxRelK + 1) * kD * sizeof(float),
+              "the V buffers stage the label vectors");
+
+template <typename T, typename Pos>
+__device__ __forceinline__ void build_row_table(float* rt, float* stage, const AttnArgs& a,
+                                                int32_t h, const T* qb, Pos pos, int32_t tid) {
+  using TT = TileTraits<T>;
+  constexpr int32_t kTPR = TT::kThreads / TT::kTQ;  // threads per query row
+  const int32_t nl = 2 * a.rel_k + 1;
+  const f32x4* av = reinterpret_cast<const f32x4*>(a.rel_vec + (size_t)h * nl * kD);
+  for (int32_t x = tid; x < nl * (kD / 4); x += TT::kThreads)
+    reinterpret_cast<f32x4*>(stage)[x] = av[x];
+  __syncthreads();
+  const int32_t r = tid % TT::kTQ, sub = tid / TT::kTQ;  // sub is the same across a wave
+  const T* qr = qb + (size_t)pos(r) * kD;
+  const float* sb = a.rel_bias ? a.rel_bias + h * nl : nullptr;
+  // Half a query row at a time in registers; this thread's labels sub,
+  // sub + kTPR, ... in groups of kGroup; each partial sum goes straight to the
+  // thread's own table entries (the second half adds to the first).
+  constexpr int32_t kGroup = 8;
+#pragma unroll 1
+  for (int32_t d0 = 0; d0 < kD; d0 += 32) {
+    float qv[32];
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 x = ldg16(qr + d0 + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qv[8 * c + 2 * e] = __builtin_bit_cast(float, x[e] << 16);
+          qv[8 * c + 2 * e + 1] = __builtin_bit_cast(float, x[e] & 0xffff0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const f32x4 x = __builtin_bit_cast(f32x4, ldg16(qr + d0 + 4 * c));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv[4 * c + e] = x[e];
+      }
+    }
+#pragma unroll 1
+    for (int32_t j0 = 0; sub + j0 * kTPR < nl; j0 += kGroup) {
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        const int32_t l = sub + (j0 + j) * kTPR;
+        if (l < nl) {
+          const f32x4* al = reinterpret_cast<const f32x4*>(stage + l * kD + d0);
+          float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+          for (int c = 0; c < 8; c += 2) {
+            const f32x4 x0 = al[c], x1 = al[c + 1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              s0 = __builtin_fmaf(qv[4 * c + e], x0[e], s0);
+              s1 = __builtin_fmaf(qv[4 * c + 4 + e], x1[e], s1);
+            }
+          }
+          float* dst = rt + r * nl + l;
+          *dst = (d0 == 0 ? (sb ? sb[l] * kInvScale : 0.f) : *dst) + (s0 + s1);
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // band workgroup: one query tile of one residue class (positions c + d*t)
 // ---------------------------------------------------------------------------
@@ -48,7 +124,7 @@ __device__ __forceinline__ void load_bias_table(typename TileTraits<T>::Smem& sm
 // compiled without its code).
 template <typename T, bool BIAS>
 __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileTraits<T>::Smem& sm,
-                                               int32_t bw) {
+                                               float* rowtab, int32_t bw) {
   using TT = TileTraits<T>;
   using O = typename OutT<T>::type;
   constexpr int32_t kTQ = TT::kTQ;
@@ -88,6 +164,9 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   const int32_t qi = TT::qrow(wave, lane, 0);
   const int32_t qpos = qbase + d * min(qi, qcount - 1);
   const bool dead = TT::kQW * wave >= qcount;  // no valid row in this wave
+  if (BIAS && a.rel_vec)  // before the wave state is live
+    build_row_table<T>(rowtab, reinterpret_cast<float*>(&sm.v[0][0]), a, h, qb,
+                       [&](int32_t r) { return qbase + d * min(r, qcount - 1); }, tid);
   typename TT::Wave w;
   TT::load_q(w, qb, &qpos, lane);
 
@@ -96,7 +175,7 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   const int32_t lo = max(0, t0 - R);
   const int32_t hi = a.causal ? (t0 + qcount - 1) : min(n_c - 1, t0 + qcount - 1 + R);
   const int32_t n_band = (hi - lo + 1 + kTK - 1) / kTK;
-  const bool want_bias = a.rel_bias != nullptr;
+  const bool want_bias = a.rel_bias != nullptr || a.rel_vec != nullptr;
   GlobInfo gi = {kGlobNone, a.gidx, a.n_global};
   if (want_bias && a.n_global > 0) {
     if (hi - lo + 1 <= 32 * kGMaskWords) {
@@ -106,7 +185,8 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
       gi.mode = kGlobSearch;
     }
   }
-  const BiasRule br = {want_bias ? sm.bias : nullptr, a.rel_k, 0};
+  const BiasRule br = {!want_bias ? nullptr : a.rel_vec ? rowtab : sm.bias, a.rel_k, 0,
+                       a.rel_vec ? 2 * a.rel_k + 1 : 0};
 
   auto band_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = lo + n * kTK;
@@ -280,7 +360,8 @@ __device__ __forceinline__ void merge_global_tile(float* ws_o, float* ws_lse, co
 // ---------------------------------------------------------------------------
 template <typename T, bool BIAS>
 __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
-                                                 typename TileTraits<T>::Smem& sm, int32_t gw) {
+                                                 typename TileTraits<T>::Smem& sm, float* rowtab,
+                                                 int32_t gw) {
   using TT = TileTraits<T>;
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -299,7 +380,7 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   if (a.causal) j1 = min(j1, i_max + 1);
   const int32_t n_tiles = j1 > j0 ? (j1 - j0 + kTK - 1) / kTK : 0;
   load_bias_table<T>(sm, a, h, tid);
-  const bool want_bias = a.rel_bias != nullptr;
+  const bool want_bias = a.rel_bias != nullptr || a.rel_vec != nullptr;
   GlobInfo gi = {kGlobNone, a.gidx, a.n_global};
   if (want_bias && n_tiles > 0) {
     build_gmask<T>(sm, a.gidx, a.n_global, j0, 1, j1 - j0, tid);  // j1 - j0 <= chunk_len
@@ -309,6 +390,9 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   const T* qb = reinterpret_cast<const T*>(a.qg) + bh * head_elems;
   const T* kb = reinterpret_cast<const T*>(a.kg) + bh * head_elems;
   const T* vb = reinterpret_cast<const T*>(a.vg) + bh * head_elems;
+  if (BIAS && a.rel_vec)
+    build_row_table<T>(rowtab, reinterpret_cast<float*>(&sm.v[0][0]), a, h, qb,
+                       [&](int32_t r) { return qidx[min(r, qcount - 1)]; }, tid);
   // A tile of at most half the workgroup's rows (bf16: two key sub-tiles per
   // tile) keeps every wave busy: waves w and w + 2 take the same rows, wave w
   // the first 32 keys of each tile and wave w + 2 the last 32, and their
@@ -328,7 +412,8 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
     const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= i_min);
     mr = {kRange, full ? 0 : 1, 1, -u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
   };
-  const BiasRule br = {want_bias ? sm.bias : nullptr, a.rel_k, 1};
+  const BiasRule br = {!want_bias ? nullptr : a.rel_vec ? rowtab : sm.bias, a.rel_k, 1,
+                       a.rel_vec ? 2 * a.rel_k + 1 : 0};
   run_tiles<T, false, BIAS>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2,
                       split ? (wave >> 1) : -1);
   bool holds_rows = true;  // this wave holds a final running state
@@ -367,11 +452,15 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
 }
 
 // At least kMinWavesPerEU waves per SIMD// At least kMinWavesPerEU waves per SIMD: that bounds each wave's registers.
-template <typename T>
+// BIAS: a relative-position bias (scalar table and/or key-side label vectors)
+// is given; the kernel without it carries none of the bias code.
+template <typename T, bool BIAS>
 __global__ __launch_bounds__(TileTraits<T>::kThreads)
 __attribute__((amdgpu_waves_per_eu(TileTraits<T>::kMinWavesPerEU)))
 void attn_fwd_kernel(AttnArgs a) {
   __shared__ typename TileTraits<T>::Smem sm;
+  // per-row label table (key-side label vectors only; sized at launch, else empty)
+  extern __shared__ float rowtab[];
   // Block b runs on XCD b % 8. Each XCD takes an equal share of the global-row
   // workgroups, then an equal share of the band workgroups, each share a
   // contiguous range (workgroups of one head then share K/V in that XCD's L2,
@@ -381,14 +470,10 @@ void attn_fwd_kernel(AttnArgs a) {
   const int32_t bper = (a.n_band_wg + kXcds - 1) / kXcds;
   const int32_t gcnt = min(gper, max(0, a.n_glob_wg - x * gper));
   const int32_t bcnt = min(bper, max(0, a.n_band_wg - x * bper));
-  const bool bias = a.rel_bias != nullptr;
-  if (j < gcnt) {
-    if (bias) global_workgroup<T, true>(a, sm, x * gper + j);
-    else global_workgroup<T, false>(a, sm, x * gper + j);
-  } else if (j - gcnt < bcnt) {
-    if (bias) band_workgroup<T, true>(a, sm, x * bper + (j - gcnt));
-    else band_workgroup<T, false>(a, sm, x * bper + (j - gcnt));
-  }
+  if (j < gcnt)
+    global_workgroup<T, BIAS>(a, sm, rowtab, x * gper + j);
+  else if (j - gcnt < bcnt)
+    band_workgroup<T, BIAS>(a, sm, rowtab, x * bper + (j - gcnt));
 }
 
 hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
@@ -396,12 +481,20 @@ hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
   // per-XCD shares of each kind (see attn_fwd_kernel)
   const int64_t grid = (int64_t)kXcds * ((a.n_glob_wg + kXcds - 1) / kXcds +
                                          (a.n_band_wg + kXcds - 1) / kXcds);
-  if (dtype == 1)
-    hipLaunchKernelGGL(attn_fwd_kernel<bf16>, dim3((uint32_t)grid),
-                       dim3(TileTraits<bf16>::kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<float>, dim3((uint32_t)grid),
-                       dim3(TileTraits<float>::kThreads), 0, stream, a);
+  // dynamic LDS: the per-row label table of key-side label vectors
+  const size_t rows = dtype == 1 ? TileTraits<bf16>::kTQ : TileTraits<float>::kTQ;
+  const uint32_t dyn = a.rel_vec ? (uint32_t)(rows * (2 * a.rel_k + 1) * sizeof(float)) : 0u;
+  const bool bias = a.rel_bias != nullptr || a.rel_vec != nullptr;
+  const dim3 g((uint32_t)grid);
+  if (dtype == 1) {
+    const dim3 b(TileTraits<bf16>::kThreads);
+    if (bias) hipLaunchKernelGGL((attn_fwd_kernel<bf16, true>), g, b, dyn, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<bf16, false>), g, b, dyn, stream, a);
+  } else {
+    const dim3 b(TileTraits<float>::kThreads);
+    if (bias) hipLaunchKernelGGL((attn_fwd_kernel<float, true>), g, b, dyn, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<float, false>), g, b, dyn, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -61,7 +61,7 @@ __device__ __forceinline__ bool dilated_tile(const DilArgs& a, TileTraits<bf16>:
     const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= t0);
     mr = {kRange, full ? 0 : 1, 0, t0 - u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
   };
-  const BiasRule br = {nullptr, 0, 0};
+  const BiasRule br = {nullptr, 0, 0, 0};
   const GlobInfo gi = {kGlobNone, nullptr, 0};
   run_tiles<bf16, false, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2);
   dt = {base, r, t0, qcount, qi, qpos};

@@ -19,6 +19,7 @@ struct AttnArgs {
   int32_t radius, causal;
   int32_t dil[kMaxHeadsDil];
   const float* rel_bias;
+  const float* rel_vec;  // [H][2k+1][D] key-side label vectors, or null
   int32_t rel_k;
   void* out;
   float* lse;

@@ -192,12 +192,15 @@ struct GlobInfo {
   int32_t n_global;
 };
 
-// Bias source: the scalar relative-position table of one head (ETC page,
-// §3.4 "Relative Position Encoding": labels clip j - i to [-k, k]).
+// Bias source (ETC page, §3.4 "Relative Position Encoding": labels clip
+// j - i to [-k, k]): the head's table of 2k+1 scalars, or, with key-side label
+// vectors a_l, a table per query row of q_i . a_l (plus the scalar when both
+// are given), the precompute the page describes.
 struct BiasRule {
-  const float* tab;   // LDS copy of the head's 2k+1 entries (times sqrt(D)), or null
+  const float* tab;   // LDS, in q.k units (scalars times sqrt(D)), or null
   int32_t k;
   int32_t key_global_is_same_kind;  // 1: pair is same-kind iff the key is global
+  int32_t row_stride;               // 0: one table; else query row qi's table at tab + qi * row_stride
 };
 
 // Position of key row x of a tile (x clamped into [0, count) by the caller).
@@ -755,17 +758,18 @@ __device__ __forceinline__ void build_gmask(typename TileTraits<T>::Smem& sm, co
 // all_same: every key of the tile is of the query's kind (no per-key test).
 template <typename T>
 __device__ __forceinline__ void add_bias(float* s, const typename TileTraits<T>::Smem& sm,
-                                         int32_t buf, const BiasRule& br, int sb, int32_t qpos,
-                                         int32_t lane, bool all_same) {
+                                         int32_t buf, const BiasRule& br, int sb, int32_t qi,
+                                         int32_t qpos, int32_t lane, bool all_same) {
   using TT = TileTraits<T>;
   int32_t kl = TT::key_lane(lane);
   asm("" : "+v"(kl));  // opaque per call: keeps kl-derived per-element values out of loop-invariant hoisting
+  const float* tab = br.tab + qi * br.row_stride + br.k;
   if (all_same) {
 #pragma unroll
     for (int r = 0; r < TT::kNS; ++r) {
       const int32_t kj = TT::key_const(sb, r) + kl;
       const int32_t dl = min(max(sm.kpos[buf][kj] - qpos, -br.k), br.k);
-      s[r] += br.tab[dl + br.k];
+      s[r] += tab[dl];
     }
     return;
   }
@@ -774,7 +778,7 @@ __device__ __forceinline__ void add_bias(float* s, const typename TileTraits<T>:
     const int32_t kj = TT::key_const(sb, r) + kl;
     const bool same = (sm.kglob[buf][kj] != 0) == (br.key_global_is_same_kind != 0);
     const int32_t dl = min(max(sm.kpos[buf][kj] - qpos, -br.k), br.k);
-    const float b = br.tab[dl + br.k];  // always read: keeps the loop branch-free
+    const float b = tab[dl];  // always read: keeps the loop branch-free
     s[r] += same ? b : 0.f;
   }
 }
@@ -968,8 +972,8 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
         if (k0 - q1 >= br.k) { uniform = true; ue = 2 * br.k; }
         else if (k1 - q0 <= -br.k) { uniform = true; ue = 0; }
       }
-      if (uniform) badd = br.tab[ue];
-      else add_bias<T>(s, sm, buf, br, sb, qpos, lane, all_same);
+      if (uniform) badd = br.tab[qi * br.row_stride + ue];  // per query row with label vectors
+      else add_bias<T>(s, sm, buf, br, sb, qi, qpos, lane, all_same);
     }
     if (cls[sb] == kPartial) mask_tile<T>(s, sm, buf, mr, sb, kcount, qi, qpos, lane);
     sub_update<T, BIAS>(sm, buf, w, lane, sb, s, scale_log2, badd);

@@ -9,8 +9,9 @@ tokens, ETC long inputs with one global summary token per sentence, character
 language modelling at 16,384 tokens, LongNet's 32K sequences); no dataset is
 read. Recipe: ``torch.Generator('cpu').manual_seed(seed)``; draw order q, k, v,
 then qg, kg, vg (when the workload has separate global projections), then the
-relative-bias table as 0.1 * N(0,1); values iid N(0,1) in fp32, then rounded to
-bf16 (round-to-nearest-even) for bf16 workloads.
+relative-bias table as 0.1 * N(0,1), then the key-side label vectors as
+0.1 * N(0,1); values iid N(0,1) in fp32, then rounded to bf16
+(round-to-nearest-even) for bf16 workloads (the bias tables stay fp32).
 """
 from __future__ import annotations
 
@@ -35,7 +36,9 @@ class Workload:
     global_idx: Tuple[int, ...] = ()
     dilation: Optional[Tuple[int, ...]] = None  # per head; None = all 1
     causal: bool = False
-    rel_k: int = 0                          # >0: scalar relative bias table [H][2k+1]
+    rel_k: int = 0                          # >0: relative-position labels clip at k
+    rel_kind: str = "scalar"                # with rel_k > 0: "scalar" table [H][2k+1],
+                                            # "vector" key-side vectors [H][2k+1][D], or "both"
     separate_global: bool = False
     pairs: Tuple[Tuple[int, int], ...] = ()  # LongNet (segment length w, dilation r)
     seed: int = 0
@@ -61,9 +64,16 @@ LONGNET_SHARE = Workload("longnet-n32768-5pairs", B=1, H=12, N=32768, kind="dila
                          pairs=((2048, 1), (4096, 2), (8192, 4), (16384, 6), (32768, 12)),
                          seed=1005)
 
+# ETC's own relative-position mechanism on the same shape: a learned key-side
+# vector per label and head instead of the scalar stand-in.
+ETC_VECTORS = Workload("etc-ng256-nl4096-r84-relvec12", B=1, H=12, N=256 + 4096, radius=84,
+                       global_idx=tuple(range(256)), rel_k=12, rel_kind="vector", seed=1006)
+
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in
-                                  (TINY, LONGFORMER_BASE, ETC_SHAPE, CHARLM_DILATED, LONGNET_SHARE)}
-ORDERED: List[Workload] = [TINY, LONGFORMER_BASE, ETC_SHAPE, CHARLM_DILATED, LONGNET_SHARE]
+                                  (TINY, LONGFORMER_BASE, ETC_SHAPE, CHARLM_DILATED, LONGNET_SHARE,
+                                   ETC_VECTORS)}
+ORDERED: List[Workload] = [TINY, LONGFORMER_BASE, ETC_SHAPE, CHARLM_DILATED, LONGNET_SHARE,
+                           ETC_VECTORS]
 
 
 @dataclass
@@ -78,6 +88,7 @@ class Inputs:
     vg: Optional[torch.Tensor] = None
     rel_bias: Optional[torch.Tensor] = None
     extra: dict = field(default_factory=dict)
+    rel_vec: Optional[torch.Tensor] = None
 
 
 def make_inputs(w: Workload, seed: Optional[int] = None) -> Inputs:
@@ -92,13 +103,16 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Inputs:
     qg = kg = vg = None
     if w.separate_global:
         qg, kg, vg = draw(shape), draw(shape), draw(shape)
-    rb = None
-    if w.rel_k > 0:
+    rb = rv = None
+    if w.rel_k > 0 and w.rel_kind in ("scalar", "both"):
         rb = 0.1 * draw((w.H, 2 * w.rel_k + 1))
+    if w.rel_k > 0 and w.rel_kind in ("vector", "both"):
+        rv = 0.1 * draw((w.H, 2 * w.rel_k + 1, w.D))
     dt = w.torch_dtype
     cast = (lambda t: None if t is None else t.to(dt).contiguous())
     return Inputs(cast(q), cast(k), cast(v), cast(qg), cast(kg), cast(vg),
-                  None if rb is None else rb.contiguous())
+                  None if rb is None else rb.contiguous(),
+                  rel_vec=None if rv is None else rv.contiguous())
 
 
 def sample_rows(w: Workload, n: int, seed: int = 7, must_include=()) -> torch.Tensor:

@@ -51,7 +51,8 @@ def gpu_attn(w: W.Workload, inp: W.Inputs, dev, **kw):
     g = torch.tensor(w.global_idx, dtype=torch.int32, device=dev) if w.global_idx else None
     d = lambda t: None if t is None else t.to(dev)
     out, lse = la.la_attn_forward(d(inp.q), d(inp.k), d(inp.v), g, w.radius, w.dilation, w.causal,
-                                  d(inp.rel_bias), qg=d(inp.qg), kg=d(inp.kg), vg=d(inp.vg), **kw)
+                                  d(inp.rel_bias), qg=d(inp.qg), kg=d(inp.kg), vg=d(inp.vg),
+                                  rel_vec=d(inp.rel_vec), **kw)
     torch.cuda.synchronize()
     return out, lse
 
@@ -66,7 +67,7 @@ def gpu_dilated(w: W.Workload, inp: W.Inputs, dev):
 def oracle_attn(w: W.Workload, inp: W.Inputs, sel=None):
     return oracle.attn_rows(to64(inp.q), to64(inp.k), to64(inp.v), w.global_idx, w.radius,
                             w.dilation, w.causal, to64(inp.rel_bias), to64(inp.qg), to64(inp.kg),
-                            to64(inp.vg), sel=sel)
+                            to64(inp.vg), sel=sel, rel_vec=to64(inp.rel_vec))
 
 
 def oracle_dilated(w: W.Workload, inp: W.Inputs, sel=None):
@@ -112,14 +113,25 @@ SMALL = [
     ("relbias-sep", 300, 2, 33, None, False, (0, 1, 2, 150, 299), 3, True, "bf16"),
     ("relbias-dil-causal", 350, 4, 17, (1, 2, 3, 4), True, (5, 64, 65, 200, 349), 7, False, "bf16"),
     ("all-global", 96, 1, 2, None, False, tuple(range(96)), 0, False, "bf16"),
+    # ETC key-side label vectors (rel_k > 0 with a kind): alone, with the scalar table, fp32,
+    # separate projections, causal and dilated windows
+    ("relvec", 400, 3, 21, None, False, tuple(range(30)), (5, "vector"), False, "bf16"),
+    ("relvec-both-sep", 300, 2, 33, None, False, (0, 1, 2, 150, 299), (3, "both"), True, "bf16"),
+    ("relvec-f32-causal", 260, 2, 40, (1, 2), True, (3, 77, 200), (12, "vector"), False, "f32"),
+    ("relvec-dil-causal", 350, 4, 17, (1, 2, 3, 4), True, (5, 64, 65, 200, 349), (7, "both"),
+     False, "bf16"),
+    ("relvec-etc-like", 544, 2, 10, None, False, tuple(range(32)), (12, "vector"), False, "bf16"),
 ]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_band_global(dev, case):
     name, N, H, R, dil, causal, G, rk, sep, dt = case
+    kind = "scalar"
+    if isinstance(rk, tuple):
+        rk, kind = rk
     w = W.Workload(name, B=2, H=H, N=N, dtype=dt, radius=R, global_idx=G, dilation=dil,
-                   causal=causal, rel_k=rk, separate_global=sep, seed=77)
+                   causal=causal, rel_k=rk, rel_kind=kind, separate_global=sep, seed=77)
     inp = W.make_inputs(w)
     say(f"case {name}: N={N} H={H} R={R} dil={dil} causal={causal} |G|={len(G)} rel_k={rk} "
         f"sep={sep} {dt}")
