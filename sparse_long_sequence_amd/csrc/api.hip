@@ -22,7 +22,10 @@ la_status fail(la_status s, const std::string& msg) {
 }
 
 constexpr int32_t kDHead = 64;
-constexpr int32_t kChunk = 640;  // keys per global-row partial (10 key tiles)
+// Keys per global-row partial: at least 8 chunks per row when that leaves a
+// whole key tile each (short sequences spread their global rows over several
+// workgroups), at most 10 key tiles.
+constexpr int32_t kChunkMax = 640;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -43,7 +46,11 @@ la_status check_dims(const la_dims* d, bool need_bf16) {
 
 bool is_empty(const la_dims* d) { return d->B == 0 || d->H == 0 || d->N == 0; }
 
-int32_t n_chunks_of(int32_t N) { return (N + kChunk - 1) / kChunk; }
+int32_t chunk_len_of(int32_t N) {
+  const int32_t c = ((N + 7) / 8 + 63) / 64 * 64;
+  return std::min(kChunkMax, std::max(64, c));
+}
+int32_t n_chunks_of(int32_t N) { return (N + chunk_len_of(N) - 1) / chunk_len_of(N); }
 
 // Workspace of la_attn_forward: global-row partials, fp32 O then fp32 lse,
 // then one uint32 arrival counter per tile of global rows (zero between calls).
@@ -233,7 +240,7 @@ la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, con
     // partials are addressed with 32-bit byte offsets
     if (lay.cnt_off > (size_t)0x7fffffff) return fail(LA_EUNSUPPORTED, "global-row partials above 2 GiB");
   }
-  a.chunk_len = kChunk;
+  a.chunk_len = chunk_len_of(dims->N);
   a.n_chunks = n_chunks_of(dims->N);
   const int32_t tq = la::host_query_tile(dims->dtype);
   int32_t tiles = 0;

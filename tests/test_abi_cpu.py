@@ -106,10 +106,10 @@ def test_dilated_argument_errors(L):
 def test_workspace_sizes(L):
     d = LaDims(2, 12, 4096, 64, la.LA_BF16)
     assert la.la_attn_workspace_size(d, 0) == 0
-    # 64 global rows x 7 key chunks of 640 per (b, h): fp32 O plus fp32 lse,
+    # 64 global rows x 8 key chunks of 512 per (b, h): fp32 O plus fp32 lse,
     # then one arrival counter per (b, h) and 128-row tile of global rows,
     # each part padded to 256 bytes
-    parts = 2 * 12 * 64 * 7
+    parts = 2 * 12 * 64 * 8
     assert la.la_attn_workspace_size(d, 64) == parts * 64 * 4 + parts * 4 + 256
     assert la.la_attn_workspace_size(LaDims(1, 1, 10, 64, la.LA_BF16), 11) == 0  # n_global > N
     d5 = LaDims(1, 12, 32768, 64, la.LA_BF16)
