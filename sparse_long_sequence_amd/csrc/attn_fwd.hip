@@ -207,14 +207,17 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   if (g_run) {
     const int32_t n_gt = (ng + kTK - 1) / kTK;
     const int32_t glob_mode = want_bias ? kGlobAll : kGlobNone;
+    // The global key tiles come first: they are the same for every query tile
+    // of the head, so the workgroups' first K/V loads mostly hit in L2 while
+    // their band tiles stream in behind (the online softmax is order-free).
     auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
-      if (n < n_band) {
-        band_desc(n, kt, mr);
+      if (n >= n_gt) {
+        band_desc(n - n_gt, kt, mr);
         return;
       }
       // keys of G outside the window (a global key in the window is counted
       // there); a tile that cannot hold an allowed pair gets count 0
-      const int32_t gt = n - n_band;
+      const int32_t gt = n;
       const int32_t cnt = min(kTK, ng - gt * kTK);
       const int32_t gl = g_first + gt * kTK, gh = gl + cnt - 1;
       const bool all_in_band =
@@ -222,9 +225,13 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
       const bool none_causal = a.causal && gl > i_hi;
       const bool keep = !all_in_band && !none_causal;
       kt = {nullptr, gl, 1, keep ? cnt : 0, 0, glob_mode};
+      // every key outside every row's window (and not after any row, causal):
+      // no mask needed
+      const bool all_out = cnt == kTK && (gh < i_lo - R || (!a.causal && gl > i_hi + R)) &&
+                           (!a.causal || gh <= i_lo);
       // key gl + kj is allowed iff its distance kj - (qpos - gl) to the query
       // lies outside the window [-R, R] (causal: [-R, inf), so also j <= i)
-      mr = {kOutside, 1, 1, -gl, -R, a.causal ? kFar : R, 0, 0, 1};
+      mr = {kOutside, all_out ? 0 : 1, 1, -gl, -R, a.causal ? kFar : R, 0, 0, 1};
     };
     run_tiles<T, false, BIAS>(sm, w, kb, vb, n_band + n_gt, desc, br, gi, qi, qpos, dead,
                         a.scale_log2);
