@@ -87,9 +87,13 @@ typedef struct {
    * keep q, k, v (for their global columns too). */
   const void *qg, *kg, *vg;
   /* Device scratch of at least la_attn_workspace_size() bytes, 256-byte aligned;
-   * required when n_global > 0. It must be zero-filled before its first use
-   * (it holds arrival counters that every call leaves at zero again); the rest
-   * is overwritten. Calls that share a workspace must not overlap in time. */
+   * required when n_global > 0. It holds arrival counters, which must be zero
+   * when a call starts; every call leaves its counters at zero again. A
+   * workspace zero-filled once therefore serves any number of calls with the
+   * same dims and n_global; before a call with other dims or n_global (whose
+   * counters may sit where earlier calls left other data) it must be
+   * zero-filled again. The rest is overwritten. Calls that share a workspace
+   * must not overlap in time. */
   void *workspace;
   size_t workspace_bytes;
   /* Key-side relative-position vectors (ETC page, §3.4 "Relative Position

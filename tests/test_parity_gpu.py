@@ -265,6 +265,79 @@ def test_workload_parity(dev, w):
 
 
 # --------------------------------------------------------------------------
+# limits: the largest head count, label clip and pattern count the library
+# takes, a long band, many scattered global tokens, a reused workspace
+# --------------------------------------------------------------------------
+def test_limits_heads_and_labels(dev):
+    # H = 64 (per-head dilations 1..4), rel_k = 31 with scalar table and vectors
+    w = W.Workload("limits-h64-k31", B=1, H=64, N=300, radius=23, dilation=tuple(1 + h % 4 for h in range(64)),
+                   global_idx=(0, 7, 150, 299), rel_k=31, rel_kind="both", seed=91)
+    inp = W.make_inputs(w)
+    say(f"case {w.name}")
+    out, lse = gpu_attn(w, inp, dev)
+    o_ref, l_ref = oracle_attn(w, inp)
+    compare(w, out, lse, o_ref, l_ref, tag=w.name)
+
+
+def test_limits_sixteen_patterns(dev):
+    pairs = tuple((64 * (1 + p % 4) * (1 + p // 8), 1 + p % 5) for p in range(16))
+    w = W.Workload("limits-16-pairs", B=1, H=5, N=1000, kind="dilated", causal=True, pairs=pairs,
+                   seed=92)
+    inp = W.make_inputs(w)
+    say(f"case {w.name}: pairs={pairs}")
+    out, lse = gpu_dilated(w, inp, dev)
+    o_ref, l_ref = oracle_dilated(w, inp)
+    compare(w, out, lse, o_ref, l_ref, tag=w.name)
+
+
+def test_limits_long_band(dev):
+    w = W.Workload("limits-n131072", B=1, H=1, N=131072, radius=512, global_idx=(0, 1, 65536, 131071),
+                   seed=93)
+    inp = W.make_inputs(w)
+    say(f"case {w.name}")
+    out, lse = gpu_attn(w, inp, dev)
+    sel = _sel_rows(w, 800)
+    o_ref, l_ref = oracle_attn(w, inp, sel)
+    compare(w, out, lse, o_ref, l_ref, sel, tag=w.name)
+
+
+def test_limits_many_scattered_globals(dev):
+    g = tuple(sorted(set(range(0, 4096, 5)) | {4095}))  # 820 global tokens: gathered columns
+    w = W.Workload("limits-820-globals", B=1, H=2, N=4096, radius=100, dilation=(1, 3),
+                   global_idx=g, separate_global=True, seed=94)
+    inp = W.make_inputs(w)
+    say(f"case {w.name}: |G|={len(g)}")
+    out, lse = gpu_attn(w, inp, dev)
+    sel = _sel_rows(w, 600)
+    o_ref, l_ref = oracle_attn(w, inp, sel)
+    compare(w, out, lse, o_ref, l_ref, sel, tag=w.name)
+
+
+def test_workspace_reuse(dev):
+    # One workspace, zero-filled once, serves repeated calls of one shape: each
+    # call leaves its arrival counters at zero. Before a call of another shape
+    # (its counters may lie where the previous call left partials) it is
+    # zero-filled again, as the interface requires.
+    wa = W.Workload("reuse-a", B=2, H=3, N=1500, radius=60, global_idx=tuple(range(0, 1500, 7)),
+                    seed=95)
+    wb = W.Workload("reuse-b", B=1, H=2, N=700, radius=30, global_idx=(3, 4, 5, 600), seed=96)
+    nb = max(la.la_attn_workspace_size(la.LaDims(w.B, w.H, w.N, 64, la.LA_BF16), len(w.global_idx))
+             for w in (wa, wb))
+    ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    prev = None
+    for w in (wa, wa, wa, wb, wb, wa):
+        if prev is not None and w is not prev:
+            ws.zero_()
+        prev = w
+        inp = W.make_inputs(w)
+        say(f"case {w.name} (shared workspace)")
+        out, lse = gpu_attn(w, inp, dev, workspace=ws)
+        o_ref, l_ref = oracle_attn(w, inp)
+        compare(w, out, lse, o_ref, l_ref, tag=w.name)
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
 # determinism, streams, graph capture
 # --------------------------------------------------------------------------
 def test_deterministic(dev):
