@@ -8,16 +8,20 @@ chunk partials by its last-finishing chunk workgroup, all in one launch.
 Inputs are seeded synthetic N(0,1) tensors already resident in device memory.
 
 Prints one JSON line. `value` is useful TFLOP/s (4*D FLOPs per allowed
-(query, key) pair) on that workload; `roofline` relates the call's average
-duration, timed with HIP events on the stream its kernels run on, to the bf16
-MFMA peak, and reports the HBM traffic that rocprofv3's FETCH_SIZE/WRITE_SIZE
-counters measured for the same kernels (read from profiles/, and null when the
-kernel sources changed since); `workloads` times the other four workloads the
-same way; `cpu_baseline` times the fp64 CPU oracle on a bounded row sample of
-the same workload on the host cores.
+(query, key) pair) on that workload; `roofline` relates the call's single
+kernel launch, its average duration taken from HIP events around the timed
+region on the stream it runs on, to the bf16 MFMA peak, and reports the HBM
+traffic that rocprofv3's FETCH_SIZE/WRITE_SIZE counters measured for that
+kernel (read from profiles/, and null when the kernel sources changed since);
+`workloads` times every workload the same way; `cpu_baseline` times the fp64
+CPU oracle on a bounded row sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only NAME]
-                       [--copy-probe]
+                       [--copy-probe] [--settle SECONDS]
+
+Each workload: W untimed warm-up calls, then untimed calls until the GPU has
+been busy for 0.25 s (its clocks ramp up under load), then exactly K calls
+timed as one region between two events, then K calls with an event pair each.
 
 --copy-probe also runs a plain device copy of 256 MiB (torch.neg, fp32) a few
 times: under rocprofv3 --pmc its FETCH_SIZE and WRITE_SIZE give the factor that
@@ -85,13 +89,24 @@ class Call:
         self.bound()
 
 
-def time_calls(call, steps, warmup):
-    """(ms per step over the timed region, mean per-launch ms from event pairs)."""
+# After the warm-up steps, untimed calls continue until the GPU has been busy
+# this long: its clocks ramp up under load over some tens of milliseconds, and
+# a region timed straight after a short warm-up runs partly below speed.
+SETTLE_S = 0.25
+
+
+def time_calls(call, steps, warmup, settle_s=SETTLE_S):
+    """(ms per step over the timed region, mean and median ms of per-call event pairs)."""
     import torch
 
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(16):
+            call()
+        torch.cuda.synchronize()
     # region timing: K back-to-back calls
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -213,6 +228,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="time only this workload name")
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed calls after the warm-up (0 for counter runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 256 MiB device copy (counter scaling under rocprofv3)")
     args = ap.parse_args()
@@ -238,16 +255,19 @@ def main():
         log(f"bench: {w.name} (B={w.B} H={w.H} N={w.N} {w.dtype})")
         call = Call(w, dev)
         steps = args.steps
-        region_ms, mean_ms, med_ms = time_calls(call, steps, args.warmup)
+        region_ms, mean_ms, med_ms = time_calls(call, steps, args.warmup, args.settle)
         fl = F.useful_flops(w)
         by = F.algorithmic_bytes(w)
         peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        # throughput figures from the timed region of back-to-back calls; the
+        # event-pair figures (one pair around each call) add the events' cost
         results[w.name] = {
-            "ms_per_call": round(region_ms, 5), "ms_per_launch_mean": round(mean_ms, 5),
-            "ms_per_launch_median": round(med_ms, 5),
-            "useful_tflops": round(fl / (mean_ms * 1e-3) / 1e12, 3),
-            "frac_mfma_peak": round(fl / (mean_ms * 1e-3) / 1e12 / peak, 4),
-            "hbm_gbs_algorithmic": round(by / (mean_ms * 1e-3) / 1e9, 1),
+            "ms_per_call": round(region_ms, 5),
+            "ms_per_call_event_pair_mean": round(mean_ms, 5),
+            "ms_per_call_event_pair_median": round(med_ms, 5),
+            "useful_tflops": round(fl / (region_ms * 1e-3) / 1e12, 3),
+            "frac_mfma_peak": round(fl / (region_ms * 1e-3) / 1e12 / peak, 4),
+            "hbm_gbs_algorithmic": round(by / (region_ms * 1e-3) / 1e9, 1),
             "useful_flop": fl, "algorithmic_bytes": by,
         }
         log(f"  {results[w.name]}")
@@ -257,7 +277,9 @@ def main():
     r = results[head.name]
     fl = F.useful_flops(head)
     by = F.algorithmic_bytes(head)
-    achieved = fl / (r["ms_per_launch_mean"] * 1e-3) / 1e12
+    # the call is one launch of attn_fwd_kernel: the timed region over K
+    # back-to-back calls gives its average launch duration (gaps included)
+    achieved = fl / (r["ms_per_call"] * 1e-3) / 1e12
     traffic = measured_traffic()
     line = {
         "metric": METRIC,
@@ -282,7 +304,7 @@ def main():
                      "traffic_unit": "HBM bytes per call (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                      "algorithmic_bytes": by,
                      "kernel": "attn_fwd_kernel<bf16> (one launch per call)",
-                     "hbm_gbs_algorithmic": round(by / (r["ms_per_launch_mean"] * 1e-3) / 1e9, 1),
+                     "hbm_gbs_algorithmic": round(by / (r["ms_per_call"] * 1e-3) / 1e9, 1),
                      "hbm_peak_gbs": HBM_PEAK_GBS},
         "workloads": results,
     }
