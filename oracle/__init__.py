@@ -73,7 +73,7 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.lo_attn_rows.restype = ctypes.c_int32
     lib.lo_attn_rows.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 6 + [
         _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int32, _f64p, _f64p,
-        ctypes.c_int32, _i32p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int32]
+        ctypes.c_int32, _i32p, _i32p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int32]
     lib.lo_longnet_rows.restype = ctypes.c_int32
     lib.lo_longnet_rows.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 3 + [
         _i32p, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int64, _f64p, _f64p,
@@ -142,13 +142,14 @@ def longnet_mult_rows(N: int, head: int, pairs: Sequence[Sequence[int]], causal:
 
 def attn_rows(q, k, v, global_idx=(), radius: int = 0, dilation=None, causal: bool = False,
               rel_bias=None, qg=None, kg=None, vg=None, sel=None, n_threads: int = 0, lib=None,
-              rel_vec=None):
+              rel_vec=None, seg=None):
     """Band + global attention in fp64.
 
     ``q, k, v`` (and optional ``qg, kg, vg``) are ``[B,H,N,D]``. ``dilation`` is
     per head (``None`` = all 1). ``rel_bias`` is ``[H, 2k+1]`` (a scalar per
     label) and ``rel_vec`` ``[H, 2k+1, D]`` (a key-side vector per label); either,
-    both or neither may be given, with the same k. ``sel`` is an
+    both or neither may be given, with the same k. ``seg`` (``[B,N]`` int) gives
+    each token a segment (document) id: pairs across segments are masked. ``sel`` is an
     ``[n,3]`` array of ``(b,h,i)`` rows (``None`` = all rows). Returns
     ``(out [n,D], lse [n])`` as float64; with ``sel=None`` they are reshaped to
     ``[B,H,N,D]`` and ``[B,H,N]``.
@@ -183,13 +184,18 @@ def attn_rows(q, k, v, global_idx=(), radius: int = 0, dilation=None, causal: bo
         if rb is not None and rv.shape[1] != rb.shape[1]:
             raise ValueError("rel_bias and rel_vec need the same k")
         rk = (rv.shape[1] - 1) // 2
+    sg = None
+    if seg is not None:
+        sg = _i32(seg)
+        if sg.shape != (B, N):
+            raise ValueError("seg must be [B, N]")
     s, n = _sel(sel, B, H, N)
     out = np.zeros((n, D), dtype=np.float64)
     lse = np.zeros((n,), dtype=np.float64)
     rc = lib.lo_attn_rows(B, H, N, D, _p(q, _f64p), _p(k, _f64p), _p(v, _f64p), _p(qg, _f64p),
                           _p(kg, _f64p), _p(vg, _f64p), _p(g, _i32p), g.shape[0], radius,
                           _p(dil, _i32p), int(causal), _p(rb, _f64p), _p(rv, _f64p), rk,
-                          _p(s, _i32p), n,
+                          _p(sg, _i32p), _p(s, _i32p), n,
                           _p(out, _f64p), _p(lse, _f64p), n_threads)
     if rc != 0:
         raise ValueError("lo_attn_rows rejected its arguments")

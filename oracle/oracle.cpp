@@ -32,6 +32,9 @@
 //     label clamp(j-i, -k, k); mixed pairs get neither;
 //   * with separate global projections, a global row i uses qg_i, kg_j, vg_j
 //     for every key j; non-global rows use q, k, v, also for global columns;
+//   * per-instance masks for packed documents: with a segment id per token,
+//     a pair whose tokens carry different ids is masked in all four pieces
+//     (g2g, g2l, l2g, l2l), on top of the pattern;
 //   * LongNet head h keeps, in each segment, the positions whose offset from
 //     the segment start is congruent to h mod r; the last segment is truncated
 //     to N; attention inside a segment is causal in position when causal != 0;
@@ -211,7 +214,11 @@ int32_t lo_longnet_mult_rows(int32_t N, int32_t head, const int32_t* w, const in
   return 0;
 }
 
-// Band + global attention (Longformer / ETC), fp64.
+// Band + global attention (Longformer / ETC), fp64. seg: [B][N] segment ids
+// or null; with it, c_ij also needs seg[b][i] == seg[b][j] (ETC page, §3.4
+// "Per-instance attention masks": documents packed into one input are masked
+// from each other in l2l and through the global tokens; §3.4 Global-Local
+// Attention, the binary masks M of each piece).
 // q, k, v: [B,H,N,D]; qg, kg, vg: all null (shared projections) or all
 // [B,H,N,D] (Longformer page, §3.4 "Separate Linear Projections for Local vs.
 // Global Attention"). dilation: [H] (null = all 1). rel_bias: [H][2*rel_k+1]
@@ -225,8 +232,8 @@ int32_t lo_attn_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q
                      const double* v, const double* qg, const double* kg, const double* vg,
                      const int32_t* gidx, int32_t n_global, int32_t radius, const int32_t* dilation,
                      int32_t causal, const double* rel_bias, const double* rel_vec, int32_t rel_k,
-                     const int32_t* sel, int64_t n_sel, double* out, double* lse,
-                     int32_t n_threads) {
+                     const int32_t* seg, const int32_t* sel, int64_t n_sel, double* out,
+                     double* lse, int32_t n_threads) {
   if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || radius < 0 || n_global < 0) return -1;
   if (!q || !k || !v || !out || !lse) return -1;
   if ((qg || kg || vg) && !(qg && kg && vg)) return -1;
@@ -251,8 +258,11 @@ int32_t lo_attn_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q
     const double* kb = (sep ? kg : k) + head_off;
     const double* vb = (sep ? vg : v) + head_off;
     std::vector<double> weight(N);
-    for (int32_t j = 0; j < N; ++j)  // the explicit mask row c_i,:
+    const int32_t* sb = seg ? seg + (size_t)b * N : nullptr;
+    for (int32_t j = 0; j < N; ++j) {  // the explicit mask row c_i,:
       weight[j] = mask_entry(i, j, ig, is_glob[j] != 0, radius, dil, causal);
+      if (sb && sb[j] != sb[i]) weight[j] = 0.0;  // another document
+    }
     const double* tab = rel_bias ? rel_bias + (size_t)h * (2 * rel_k + 1) : nullptr;
     const double* vec = rel_vec ? rel_vec + (size_t)h * (2 * rel_k + 1) * D : nullptr;
     const double scale = 1.0 / std::sqrt((double)D);

@@ -109,12 +109,14 @@ def bf_attend(qi, keys, K, V, bias=None):
     return out, M + math.log(Z)
 
 
-def bf_band_head(q, k, v, G, R, d, causal, qg=None, kg=None, vg=None, relb=None, relv=None):
+def bf_band_head(q, k, v, G, R, d, causal, qg=None, kg=None, vg=None, relb=None, relv=None,
+                 seg=None):
     """Longformer pattern by enumeration: keys i + d*m, m in [-R, R] (causal:
     [-R, 0]), inside [0, N); plus the global columns; global rows see all.
     relv ([2k+1][D]): ETC's key-side label vectors, the logit written out as
     q_i . (k_j + a_l) / sqrt(D) for same-kind pairs (bf_attend adds the
-    q_i . k_j / sqrt(D) part, so the bias is the remaining q_i . a_l / sqrt(D))."""
+    q_i . k_j / sqrt(D) part, so the bias is the remaining q_i . a_l / sqrt(D)).
+    seg: a segment id per position; keys of another segment are dropped."""
     N = len(q)
     Gs = set(G)
     outs, lses = [], []
@@ -128,6 +130,8 @@ def bf_band_head(q, k, v, G, R, d, causal, qg=None, kg=None, vg=None, relb=None,
             ks |= {g for g in Gs if (not causal or g <= i)}
             keys = sorted(ks)
             Q, K, V = q, k, v
+        if seg is not None:
+            keys = [j for j in keys if seg[j] == seg[i]]
         bias = None
         if relb is not None or relv is not None:
             kk = (len((relb if relb is not None else relv)) - 1) // 2
@@ -387,14 +391,18 @@ def pin_brute_force_band(lib):
         qg, kg, vg = rand_qkv(rng, 1, H, N, D) if sep else (None, None, None)
         relb = rng.standard_normal((H, 7)) if t % 4 == 2 else None
         relv = rng.standard_normal((H, 7, D)) if t % 4 in (1, 2) else None
+        seg = np.sort(rng.integers(0, 3, size=N)) if t % 5 in (0, 3) else None
+        if t == 8:
+            seg = rng.integers(0, 2, size=N)  # interleaved ids, not runs
         o, l = oracle.attn_rows(q, k, v, G, R, dil, causal, relb, qg, kg, vg, lib=lib,
-                                rel_vec=relv)
+                                rel_vec=relv, seg=None if seg is None else seg[None])
         for h in range(H):
             ob, lb = bf_band_head(q[0, h].tolist(), k[0, h].tolist(), v[0, h].tolist(), G, R,
                                   dil[h], causal,
                                   *(x[0, h].tolist() for x in (qg, kg, vg)) if sep else (None,) * 3,
                                   relb=None if relb is None else relb[h].tolist(),
-                                  relv=None if relv is None else relv[h].tolist())
+                                  relv=None if relv is None else relv[h].tolist(),
+                                  seg=None if seg is None else seg.tolist())
             assert np.abs(o[0, h] - ob).max() < 1e-12, (t, h)
             assert np.abs(l[0, h] - lb).max() < 1e-12, (t, h)
 
@@ -442,6 +450,56 @@ def pin_relvec_reduces_to_scalar(lib):
         o4, l4 = oracle.attn_rows(q, kk, v, G, R, [1, 2, 1], causal, 2 * b, qg, kg, vg, lib=lib)
         assert np.abs(o3 - o4).max() < 1e-12, t
         assert np.abs(l3 - l4).max() < 1e-12, t
+
+
+def pin_packing_equals_separate_documents(lib):
+    """Documents packed into one input with segment masks (ETC page, §3.4
+    "Per-instance attention masks") attend exactly as each document alone: the
+    window, global rows and columns, dilation, causality, separate
+    projections and relative labels all stay inside a document."""
+    rng = np.random.default_rng(13)
+    H, D = 2, 4
+    # per batch row: document lengths and each document's local global tokens
+    layouts = [[(9, (0, 1)), (14, (2,)), (6, ()), (11, (0, 10))],
+               [(17, (3, 4)), (23, (0,))]]
+    N = max(sum(n for n, _ in lay) for lay in layouts)
+    for causal, R, dil, sep, rel in ((False, 3, [1, 2], False, True), (True, 4, [2, 1], True, False)):
+        B = len(layouts)
+        q, k, v = rand_qkv(rng, B, H, N, D)
+        qg, kg, vg = rand_qkv(rng, B, H, N, D) if sep else (None, None, None)
+        relb = rng.standard_normal((H, 7)) if rel else None
+        relv = rng.standard_normal((H, 7, D)) if rel else None
+        for b, lay in enumerate(layouts):
+            seg = np.full(N, len(lay), dtype=np.int32)  # the tail past the last document
+            G, off = [], 0
+            for dn, (n, gl) in enumerate(lay):
+                seg[off:off + n] = dn
+                G += [off + g for g in gl]
+                off += n
+            # the packed row b alone as a batch of one (global positions differ per row)
+            one = lambda x: None if x is None else x[b:b + 1]
+            o, l = oracle.attn_rows(one(q), one(k), one(v), G, R, dil, causal, relb, one(qg), one(kg),
+                                    one(vg), lib=lib, rel_vec=relv, seg=seg[None])
+            off = 0
+            for n, gl in lay:
+                part = lambda x: None if x is None else x[b:b + 1, :, off:off + n]
+                od, ld = oracle.attn_rows(part(q), part(k), part(v), gl, R, dil, causal, relb,
+                                          part(qg), part(kg), part(vg), lib=lib, rel_vec=relv)
+                assert np.abs(o[0, :, off:off + n] - od[0]).max() < 1e-12, (b, off)
+                assert np.abs(l[0, :, off:off + n] - ld[0]).max() < 1e-12, (b, off)
+                off += n
+    # each batch row takes its own segment ids: two rows with different
+    # segmentations in one call equal the rows called alone
+    B, N = 2, 30
+    q, k, v = rand_qkv(rng, B, H, N, D)
+    segs = np.stack([np.repeat([0, 1, 2], [7, 12, 11]), np.repeat([0, 1], [20, 10])]).astype(np.int32)
+    G = (0, 9, 25)
+    o, l = oracle.attn_rows(q, k, v, G, 3, None, False, lib=lib, seg=segs)
+    for b in range(B):
+        ob, lb = oracle.attn_rows(q[b:b + 1], k[b:b + 1], v[b:b + 1], G, 3, None, False, lib=lib,
+                                  seg=segs[b:b + 1])
+        assert np.abs(o[b] - ob[0]).max() < 1e-12, b
+        assert np.abs(l[b] - lb[0]).max() < 1e-12, b
 
 
 def pin_brute_force_longnet(lib):
@@ -512,7 +570,8 @@ def pin_sampled_rows_match_full(lib):
 PINS = [pin_mask_matches_enumeration, pin_counts_closed_form, pin_counts_full_workloads,
         pin_longnet_counts, pin_longnet_worked_example, pin_longnet_offsets_partition,
         pin_dense_special_cases, pin_global_rows_are_full_rows, pin_brute_force_band,
-        pin_etc_four_pieces, pin_relvec_reduces_to_scalar, pin_brute_force_longnet,
+        pin_etc_four_pieces, pin_relvec_reduces_to_scalar, pin_packing_equals_separate_documents,
+        pin_brute_force_longnet,
         pin_longnet_paths_agree,
         pin_rows_sum_to_one, pin_uncovered_rows, pin_sampled_rows_match_full]
 
@@ -531,6 +590,10 @@ MUTANTS = [
     ("dropped-scale", "logit[j] = dot * scale + bias(j);", "logit[j] = dot + bias(j);"),
     ("bias-index-sign", "double b = tab ? tab[dlt + rel_k] : 0.0;",
      "double b = tab ? tab[rel_k - dlt] : 0.0;"),
+    ("segments-ignored-by-global-rows", "if (sb && sb[j] != sb[i]) weight[j] = 0.0;",
+     "if (sb && sb[j] != sb[i] && !ig) weight[j] = 0.0;"),
+    ("segments-of-another-batch-row", "const int32_t* sb = seg ? seg + (size_t)b * N : nullptr;",
+     "const int32_t* sb = seg ? seg : nullptr;"),
     ("relvec-label-sign", "const double* al = vec + (size_t)(dlt + rel_k) * D;",
      "const double* al = vec + (size_t)(rel_k - dlt) * D;"),
     ("relvec-unscaled", "b += dot * scale;", "b += dot;"),
