@@ -65,6 +65,7 @@ class Call:
         self.qg, self.kg, self.vg = d(inp.qg), d(inp.kg), d(inp.vg)
         self.rb = d(inp.rel_bias)
         self.rv = d(inp.rel_vec)
+        self.seg = d(inp.seg)
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty(self.q.shape[:3], dtype=torch.float32, device=dev)
         self.g = (torch.tensor(w.global_idx, dtype=torch.int32, device=dev)
@@ -82,7 +83,7 @@ class Call:
         else:
             self.bound = la.bind_attn(self.q, self.k, self.v, self.g, w.radius, w.dilation,
                                       w.causal, self.rb, out=self.out, lse=self.lse, qg=self.qg,
-                                      rel_vec=self.rv,
+                                      rel_vec=self.rv, seg_ids=self.seg,
                                       kg=self.kg, vg=self.vg, workspace=self.ws)
 
     def __call__(self):
@@ -146,6 +147,7 @@ def cpu_baseline(w, budget_s=20.0):
     f = lambda t: None if t is None else t.to(torch.float64).numpy()
     q, k, v, qg, kg, vg, rb, rv = (f(x) for x in (inp.q, inp.k, inp.v, inp.qg, inp.kg, inp.vg,
                                                   inp.rel_bias, inp.rel_vec))
+    seg = None if inp.seg is None else inp.seg.numpy()
     total_rows = w.B * w.H * w.N
     n = min(total_rows, 2048)
     elapsed = 0.0
@@ -156,7 +158,7 @@ def cpu_baseline(w, budget_s=20.0):
             oracle.longnet_rows(q, k, v, w.pairs, w.causal, sel=sel, n_threads=cores)
         else:
             oracle.attn_rows(q, k, v, w.global_idx, w.radius, w.dilation, w.causal, rb, qg, kg, vg,
-                             sel=sel, n_threads=cores, rel_vec=rv)
+                             sel=sel, n_threads=cores, rel_vec=rv, seg=seg)
         elapsed = time.perf_counter() - t
         if elapsed >= budget_s / 4 or n >= total_rows:
             break

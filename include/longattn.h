@@ -104,6 +104,12 @@ typedef struct {
    * page's implementation note describes; such calls use 2*rel_k+1 fp32 of LDS
    * per query row of a workgroup beyond the usual. */
   const float *rel_vec;
+  /* Per-instance segment masks for packed documents (ETC page, §3.4
+   * "Per-instance attention masks"): device int32 [B][N], a segment id per
+   * position, or NULL. A pair (i,j) whose positions carry different ids is
+   * excluded in every piece (band, global rows, global columns), on top of the
+   * pattern. Any int32 values; a segment need not be contiguous. */
+  const int32_t *seg_ids;
 } la_attn_ext;
 
 /* Optional extras of la_dilated_forward; pass NULL for none. */

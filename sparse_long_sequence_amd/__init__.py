@@ -50,7 +50,8 @@ class LaDims(ctypes.Structure):
 class LaAttnExt(ctypes.Structure):
     _fields_ = [("rel_k", ctypes.c_int32), ("qg", ctypes.c_void_p), ("kg", ctypes.c_void_p),
                 ("vg", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("rel_vec", ctypes.c_void_p)]
+                ("workspace_bytes", ctypes.c_size_t), ("rel_vec", ctypes.c_void_p),
+                ("seg_ids", ctypes.c_void_p)]
 
 
 class LaDilatedExt(ctypes.Structure):
@@ -193,11 +194,13 @@ def bind_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
               lse: Optional[torch.Tensor] = None, qg: Optional[torch.Tensor] = None,
               kg: Optional[torch.Tensor] = None, vg: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, stream=None,
-              want_lse: bool = True, rel_vec: Optional[torch.Tensor] = None) -> BoundCall:
+              want_lse: bool = True, rel_vec: Optional[torch.Tensor] = None,
+              seg_ids: Optional[torch.Tensor] = None) -> BoundCall:
     """Validate and marshal a :func:`la_attn_forward` call without issuing it.
 
     ``rel_vec`` is a device fp32 ``[H, 2k+1, D]`` tensor of key-side label
-    vectors (with or without ``rel_bias``, same k)."""
+    vectors (with or without ``rel_bias``, same k). ``seg_ids`` is a device
+    int32 ``[B, N]`` tensor of segment ids: pairs across segments are masked."""
     dims = _dims(q)
     for name, t in (("k", k), ("v", v)):
         _dev(t, q, name)
@@ -241,15 +244,22 @@ def bind_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         rk = kv
         rel_vec = rel_vec.contiguous()
         vptr = rel_vec.data_ptr()
+    sptr = 0
+    if seg_ids is not None:
+        if seg_ids.dtype != torch.int32 or not seg_ids.is_cuda \
+                or tuple(seg_ids.shape) != (dims.B, dims.N):
+            raise LaError(LA_EINVAL, "seg_ids must be a device int32 [B, N] tensor")
+        seg_ids = seg_ids.contiguous()
+        sptr = seg_ids.data_ptr()
     sep = qg is not None
     ws = _workspace(la_attn_workspace_size(dims, n_global, sep), q.device, workspace)
     ext = LaAttnExt(rk, _dev(qg, q, "qg") or None, _dev(kg, q, "kg") or None,
                     _dev(vg, q, "vg") or None, ws.data_ptr() if ws is not None else None,
-                    ws.numel() if ws is not None else 0, vptr or None)
+                    ws.numel() if ws is not None else 0, vptr or None, sptr or None)
     args = (ctypes.byref(dims), qptr, k.data_ptr(), v.data_ptr(), gptr or None, n_global,
             int(radius), dil, int(bool(causal)), rptr or None, out.data_ptr(),
             lse.data_ptr() if lse is not None else None, _stream(q, stream), ctypes.byref(ext))
-    keep = (dims, ext, dil, q, k, v, global_idx, rel_bias, rel_vec, qg, kg, vg, ws)
+    keep = (dims, ext, dil, q, k, v, global_idx, rel_bias, rel_vec, seg_ids, qg, kg, vg, ws)
     return BoundCall(lib().la_attn_forward, args, keep, out, lse)
 
 
@@ -260,17 +270,19 @@ def la_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     lse: Optional[torch.Tensor] = None, qg: Optional[torch.Tensor] = None,
                     kg: Optional[torch.Tensor] = None, vg: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, stream=None,
-                    want_lse: bool = True, rel_vec: Optional[torch.Tensor] = None
+                    want_lse: bool = True, rel_vec: Optional[torch.Tensor] = None,
+                    seg_ids: Optional[torch.Tensor] = None
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Band + global attention; returns ``(out, lse)``.
 
     ``global_idx`` is a device int32 tensor of strictly increasing positions.
     ``rel_bias`` is a device fp32 ``[H, 2k+1]`` table and ``rel_vec`` a device
-    fp32 ``[H, 2k+1, D]`` table of key-side label vectors. ``out``, ``lse`` and
+    fp32 ``[H, 2k+1, D]`` table of key-side label vectors. ``seg_ids`` (device
+    int32 ``[B, N]``) masks pairs across segments. ``out``, ``lse`` and
     the workspace are allocated with torch when not given.
     """
     return bind_attn(q, k, v, global_idx, radius, dilation, causal, rel_bias, out, lse, qg, kg,
-                     vg, workspace, stream, want_lse, rel_vec)()
+                     vg, workspace, stream, want_lse, rel_vec, seg_ids)()
 
 
 def bind_dilated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

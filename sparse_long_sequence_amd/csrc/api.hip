@@ -195,6 +195,9 @@ la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, con
   if (!rel_bias && !rel_vec && rel_k != 0)
     return fail(LA_EINVAL, "ext->rel_k set without rel_bias or ext->rel_vec");
   if (rel_vec && !aligned16(rel_vec)) return fail(LA_EINVAL, "ext->rel_vec must be 16-byte aligned");
+  const int32_t* seg_ids = ext ? ext->seg_ids : nullptr;
+  if (seg_ids && ((uintptr_t)seg_ids & 3u) != 0)
+    return fail(LA_EINVAL, "ext->seg_ids must be 4-byte aligned");
   if (rel_k > la::kMaxRelK) return fail(LA_EUNSUPPORTED, "rel_k above 31");
   const void *qg = q, *kg = k, *vg = v;
   if (ext && (ext->qg || ext->kg || ext->vg)) {
@@ -228,6 +231,7 @@ la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, con
   a.causal = causal;
   a.rel_bias = rel_bias;
   a.rel_vec = rel_vec;
+  a.seg = seg_ids;
   a.rel_k = rel_k;
   a.out = out;
   a.lse = lse;

@@ -117,12 +117,21 @@ __device__ __forceinline__ void build_row_table(float* rt, float* stage, const A
   __syncthreads();
 }
 
+// Segment masks: this lane's query row's segment id and the range of ids over
+// the wave's rows (segb: the batch row's ids).
+__device__ __forceinline__ void segment_rows(GlobInfo& gi, const int32_t* segb, int32_t qpos) {
+  gi.segb = segb;
+  gi.sq = segb[qpos];
+  gi.sq_min = __builtin_amdgcn_readfirstlane(wave_min(gi.sq));  // uniform: scalar registers
+  gi.sq_max = __builtin_amdgcn_readfirstlane(wave_max(gi.sq));
+}
+
 // ---------------------------------------------------------------------------
 // band workgroup: one query tile of one residue class (positions c + d*t)
 // ---------------------------------------------------------------------------
 // BIAS: a relative-position bias table is given (the no-bias loops are
 // compiled without its code).
-template <typename T, bool BIAS>
+template <typename T, bool BIAS, bool SEG>
 __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileTraits<T>::Smem& sm,
                                                float* rowtab, int32_t bw) {
   using TT = TileTraits<T>;
@@ -176,7 +185,8 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   const int32_t hi = a.causal ? (t0 + qcount - 1) : min(n_c - 1, t0 + qcount - 1 + R);
   const int32_t n_band = (hi - lo + 1 + kTK - 1) / kTK;
   const bool want_bias = a.rel_bias != nullptr || a.rel_vec != nullptr;
-  GlobInfo gi = {kGlobNone, a.gidx, a.n_global};
+  GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
+  if (SEG) segment_rows(gi, a.seg + (size_t)(bh / a.H) * N, qpos);
   if (want_bias && a.n_global > 0) {
     if (hi - lo + 1 <= 32 * kGMaskWords) {
       build_gmask<T>(sm, a.gidx, a.n_global, c + d * lo, d, hi - lo + 1, tid);
@@ -233,10 +243,10 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
       // lies outside the window [-R, R] (causal: [-R, inf), so also j <= i)
       mr = {kOutside, all_out ? 0 : 1, 1, -gl, -R, a.causal ? kFar : R, 0, 0, 1};
     };
-    run_tiles<T, false, BIAS>(sm, w, kb, vb, n_band + n_gt, desc, br, gi, qi, qpos, dead,
+    run_tiles<T, false, BIAS, SEG>(sm, w, kb, vb, n_band + n_gt, desc, br, gi, qi, qpos, dead,
                         a.scale_log2);
   } else {
-    run_tiles<T, false, BIAS>(sm, w, kb, vb, n_band, band_desc, br, gi, qi, qpos, dead, a.scale_log2);
+    run_tiles<T, false, BIAS, SEG>(sm, w, kb, vb, n_band, band_desc, br, gi, qi, qpos, dead, a.scale_log2);
   }
 
   if (a.n_global > 0 && !g_run) {
@@ -271,8 +281,9 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
       const bool full = kcount == kTK && outside && causal_ok;
       mr = {kGlobCol, full ? 0 : 1, 0, 0, 0, 0, a.causal, R, d};
     };
-    const GlobInfo gall = {want_bias ? kGlobAll : kGlobNone, a.gidx, a.n_global};
-    run_tiles<T, true, BIAS>(sm, w, kb, vb, n_glob, glob_desc, br, gall, qi, qpos, dead, a.scale_log2);
+    const GlobInfo gall = {want_bias ? kGlobAll : kGlobNone, a.gidx, a.n_global,
+                           gi.segb, gi.sq, gi.sq_min, gi.sq_max};
+    run_tiles<T, true, BIAS, SEG>(sm, w, kb, vb, n_glob, glob_desc, br, gall, qi, qpos, dead, a.scale_log2);
   }
 
   // epilogue: rows outside G (the global-row pass owns the rest)
@@ -365,7 +376,7 @@ __device__ __forceinline__ void merge_global_tile(float* ws_o, float* ws_lse, co
 // ---------------------------------------------------------------------------
 // global-row workgroup: one tile of global rows against one chunk of keys
 // ---------------------------------------------------------------------------
-template <typename T, bool BIAS>
+template <typename T, bool BIAS, bool SEG>
 __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
                                                  typename TileTraits<T>::Smem& sm, float* rowtab,
                                                  int32_t gw) {
@@ -388,7 +399,7 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   const int32_t n_tiles = j1 > j0 ? (j1 - j0 + kTK - 1) / kTK : 0;
   load_bias_table<T>(sm, a, h, tid);
   const bool want_bias = a.rel_bias != nullptr || a.rel_vec != nullptr;
-  GlobInfo gi = {kGlobNone, a.gidx, a.n_global};
+  GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
   if (want_bias && n_tiles > 0) {
     build_gmask<T>(sm, a.gidx, a.n_global, j0, 1, j1 - j0, tid);  // j1 - j0 <= chunk_len
     gi.mode = kGlobBitmap;
@@ -408,6 +419,7 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   const int32_t wrow = split ? (wave & 1) : wave;
   const int32_t qi = TT::qrow(wrow, lane, 0);
   const int32_t qpos = qidx[min(qi, qcount - 1)];
+  if (SEG) segment_rows(gi, a.seg + (size_t)(bh / a.H) * N, qpos);
   const bool dead = TT::kQW * wrow >= qcount;  // no valid row in this wave
   typename TT::Wave w;
   TT::load_q(w, qb, &qpos, lane);
@@ -421,7 +433,7 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   };
   const BiasRule br = {!want_bias ? nullptr : a.rel_vec ? rowtab : sm.bias, a.rel_k, 1,
                        a.rel_vec ? 2 * a.rel_k + 1 : 0};
-  run_tiles<T, false, BIAS>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2,
+  run_tiles<T, false, BIAS, SEG>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2,
                       split ? (wave >> 1) : -1);
   bool holds_rows = true;  // this wave holds a final running state
   if constexpr (TT::kSub == 2) {
@@ -460,8 +472,9 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
 
 // At least kMinWavesPerEU waves per SIMD// At least kMinWavesPerEU waves per SIMD: that bounds each wave's registers.
 // BIAS: a relative-position bias (scalar table and/or key-side label vectors)
-// is given; the kernel without it carries none of the bias code.
-template <typename T, bool BIAS>
+// is given; SEG: segment masks are given. Each kernel carries only the code
+// its flags need.
+template <typename T, bool BIAS, bool SEG>
 __global__ __launch_bounds__(TileTraits<T>::kThreads)
 __attribute__((amdgpu_waves_per_eu(TileTraits<T>::kMinWavesPerEU)))
 void attn_fwd_kernel(AttnArgs a) {
@@ -478,9 +491,9 @@ void attn_fwd_kernel(AttnArgs a) {
   const int32_t gcnt = min(gper, max(0, a.n_glob_wg - x * gper));
   const int32_t bcnt = min(bper, max(0, a.n_band_wg - x * bper));
   if (j < gcnt)
-    global_workgroup<T, BIAS>(a, sm, rowtab, x * gper + j);
+    global_workgroup<T, BIAS, SEG>(a, sm, rowtab, x * gper + j);
   else if (j - gcnt < bcnt)
-    band_workgroup<T, BIAS>(a, sm, rowtab, x * bper + (j - gcnt));
+    band_workgroup<T, BIAS, SEG>(a, sm, rowtab, x * bper + (j - gcnt));
 }
 
 hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
@@ -492,15 +505,20 @@ hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
   const size_t rows = dtype == 1 ? TileTraits<bf16>::kTQ : TileTraits<float>::kTQ;
   const uint32_t dyn = a.rel_vec ? (uint32_t)(rows * (2 * a.rel_k + 1) * sizeof(float)) : 0u;
   const bool bias = a.rel_bias != nullptr || a.rel_vec != nullptr;
+  const bool seg = a.seg != nullptr;
   const dim3 g((uint32_t)grid);
   if (dtype == 1) {
     const dim3 b(TileTraits<bf16>::kThreads);
-    if (bias) hipLaunchKernelGGL((attn_fwd_kernel<bf16, true>), g, b, dyn, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<bf16, false>), g, b, dyn, stream, a);
+    if (bias && seg) hipLaunchKernelGGL((attn_fwd_kernel<bf16, true, true>), g, b, dyn, stream, a);
+    else if (bias) hipLaunchKernelGGL((attn_fwd_kernel<bf16, true, false>), g, b, dyn, stream, a);
+    else if (seg) hipLaunchKernelGGL((attn_fwd_kernel<bf16, false, true>), g, b, dyn, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<bf16, false, false>), g, b, dyn, stream, a);
   } else {
     const dim3 b(TileTraits<float>::kThreads);
-    if (bias) hipLaunchKernelGGL((attn_fwd_kernel<float, true>), g, b, dyn, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<float, false>), g, b, dyn, stream, a);
+    if (bias && seg) hipLaunchKernelGGL((attn_fwd_kernel<float, true, true>), g, b, dyn, stream, a);
+    else if (bias) hipLaunchKernelGGL((attn_fwd_kernel<float, true, false>), g, b, dyn, stream, a);
+    else if (seg) hipLaunchKernelGGL((attn_fwd_kernel<float, false, true>), g, b, dyn, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<float, false, false>), g, b, dyn, stream, a);
   }
   return hipGetLastError();
 }

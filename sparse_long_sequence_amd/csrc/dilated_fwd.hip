@@ -63,7 +63,7 @@ __device__ __forceinline__ bool dilated_tile(const DilArgs& a, TileTraits<bf16>:
   };
   const BiasRule br = {nullptr, 0, 0, 0};
   const GlobInfo gi = {kGlobNone, nullptr, 0};
-  run_tiles<bf16, false, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2);
+  run_tiles<bf16, false, false, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2);
   dt = {base, r, t0, qcount, qi, qpos};
   return true;
 }

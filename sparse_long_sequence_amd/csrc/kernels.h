@@ -20,6 +20,7 @@ struct AttnArgs {
   int32_t dil[kMaxHeadsDil];
   const float* rel_bias;
   const float* rel_vec;  // [H][2k+1][D] key-side label vectors, or null
+  const int32_t* seg;    // [B][N] segment id per position (packed documents), or null
   int32_t rel_k;
   void* out;
   float* lse;

@@ -190,7 +190,24 @@ struct GlobInfo {
   int32_t mode;
   const int32_t* gidx;
   int32_t n_global;
+  // Per-instance segment masks (packed documents; ETC page, §3.4 "Per-instance
+  // attention masks"): the batch row's segment id per position, or null; this
+  // lane's query row's id and the min / max id over the wave's rows.
+  const int32_t* segb;
+  int32_t sq, sq_min, sq_max;
 };
+
+// min / max over the 64 lanes of a wave
+__device__ __forceinline__ int32_t wave_min(int32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int32_t wave_max(int32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
 
 // Bias source (ETC page, §3.4 "Relative Position Encoding": labels clip
 // j - i to [-k, k]): the head's table of 2k+1 scalars, or, with key-side label
@@ -254,6 +271,8 @@ struct TileTraits<bf16> {
     alignas(16) float bias[64];
     alignas(16) uint32_t gmask[kGMaskWords];
     alignas(16) uint8_t kglob[2][kTK];
+    alignas(16) int32_t kseg[2][kTK];  // segment ids of the staged keys (segment masks only)
+    int32_t segr[2][2];                // per staged tile: min and max of kseg
     int32_t gcls[2];  // per staged tile: bit 0 some key is global, bit 1 every key is
   };
   struct Prefetch {
@@ -562,6 +581,8 @@ struct TileTraits<float> {
     alignas(16) float bias[64];
     alignas(16) uint32_t gmask[kGMaskWords];
     alignas(16) uint8_t kglob[2][kTK];
+    alignas(16) int32_t kseg[2][kTK];  // segment ids of the staged keys (segment masks only)
+    int32_t segr[2][2];                // per staged tile: min and max of kseg
     int32_t gcls[2];  // per staged tile: bit 0 some key is global, bit 1 every key is
   };
   struct Prefetch {
@@ -710,8 +731,9 @@ struct TileTraits<float> {
   }
 };
 
-// Per-key position and global flag of a staged tile (tid < 64 write them).
-template <typename T>
+// Per-key position and global flag of a staged tile (tid < 64 write them);
+// SEG: also the keys' segment ids and their range, when gi has them.
+template <typename T, bool SEG>
 __device__ __forceinline__ void stage_meta(typename TileTraits<T>::Smem& sm, int32_t buf,
                                            const KeyMeta& mt, const GlobInfo& gi, int32_t mode,
                                            int32_t tid) {
@@ -730,6 +752,15 @@ __device__ __forceinline__ void stage_meta(typename TileTraits<T>::Smem& sm, int
       // (tid < 64) gives the tile's any / all
       const uint64_t g = __ballot(f != 0);
       if (tid == 0) sm.gcls[buf] = (g != 0ull ? 1 : 0) | (g == ~0ull ? 2 : 0);
+    }
+    if (SEG && gi.segb) {  // the keys' segment ids and their range (wave 0: tid < 64)
+      const int32_t sk = gi.segb[mt.pos];
+      sm.kseg[buf][tid] = sk;
+      const int32_t mn = wave_min(sk), mx = wave_max(sk);
+      if (tid == 0) {
+        sm.segr[buf][0] = mn;
+        sm.segr[buf][1] = mx;
+      }
     }
   }
 }
@@ -832,6 +863,21 @@ __device__ __forceinline__ void mask_tile(float* s, const typename TileTraits<T>
   }
 }
 
+// Exclude the pairs of sub-tile sb whose key lies in another segment than
+// this lane's query row (segment masks).
+template <typename T>
+__device__ __forceinline__ void mask_segments(float* s, const typename TileTraits<T>::Smem& sm,
+                                              int32_t buf, int sb, int32_t sq, int32_t lane) {
+  using TT = TileTraits<T>;
+  int32_t kl = TT::key_lane(lane);
+  asm("" : "+v"(kl));  // opaque per call, as in mask_tile
+#pragma unroll
+  for (int r = 0; r < TT::kNS; ++r) {
+    const int32_t kj = TT::key_const(sb, r) + kl;
+    s[r] = sm.kseg[buf][kj] == sq ? s[r] : kNegInf;
+  }
+}
+
 // The running max moves only when a row's sub-tile max exceeds it by more
 // than this many log2 units; p = 2^(t - m) then stays below 2^8, and the final
 // O = sum p v / sum p is unchanged, so most sub-tiles skip the O rescale.
@@ -899,13 +945,13 @@ __device__ __forceinline__ void sub_update(const typename TileTraits<T>::Smem& s
 // range. When every sub-tile is full and no bias applies, the fast path runs
 // the sub-tiles one after the other with no mask or bias code. Otherwise each
 // sub-tile is skipped (no allowed pair), or biased and masked as needed.
-template <typename T, bool BIAS>
+template <typename T, bool BIAS, bool SEG>
 __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem& sm, int32_t buf,
                                              typename TileTraits<T>::Wave& w, int32_t lane,
                                              const MaskRule& mr, const BiasRule& br,
-                                             const KeyTile& kt, bool strided, int32_t qi,
-                                             int32_t qpos, bool dead, float scale_log2,
-                                             int32_t only_sb) {
+                                             const GlobInfo& gi, const KeyTile& kt, bool strided,
+                                             int32_t qi, int32_t qpos, bool dead,
+                                             float scale_log2, int32_t only_sb) {
   using TT = TileTraits<T>;
   constexpr int SB = TT::kSub;
   const int32_t kcount = kt.count;
@@ -923,7 +969,7 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
     // (kGlobNone: no key is global, and the class word was not written)
     const int32_t gc = kt.gmode == kGlobNone ? 0 : __builtin_amdgcn_readfirstlane(sm.gcls[buf]);
     const bool any_g = (gc & 1) != 0, all_g = (gc & 2) != 0;
-    bias_on = br.key_global_is_same_kind ? any_g : !all_g;
+    bias_on = br.tab != nullptr && (br.key_global_is_same_kind ? any_g : !all_g);
     all_same = br.key_global_is_same_kind ? all_g : !any_g;
   }
   // A tile every pair of which is allowed for all of the workgroup's rows
@@ -940,6 +986,26 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
     for (int sb = 0; sb < SB; ++sb) {
       cls[sb] = (dead || (only_sb >= 0 && sb != only_sb)) ? kEmpty : classify<T>(mr, kcount, sb, r0, r1);
       fast = fast && cls[sb] == kFull;
+    }
+  }
+  // Segment masks (SEG): keys of one other segment only: nothing allowed;
+  // keys and rows all of one segment: no change; otherwise every computed
+  // sub-tile is masked per element.
+  bool seg_check = false;
+  if constexpr (SEG) {
+    if (gi.segb && kcount > 0) {
+      const int32_t kmn = __builtin_amdgcn_readfirstlane(sm.segr[buf][0]);
+      const int32_t kmx = __builtin_amdgcn_readfirstlane(sm.segr[buf][1]);
+      if (kmx < gi.sq_min || kmn > gi.sq_max) {
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) cls[sb] = kEmpty;
+        fast = false;
+      } else if (!(kmn == kmx && gi.sq_min == gi.sq_max && kmn == gi.sq_min)) {
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) cls[sb] = cls[sb] == kFull ? kPartial : cls[sb];
+        fast = false;
+        seg_check = true;
+      }
     }
   }
   if (fast) {
@@ -976,6 +1042,7 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
       else add_bias<T>(s, sm, buf, br, sb, qi, qpos, lane, all_same);
     }
     if (cls[sb] == kPartial) mask_tile<T>(s, sm, buf, mr, sb, kcount, qi, qpos, lane);
+    if (SEG && seg_check) mask_segments<T>(s, sm, buf, sb, gi.sq, lane);
     sub_update<T, BIAS>(sm, buf, w, lane, sb, s, scale_log2, badd);
   }
 }
@@ -988,10 +1055,11 @@ struct BufTag {
 
 // The key-tile loop: tiles 0..n_tiles-1 described by desc(n, KeyTile&, MaskRule&),
 // all strided with one stride or all gathered (GATHER); BIAS: br holds a bias
-// table (compiled out otherwise). only_sb >= 0: this
+// table (compiled out otherwise); SEG: gi holds segment ids (compiled out
+// otherwise). only_sb >= 0: this
 // wave computes only that key sub-tile of every tile (the others are left to
 // other waves holding the same rows).
-template <typename T, bool GATHER, bool BIAS, typename Desc>
+template <typename T, bool GATHER, bool BIAS, bool SEG, typename Desc>
 __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
                                           typename TileTraits<T>::Wave& w, const T* kb,
                                           const T* vb, int32_t n_tiles, Desc desc,
@@ -1008,7 +1076,7 @@ __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
   const FetchPlan fp = TT::plan(kt.stride, tid);
   TT::template fetch<GATHER>(pf, sm, 0, kb, vb, kt, fp, tid);
   TT::stage(sm, 0, pf, tid);
-  stage_meta<T>(sm, 0, pf.meta, gi, kt.gmode, tid);
+  stage_meta<T, SEG>(sm, 0, pf.meta, gi, kt.gmode, tid);
   __syncthreads();
   // Tile n computes from LDS buffer n & 1 while tile n + 1 loads into the
   // other. The loop is unrolled by two so that the buffer of each step is a
@@ -1022,11 +1090,11 @@ __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
       desc(n + 1, kt_next, mr_next);
       TT::template fetch<GATHER>(pf, sm, buf ^ 1, kb, vb, kt_next, fp, tid);
     }
-    process_tile<T, BIAS>(sm, buf, w, lane, mr, br, kt, !GATHER, qi, qpos, dead, scale_log2,
+    process_tile<T, BIAS, SEG>(sm, buf, w, lane, mr, br, gi, kt, !GATHER, qi, qpos, dead, scale_log2,
                           only_sb);
     if (more) {
       TT::stage(sm, buf ^ 1, pf, tid);
-      stage_meta<T>(sm, buf ^ 1, pf.meta, gi, kt_next.gmode, tid);
+      stage_meta<T, SEG>(sm, buf ^ 1, pf.meta, gi, kt_next.gmode, tid);
       kt = kt_next;
       mr = mr_next;
     }

@@ -15,26 +15,37 @@ from .workloads import Workload
 
 
 def band_global_pairs(w: Workload) -> int:
-    """Allowed pairs of the band + global pattern, summed over batch and heads."""
+    """Allowed pairs of the band + global pattern, summed over batch and heads.
+    With packed documents (contiguous runs of positions) every piece stays
+    inside a row's own document."""
     N, R = w.N, w.radius
     G = np.array(sorted(w.global_idx), dtype=np.int64)
     is_g = np.zeros(N, dtype=bool)
     is_g[G] = True
     i = np.arange(N, dtype=np.int64)
+    # the run [s0, s1) of positions that a row may attend within
+    s0 = np.zeros(N, dtype=np.int64)
+    s1 = np.full(N, N, dtype=np.int64)
+    doc = np.zeros(N, dtype=np.int64)
+    if w.documents:
+        off = 0
+        for dn, n in enumerate(w.documents):
+            s0[off:off + n], s1[off:off + n], doc[off:off + n] = off, off + n, dn
+            off += n
+        s0[off:], s1[off:], doc[off:] = off, N, len(w.documents)
     total = 0
     for h in range(w.H):
         d = w.dilation[h] if w.dilation else 1
-        # window keys i + d*m inside [0, N): m from -min(R, i//d) to min(R, (N-1-i)//d)
-        left = np.minimum(R, i // d)
-        right = np.zeros_like(i) if w.causal else np.minimum(R, (N - 1 - i) // d)
+        left = np.minimum(R, (i - s0) // d)
+        right = np.zeros_like(i) if w.causal else np.minimum(R, (s1 - 1 - i) // d)
         cnt = left + right + 1
         if G.size:
-            # globals outside the window (and not after i when causal)
             dl = G[None, :] - i[:, None]
             in_band = (dl % d == 0) & (np.abs(dl) <= d * R) & ((dl <= 0) if w.causal else True)
             ok = (dl <= 0) if w.causal else np.ones_like(in_band)
-            cnt = cnt + (ok & ~in_band).sum(axis=1)
-        rows_g = (i + 1) if w.causal else np.full(N, N, dtype=np.int64)
+            same = doc[G][None, :] == doc[:, None]
+            cnt = cnt + (ok & ~in_band & same).sum(axis=1)
+        rows_g = (i - s0 + 1) if w.causal else (s1 - s0)
         cnt = np.where(is_g, rows_g, cnt)
         total += int(cnt.sum())
     return total * w.B

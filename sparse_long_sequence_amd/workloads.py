@@ -41,6 +41,8 @@ class Workload:
                                             # "vector" key-side vectors [H][2k+1][D], or "both"
     separate_global: bool = False
     pairs: Tuple[Tuple[int, int], ...] = ()  # LongNet (segment length w, dilation r)
+    documents: Tuple[int, ...] = ()         # packed documents: lengths in order (segment
+                                            # masks; positions past them form one more)
     seed: int = 0
 
     @property
@@ -66,14 +68,21 @@ LONGNET_SHARE = Workload("longnet-n32768-5pairs", B=1, H=12, N=32768, kind="dila
 
 # ETC's own relative-position mechanism on the same shape: a learned key-side
 # vector per label and head instead of the scalar stand-in.
+# Document packing (per-instance segment masks): the Longformer-base shape
+# holding four documents of 1024 tokens per sequence, each with its first 16
+# tokens global.
+PACKED = Workload("longformer-packed-4x1024-g16", B=2, H=12, N=4096, radius=256,
+                  global_idx=tuple(d * 1024 + t for d in range(4) for t in range(16)),
+                  separate_global=True, documents=(1024, 1024, 1024, 1024), seed=1007)
+
 ETC_VECTORS = Workload("etc-ng256-nl4096-r84-relvec12", B=1, H=12, N=256 + 4096, radius=84,
                        global_idx=tuple(range(256)), rel_k=12, rel_kind="vector", seed=1006)
 
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in
                                   (TINY, LONGFORMER_BASE, ETC_SHAPE, CHARLM_DILATED, LONGNET_SHARE,
-                                   ETC_VECTORS)}
+                                   ETC_VECTORS, PACKED)}
 ORDERED: List[Workload] = [TINY, LONGFORMER_BASE, ETC_SHAPE, CHARLM_DILATED, LONGNET_SHARE,
-                           ETC_VECTORS]
+                           ETC_VECTORS, PACKED]
 
 
 @dataclass
@@ -89,6 +98,7 @@ class Inputs:
     rel_bias: Optional[torch.Tensor] = None
     extra: dict = field(default_factory=dict)
     rel_vec: Optional[torch.Tensor] = None
+    seg: Optional[torch.Tensor] = None      # int32 [B, N] segment ids
 
 
 def make_inputs(w: Workload, seed: Optional[int] = None) -> Inputs:
@@ -110,9 +120,17 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Inputs:
         rv = 0.1 * draw((w.H, 2 * w.rel_k + 1, w.D))
     dt = w.torch_dtype
     cast = (lambda t: None if t is None else t.to(dt).contiguous())
+    seg = None
+    if w.documents:
+        ids = torch.full((w.N,), len(w.documents), dtype=torch.int32)
+        off = 0
+        for dn, n in enumerate(w.documents):
+            ids[off:off + n] = dn
+            off += n
+        seg = ids.expand(w.B, w.N).contiguous()
     return Inputs(cast(q), cast(k), cast(v), cast(qg), cast(kg), cast(vg),
                   None if rb is None else rb.contiguous(),
-                  rel_vec=None if rv is None else rv.contiguous())
+                  rel_vec=None if rv is None else rv.contiguous(), seg=seg)
 
 
 def sample_rows(w: Workload, n: int, seed: int = 7, must_include=()) -> torch.Tensor:

@@ -52,7 +52,7 @@ def gpu_attn(w: W.Workload, inp: W.Inputs, dev, **kw):
     d = lambda t: None if t is None else t.to(dev)
     out, lse = la.la_attn_forward(d(inp.q), d(inp.k), d(inp.v), g, w.radius, w.dilation, w.causal,
                                   d(inp.rel_bias), qg=d(inp.qg), kg=d(inp.kg), vg=d(inp.vg),
-                                  rel_vec=d(inp.rel_vec), **kw)
+                                  rel_vec=d(inp.rel_vec), seg_ids=d(inp.seg), **kw)
     torch.cuda.synchronize()
     return out, lse
 
@@ -67,7 +67,8 @@ def gpu_dilated(w: W.Workload, inp: W.Inputs, dev):
 def oracle_attn(w: W.Workload, inp: W.Inputs, sel=None):
     return oracle.attn_rows(to64(inp.q), to64(inp.k), to64(inp.v), w.global_idx, w.radius,
                             w.dilation, w.causal, to64(inp.rel_bias), to64(inp.qg), to64(inp.kg),
-                            to64(inp.vg), sel=sel, rel_vec=to64(inp.rel_vec))
+                            to64(inp.vg), sel=sel, rel_vec=to64(inp.rel_vec),
+                            seg=None if inp.seg is None else inp.seg.numpy())
 
 
 def oracle_dilated(w: W.Workload, inp: W.Inputs, sel=None):
@@ -163,6 +164,46 @@ def test_small_dilated(dev, case):
     out, lse = gpu_dilated(w, inp, dev)
     o_ref, l_ref = oracle_dilated(w, inp)
     compare(w, out, lse, o_ref, l_ref, tag=name)
+
+
+# --------------------------------------------------------------------------
+# per-instance segment masks (packed documents): all rows compared
+# --------------------------------------------------------------------------
+def _seg_case(name, B, H, N, R, G, seg_rows, dtype="bf16", causal=False, dil=None, rel=None,
+              sep=False):
+    kind, rk = ("scalar", 0) if rel is None else (rel[1], rel[0])
+    w = W.Workload(name, B=B, H=H, N=N, dtype=dtype, radius=R, global_idx=G, dilation=dil,
+                   causal=causal, rel_k=rk, rel_kind=kind, separate_global=sep, seed=79)
+    return w, torch.tensor(np.stack(seg_rows), dtype=torch.int32)
+
+
+SEG_CASES = [
+    # documents of different lengths per batch row, each with its own global tokens
+    lambda: _seg_case("seg-packed", 2, 3, 700, 40, (0, 1, 300, 301, 650),
+                      [np.repeat([0, 1, 2], [300, 350, 50]), np.repeat([0, 1], [200, 500])]),
+    # ETC layout: each document's global tokens first, then the long tokens; label vectors
+    lambda: _seg_case("seg-etc-relvec", 1, 2, 32 + 600, 20, tuple(range(32)),
+                      [np.concatenate([np.repeat([0, 1], 16), np.repeat([0, 1], [250, 350])])],
+                      rel=(6, "both")),
+    # ids that are not runs, fp32, causal, per-head dilation (gathered global columns)
+    lambda: _seg_case("seg-interleaved-f32", 2, 2, 300, 25, (5, 100, 299),
+                      [(np.arange(300) // 37) % 3, (np.arange(300) // 11) % 2], dtype="f32",
+                      causal=True, dil=(1, 2)),
+    # separate global projections, one document holding everything but a short tail
+    lambda: _seg_case("seg-sep-tail", 1, 2, 513, 64, tuple(range(70)),
+                      [np.repeat([4, 9], [500, 13])], sep=True),
+]
+
+
+@pytest.mark.parametrize("mk", SEG_CASES, ids=[f"seg{i}" for i in range(len(SEG_CASES))])
+def test_segments(dev, mk):
+    w, seg = mk()
+    inp = W.make_inputs(w)
+    inp.seg = seg
+    say(f"case {w.name}: B={w.B} H={w.H} N={w.N} R={w.radius} |G|={len(w.global_idx)}")
+    out, lse = gpu_attn(w, inp, dev)
+    o_ref, l_ref = oracle_attn(w, inp)
+    compare(w, out, lse, o_ref, l_ref, tag=w.name)
 
 
 # --------------------------------------------------------------------------
