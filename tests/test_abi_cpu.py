@@ -72,6 +72,8 @@ def test_attn_argument_errors(L):
     # key-side label vectors: need rel_k >= 1 and a 16-byte aligned table
     assert _attn(L, d, ext=LaAttnExt(0, None, None, None, None, 0, FAKE)) == la.LA_EINVAL
     assert _attn(L, d, ext=LaAttnExt(2, None, None, None, None, 0, FAKE + 4)) == la.LA_EINVAL
+    # segment ids must be 4-byte aligned
+    assert _attn(L, d, ext=LaAttnExt(0, None, None, None, None, 0, None, FAKE + 2)) == la.LA_EINVAL
     # globals need a large enough workspace
     assert _attn(L, d, gidx=FAKE, n_global=4) == la.LA_EINVAL
     need = la.la_attn_workspace_size(d, 4)
