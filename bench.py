@@ -129,8 +129,14 @@ def time_calls(call, steps, warmup, settle_s=SETTLE_S):
     return region_ms, sum(per) / len(per), per[len(per) // 2]
 
 
-def cpu_baseline(w, budget_s=20.0):
-    """Time the fp64 oracle on a bounded sample of the workload's rows."""
+def cpu_baseline(w, min_s=10.0, max_s=30.0):
+    """Time the fp64 oracle on a bounded sample of the workload's rows.
+
+    The sample grows from 2048 rows until one pass takes a quarter of max_s or
+    covers every row; passes over it then repeat until min_s has elapsed (the
+    whole workload takes well under a second on 16 cores, too short to time
+    alone). The rate is the sampled rows' share of the useful FLOPs over the
+    time of all passes."""
     import numpy as np
     import torch
 
@@ -149,25 +155,33 @@ def cpu_baseline(w, budget_s=20.0):
                                                   inp.rel_bias, inp.rel_vec))
     seg = None if inp.seg is None else inp.seg.numpy()
     total_rows = w.B * w.H * w.N
-    n = min(total_rows, 2048)
-    elapsed = 0.0
-    while True:
-        sel = None if n >= total_rows else W.sample_rows(w, n, seed=3).numpy()[:n]
+
+    def run(sel):
         t = time.perf_counter()
         if w.kind == "dilated":
             oracle.longnet_rows(q, k, v, w.pairs, w.causal, sel=sel, n_threads=cores)
         else:
             oracle.attn_rows(q, k, v, w.global_idx, w.radius, w.dilation, w.causal, rb, qg, kg, vg,
                              sel=sel, n_threads=cores, rel_vec=rv, seg=seg)
-        elapsed = time.perf_counter() - t
-        if elapsed >= budget_s / 4 or n >= total_rows:
+        return time.perf_counter() - t
+
+    n = min(total_rows, 2048)
+    while True:
+        sel = None if n >= total_rows else W.sample_rows(w, n, seed=3).numpy()[:n]
+        elapsed = run(sel)
+        if elapsed >= max_s / 4 or n >= total_rows:
             break
-        n = min(total_rows, int(n * max(2.0, budget_s / 2 / max(elapsed, 1e-3))))
+        n = min(total_rows, int(n * max(2.0, max_s / 8 / max(elapsed, 1e-3))))
+    passes = 1
+    while elapsed < min_s:
+        elapsed += run(sel)
+        passes += 1
     # useful FLOPs of the sampled rows: the per-row share of the whole call
     flops_per_row = F.useful_flops(w) / total_rows
-    value = flops_per_row * n / elapsed / 1e12
+    value = flops_per_row * n * passes / elapsed / 1e12
     return {"value": round(value, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} of {total_rows} rows of {w.name} (fp64, masked dense softmax per row)",
+            "sample": f"{n} of {total_rows} rows of {w.name} (fp64, masked dense softmax per row), "
+                      f"{passes} passes",
             "seconds": round(elapsed, 3)}
 
 
