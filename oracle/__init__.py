@@ -19,6 +19,9 @@ Functions and the passages they follow (details in ``oracle.cpp``):
 * :func:`longnet_mixture_rows` — the same mixture in the page's own order:
   sparsify, attend, scatter, weight by softmax denominators (Eqs. 3-10, 13-15).
 * :func:`longnet_mult_rows` — the integer key multiplicity rows.
+* :func:`fixed_rows` — Sparse Transformer's fixed pattern (local block plus
+  strided summary positions; LongNet page §3.4 "Standard Self-Attention and
+  Sparse Attention (Preliminaries)"), masked dense softmax.
 
 Parity status: every function is pinned by tests in ``tests/test_oracle_pins.py``
 (closed-form counts, library special cases, the page's worked index example,
@@ -74,6 +77,10 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.lo_attn_rows.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 6 + [
         _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int32, _f64p, _f64p,
         ctypes.c_int32, _i32p, _i32p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int32]
+    lib.lo_fixed_rows.restype = ctypes.c_int32
+    lib.lo_fixed_rows.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 3 + [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int64, _f64p, _f64p,
+        ctypes.c_int32]
     lib.lo_longnet_rows.restype = ctypes.c_int32
     lib.lo_longnet_rows.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 3 + [
         _i32p, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int64, _f64p, _f64p,
@@ -199,6 +206,27 @@ def attn_rows(q, k, v, global_idx=(), radius: int = 0, dilation=None, causal: bo
                           _p(out, _f64p), _p(lse, _f64p), n_threads)
     if rc != 0:
         raise ValueError("lo_attn_rows rejected its arguments")
+    if sel is None:
+        return out.reshape(B, H, N, D), lse.reshape(B, H, N)
+    return out, lse
+
+
+def fixed_rows(q, k, v, block_len: int, summary_len: int, causal: bool = True, sel=None,
+               n_threads: int = 0, lib=None):
+    """Sparse Transformer fixed pattern in fp64 (block length l, c summary
+    positions per block; head h takes the sub-block l - c(h'+1) .. l - c h' - 1,
+    h' = h mod floor(l/c)). Shapes and returns as :func:`attn_rows`."""
+    lib = lib or load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, D = q.shape
+    s, n = _sel(sel, B, H, N)
+    out = np.zeros((n, D), dtype=np.float64)
+    lse = np.zeros((n,), dtype=np.float64)
+    rc = lib.lo_fixed_rows(B, H, N, D, _p(q, _f64p), _p(k, _f64p), _p(v, _f64p), int(block_len),
+                           int(summary_len), int(causal), _p(s, _i32p), n, _p(out, _f64p),
+                           _p(lse, _f64p), n_threads)
+    if rc != 0:
+        raise ValueError("lo_fixed_rows rejected its arguments")
     if sel is None:
         return out.reshape(B, H, N, D), lse.reshape(B, H, N)
     return out, lse

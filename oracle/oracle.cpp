@@ -95,6 +95,22 @@ bool longnet_kept(int32_t p, int32_t w, int32_t r, int32_t head) {
   return ((p - seg_start) % r) == (head % r);
 }
 
+// Sparse Transformer fixed pattern (LongNet page, §3.4 "Standard
+// Self-Attention and Sparse Attention (Preliminaries)"): the local part keeps
+// the keys of the query's own block of length l, the strided part the keys at
+// block offsets [t, t + c) of every block, here with t = l - c (h' + 1) for
+// head h, h' = h mod floor(l / c): head 0 takes the last c tokens of each
+// block, and further heads distinct sub-blocks (the page's baseline setup).
+// The mask is the union; causal adds j <= i.
+bool fixed_allows(int32_t i, int32_t j, int32_t head, int32_t l, int32_t c, int32_t causal) {
+  if (causal && j > i) return false;
+  if (i / l == j / l) return true;
+  const int32_t hp = head % std::max(1, l / c);
+  const int32_t t = l - c * (hp + 1);
+  const int32_t o = j % l;
+  return o >= t && o < t + c;
+}
+
 // Integer multiplicity of key j for query i under the mixture of patterns:
 // the number of patterns whose sparsified segment holds both i and j. By the
 // page's equivalence statement ("Mixture of Dilated Attentions": mixing with
@@ -281,6 +297,27 @@ int32_t lo_attn_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q
       return b;
     };
     attend_row(N, D, qi, kb, vb, weight, bias, out + (size_t)x * D, lse + x);
+  });
+  return 0;
+}
+
+// Sparse Transformer fixed pattern, fp64: masked dense softmax over
+// fixed_allows. q, k, v: [B,H,N,D]; sel as in lo_attn_rows.
+int32_t lo_fixed_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q, const double* k,
+                      const double* v, int32_t l, int32_t c, int32_t causal, const int32_t* sel,
+                      int64_t n_sel, double* out, double* lse, int32_t n_threads) {
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || l < 1 || c < 1 || c > l || !q || !k || !v || !out ||
+      !lse)
+    return -1;
+  const int64_t rows = sel ? n_sel : (int64_t)B * H * N;
+  parallel_rows(rows, n_threads, [&](int64_t x) {
+    int32_t b, h, i;
+    decode_row(sel, x, H, N, b, h, i);
+    const size_t head_off = ((size_t)b * H + h) * (size_t)N * D;
+    std::vector<double> weight(N);
+    for (int32_t j = 0; j < N; ++j) weight[j] = fixed_allows(i, j, h, l, c, causal) ? 1.0 : 0.0;
+    attend_row(N, D, q + head_off + (size_t)i * D, k + head_off, v + head_off, weight,
+               [](int32_t) { return 0.0; }, out + (size_t)x * D, lse + x);
   });
   return 0;
 }

@@ -502,6 +502,52 @@ def pin_packing_equals_separate_documents(lib):
         assert np.abs(l[b] - lb[0]).max() < 1e-12, b
 
 
+def _fixed_keys(i, N, h, l, c, causal):
+    """Sparse Transformer fixed pattern by enumeration: the query's own block,
+    plus offsets l - c(h'+1) .. l - c h' - 1 of every block, h' = h mod (l // c)."""
+    hp = h % max(1, l // c)
+    run = set(range(l - c * (hp + 1), l - c * hp))
+    keys = {j for j in range(N) if j // l == i // l} | {j for j in range(N) if j % l in run}
+    return sorted(j for j in keys if not causal or j <= i)
+
+
+def pin_fixed_pattern(lib):
+    """Fixed pattern: brute force on tiny inputs; c = l (every position a
+    summary) is dense attention; key counts in closed form; the heads' summary
+    runs tile the block."""
+    rng = np.random.default_rng(14)
+    for (N, l, c, causal) in ((40, 8, 2, True), (36, 12, 4, False), (30, 10, 3, True)):
+        H, D = 4, 4
+        q, k, v = rand_qkv(rng, 1, H, N, D)
+        o, lse = oracle.fixed_rows(q, k, v, l, c, causal, lib=lib)
+        for h in range(H):
+            for i in range(N):
+                ob, lb = bf_attend(q[0, h, i].tolist(), _fixed_keys(i, N, h, l, c, causal),
+                                   k[0, h].tolist(), v[0, h].tolist())
+                assert np.abs(o[0, h, i] - ob).max() < 1e-12, (N, l, c, h, i)
+                assert abs(lse[0, h, i] - lb) < 1e-12
+    q, k, v = rand_qkv(rng, 2, 3, 37, 16)
+    for causal in (True, False):
+        o_ref, l_ref = sdpa(q, k, v, causal=causal)
+        o, l = oracle.fixed_rows(q, k, v, 8, 8, causal, lib=lib)
+        assert np.abs(o - o_ref).max() < 1e-12 and np.abs(l - l_ref).max() < 1e-12
+    # counts through exp(lse) with q = 0: causal row i in block b at offset o
+    # sees o + 1 keys of its block and c of each earlier block; non-causal, the
+    # whole block and c of every other block
+    N, l, c, H = 96, 16, 4, 4
+    z = np.zeros((1, H, N, 8))
+    for causal in (True, False):
+        _, lse = oracle.fixed_rows(z, z, z, l, c, causal, lib=lib)
+        i = np.arange(N)
+        want = (i % l + 1 + (i // l) * c) if causal else (l + (N // l - 1) * c) * np.ones(N)
+        assert np.array_equal(np.rint(np.exp(lse[0])).astype(np.int64),
+                              np.broadcast_to(want, (H, N)).astype(np.int64)), causal
+    # the l // c heads' summary runs partition the block offsets
+    seen = sorted(o for h in range(l // c) for o in range(l) if
+                  o in range(l - c * (h % (l // c) + 1), l - c * (h % (l // c))))
+    assert seen == list(range(l))
+
+
 def pin_brute_force_longnet(lib):
     rng = np.random.default_rng(9)
     cases = [(24, ((4, 1), (8, 2), (24, 4)), True), (21, ((6, 1), (12, 3)), True),
@@ -571,7 +617,7 @@ PINS = [pin_mask_matches_enumeration, pin_counts_closed_form, pin_counts_full_wo
         pin_longnet_counts, pin_longnet_worked_example, pin_longnet_offsets_partition,
         pin_dense_special_cases, pin_global_rows_are_full_rows, pin_brute_force_band,
         pin_etc_four_pieces, pin_relvec_reduces_to_scalar, pin_packing_equals_separate_documents,
-        pin_brute_force_longnet,
+        pin_fixed_pattern, pin_brute_force_longnet,
         pin_longnet_paths_agree,
         pin_rows_sum_to_one, pin_uncovered_rows, pin_sampled_rows_match_full]
 
@@ -594,6 +640,11 @@ MUTANTS = [
      "if (sb && sb[j] != sb[i] && !ig) weight[j] = 0.0;"),
     ("segments-of-another-batch-row", "const int32_t* sb = seg ? seg + (size_t)b * N : nullptr;",
      "const int32_t* sb = seg ? seg : nullptr;"),
+    ("fixed-one-subblock-for-all-heads", "const int32_t hp = head % std::max(1, l / c);",
+     "const int32_t hp = 0;"),
+    ("fixed-run-one-too-long", "return o >= t && o < t + c;", "return o >= t && o <= t + c;"),
+    ("fixed-ignores-causal", "  if (causal && j > i) return false;\n  if (i / l == j / l) return true;",
+     "  if (i / l == j / l) return true;"),
     ("relvec-label-sign", "const double* al = vec + (size_t)(dlt + rel_k) * D;",
      "const double* al = vec + (size_t)(rel_k - dlt) * D;"),
     ("relvec-unscaled", "b += dot * scale;", "b += dot;"),
