@@ -71,12 +71,17 @@ class Call:
         self.g = (torch.tensor(w.global_idx, dtype=torch.int32, device=dev)
                   if w.global_idx else None)
         dims = la.LaDims(w.B, w.H, w.N, w.D, la.LA_BF16 if w.dtype == "bf16" else la.LA_F32)
-        if w.kind == "dilated":
+        if w.kind == "fixed":
+            nb = la.la_fixed_workspace_size(dims, w.fixed[0], w.fixed[1])
+        elif w.kind == "dilated":
             nb = la.la_dilated_workspace_size(dims, [p[0] for p in w.pairs], [p[1] for p in w.pairs])
         else:
             nb = la.la_attn_workspace_size(dims, len(w.global_idx), w.separate_global)
         self.ws = torch.zeros(max(nb, 1), dtype=torch.uint8, device=dev)
-        if w.kind == "dilated":
+        if w.kind == "fixed":
+            self.bound = la.bind_fixed(self.q, self.k, self.v, w.fixed[0], w.fixed[1], w.causal,
+                                       out=self.out, lse=self.lse, workspace=self.ws)
+        elif w.kind == "dilated":
             self.bound = la.bind_dilated(self.q, self.k, self.v, [p[0] for p in w.pairs],
                                          [p[1] for p in w.pairs], w.causal, out=self.out,
                                          lse=self.lse, workspace=self.ws)

@@ -149,6 +149,26 @@ la_status la_dilated_forward(const la_dims *dims, const void *q, const void *k, 
                              int32_t causal, void *out, hipStream_t stream,
                              const la_dilated_ext *ext);
 
+/* Sparse Transformer fixed pattern (LongNet page, §3.4 "Standard Self-Attention
+ * and Sparse Attention (Preliminaries)"; bf16 only). Query i attends the keys of
+ * its own block of block_len positions (local part) and, in every other block
+ * (causal: every earlier block), the summary_len positions at block offsets
+ * [t, t + summary_len), t = block_len - summary_len * (h' + 1) for head h,
+ * h' = h mod floor(block_len / summary_len): head 0 takes each block's last
+ * summary_len tokens, further heads distinct sub-blocks. One softmax over the
+ * union; causal 0 or 1 (key position <= query position).
+ *  block_len    >= 1; N must be a multiple of it (else LA_EUNSUPPORTED).
+ *  summary_len  in [1, block_len]; a multiple of 64 (else LA_EUNSUPPORTED).
+ *  out          device bf16 [B,H,N,D]; ext->lse optional as for la_dilated_forward.
+ * Requires ext->workspace of la_fixed_workspace_size() bytes (256-byte aligned,
+ * no initialisation needed). */
+la_status la_fixed_forward(const la_dims *dims, const void *q, const void *k, const void *v,
+                           int32_t block_len, int32_t summary_len, int32_t causal, void *out,
+                           hipStream_t stream, const la_dilated_ext *ext);
+
+/* Bytes of workspace la_fixed_forward needs (0 for invalid arguments). */
+size_t la_fixed_workspace_size(const la_dims *dims, int32_t block_len, int32_t summary_len);
+
 /* Bytes of workspace la_attn_forward needs for these dims and n_global
  * (0 when n_global == 0). has_separate_global is accepted for symmetry and
  * does not change the size. Returns 0 for invalid dims. */

@@ -12,7 +12,10 @@ Entry points (same names as the C ABI):
   global-token attention, with optional separate global projections and a
   per-head scalar relative-position bias (Longformer, ETC).
 * :func:`la_dilated_forward` — LongNet's mixture of dilated attentions.
+* :func:`la_fixed_forward` — Sparse Transformer's fixed pattern (local block
+  plus strided summary positions), LongNet's baseline.
 * :func:`la_attn_workspace_size`, :func:`la_dilated_workspace_size`,
+  :func:`la_fixed_workspace_size`,
   :func:`la_check_global_idx`, :func:`la_last_error`, :func:`la_version`.
 
 :func:`bind_attn` and :func:`bind_dilated` marshal a call once and return a
@@ -63,8 +66,9 @@ _i32p = ctypes.POINTER(ctypes.c_int32)
 _lib: Optional[ctypes.CDLL] = None
 
 # Every symbol include/longattn.h declares.
-EXPORTS = ("la_attn_forward", "la_dilated_forward", "la_attn_workspace_size",
-           "la_dilated_workspace_size", "la_check_global_idx", "la_last_error", "la_version")
+EXPORTS = ("la_attn_forward", "la_dilated_forward", "la_fixed_forward", "la_attn_workspace_size",
+           "la_dilated_workspace_size", "la_fixed_workspace_size", "la_check_global_idx",
+           "la_last_error", "la_version")
 
 
 def lib() -> ctypes.CDLL:
@@ -87,6 +91,12 @@ def lib() -> ctypes.CDLL:
     L.la_dilated_forward.argtypes = [ctypes.POINTER(LaDims), ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(LaDilatedExt)]
+    L.la_fixed_forward.restype = ctypes.c_int32
+    L.la_fixed_forward.argtypes = [ctypes.POINTER(LaDims), ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(LaDilatedExt)]
+    L.la_fixed_workspace_size.restype = ctypes.c_size_t
+    L.la_fixed_workspace_size.argtypes = [ctypes.POINTER(LaDims), ctypes.c_int32, ctypes.c_int32]
     L.la_attn_workspace_size.restype = ctypes.c_size_t
     L.la_attn_workspace_size.argtypes = [ctypes.POINTER(LaDims), ctypes.c_int32, ctypes.c_int32]
     L.la_dilated_workspace_size.restype = ctypes.c_size_t
@@ -322,6 +332,46 @@ def la_dilated_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """LongNet dilated attention mixture; returns ``(out, lse)``."""
     return bind_dilated(q, k, v, seg_lens, dil_rates, causal, out, lse, workspace, stream,
                         want_lse)()
+
+
+def la_fixed_workspace_size(dims: LaDims, block_len: int, summary_len: int) -> int:
+    return int(lib().la_fixed_workspace_size(ctypes.byref(dims), int(block_len), int(summary_len)))
+
+
+def bind_fixed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_len: int,
+               summary_len: int, causal: bool = True, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None, want_lse: bool = True) -> BoundCall:
+    """Validate and marshal a :func:`la_fixed_forward` call without issuing it."""
+    dims = _dims(q)
+    for name, t in (("k", k), ("v", v)):
+        _dev(t, q, name)
+    qptr = _dev(q, q, "q")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, q, "out")
+    if want_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    ws = _workspace(la_fixed_workspace_size(dims, block_len, summary_len), q.device, workspace)
+    ext = LaDilatedExt(lse.data_ptr() if lse is not None else None,
+                       ws.data_ptr() if ws is not None else None,
+                       ws.numel() if ws is not None else 0)
+    args = (ctypes.byref(dims), qptr, k.data_ptr(), v.data_ptr(), int(block_len),
+            int(summary_len), int(bool(causal)), out.data_ptr(), _stream(q, stream),
+            ctypes.byref(ext))
+    keep = (dims, ext, q, k, v, ws)
+    return BoundCall(lib().la_fixed_forward, args, keep, out, lse)
+
+
+def la_fixed_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_len: int,
+                     summary_len: int, causal: bool = True, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None, want_lse: bool = True
+                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Sparse Transformer fixed pattern (local block plus strided summary
+    positions); returns ``(out, lse)``."""
+    return bind_fixed(q, k, v, block_len, summary_len, causal, out, lse, workspace, stream,
+                      want_lse)()
 
 
 def la_check_global_idx(global_idx: torch.Tensor, N: int, stream=None) -> bool:

@@ -77,8 +77,10 @@ struct DilPlan {
   size_t ws_bytes;
 };
 
+// kind / sum_c: per pattern (null: every pattern dilated, kind 0); see DilArgs.
 la_status plan_dilated(const la_dims* d, const int32_t* w, const int32_t* r, int32_t n_pairs,
-                       DilPlan& p) {
+                       DilPlan& p, const int32_t* kind = nullptr,
+                       const int32_t* sum_c = nullptr) {
   if (!w || !r) return fail(LA_EINVAL, "seg_lens and dil_rates are required");
   if (n_pairs < 1) return fail(LA_EINVAL, "n_pairs must be >= 1");
   if (n_pairs > la::kMaxPairs) return fail(LA_EUNSUPPORTED, "more than 16 (w, r) pairs");
@@ -91,7 +93,9 @@ la_status plan_dilated(const la_dims* d, const int32_t* w, const int32_t* r, int
   a.fin = -1;
   for (int32_t k = 0; k < n_pairs; ++k) {
     if (w[k] < 1 || r[k] < 1) return fail(LA_EINVAL, "every w and r must be >= 1");
-    if (r[k] == 1 && a.fin < 0) a.fin = k;
+    a.kind[k] = kind ? kind[k] : 0;
+    a.sum_c[k] = sum_c ? sum_c[k] : 0;
+    if (r[k] == 1 && a.kind[k] == 0 && a.fin < 0) a.fin = k;
   }
   int64_t rows = 0;
   for (int32_t k = 0; k < n_pairs; ++k) {
@@ -281,6 +285,63 @@ la_status la_dilated_forward(const la_dims* dims, const void* q, const void* k, 
   if (p.ws_bytes > 0) {
     if (!ext || !ext->workspace || ext->workspace_bytes < p.ws_bytes)
       return fail(LA_EINVAL, "workspace missing or smaller than la_dilated_workspace_size()");
+    if (((uintptr_t)ext->workspace & (kAlign - 1)) != 0)
+      return fail(LA_EINVAL, "workspace must be 256-byte aligned");
+  }
+  la::DilArgs& a = p.a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.causal = causal;
+  a.out = out;
+  a.lse = ext ? ext->lse : nullptr;
+  if (p.ws_bytes > 0) {
+    a.ws_o = reinterpret_cast<float*>(ext->workspace);
+    a.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ext->workspace) +
+                                        align_up((size_t)a.rows_total * kDHead * sizeof(float)));
+  }
+  a.scale_log2 = (float)(1.0 / sqrt((double)kDHead) * 1.4426950408889634);
+  hipError_t e = la::launch_dilated(a, stream);
+  if (e != hipSuccess) return fail(LA_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(e));
+  return LA_OK;
+}
+
+// Sparse Transformer fixed pattern: the causal (or full) local block as a
+// dilated pattern (w = l, r = 1), which finishes and mixes, and the strided
+// summary keys as a second pattern of kind 1. The two key sets of a row are
+// disjoint, so mixing them by their softmax denominators is one softmax over
+// their union.
+static la_status plan_fixed(const la_dims* dims, int32_t l, int32_t c, DilPlan& p) {
+  if (l < 1 || c < 1 || c > l) return fail(LA_EINVAL, "need 1 <= summary_len <= block_len");
+  if (c % 64 != 0) return fail(LA_EUNSUPPORTED, "summary_len must be a multiple of 64");
+  if (dims->N % l != 0) return fail(LA_EUNSUPPORTED, "N must be a multiple of block_len");
+  const int32_t w[2] = {l, l}, r[2] = {1, 1}, kind[2] = {0, 1}, cs[2] = {0, c};
+  return plan_dilated(dims, w, r, 2, p, kind, cs);
+}
+
+size_t la_fixed_workspace_size(const la_dims* dims, int32_t block_len, int32_t summary_len) {
+  if (check_dims(dims, true) != LA_OK) return 0;
+  DilPlan p;
+  if (plan_fixed(dims, block_len, summary_len, p) != LA_OK) return 0;
+  return p.ws_bytes;
+}
+
+la_status la_fixed_forward(const la_dims* dims, const void* q, const void* k, const void* v,
+                           int32_t block_len, int32_t summary_len, int32_t causal, void* out,
+                           hipStream_t stream, const la_dilated_ext* ext) {
+  la_status st = check_dims(dims, true);
+  if (st != LA_OK) return st;
+  if (is_empty(dims)) return LA_OK;
+  if (!q || !k || !v || !out) return fail(LA_EINVAL, "q, k, v and out are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(LA_EINVAL, "q, k, v and out must be 16-byte aligned");
+  if (causal != 0 && causal != 1) return fail(LA_EINVAL, "causal must be 0 or 1");
+  DilPlan p;
+  st = plan_fixed(dims, block_len, summary_len, p);
+  if (st != LA_OK) return st;
+  if (p.ws_bytes > 0) {
+    if (!ext || !ext->workspace || ext->workspace_bytes < p.ws_bytes)
+      return fail(LA_EINVAL, "workspace missing or smaller than la_fixed_workspace_size()");
     if (((uintptr_t)ext->workspace & (kAlign - 1)) != 0)
       return fail(LA_EINVAL, "workspace must be 256-byte aligned");
   }

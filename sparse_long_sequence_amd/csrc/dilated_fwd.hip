@@ -50,20 +50,41 @@ __device__ __forceinline__ bool dilated_tile(const DilArgs& a, TileTraits<bf16>:
   const int32_t qpos = base + r * (t0 + min(qi, qcount - 1));
   const bool dead = TT::kQW * wave >= qcount;  // no valid row in this wave
   TT::load_q(wv, qb, &qpos, lane);
-  const int32_t hi = a.causal ? t0 + qcount - 1 : n_rows - 1;
-  const int32_t n_tiles = (hi + kTK) / kTK;
-
-  auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
-    const int32_t u0 = n * kTK;
-    const int32_t kcount = min(kTK, hi - u0 + 1);
-    kt = {nullptr, base + r * u0, r, kcount, 0, kGlobNone};
-    // gathered index difference key - query = kj - qi - (t0 - u0) <= 0 when causal
-    const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= t0);
-    mr = {kRange, full ? 0 : 1, 0, t0 - u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
-  };
   const BiasRule br = {nullptr, 0, 0, 0};
   const GlobInfo gi = {kGlobNone, nullptr, 0};
-  run_tiles<bf16, false, false, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2);
+  if (a.kind[k] == 1) {
+    // Fixed pattern, strided part (LongNet page, §3.4 "Standard Self-Attention
+    // and Sparse Attention (Preliminaries)"): the c summary positions at block
+    // offsets [toff, toff + c) of every other block (causal: every earlier
+    // block). c is a multiple of 64, so a key tile is one contiguous run, and
+    // every pair of it is allowed.
+    const int32_t c = a.sum_c[k];
+    const int32_t hp = h % max(1, w / c);
+    const int32_t toff = w - c * (hp + 1);
+    const int32_t n_keys = (a.causal ? seg : a.nseg[k] - 1) * c;
+    auto desc_sum = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+      const int32_t x0 = n * kTK;
+      const int32_t kb = x0 / c;
+      const int32_t blk = (a.causal || kb < seg) ? kb : kb + 1;  // the blocks other than seg
+      kt = {nullptr, blk * w + toff + (x0 - kb * c), 1, kTK, 0, kGlobNone};
+      mr = {kRange, 0, 0, 0, -kFar, kFar, 0, 0, 1};
+    };
+    run_tiles<bf16, false, false, false>(sm, wv, kb, vb, n_keys / kTK, desc_sum, br, gi, qi, qpos,
+                                         dead, a.scale_log2);
+  } else {
+    const int32_t hi = a.causal ? t0 + qcount - 1 : n_rows - 1;
+    const int32_t n_tiles = (hi + kTK) / kTK;
+    auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+      const int32_t u0 = n * kTK;
+      const int32_t kcount = min(kTK, hi - u0 + 1);
+      kt = {nullptr, base + r * u0, r, kcount, 0, kGlobNone};
+      // gathered index difference key - query = kj - qi - (t0 - u0) <= 0 when causal
+      const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= t0);
+      mr = {kRange, full ? 0 : 1, 0, t0 - u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
+    };
+    run_tiles<bf16, false, false, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead,
+                                         a.scale_log2);
+  }
   dt = {base, r, t0, qcount, qi, qpos};
   return true;
 }

@@ -39,6 +39,10 @@ struct DilArgs {
   const void *q, *k, *v;
   int32_t B, H, N, causal, n_pairs;
   int32_t w[kMaxPairs], r[kMaxPairs];
+  // kind 0: a dilated pattern (w, r); kind 1 (r = 1): the strided summary
+  // keys of Sparse Transformer's fixed pattern, c = sum_c[k] positions per
+  // block of length w, the run per head as in la_fixed_forward
+  int32_t kind[kMaxPairs], sum_c[kMaxPairs];
   float inv_w[kMaxPairs], inv_r[kMaxPairs];  // 1/w, 1/r (fp32) for division without divides
   int32_t nseg[kMaxPairs];      // segments of pattern k: ceil(N / w)
   int32_t seg_rows[kMaxPairs];  // partial rows reserved per segment: ceil(w / r)

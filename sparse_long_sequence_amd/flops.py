@@ -64,8 +64,24 @@ def dilated_pairs(w: Workload) -> int:
     return total * w.B
 
 
+def fixed_pairs(w: Workload) -> int:
+    """Pairs of the fixed pattern (N a multiple of l): the own block (causal: up
+    to the query) plus c summary keys of every other (causal: earlier) block."""
+    l, c = w.fixed
+    nb = w.N // l
+    if w.causal:
+        per_head = nb * l * (l + 1) // 2 + c * l * nb * (nb - 1) // 2
+    else:
+        per_head = nb * l * l + nb * l * (nb - 1) * c
+    return per_head * w.H * w.B
+
+
 def useful_pairs(w: Workload) -> int:
-    return dilated_pairs(w) if w.kind == "dilated" else band_global_pairs(w)
+    if w.kind == "dilated":
+        return dilated_pairs(w)
+    if w.kind == "fixed":
+        return fixed_pairs(w)
+    return band_global_pairs(w)
 
 
 def useful_flops(w: Workload) -> int:

@@ -31,7 +31,8 @@ class Workload:
     N: int
     D: int = 64
     dtype: str = "bf16"                     # "bf16" or "f32"
-    kind: str = "band"                      # "band" (la_attn_forward) or "dilated" (la_dilated_forward)
+    kind: str = "band"                      # "band" (la_attn_forward), "dilated" (la_dilated_forward)
+                                            # or "fixed" (la_fixed_forward)
     radius: int = 0
     global_idx: Tuple[int, ...] = ()
     dilation: Optional[Tuple[int, ...]] = None  # per head; None = all 1
@@ -41,6 +42,7 @@ class Workload:
                                             # "vector" key-side vectors [H][2k+1][D], or "both"
     separate_global: bool = False
     pairs: Tuple[Tuple[int, int], ...] = ()  # LongNet (segment length w, dilation r)
+    fixed: Tuple[int, int] = ()             # fixed pattern: (block length l, summary length c)
     documents: Tuple[int, ...] = ()         # packed documents: lengths in order (segment
                                             # masks; positions past them form one more)
     seed: int = 0
@@ -68,6 +70,13 @@ LONGNET_SHARE = Workload("longnet-n32768-5pairs", B=1, H=12, N=32768, kind="dila
 
 # ETC's own relative-position mechanism on the same shape: a learned key-side
 # vector per label and head instead of the scalar stand-in.
+# Sparse Transformer's fixed pattern, LongNet's baseline, on the LongNet shape:
+# blocks of 2048 and 128 summary positions per block (the block size the
+# LongNet page names; c sets the sparsity, here within 10% of the LongNet
+# workload's pairs, as that page matches the two by FLOPs).
+FIXED_SHARE = Workload("sparse-transformer-fixed-n32768-l2048-c128", B=1, H=12, N=32768,
+                       kind="fixed", causal=True, fixed=(2048, 128), seed=1008)
+
 # Document packing (per-instance segment masks): the Longformer-base shape
 # holding four documents of 1024 tokens per sequence, each with its first 16
 # tokens global.
@@ -80,9 +89,9 @@ ETC_VECTORS = Workload("etc-ng256-nl4096-r84-relvec12", B=1, H=12, N=256 + 4096,
 
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in
                                   (TINY, LONGFORMER_BASE, ETC_SHAPE, CHARLM_DILATED, LONGNET_SHARE,
-                                   ETC_VECTORS, PACKED)}
+                                   ETC_VECTORS, PACKED, FIXED_SHARE)}
 ORDERED: List[Workload] = [TINY, LONGFORMER_BASE, ETC_SHAPE, CHARLM_DILATED, LONGNET_SHARE,
-                           ETC_VECTORS, PACKED]
+                           ETC_VECTORS, PACKED, FIXED_SHARE]
 
 
 @dataclass

@@ -105,6 +105,24 @@ def test_dilated_argument_errors(L):
     assert call(ext=LaDilatedExt(None, FAKE, need - 1)) == la.LA_EINVAL
 
 
+def test_fixed_argument_errors(L):
+    d = LaDims(1, 2, 1024, 64, la.LA_BF16)
+    need = la.la_fixed_workspace_size(d, 256, 64)
+    assert need > 0
+    ext = LaDilatedExt(None, FAKE, need)
+
+    def call(dims=d, l=256, c=64, causal=1, e=ext):
+        return L.la_fixed_forward(ctypes.byref(dims), FAKE, FAKE, FAKE, l, c, causal, FAKE, None,
+                                  ctypes.byref(e) if e is not None else None)
+    assert call(c=96) == la.LA_EUNSUPPORTED         # summary not a multiple of 64
+    assert call(l=300) == la.LA_EUNSUPPORTED        # N not a multiple of the block
+    assert call(c=512) == la.LA_EINVAL              # summary longer than the block
+    assert call(causal=2) == la.LA_EINVAL
+    assert call(e=None) == la.LA_EINVAL             # no workspace
+    assert call(dims=LaDims(1, 2, 1024, 64, la.LA_F32)) == la.LA_EUNSUPPORTED
+    assert la.la_fixed_workspace_size(d, 256, 96) == 0
+
+
 def test_workspace_sizes(L):
     d = LaDims(2, 12, 4096, 64, la.LA_BF16)
     assert la.la_attn_workspace_size(d, 0) == 0

@@ -71,6 +71,18 @@ def oracle_attn(w: W.Workload, inp: W.Inputs, sel=None):
                             seg=None if inp.seg is None else inp.seg.numpy())
 
 
+def gpu_fixed(w: W.Workload, inp: W.Inputs, dev):
+    out, lse = la.la_fixed_forward(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), w.fixed[0],
+                                   w.fixed[1], w.causal)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_fixed(w: W.Workload, inp: W.Inputs, sel=None):
+    return oracle.fixed_rows(to64(inp.q), to64(inp.k), to64(inp.v), w.fixed[0], w.fixed[1],
+                             w.causal, sel=sel)
+
+
 def oracle_dilated(w: W.Workload, inp: W.Inputs, sel=None):
     return oracle.longnet_rows(to64(inp.q), to64(inp.k), to64(inp.v), w.pairs, w.causal, sel=sel)
 
@@ -207,6 +219,30 @@ def test_segments(dev, mk):
 
 
 # --------------------------------------------------------------------------
+# Sparse Transformer fixed pattern: all rows compared
+# --------------------------------------------------------------------------
+FIXED_CASES = [
+    # name, B, N, H, (l, c), causal
+    ("fixed-heads-wrap", 1, 512, 4, (128, 64), True),     # 4 heads over 2 sub-blocks
+    ("fixed-noncausal", 2, 384, 3, (128, 64), False),
+    ("fixed-c-equals-l", 1, 256, 2, (128, 128), True),    # dense causal attention
+    ("fixed-long-blocks", 1, 1024, 5, (512, 128), True),  # several query tiles per block
+    ("fixed-one-block", 1, 256, 2, (256, 64), False),     # no other block: local part only
+]
+
+
+@pytest.mark.parametrize("case", FIXED_CASES, ids=[c[0] for c in FIXED_CASES])
+def test_fixed_pattern(dev, case):
+    name, B, N, H, lc, causal = case
+    w = W.Workload(name, B=B, H=H, N=N, kind="fixed", causal=causal, fixed=lc, seed=81)
+    inp = W.make_inputs(w)
+    say(f"case {name}: B={B} N={N} H={H} (l, c)={lc} causal={causal}")
+    out, lse = gpu_fixed(w, inp, dev)
+    o_ref, l_ref = oracle_fixed(w, inp)
+    compare(w, out, lse, o_ref, l_ref, tag=name)
+
+
+# --------------------------------------------------------------------------
 # exact mask and global-index handling (Q = 0, V = one-hot(j mod 64))
 # --------------------------------------------------------------------------
 def _mask_inputs(w, dev):
@@ -293,6 +329,12 @@ def test_workload_parity(dev, w):
         out, lse = gpu_dilated(w, inp, dev)
         sel = _sel_rows(w, 1500)
         o_ref, l_ref = oracle_dilated(w, inp, sel)
+        compare(w, out, lse, o_ref, l_ref, sel, tag=w.name)
+        return
+    if w.kind == "fixed":
+        out, lse = gpu_fixed(w, inp, dev)
+        sel = _sel_rows(w, 1500)
+        o_ref, l_ref = oracle_fixed(w, inp, sel)
         compare(w, out, lse, o_ref, l_ref, sel, tag=w.name)
         return
     out, lse = gpu_attn(w, inp, dev)
