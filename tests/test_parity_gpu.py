@@ -475,3 +475,39 @@ def test_graph_capture(dev):
         torch.cuda.synchronize()
         assert torch.equal(out, ref) and torch.equal(lse, ref_lse), f"replay {rep}"
         _ = (q.float() * 2).sum().item()  # unrelated eager work between replays
+
+
+def test_graph_capture_dilated_and_fixed(dev):
+    # the two-launch calls (pattern partials, then the finisher) replay in a graph
+    w = W.Workload("graph-longnet", B=1, H=3, N=1024, kind="dilated", causal=True,
+                   pairs=((256, 1), (512, 2), (1024, 4)), seed=6)
+    inp = W.make_inputs(w)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    seg, dil = [p[0] for p in w.pairs], [p[1] for p in w.pairs]
+    ref, ref_lse = la.la_dilated_forward(q, k, v, seg, dil, True)
+    ref_f, ref_flse = la.la_fixed_forward(q, k, v, 256, 64, True)
+    dims = la.LaDims(1, 3, 1024, 64, la.LA_BF16)
+    out, out_f = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    lse_f = torch.empty_like(lse)
+    ws = torch.empty(la.la_dilated_workspace_size(dims, seg, dil), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(la.la_fixed_workspace_size(dims, 256, 64), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            la.la_dilated_forward(q, k, v, seg, dil, True, out=out, lse=lse, workspace=ws, stream=s)
+            la.la_fixed_forward(q, k, v, 256, 64, True, out=out_f, lse=lse_f, workspace=ws_f,
+                                stream=s)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        out_f.fill_(float("nan"))
+        lse.zero_()
+        lse_f.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(lse, ref_lse), f"dilated replay {rep}"
+        assert torch.equal(out_f, ref_f) and torch.equal(lse_f, ref_flse), f"fixed replay {rep}"
+
