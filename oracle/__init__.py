@@ -89,6 +89,10 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.lo_longnet_mixture_rows.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 3 + [
         _i32p, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int64, _f64p, _f64p,
         _f64p, _f64p, ctypes.c_int32]
+    lib.lo_attn_backward.restype = ctypes.c_int32
+    lib.lo_attn_backward.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 6 + [
+        _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p] + [_f64p] * 7 + [
+        ctypes.c_int32]
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -209,6 +213,42 @@ def attn_rows(q, k, v, global_idx=(), radius: int = 0, dilation=None, causal: bo
     if sel is None:
         return out.reshape(B, H, N, D), lse.reshape(B, H, N)
     return out, lse
+
+
+def attn_backward(q, k, v, dout, global_idx=(), radius: int = 0, dilation=None,
+                  causal: bool = False, qg=None, kg=None, vg=None, seg=None, n_threads: int = 0,
+                  lib=None):
+    """Gradients of band + global attention in fp64 for upstream gradient ``dout``.
+
+    Arguments as in :func:`attn_rows` (no bias). Returns ``(dq, dk, dv)``, or
+    ``(dq, dk, dv, dqg, dkg, dvg)`` with separate global projections, each
+    ``[B,H,N,D]`` float64.
+    """
+    lib = lib or load()
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape or do.shape != q.shape:
+        raise ValueError("q, k, v, dout shapes differ")
+    sep = [x is not None for x in (qg, kg, vg)]
+    if any(sep) and not all(sep):
+        raise ValueError("qg, kg, vg must be given together")
+    qg, kg, vg = [None if x is None else _f64(x) for x in (qg, kg, vg)]
+    g = _i32(sorted(global_idx))
+    dil = None if dilation is None else _i32(dilation)
+    if dil is not None and dil.shape != (H,):
+        raise ValueError("dilation must have one entry per head")
+    sg = None if seg is None else _i32(seg)
+    if sg is not None and sg.shape != (B, N):
+        raise ValueError("seg must be [B, N]")
+    grads = [np.zeros_like(q) for _ in range(6 if all(sep) else 3)]
+    ptr = [_p(x, _f64p) for x in grads] + [None] * (6 - len(grads))
+    rc = lib.lo_attn_backward(B, H, N, D, _p(q, _f64p), _p(k, _f64p), _p(v, _f64p),
+                              _p(qg, _f64p), _p(kg, _f64p), _p(vg, _f64p), _p(g, _i32p),
+                              g.shape[0], radius, _p(dil, _i32p), int(causal), _p(sg, _i32p),
+                              _p(do, _f64p), *ptr, n_threads)
+    if rc != 0:
+        raise ValueError("lo_attn_backward rejected its arguments")
+    return tuple(grads)
 
 
 def fixed_rows(q, k, v, block_len: int, summary_len: int, causal: bool = True, sel=None,

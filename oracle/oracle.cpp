@@ -301,6 +301,102 @@ int32_t lo_attn_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q
   return 0;
 }
 
+// Backward of band + global attention, fp64: the chain rule through the
+// definition above (LongNet page, §3.4 "Standard Self-Attention and Sparse
+// Attention (Preliminaries)", Eq. 2, differentiated), for a loss whose gradient
+// with respect to O is dout. With P_ij = c_ij exp(s_ij) / Z_i from this
+// oracle's own forward:
+//   dV_j  = sum_i P_ij dO_i           dP_ij = dO_i . v_j
+//   D_i   = sum_j P_ij dP_ij          dS_ij = P_ij (dP_ij - D_i)
+//   dQ_i  = sum_j dS_ij k_j / sqrt(D)  dK_j = sum_i dS_ij q_i / sqrt(D)
+// The mask is lo_attn_rows's (pattern, causal, segments); no bias. A global
+// row with separate projections differentiates through qg_i, kg_j, vg_j, so its
+// terms go to dqg, dkg, dvg (given iff qg, kg, vg are). Heads are split over
+// threads; rows are visited in order within a head, so sums are deterministic.
+int32_t lo_attn_backward(int32_t B, int32_t H, int32_t N, int32_t D, const double* q,
+                         const double* k, const double* v, const double* qg, const double* kg,
+                         const double* vg, const int32_t* gidx, int32_t n_global, int32_t radius,
+                         const int32_t* dilation, int32_t causal, const int32_t* seg,
+                         const double* dout, double* dq, double* dk, double* dv, double* dqg,
+                         double* dkg, double* dvg, int32_t n_threads) {
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || radius < 0 || n_global < 0) return -1;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+  const bool sep_all = qg && kg && vg && dqg && dkg && dvg;
+  if ((qg || kg || vg || dqg || dkg || dvg) && !sep_all) return -1;
+  if (n_global > 0 && !gidx) return -1;
+  if (dilation)
+    for (int32_t h = 0; h < H; ++h)
+      if (dilation[h] < 1) return -1;
+  std::vector<uint8_t> is_glob(N, 0);
+  for (int32_t g = 0; g < n_global; ++g)
+    if (gidx[g] >= 0 && gidx[g] < N) is_glob[gidx[g]] = 1;
+  const double scale = 1.0 / std::sqrt((double)D);
+  const size_t head_elems = (size_t)N * D;
+  parallel_rows((int64_t)B * H, n_threads, [&](int64_t bh) {
+    const int32_t b = (int32_t)(bh / H), h = (int32_t)(bh % H);
+    const int32_t dil = dilation ? dilation[h] : 1;
+    const size_t off = (size_t)bh * head_elems;
+    double* outs[6] = {dq, dk, dv, dqg, dkg, dvg};
+    for (double* o : outs)
+      if (o) std::fill(o + off, o + off + head_elems, 0.0);
+    const int32_t* segb = seg ? seg + (size_t)b * N : nullptr;
+    std::vector<double> P(N), dP(N);
+    for (int32_t i = 0; i < N; ++i) {
+      const bool ig = is_glob[i] != 0;
+      const bool sep = ig && sep_all;
+      const double* qi = (sep ? qg : q) + off + (size_t)i * D;
+      const double* kb = (sep ? kg : k) + off;
+      const double* vb = (sep ? vg : v) + off;
+      double* dqi = (sep ? dqg : dq) + off + (size_t)i * D;
+      double* dkb = (sep ? dkg : dk) + off;
+      double* dvb = (sep ? dvg : dv) + off;
+      const double* doi = dout + off + (size_t)i * D;
+      // forward of row i: the allowed keys' probabilities
+      double M = -std::numeric_limits<double>::infinity();
+      for (int32_t j = 0; j < N; ++j) {
+        bool c = mask_entry(i, j, ig, is_glob[j] != 0, radius, dil, causal) != 0;
+        if (segb && segb[j] != segb[i]) c = false;
+        if (!c) {
+          P[j] = -std::numeric_limits<double>::infinity();
+          continue;
+        }
+        double dot = 0.0;
+        for (int32_t d = 0; d < D; ++d) dot += qi[d] * kb[(size_t)j * D + d];
+        P[j] = dot * scale;  // the logit for now
+        M = std::max(M, P[j]);
+      }
+      if (M == -std::numeric_limits<double>::infinity()) continue;  // no key: O = 0, no gradient
+      double Z = 0.0;
+      for (int32_t j = 0; j < N; ++j) {
+        P[j] = std::exp(P[j] - M);  // exp(-inf) = 0 for excluded keys
+        Z += P[j];
+      }
+      double Di = 0.0;
+      for (int32_t j = 0; j < N; ++j) {
+        P[j] /= Z;
+        if (P[j] == 0.0) {
+          dP[j] = 0.0;
+          continue;
+        }
+        double dot = 0.0;
+        for (int32_t d = 0; d < D; ++d) dot += doi[d] * vb[(size_t)j * D + d];
+        dP[j] = dot;
+        Di += P[j] * dot;
+      }
+      for (int32_t j = 0; j < N; ++j) {
+        if (P[j] == 0.0) continue;
+        const double dS = P[j] * (dP[j] - Di);
+        for (int32_t d = 0; d < D; ++d) {
+          dvb[(size_t)j * D + d] += P[j] * doi[d];
+          dqi[d] += dS * kb[(size_t)j * D + d] * scale;
+          dkb[(size_t)j * D + d] += dS * qi[d] * scale;
+        }
+      }
+    }
+  });
+  return 0;
+}
+
 // Sparse Transformer fixed pattern, fp64: masked dense softmax over
 // fixed_allows. q, k, v: [B,H,N,D]; sel as in lo_attn_rows.
 int32_t lo_fixed_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q, const double* k,

@@ -613,13 +613,97 @@ def pin_sampled_rows_match_full(lib):
         assert np.array_equal(os_[x], o[b, h, i]) and ls_[x] == l[b, h, i]
 
 
+# --- backward -------------------------------------------------------------
+
+def _fd_loss(lib, args, kw, dout):
+    o, _ = oracle.attn_rows(*args, **kw, lib=lib)
+    return float((o * dout).sum())
+
+
+def pin_backward_finite_differences(lib):
+    """The backward against central differences of the forward's loss sum(dO * O)
+    (fp64, eps 1e-6): shared and separate projections, causal, dilation, segments."""
+    cases = [
+        dict(N=16, glob=(0, 5), R=2, dil=[1, 2], causal=False, sep=False, seg=False),
+        dict(N=18, glob=(3, 11), R=3, dil=[2, 1], causal=True, sep=True, seg=False),
+        dict(N=16, glob=(0, 8), R=2, dil=[1, 1], causal=False, sep=True, seg=True),
+    ]
+    rng = np.random.default_rng(21)
+    for c in cases:
+        B, H, N, D = 2, 2, c["N"], 4
+        q, k, v = rand_qkv(rng, B, H, N, D)
+        qg, kg, vg = rand_qkv(rng, B, H, N, D) if c["sep"] else (None, None, None)
+        seg = np.repeat(np.arange(2), N // 2)[None].repeat(B, 0) if c["seg"] else None
+        dout = rng.standard_normal((B, H, N, D))
+        grads = oracle.attn_backward(q, k, v, dout, c["glob"], c["R"], c["dil"], c["causal"],
+                                     qg, kg, vg, seg=seg, lib=lib)
+        tensors = [q, k, v] + ([qg, kg, vg] if c["sep"] else [])
+        kw = dict(global_idx=c["glob"], radius=c["R"], dilation=c["dil"], causal=c["causal"],
+                  qg=qg, kg=kg, vg=vg, seg=seg)
+        eps = 1e-6
+        for t, g in zip(tensors, grads):
+            coords = [tuple(rng.integers(0, n) for n in t.shape) for _ in range(6)]
+            coords += [(0, 1, c["glob"][0], 2), (1, 0, c["glob"][1], 0)]  # global rows / keys
+            for x in coords:
+                old = t[x]
+                t[x] = old + eps
+                lp = _fd_loss(lib, (q, k, v), kw, dout)
+                t[x] = old - eps
+                lm = _fd_loss(lib, (q, k, v), kw, dout)
+                t[x] = old
+                fd = (lp - lm) / (2 * eps)
+                assert abs(fd - g[x]) <= 1e-6 * (1 + abs(fd)), (c, x, fd, g[x])
+
+
+def pin_backward_dense_autograd(lib):
+    """A window covering every key, no global token: the gradients of dense
+    softmax attention, from torch autograd in float64."""
+    rng = np.random.default_rng(22)
+    for causal in (False, True):
+        q, k, v = rand_qkv(rng, 1, 2, 12, 8)
+        dout = rng.standard_normal(q.shape)
+        grads = oracle.attn_backward(q, k, v, dout, (), 12, None, causal, lib=lib)
+        t = [torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v)]
+        s = t[0] @ t[1].transpose(-1, -2) / math.sqrt(8)
+        if causal:
+            s = s.masked_fill(torch.ones(12, 12, dtype=torch.bool).triu(1), float("-inf"))
+        o = torch.softmax(s, -1) @ t[2]
+        o.backward(torch.from_numpy(dout))
+        for a, b in zip(grads, t):
+            assert np.allclose(a, b.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def pin_backward_shift_invariants(lib):
+    """Shifting every key of one projection by c moves each row's logits by a
+    constant, so the keys' gradients sum to 0; shifting every value by c moves
+    each output by c, so the values' gradients sum to the rows' dO (per head,
+    per projection set)."""
+    rng = np.random.default_rng(23)
+    B, H, N, D = 1, 3, 40, 6
+    q, k, v = rand_qkv(rng, B, H, N, D)
+    qg, kg, vg = rand_qkv(rng, B, H, N, D)
+    dout = rng.standard_normal(q.shape)
+    glob = (2, 17, 30)
+    dq, dk, dv, dqg, dkg, dvg = oracle.attn_backward(q, k, v, dout, glob, 4, [1, 3, 2], True,
+                                                     qg, kg, vg, lib=lib)
+    isg = np.zeros(N, bool)
+    isg[list(glob)] = True
+    assert np.allclose(dk.sum(2), 0, atol=1e-12) and np.allclose(dkg.sum(2), 0, atol=1e-12)
+    assert np.allclose(dv.sum(2), dout[:, :, ~isg].sum(2), atol=1e-12)
+    assert np.allclose(dvg.sum(2), dout[:, :, isg].sum(2), atol=1e-12)
+    # global rows touch only the separate projections' gradients, and conversely
+    assert (dqg[:, :, ~isg] == 0).all() and (dq[:, :, isg] == 0).all()
+
+
 PINS = [pin_mask_matches_enumeration, pin_counts_closed_form, pin_counts_full_workloads,
         pin_longnet_counts, pin_longnet_worked_example, pin_longnet_offsets_partition,
         pin_dense_special_cases, pin_global_rows_are_full_rows, pin_brute_force_band,
         pin_etc_four_pieces, pin_relvec_reduces_to_scalar, pin_packing_equals_separate_documents,
         pin_fixed_pattern, pin_brute_force_longnet,
         pin_longnet_paths_agree,
-        pin_rows_sum_to_one, pin_uncovered_rows, pin_sampled_rows_match_full]
+        pin_rows_sum_to_one, pin_uncovered_rows, pin_sampled_rows_match_full,
+        pin_backward_finite_differences, pin_backward_dense_autograd,
+        pin_backward_shift_invariants]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -666,6 +750,14 @@ MUTANTS = [
     ("mixture-excludes-self", "if (!causal || j <= i) weight[j] = 1.0;",
      "if (!causal || j < i) weight[j] = 1.0;"),
     ("mixture-no-scatter", "if ((i - seg_start) % r[p] != off) continue;  // scattered zero row", ""),
+    ("backward-without-delta", "const double dS = P[j] * (dP[j] - Di);",
+     "const double dS = P[j] * dP[j];"),
+    ("backward-dk-unscaled", "dkb[(size_t)j * D + d] += dS * qi[d] * scale;",
+     "dkb[(size_t)j * D + d] += dS * qi[d];"),
+    ("backward-dv-from-dS", "dvb[(size_t)j * D + d] += P[j] * doi[d];",
+     "dvb[(size_t)j * D + d] += dS * doi[d];"),
+    ("backward-global-keys-to-shared", "double* dkb = (sep ? dkg : dk) + off;",
+     "double* dkb = dk + off;"),
 ]
 
 
