@@ -169,6 +169,42 @@ la_status la_fixed_forward(const la_dims *dims, const void *q, const void *k, co
 /* Bytes of workspace la_fixed_forward needs (0 for invalid arguments). */
 size_t la_fixed_workspace_size(const la_dims *dims, int32_t block_len, int32_t summary_len);
 
+/* Optional arguments of la_attn_backward. */
+typedef struct {
+  const void *qg, *kg, *vg; /* separate global projections as given to the forward (all or none) */
+  float *dqg, *dkg, *dvg;   /* their gradients, fp32 [B,H,N,D]: required iff qg, kg, vg are */
+  const int32_t *seg_ids;   /* device int32 [B][N] segment ids as given to the forward, or NULL */
+  void *workspace;          /* la_attn_backward_workspace_size() bytes, 256-byte aligned */
+  size_t workspace_bytes;
+} la_attn_bwd_ext;
+
+/* Backward of la_attn_forward for the band + global pattern (the training step
+ * after it; the chain rule through masked softmax attention, LongNet page,
+ * §3.4 "Standard Self-Attention and Sparse Attention (Preliminaries)", Eq. 2).
+ * With P_ij = c_ij exp(q_i.k_j / sqrt(D) - lse_i) over the forward's mask c:
+ *   D_i = dO_i . O_i,  dS_ij = P_ij (dO_i . v_j - D_i),
+ *   dq_i = sum_j dS_ij k_j / sqrt(D),  dk_j = sum_i dS_ij q_i / sqrt(D),
+ *   dv_j = sum_i P_ij dO_i.
+ * With separate global projections a global row's terms go to ext->dqg,
+ * ext->dkg, ext->dvg (through qg_i, kg_j, vg_j), every other row's to dq, dk, dv;
+ * each of the six is fully written (rows that receive nothing get 0).
+ *  q, k, v, global_idx, n_global, radius, dilation, causal: as given to the
+ *               forward; rel_bias / rel_vec are not supported here.
+ *  out, lse     the forward's output (dims/dtype as q) and its lse (fp32 [B,H,N],
+ *               required).
+ *  dout         device [B,H,N,D] in q's dtype: the loss gradient w.r.t. out.
+ *  dq, dk, dv   device fp32 [B,H,N,D] outputs; must not alias any input.
+ * Requires ext->workspace (fully overwritten). Pointers 16-byte aligned. Errors
+ * as for la_attn_forward. Two launches on `stream`, no allocation. */
+la_status la_attn_backward(const la_dims *dims, const void *q, const void *k, const void *v,
+                           const int32_t *global_idx, int32_t n_global, int32_t radius,
+                           const int32_t *dilation, int32_t causal, const void *out,
+                           const float *lse, const void *dout, float *dq, float *dk, float *dv,
+                           hipStream_t stream, const la_attn_bwd_ext *ext);
+
+/* Bytes of workspace la_attn_backward needs (0 for invalid dims). */
+size_t la_attn_backward_workspace_size(const la_dims *dims);
+
 /* Bytes of workspace la_attn_forward needs for these dims and n_global
  * (0 when n_global == 0). has_separate_global is accepted for symmetry and
  * does not change the size. Returns 0 for invalid dims. */

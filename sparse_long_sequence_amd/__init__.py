@@ -62,13 +62,20 @@ class LaDilatedExt(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
+class LaAttnBwdExt(ctypes.Structure):
+    _fields_ = [("qg", ctypes.c_void_p), ("kg", ctypes.c_void_p), ("vg", ctypes.c_void_p),
+                ("dqg", ctypes.c_void_p), ("dkg", ctypes.c_void_p), ("dvg", ctypes.c_void_p),
+                ("seg_ids", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _lib: Optional[ctypes.CDLL] = None
 
 # Every symbol include/longattn.h declares.
 EXPORTS = ("la_attn_forward", "la_dilated_forward", "la_fixed_forward", "la_attn_workspace_size",
            "la_dilated_workspace_size", "la_fixed_workspace_size", "la_check_global_idx",
-           "la_last_error", "la_version")
+           "la_last_error", "la_version", "la_attn_backward", "la_attn_backward_workspace_size")
 
 
 def lib() -> ctypes.CDLL:
@@ -101,6 +108,13 @@ def lib() -> ctypes.CDLL:
     L.la_attn_workspace_size.argtypes = [ctypes.POINTER(LaDims), ctypes.c_int32, ctypes.c_int32]
     L.la_dilated_workspace_size.restype = ctypes.c_size_t
     L.la_dilated_workspace_size.argtypes = [ctypes.POINTER(LaDims), _i32p, _i32p, ctypes.c_int32]
+    L.la_attn_backward.restype = ctypes.c_int32
+    L.la_attn_backward.argtypes = [ctypes.POINTER(LaDims), ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   _i32p, ctypes.c_int32] + [ctypes.c_void_p] * 6 + [
+                                   ctypes.c_void_p, ctypes.POINTER(LaAttnBwdExt)]
+    L.la_attn_backward_workspace_size.restype = ctypes.c_size_t
+    L.la_attn_backward_workspace_size.argtypes = [ctypes.POINTER(LaDims)]
     L.la_check_global_idx.restype = ctypes.c_int32
     L.la_check_global_idx.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p]
@@ -372,6 +386,76 @@ def la_fixed_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_le
     positions); returns ``(out, lse)``."""
     return bind_fixed(q, k, v, block_len, summary_len, causal, out, lse, workspace, stream,
                       want_lse)()
+
+
+def la_attn_backward_workspace_size(dims: LaDims) -> int:
+    return int(lib().la_attn_backward_workspace_size(ctypes.byref(dims)))
+
+
+def bind_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                       lse: torch.Tensor, dout: torch.Tensor,
+                       global_idx: Optional[torch.Tensor] = None, radius: int = 0,
+                       dilation: Optional[Sequence[int]] = None, causal: bool = False,
+                       qg: Optional[torch.Tensor] = None, kg: Optional[torch.Tensor] = None,
+                       vg: Optional[torch.Tensor] = None, seg_ids: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> BoundCall:
+    """Validate and marshal a :func:`la_attn_backward` call without issuing it.
+
+    ``out`` and ``lse`` are the forward's outputs for the same arguments and
+    ``dout`` the loss gradient w.r.t. ``out`` (dtype of ``q``). The call's
+    results are fp32 ``(dq, dk, dv)``, plus ``(dqg, dkg, dvg)`` with separate
+    global projections."""
+    dims = _dims(q)
+    ptrs = [_dev(t, q, name) for name, t in (("q", q), ("k", k), ("v", v), ("out", out),
+                                             ("dout", dout))]
+    if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() \
+            or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise LaError(LA_EINVAL, "lse must be a contiguous device fp32 [B, H, N] tensor")
+    n_global, gptr = 0, 0
+    if global_idx is not None:
+        if global_idx.dtype != torch.int32 or not global_idx.is_cuda or global_idx.dim() != 1:
+            raise LaError(LA_EINVAL, "global_idx must be a 1-D device int32 tensor")
+        n_global = global_idx.numel()
+        gptr = global_idx.data_ptr() if n_global else 0
+    if dilation is not None and len(dilation) != dims.H:
+        raise LaError(LA_EINVAL, "dilation needs one entry per head")
+    dil = None if dilation is None else _host_i32(dilation)
+    sptr = 0
+    if seg_ids is not None:
+        if seg_ids.dtype != torch.int32 or not seg_ids.is_cuda \
+                or tuple(seg_ids.shape) != (dims.B, dims.N):
+            raise LaError(LA_EINVAL, "seg_ids must be a device int32 [B, N] tensor")
+        seg_ids = seg_ids.contiguous()
+        sptr = seg_ids.data_ptr()
+    sep = qg is not None
+    grads = [torch.empty(q.shape, dtype=torch.float32, device=q.device)
+             for _ in range(6 if sep else 3)]
+    gp = [None] * 6
+    if sep:
+        gp = [_dev(qg, q, "qg"), _dev(kg, q, "kg"), _dev(vg, q, "vg")] + \
+             [t.data_ptr() for t in grads[3:]]
+    ws = _workspace(la_attn_backward_workspace_size(dims), q.device, workspace)
+    ext = LaAttnBwdExt(*gp, sptr or None, ws.data_ptr() if ws is not None else None,
+                       ws.numel() if ws is not None else 0)
+    args = (ctypes.byref(dims), ptrs[0], ptrs[1], ptrs[2], gptr or None, n_global, int(radius),
+            dil, int(bool(causal)), ptrs[3], lse.data_ptr(), ptrs[4],
+            grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(), _stream(q, stream),
+            ctypes.byref(ext))
+    keep = (dims, ext, dil, q, k, v, out, lse, dout, global_idx, seg_ids, qg, kg, vg, ws)
+    call = BoundCall(lib().la_attn_backward, args, keep, None, None)
+    call.grads = tuple(grads)
+    return call
+
+
+def la_attn_backward(q, k, v, out, lse, dout, global_idx=None, radius: int = 0, dilation=None,
+                     causal: bool = False, qg=None, kg=None, vg=None, seg_ids=None,
+                     workspace=None, stream=None):
+    """One backward call; returns fp32 ``(dq, dk, dv)`` or, with separate global
+    projections, ``(dq, dk, dv, dqg, dkg, dvg)``."""
+    call = bind_attn_backward(q, k, v, out, lse, dout, global_idx, radius, dilation, causal,
+                              qg, kg, vg, seg_ids, workspace, stream)
+    call()
+    return call.grads
 
 
 def la_check_global_idx(global_idx: torch.Tensor, N: int, stream=None) -> bool:

@@ -363,6 +363,82 @@ la_status la_fixed_forward(const la_dims* dims, const void* q, const void* k, co
   return LA_OK;
 }
 
+size_t la_attn_backward_workspace_size(const la_dims* dims) {
+  if (check_dims(dims, false) != LA_OK) return 0;
+  return align_up((size_t)dims->B * dims->H * dims->N * sizeof(float));
+}
+
+la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, const void* v,
+                           const int32_t* global_idx, int32_t n_global, int32_t radius,
+                           const int32_t* dilation, int32_t causal, const void* out,
+                           const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                           hipStream_t stream, const la_attn_bwd_ext* ext) {
+  la_status st = check_dims(dims, false);
+  if (st != LA_OK) return st;
+  if (is_empty(dims)) return LA_OK;
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv)
+    return fail(LA_EINVAL, "q, k, v, out, lse, dout, dq, dk and dv are required");
+  const void* ptrs[] = {q, k, v, out, lse, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(LA_EINVAL, "tensors must be 16-byte aligned");
+  if (n_global < 0 || n_global > dims->N) return fail(LA_EINVAL, "n_global must be in [0, N]");
+  if ((n_global > 0) != (global_idx != nullptr))
+    return fail(LA_EINVAL, "global_idx must be non-NULL exactly when n_global > 0");
+  if (radius < 0) return fail(LA_EINVAL, "radius must be >= 0");
+  if (causal != 0 && causal != 1) return fail(LA_EINVAL, "causal must be 0 or 1");
+  if (dims->H > la::kMaxHeadsDil) return fail(LA_EUNSUPPORTED, "H above 64");
+  la::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int32_t h = 0; h < dims->H; ++h) {
+    a.dil[h] = dilation ? dilation[h] : 1;
+    if (a.dil[h] < 1) return fail(LA_EINVAL, "dilation entries must be >= 1");
+  }
+  if (!ext || !ext->workspace || ext->workspace_bytes < la_attn_backward_workspace_size(dims))
+    return fail(LA_EINVAL, "workspace missing or smaller than la_attn_backward_workspace_size()");
+  if (((uintptr_t)ext->workspace & (kAlign - 1)) != 0)
+    return fail(LA_EINVAL, "workspace must be 256-byte aligned");
+  const bool sep_in = ext->qg || ext->kg || ext->vg;
+  const bool sep_out = ext->dqg || ext->dkg || ext->dvg;
+  if (sep_in || sep_out) {
+    if (!(ext->qg && ext->kg && ext->vg && ext->dqg && ext->dkg && ext->dvg))
+      return fail(LA_EINVAL, "qg, kg, vg and dqg, dkg, dvg: all six or none");
+    const void* gp[] = {ext->qg, ext->kg, ext->vg, ext->dqg, ext->dkg, ext->dvg};
+    for (const void* p : gp)
+      if (!aligned16(p)) return fail(LA_EINVAL, "tensors must be 16-byte aligned");
+  }
+  if (ext->seg_ids && ((uintptr_t)ext->seg_ids & 3u) != 0)
+    return fail(LA_EINVAL, "ext->seg_ids must be 4-byte aligned");
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.qg = ext->qg;
+  a.kg = ext->kg;
+  a.vg = ext->vg;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.gidx = global_idx;
+  a.seg = ext->seg_ids;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dqg = ext->dqg;
+  a.dkg = ext->dkg;
+  a.dvg = ext->dvg;
+  a.delta = reinterpret_cast<float*>(ext->workspace);
+  a.n_global = n_global;
+  a.B = dims->B;
+  a.H = dims->H;
+  a.N = dims->N;
+  a.radius = radius;
+  a.causal = causal;
+  a.sep = sep_in ? 1 : 0;
+  a.scale = (float)(1.0 / sqrt((double)kDHead));
+  hipError_t e = la::launch_attn_bwd(a, dims->dtype, stream);
+  if (e != hipSuccess) return fail(LA_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(e));
+  return LA_OK;
+}
+
 la_status la_check_global_idx(const int32_t* global_idx, int32_t n_global, int32_t N,
                               hipStream_t stream) {
   if (n_global < 0 || n_global > N) return fail(LA_EINVAL, "n_global must be in [0, N]");

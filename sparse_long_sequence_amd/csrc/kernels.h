@@ -72,7 +72,22 @@ struct DilArgs {
   float scale_log2;
 };
 
+// Backward of band + global attention (attn_bwd.hip). Tensors are [B,H,N,64];
+// q, k, v, qg, kg, vg, out, dout in the call's dtype; gradients fp32.
+struct BwdArgs {
+  const void *q, *k, *v, *qg, *kg, *vg, *out, *dout;
+  const float* lse;
+  const int32_t* gidx;
+  const int32_t* seg;
+  float *dq, *dk, *dv, *dqg, *dkg, *dvg;
+  float* delta;  // workspace: D_i = dO_i . O_i per row
+  int32_t n_global, B, H, N, radius, causal, sep;
+  int32_t dil[kMaxHeadsDil];
+  float scale;
+};
+
 hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream);
+hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream);
 hipError_t launch_dilated(const DilArgs& a, hipStream_t stream);
 int32_t host_band_tiles_of_head(int32_t N, int32_t d, int32_t tq);
 int32_t host_query_tile(int32_t dtype);  // query rows per workgroup

@@ -123,6 +123,36 @@ def test_fixed_argument_errors(L):
     assert la.la_fixed_workspace_size(d, 256, 96) == 0
 
 
+def test_backward_argument_errors(L):
+    d = LaDims(1, 2, 128, 64, la.LA_BF16)
+    need = la.la_attn_backward_workspace_size(d)
+    assert need == 1 * 2 * 128 * 4 + 256 - (1 * 2 * 128 * 4) % 256 or need == 1 * 2 * 128 * 4
+    ext = la.LaAttnBwdExt(None, None, None, None, None, None, None, FAKE, need)
+
+    def call(dims=d, q=FAKE, lse=FAKE, dq=FAKE, gidx=None, n_global=0, radius=4, causal=0,
+             e=ext):
+        return L.la_attn_backward(ctypes.byref(dims) if dims is not None else None, q, FAKE, FAKE,
+                                  gidx, n_global, radius, None, causal, FAKE, lse, FAKE, dq, FAKE,
+                                  FAKE, None, ctypes.byref(e) if e is not None else None)
+    assert call(dims=None) == la.LA_EINVAL
+    assert call(q=None) == la.LA_EINVAL
+    assert call(lse=None) == la.LA_EINVAL                      # lse is required
+    assert call(dq=FAKE + 4) == la.LA_EINVAL                   # misaligned
+    assert call(radius=-1) == la.LA_EINVAL
+    assert call(causal=2) == la.LA_EINVAL
+    assert call(n_global=2) == la.LA_EINVAL                    # count without indices
+    assert call(e=None) == la.LA_EINVAL                        # no workspace
+    assert call(e=la.LaAttnBwdExt(None, None, None, None, None, None, None, FAKE, need - 1)) \
+        == la.LA_EINVAL
+    assert call(e=la.LaAttnBwdExt(FAKE, FAKE, FAKE, None, None, None, None, FAKE, need)) \
+        == la.LA_EINVAL                                        # qg.. without dqg..
+    assert call(e=la.LaAttnBwdExt(None, None, None, None, None, None, FAKE + 2, FAKE, need)) \
+        == la.LA_EINVAL                                        # misaligned seg_ids
+    assert call(dims=LaDims(1, 2, 128, 32, la.LA_BF16)) == la.LA_EUNSUPPORTED
+    assert "D == 64" in la.la_last_error()
+    assert call(dims=LaDims(0, 2, 128, 64, la.LA_BF16), e=None) == la.LA_OK  # empty: no-op
+
+
 def test_workspace_sizes(L):
     d = LaDims(2, 12, 4096, 64, la.LA_BF16)
     assert la.la_attn_workspace_size(d, 0) == 0

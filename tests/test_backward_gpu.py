@@ -1,0 +1,127 @@
+"""Parity of the HIP backward (la_attn_backward) with the fp64 oracle's backward.
+
+The GPU forward supplies out and lse (the backward's inputs by contract); the
+oracle gets only q, k, v (and qg, kg, vg), the mask arguments and dout, and
+recomputes everything else in fp64.
+
+Bar: per gradient tensor, max |gpu - oracle| <= tol * max |oracle|, with tol
+1e-4 for fp32 inputs and 2e-2 for bf16. For bf16, the forward's output O is
+rounded to bf16 (relative 2^-9) before it enters D_i = dO_i . O_i, and its lse
+sums bf16-rounded probabilities; P_ij = exp(s_ij - lse_i) and dS_ij then carry
+relative errors of a few 2^-9 against the exact values, which the oracle uses.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_long_sequence_amd as la
+from sparse_long_sequence_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    la.lib()
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rand(gen, shape, dtype):
+    return torch.randn(shape, generator=gen).to(TORCH[dtype])
+
+
+def to64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def check(tag, dtype, got, ref):
+    names = ("dq", "dk", "dv", "dqg", "dkg", "dvg")
+    assert len(got) == len(ref)
+    for name, g, r in zip(names, got, ref):
+        g = to64(g)
+        scale = max(np.abs(r).max(), 1e-30)
+        err = np.abs(g - r).max()
+        assert np.isfinite(g).all(), f"{tag} {name}: non-finite"
+        assert err <= TOL[dtype] * scale, f"{tag} {name}: max err {err} > {TOL[dtype]} * {scale}"
+
+
+def run_case(dev, tag, dtype, B, H, N, glob, R, dil, causal, sep, seg_rows, seed,
+             inputs=None):
+    say(f"backward {tag}: {dtype} B={B} H={H} N={N} |G|={len(glob)} R={R} dil={dil} "
+        f"causal={causal} sep={sep} seg={seg_rows}")
+    gen = torch.Generator().manual_seed(seed)
+    if inputs is None:
+        q, k, v = (rand(gen, (B, H, N, 64), dtype) for _ in range(3))
+        qg, kg, vg = (rand(gen, (B, H, N, 64), dtype) for _ in range(3)) if sep else (None,) * 3
+    else:
+        q, k, v, qg, kg, vg = inputs
+    dout = rand(gen, (B, H, N, 64), dtype)
+    seg = None
+    if seg_rows:
+        # documents of the given lengths, one id each, per batch row
+        seg = torch.tensor(np.concatenate([np.full(n, x, np.int32) for x, n in enumerate(seg_rows)])
+                           )[None].repeat(B, 1)
+    d = lambda t: None if t is None else t.to(dev).contiguous()
+    gidx = torch.tensor(sorted(glob), dtype=torch.int32, device=dev) if glob else None
+    out, lse = la.la_attn_forward(d(q), d(k), d(v), gidx, R, dil, causal, qg=d(qg), kg=d(kg),
+                                  vg=d(vg), seg_ids=d(seg))
+    grads = la.la_attn_backward(d(q), d(k), d(v), out, lse, d(dout), gidx, R, dil, causal,
+                                qg=d(qg), kg=d(kg), vg=d(vg), seg_ids=d(seg))
+    torch.cuda.synchronize()
+    f64 = lambda t: None if t is None else to64(t)
+    ref = oracle.attn_backward(f64(q), f64(k), f64(v), f64(dout), tuple(glob), R, dil, causal,
+                               f64(qg), f64(kg), f64(vg),
+                               seg=None if seg is None else seg.numpy())
+    check(tag, dtype, grads, ref)
+    return grads
+
+
+CASES = [
+    # tag, dtype, B, H, N, globals, R, dilation, causal, separate, segments
+    ("shared", "bf16", 2, 2, 300, (0, 5, 100), 16, [1, 2], False, False, None),
+    ("separate-causal", "bf16", 1, 2, 257, (3, 64, 65, 200), 8, [1, 3], True, True, None),
+    ("segments", "bf16", 1, 3, 256, (0, 100, 200), 12, None, False, False, (100, 100, 56)),
+    ("f32-causal", "f32", 1, 2, 200, (), 20, [1, 1], True, False, None),
+    ("f32-separate", "f32", 1, 1, 130, (7, 64), 5, [2], False, True, None),
+    ("dense-window", "bf16", 1, 2, 96, (), 96, None, False, False, None),
+    ("no-window", "bf16", 1, 1, 128, (10, 11), 0, None, False, False, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_backward_small(dev, case):
+    tag, dtype, B, H, N, glob, R, dil, causal, sep, seg = case
+    run_case(dev, tag, dtype, B, H, N, glob, R, dil, causal, sep, seg,
+             seed=300 + CASES.index(case))
+
+
+def test_backward_deterministic(dev):
+    """Two calls give bitwise equal gradients (no atomics, fixed order)."""
+    a = run_case(dev, "det-1", "bf16", 1, 2, 200, (0, 50), 10, None, False, True, None, seed=7)
+    b = run_case(dev, "det-2", "bf16", 1, 2, 200, (0, 50), 10, None, False, True, None, seed=7)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_longformer_base(dev):
+    """The Longformer-base shape (B=2, H=12, N=4096, R=256, 64 global tokens with
+    separate projections), every element against the oracle."""
+    w = W.LONGFORMER_BASE
+    inp = W.make_inputs(w)
+    run_case(dev, "longformer-base", "bf16", w.B, w.H, w.N, w.global_idx, w.radius, None,
+             w.causal, True, None, seed=w.seed,
+             inputs=(inp.q, inp.k, inp.v, inp.qg, inp.kg, inp.vg))
