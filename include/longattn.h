@@ -202,7 +202,8 @@ la_status la_attn_backward(const la_dims *dims, const void *q, const void *k, co
                            const float *lse, const void *dout, float *dq, float *dk, float *dv,
                            hipStream_t stream, const la_attn_bwd_ext *ext);
 
-/* Bytes of workspace la_attn_backward needs (0 for invalid dims). */
+/* Bytes of workspace la_attn_backward needs (0 for invalid dims): fp32 D_i per
+ * row and one global-flag byte per position, each part padded to 256 bytes. */
 size_t la_attn_backward_workspace_size(const la_dims *dims);
 
 /* Bytes of workspace la_attn_forward needs for these dims and n_global

@@ -365,7 +365,8 @@ la_status la_fixed_forward(const la_dims* dims, const void* q, const void* k, co
 
 size_t la_attn_backward_workspace_size(const la_dims* dims) {
   if (check_dims(dims, false) != LA_OK) return 0;
-  return align_up((size_t)dims->B * dims->H * dims->N * sizeof(float));
+  // D_i per row, then one global flag byte per position
+  return align_up((size_t)dims->B * dims->H * dims->N * sizeof(float)) + align_up((size_t)dims->N);
 }
 
 la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, const void* v,
@@ -426,6 +427,8 @@ la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, co
   a.dkg = ext->dkg;
   a.dvg = ext->dvg;
   a.delta = reinterpret_cast<float*>(ext->workspace);
+  a.gflag = reinterpret_cast<uint8_t*>(ext->workspace) +
+            align_up((size_t)dims->B * dims->H * dims->N * sizeof(float));
   a.n_global = n_global;
   a.B = dims->B;
   a.H = dims->H;

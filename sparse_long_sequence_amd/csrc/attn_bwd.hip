@@ -14,9 +14,10 @@
 // Linear Projections for Local vs. Global Attention") differentiate through
 // qg_i, kg_j, vg_j, so their terms land in dqg, dkg, dvg.
 //
-// Two launches, no atomics: a query-centric pass (one wave per row) writes
-// D_i and dQ_i; a key-centric pass (one wave per key) visits every row that
-// attends to its key and writes dK_j and dV_j in one store. Lane d of a wave
+// No atomics: after a pass that marks the global positions, a query-centric
+// pass (one wave per row) writes D_i and dQ_i, and a key-centric pass (one
+// wave per key) visits every row that attends to its key and writes dK_j and
+// dV_j in one store. Lane d of a wave
 // holds element d of the 64-wide vectors; dot products are wave reductions.
 // This is the plain first form of the backward: fp32 VALU work, no MFMA.
 #include <hip/hip_runtime.h>
@@ -51,9 +52,14 @@ __device__ __forceinline__ bool in_band(int32_t i, int32_t j, int32_t R, int32_t
   return t >= -R && t <= R;
 }
 
-__device__ __forceinline__ bool is_global(const BwdArgs& a, int32_t p) {
-  return a.n_global > 0 && sorted_contains(a.gidx, a.n_global, p);
+// Global flags of the N positions (one byte each, in the workspace), so the
+// loops below test membership with one load instead of a search.
+__global__ __launch_bounds__(256) void bwd_flags_kernel(BwdArgs a) {
+  const int32_t p = (int32_t)(blockIdx.x * 256 + threadIdx.x);
+  if (p < a.N) a.gflag[p] = (a.n_global > 0 && sorted_contains(a.gidx, a.n_global, p)) ? 1 : 0;
 }
+
+constexpr int kBatch = 4;  // pairs whose loads and reductions are issued together
 
 // Row i's gradient dQ_i (query-centric), and D_i into the workspace.
 template <typename T>
@@ -67,7 +73,7 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_kernel(BwdArgs a) {
   const int64_t bh = row / N;
   const int32_t h = (int32_t)(bh % a.H), b = (int32_t)(bh / a.H);
   const size_t hoff = (size_t)bh * N * kD;
-  const bool ig = is_global(a, i);
+  const bool ig = a.gflag[i] != 0;
   const bool sep = ig && a.sep;
   const T* Q = static_cast<const T*>(sep ? a.qg : a.q) + hoff;
   const T* K = static_cast<const T*>(sep ? a.kg : a.k) + hoff;
@@ -81,33 +87,47 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_kernel(BwdArgs a) {
   const int32_t* segb = a.seg ? a.seg + (size_t)b * N : nullptr;
   const int32_t si = segb ? segb[i] : 0;
   float acc = 0.f;
-  auto visit = [&](int32_t j) {
-    const float kv = load_el(K + (size_t)j * kD + lane);
-    const float vv = load_el(V + (size_t)j * kD + lane);
-    const float p = __expf(wave_sum(qv * kv) * a.scale - lse);
-    const float dp = wave_sum(dov * vv);
-    acc += p * (dp - Di) * kv;
+  // keys key_of(x), x in [0, n) (-1: skip), kBatch at a time; a skipped slot
+  // reads row i (always valid) and gets weight 0
+  auto sweep = [&](int32_t n, auto key_of) {
+    for (int32_t x0 = 0; x0 < n; x0 += kBatch) {
+      int32_t j[kBatch];
+      float kv[kBatch], vv[kBatch], s[kBatch], dp[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        j[e] = x0 + e < n ? key_of(x0 + e) : -1;
+        if (j[e] >= 0 && segb && segb[j[e]] != si) j[e] = -1;
+        const int32_t r = j[e] >= 0 ? j[e] : i;
+        kv[e] = load_el(K + (size_t)r * kD + lane);
+        vv[e] = load_el(V + (size_t)r * kD + lane);
+      }
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        s[e] = wave_sum(qv * kv[e]);
+        dp[e] = wave_sum(dov * vv[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const float p = j[e] >= 0 ? __expf(s[e] * a.scale - lse) : 0.f;
+        acc += p * (dp[e] - Di) * kv[e];
+      }
+    }
   };
   if (lse != kNegInf) {  // a row without keys has no gradient
     if (ig) {  // a global row attends to every key (causal: up to itself)
-      const int32_t last = a.causal ? i : N - 1;
-      for (int32_t j = 0; j <= last; ++j)
-        if (!segb || segb[j] == si) visit(j);
+      sweep(a.causal ? i + 1 : N, [&](int32_t x) { return x; });
     } else {
       const int32_t d = a.dil[h], R = a.radius;
       // the window's keys inside [0, N): t in [t0, t1]
       const int32_t t0 = -min(R, i / d);
       const int32_t t1 = a.causal ? 0 : min(R, (N - 1 - i) / d);
-      for (int32_t t = t0; t <= t1; ++t) {
-        const int32_t j = i + t * d;
-        if (!segb || segb[j] == si) visit(j);
-      }
+      sweep(t1 - t0 + 1, [&](int32_t x) { return i + (t0 + x) * d; });
       // global keys outside the window (a global key in it was counted there)
-      for (int32_t g = 0; g < a.n_global; ++g) {
-        const int32_t j = a.gidx[g];
-        if (j < 0 || j >= N || (a.causal && j > i) || in_band(i, j, R, d, a.causal)) continue;
-        if (!segb || segb[j] == si) visit(j);
-      }
+      sweep(a.n_global, [&](int32_t x) {
+        const int32_t j = a.gidx[x];
+        const bool skip = j < 0 || j >= N || (a.causal && j > i) || in_band(i, j, R, d, a.causal);
+        return skip ? -1 : j;
+      });
     }
   }
   const float g = acc * a.scale;
@@ -137,18 +157,39 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_kernel(BwdArgs a) {
   const int32_t* segb = a.seg ? a.seg + (size_t)b * N : nullptr;
   const int32_t sj = segb ? segb[j] : 0;
   const int32_t d = a.dil[h], R = a.radius;
-  const bool jg = is_global(a, j);
+  const bool jg = a.gflag[j] != 0;
 
-  // one (row, key) pair through projections (Q, K, V) into (dk, dv)
-  auto pair = [&](const T* Q, float kv, float vv, int32_t i, float& dk, float& dv) {
-    const float li = lse[i];
-    if (li == kNegInf) return;
-    const float qv = load_el(Q + (size_t)i * kD + lane);
-    const float dov = load_el(dO + (size_t)i * kD + lane);
-    const float p = __expf(wave_sum(qv * kv) * a.scale - li);
-    const float dp = wave_sum(dov * vv);
-    dv += p * dov;
-    dk += p * (dp - delta[i]) * qv;
+  // rows row_of(x), x in [0, n) (-1: skip), through projections Q with this
+  // key's (kv, vv), into (dk, dv); kBatch rows at a time, a skipped slot reads
+  // row j (always valid) and gets weight 0
+  auto sweep = [&](int32_t n, const T* Q, float kv, float vv, float& dk, float& dv,
+                   auto row_of) {
+    for (int32_t x0 = 0; x0 < n; x0 += kBatch) {
+      int32_t i[kBatch];
+      float qv[kBatch], dov[kBatch], li[kBatch], di[kBatch], s[kBatch], dp[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        i[e] = x0 + e < n ? row_of(x0 + e) : -1;
+        if (i[e] >= 0 && segb && segb[i[e]] != sj) i[e] = -1;
+        const int32_t r = i[e] >= 0 ? i[e] : j;
+        qv[e] = load_el(Q + (size_t)r * kD + lane);
+        dov[e] = load_el(dO + (size_t)r * kD + lane);
+        li[e] = lse[r];
+        di[e] = delta[r];
+      }
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        s[e] = wave_sum(qv[e] * kv);
+        dp[e] = wave_sum(dov[e] * vv);
+      }
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const bool on = i[e] >= 0 && li[e] != kNegInf;
+        const float p = on ? __expf(s[e] * a.scale - li[e]) : 0.f;
+        dv += p * dov[e];
+        dk += p * (dp[e] - di[e]) * qv[e];
+      }
+    }
   };
 
   const T* Qs = static_cast<const T*>(a.q) + hoff;
@@ -159,36 +200,32 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_kernel(BwdArgs a) {
   {
     const int32_t u0 = a.causal ? 0 : -min(R, j / d);
     const int32_t u1 = min(R, (N - 1 - j) / d);
-    for (int32_t u = u0; u <= u1; ++u) {
-      const int32_t i = j + u * d;
-      if (is_global(a, i) || (segb && segb[i] != sj)) continue;
-      pair(Qs, kv, vv, i, dk, dv);
-    }
+    sweep(u1 - u0 + 1, Qs, kv, vv, dk, dv, [&](int32_t x) {
+      const int32_t i = j + (u0 + x) * d;
+      return a.gflag[i] ? -1 : i;
+    });
   }
   // a global key: every other non-global row (causal: from j on)
   if (jg) {
-    for (int32_t i = a.causal ? j : 0; i < N; ++i) {
-      if (in_band(i, j, R, d, a.causal) || is_global(a, i) || (segb && segb[i] != sj)) continue;
-      pair(Qs, kv, vv, i, dk, dv);
-    }
+    const int32_t i0 = a.causal ? j : 0;
+    sweep(N - i0, Qs, kv, vv, dk, dv, [&](int32_t x) {
+      const int32_t i = i0 + x;
+      return (in_band(i, j, R, d, a.causal) || a.gflag[i]) ? -1 : i;
+    });
   }
   // global rows attend to every key (causal: rows from j on)
+  auto grow = [&](int32_t x) {
+    const int32_t i = a.gidx[x];
+    return (i < 0 || i >= N || (a.causal && i < j)) ? -1 : i;
+  };
   if (!a.sep) {
-    for (int32_t g = 0; g < a.n_global; ++g) {
-      const int32_t i = a.gidx[g];
-      if (i < 0 || i >= N || (a.causal && i < j) || (segb && segb[i] != sj)) continue;
-      pair(Qs, kv, vv, i, dk, dv);
-    }
+    sweep(a.n_global, Qs, kv, vv, dk, dv, grow);
   } else {
     const T* Qg = static_cast<const T*>(a.qg) + hoff;
     const float kgv = load_el(static_cast<const T*>(a.kg) + hoff + (size_t)j * kD + lane);
     const float vgv = load_el(static_cast<const T*>(a.vg) + hoff + (size_t)j * kD + lane);
     float dkg = 0.f, dvg = 0.f;
-    for (int32_t g = 0; g < a.n_global; ++g) {
-      const int32_t i = a.gidx[g];
-      if (i < 0 || i >= N || (a.causal && i < j) || (segb && segb[i] != sj)) continue;
-      pair(Qg, kgv, vgv, i, dkg, dvg);
-    }
+    sweep(a.n_global, Qg, kgv, vgv, dkg, dvg, grow);
     a.dkg[hoff + (size_t)j * kD + lane] = dkg * a.scale;
     a.dvg[hoff + (size_t)j * kD + lane] = dvg;
   }
@@ -202,6 +239,7 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) 
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   if (rows <= 0) return hipSuccess;
   const dim3 g((uint32_t)((rows + kWavesBwd - 1) / kWavesBwd)), blk(64 * kWavesBwd);
+  hipLaunchKernelGGL(bwd_flags_kernel, dim3((uint32_t)((a.N + 255) / 256)), dim3(256), 0, stream, a);
   if (dtype == 1) {
     hipLaunchKernelGGL(bwd_dq_kernel<bf16>, g, blk, 0, stream, a);
     hipLaunchKernelGGL(bwd_dkv_kernel<bf16>, g, blk, 0, stream, a);

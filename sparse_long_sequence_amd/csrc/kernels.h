@@ -81,6 +81,7 @@ struct BwdArgs {
   const int32_t* seg;
   float *dq, *dk, *dv, *dqg, *dkg, *dvg;
   float* delta;  // workspace: D_i = dO_i . O_i per row
+  uint8_t* gflag;  // workspace: 1 at the N positions in global_idx
   int32_t n_global, B, H, N, radius, causal, sep;
   int32_t dil[kMaxHeadsDil];
   float scale;
