@@ -34,11 +34,22 @@ constexpr int kWavesBwd = 4;  // rows (or keys) per workgroup
 __device__ __forceinline__ float load_el(const float* p) { return *p; }
 __device__ __forceinline__ float load_el(const bf16* p) { return (float)*p; }
 
-// Sum over the 64 lanes; every lane gets the same value.
+// Sum over the 64 lanes, in registers; every lane gets the same value (each
+// step adds a lane's value and its partner's, a commutative pair). DPP moves
+// within rows of 16 lanes: quad_perm [1,0,3,2] and [2,3,0,1] (partners l^1,
+// l^2), row_half_mirror (8 lanes reversed: the other quad) and row_mirror (16
+// lanes reversed: the other half-row); then the gfx950 half-wave swaps.
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                            0xF, 0xF, true));
+}
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x += dpp_partner<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_partner<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_partner<0x141>(x);  // row_half_mirror
+  x += dpp_partner<0x140>(x);  // row_mirror
+  return xor32_sum(xor16_sum(x));
 }
 
 // Dilated window of row i (the forward's band): j - i = t * dil, |t| <= R,
@@ -59,7 +70,7 @@ __global__ __launch_bounds__(256) void bwd_flags_kernel(BwdArgs a) {
   if (p < a.N) a.gflag[p] = (a.n_global > 0 && sorted_contains(a.gidx, a.n_global, p)) ? 1 : 0;
 }
 
-constexpr int kBatch = 4;  // pairs whose loads and reductions are issued together
+constexpr int kBatch = 8;  // pairs whose loads and reductions are issued together
 
 // Row i's gradient dQ_i (query-centric), and D_i into the workspace.
 template <typename T>
