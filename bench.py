@@ -195,12 +195,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_longformer_base_traffic.
 
 
 def kernel_sources_digest() -> str:
-    """sha256 over the sources the HIP library is built from (and its build flags)."""
+    """sha256 over the sources the forward kernels and their launches are built from
+    (and the build flags); the backward's own source, attn_bwd.hip, is left out."""
     import glob
 
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "sparse_long_sequence_amd")
-    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + \
+    files = sorted(f for f in glob.glob(os.path.join(pkg, "csrc", "*"))
+                   if os.path.basename(f) != "attn_bwd.hip") + \
         sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))) + [os.path.join(pkg, "build.py")]
     for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
