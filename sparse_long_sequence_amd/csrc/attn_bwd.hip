@@ -19,7 +19,9 @@
 // wave per key) visits every row that attends to its key and writes dK_j and
 // dV_j in one store. Lane d of a wave
 // holds element d of the 64-wide vectors; dot products are wave reductions.
-// This is the plain first form of the backward: fp32 VALU work, no MFMA.
+// This is the plain first form of the backward: fp32 VALU work, no MFMA. The
+// fp32 path keeps one lane per vector element (dot products as wave sums); the
+// bf16 path (below) puts one key or row on each lane instead.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -244,6 +246,228 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_kernel(BwdArgs a) {
   a.dv[hoff + (size_t)j * kD + lane] = dv;
 }
 
+// ---------------------------------------------------------------------------
+// bf16 form: one lane per key (dQ) or per row (dK, dV). Each lane loads whole
+// 128-byte rows and forms its own dot products against the wave's query or key
+// vectors, which sit in LDS (read as broadcasts), so a pair costs no cross-lane
+// work; each lane keeps a 64-wide partial gradient, summed across the lanes once
+// per row (or key) at the end.
+// ---------------------------------------------------------------------------
+
+// Eight bf16 (one 16-byte chunk, element 2e in the low half of word e) to fp32.
+__device__ __forceinline__ void unpack8(const uint4& u, float (&f)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = __builtin_bit_cast(float, w[e] << 16);
+    f[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xffff0000u);
+  }
+}
+
+// A 64-element bf16 row as eight 16-byte chunks.
+__device__ __forceinline__ void load_row(const bf16* row, uint4 (&c)[8]) {
+  const uint4* p = reinterpret_cast<const uint4*>(row);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) c[k] = p[k];
+}
+
+// x . y over 64 elements: x packed in chunks, y a wave vector in LDS.
+__device__ __forceinline__ float dot_row(const uint4 (&c)[8], const float* y) {
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float f[8];
+    unpack8(c[k], f);
+    const float4 y0 = *reinterpret_cast<const float4*>(y + 8 * k);
+    const float4 y1 = *reinterpret_cast<const float4*>(y + 8 * k + 4);
+    s += f[0] * y0.x + f[1] * y0.y + f[2] * y0.z + f[3] * y0.w;
+    s += f[4] * y1.x + f[5] * y1.y + f[6] * y1.z + f[7] * y1.w;
+  }
+  return s;
+}
+
+// acc += w * row (row packed in chunks)
+__device__ __forceinline__ void axpy_row(float (&acc)[kD], float w, const uint4 (&c)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float f[8];
+    unpack8(c[k], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[8 * k + e] += w * f[e];
+  }
+}
+
+// Lane d receives the sum over the lanes of acc[d].
+__device__ __forceinline__ float lane_totals(const float (&acc)[kD], int32_t lane) {
+  float res = 0.f;
+#pragma unroll
+  for (int d = 0; d < kD; ++d) {
+    const float t = wave_sum(acc[d]);
+    res = lane == d ? t : res;
+  }
+  return res;
+}
+
+__global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_rows_kernel(BwdArgs a) {
+  __shared__ float vq[kWavesBwd][kD], vdo[kWavesBwd][kD];
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t wv = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  const int64_t row0 = (int64_t)blockIdx.x * kWavesBwd + wv;
+  const bool valid = row0 < rows;
+  const int64_t row = valid ? row0 : rows - 1;  // a wave past the end stages a valid row
+  const int32_t N = a.N;
+  const int32_t i = (int32_t)(row % N);
+  const int64_t bh = row / N;
+  const int32_t h = (int32_t)(bh % a.H), b = (int32_t)(bh / a.H);
+  const size_t hoff = (size_t)bh * N * kD;
+  const bool ig = a.gflag[i] != 0;
+  const bool sep = ig && a.sep;
+  const bf16* Q = static_cast<const bf16*>(sep ? a.qg : a.q) + hoff;
+  const bf16* K = static_cast<const bf16*>(sep ? a.kg : a.k) + hoff;
+  const bf16* V = static_cast<const bf16*>(sep ? a.vg : a.v) + hoff;
+  const float dov = load_el(static_cast<const bf16*>(a.dout) + hoff + (size_t)i * kD + lane);
+  const float ov = load_el(static_cast<const bf16*>(a.out) + hoff + (size_t)i * kD + lane);
+  const float Di = wave_sum(dov * ov);
+  vq[wv][lane] = load_el(Q + (size_t)i * kD + lane);
+  vdo[wv][lane] = dov;
+  __syncthreads();  // the only barrier: every wave reaches it
+  if (!valid) return;
+  if (lane == 0) a.delta[row] = Di;
+  const float lse = a.lse[row];
+  const int32_t* segb = a.seg ? a.seg + (size_t)b * N : nullptr;
+  const int32_t si = segb ? segb[i] : 0;
+  float acc[kD];
+#pragma unroll
+  for (int d = 0; d < kD; ++d) acc[d] = 0.f;
+  // keys key_of(x), x in [0, n) (-1: skip), one per lane; a skipped lane
+  // reads row i (always valid) and gets weight 0
+  auto sweep = [&](int32_t n, auto key_of) {
+    for (int32_t x0 = 0; x0 < n; x0 += 64) {
+      const int32_t x = x0 + lane;
+      int32_t j = x < n ? key_of(x) : -1;
+      if (j >= 0 && segb && segb[j] != si) j = -1;
+      const int32_t r = j >= 0 ? j : i;
+      uint4 kc[8], vc[8];
+      load_row(K + (size_t)r * kD, kc);
+      load_row(V + (size_t)r * kD, vc);
+      const float s = dot_row(kc, vq[wv]);
+      const float dp = dot_row(vc, vdo[wv]);
+      const float p = j >= 0 ? __expf(s * a.scale - lse) : 0.f;
+      axpy_row(acc, p * (dp - Di), kc);
+    }
+  };
+  if (lse != kNegInf) {
+    if (ig) {
+      sweep(a.causal ? i + 1 : N, [&](int32_t x) { return x; });
+    } else {
+      const int32_t d = a.dil[h], R = a.radius;
+      const int32_t t0 = -min(R, i / d);
+      const int32_t t1 = a.causal ? 0 : min(R, (N - 1 - i) / d);
+      sweep(t1 - t0 + 1, [&](int32_t x) { return i + (t0 + x) * d; });
+      sweep(a.n_global, [&](int32_t x) {
+        const int32_t j = a.gidx[x];
+        const bool skip = j < 0 || j >= N || (a.causal && j > i) || in_band(i, j, R, d, a.causal);
+        return skip ? -1 : j;
+      });
+    }
+  }
+  const float g = lane_totals(acc, lane) * a.scale;
+  if (a.sep) {
+    a.dq[hoff + (size_t)i * kD + lane] = ig ? 0.f : g;
+    a.dqg[hoff + (size_t)i * kD + lane] = ig ? g : 0.f;
+  } else {
+    a.dq[hoff + (size_t)i * kD + lane] = g;
+  }
+}
+
+__global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_rows_kernel(BwdArgs a) {
+  // this wave's key and value vectors, shared and (separate projections) global
+  __shared__ float vk[kWavesBwd][kD], vv[kWavesBwd][kD], vkg[kWavesBwd][kD], vvg[kWavesBwd][kD];
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t wv = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
+  const int64_t keys = (int64_t)a.B * a.H * a.N;
+  const int64_t key0 = (int64_t)blockIdx.x * kWavesBwd + wv;
+  const bool valid = key0 < keys;
+  const int64_t key = valid ? key0 : keys - 1;
+  const int32_t N = a.N;
+  const int32_t j = (int32_t)(key % N);
+  const int64_t bh = key / N;
+  const int32_t h = (int32_t)(bh % a.H), b = (int32_t)(bh / a.H);
+  const size_t hoff = (size_t)bh * N * kD;
+  const size_t jo = hoff + (size_t)j * kD + lane;
+  vk[wv][lane] = load_el(static_cast<const bf16*>(a.k) + jo);
+  vv[wv][lane] = load_el(static_cast<const bf16*>(a.v) + jo);
+  if (a.sep) {
+    vkg[wv][lane] = load_el(static_cast<const bf16*>(a.kg) + jo);
+    vvg[wv][lane] = load_el(static_cast<const bf16*>(a.vg) + jo);
+  }
+  __syncthreads();  // the only barrier: every wave reaches it
+  if (!valid) return;
+  const float* lse = a.lse + (size_t)bh * N;
+  const float* delta = a.delta + (size_t)bh * N;
+  const bf16* dO = static_cast<const bf16*>(a.dout) + hoff;
+  const int32_t* segb = a.seg ? a.seg + (size_t)b * N : nullptr;
+  const int32_t sj = segb ? segb[j] : 0;
+  const int32_t d = a.dil[h], R = a.radius;
+  const bool jg = a.gflag[j] != 0;
+  float ak[kD], av[kD];
+  auto zero = [&]() {
+#pragma unroll
+    for (int e = 0; e < kD; ++e) ak[e] = av[e] = 0.f;
+  };
+  // rows row_of(x), x in [0, n) (-1: skip), one per lane, through projection Q
+  // against key vectors (kvec, vvec); a skipped lane reads row j and gets weight 0
+  auto sweep = [&](int32_t n, const bf16* Q, const float* kvec, const float* vvec, auto row_of) {
+    for (int32_t x0 = 0; x0 < n; x0 += 64) {
+      const int32_t x = x0 + lane;
+      int32_t i = x < n ? row_of(x) : -1;
+      if (i >= 0 && segb && segb[i] != sj) i = -1;
+      const int32_t r = i >= 0 ? i : j;
+      uint4 qc[8], oc[8];
+      load_row(Q + (size_t)r * kD, qc);
+      load_row(dO + (size_t)r * kD, oc);
+      const float li = lse[r], di = delta[r];
+      const float s = dot_row(qc, kvec);
+      const float dp = dot_row(oc, vvec);
+      const bool on = i >= 0 && li != kNegInf;
+      const float p = on ? __expf(s * a.scale - li) : 0.f;
+      axpy_row(av, p, oc);
+      axpy_row(ak, p * (dp - di), qc);
+    }
+  };
+  const bf16* Qs = static_cast<const bf16*>(a.q) + hoff;
+  zero();
+  {
+    const int32_t u0 = a.causal ? 0 : -min(R, j / d);
+    const int32_t u1 = min(R, (N - 1 - j) / d);
+    sweep(u1 - u0 + 1, Qs, vk[wv], vv[wv], [&](int32_t x) {
+      const int32_t i = j + (u0 + x) * d;
+      return a.gflag[i] ? -1 : i;
+    });
+  }
+  if (jg) {
+    const int32_t i0 = a.causal ? j : 0;
+    sweep(N - i0, Qs, vk[wv], vv[wv], [&](int32_t x) {
+      const int32_t i = i0 + x;
+      return (in_band(i, j, R, d, a.causal) || a.gflag[i]) ? -1 : i;
+    });
+  }
+  auto grow = [&](int32_t x) {
+    const int32_t i = a.gidx[x];
+    return (i < 0 || i >= N || (a.causal && i < j)) ? -1 : i;
+  };
+  if (!a.sep) sweep(a.n_global, Qs, vk[wv], vv[wv], grow);
+  a.dk[hoff + (size_t)j * kD + lane] = lane_totals(ak, lane) * a.scale;
+  a.dv[hoff + (size_t)j * kD + lane] = lane_totals(av, lane);
+  if (a.sep) {
+    zero();
+    sweep(a.n_global, static_cast<const bf16*>(a.qg) + hoff, vkg[wv], vvg[wv], grow);
+    a.dkg[hoff + (size_t)j * kD + lane] = lane_totals(ak, lane) * a.scale;
+    a.dvg[hoff + (size_t)j * kD + lane] = lane_totals(av, lane);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) {
@@ -252,8 +476,8 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) 
   const dim3 g((uint32_t)((rows + kWavesBwd - 1) / kWavesBwd)), blk(64 * kWavesBwd);
   hipLaunchKernelGGL(bwd_flags_kernel, dim3((uint32_t)((a.N + 255) / 256)), dim3(256), 0, stream, a);
   if (dtype == 1) {
-    hipLaunchKernelGGL(bwd_dq_kernel<bf16>, g, blk, 0, stream, a);
-    hipLaunchKernelGGL(bwd_dkv_kernel<bf16>, g, blk, 0, stream, a);
+    hipLaunchKernelGGL(bwd_dq_rows_kernel, g, blk, 0, stream, a);
+    hipLaunchKernelGGL(bwd_dkv_rows_kernel, g, blk, 0, stream, a);
   } else {
     hipLaunchKernelGGL(bwd_dq_kernel<float>, g, blk, 0, stream, a);
     hipLaunchKernelGGL(bwd_dkv_kernel<float>, g, blk, 0, stream, a);
