@@ -286,12 +286,16 @@ __device__ __forceinline__ float dot_row(const uint4 (&c)[8], const float* y) {
   return s;
 }
 
-// acc += w * row (row packed in chunks)
+// acc += w * row (row packed in chunks). The chunk is unpacked again here
+// (an opaque copy of its words) rather than kept unpacked from the dot
+// product, which would hold 64 more registers per row.
 __device__ __forceinline__ void axpy_row(float (&acc)[kD], float w, const uint4 (&c)[8]) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
+    uint4 u = c[k];
+    asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
     float f[8];
-    unpack8(c[k], f);
+    unpack8(u, f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[8 * k + e] += w * f[e];
   }
@@ -411,14 +415,13 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_rows_kernel(BwdArgs a)
   const int32_t sj = segb ? segb[j] : 0;
   const int32_t d = a.dil[h], R = a.radius;
   const bool jg = a.gflag[j] != 0;
-  float ak[kD], av[kD];
-  auto zero = [&]() {
-#pragma unroll
-    for (int e = 0; e < kD; ++e) ak[e] = av[e] = 0.f;
-  };
+  // Two passes over the same rows, one accumulator live at a time: dV (needs
+  // s only) and then dK (needs s and dP).
+  float acc[kD];
   // rows row_of(x), x in [0, n) (-1: skip), one per lane, through projection Q
   // against key vectors (kvec, vvec); a skipped lane reads row j and gets weight 0
-  auto sweep = [&](int32_t n, const bf16* Q, const float* kvec, const float* vvec, auto row_of) {
+  auto sweep = [&](bool dk_pass, int32_t n, const bf16* Q, const float* kvec, const float* vvec,
+                   auto row_of) __attribute__((always_inline)) {
     for (int32_t x0 = 0; x0 < n; x0 += 64) {
       const int32_t x = x0 + lane;
       int32_t i = x < n ? row_of(x) : -1;
@@ -427,44 +430,56 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_rows_kernel(BwdArgs a)
       uint4 qc[8], oc[8];
       load_row(Q + (size_t)r * kD, qc);
       load_row(dO + (size_t)r * kD, oc);
-      const float li = lse[r], di = delta[r];
-      const float s = dot_row(qc, kvec);
-      const float dp = dot_row(oc, vvec);
+      const float li = lse[r];
+      const float sc = dot_row(qc, kvec);
       const bool on = i >= 0 && li != kNegInf;
-      const float p = on ? __expf(s * a.scale - li) : 0.f;
-      axpy_row(av, p, oc);
-      axpy_row(ak, p * (dp - di), qc);
+      const float p = on ? __expf(sc * a.scale - li) : 0.f;
+      if (dk_pass) {
+        const float dp = dot_row(oc, vvec);
+        axpy_row(acc, p * (dp - delta[r]), qc);
+      } else {
+        axpy_row(acc, p, oc);
+      }
     }
   };
   const bf16* Qs = static_cast<const bf16*>(a.q) + hoff;
-  zero();
-  {
-    const int32_t u0 = a.causal ? 0 : -min(R, j / d);
-    const int32_t u1 = min(R, (N - 1 - j) / d);
-    sweep(u1 - u0 + 1, Qs, vk[wv], vv[wv], [&](int32_t x) {
-      const int32_t i = j + (u0 + x) * d;
-      return a.gflag[i] ? -1 : i;
-    });
-  }
-  if (jg) {
-    const int32_t i0 = a.causal ? j : 0;
-    sweep(N - i0, Qs, vk[wv], vv[wv], [&](int32_t x) {
-      const int32_t i = i0 + x;
-      return (in_band(i, j, R, d, a.causal) || a.gflag[i]) ? -1 : i;
-    });
-  }
   auto grow = [&](int32_t x) {
     const int32_t i = a.gidx[x];
     return (i < 0 || i >= N || (a.causal && i < j)) ? -1 : i;
   };
-  if (!a.sep) sweep(a.n_global, Qs, vk[wv], vv[wv], grow);
-  a.dk[hoff + (size_t)j * kD + lane] = lane_totals(ak, lane) * a.scale;
-  a.dv[hoff + (size_t)j * kD + lane] = lane_totals(av, lane);
-  if (a.sep) {
-    zero();
-    sweep(a.n_global, static_cast<const bf16*>(a.qg) + hoff, vkg[wv], vvg[wv], grow);
-    a.dkg[hoff + (size_t)j * kD + lane] = lane_totals(ak, lane) * a.scale;
-    a.dvg[hoff + (size_t)j * kD + lane] = lane_totals(av, lane);
+  // every row that reaches key j through the shared projections
+  auto shared_rows = [&](bool dk_pass) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < kD; ++e) acc[e] = 0.f;
+    const int32_t u0 = a.causal ? 0 : -min(R, j / d);
+    const int32_t u1 = min(R, (N - 1 - j) / d);
+    sweep(dk_pass, u1 - u0 + 1, Qs, vk[wv], vv[wv], [&](int32_t x) {
+      const int32_t i = j + (u0 + x) * d;
+      return a.gflag[i] ? -1 : i;
+    });
+    if (jg) {
+      const int32_t i0 = a.causal ? j : 0;
+      sweep(dk_pass, N - i0, Qs, vk[wv], vv[wv], [&](int32_t x) {
+        const int32_t i = i0 + x;
+        return (in_band(i, j, R, d, a.causal) || a.gflag[i]) ? -1 : i;
+      });
+    }
+    if (!a.sep) sweep(dk_pass, a.n_global, Qs, vk[wv], vv[wv], grow);
+  };
+  shared_rows(false);
+  a.dv[hoff + (size_t)j * kD + lane] = lane_totals(acc, lane);
+  shared_rows(true);
+  a.dk[hoff + (size_t)j * kD + lane] = lane_totals(acc, lane) * a.scale;
+  if (a.sep) {  // the global rows, through qg_i, kg_j, vg_j
+    const bf16* Qg = static_cast<const bf16*>(a.qg) + hoff;
+#pragma unroll
+    for (int e = 0; e < kD; ++e) acc[e] = 0.f;
+    sweep(false, a.n_global, Qg, vkg[wv], vvg[wv], grow);
+    a.dvg[hoff + (size_t)j * kD + lane] = lane_totals(acc, lane);
+#pragma unroll
+    for (int e = 0; e < kD; ++e) acc[e] = 0.f;
+    sweep(true, a.n_global, Qg, vkg[wv], vvg[wv], grow);
+    a.dkg[hoff + (size_t)j * kD + lane] = lane_totals(acc, lane) * a.scale;
   }
 }
 
