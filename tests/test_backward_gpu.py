@@ -125,3 +125,43 @@ def test_backward_longformer_base(dev):
     run_case(dev, "longformer-base", "bf16", w.B, w.H, w.N, w.global_idx, w.radius, None,
              w.causal, True, None, seed=w.seed,
              inputs=(inp.q, inp.k, inp.v, inp.qg, inp.kg, inp.vg))
+
+
+def test_backward_graph_replay(dev):
+    """The backward call captured in a HIP graph (it writes its whole workspace
+    with kernels, no memset) and replayed, with eager work between replays:
+    every replay equals the eager result bit for bit."""
+    gen = torch.Generator().manual_seed(31)
+    B, H, N = 1, 2, 320
+    q, k, v, dout = (rand(gen, (B, H, N, 64), "bf16").to(dev) for _ in range(4))
+    g = torch.tensor([0, 7, 200], dtype=torch.int32, device=dev)
+    out, lse = la.la_attn_forward(q, k, v, g, 24, [1, 2], True)
+    call = la.bind_attn_backward(q, k, v, out, lse, dout, g, 24, [1, 2], True)
+    call()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in call.grads]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call_s = la.bind_attn_backward(q, k, v, out, lse, dout, g, 24, [1, 2], True, stream=s)
+        call_s()  # warm-up on the capture stream
+        s.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            call_s()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for t in call_s.grads:
+            t.fill_(float("nan"))
+        la.la_attn_forward(k, q, v, g, 8)  # unrelated eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(call_s.grads, eager):
+            assert torch.equal(x, y), f"replay {rep} differs"
+
+
+def test_backward_empty_batch(dev):
+    q = torch.empty(0, 2, 64, 64, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(0, 2, 64, dtype=torch.float32, device=dev)
+    grads = la.la_attn_backward(q, q, q, q, lse, q, None, 4)
+    assert len(grads) == 3 and all(t.numel() == 0 for t in grads)
