@@ -211,6 +211,19 @@ class BoundCall:
         return self.out, self.lse
 
 
+class BoundBackward(BoundCall):
+    """A marshalled :func:`la_attn_backward` call; calling it re-issues the call
+    and returns its gradient tensors (``grads``), which every call overwrites."""
+
+    def __init__(self, fn, args, keep, grads):
+        super().__init__(fn, args, keep, None, None)
+        self.grads = grads
+
+    def __call__(self) -> Tuple[torch.Tensor, ...]:
+        super().__call__()
+        return self.grads
+
+
 def bind_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
               global_idx: Optional[torch.Tensor] = None, radius: int = 0,
               dilation: Optional[Sequence[int]] = None, causal: bool = False,
@@ -398,7 +411,7 @@ def bind_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
                        dilation: Optional[Sequence[int]] = None, causal: bool = False,
                        qg: Optional[torch.Tensor] = None, kg: Optional[torch.Tensor] = None,
                        vg: Optional[torch.Tensor] = None, seg_ids: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None, stream=None) -> BoundCall:
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> BoundBackward:
     """Validate and marshal a :func:`la_attn_backward` call without issuing it.
 
     ``out`` and ``lse`` are the forward's outputs for the same arguments and
@@ -442,9 +455,7 @@ def bind_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
             grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(), _stream(q, stream),
             ctypes.byref(ext))
     keep = (dims, ext, dil, q, k, v, out, lse, dout, global_idx, seg_ids, qg, kg, vg, ws)
-    call = BoundCall(lib().la_attn_backward, args, keep, None, None)
-    call.grads = tuple(grads)
-    return call
+    return BoundBackward(lib().la_attn_backward, args, keep, tuple(grads))
 
 
 def la_attn_backward(q, k, v, out, lse, dout, global_idx=None, radius: int = 0, dilation=None,
@@ -452,10 +463,8 @@ def la_attn_backward(q, k, v, out, lse, dout, global_idx=None, radius: int = 0, 
                      workspace=None, stream=None):
     """One backward call; returns fp32 ``(dq, dk, dv)`` or, with separate global
     projections, ``(dq, dk, dv, dqg, dkg, dvg)``."""
-    call = bind_attn_backward(q, k, v, out, lse, dout, global_idx, radius, dilation, causal,
-                              qg, kg, vg, seg_ids, workspace, stream)
-    call()
-    return call.grads
+    return bind_attn_backward(q, k, v, out, lse, dout, global_idx, radius, dilation, causal,
+                              qg, kg, vg, seg_ids, workspace, stream)()
 
 
 def la_check_global_idx(global_idx: torch.Tensor, N: int, stream=None) -> bool:
