@@ -89,6 +89,9 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.lo_longnet_mixture_rows.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 3 + [
         _i32p, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int64, _f64p, _f64p,
         _f64p, _f64p, ctypes.c_int32]
+    lib.lo_longnet_backward.restype = ctypes.c_int32
+    lib.lo_longnet_backward.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 3 + [
+        _i32p, _i32p, ctypes.c_int32, ctypes.c_int32] + [_f64p] * 4 + [ctypes.c_int32]
     lib.lo_attn_backward.restype = ctypes.c_int32
     lib.lo_attn_backward.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 6 + [
         _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p] + [_f64p] * 7 + [
@@ -248,6 +251,21 @@ def attn_backward(q, k, v, dout, global_idx=(), radius: int = 0, dilation=None,
                               _p(do, _f64p), *ptr, n_threads)
     if rc != 0:
         raise ValueError("lo_attn_backward rejected its arguments")
+    return tuple(grads)
+
+
+def longnet_backward(q, k, v, dout, pairs, causal: bool = True, n_threads: int = 0, lib=None):
+    """Gradients ``(dq, dk, dv)`` of the LongNet mixture in fp64 (``[B,H,N,D]``)."""
+    lib = lib or load()
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, D = q.shape
+    w, r = _pairs(pairs)
+    grads = [np.zeros_like(q) for _ in range(3)]
+    rc = lib.lo_longnet_backward(B, H, N, D, _p(q, _f64p), _p(k, _f64p), _p(v, _f64p),
+                                 _p(w, _i32p), _p(r, _i32p), w.shape[0], int(causal),
+                                 _p(do, _f64p), *[_p(x, _f64p) for x in grads], n_threads)
+    if rc != 0:
+        raise ValueError("lo_longnet_backward rejected its arguments")
     return tuple(grads)
 
 

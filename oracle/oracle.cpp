@@ -397,6 +397,70 @@ int32_t lo_attn_backward(int32_t B, int32_t H, int32_t N, int32_t D, const doubl
   return 0;
 }
 
+// Backward of the LongNet mixture, fp64. By the mixture's equivalence (one
+// softmax over the multiset of the patterns' keys, "Mixture of Dilated
+// Attentions"), P_ij = c_ij exp(s_ij) / Z_i with c the integer multiplicity of
+// longnet_mult, and the gradients follow the same chain rule as
+// lo_attn_backward. A row no pattern covers has no gradient.
+int32_t lo_longnet_backward(int32_t B, int32_t H, int32_t N, int32_t D, const double* q,
+                            const double* k, const double* v, const int32_t* w, const int32_t* r,
+                            int32_t n_pairs, int32_t causal, const double* dout, double* dq,
+                            double* dk, double* dv, int32_t n_threads) {
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || n_pairs < 1 || !q || !k || !v || !dout || !dq ||
+      !dk || !dv)
+    return -1;
+  for (int32_t p = 0; p < n_pairs; ++p)
+    if (w[p] < 1 || r[p] < 1) return -1;
+  const double scale = 1.0 / std::sqrt((double)D);
+  const size_t head_elems = (size_t)N * D;
+  parallel_rows((int64_t)B * H, n_threads, [&](int64_t bh) {
+    const int32_t h = (int32_t)(bh % H);
+    const size_t off = (size_t)bh * head_elems;
+    for (double* o : {dq, dk, dv}) std::fill(o + off, o + off + head_elems, 0.0);
+    std::vector<double> P(N), dP(N);
+    for (int32_t i = 0; i < N; ++i) {
+      const double* qi = q + off + (size_t)i * D;
+      const double* doi = dout + off + (size_t)i * D;
+      double M = -std::numeric_limits<double>::infinity();
+      for (int32_t j = 0; j < N; ++j) {
+        const int32_t c = longnet_mult(i, j, h, w, r, n_pairs, causal);
+        P[j] = c;  // the multiplicity for now
+        if (c == 0) continue;
+        double dot = 0.0;
+        for (int32_t d = 0; d < D; ++d) dot += qi[d] * k[off + (size_t)j * D + d];
+        dP[j] = dot * scale;  // the logit for now
+        M = std::max(M, dP[j]);
+      }
+      if (M == -std::numeric_limits<double>::infinity()) continue;
+      double Z = 0.0;
+      for (int32_t j = 0; j < N; ++j) {
+        if (P[j] == 0.0) continue;
+        P[j] *= std::exp(dP[j] - M);
+        Z += P[j];
+      }
+      double Di = 0.0;
+      for (int32_t j = 0; j < N; ++j) {
+        if (P[j] == 0.0) continue;
+        P[j] /= Z;
+        double dot = 0.0;
+        for (int32_t d = 0; d < D; ++d) dot += doi[d] * v[off + (size_t)j * D + d];
+        dP[j] = dot;
+        Di += P[j] * dot;
+      }
+      for (int32_t j = 0; j < N; ++j) {
+        if (P[j] == 0.0) continue;
+        const double g = P[j] * (dP[j] - Di);
+        for (int32_t d = 0; d < D; ++d) {
+          dv[off + (size_t)j * D + d] += P[j] * doi[d];
+          dq[off + (size_t)i * D + d] += g * k[off + (size_t)j * D + d] * scale;
+          dk[off + (size_t)j * D + d] += g * qi[d] * scale;
+        }
+      }
+    }
+  });
+  return 0;
+}
+
 // Sparse Transformer fixed pattern, fp64: masked dense softmax over
 // fixed_allows. q, k, v: [B,H,N,D]; sel as in lo_attn_rows.
 int32_t lo_fixed_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q, const double* k,

@@ -695,6 +695,41 @@ def pin_backward_shift_invariants(lib):
     assert (dqg[:, :, ~isg] == 0).all() and (dq[:, :, isg] == 0).all()
 
 
+def pin_longnet_backward(lib):
+    """The LongNet mixture's backward against central differences of its forward
+    loss (overlapping patterns, so some keys count twice); a single (N, 1)
+    pattern against torch float64 autograd of dense causal attention; the
+    keys' gradients summing to 0 per head."""
+    rng = np.random.default_rng(24)
+    B, H, N, D = 1, 3, 24, 4
+    q, k, v = rand_qkv(rng, B, H, N, D)
+    dout = rng.standard_normal(q.shape)
+    pairs = [(8, 1), (16, 2), (24, 3)]
+    for causal in (True, False):
+        dq, dk, dv = oracle.longnet_backward(q, k, v, dout, pairs, causal, lib=lib)
+        assert np.allclose(dk.sum(2), 0, atol=1e-12)
+        for t, g in ((q, dq), (k, dk), (v, dv)):
+            for _ in range(6):
+                x = tuple(rng.integers(0, n) for n in t.shape)
+                old = t[x]
+                t[x] = old + 1e-6
+                lp = float((oracle.longnet_rows(q, k, v, pairs, causal, lib=lib)[0] * dout).sum())
+                t[x] = old - 1e-6
+                lm = float((oracle.longnet_rows(q, k, v, pairs, causal, lib=lib)[0] * dout).sum())
+                t[x] = old
+                fd = (lp - lm) / 2e-6
+                assert abs(fd - g[x]) <= 1e-6 * (1 + abs(fd)), (causal, x, fd, g[x])
+    q, k, v = rand_qkv(rng, 1, 2, 16, 8)
+    dout = rng.standard_normal(q.shape)
+    grads = oracle.longnet_backward(q, k, v, dout, [(16, 1)], True, lib=lib)
+    t = [torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v)]
+    sc = (t[0] @ t[1].transpose(-1, -2) / math.sqrt(8)).masked_fill(
+        torch.ones(16, 16, dtype=torch.bool).triu(1), float("-inf"))
+    (torch.softmax(sc, -1) @ t[2]).backward(torch.from_numpy(dout))
+    for a_, b_ in zip(grads, t):
+        assert np.allclose(a_, b_.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
 PINS = [pin_mask_matches_enumeration, pin_counts_closed_form, pin_counts_full_workloads,
         pin_longnet_counts, pin_longnet_worked_example, pin_longnet_offsets_partition,
         pin_dense_special_cases, pin_global_rows_are_full_rows, pin_brute_force_band,
@@ -703,7 +738,7 @@ PINS = [pin_mask_matches_enumeration, pin_counts_closed_form, pin_counts_full_wo
         pin_longnet_paths_agree,
         pin_rows_sum_to_one, pin_uncovered_rows, pin_sampled_rows_match_full,
         pin_backward_finite_differences, pin_backward_dense_autograd,
-        pin_backward_shift_invariants]
+        pin_backward_shift_invariants, pin_longnet_backward]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -758,6 +793,8 @@ MUTANTS = [
      "dvb[(size_t)j * D + d] += dS * doi[d];"),
     ("backward-global-keys-to-shared", "double* dkb = (sep ? dkg : dk) + off;",
      "double* dkb = dk + off;"),
+    ("longnet-backward-multiplicity-one", "P[j] = c;  // the multiplicity for now",
+     "P[j] = c ? 1 : 0;  // the multiplicity for now"),
 ]
 
 
