@@ -206,6 +206,26 @@ la_status la_attn_backward(const la_dims *dims, const void *q, const void *k, co
  * row and one global-flag byte per position, each part padded to 256 bytes. */
 size_t la_attn_backward_workspace_size(const la_dims *dims);
 
+/* Backward of la_dilated_forward (bf16 only). The mixture is one softmax over
+ * the multiset of the patterns' keys (LongNet page, §3.4 "Mixture of Dilated
+ * Attentions"), so with c_ij the number of patterns that pair i with j and lse
+ * the forward's (mixture) lse, P_ij = c_ij exp(q_i.k_j / sqrt(D) - lse_i), and
+ * the gradients follow the formulas of la_attn_backward.
+ *  q, k, v, seg_lens, dil_rates, n_pairs, causal: as given to the forward.
+ *  out, lse     the forward's output and its ext->lse (fp32 [B,H,N], required).
+ *  dout         device bf16 [B,H,N,D]: the loss gradient w.r.t. out.
+ *  dq, dk, dv   device fp32 [B,H,N,D] outputs (fully written; must not alias inputs).
+ *  workspace    la_dilated_backward_workspace_size() bytes, 256-byte aligned.
+ * Errors as for la_dilated_forward. Two launches on `stream`, no allocation. */
+la_status la_dilated_backward(const la_dims *dims, const void *q, const void *k, const void *v,
+                              const int32_t *seg_lens, const int32_t *dil_rates, int32_t n_pairs,
+                              int32_t causal, const void *out, const float *lse,
+                              const void *dout, float *dq, float *dk, float *dv,
+                              hipStream_t stream, void *workspace, size_t workspace_bytes);
+
+/* Bytes of workspace la_dilated_backward needs (0 for invalid dims): fp32 D_i per row. */
+size_t la_dilated_backward_workspace_size(const la_dims *dims);
+
 /* Bytes of workspace la_attn_forward needs for these dims and n_global
  * (0 when n_global == 0). has_separate_global is accepted for symmetry and
  * does not change the size. Returns 0 for invalid dims. */

@@ -75,7 +75,8 @@ _lib: Optional[ctypes.CDLL] = None
 # Every symbol include/longattn.h declares.
 EXPORTS = ("la_attn_forward", "la_dilated_forward", "la_fixed_forward", "la_attn_workspace_size",
            "la_dilated_workspace_size", "la_fixed_workspace_size", "la_check_global_idx",
-           "la_last_error", "la_version", "la_attn_backward", "la_attn_backward_workspace_size")
+           "la_last_error", "la_version", "la_attn_backward", "la_attn_backward_workspace_size",
+           "la_dilated_backward", "la_dilated_backward_workspace_size")
 
 
 def lib() -> ctypes.CDLL:
@@ -115,6 +116,13 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_void_p, ctypes.POINTER(LaAttnBwdExt)]
     L.la_attn_backward_workspace_size.restype = ctypes.c_size_t
     L.la_attn_backward_workspace_size.argtypes = [ctypes.POINTER(LaDims)]
+    L.la_dilated_backward.restype = ctypes.c_int32
+    L.la_dilated_backward.argtypes = [ctypes.POINTER(LaDims), ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, _i32p, _i32p, ctypes.c_int32,
+                                      ctypes.c_int32] + [ctypes.c_void_p] * 6 + [
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
+    L.la_dilated_backward_workspace_size.restype = ctypes.c_size_t
+    L.la_dilated_backward_workspace_size.argtypes = [ctypes.POINTER(LaDims)]
     L.la_check_global_idx.restype = ctypes.c_int32
     L.la_check_global_idx.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p]
@@ -465,6 +473,42 @@ def la_attn_backward(q, k, v, out, lse, dout, global_idx=None, radius: int = 0, 
     projections, ``(dq, dk, dv, dqg, dkg, dvg)``."""
     return bind_attn_backward(q, k, v, out, lse, dout, global_idx, radius, dilation, causal,
                               qg, kg, vg, seg_ids, workspace, stream)()
+
+
+def la_dilated_backward_workspace_size(dims: LaDims) -> int:
+    return int(lib().la_dilated_backward_workspace_size(ctypes.byref(dims)))
+
+
+def bind_dilated_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                          lse: torch.Tensor, dout: torch.Tensor, seg_lens: Sequence[int],
+                          dil_rates: Sequence[int], causal: bool = True,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> BoundBackward:
+    """Validate and marshal a :func:`la_dilated_backward` call; calling the
+    result returns fp32 ``(dq, dk, dv)``. ``out`` and ``lse`` are the forward's."""
+    dims = _dims(q)
+    ptrs = [_dev(t, q, name) for name, t in (("q", q), ("k", k), ("v", v), ("out", out),
+                                             ("dout", dout))]
+    if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() \
+            or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise LaError(LA_EINVAL, "lse must be a contiguous device fp32 [B, H, N] tensor")
+    if len(seg_lens) != len(dil_rates):
+        raise LaError(LA_EINVAL, "seg_lens and dil_rates differ in length")
+    w, r = _host_i32(seg_lens), _host_i32(dil_rates)
+    grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    ws = _workspace(la_dilated_backward_workspace_size(dims), q.device, workspace)
+    args = (ctypes.byref(dims), ptrs[0], ptrs[1], ptrs[2], w, r, len(seg_lens), int(bool(causal)),
+            ptrs[3], lse.data_ptr(), ptrs[4], grads[0].data_ptr(), grads[1].data_ptr(),
+            grads[2].data_ptr(), _stream(q, stream), ws.data_ptr() if ws is not None else None,
+            ws.numel() if ws is not None else 0)
+    keep = (dims, w, r, q, k, v, out, lse, dout, ws)
+    return BoundBackward(lib().la_dilated_backward, args, keep, grads)
+
+
+def la_dilated_backward(q, k, v, out, lse, dout, seg_lens, dil_rates, causal: bool = True,
+                        workspace=None, stream=None):
+    """One LongNet backward call; returns fp32 ``(dq, dk, dv)``."""
+    return bind_dilated_backward(q, k, v, out, lse, dout, seg_lens, dil_rates, causal, workspace,
+                                 stream)()
 
 
 def la_check_global_idx(global_idx: torch.Tensor, N: int, stream=None) -> bool:

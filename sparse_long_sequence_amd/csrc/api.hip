@@ -442,6 +442,61 @@ la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, co
   return LA_OK;
 }
 
+size_t la_dilated_backward_workspace_size(const la_dims* dims) {
+  if (check_dims(dims, true) != LA_OK) return 0;
+  return align_up((size_t)dims->B * dims->H * dims->N * sizeof(float));
+}
+
+la_status la_dilated_backward(const la_dims* dims, const void* q, const void* k, const void* v,
+                              const int32_t* seg_lens, const int32_t* dil_rates, int32_t n_pairs,
+                              int32_t causal, const void* out, const float* lse, const void* dout,
+                              float* dq, float* dk, float* dv, hipStream_t stream, void* workspace,
+                              size_t workspace_bytes) {
+  la_status st = check_dims(dims, true);
+  if (st != LA_OK) return st;
+  if (is_empty(dims)) return LA_OK;
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv)
+    return fail(LA_EINVAL, "q, k, v, out, lse, dout, dq, dk and dv are required");
+  const void* ptrs[] = {q, k, v, out, lse, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(LA_EINVAL, "tensors must be 16-byte aligned");
+  if (!seg_lens || !dil_rates || n_pairs < 1)
+    return fail(LA_EINVAL, "seg_lens, dil_rates and n_pairs >= 1 are required");
+  if (n_pairs > la::kMaxPairs) return fail(LA_EUNSUPPORTED, "more than 16 patterns");
+  if (causal != 0 && causal != 1) return fail(LA_EINVAL, "causal must be 0 or 1");
+  la::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int32_t p = 0; p < n_pairs; ++p) {
+    if (seg_lens[p] < 1 || dil_rates[p] < 1)
+      return fail(LA_EINVAL, "segment lengths and dilation rates must be >= 1");
+    a.pw[p] = seg_lens[p];
+    a.pr[p] = dil_rates[p];
+  }
+  if (!workspace || workspace_bytes < la_dilated_backward_workspace_size(dims))
+    return fail(LA_EINVAL, "workspace missing or smaller than la_dilated_backward_workspace_size()");
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return fail(LA_EINVAL, "workspace must be 256-byte aligned");
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = reinterpret_cast<float*>(workspace);
+  a.B = dims->B;
+  a.H = dims->H;
+  a.N = dims->N;
+  a.causal = causal;
+  a.n_pairs = n_pairs;
+  a.scale = (float)(1.0 / sqrt((double)kDHead));
+  hipError_t e = la::launch_dilated_bwd(a, stream);
+  if (e != hipSuccess) return fail(LA_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(e));
+  return LA_OK;
+}
+
 la_status la_check_global_idx(const int32_t* global_idx, int32_t n_global, int32_t N,
                               hipStream_t stream) {
   if (n_global < 0 || n_global > N) return fail(LA_EINVAL, "n_global must be in [0, N]");

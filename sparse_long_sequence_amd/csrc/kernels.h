@@ -85,10 +85,14 @@ struct BwdArgs {
   int32_t n_global, B, H, N, radius, causal, sep;
   int32_t dil[kMaxHeadsDil];
   float scale;
+  // LongNet mixture (launch_dilated_bwd only): patterns (w, r)
+  int32_t n_pairs;
+  int32_t pw[kMaxPairs], pr[kMaxPairs];
 };
 
 hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream);
 hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream);
+hipError_t launch_dilated_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dilated(const DilArgs& a, hipStream_t stream);
 int32_t host_band_tiles_of_head(int32_t N, int32_t d, int32_t tq);
 int32_t host_query_tile(int32_t dtype);  // query rows per workgroup

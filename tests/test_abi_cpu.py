@@ -153,6 +153,28 @@ def test_backward_argument_errors(L):
     assert call(dims=LaDims(0, 2, 128, 64, la.LA_BF16), e=None) == la.LA_OK  # empty: no-op
 
 
+def test_dilated_backward_argument_errors(L):
+    d = LaDims(1, 2, 256, 64, la.LA_BF16)
+    need = la.la_dilated_backward_workspace_size(d)
+    assert need == 1 * 2 * 256 * 4                          # D_i per row, 256-byte multiple
+    w = (ctypes.c_int32 * 2)(64, 128)
+    r = (ctypes.c_int32 * 2)(1, 2)
+
+    def call(dims=d, w=w, r=r, n=2, causal=1, lse=FAKE, ws=FAKE, nbytes=need):
+        return L.la_dilated_backward(ctypes.byref(dims), FAKE, FAKE, FAKE, w, r, n, causal, FAKE,
+                                     lse, FAKE, FAKE, FAKE, FAKE, None, ws, nbytes)
+    assert call(dims=LaDims(1, 2, 256, 64, la.LA_F32)) == la.LA_EUNSUPPORTED
+    assert call(n=0) == la.LA_EINVAL
+    assert call(r=(ctypes.c_int32 * 2)(1, 0)) == la.LA_EINVAL
+    big = (ctypes.c_int32 * 17)(*([64] * 17))
+    assert call(w=big, r=(ctypes.c_int32 * 17)(*([1] * 17)), n=17) == la.LA_EUNSUPPORTED
+    assert call(causal=2) == la.LA_EINVAL
+    assert call(lse=None) == la.LA_EINVAL
+    assert call(ws=None) == la.LA_EINVAL
+    assert call(nbytes=need - 1) == la.LA_EINVAL
+    assert call(dims=LaDims(0, 2, 256, 64, la.LA_BF16), ws=None) == la.LA_OK  # empty: no-op
+
+
 def test_workspace_sizes(L):
     d = LaDims(2, 12, 4096, 64, la.LA_BF16)
     assert la.la_attn_workspace_size(d, 0) == 0

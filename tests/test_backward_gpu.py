@@ -165,3 +165,29 @@ def test_backward_empty_batch(dev):
     lse = torch.empty(0, 2, 64, dtype=torch.float32, device=dev)
     grads = la.la_attn_backward(q, q, q, q, lse, q, None, 4)
     assert len(grads) == 3 and all(t.numel() == 0 for t in grads)
+
+
+LONGNET_CASES = [
+    # tag, B, H, N, pairs, causal
+    ("causal", 1, 4, 512, ((128, 1), (256, 2), (512, 4)), True),
+    ("non-causal", 2, 3, 384, ((64, 1), (192, 3)), False),
+    ("ragged-last-segment", 1, 6, 600, ((256, 1), (512, 2), (600, 6)), True),
+    ("n4096", 1, 2, 4096, ((1024, 1), (2048, 2), (4096, 4)), True),
+]
+
+
+@pytest.mark.parametrize("case", LONGNET_CASES, ids=[c[0] for c in LONGNET_CASES])
+def test_backward_longnet(dev, case):
+    """The LongNet mixture's backward against the oracle's multiplicity-weighted
+    chain rule; the forward supplies out and its mixture lse."""
+    tag, B, H, N, pairs, causal = case
+    say(f"longnet backward {tag}: B={B} H={H} N={N} pairs={pairs} causal={causal}")
+    gen = torch.Generator().manual_seed(400 + LONGNET_CASES.index(case))
+    q, k, v, dout = (rand(gen, (B, H, N, 64), "bf16") for _ in range(4))
+    d = lambda t: t.to(dev).contiguous()
+    w, r = [p[0] for p in pairs], [p[1] for p in pairs]
+    out, lse = la.la_dilated_forward(d(q), d(k), d(v), w, r, causal)
+    grads = la.la_dilated_backward(d(q), d(k), d(v), out, lse, d(dout), w, r, causal)
+    torch.cuda.synchronize()
+    ref = oracle.longnet_backward(to64(q), to64(k), to64(v), to64(dout), pairs, causal)
+    check(f"longnet-{tag}", "bf16", grads, ref)
