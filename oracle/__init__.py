@@ -19,6 +19,8 @@ Functions and the passages they follow (details in ``oracle.cpp``):
 * :func:`longnet_mixture_rows` — the same mixture in the page's own order:
   sparsify, attend, scatter, weight by softmax denominators (Eqs. 3-10, 13-15).
 * :func:`longnet_mult_rows` — the integer key multiplicity rows.
+* :func:`longnet_backward_sel` — the LongNet mixture's gradients for chosen
+  rows (dq) and keys (dk, dv), each row evaluated in full by the definition.
 * :func:`fixed_rows` — Sparse Transformer's fixed pattern (local block plus
   strided summary positions; LongNet page §3.4 "Standard Self-Attention and
   Sparse Attention (Preliminaries)"), masked dense softmax.
@@ -92,6 +94,10 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.lo_longnet_backward.restype = ctypes.c_int32
     lib.lo_longnet_backward.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 3 + [
         _i32p, _i32p, ctypes.c_int32, ctypes.c_int32] + [_f64p] * 4 + [ctypes.c_int32]
+    lib.lo_longnet_backward_sel.restype = ctypes.c_int32
+    lib.lo_longnet_backward_sel.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 3 + [
+        _i32p, _i32p, ctypes.c_int32, ctypes.c_int32, _f64p, _i32p, ctypes.c_int64, _f64p,
+        _i32p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int32]
     lib.lo_attn_backward.restype = ctypes.c_int32
     lib.lo_attn_backward.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 6 + [
         _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p] + [_f64p] * 7 + [
@@ -267,6 +273,30 @@ def longnet_backward(q, k, v, dout, pairs, causal: bool = True, n_threads: int =
     if rc != 0:
         raise ValueError("lo_longnet_backward rejected its arguments")
     return tuple(grads)
+
+
+def longnet_backward_sel(q, k, v, dout, pairs, causal: bool = True, rows=None, keys=None,
+                         n_threads: int = 0, lib=None):
+    """Chosen LongNet mixture gradients in fp64: ``dq`` of the ``rows`` and ``dk``,
+    ``dv`` of the ``keys`` (each an ``[n, 3]`` array of (b, h, position)),
+    every row involved evaluated in full. Returns ``(dq [n_rows, D],
+    dk [n_keys, D], dv [n_keys, D])``."""
+    lib = lib or load()
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, D = q.shape
+    w, r = _pairs(pairs)
+    rs, nr = _sel(np.zeros((0, 3)) if rows is None else rows, B, H, N)
+    ks, nk = _sel(np.zeros((0, 3)) if keys is None else keys, B, H, N)
+    dq = np.zeros((nr, D))
+    dk = np.zeros((nk, D))
+    dv = np.zeros((nk, D))
+    rc = lib.lo_longnet_backward_sel(B, H, N, D, _p(q, _f64p), _p(k, _f64p), _p(v, _f64p),
+                                     _p(w, _i32p), _p(r, _i32p), w.shape[0], int(causal),
+                                     _p(do, _f64p), _p(rs, _i32p), nr, _p(dq, _f64p),
+                                     _p(ks, _i32p), nk, _p(dk, _f64p), _p(dv, _f64p), n_threads)
+    if rc != 0:
+        raise ValueError("lo_longnet_backward_sel rejected its arguments")
+    return dq, dk, dv
 
 
 def fixed_rows(q, k, v, block_len: int, summary_len: int, causal: bool = True, sel=None,

@@ -461,6 +461,120 @@ int32_t lo_longnet_backward(int32_t B, int32_t H, int32_t N, int32_t D, const do
   return 0;
 }
 
+}  // extern "C"
+
+// The same gradients for chosen outputs only, for shapes where the full
+// backward is too slow: dq of the chosen rows (b, h, i), and dk, dv of the
+// chosen keys (b, h, j). Each row that enters is evaluated in full by the
+// definition: its multiplicity row c_i,:, logits, lse_i = ln sum_j c_ij e^s_ij
+// and D_i = sum_j P_ij (dO_i . v_j); a chosen key j then sums over every row i
+// with c_ij > 0. A row no pattern covers contributes nothing.
+namespace {
+
+struct LongnetRow {
+  std::vector<double> c, logit;  // c_i,: and the scaled logits where c > 0
+  double lse = 0.0, Di = 0.0;
+  bool covered = false;
+};
+
+void longnet_row(int32_t N, int32_t D, int32_t h, int32_t i, const double* q, const double* k,
+                 const double* v, const double* dout, const int32_t* w, const int32_t* r,
+                 int32_t n_pairs, int32_t causal, LongnetRow& row) {
+  const double scale = 1.0 / std::sqrt((double)D);
+  row.c.assign(N, 0.0);
+  row.logit.assign(N, 0.0);
+  const double* qi = q + (size_t)i * D;
+  double M = -std::numeric_limits<double>::infinity();
+  for (int32_t j = 0; j < N; ++j) {
+    row.c[j] = longnet_mult(i, j, h, w, r, n_pairs, causal);
+    if (row.c[j] == 0.0) continue;
+    double dot = 0.0;
+    for (int32_t d = 0; d < D; ++d) dot += qi[d] * k[(size_t)j * D + d];
+    row.logit[j] = dot * scale;
+    M = std::max(M, row.logit[j]);
+  }
+  row.covered = M != -std::numeric_limits<double>::infinity();
+  if (!row.covered) return;
+  double Z = 0.0;
+  for (int32_t j = 0; j < N; ++j)
+    if (row.c[j] != 0.0) Z += row.c[j] * std::exp(row.logit[j] - M);
+  row.lse = M + std::log(Z);
+  const double* doi = dout + (size_t)i * D;
+  row.Di = 0.0;
+  for (int32_t j = 0; j < N; ++j) {
+    if (row.c[j] == 0.0) continue;
+    double dp = 0.0;
+    for (int32_t d = 0; d < D; ++d) dp += doi[d] * v[(size_t)j * D + d];
+    row.Di += row.c[j] * std::exp(row.logit[j] - row.lse) * dp;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lo_longnet_backward_sel(int32_t B, int32_t H, int32_t N, int32_t D, const double* q,
+                                const double* k, const double* v, const int32_t* w,
+                                const int32_t* r, int32_t n_pairs, int32_t causal,
+                                const double* dout, const int32_t* rows, int64_t n_rows,
+                                double* dq_rows, const int32_t* keys, int64_t n_keys,
+                                double* dk_keys, double* dv_keys, int32_t n_threads) {
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || n_pairs < 1 || !q || !k || !v || !dout) return -1;
+  if ((n_rows > 0 && (!rows || !dq_rows)) || (n_keys > 0 && (!keys || !dk_keys || !dv_keys)))
+    return -1;
+  for (int32_t p = 0; p < n_pairs; ++p)
+    if (w[p] < 1 || r[p] < 1) return -1;
+  const double scale = 1.0 / std::sqrt((double)D);
+  const size_t head_elems = (size_t)N * D;
+  // dq_i = sum_j P_ij (dP_ij - D_i) k_j / sqrt(D)
+  parallel_rows(n_rows, n_threads, [&](int64_t x) {
+    const int32_t b = rows[3 * x], h = rows[3 * x + 1], i = rows[3 * x + 2];
+    const size_t off = ((size_t)b * H + h) * head_elems;
+    double* dqi = dq_rows + (size_t)x * D;
+    for (int32_t d = 0; d < D; ++d) dqi[d] = 0.0;
+    LongnetRow row;
+    longnet_row(N, D, h, i, q + off, k + off, v + off, dout + off, w, r, n_pairs, causal, row);
+    if (!row.covered) return;
+    const double* doi = dout + off + (size_t)i * D;
+    for (int32_t j = 0; j < N; ++j) {
+      if (row.c[j] == 0.0) continue;
+      const double P = row.c[j] * std::exp(row.logit[j] - row.lse);
+      double dp = 0.0;
+      for (int32_t d = 0; d < D; ++d) dp += doi[d] * v[off + (size_t)j * D + d];
+      const double g = P * (dp - row.Di);
+      for (int32_t d = 0; d < D; ++d) dqi[d] += g * k[off + (size_t)j * D + d] * scale;
+    }
+  });
+  // dk_j = sum_i P_ij (dP_ij - D_i) q_i / sqrt(D),  dv_j = sum_i P_ij dO_i
+  parallel_rows(n_keys, n_threads, [&](int64_t x) {
+    const int32_t b = keys[3 * x], h = keys[3 * x + 1], j = keys[3 * x + 2];
+    const size_t off = ((size_t)b * H + h) * head_elems;
+    double* dkj = dk_keys + (size_t)x * D;
+    double* dvj = dv_keys + (size_t)x * D;
+    for (int32_t d = 0; d < D; ++d) dkj[d] = dvj[d] = 0.0;
+    LongnetRow row;
+    for (int32_t i = 0; i < N; ++i) {
+      if (longnet_mult(i, j, h, w, r, n_pairs, causal) == 0) continue;
+      longnet_row(N, D, h, i, q + off, k + off, v + off, dout + off, w, r, n_pairs, causal, row);
+      const double* qi = q + off + (size_t)i * D;
+      const double* doi = dout + off + (size_t)i * D;
+      const double P = row.c[j] * std::exp(row.logit[j] - row.lse);
+      double dp = 0.0;
+      for (int32_t d = 0; d < D; ++d) dp += doi[d] * v[off + (size_t)j * D + d];
+      const double g = P * (dp - row.Di);
+      for (int32_t d = 0; d < D; ++d) {
+        dkj[d] += g * qi[d] * scale;
+        dvj[d] += P * doi[d];
+      }
+    }
+  });
+  return 0;
+}
+
+}  // extern "C"
+
+extern "C" {
+
 // Sparse Transformer fixed pattern, fp64: masked dense softmax over
 // fixed_allows. q, k, v: [B,H,N,D]; sel as in lo_attn_rows.
 int32_t lo_fixed_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q, const double* k,

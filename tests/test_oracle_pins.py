@@ -730,6 +730,48 @@ def pin_longnet_backward(lib):
         assert np.allclose(a_, b_.grad.numpy(), rtol=1e-10, atol=1e-12)
 
 
+def pin_longnet_per_pattern_outputs(lib):
+    """The page-order mixture's per-pattern outputs: pattern k's O_k and lse_k
+    equal the mixture of that single pattern alone (for a row the pattern skips,
+    O_k = 0 and lse_k = -inf), and mixing them with weights e^{lse_k} gives the
+    mixture's own output."""
+    rng = np.random.default_rng(25)
+    pairs = ((8, 1), (16, 2), (24, 3), (20, 4))
+    q, k, v = rand_qkv(rng, 2, 5, 40, 6)
+    for causal in (True, False):
+        o, l, ok, lk = oracle.longnet_mixture_rows(q, k, v, pairs, causal, per_pattern=True,
+                                                   lib=lib)
+        ok, lk = ok.reshape(len(pairs), -1, 6), lk.reshape(len(pairs), -1)
+        for p_, pair in enumerate(pairs):
+            o1, l1 = oracle.longnet_rows(q, k, v, [pair], causal, lib=lib)
+            fin = np.isfinite(l1.reshape(-1))
+            assert np.array_equal(np.isfinite(lk[p_]), fin), (pair, causal)
+            assert np.abs(lk[p_][fin] - l1.reshape(-1)[fin]).max() < 1e-12
+            assert np.abs(ok[p_] - o1.reshape(-1, 6)).max() < 1e-12
+            assert (ok[p_][~fin] == 0).all()
+        wgt = np.exp(lk - l.reshape(-1)[None])
+        assert np.abs((wgt[..., None] * ok).sum(0) - o.reshape(-1, 6)).max() < 1e-12
+
+
+def pin_longnet_backward_selected(lib):
+    """Chosen-row / chosen-key gradients against the full backward (itself
+    pinned by finite differences), with overlapping patterns so that some
+    pairs count twice, rows no pattern covers, and a ragged last segment."""
+    rng = np.random.default_rng(26)
+    B, H, N, D = 2, 4, 30, 4
+    q, k, v = rand_qkv(rng, B, H, N, D)
+    dout = rng.standard_normal(q.shape)
+    for pairs, causal in ((((8, 1), (16, 2), (16, 1), (30, 4)), True),
+                          (((12, 2), (30, 3)), False)):
+        dq, dk, dv = oracle.longnet_backward(q, k, v, dout, pairs, causal, lib=lib)
+        allr = np.array([(b, h, i) for b in range(B) for h in range(H) for i in range(N)])
+        sq, sk, sv = oracle.longnet_backward_sel(q, k, v, dout, pairs, causal, rows=allr,
+                                                 keys=allr[::-1], lib=lib)
+        assert np.abs(sq - dq.reshape(-1, D)).max() < 1e-12, pairs
+        assert np.abs(sk[::-1] - dk.reshape(-1, D)).max() < 1e-12, pairs
+        assert np.abs(sv[::-1] - dv.reshape(-1, D)).max() < 1e-12, pairs
+
+
 PINS = [pin_mask_matches_enumeration, pin_counts_closed_form, pin_counts_full_workloads,
         pin_longnet_counts, pin_longnet_worked_example, pin_longnet_offsets_partition,
         pin_dense_special_cases, pin_global_rows_are_full_rows, pin_brute_force_band,
@@ -738,7 +780,8 @@ PINS = [pin_mask_matches_enumeration, pin_counts_closed_form, pin_counts_full_wo
         pin_longnet_paths_agree,
         pin_rows_sum_to_one, pin_uncovered_rows, pin_sampled_rows_match_full,
         pin_backward_finite_differences, pin_backward_dense_autograd,
-        pin_backward_shift_invariants, pin_longnet_backward]
+        pin_backward_shift_invariants, pin_longnet_backward, pin_longnet_per_pattern_outputs,
+        pin_longnet_backward_selected]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -795,6 +838,14 @@ MUTANTS = [
      "double* dkb = dk + off;"),
     ("longnet-backward-multiplicity-one", "P[j] = c;  // the multiplicity for now",
      "P[j] = c ? 1 : 0;  // the multiplicity for now"),
+    ("per-pattern-lse-is-mixture-lse", "lse_k[(size_t)p * rows + x] = Lk[p];",
+     "lse_k[(size_t)p * rows + x] = Lmax;"),
+    ("selected-delta-without-multiplicity",
+     "row.Di += row.c[j] * std::exp(row.logit[j] - row.lse) * dp;",
+     "row.Di += std::exp(row.logit[j] - row.lse) * dp;"),
+    ("selected-dv-from-dS", "dvj[d] += P * doi[d];", "dvj[d] += g * doi[d];"),
+    ("selected-dq-unscaled", "for (int32_t d = 0; d < D; ++d) dqi[d] += g * k[off + (size_t)j * D + d] * scale;",
+     "for (int32_t d = 0; d < D; ++d) dqi[d] += g * k[off + (size_t)j * D + d];"),
 ]
 
 
