@@ -33,6 +33,8 @@
  * Conventions for every call:
  *   - B, H, N >= 0; a call with B, H or N equal to 0 does nothing and returns
  *     LA_OK (after the remaining argument checks that need no pointer).
+ *     N must be below 2^24 and B*H*N at most 2^31 (LA_EUNSUPPORTED otherwise):
+ *     the kernels address a head's rows with 32-bit byte offsets.
  *   - q, k, v, out (and qg, kg, vg) are device tensors, contiguous [B,H,N,D]
  *     row-major, 16-byte aligned, of the dtype in la_dims (bf16 or fp32);
  *     D must be 64 and la_attn_forward takes H <= 64 (LA_EUNSUPPORTED above).
@@ -42,8 +44,9 @@
  *     denominator, lse_i = ln sum_j c_ij exp(s_ij).
  *   - Ownership: the caller owns every buffer. The library allocates nothing,
  *     keeps no pointer after returning, never writes its inputs, and fully
- *     overwrites out and lse. The workspace is scratch (see la_attn_ext for the
- *     part of it that must start at zero). out must not alias an input.
+ *     overwrites out and lse. The workspace is scratch whose contents on entry
+ *     do not matter (nothing in it needs initialisation). out must not alias
+ *     an input.
  *   - All work is enqueued on `stream` (0 = the null stream); the call returns
  *     without synchronising and issues no device-to-host copy.
  *   - Errors: host-detectable argument errors return LA_EINVAL and enqueue
@@ -87,13 +90,12 @@ typedef struct {
    * keep q, k, v (for their global columns too). */
   const void *qg, *kg, *vg;
   /* Device scratch of at least la_attn_workspace_size() bytes, 256-byte aligned;
-   * required when n_global > 0. It holds arrival counters, which must be zero
-   * when a call starts; every call leaves its counters at zero again. A
-   * workspace zero-filled once therefore serves any number of calls with the
-   * same dims and n_global; before a call with other dims or n_global (whose
-   * counters may sit where earlier calls left other data) it must be
-   * zero-filled again. The rest is overwritten. Calls that share a workspace
-   * must not overlap in time. */
+   * required when n_global > 0. Its contents on entry do not matter and need no
+   * initialisation: it holds the global rows' key-chunk partials, which the call
+   * writes before reading, and one arrival counter word per tile of global rows,
+   * tagged with a token unique to the call (a quiet-NaN bit pattern no fp32
+   * value this library writes can hold), so words left by earlier calls of any
+   * shape are ignored. Calls that share a workspace must not overlap in time. */
   void *workspace;
   size_t workspace_bytes;
   /* Key-side relative-position vectors (ETC page, §3.4 "Relative Position
@@ -195,7 +197,7 @@ typedef struct {
  *  dout         device [B,H,N,D] in q's dtype: the loss gradient w.r.t. out.
  *  dq, dk, dv   device fp32 [B,H,N,D] outputs; must not alias any input.
  * Requires ext->workspace (fully overwritten). Pointers 16-byte aligned. Errors
- * as for la_attn_forward. Two launches on `stream`, no allocation. */
+ * as for la_attn_forward. Three launches on `stream`, no allocation. */
 la_status la_attn_backward(const la_dims *dims, const void *q, const void *k, const void *v,
                            const int32_t *global_idx, int32_t n_global, int32_t radius,
                            const int32_t *dilation, int32_t causal, const void *out,

@@ -194,9 +194,9 @@ def _workspace(nbytes: int, device, given: Optional[torch.Tensor]) -> Optional[t
         if given.numel() * given.element_size() < nbytes or not given.is_cuda:
             raise LaError(LA_EINVAL, "workspace tensor too small")
         return given
-    # torch's caching allocator returns 512-byte aligned blocks; zero-filled,
-    # as the band + global call's arrival counters must start at zero
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    # torch's caching allocator returns 512-byte aligned blocks; the library
+    # needs no particular contents in a workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 class BoundCall:

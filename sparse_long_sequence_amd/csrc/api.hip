@@ -6,9 +6,11 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <string>
 #include <vector>
 
+#include "entry.h"
 #include "kernels.h"
 #include "longattn.h"
 
@@ -22,6 +24,7 @@ la_status fail(la_status s, const std::string& msg) {
 }
 
 constexpr int32_t kDHead = 64;
+constexpr int32_t kMaxN = 1 << 24;
 // Keys per global-row partial: at least 8 chunks per row when that leaves a
 // whole key tile each (short sequences spread their global rows over several
 // workgroups), at most 10 key tiles.
@@ -41,7 +44,19 @@ la_status check_dims(const la_dims* d, bool need_bf16) {
   if (need_bf16 && d->dtype != LA_BF16) return fail(LA_EUNSUPPORTED, "this call is built for bf16 only");
   const int64_t total = (int64_t)d->B * d->H * d->N;
   if (total > (int64_t)1 << 31) return fail(LA_EUNSUPPORTED, "B*H*N above 2^31 rows");
+  // bf16 tiles are addressed with 32-bit byte offsets within a head (N * 128 B)
+  // and the LongNet index arithmetic divides positions in fp32
+  if (d->N >= kMaxN) return fail(LA_EUNSUPPORTED, "N must be below 2^24");
   return LA_OK;
+}
+
+// A fresh token per band + global call: a quiet-NaN bit pattern (payload
+// 1 .. 2^22 - 1), which no fp32 partial or lse ever holds, so counter words
+// left by earlier calls (or partial data at the same offset) never match it.
+uint32_t next_token() {
+  static std::atomic<uint32_t> seq{0};
+  const uint32_t n = seq.fetch_add(1, std::memory_order_relaxed);
+  return 0x7FC00000u | (1u + n % 0x3FFFFFu);
 }
 
 bool is_empty(const la_dims* d) { return d->B == 0 || d->H == 0 || d->N == 0; }
@@ -53,7 +68,8 @@ int32_t chunk_len_of(int32_t N) {
 int32_t n_chunks_of(int32_t N) { return (N + chunk_len_of(N) - 1) / chunk_len_of(N); }
 
 // Workspace of la_attn_forward: global-row partials, fp32 O then fp32 lse,
-// then one uint32 arrival counter per tile of global rows (zero between calls).
+// then one 64-bit arrival counter word per tile of global rows (tagged with
+// the call's token; no initialisation needed).
 struct AttnWs {
   size_t o_off, lse_off, cnt_off, bytes;
 };
@@ -66,7 +82,7 @@ AttnWs attn_ws_layout(const la_dims* d, int32_t n_global) {
   const size_t tiles = (size_t)d->B * d->H * ((n_global + tq - 1) / tq);
   w.lse_off = align_up(parts * kDHead * sizeof(float));
   w.cnt_off = w.lse_off + align_up(parts * sizeof(float));
-  w.bytes = w.cnt_off + align_up(tiles * sizeof(uint32_t));
+  w.bytes = w.cnt_off + align_up(tiles * sizeof(uint64_t));
   return w;
 }
 
@@ -169,10 +185,18 @@ size_t la_dilated_workspace_size(const la_dims* dims, const int32_t* seg_lens,
   return p.ws_bytes;
 }
 
-la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, const void* v,
+}  // extern "C"
+
+namespace la {
+
+// la_attn_forward with its workspace given apart from ext (ext->workspace is
+// not read): the caller's buffer, or the allocation-free entry point's
+// device scratch. ws_limit > 0 caps the workspace a call may need.
+la_status attn_forward_ws(const la_dims* dims, const void* q, const void* k, const void* v,
                           const int32_t* global_idx, int32_t n_global, int32_t radius,
                           const int32_t* dilation, int32_t causal, const float* rel_bias,
-                          void* out, float* lse, hipStream_t stream, const la_attn_ext* ext) {
+                          void* out, float* lse, hipStream_t stream, const la_attn_ext* ext,
+                          WorkspaceSource src) {
   la_status st = check_dims(dims, false);
   if (st != LA_OK) return st;
   if (is_empty(dims)) return LA_OK;  // nothing to compute
@@ -213,10 +237,22 @@ la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, con
     vg = ext->vg;
   }
   const size_t need = attn_ws_bytes(dims, n_global);
+  void* ws = nullptr;
   if (need > 0) {
-    if (!ext || !ext->workspace || ext->workspace_bytes < need)
-      return fail(LA_EINVAL, "workspace missing or smaller than la_attn_workspace_size()");
-    if (((uintptr_t)ext->workspace & (kAlign - 1)) != 0)
+    if (src.fixed_bytes > 0) {
+      if (need > src.fixed_bytes)
+        return fail(LA_EUNSUPPORTED, "this call needs " + std::to_string(need) +
+                                         " bytes of scratch, above the " +
+                                         std::to_string(src.fixed_bytes) +
+                                         " bytes the allocation-free entry point holds");
+      ws = src.get();
+      if (!ws) return fail(LA_EHIP, std::string("device scratch unavailable: ") + g_err);
+    } else {
+      if (!ext || !ext->workspace || ext->workspace_bytes < need)
+        return fail(LA_EINVAL, "workspace missing or smaller than la_attn_workspace_size()");
+      ws = ext->workspace;
+    }
+    if (((uintptr_t)ws & (kAlign - 1)) != 0)
       return fail(LA_EINVAL, "workspace must be 256-byte aligned");
   }
 
@@ -241,10 +277,11 @@ la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, con
   a.lse = lse;
   if (need > 0) {
     const AttnWs lay = attn_ws_layout(dims, n_global);
-    char* base = reinterpret_cast<char*>(ext->workspace);
+    char* base = reinterpret_cast<char*>(ws);
     a.ws_o = reinterpret_cast<float*>(base + lay.o_off);
     a.ws_lse = reinterpret_cast<float*>(base + lay.lse_off);
-    a.ws_cnt = reinterpret_cast<uint32_t*>(base + lay.cnt_off);
+    a.ws_cnt = reinterpret_cast<uint64_t*>(base + lay.cnt_off);
+    a.token = next_token();
     // partials are addressed with 32-bit byte offsets
     if (lay.cnt_off > (size_t)0x7fffffff) return fail(LA_EUNSUPPORTED, "global-row partials above 2 GiB");
   }
@@ -265,6 +302,20 @@ la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, con
   hipError_t e = la::launch_attn(a, dims->dtype, stream);
   if (e != hipSuccess) return fail(LA_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(e));
   return LA_OK;
+}
+
+la_status set_error(la_status s, const char* msg) { return fail(s, msg); }
+
+}  // namespace la
+
+extern "C" {
+
+la_status la_attn_forward(const la_dims* dims, const void* q, const void* k, const void* v,
+                          const int32_t* global_idx, int32_t n_global, int32_t radius,
+                          const int32_t* dilation, int32_t causal, const float* rel_bias,
+                          void* out, float* lse, hipStream_t stream, const la_attn_ext* ext) {
+  return la::attn_forward_ws(dims, q, k, v, global_idx, n_global, radius, dilation, causal,
+                             rel_bias, out, lse, stream, ext, la::WorkspaceSource{});
 }
 
 la_status la_dilated_forward(const la_dims* dims, const void* q, const void* k, const void* v,

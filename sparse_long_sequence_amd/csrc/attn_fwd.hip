@@ -453,15 +453,24 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
     if (TT::row_leader(lane))
       st_coh4(rl, prow * 4, l_tot > 0.f ? (w.m[0] + __log2f(l_tot)) * kLn2 : kNegInf);
   }
-  // Arrival: the last chunk workgroup of this tile merges all its chunks.
+  // Arrival: the last chunk workgroup of this tile merges all its chunks. The
+  // counter word carries the call's token in its high half; a word with any
+  // other high half (zero, another call's token, stale partial data: fp32
+  // values, never this NaN pattern) is taken as no arrival yet.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
   __syncthreads();
   int32_t* flag = reinterpret_cast<int32_t*>(&sm.gcls[0]);
-  uint32_t* cnt = a.ws_cnt + (bh * a.n_gq_tiles + gq);
+  uint64_t* cnt = a.ws_cnt + (bh * a.n_gq_tiles + gq);
   if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old + 1u == (uint32_t)a.n_chunks;
-    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t tag = (uint64_t)a.token << 32;
+    uint64_t old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t nv;
+    do {
+      nv = (old >> 32) == (uint64_t)a.token ? old + 1u : tag + 1u;
+    } while (!__hip_atomic_compare_exchange_strong(cnt, &old, nv, __ATOMIC_RELAXED,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const bool last = (uint32_t)nv == (uint32_t)a.n_chunks;
+    if (last) __hip_atomic_store(cnt, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = last ? 1 : 0;
   }
   __syncthreads();
@@ -470,7 +479,7 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
                        gq * kTQ, qcount);
 }
 
-// At least kMinWavesPerEU waves per SIMD// At least kMinWavesPerEU waves per SIMD: that bounds each wave's registers.
+// At least kMinWavesPerEU waves per SIMD: that bounds each wave's registers.
 // BIAS: a relative-position bias (scalar table and/or key-side label vectors)
 // is given; SEG: segment masks are given. Each kernel carries only the code
 // its flags need.

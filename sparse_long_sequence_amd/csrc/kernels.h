@@ -26,7 +26,11 @@ struct AttnArgs {
   float* lse;
   float* ws_o;      // [B*H][n_global][n_chunks][D] global-row partials
   float* ws_lse;    // [B*H][n_global][n_chunks]
-  uint32_t* ws_cnt; // [B*H][n_gq_tiles] chunk arrivals per global-row tile (0 between calls)
+  // [B*H][n_gq_tiles] chunk arrivals per global-row tile: (token << 32) | count.
+  // A word whose high half is not this call's token counts as 0, so whatever
+  // an earlier call left there is ignored; the tile's last arrival writes 0.
+  uint64_t* ws_cnt;
+  uint32_t token;   // unique per call: a quiet-NaN bit pattern no fp32 partial holds
   int32_t chunk_len, n_chunks;
   int32_t band_tiles_per_head;
   int32_t n_band_wg;

@@ -80,6 +80,11 @@ def test_attn_argument_errors(L):
     assert _attn(L, d, gidx=FAKE, n_global=4,
                  ext=LaAttnExt(0, None, None, None, FAKE, need - 1)) == la.LA_EINVAL
     assert _attn(L, LaDims(1, 65, 128, 64, la.LA_BF16)) == la.LA_EUNSUPPORTED
+    # a head of 2^24 rows or more is refused (32-bit byte offsets within a head)
+    assert _attn(L, LaDims(1, 1, 1 << 24, 64, la.LA_BF16)) == la.LA_EUNSUPPORTED
+    assert "2^24" in la.la_last_error()
+    assert _attn(L, LaDims(1, 1, 1 << 24, 64, la.LA_F32)) == la.LA_EUNSUPPORTED
+    assert la.la_attn_workspace_size(LaDims(1, 1, 1 << 24, 64, la.LA_BF16), 4) == 0
     # empty tensors are a no-op
     assert _attn(L, LaDims(0, 2, 128, 64, la.LA_BF16), q=None, k=None, v=None, out=None) == la.LA_OK
 
@@ -103,6 +108,7 @@ def test_dilated_argument_errors(L):
     assert call() == la.LA_EINVAL  # no workspace
     need = la.la_dilated_workspace_size(d, [64, 128], [1, 2])
     assert call(ext=LaDilatedExt(None, FAKE, need - 1)) == la.LA_EINVAL
+    assert call(dims=LaDims(1, 1, 1 << 24, 64, la.LA_BF16)) == la.LA_EUNSUPPORTED
 
 
 def test_fixed_argument_errors(L):
@@ -179,8 +185,8 @@ def test_workspace_sizes(L):
     d = LaDims(2, 12, 4096, 64, la.LA_BF16)
     assert la.la_attn_workspace_size(d, 0) == 0
     # 64 global rows x 8 key chunks of 512 per (b, h): fp32 O plus fp32 lse,
-    # then one arrival counter per (b, h) and 128-row tile of global rows,
-    # each part padded to 256 bytes
+    # then one 64-bit arrival counter word per (b, h) and 128-row tile of
+    # global rows, each part padded to 256 bytes
     parts = 2 * 12 * 64 * 8
     assert la.la_attn_workspace_size(d, 64) == parts * 64 * 4 + parts * 4 + 256
     assert la.la_attn_workspace_size(LaDims(1, 1, 10, 64, la.LA_BF16), 11) == 0  # n_global > N

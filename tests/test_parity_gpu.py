@@ -305,14 +305,60 @@ def test_mask_exact_longnet(dev):
         assert np.array_equal(np.rint(o[0, h] * cnt[:, None]).astype(np.int64), res), f"h={h}"
 
 
+def _mask_compare(tag, out, lse, o_ref, l_ref):
+    """Exact comparison of allowed-key counts and key residues (Q = 0, one-hot V):
+    the GPU's rint(exp(lse)) and rint(O * count) against the oracle's."""
+    cnt_ref = np.rint(np.exp(l_ref)).astype(np.int64)
+    cnt = np.rint(np.exp(to64(lse))).astype(np.int64)
+    assert np.array_equal(cnt, cnt_ref), f"{tag}: key counts differ"
+    res_ref = np.rint(o_ref * cnt_ref[..., None]).astype(np.int64)
+    res = np.rint(to64(out) * cnt_ref[..., None]).astype(np.int64)
+    assert np.array_equal(res, res_ref), f"{tag}: allowed key sets differ"
+
+
+FIXED_MASK_CASES = [
+    W.Workload("mask-fixed-causal", B=1, H=5, N=1024, kind="fixed", causal=True, fixed=(256, 64)),
+    W.Workload("mask-fixed-full", B=1, H=3, N=768, kind="fixed", causal=False, fixed=(256, 128)),
+]
+
+
+@pytest.mark.parametrize("w", FIXED_MASK_CASES, ids=[w.name for w in FIXED_MASK_CASES])
+def test_mask_exact_fixed(dev, w):
+    say(f"case {w.name}")
+    inp = _mask_inputs(w, dev)
+    out, lse = gpu_fixed(w, inp, dev)
+    o_ref, l_ref = oracle_fixed(w, inp)
+    _mask_compare(w.name, out, lse, o_ref, l_ref)
+
+
+def test_mask_exact_segments(dev):
+    # packed documents of different lengths per batch row, globals in several
+    # documents, a dilated head and a causal window: every row's key set
+    w = W.Workload("mask-segments", B=2, H=2, N=900, radius=60, dilation=(1, 3), causal=False,
+                   global_idx=(0, 1, 300, 301, 640, 899))
+    inp = _mask_inputs(w, dev)
+    inp.seg = torch.tensor(np.stack([np.repeat([0, 1, 2], [300, 340, 260]),
+                                     np.repeat([5, 6], [640, 260])]), dtype=torch.int32)
+    say(f"case {w.name}")
+    out, lse = gpu_attn(w, inp, dev)
+    o_ref, l_ref = oracle_attn(w, inp)
+    _mask_compare(w.name, out, lse, o_ref, l_ref)
+    wc = w.with_(name="mask-segments-causal", causal=True)
+    out, lse = gpu_attn(wc, inp, dev)
+    o_ref, l_ref = oracle_attn(wc, inp)
+    _mask_compare(wc.name, out, lse, o_ref, l_ref)
+
+
 # --------------------------------------------------------------------------
-# the five workloads at full size, in the launch configuration the bench times
+# the workloads at full size, in the launch configuration the bench times
 # --------------------------------------------------------------------------
 def _sel_rows(w, n):
+    """Tile edges (every 64th position and its neighbours), edges of the
+    sequence, random rows, and every global row of two heads."""
     must = set()
     for t in range(0, w.N, 64):
         must |= {t - 1, t, t + 1}
-    must = sorted(i for i in must if 0 <= i < w.N)[:64]
+    must = sorted(i for i in must if 0 <= i < w.N)
     rows = W.sample_rows(w, n, seed=11, must_include=must).numpy()
     if w.global_idx:  # every global row of two heads (the separate pass)
         g = np.array(w.global_idx)
@@ -321,30 +367,27 @@ def _sel_rows(w, n):
     return rows.astype(np.int32)
 
 
+# heads with distinct offsets under every pattern of the 32K workloads
+# (h mod r for r = 2, 4, 6, 12; summary sub-block h mod 16)
+HEADS_32K = (0, 5, 11)
+
+
 @pytest.mark.parametrize("w", W.ORDERED, ids=[w.name for w in W.ORDERED])
 def test_workload_parity(dev, w):
     say(f"workload {w.name}: B={w.B} H={w.H} N={w.N} {w.dtype}")
     inp = W.make_inputs(w)
-    if w.kind == "dilated":
-        out, lse = gpu_dilated(w, inp, dev)
-        sel = _sel_rows(w, 1500)
-        o_ref, l_ref = oracle_dilated(w, inp, sel)
-        compare(w, out, lse, o_ref, l_ref, sel, tag=w.name)
-        return
-    if w.kind == "fixed":
-        out, lse = gpu_fixed(w, inp, dev)
-        sel = _sel_rows(w, 1500)
-        o_ref, l_ref = oracle_fixed(w, inp, sel)
+    if w.kind in ("dilated", "fixed"):
+        out, lse = gpu_dilated(w, inp, dev) if w.kind == "dilated" else gpu_fixed(w, inp, dev)
+        # every row of three heads
+        sel = np.array([(b, h, i) for b in range(w.B) for h in HEADS_32K for i in range(w.N)],
+                       dtype=np.int32)
+        ref = oracle_dilated if w.kind == "dilated" else oracle_fixed
+        o_ref, l_ref = ref(w, inp, sel)
         compare(w, out, lse, o_ref, l_ref, sel, tag=w.name)
         return
     out, lse = gpu_attn(w, inp, dev)
-    if w.B * w.H * w.N <= 1 << 14:
-        o_ref, l_ref = oracle_attn(w, inp)
-        compare(w, out, lse, o_ref, l_ref, tag=w.name)
-    else:
-        sel = _sel_rows(w, 3000)
-        o_ref, l_ref = oracle_attn(w, inp, sel)
-        compare(w, out, lse, o_ref, l_ref, sel, tag=w.name)
+    o_ref, l_ref = oracle_attn(w, inp)  # every row
+    compare(w, out, lse, o_ref, l_ref, tag=w.name)
 
 
 # --------------------------------------------------------------------------
@@ -397,23 +440,25 @@ def test_limits_many_scattered_globals(dev):
 
 
 def test_workspace_reuse(dev):
-    # One workspace, zero-filled once, serves repeated calls of one shape: each
-    # call leaves its arrival counters at zero. Before a call of another shape
-    # (its counters may lie where the previous call left partials) it is
-    # zero-filled again, as the interface requires.
+    # One workspace, never zero-filled, serves calls of several shapes in turn:
+    # its initial contents are arbitrary bytes, and every call leaves partials
+    # and counter words where a call of another shape keeps its own. Each
+    # call's result must not depend on any of it.
     wa = W.Workload("reuse-a", B=2, H=3, N=1500, radius=60, global_idx=tuple(range(0, 1500, 7)),
                     seed=95)
     wb = W.Workload("reuse-b", B=1, H=2, N=700, radius=30, global_idx=(3, 4, 5, 600), seed=96)
     nb = max(la.la_attn_workspace_size(la.LaDims(w.B, w.H, w.N, 64, la.LA_BF16), len(w.global_idx))
              for w in (wa, wb))
-    ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
-    prev = None
-    for w in (wa, wa, wa, wb, wb, wa):
-        if prev is not None and w is not prev:
-            ws.zero_()
-        prev = w
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    for x, fill in enumerate(("ones", "random", None, None, None, None)):
+        w = (wa, wa, wb, wb, wa, wb)[x]
+        if fill == "ones":
+            ws.fill_(0xFF)
+        elif fill == "random":
+            ws.copy_(torch.randint(0, 256, (nb,), dtype=torch.uint8,
+                                   generator=torch.Generator().manual_seed(x)).to(dev))
         inp = W.make_inputs(w)
-        say(f"case {w.name} (shared workspace)")
+        say(f"case {w.name} (shared workspace, fill={fill})")
         out, lse = gpu_attn(w, inp, dev, workspace=ws)
         o_ref, l_ref = oracle_attn(w, inp)
         compare(w, out, lse, o_ref, l_ref, tag=w.name)
