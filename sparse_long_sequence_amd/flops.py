@@ -51,17 +51,23 @@ def band_global_pairs(w: Workload) -> int:
     return total * w.B
 
 
+def dilated_pairs_head(w: Workload, h: int) -> int:
+    """Pairs attended by all (w, r) patterns in head h of one batch row (a pair
+    counted once per pattern): per segment, the kept rows of the head's offset
+    attend each other (causal: a triangle)."""
+    total = 0
+    for (seg_w, r) in w.pairs:
+        s = h % r
+        for start in range(0, w.N, seg_w):
+            L = min(seg_w, w.N - start)
+            n = (L - s + r - 1) // r if s < L else 0
+            total += n * (n + 1) // 2 if w.causal else n * n
+    return total
+
+
 def dilated_pairs(w: Workload) -> int:
     """Pairs attended by all (w, r) patterns (a pair counted once per pattern)."""
-    total = 0
-    for h in range(w.H):
-        for (seg_w, r) in w.pairs:
-            s = h % r
-            for start in range(0, w.N, seg_w):
-                L = min(seg_w, w.N - start)
-                n = (L - s + r - 1) // r if s < L else 0
-                total += n * (n + 1) // 2 if w.causal else n * n
-    return total * w.B
+    return w.B * sum(dilated_pairs_head(w, h) for h in range(w.H))
 
 
 def fixed_pairs(w: Workload) -> int:

@@ -4,11 +4,14 @@ The GPU forward supplies out and lse (the backward's inputs by contract); the
 oracle gets only q, k, v (and qg, kg, vg), the mask arguments and dout, and
 recomputes everything else in fp64.
 
-Bar: per gradient tensor, max |gpu - oracle| <= tol * max |oracle|, with tol
-1e-4 for fp32 inputs and 2e-2 for bf16. For bf16, the forward's output O is
-rounded to bf16 (relative 2^-9) before it enters D_i = dO_i . O_i, and its lse
-sums bf16-rounded probabilities; P_ij = exp(s_ij - lse_i) and dS_ij then carry
-relative errors of a few 2^-9 against the exact values, which the oracle uses.
+Bar, element-wise: |gpu - oracle| <= a * max|oracle| + b * |oracle| for every
+entry of every gradient tensor, with (a, b) = (1e-5, 1e-4) for fp32 inputs and
+(5e-3, 1e-2) for bf16. For bf16, the forward's output O is rounded to bf16
+(relative 2^-9) before it enters D_i = dO_i . O_i, and its lse sums
+bf16-rounded probabilities (relative error up to 2^-8); P_ij = exp(s_ij - lse_i)
+and dS_ij then carry relative errors of a few 2^-9 against the exact values,
+which the oracle uses, and a gradient entry sums many such terms of both signs,
+so its error scales with the tensor's largest entries rather than its own.
 """
 from __future__ import annotations
 
@@ -24,7 +27,8 @@ from sparse_long_sequence_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
+TOL_ABS = {"f32": 1e-5, "bf16": 5e-3}  # times max |oracle| of the tensor
+TOL_REL = {"f32": 1e-4, "bf16": 1e-2}  # times |oracle| of the entry
 TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
@@ -48,15 +52,17 @@ def to64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def check(tag, dtype, got, ref):
-    names = ("dq", "dk", "dv", "dqg", "dkg", "dvg")
+def check(tag, dtype, got, ref, names=("dq", "dk", "dv", "dqg", "dkg", "dvg")):
     assert len(got) == len(ref)
     for name, g, r in zip(names, got, ref):
-        g = to64(g)
+        g = g if isinstance(g, np.ndarray) else to64(g)
         scale = max(np.abs(r).max(), 1e-30)
-        err = np.abs(g - r).max()
+        err = np.abs(g - r)
+        bound = TOL_ABS[dtype] * scale + TOL_REL[dtype] * np.abs(r)
         assert np.isfinite(g).all(), f"{tag} {name}: non-finite"
-        assert err <= TOL[dtype] * scale, f"{tag} {name}: max err {err} > {TOL[dtype]} * {scale}"
+        say(f"{tag} {name}: max|err|/max|ref| = {err.max() / scale:.2e}, "
+            f"worst err/bound = {(err / bound).max():.3f}")
+        assert (err <= bound).all(), f"{tag} {name}: max err/bound {(err / bound).max()}"
 
 
 def run_case(dev, tag, dtype, B, H, N, glob, R, dil, causal, sep, seg_rows, seed,
@@ -173,6 +179,8 @@ LONGNET_CASES = [
     ("non-causal", 2, 3, 384, ((64, 1), (192, 3)), False),
     ("ragged-last-segment", 1, 6, 600, ((256, 1), (512, 2), (600, 6)), True),
     ("n4096", 1, 2, 4096, ((1024, 1), (2048, 2), (4096, 4)), True),
+    # no dilation-1 pattern: rows that no pattern covers have lse = -inf and no gradient
+    ("no-r1-uncovered", 1, 5, 333, ((64, 2), (128, 3), (333, 5)), True),
 ]
 
 
@@ -191,3 +199,68 @@ def test_backward_longnet(dev, case):
     torch.cuda.synchronize()
     ref = oracle.longnet_backward(to64(q), to64(k), to64(v), to64(dout), pairs, causal)
     check(f"longnet-{tag}", "bf16", grads, ref)
+    if all(r_ > 1 for r_ in r):
+        # a row no pattern keeps: for head h, offset h mod r differs from the
+        # row's residue in every pattern's segment
+        mult = [oracle.longnet_mult_rows(N, h, pairs, causal) for h in range(H)]
+        unc = np.array([[m[i].sum() == 0 for i in range(N)] for m in mult])
+        assert unc.any()
+        assert np.isneginf(to64(lse)[:, unc]).all()
+        assert (to64(grads[0])[:, unc] == 0).all(), "uncovered rows must get dq = 0"
+
+
+def _segment_end_keys(w, h):
+    """Keys j at the ends of the 8192-aligned segments that the (32768, 12)
+    pattern does not keep for head h (and the sequence's last keys): causal
+    rows attend them only from the same short tail of each segment, so the
+    oracle evaluates few rows per key."""
+    keys = []
+    for end in range(8192, w.N + 1, 8192):
+        for t in (0, 1, 2, 5, 17, 40):
+            j = end - 1 - t
+            if end == w.N or (j % 12) != (h % 12):
+                keys.append(j)
+    return keys
+
+
+def test_backward_longnet_full_shape(dev):
+    """The LongNet workload's own shape (B=1, H=12, N=32768, five patterns,
+    causal), heads 0, 5 and 11 (distinct offsets under every pattern): dq of
+    every tile-edge row of those heads' segments and some random rows, dk and dv
+    of keys at segment ends, against the oracle's chosen-output gradients; and,
+    over every key of those heads, the two sums the chain rule fixes: sum_j dk_j
+    = 0 and sum_j dv_j = sum_i dO_i (every row is covered: a pattern has r = 1)."""
+    w = W.LONGNET_SHARE
+    inp = W.make_inputs(w)
+    dout = torch.randn(inp.q.shape, generator=torch.Generator().manual_seed(410)).to(torch.bfloat16)
+    d = lambda t: t.to(dev).contiguous()
+    seg, dil = [p[0] for p in w.pairs], [p[1] for p in w.pairs]
+    say(f"longnet backward full shape: B={w.B} H={w.H} N={w.N} pairs={w.pairs}")
+    out, lse = la.la_dilated_forward(d(inp.q), d(inp.k), d(inp.v), seg, dil, True)
+    grads = la.la_dilated_backward(d(inp.q), d(inp.k), d(inp.v), out, lse, d(dout), seg, dil, True)
+    torch.cuda.synchronize()
+    g64 = [to64(t) for t in grads]
+    rng = np.random.default_rng(411)
+    rows, keys = [], []
+    for h in (0, 5, 11):
+        edge = sorted({x for t in range(0, w.N, 2048) for x in (t, t + 1, t + 63, t + 64,
+                                                                 t + 2047)})
+        for i in edge + rng.integers(0, w.N, 24).tolist():
+            rows.append((0, h, i))
+        keys += [(0, h, j) for j in _segment_end_keys(w, h)]
+    rows, keys = np.array(rows), np.array(keys)
+    f = lambda t: t.to(torch.float64).numpy()
+    dq_ref, dk_ref, dv_ref = oracle.longnet_backward_sel(f(inp.q), f(inp.k), f(inp.v), f(dout),
+                                                         w.pairs, True, rows=rows, keys=keys)
+    pick = lambda g, s: g[s[:, 0], s[:, 1], s[:, 2]]
+    check("longnet-full-dq", "bf16", [pick(g64[0], rows)], [dq_ref], names=("dq",))
+    check("longnet-full-dkv", "bf16", [pick(g64[1], keys), pick(g64[2], keys)], [dk_ref, dv_ref],
+          names=("dk", "dv"))
+    do64 = to64(dout)
+    for h in (0, 5, 11):
+        dk_sum = g64[1][0, h].sum(0)
+        dk_mag = np.abs(g64[1][0, h]).sum(0)
+        assert (np.abs(dk_sum) <= 1e-3 * dk_mag + 1e-6).all(), f"h={h}: sum of dk is not 0"
+        dv_sum, do_sum = g64[2][0, h].sum(0), do64[0, h].sum(0)
+        assert np.abs(dv_sum - do_sum).max() <= 2e-2 * np.abs(do64[0, h]).sum(0).max() / 64, \
+            f"h={h}: sum of dv differs from sum of dO"
