@@ -17,11 +17,17 @@ kernel (read from profiles/, and null when the kernel sources changed since);
 CPU oracle on a bounded row sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only NAME]
-                       [--copy-probe] [--settle SECONDS]
+                       [--copy-probe] [--settle SECONDS] [--backward]
 
 Each workload: W untimed warm-up calls, then untimed calls until the GPU has
 been busy for 0.25 s (its clocks ramp up under load), then exactly K calls
-timed as one region between two events, then K calls with an event pair each.
+timed as one region between two events, then K calls with an event pair each,
+then K cold calls: before each, a 512 MiB buffer is written (more than the
+L2 caches and the 256 MiB MALL hold), and an event pair times the call alone.
+
+--backward times la_attn_backward on the Longformer-base workload and
+la_dilated_backward on the LongNet workload instead (same method; the
+forward's out and lse are computed once, untimed) and prints their JSON line.
 
 --copy-probe also runs a plain device copy of 256 MiB (torch.neg, fp32) a few
 times: under rocprofv3 --pmc its FETCH_SIZE and WRITE_SIZE give the factor that
@@ -101,8 +107,23 @@ class Call:
 SETTLE_S = 0.25
 
 
-def time_calls(call, steps, warmup, settle_s=SETTLE_S):
-    """(ms per step over the timed region, mean and median ms of per-call event pairs)."""
+FLUSH_BYTES = 512 << 20
+_flush = None
+
+
+def flush_caches(dev):
+    """Write a 512 MiB buffer: evicts the inputs from the L2 caches and the MALL."""
+    import torch
+
+    global _flush
+    if _flush is None:
+        _flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    _flush.fill_(1.0)
+
+
+def time_calls(call, steps, warmup, settle_s=SETTLE_S, cold=True):
+    """(ms per step over the timed region, mean and median ms of per-call event
+    pairs, median ms of cold calls or None)."""
     import torch
 
     for _ in range(warmup):
@@ -131,7 +152,54 @@ def time_calls(call, steps, warmup, settle_s=SETTLE_S):
         b.record()
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) for a, b in ev)
-    return region_ms, sum(per) / len(per), per[len(per) // 2]
+    cold_ms = None
+    if cold:
+        dev = torch.device("cuda", torch.cuda.current_device())
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            flush_caches(dev)
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        cl = sorted(a.elapsed_time(b) for a, b in ev)
+        cold_ms = cl[len(cl) // 2]
+    return region_ms, sum(per) / len(per), per[len(per) // 2], cold_ms
+
+
+def cgroup_cpu_quota():
+    """CPUs' worth of time the job's cgroup allows (cpu.max quota / period), or None."""
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as fh:
+            quota, period = fh.read().split()[:2]
+        if quota != "max":
+            return max(1, int(int(quota) / int(period)))
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def host_cores() -> int:
+    """Every core this process may use: its affinity mask, capped by the cgroup's
+    CPU quota when one is set (threads beyond it would only be throttled)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    q = cgroup_cpu_quota()
+    return min(n, q) if q else n
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(w, min_s=10.0, max_s=30.0):
@@ -149,11 +217,7 @@ def cpu_baseline(w, min_s=10.0, max_s=30.0):
     from sparse_long_sequence_amd import flops as F
     from sparse_long_sequence_amd import workloads as W
 
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
+    cores = host_cores()
     inp = W.make_inputs(w)
     f = lambda t: None if t is None else t.to(torch.float64).numpy()
     q, k, v, qg, kg, vg, rb, rv = (f(x) for x in (inp.q, inp.k, inp.v, inp.qg, inp.kg, inp.vg,
@@ -187,7 +251,9 @@ def cpu_baseline(w, min_s=10.0, max_s=30.0):
     return {"value": round(value, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of {total_rows} rows of {w.name} (fp64, masked dense softmax per row), "
                       f"{passes} passes",
-            "seconds": round(elapsed, 3)}
+            "seconds": round(elapsed, 3), "nproc": os.cpu_count(),
+            "affinity_cores": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+            else None, "cgroup_cpu_quota": cgroup_cpu_quota(), "cpu_model": cpu_model()}
 
 
 COPY_PROBE_BYTES = 256 << 20
@@ -244,6 +310,51 @@ def copy_probe(dev, reps=3):
     torch.cuda.synchronize()
 
 
+def bench_backward(dev, args):
+    """Backward calls, timed like the forward: the Longformer-base band + global
+    backward (dq, dk, dv and the separate global projections' gradients) and
+    the LongNet mixture's backward. Useful work: 10*D FLOPs per allowed pair
+    (q.k and dO.v recomputed, then dV, dQ and dK, 2*D each)."""
+    import torch
+
+    import sparse_long_sequence_amd as la
+    from sparse_long_sequence_amd import flops as F
+    from sparse_long_sequence_amd import workloads as W
+
+    res = {}
+    for w in (W.LONGFORMER_BASE, W.LONGNET_SHARE):
+        log(f"bench backward: {w.name}")
+        c = Call(w, dev)
+        c()
+        dout = torch.randn(c.q.shape, generator=torch.Generator().manual_seed(7)).to(
+            c.q.dtype).to(dev)
+        if w.kind == "dilated":
+            call = la.bind_dilated_backward(c.q, c.k, c.v, c.out, c.lse, dout,
+                                            [p[0] for p in w.pairs], [p[1] for p in w.pairs],
+                                            w.causal)
+        else:
+            call = la.bind_attn_backward(c.q, c.k, c.v, c.out, c.lse, dout, c.g, w.radius,
+                                         w.dilation, w.causal, qg=c.qg, kg=c.kg, vg=c.vg)
+        steps = max(3, min(args.steps, 20))
+        region_ms, mean_ms, med_ms, _ = time_calls(call, steps, min(args.warmup, 3), args.settle,
+                                                   cold=False)
+        fl = 10 * w.D * F.useful_pairs(w)
+        res[w.name] = {"ms_per_call": round(region_ms, 4),
+                       "ms_per_call_event_pair_median": round(med_ms, 4),
+                       "useful_tflops": round(fl / (region_ms * 1e-3) / 1e12, 3),
+                       "useful_flop": fl, "steps": steps}
+        log(f"  {res[w.name]}")
+        del c, call
+        torch.cuda.empty_cache()
+    h = res[W.LONGFORMER_BASE.name]
+    return {"metric": "backward ms/call and useful TFLOP/s (10*D FLOPs per allowed pair)",
+            "value": h["useful_tflops"], "unit": "TFLOP/s", "n_gpus": 1,
+            "ms_per_step": h["ms_per_call"], "higher_is_better": True, "dtype": "bf16",
+            "data": "synthetic (seeded iid N(0,1), cast to bf16)",
+            "config": {"workload": W.LONGFORMER_BASE.name, "pass": "backward"},
+            "workloads": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +366,8 @@ def main():
                     help="seconds of untimed calls after the warm-up (0 for counter runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 256 MiB device copy (counter scaling under rocprofv3)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the two backward calls instead of the forward workloads")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -267,6 +380,9 @@ def main():
     from sparse_long_sequence_amd import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.backward:
+        print(json.dumps(bench_backward(dev, args)), flush=True)
+        return
     if args.copy_probe:
         log("bench: copy probe (torch.neg, 256 MiB fp32)")
         copy_probe(dev)
@@ -278,7 +394,7 @@ def main():
         log(f"bench: {w.name} (B={w.B} H={w.H} N={w.N} {w.dtype})")
         call = Call(w, dev)
         steps = args.steps
-        region_ms, mean_ms, med_ms = time_calls(call, steps, args.warmup, args.settle)
+        region_ms, mean_ms, med_ms, cold_ms = time_calls(call, steps, args.warmup, args.settle)
         fl = F.useful_flops(w)
         by = F.algorithmic_bytes(w)
         peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
@@ -288,6 +404,8 @@ def main():
             "ms_per_call": round(region_ms, 5),
             "ms_per_call_event_pair_mean": round(mean_ms, 5),
             "ms_per_call_event_pair_median": round(med_ms, 5),
+            "ms_per_call_cold_median": round(cold_ms, 5),
+            "useful_tflops_cold": round(fl / (cold_ms * 1e-3) / 1e12, 3),
             "useful_tflops": round(fl / (region_ms * 1e-3) / 1e12, 3),
             "frac_mfma_peak": round(fl / (region_ms * 1e-3) / 1e12 / peak, 4),
             "hbm_gbs_algorithmic": round(by / (region_ms * 1e-3) / 1e9, 1),
@@ -312,6 +430,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": r["ms_per_call"],
+        "ms_per_step_cold": r["ms_per_call_cold_median"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
