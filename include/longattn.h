@@ -136,6 +136,25 @@ la_status la_attn_forward(const la_dims *dims, const void *q, const void *k, con
                           const int32_t *dilation, int32_t causal, const float *rel_bias,
                           void *out, float *lse, hipStream_t stream, const la_attn_ext *ext);
 
+/* Allocation-free variant of la_attn_forward, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Arguments, results and errors are those of
+ * la_attn_forward, except that no workspace is passed (ext may be NULL; if
+ * given, ext->workspace must be NULL and ext->workspace_bytes 0, else
+ * LA_EINVAL): the call uses a fixed 32 MiB scratch array in the library's
+ * device memory instead, one copy per GPU, held from the first call on that
+ * GPU (its address is looked up then, with that GPU current) until the process
+ * ends. A call whose la_attn_workspace_size() exceeds 32 MiB returns
+ * LA_EUNSUPPORTED and enqueues nothing. The call allocates nothing and needs
+ * nothing cleared between calls. All calls on one GPU share the array: calls
+ * that overlap in time on one GPU (other streams or host threads) race, and
+ * the caller must serialise them. */
+la_status la_attn_forward_noalloc(const la_dims *dims, const void *q, const void *k,
+                                  const void *v, const int32_t *global_idx, int32_t n_global,
+                                  int32_t radius, const int32_t *dilation, int32_t causal,
+                                  const float *rel_bias, void *out, float *lse,
+                                  hipStream_t stream, const la_attn_ext *ext);
+
 /* LongNet dilated attention mixture (bf16 only).
  *  seg_lens, dil_rates  host int32[n_pairs]: segment length w_k >= 1 and dilation r_k >= 1.
  *                       1 <= n_pairs <= 16. The last segment of a pattern is

@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
 * :func:`la_dilated_forward` — LongNet's mixture of dilated attentions.
 * :func:`la_fixed_forward` — Sparse Transformer's fixed pattern (local block
   plus strided summary positions), LongNet's baseline.
+* :func:`la_attn_forward_noalloc` — ``la_attn_forward`` with the library's
+  fixed device scratch instead of a workspace (for callers that cannot allocate).
 * :func:`la_attn_workspace_size`, :func:`la_dilated_workspace_size`,
   :func:`la_fixed_workspace_size`,
   :func:`la_check_global_idx`, :func:`la_last_error`, :func:`la_version`.
@@ -76,7 +78,8 @@ _lib: Optional[ctypes.CDLL] = None
 EXPORTS = ("la_attn_forward", "la_dilated_forward", "la_fixed_forward", "la_attn_workspace_size",
            "la_dilated_workspace_size", "la_fixed_workspace_size", "la_check_global_idx",
            "la_last_error", "la_version", "la_attn_backward", "la_attn_backward_workspace_size",
-           "la_dilated_backward", "la_dilated_backward_workspace_size")
+           "la_dilated_backward", "la_dilated_backward_workspace_size",
+           "la_attn_forward_noalloc")
 
 
 def lib() -> ctypes.CDLL:
@@ -95,6 +98,8 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                   _i32p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(LaAttnExt)]
+    L.la_attn_forward_noalloc.restype = ctypes.c_int32
+    L.la_attn_forward_noalloc.argtypes = L.la_attn_forward.argtypes
     L.la_dilated_forward.restype = ctypes.c_int32
     L.la_dilated_forward.argtypes = [ctypes.POINTER(LaDims), ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
@@ -240,8 +245,11 @@ def bind_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
               kg: Optional[torch.Tensor] = None, vg: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, stream=None,
               want_lse: bool = True, rel_vec: Optional[torch.Tensor] = None,
-              seg_ids: Optional[torch.Tensor] = None) -> BoundCall:
+              seg_ids: Optional[torch.Tensor] = None, noalloc: bool = False) -> BoundCall:
     """Validate and marshal a :func:`la_attn_forward` call without issuing it.
+
+    ``noalloc`` marshals :func:`la_attn_forward_noalloc` instead (no workspace:
+    the library's fixed device scratch).
 
     ``rel_vec`` is a device fp32 ``[H, 2k+1, D]`` tensor of key-side label
     vectors (with or without ``rel_bias``, same k). ``seg_ids`` is a device
@@ -297,7 +305,12 @@ def bind_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         seg_ids = seg_ids.contiguous()
         sptr = seg_ids.data_ptr()
     sep = qg is not None
-    ws = _workspace(la_attn_workspace_size(dims, n_global, sep), q.device, workspace)
+    if noalloc:
+        if workspace is not None:
+            raise LaError(LA_EINVAL, "la_attn_forward_noalloc takes no workspace")
+        ws = None
+    else:
+        ws = _workspace(la_attn_workspace_size(dims, n_global, sep), q.device, workspace)
     ext = LaAttnExt(rk, _dev(qg, q, "qg") or None, _dev(kg, q, "kg") or None,
                     _dev(vg, q, "vg") or None, ws.data_ptr() if ws is not None else None,
                     ws.numel() if ws is not None else 0, vptr or None, sptr or None)
@@ -305,7 +318,8 @@ def bind_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             int(radius), dil, int(bool(causal)), rptr or None, out.data_ptr(),
             lse.data_ptr() if lse is not None else None, _stream(q, stream), ctypes.byref(ext))
     keep = (dims, ext, dil, q, k, v, global_idx, rel_bias, rel_vec, seg_ids, qg, kg, vg, ws)
-    return BoundCall(lib().la_attn_forward, args, keep, out, lse)
+    fn = lib().la_attn_forward_noalloc if noalloc else lib().la_attn_forward
+    return BoundCall(fn, args, keep, out, lse)
 
 
 def la_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -328,6 +342,24 @@ def la_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """
     return bind_attn(q, k, v, global_idx, radius, dilation, causal, rel_bias, out, lse, qg, kg,
                      vg, workspace, stream, want_lse, rel_vec, seg_ids)()
+
+
+def la_attn_forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            global_idx: Optional[torch.Tensor] = None, radius: int = 0,
+                            dilation: Optional[Sequence[int]] = None, causal: bool = False,
+                            rel_bias: Optional[torch.Tensor] = None,
+                            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                            qg: Optional[torch.Tensor] = None, kg: Optional[torch.Tensor] = None,
+                            vg: Optional[torch.Tensor] = None, stream=None, want_lse: bool = True,
+                            rel_vec: Optional[torch.Tensor] = None,
+                            seg_ids: Optional[torch.Tensor] = None
+                            ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """:func:`la_attn_forward` without a workspace: the library's fixed device
+    scratch (32 MiB per GPU) holds the global rows' partials. The C call
+    allocates nothing; ``out`` and ``lse`` are still allocated here when not
+    given. Calls that overlap in time on one GPU race."""
+    return bind_attn(q, k, v, global_idx, radius, dilation, causal, rel_bias, out, lse, qg, kg,
+                     vg, None, stream, want_lse, rel_vec, seg_ids, noalloc=True)()
 
 
 def bind_dilated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -89,6 +89,26 @@ def test_attn_argument_errors(L):
     assert _attn(L, LaDims(0, 2, 128, 64, la.LA_BF16), q=None, k=None, v=None, out=None) == la.LA_OK
 
 
+def test_noalloc_argument_errors(L):
+    d = LaDims(1, 2, 128, 64, la.LA_BF16)
+
+    def call(dims=d, gidx=None, n_global=0, ext=None):
+        return L.la_attn_forward_noalloc(ctypes.byref(dims), FAKE, FAKE, FAKE, gidx, n_global, 4,
+                                         None, 0, None, FAKE, None, None,
+                                         ctypes.byref(ext) if ext is not None else None)
+    # argument errors as for la_attn_forward
+    assert call(dims=LaDims(1, 2, 128, 32, la.LA_BF16)) == la.LA_EUNSUPPORTED
+    assert call(n_global=3) == la.LA_EINVAL
+    # no workspace may be passed
+    assert call(ext=LaAttnExt(0, None, None, None, FAKE, 1024)) == la.LA_EINVAL
+    assert "no workspace" in la.la_last_error()
+    # a call needing more than the 32 MiB device scratch is refused up front
+    big = LaDims(4, 16, 8192, 64, la.LA_BF16)
+    assert la.la_attn_workspace_size(big, 1024) > 32 << 20
+    assert call(dims=big, gidx=FAKE, n_global=1024) == la.LA_EUNSUPPORTED
+    assert "scratch" in la.la_last_error()
+
+
 def test_dilated_argument_errors(L):
     d = LaDims(1, 2, 256, 64, la.LA_BF16)
     w = (ctypes.c_int32 * 2)(64, 128)
