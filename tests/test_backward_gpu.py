@@ -5,7 +5,7 @@ oracle gets only q, k, v (and qg, kg, vg), the mask arguments and dout, and
 recomputes everything else in fp64.
 
 Bar, element-wise: |gpu - oracle| <= a * max|oracle| + b * |oracle| for every
-entry of every gradient tensor, with (a, b) = (1e-5, 1e-4) for fp32 inputs and
+entry of every gradient tensor, with (a, b) = (2e-6, 2e-5) for fp32 inputs and
 (5e-3, 1e-2) for bf16. For bf16, the forward's output O is rounded to bf16
 (relative 2^-9) before it enters D_i = dO_i . O_i, and its lse sums
 bf16-rounded probabilities (relative error up to 2^-8); P_ij = exp(s_ij - lse_i)
@@ -27,8 +27,8 @@ from sparse_long_sequence_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-TOL_ABS = {"f32": 1e-5, "bf16": 5e-3}  # times max |oracle| of the tensor
-TOL_REL = {"f32": 1e-4, "bf16": 1e-2}  # times |oracle| of the entry
+TOL_ABS = {"f32": 2e-6, "bf16": 5e-3}  # times max |oracle| of the tensor
+TOL_REL = {"f32": 2e-5, "bf16": 1e-2}  # times |oracle| of the entry
 TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
