@@ -78,7 +78,8 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.lo_attn_rows.restype = ctypes.c_int32
     lib.lo_attn_rows.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 6 + [
         _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int32, _f64p, _f64p,
-        ctypes.c_int32, _i32p, _i32p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int32]
+        ctypes.c_int32, _i32p, _i32p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int32,
+        _u8p, _u8p, ctypes.c_int32, ctypes.c_int32]
     lib.lo_fixed_rows.restype = ctypes.c_int32
     lib.lo_fixed_rows.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 3 + [
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int64, _f64p, _f64p,
@@ -160,19 +161,29 @@ def longnet_mult_rows(N: int, head: int, pairs: Sequence[Sequence[int]], causal:
     return m
 
 
+LABEL_DISTANCE = 0xFE  # a pair's usual clipped-distance label
+LABEL_MASKED = 0xFF    # any value >= the vocabulary size (but LABEL_DISTANCE) masks the pair
+
+
 def attn_rows(q, k, v, global_idx=(), radius: int = 0, dilation=None, causal: bool = False,
               rel_bias=None, qg=None, kg=None, vg=None, sel=None, n_threads: int = 0, lib=None,
-              rel_vec=None, seg=None):
+              rel_vec=None, seg=None, rel_k=None, glabel=None, llabel=None, seg_pieces: int = 0):
     """Band + global attention in fp64.
 
     ``q, k, v`` (and optional ``qg, kg, vg``) are ``[B,H,N,D]``. ``dilation`` is
-    per head (``None`` = all 1). ``rel_bias`` is ``[H, 2k+1]`` (a scalar per
-    label) and ``rel_vec`` ``[H, 2k+1, D]`` (a key-side vector per label); either,
-    both or neither may be given, with the same k. ``seg`` (``[B,N]`` int) gives
-    each token a segment (document) id: pairs across segments are masked. ``sel`` is an
-    ``[n,3]`` array of ``(b,h,i)`` rows (``None`` = all rows). Returns
-    ``(out [n,D], lse [n])`` as float64; with ``sel=None`` they are reshaped to
-    ``[B,H,N,D]`` and ``[B,H,N]``.
+    per head (``None`` = all 1). ``rel_bias`` is ``[H, V]`` (a scalar per
+    label) and ``rel_vec`` ``[H, V, D]`` (a key-side vector per label); either,
+    both or neither may be given. The vocabulary is the 2k+1 clipped-distance
+    labels (``V = 2k+1``, k from the table's width unless ``rel_k`` is given),
+    followed by ``V - 2k - 1`` structural labels. ``seg`` (``[B,N]`` int)
+    gives each token a segment id: pairs across segments are masked in the
+    pieces ``seg_pieces`` selects (bits g2g 1, g2l 2, l2g 4, l2l 8; 0 = all).
+    ``glabel`` (``[B, n_global, N]`` uint8) labels the pairs of each global query
+    (g2g, g2l) and ``llabel`` (``[B, N, n_global]`` uint8) the pairs of a non-global
+    query with each global key (l2g): a vocabulary index, ``LABEL_DISTANCE``, or
+    a masked pair (any other value). ``sel`` is an ``[n,3]`` array of ``(b,h,i)``
+    rows (``None`` = all rows). Returns ``(out [n,D], lse [n])`` as float64; with
+    ``sel=None`` they are reshaped to ``[B,H,N,D]`` and ``[B,H,N]``.
     """
     lib = lib or load()
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -190,25 +201,43 @@ def attn_rows(q, k, v, global_idx=(), radius: int = 0, dilation=None, causal: bo
     dil = None if dilation is None else _i32(dilation)
     if dil is not None and dil.shape != (H,):
         raise ValueError("dilation must have one entry per head")
-    rb, rk = None, 0
-    if rel_bias is not None:
-        rb = _f64(rel_bias)
-        if rb.ndim != 2 or rb.shape[0] != H or rb.shape[1] % 2 != 1:
-            raise ValueError("rel_bias must be [H, 2k+1]")
-        rk = (rb.shape[1] - 1) // 2
-    rv = None
-    if rel_vec is not None:
-        rv = _f64(rel_vec)
-        if rv.ndim != 3 or rv.shape[0] != H or rv.shape[1] % 2 != 1 or rv.shape[2] != D:
-            raise ValueError("rel_vec must be [H, 2k+1, D]")
-        if rb is not None and rv.shape[1] != rb.shape[1]:
-            raise ValueError("rel_bias and rel_vec need the same k")
-        rk = (rv.shape[1] - 1) // 2
+    rb = None if rel_bias is None else _f64(rel_bias)
+    rv = None if rel_vec is None else _f64(rel_vec)
+    V = None
+    if rb is not None:
+        if rb.ndim != 2 or rb.shape[0] != H:
+            raise ValueError("rel_bias must be [H, V]")
+        V = rb.shape[1]
+    if rv is not None:
+        if rv.ndim != 3 or rv.shape[0] != H or rv.shape[2] != D:
+            raise ValueError("rel_vec must be [H, V, D]")
+        if V is not None and rv.shape[1] != V:
+            raise ValueError("rel_bias and rel_vec need the same vocabulary")
+        V = rv.shape[1]
+    rk = 0
+    if V is not None:
+        if rel_k is None:
+            if V % 2 != 1:
+                raise ValueError("give rel_k with a vocabulary of structural labels")
+            rel_k = (V - 1) // 2
+        rk = int(rel_k)
+        if V < 2 * rk + 1:
+            raise ValueError("the vocabulary holds fewer than 2k+1 labels")
+    nlab = 0 if V is None else V
     sg = None
     if seg is not None:
         sg = _i32(seg)
         if sg.shape != (B, N):
             raise ValueError("seg must be [B, N]")
+    gl = ll = None
+    if glabel is not None:
+        gl = np.ascontiguousarray(np.asarray(glabel, dtype=np.uint8))
+        if gl.shape != (B, g.shape[0], N):
+            raise ValueError("glabel must be [B, n_global, N]")
+    if llabel is not None:
+        ll = np.ascontiguousarray(np.asarray(llabel, dtype=np.uint8))
+        if ll.shape != (B, N, g.shape[0]):
+            raise ValueError("llabel must be [B, N, n_global]")
     s, n = _sel(sel, B, H, N)
     out = np.zeros((n, D), dtype=np.float64)
     lse = np.zeros((n,), dtype=np.float64)
@@ -216,7 +245,8 @@ def attn_rows(q, k, v, global_idx=(), radius: int = 0, dilation=None, causal: bo
                           _p(kg, _f64p), _p(vg, _f64p), _p(g, _i32p), g.shape[0], radius,
                           _p(dil, _i32p), int(causal), _p(rb, _f64p), _p(rv, _f64p), rk,
                           _p(sg, _i32p), _p(s, _i32p), n,
-                          _p(out, _f64p), _p(lse, _f64p), n_threads)
+                          _p(out, _f64p), _p(lse, _f64p), n_threads, _p(gl, _u8p), _p(ll, _u8p),
+                          nlab, int(seg_pieces))
     if rc != 0:
         raise ValueError("lo_attn_rows rejected its arguments")
     if sel is None:

@@ -127,6 +127,11 @@ int32_t longnet_mult(int32_t i, int32_t j, int32_t head, const int32_t* w, const
   return m;
 }
 
+// A pair's label in the per-pair label inputs: its usual clipped-distance
+// label (kLabelDistance) or an index into the label vocabulary; every other
+// value masks the pair.
+constexpr int32_t kLabelDistance = 0xFE;
+
 // ---------------------------------------------------------------------------
 // Masked dense softmax attention of one query row (the definition above).
 // weight[j] is c_ij (0 excludes the key). bias(j) adds to the scaled logit.
@@ -244,24 +249,49 @@ int32_t lo_longnet_mult_rows(int32_t N, int32_t head, const int32_t* w, const in
 // Position Encoding", Steps 1-3: labels clip j - i at k; one vector per label
 // and head). Either, both or neither may be given. sel: n_sel (b,h,i) triples
 // or null for all B*H*N rows. out: [n_sel][D]; lse: [n_sel].
+//
+// Per-instance per-piece masks and structural labels (ETC page, §3.4
+// "Global-Local Attention": the binary masks M^{g2g}, M^{g2l}, M^{l2g},
+// M^{l2l}; "Per-instance attention masks"; "Relative Position Encoding",
+// Step 1: labels for relations such as "token belongs to this sentence", and
+// its implementation note: one label per (i, j) pair, gathered). The piece of
+// a pair follows from whether i and j are global. glabel [B][n_global][N]
+// gives the label of each pair whose query is the g-th global token (g2g,
+// g2l); llabel [B][N][n_global] the label of each pair of a non-global query
+// and the g-th global key (l2g). A label is an index into the vocabulary of
+// n_labels entries (rel_bias [H][n_labels], rel_vec [H][n_labels][D];
+// n_labels == 0: the 2k+1 distance labels alone), kLabelDistance for the
+// pair's usual label (the clipped distance for same-kind pairs, none for mixed
+// pairs), or any other value for a masked pair (M = 0). An explicit label
+// applies to any pair, mixed ones included. seg_pieces selects the pieces that
+// segment ids mask (bits g2g 1, g2l 2, l2g 4, l2l 8; 0 means all four).
 int32_t lo_attn_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q, const double* k,
                      const double* v, const double* qg, const double* kg, const double* vg,
                      const int32_t* gidx, int32_t n_global, int32_t radius, const int32_t* dilation,
                      int32_t causal, const double* rel_bias, const double* rel_vec, int32_t rel_k,
                      const int32_t* seg, const int32_t* sel, int64_t n_sel, double* out,
-                     double* lse, int32_t n_threads) {
+                     double* lse, int32_t n_threads, const uint8_t* glabel,
+                     const uint8_t* llabel, int32_t n_labels, int32_t seg_pieces) {
   if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || radius < 0 || n_global < 0) return -1;
   if (!q || !k || !v || !out || !lse) return -1;
   if ((qg || kg || vg) && !(qg && kg && vg)) return -1;
   if (n_global > 0 && !gidx) return -1;
   if ((rel_bias || rel_vec) && rel_k < 0) return -1;
+  const int32_t V = n_labels > 0 ? n_labels : 2 * rel_k + 1;  // vocabulary size
+  if (n_labels > 0 && n_labels < 2 * rel_k + 1) return -1;
+  if ((glabel || llabel) && n_global == 0) return -1;
+  const int32_t pieces = seg_pieces ? seg_pieces : 15;
   if (dilation)
     for (int32_t h = 0; h < H; ++h)
       if (dilation[h] < 1) return -1;
   const int64_t rows = sel ? n_sel : (int64_t)B * H * N;
   std::vector<uint8_t> is_glob(N, 0);
+  std::vector<int32_t> grank(N, -1);  // index of a global position in global_idx
   for (int32_t g = 0; g < n_global; ++g)
-    if (gidx[g] >= 0 && gidx[g] < N) is_glob[gidx[g]] = 1;
+    if (gidx[g] >= 0 && gidx[g] < N) {
+      is_glob[gidx[g]] = 1;
+      grank[gidx[g]] = g;
+    }
   parallel_rows(rows, n_threads, [&](int64_t x) {
     int32_t b, h, i;
     decode_row(sel, x, H, N, b, h, i);
@@ -274,22 +304,34 @@ int32_t lo_attn_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q
     const double* kb = (sep ? kg : k) + head_off;
     const double* vb = (sep ? vg : v) + head_off;
     std::vector<double> weight(N);
+    std::vector<int32_t> label(N, kLabelDistance);  // each pair's label
     const int32_t* sb = seg ? seg + (size_t)b * N : nullptr;
     for (int32_t j = 0; j < N; ++j) {  // the explicit mask row c_i,:
-      weight[j] = mask_entry(i, j, ig, is_glob[j] != 0, radius, dil, causal);
-      if (sb && sb[j] != sb[i]) weight[j] = 0.0;  // another document
+      const bool jg = is_glob[j] != 0;
+      weight[j] = mask_entry(i, j, ig, jg, radius, dil, causal);
+      const int32_t piece = ig ? (jg ? 1 : 2) : (jg ? 4 : 8);  // g2g, g2l, l2g, l2l
+      if (sb && (pieces & piece) && sb[j] != sb[i]) weight[j] = 0.0;  // another segment
+      if (ig && glabel)
+        label[j] = glabel[((size_t)b * n_global + grank[i]) * N + j];
+      else if (!ig && jg && llabel)
+        label[j] = llabel[((size_t)b * N + i) * n_global + grank[j]];
+      if (label[j] != kLabelDistance && label[j] >= V) weight[j] = 0.0;  // M = 0
     }
-    const double* tab = rel_bias ? rel_bias + (size_t)h * (2 * rel_k + 1) : nullptr;
-    const double* vec = rel_vec ? rel_vec + (size_t)h * (2 * rel_k + 1) * D : nullptr;
+    const double* tab = rel_bias ? rel_bias + (size_t)h * V : nullptr;
+    const double* vec = rel_vec ? rel_vec + (size_t)h * V * D : nullptr;
     const double scale = 1.0 / std::sqrt((double)D);
     auto bias = [&](int32_t j) -> double {
       if (!tab && !vec) return 0.0;
-      if ((is_glob[j] != 0) != ig) return 0.0;  // mixed global/non-global pair
-      int64_t dlt = (int64_t)j - i;
-      dlt = std::max<int64_t>(-rel_k, std::min<int64_t>(rel_k, dlt));
-      double b = tab ? tab[dlt + rel_k] : 0.0;
+      int32_t l = label[j];
+      if (l == kLabelDistance) {
+        if ((is_glob[j] != 0) != ig) return 0.0;  // mixed global/non-global pair
+        int64_t dlt = (int64_t)j - i;
+        dlt = std::max<int64_t>(-rel_k, std::min<int64_t>(rel_k, dlt));
+        l = (int32_t)(dlt + rel_k);
+      }
+      double b = tab ? tab[l] : 0.0;
       if (vec) {  // q_i . a_l / sqrt(D): the key-side vector's share of the logit
-        const double* al = vec + (size_t)(dlt + rel_k) * D;
+        const double* al = vec + (size_t)l * D;
         double dot = 0.0;
         for (int32_t d = 0; d < D; ++d) dot += qi[d] * al[d];
         b += dot * scale;

@@ -772,6 +772,201 @@ def pin_longnet_backward_selected(lib):
         assert np.abs(sv[::-1] - dv.reshape(-1, D)).max() < 1e-12, pairs
 
 
+DIST, MASK = oracle.LABEL_DISTANCE, oracle.LABEL_MASKED
+
+
+def bf_etc_structured(qg_, kg_, vg_, ql, kl, vl, r, tab, vec, M, L, kk):
+    """ETC global-local attention from its four pieces with explicit per-piece
+    masks M[piece] (1 = edge) and per-pair labels L[piece] (a vocabulary index,
+    or None for the clipped-distance label); the logit of an edge with label l
+    is q_i . (k_j + a_l) / sqrt(D) + b_l. l2l also needs |i - j| <= r."""
+    ng, nl = len(qg_), len(ql)
+    D = len(ql[0])
+    sc = 1.0 / math.sqrt(D)
+
+    def logit(qi, kj, lab):
+        e = sc * _dot(qi, kj)
+        if lab is not None:
+            e += tab[lab] + sc * _dot(qi, vec[lab])
+        return e
+
+    def dist(i, j):
+        return max(-kk, min(kk, j - i)) + kk
+
+    out, lse = [], []
+    for i in range(ng):  # one softmax over [g2g ; g2l]
+        e, vals = [], []
+        for j in range(ng):
+            if M["g2g"][i][j]:
+                lab = L["g2g"][i][j]
+                e.append(logit(qg_[i], kg_[j], dist(i, j) if lab is None else lab))
+                vals.append(vg_[j])
+        for j in range(nl):
+            if M["g2l"][i][j]:
+                e.append(logit(qg_[i], kl[j], L["g2l"][i][j]))
+                vals.append(vl[j])
+        out_i, lse_i = _softmax_mix(e, vals, D)
+        out.append(out_i)
+        lse.append(lse_i)
+    for i in range(nl):  # one softmax over [l2g ; l2l]
+        e, vals = [], []
+        for j in range(ng):
+            if M["l2g"][i][j]:
+                e.append(logit(ql[i], kg_[j], L["l2g"][i][j]))
+                vals.append(vg_[j])
+        for j in range(max(0, i - r), min(nl, i + r + 1)):
+            if M["l2l"][i][j]:
+                e.append(logit(ql[i], kl[j], dist(i, j)))
+                vals.append(vl[j])
+        out_i, lse_i = _softmax_mix(e, vals, D)
+        out.append(out_i)
+        lse.append(lse_i)
+    return np.array(out), np.array(lse)
+
+
+def _softmax_mix(e, vals, D):
+    if not e:
+        return [0.0] * D, -math.inf
+    Mx = max(e)
+    p = [math.exp(x - Mx) for x in e]
+    Z = sum(p)
+    return [sum(p[t] * vals[t][c] for t in range(len(p))) / Z for c in range(D)], Mx + math.log(Z)
+
+
+def pin_etc_structured_pieces(lib):
+    """Per-instance per-piece masks and structural labels (ETC page, 3.4
+    "Per-instance attention masks", "How Global-Local Attention Encodes
+    Structured Inputs", "Relative Position Encoding" Step 1): two contexts of
+    two sentences each; global input = CLS, one token per context, one per
+    sentence, one candidate answer; hard g2l (a sentence token sees only its
+    sentence's word pieces), no cross-context g2g for sentence tokens (context
+    tokens exempt), no cross-context l2l; labels belongs / does-not-belong on
+    sentence <-> word-piece edges, mention on candidate <-> mention edges,
+    part-of on sentence -> context edges. The four-piece brute force with the
+    explicit matrices equals the oracle's one concatenated call."""
+    rng = np.random.default_rng(27)
+    D, kk, r = 4, 2, 2
+    sent = [0] * 4 + [1] * 3 + [2] * 5 + [3] * 4   # word piece -> sentence
+    ctx_of_sent = [0, 0, 1, 1]
+    nl = len(sent)
+    ctx = [ctx_of_sent[s_] for s_ in sent]
+    # global tokens: 0 CLS, 1-2 contexts, 3-6 sentences, 7 candidate
+    kind = ["cls", "ctx", "ctx", "sent", "sent", "sent", "sent", "cand"]
+    gctx = [None, 0, 1, 0, 0, 1, 1, None]
+    gsent = [None, None, None, 0, 1, 2, 3, None]
+    mention = {5, 12}          # word pieces mentioning the candidate
+    ng = len(kind)
+    V = 2 * kk + 1 + 4
+    BEL, NOT, MEN, PART = 2 * kk + 1, 2 * kk + 2, 2 * kk + 3, 2 * kk + 4
+    M = {p_: [[1] * (ng if p_.endswith("2g") else nl) for _ in range(ng if p_[0] == "g" else nl)]
+         for p_ in ("g2g", "g2l", "l2g", "l2l")}
+    L = {p_: [[None] * (ng if p_.endswith("2g") else nl) for _ in range(ng if p_[0] == "g" else nl)]
+         for p_ in ("g2g", "g2l", "l2g")}
+    for g in range(ng):
+        for j in range(nl):
+            if kind[g] == "sent":
+                M["g2l"][g][j] = int(sent[j] == gsent[g])            # hard g2l
+                L["g2l"][g][j] = BEL if sent[j] == gsent[g] else NOT
+            if kind[g] == "cand" and j in mention:
+                L["g2l"][g][j] = MEN
+        for g2 in range(ng):
+            if kind[g] == "sent" and kind[g2] == "sent" and gctx[g] != gctx[g2]:
+                M["g2g"][g][g2] = 0                                 # cross-context sentence pair
+            if kind[g] == "sent" and kind[g2] == "ctx" and gctx[g] == gctx[g2]:
+                L["g2g"][g][g2] = PART
+    for i in range(nl):
+        for g in range(ng):
+            if kind[g] == "sent":
+                L["l2g"][i][g] = BEL if sent[i] == gsent[g] else NOT
+            if kind[g] == "cand" and i in mention:
+                L["l2g"][i][g] = MEN
+        for j in range(nl):
+            M["l2l"][i][j] = int(ctx[i] == ctx[j])                   # no cross-context l2l
+    q = rng.standard_normal((1, 2, ng + nl, D))
+    k = rng.standard_normal((1, 2, ng + nl, D))
+    v = rng.standard_normal((1, 2, ng + nl, D))
+    tab = 0.3 * rng.standard_normal((2, V))
+    vec = 0.3 * rng.standard_normal((2, V, D))
+    N = ng + nl
+    glabel = np.full((1, ng, N), DIST, dtype=np.uint8)
+    llabel = np.full((1, N, ng), DIST, dtype=np.uint8)
+    for g in range(ng):
+        for j in range(N):
+            piece, jj = ("g2g", j) if j < ng else ("g2l", j - ng)
+            lab = L[piece][g][jj]
+            glabel[0, g, j] = MASK if not M[piece][g][jj] else (DIST if lab is None else lab)
+    for i in range(nl):
+        for g in range(ng):
+            lab = L["l2g"][i][g]
+            llabel[0, ng + i, g] = MASK if not M["l2g"][i][g] else (DIST if lab is None else lab)
+    seg = np.array([[0] * ng + [c_ + 1 for c_ in ctx]])  # l2l only
+    o, l = oracle.attn_rows(q, k, v, range(ng), r, rel_bias=tab, rel_vec=vec, rel_k=kk,
+                            glabel=glabel, llabel=llabel, seg=seg, seg_pieces=8, lib=lib)
+    for h in range(2):
+        ob, lb = bf_etc_structured(q[0, h, :ng].tolist(), k[0, h, :ng].tolist(),
+                                   v[0, h, :ng].tolist(), q[0, h, ng:].tolist(),
+                                   k[0, h, ng:].tolist(), v[0, h, ng:].tolist(), r, tab[h],
+                                   vec[h].tolist(), M, L, kk)
+        assert np.abs(o[0, h] - ob).max() < 1e-12, h
+        assert np.abs(l[0, h] - lb).max() < 1e-12, h
+
+
+def pin_labels_scattered_globals(lib):
+    """Label inputs with scattered global positions (Longformer layout, a
+    dilated head, separate global projections): against masked softmax over an
+    explicit label matrix built position by position; and all-default labels
+    equal no label input at all."""
+    rng = np.random.default_rng(28)
+    B, H, N, D, R, kk = 2, 2, 30, 4, 3, 2
+    G = [2, 9, 10, 23]
+    V = 2 * kk + 1 + 2
+    q, k, v = rand_qkv(rng, B, H, N, D)
+    qg, kg, vg = rand_qkv(rng, B, H, N, D)
+    tab = 0.3 * rng.standard_normal((H, V))
+    vec = 0.3 * rng.standard_normal((H, V, D))
+    glabel = rng.choice([0, 3, V - 1, V - 2, DIST, DIST, MASK], size=(B, len(G), N)).astype(np.uint8)
+    llabel = rng.choice([1, V - 1, DIST, MASK, 200], size=(B, N, len(G))).astype(np.uint8)
+    dil = [1, 2]
+    o, l = oracle.attn_rows(q, k, v, G, R, dil, False, tab, qg, kg, vg, rel_vec=vec, rel_k=kk,
+                            glabel=glabel, llabel=llabel, lib=lib)
+    sc = 1.0 / math.sqrt(D)
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                ig = i in G
+                Q, K_, V_ = (qg, kg, vg) if ig else (q, k, v)
+                e, vals = [], []
+                for j in range(N):
+                    jg = j in G
+                    band = (j - i) % dil[h] == 0 and abs(j - i) <= dil[h] * R
+                    if not (ig or jg or band):
+                        continue
+                    if ig:
+                        lab = int(glabel[b, G.index(i), j])
+                    elif jg:
+                        lab = int(llabel[b, i, G.index(j)])
+                    else:
+                        lab = DIST
+                    if lab != DIST and lab >= V:
+                        continue                       # masked pair
+                    if lab == DIST:
+                        lab = (max(-kk, min(kk, j - i)) + kk) if ig == jg else None
+                    x = sc * _dot(Q[b, h, i], K_[b, h, j])
+                    if lab is not None:
+                        x += tab[h, lab] + sc * _dot(Q[b, h, i], vec[h, lab])
+                    e.append(x)
+                    vals.append(V_[b, h, j].tolist())
+                ob, lb = _softmax_mix(e, vals, D)
+                assert np.abs(o[b, h, i] - ob).max() < 1e-12, (b, h, i)
+                assert (np.isneginf(lb) and np.isneginf(l[b, h, i])) or abs(l[b, h, i] - lb) < 1e-12
+    dflt = np.full_like(glabel, DIST), np.full_like(llabel, DIST)
+    o1, l1 = oracle.attn_rows(q, k, v, G, R, dil, False, tab[:, :2 * kk + 1], qg, kg, vg,
+                              rel_vec=vec[:, :2 * kk + 1], glabel=dflt[0], llabel=dflt[1], lib=lib)
+    o2, l2 = oracle.attn_rows(q, k, v, G, R, dil, False, tab[:, :2 * kk + 1], qg, kg, vg,
+                              rel_vec=vec[:, :2 * kk + 1], lib=lib)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 PINS = [pin_mask_matches_enumeration, pin_counts_closed_form, pin_counts_full_workloads,
         pin_longnet_counts, pin_longnet_worked_example, pin_longnet_offsets_partition,
         pin_dense_special_cases, pin_global_rows_are_full_rows, pin_brute_force_band,
@@ -781,7 +976,7 @@ PINS = [pin_mask_matches_enumeration, pin_counts_closed_form, pin_counts_full_wo
         pin_rows_sum_to_one, pin_uncovered_rows, pin_sampled_rows_match_full,
         pin_backward_finite_differences, pin_backward_dense_autograd,
         pin_backward_shift_invariants, pin_longnet_backward, pin_longnet_per_pattern_outputs,
-        pin_longnet_backward_selected]
+        pin_longnet_backward_selected, pin_etc_structured_pieces, pin_labels_scattered_globals]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -796,10 +991,9 @@ MUTANTS = [
     ("exclusive-window-end", "return steps >= -(int64_t)radius && steps <= (int64_t)radius;",
      "return steps >= -(int64_t)radius && steps < (int64_t)radius;"),
     ("dropped-scale", "logit[j] = dot * scale + bias(j);", "logit[j] = dot + bias(j);"),
-    ("bias-index-sign", "double b = tab ? tab[dlt + rel_k] : 0.0;",
-     "double b = tab ? tab[rel_k - dlt] : 0.0;"),
-    ("segments-ignored-by-global-rows", "if (sb && sb[j] != sb[i]) weight[j] = 0.0;",
-     "if (sb && sb[j] != sb[i] && !ig) weight[j] = 0.0;"),
+    ("bias-index-sign", "l = (int32_t)(dlt + rel_k);", "l = (int32_t)(rel_k - dlt);"),
+    ("segments-ignored-by-global-rows", "if (sb && (pieces & piece) && sb[j] != sb[i]) weight[j] = 0.0;",
+     "if (sb && (pieces & piece) && sb[j] != sb[i] && !ig) weight[j] = 0.0;"),
     ("segments-of-another-batch-row", "const int32_t* sb = seg ? seg + (size_t)b * N : nullptr;",
      "const int32_t* sb = seg ? seg : nullptr;"),
     ("fixed-one-subblock-for-all-heads", "const int32_t hp = head % std::max(1, l / c);",
@@ -807,8 +1001,8 @@ MUTANTS = [
     ("fixed-run-one-too-long", "return o >= t && o < t + c;", "return o >= t && o <= t + c;"),
     ("fixed-ignores-causal", "  if (causal && j > i) return false;\n  if (i / l == j / l) return true;",
      "  if (i / l == j / l) return true;"),
-    ("relvec-label-sign", "const double* al = vec + (size_t)(dlt + rel_k) * D;",
-     "const double* al = vec + (size_t)(rel_k - dlt) * D;"),
+    ("relvec-label-sign", "const double* al = vec + (size_t)l * D;",
+     "const double* al = vec + (size_t)(2 * rel_k - l) * D;"),
     ("relvec-unscaled", "b += dot * scale;", "b += dot;"),
     ("relvec-against-key", "for (int32_t d = 0; d < D; ++d) dot += qi[d] * al[d];",
      "for (int32_t d = 0; d < D; ++d) dot += kb[(size_t)j * D + d] * al[d];"),
@@ -844,6 +1038,15 @@ MUTANTS = [
      "row.Di += row.c[j] * std::exp(row.logit[j] - row.lse) * dp;",
      "row.Di += std::exp(row.logit[j] - row.lse) * dp;"),
     ("selected-dv-from-dS", "dvj[d] += P * doi[d];", "dvj[d] += g * doi[d];"),
+    ("l2g-labels-transposed", "label[j] = llabel[((size_t)b * N + i) * n_global + grank[j]];",
+     "label[j] = llabel[((size_t)b * n_global + grank[j]) * N + i];"),
+    ("global-labels-by-position", "label[j] = glabel[((size_t)b * n_global + grank[i]) * N + j];",
+     "label[j] = glabel[((size_t)b * n_global + i) * N + j];"),
+    ("masked-label-ignored", "if (label[j] != kLabelDistance && label[j] >= V) weight[j] = 0.0;  // M = 0", ""),
+    ("segments-mask-every-piece", "const int32_t pieces = seg_pieces ? seg_pieces : 15;",
+     "const int32_t pieces = 15;"),
+    ("explicit-labels-same-kind-only", "      if (!tab && !vec) return 0.0;\n      int32_t l = label[j];",
+     "      if (!tab && !vec) return 0.0;\n      if ((is_glob[j] != 0) != ig) return 0.0;\n      int32_t l = label[j];"),
     ("selected-dq-unscaled", "for (int32_t d = 0; d < D; ++d) dqi[d] += g * k[off + (size_t)j * D + d] * scale;",
      "for (int32_t d = 0; d < D; ++d) dqi[d] += g * k[off + (size_t)j * D + d];"),
 ]
