@@ -72,6 +72,10 @@ class Call:
         self.rb = d(inp.rel_bias)
         self.rv = d(inp.rel_vec)
         self.seg = d(inp.seg)
+        self.lab = {}
+        if inp.glabel is not None or inp.llabel is not None or inp.seg_pieces:
+            self.lab = dict(glabel=d(inp.glabel), llabel=d(inp.llabel),
+                            seg_pieces=inp.seg_pieces, rel_k=inp.rel_k)
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty(self.q.shape[:3], dtype=torch.float32, device=dev)
         self.g = (torch.tensor(w.global_idx, dtype=torch.int32, device=dev)
@@ -95,7 +99,7 @@ class Call:
             self.bound = la.bind_attn(self.q, self.k, self.v, self.g, w.radius, w.dilation,
                                       w.causal, self.rb, out=self.out, lse=self.lse, qg=self.qg,
                                       rel_vec=self.rv, seg_ids=self.seg,
-                                      kg=self.kg, vg=self.vg, workspace=self.ws)
+                                      kg=self.kg, vg=self.vg, workspace=self.ws, **self.lab)
 
     def __call__(self):
         self.bound()

@@ -80,10 +80,11 @@ typedef struct {
 
 /* Optional extras of la_attn_forward; pass NULL for none. */
 typedef struct {
-  /* rel_bias holds H*(2*rel_k+1) fp32 entries; entry [h][clamp(j-i,-rel_k,rel_k)+rel_k]
-   * is added to the logit of every pair (i,j) whose members are of the same kind
-   * (both global or both non-global). Required (> 0) iff rel_bias != NULL or
-   * rel_vec != NULL. */
+  /* rel_bias holds H*V fp32 entries (V = n_labels, or 2*rel_k+1 when that is
+   * 0); entry [h][clamp(j-i,-rel_k,rel_k)+rel_k] is added to the logit of every
+   * pair (i,j) whose members are of the same kind (both global or both
+   * non-global), unless a label matrix gives the pair another label. Required
+   * (> 0) iff rel_bias != NULL or rel_vec != NULL. */
   int32_t rel_k;
   /* Separate projections for the global rows: all three or none, dims as q.
    * A global row i then uses qg_i, kg_j, vg_j for every key j; non-global rows
@@ -99,19 +100,46 @@ typedef struct {
   void *workspace;
   size_t workspace_bytes;
   /* Key-side relative-position vectors (ETC page, §3.4 "Relative Position
-   * Encoding", Steps 2-3): device fp32 [H][2*rel_k+1][D], 16-byte aligned, or
+   * Encoding", Steps 2-3): device fp32 [H][V][D] (V as for rel_bias), 16-byte aligned, or
    * NULL. For a same-kind pair (i,j) with label l = clamp(j-i,-rel_k,rel_k) the
    * logit becomes q_i . (k_j + a_{h,l}) / sqrt(D) (plus rel_bias when both are
    * given). The kernels precompute q_i . a_{h,l} per query row and label, as the
-   * page's implementation note describes; such calls use 2*rel_k+1 fp32 of LDS
-   * per query row of a workgroup beyond the usual. */
+   * page's implementation note describes; such calls use V fp32 of LDS per
+   * query row of a workgroup beyond the usual. */
   const float *rel_vec;
   /* Per-instance segment masks for packed documents (ETC page, §3.4
    * "Per-instance attention masks"): device int32 [B][N], a segment id per
    * position, or NULL. A pair (i,j) whose positions carry different ids is
    * excluded in every piece (band, global rows, global columns), on top of the
-   * pattern. Any int32 values; a segment need not be contiguous. */
+   * pattern. Any int32 values; a segment need not be contiguous. seg_pieces
+   * (below) can restrict this to some pieces. */
   const int32_t *seg_ids;
+  /* Per-instance per-piece masks and structural relation labels for the pieces
+   * with a global token (ETC page, §3.4 "Global-Local Attention": a binary mask
+   * M per piece; "Per-instance attention masks": hard g2l masking;
+   * "Relative Position Encoding", Step 1: labels for structural relations, and
+   * its implementation note: a label gathered per pair). The piece of a pair
+   * (i,j) follows from whether i and j are in global_idx.
+   *  glabel   device uint8 [B][n_global][N] or NULL: the label of every pair
+   *           whose query is global_idx[g] (g2g and g2l pieces);
+   *  llabel   device uint8 [B][N][n_global] or NULL: the label of every pair of
+   *           a non-global query i and the key global_idx[g] (l2g piece).
+   * A label value l < n_labels selects entry l of rel_bias [H][n_labels] and of
+   * rel_vec [H][n_labels][D] for that pair, whatever its piece; 0xFE keeps the
+   * pair's usual label (the clipped distance for same-kind pairs, none for
+   * mixed pairs); any other value masks the pair (M = 0). Entries of pairs the
+   * pattern excludes are not read. Label matrices need n_global > 0 and at most
+   * 2^31 entries per batch row.
+   *  n_labels   size of the label vocabulary: 0 (the 2*rel_k+1 distance labels
+   *             only) or in [2*rel_k+1, 64]; the structural labels follow the
+   *             distance labels. Needs rel_bias or rel_vec when non-zero.
+   *  seg_pieces the pieces seg_ids mask, as bits g2g 1, g2l 2, l2g 4, l2l 8
+   *             (0 = all four: packed documents), e.g. 8 to mask l2l across
+   *             contexts while every word piece still reads every global token. */
+  const uint8_t *glabel;
+  const uint8_t *llabel;
+  int32_t n_labels;
+  int32_t seg_pieces;
 } la_attn_ext;
 
 /* Optional extras of la_dilated_forward; pass NULL for none. */
@@ -266,7 +294,8 @@ la_status la_check_global_idx(const int32_t *global_idx, int32_t n_global, int32
 /* Message of the last non-OK status on this thread ("" if none). */
 const char *la_last_error(void);
 
-/* ABI version of this library. */
+/* ABI version of this library (2: la_attn_ext carries label matrices, n_labels
+ * and seg_pieces after seg_ids). */
 int32_t la_version(void);
 
 #ifdef __cplusplus

@@ -56,7 +56,13 @@ class LaAttnExt(ctypes.Structure):
     _fields_ = [("rel_k", ctypes.c_int32), ("qg", ctypes.c_void_p), ("kg", ctypes.c_void_p),
                 ("vg", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("rel_vec", ctypes.c_void_p),
-                ("seg_ids", ctypes.c_void_p)]
+                ("seg_ids", ctypes.c_void_p), ("glabel", ctypes.c_void_p),
+                ("llabel", ctypes.c_void_p), ("n_labels", ctypes.c_int32),
+                ("seg_pieces", ctypes.c_int32)]
+
+
+LABEL_DISTANCE = 0xFE  # a pair keeps its usual clipped-distance label
+LABEL_MASKED = 0xFF    # a masked pair (any value >= the vocabulary size but 0xFE)
 
 
 class LaDilatedExt(ctypes.Structure):
@@ -245,8 +251,17 @@ def bind_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
               kg: Optional[torch.Tensor] = None, vg: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, stream=None,
               want_lse: bool = True, rel_vec: Optional[torch.Tensor] = None,
-              seg_ids: Optional[torch.Tensor] = None, noalloc: bool = False) -> BoundCall:
+              seg_ids: Optional[torch.Tensor] = None, noalloc: bool = False,
+              rel_k: Optional[int] = None, glabel: Optional[torch.Tensor] = None,
+              llabel: Optional[torch.Tensor] = None, seg_pieces: int = 0) -> BoundCall:
     """Validate and marshal a :func:`la_attn_forward` call without issuing it.
+
+    With structural labels the tables are ``rel_bias [H, V]`` and ``rel_vec
+    [H, V, D]`` for a vocabulary of V labels (the 2k+1 distance labels, then
+    the structural ones; give ``rel_k`` when V > 2k+1). ``glabel`` (device
+    uint8 ``[B, n_global, N]``) and ``llabel`` (``[B, N, n_global]``) give per-pair
+    labels of the pieces with a global token; ``seg_pieces`` selects the pieces
+    ``seg_ids`` masks (bits g2g 1, g2l 2, l2g 4, l2l 8; 0 = all).
 
     ``noalloc`` marshals :func:`la_attn_forward_noalloc` instead (no workspace:
     the library's fixed device scratch).
@@ -276,27 +291,44 @@ def bind_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     dil = None if dilation is None else _host_i32(dilation)
     if dilation is not None and len(dilation) != dims.H:
         raise LaError(LA_EINVAL, "dilation needs one entry per head")
-    rk = 0
+    V = None
     rptr = 0
     if rel_bias is not None:
         if rel_bias.dtype != torch.float32 or not rel_bias.is_cuda or rel_bias.dim() != 2 \
-                or rel_bias.shape[0] != dims.H or rel_bias.shape[1] % 2 != 1:
-            raise LaError(LA_EINVAL, "rel_bias must be a device fp32 [H, 2k+1] tensor")
-        rk = (rel_bias.shape[1] - 1) // 2
+                or rel_bias.shape[0] != dims.H:
+            raise LaError(LA_EINVAL, "rel_bias must be a device fp32 [H, V] tensor")
+        V = rel_bias.shape[1]
         rel_bias = rel_bias.contiguous()
         rptr = rel_bias.data_ptr()
     vptr = 0
     if rel_vec is not None:
         if rel_vec.dtype != torch.float32 or not rel_vec.is_cuda or rel_vec.dim() != 3 \
-                or rel_vec.shape[0] != dims.H or rel_vec.shape[1] % 2 != 1 \
-                or rel_vec.shape[2] != dims.D:
-            raise LaError(LA_EINVAL, "rel_vec must be a device fp32 [H, 2k+1, D] tensor")
-        kv = (rel_vec.shape[1] - 1) // 2
-        if rel_bias is not None and kv != rk:
-            raise LaError(LA_EINVAL, "rel_bias and rel_vec need the same k")
-        rk = kv
+                or rel_vec.shape[0] != dims.H or rel_vec.shape[2] != dims.D:
+            raise LaError(LA_EINVAL, "rel_vec must be a device fp32 [H, V, D] tensor")
+        if V is not None and rel_vec.shape[1] != V:
+            raise LaError(LA_EINVAL, "rel_bias and rel_vec need the same vocabulary")
+        V = rel_vec.shape[1]
         rel_vec = rel_vec.contiguous()
         vptr = rel_vec.data_ptr()
+    rk, n_labels = 0, 0
+    if V is not None:
+        if rel_k is None:
+            if V % 2 != 1:
+                raise LaError(LA_EINVAL, "give rel_k with a vocabulary of structural labels")
+            rel_k = (V - 1) // 2
+        rk = int(rel_k)
+        n_labels = 0 if V == 2 * rk + 1 else V
+    lptr = []
+    for name, t, shape in (("glabel", glabel, (dims.B, n_global, dims.N)),
+                           ("llabel", llabel, (dims.B, dims.N, n_global))):
+        if t is None:
+            lptr.append(None)
+            continue
+        if t.dtype != torch.uint8 or not t.is_cuda or tuple(t.shape) != shape:
+            raise LaError(LA_EINVAL, f"{name} must be a device uint8 {list(shape)} tensor")
+        lptr.append(t.contiguous().data_ptr())
+    glabel = None if glabel is None else glabel.contiguous()
+    llabel = None if llabel is None else llabel.contiguous()
     sptr = 0
     if seg_ids is not None:
         if seg_ids.dtype != torch.int32 or not seg_ids.is_cuda \
@@ -313,11 +345,13 @@ def bind_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         ws = _workspace(la_attn_workspace_size(dims, n_global, sep), q.device, workspace)
     ext = LaAttnExt(rk, _dev(qg, q, "qg") or None, _dev(kg, q, "kg") or None,
                     _dev(vg, q, "vg") or None, ws.data_ptr() if ws is not None else None,
-                    ws.numel() if ws is not None else 0, vptr or None, sptr or None)
+                    ws.numel() if ws is not None else 0, vptr or None, sptr or None,
+                    lptr[0], lptr[1], n_labels, int(seg_pieces))
     args = (ctypes.byref(dims), qptr, k.data_ptr(), v.data_ptr(), gptr or None, n_global,
             int(radius), dil, int(bool(causal)), rptr or None, out.data_ptr(),
             lse.data_ptr() if lse is not None else None, _stream(q, stream), ctypes.byref(ext))
-    keep = (dims, ext, dil, q, k, v, global_idx, rel_bias, rel_vec, seg_ids, qg, kg, vg, ws)
+    keep = (dims, ext, dil, q, k, v, global_idx, rel_bias, rel_vec, seg_ids, qg, kg, vg, ws,
+            glabel, llabel)
     fn = lib().la_attn_forward_noalloc if noalloc else lib().la_attn_forward
     return BoundCall(fn, args, keep, out, lse)
 
@@ -330,18 +364,21 @@ def la_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     kg: Optional[torch.Tensor] = None, vg: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, stream=None,
                     want_lse: bool = True, rel_vec: Optional[torch.Tensor] = None,
-                    seg_ids: Optional[torch.Tensor] = None
-                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                    seg_ids: Optional[torch.Tensor] = None, rel_k: Optional[int] = None,
+                    glabel: Optional[torch.Tensor] = None, llabel: Optional[torch.Tensor] = None,
+                    seg_pieces: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Band + global attention; returns ``(out, lse)``.
 
     ``global_idx`` is a device int32 tensor of strictly increasing positions.
     ``rel_bias`` is a device fp32 ``[H, 2k+1]`` table and ``rel_vec`` a device
     fp32 ``[H, 2k+1, D]`` table of key-side label vectors. ``seg_ids`` (device
     int32 ``[B, N]``) masks pairs across segments. ``out``, ``lse`` and
-    the workspace are allocated with torch when not given.
+    the workspace are allocated with torch when not given. Structural labels
+    and piece-selected segment masks: see :func:`bind_attn`.
     """
     return bind_attn(q, k, v, global_idx, radius, dilation, causal, rel_bias, out, lse, qg, kg,
-                     vg, workspace, stream, want_lse, rel_vec, seg_ids)()
+                     vg, workspace, stream, want_lse, rel_vec, seg_ids, False, rel_k, glabel,
+                     llabel, seg_pieces)()
 
 
 def la_attn_forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

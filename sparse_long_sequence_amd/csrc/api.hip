@@ -167,7 +167,7 @@ la_status plan_dilated(const la_dims* d, const int32_t* w, const int32_t* r, int
 
 extern "C" {
 
-int32_t la_version(void) { return 1; }
+int32_t la_version(void) { return 2; }
 
 const char* la_last_error(void) { return g_err.c_str(); }
 
@@ -227,6 +227,23 @@ la_status attn_forward_ws(const la_dims* dims, const void* q, const void* k, con
   if (seg_ids && ((uintptr_t)seg_ids & 3u) != 0)
     return fail(LA_EINVAL, "ext->seg_ids must be 4-byte aligned");
   if (rel_k > la::kMaxRelK) return fail(LA_EUNSUPPORTED, "rel_k above 31");
+  const uint8_t* glabel = ext ? ext->glabel : nullptr;
+  const uint8_t* llabel = ext ? ext->llabel : nullptr;
+  const int32_t n_labels = ext ? ext->n_labels : 0;
+  const int32_t seg_pieces = ext ? ext->seg_pieces : 0;
+  if (n_labels < 0 || (n_labels > 0 && n_labels < 2 * rel_k + 1))
+    return fail(LA_EINVAL, "ext->n_labels must be 0 or at least 2*rel_k+1");
+  if (n_labels > la::kMaxLabels) return fail(LA_EUNSUPPORTED, "more than 64 labels");
+  if (n_labels > 0 && !rel_bias && !rel_vec)
+    return fail(LA_EINVAL, "ext->n_labels set without rel_bias or ext->rel_vec");
+  if ((glabel || llabel) && n_global == 0)
+    return fail(LA_EINVAL, "label matrices need global tokens");
+  if (seg_pieces < 0 || seg_pieces > 15) return fail(LA_EINVAL, "ext->seg_pieces must be in [0, 15]");
+  if (glabel || llabel) {
+    // the label matrices are addressed with 32-bit offsets per batch row
+    if ((int64_t)n_global * dims->N > ((int64_t)1 << 31))
+      return fail(LA_EUNSUPPORTED, "label matrices above 2^31 entries per batch row");
+  }
   const void *qg = q, *kg = k, *vg = v;
   if (ext && (ext->qg || ext->kg || ext->vg)) {
     if (!(ext->qg && ext->kg && ext->vg)) return fail(LA_EINVAL, "qg, kg, vg: all three or none");
@@ -272,6 +289,10 @@ la_status attn_forward_ws(const la_dims* dims, const void* q, const void* k, con
   a.rel_bias = rel_bias;
   a.rel_vec = rel_vec;
   a.seg = seg_ids;
+  a.glabel = glabel;
+  a.llabel = llabel;
+  a.n_labels = n_labels > 0 ? n_labels : 2 * rel_k + 1;
+  a.seg_pieces = seg_pieces == 0 ? 15 : seg_pieces;
   a.rel_k = rel_k;
   a.out = out;
   a.lse = lse;

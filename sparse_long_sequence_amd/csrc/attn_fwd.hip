@@ -34,31 +34,38 @@ struct OutT<bf16> { typedef bf16 type; };
 template <>
 struct OutT<float> { typedef float type; };
 
-template <typename T>
+// The label vocabulary per head: the 2k+1 distance labels, and with LBL the
+// structural labels after them (n_labels entries in all).
+template <typename T, bool LBL>
 __device__ __forceinline__ void load_bias_table(typename TileTraits<T>::Smem& sm, const AttnArgs& a,
                                                 int32_t h, int32_t tid) {
-  if (a.rel_bias && tid < 2 * a.rel_k + 1)
-    sm.bias[tid] = a.rel_bias[h * (2 * a.rel_k + 1) + tid] * kInvScale;
+  if constexpr (LBL) {
+    if (a.rel_bias && tid < a.n_labels)
+      sm.bias[tid] = a.rel_bias[h * a.n_labels + tid] * kInvScale;
+  } else {
+    if (a.rel_bias && tid < 2 * a.rel_k + 1)
+      sm.bias[tid] = a.rel_bias[h * (2 * a.rel_k + 1) + tid] * kInvScale;
+  }
 }
 
 // With key-side label vectors a_l (ETC page, §3.4 "Relative Position
 // Encoding", Step 3 and its implementation note): the workgroup's table of
 // q_i . a_l for each of its query rows and each label, in q.k units, plus the
 // scalar label bias (times sqrt(D)) when one is given too. Row r's query is
-// q[pos(r)]; rt holds kTQ rows of 2k+1 entries. The head's label vectors are
-// staged in `stage` (an LDS buffer not yet in use, at least (2k+1) * D fp32);
+// q[pos(r)]; rt holds kTQ rows of V entries (every label). The head's label vectors are
+// staged in `stage` (an LDS buffer not yet in use, at least V * D fp32);
 // each thread holds a half row of its query in registers and sums one label
 // in kTPR. Ends with a barrier.
-static_assert(sizeof(TileTraits<bf16>::Smem::v) >= (2 * kMaxRelK + 1) * kD * sizeof(float) &&
-                  sizeof(TileTraits<float>::Smem::v) >= (2 * kMaxRelK + 1) * kD * sizeof(float),
+static_assert(sizeof(TileTraits<bf16>::Smem::v) >= kMaxLabels * kD * sizeof(float) &&
+                  sizeof(TileTraits<float>::Smem::v) >= kMaxLabels * kD * sizeof(float),
               "the V buffers stage the label vectors");
 
-template <typename T, typename Pos>
+template <typename T, bool LBL, typename Pos>
 __device__ __forceinline__ void build_row_table(float* rt, float* stage, const AttnArgs& a,
                                                 int32_t h, const T* qb, Pos pos, int32_t tid) {
   using TT = TileTraits<T>;
   constexpr int32_t kTPR = TT::kThreads / TT::kTQ;  // threads per query row
-  const int32_t nl = 2 * a.rel_k + 1;
+  const int32_t nl = LBL ? a.n_labels : 2 * a.rel_k + 1;
   const f32x4* av = reinterpret_cast<const f32x4*>(a.rel_vec + (size_t)h * nl * kD);
   for (int32_t x = tid; x < nl * (kD / 4); x += TT::kThreads)
     reinterpret_cast<f32x4*>(stage)[x] = av[x];
@@ -131,7 +138,7 @@ __device__ __forceinline__ void segment_rows(GlobInfo& gi, const int32_t* segb, 
 // ---------------------------------------------------------------------------
 // BIAS: a relative-position bias table is given (the no-bias loops are
 // compiled without its code).
-template <typename T, bool BIAS, bool SEG>
+template <typename T, bool BIAS, bool SEG, bool LBL>
 __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileTraits<T>::Smem& sm,
                                                float* rowtab, int32_t bw) {
   using TT = TileTraits<T>;
@@ -165,7 +172,7 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   // a tile made only of global rows belongs to the global-row pass (detected
   // here when G is one run of consecutive positions)
   if (d == 1 && g_last - g_first == ng - 1 && g_first <= i_lo && g_last >= i_hi) return;
-  load_bias_table<T>(sm, a, h, tid);
+  load_bias_table<T, LBL>(sm, a, h, tid);
 
   const T* qb = reinterpret_cast<const T*>(a.q) + bh * head_elems;
   const T* kb = reinterpret_cast<const T*>(a.k) + bh * head_elems;
@@ -174,7 +181,7 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   const int32_t qpos = qbase + d * min(qi, qcount - 1);
   const bool dead = TT::kQW * wave >= qcount;  // no valid row in this wave
   if (BIAS && a.rel_vec)  // before the wave state is live
-    build_row_table<T>(rowtab, reinterpret_cast<float*>(&sm.v[0][0]), a, h, qb,
+    build_row_table<T, LBL>(rowtab, reinterpret_cast<float*>(&sm.v[0][0]), a, h, qb,
                        [&](int32_t r) { return qbase + d * min(r, qcount - 1); }, tid);
   typename TT::Wave w;
   TT::load_q(w, qb, &qpos, lane);
@@ -185,9 +192,25 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   const int32_t hi = a.causal ? (t0 + qcount - 1) : min(n_c - 1, t0 + qcount - 1 + R);
   const int32_t n_band = (hi - lo + 1 + kTK - 1) / kTK;
   const bool want_bias = a.rel_bias != nullptr || a.rel_vec != nullptr;
+  // flags: the tiles stage their keys' global flags (for the bias, and with
+  // LBL for the labels and the piece-selected segment masks)
+  bool flags = want_bias;
   GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
-  if (SEG) segment_rows(gi, a.seg + (size_t)(bh / a.H) * N, qpos);
-  if (want_bias && a.n_global > 0) {
+  LabelRule lr = {};
+  if constexpr (LBL) {
+    // non-global rows: the labels of their global keys; segment ids mask l2g
+    // (global keys) and l2l (the others)
+    lr.lab = a.llabel ? a.llabel + (size_t)(bh / a.H) * N * a.n_global : nullptr;
+    lr.stride = (uint32_t)a.n_global;
+    lr.V = a.n_labels;
+    lr.want_rank = a.llabel != nullptr;
+    lr.seg_g = (a.seg_pieces & 4) != 0;
+    lr.seg_l = (a.seg_pieces & 8) != 0;
+    flags = flags || a.llabel != nullptr || (a.seg && a.seg_pieces != 15);
+  }
+  // (the label kernel is built with SEG and may run without segment ids)
+  if (SEG && (!LBL || a.seg)) segment_rows(gi, a.seg + (size_t)(bh / a.H) * N, qpos);
+  if (flags && a.n_global > 0) {
     if (hi - lo + 1 <= 32 * kGMaskWords) {
       build_gmask<T>(sm, a.gidx, a.n_global, c + d * lo, d, hi - lo + 1, tid);
       gi.mode = kGlobBitmap;
@@ -195,8 +218,9 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
       gi.mode = kGlobSearch;
     }
   }
-  const BiasRule br = {!want_bias ? nullptr : a.rel_vec ? rowtab : sm.bias, a.rel_k, 0,
-                       a.rel_vec ? 2 * a.rel_k + 1 : 0};
+  BiasRule br = {!want_bias ? nullptr : a.rel_vec ? rowtab : sm.bias, a.rel_k, 0,
+                 a.rel_vec ? 2 * a.rel_k + 1 : 0};
+  if constexpr (LBL) br.row_stride = a.rel_vec ? a.n_labels : 0;
 
   auto band_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = lo + n * kTK;
@@ -216,7 +240,7 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
   const bool g_run = ng > 0 && d == 1 && g_last - g_first == ng - 1;
   if (g_run) {
     const int32_t n_gt = (ng + kTK - 1) / kTK;
-    const int32_t glob_mode = want_bias ? kGlobAll : kGlobNone;
+    const int32_t glob_mode = flags ? kGlobAll : kGlobNone;
     // The global key tiles come first: they are the same for every query tile
     // of the head, so the workgroups' first K/V loads mostly hit in L2 while
     // their band tiles stream in behind (the online softmax is order-free).
@@ -234,7 +258,7 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
           a.causal ? (gl >= i_hi - R && gh <= i_lo) : (gl >= i_hi - R && gh <= i_lo + R);
       const bool none_causal = a.causal && gl > i_hi;
       const bool keep = !all_in_band && !none_causal;
-      kt = {nullptr, gl, 1, keep ? cnt : 0, 0, glob_mode};
+      kt = {nullptr, gl, 1, keep ? cnt : 0, 0, glob_mode, LBL ? 1 + gt * kTK : 0};
       // every key outside every row's window (and not after any row, causal):
       // no mask needed
       const bool all_out = cnt == kTK && (gh < i_lo - R || (!a.causal && gl > i_hi + R)) &&
@@ -243,10 +267,11 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
       // lies outside the window [-R, R] (causal: [-R, inf), so also j <= i)
       mr = {kOutside, all_out ? 0 : 1, 1, -gl, -R, a.causal ? kFar : R, 0, 0, 1};
     };
-    run_tiles<T, false, BIAS, SEG>(sm, w, kb, vb, n_band + n_gt, desc, br, gi, qi, qpos, dead,
+    run_tiles<T, false, BIAS, SEG, LBL>(sm, w, kb, vb, n_band + n_gt, desc, br, gi, lr, qi, qpos, dead,
                         a.scale_log2);
   } else {
-    run_tiles<T, false, BIAS, SEG>(sm, w, kb, vb, n_band, band_desc, br, gi, qi, qpos, dead, a.scale_log2);
+    run_tiles<T, false, BIAS, SEG, LBL>(sm, w, kb, vb, n_band, band_desc, br, gi, lr, qi, qpos, dead,
+                                        a.scale_log2);
   }
 
   if (a.n_global > 0 && !g_run) {
@@ -274,16 +299,18 @@ __device__ __forceinline__ void band_workgroup(const AttnArgs& a, typename TileT
         gt = __builtin_ctzll(m);
       }
       const int32_t kcount = min(kTK, a.n_global - gt * kTK);
-      kt = {a.gidx + gt * kTK, 0, 1, kcount, 0, want_bias ? kGlobAll : kGlobNone};
+      kt = {a.gidx + gt * kTK, 0, 1, kcount, 0, flags ? kGlobAll : kGlobNone,
+            LBL ? 1 + gt * kTK : 0};
       const int32_t gl = a.gidx[gt * kTK], gh = a.gidx[gt * kTK + kcount - 1];
       const bool outside = (gh < i_lo - d * R) || (gl > i_hi + d * R);
       const bool causal_ok = !a.causal || gh <= i_lo;
       const bool full = kcount == kTK && outside && causal_ok;
       mr = {kGlobCol, full ? 0 : 1, 0, 0, 0, 0, a.causal, R, d};
     };
-    const GlobInfo gall = {want_bias ? kGlobAll : kGlobNone, a.gidx, a.n_global,
+    const GlobInfo gall = {flags ? kGlobAll : kGlobNone, a.gidx, a.n_global,
                            gi.segb, gi.sq, gi.sq_min, gi.sq_max};
-    run_tiles<T, true, BIAS, SEG>(sm, w, kb, vb, n_glob, glob_desc, br, gall, qi, qpos, dead, a.scale_log2);
+    run_tiles<T, true, BIAS, SEG, LBL>(sm, w, kb, vb, n_glob, glob_desc, br, gall, lr, qi, qpos, dead,
+                                       a.scale_log2);
   }
 
   // epilogue: rows outside G (the global-row pass owns the rest)
@@ -376,7 +403,7 @@ __device__ __forceinline__ void merge_global_tile(float* ws_o, float* ws_lse, co
 // ---------------------------------------------------------------------------
 // global-row workgroup: one tile of global rows against one chunk of keys
 // ---------------------------------------------------------------------------
-template <typename T, bool BIAS, bool SEG>
+template <typename T, bool BIAS, bool SEG, bool LBL>
 __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
                                                  typename TileTraits<T>::Smem& sm, float* rowtab,
                                                  int32_t gw) {
@@ -397,10 +424,24 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   int32_t j1 = min(N, j0 + a.chunk_len);
   if (a.causal) j1 = min(j1, i_max + 1);
   const int32_t n_tiles = j1 > j0 ? (j1 - j0 + kTK - 1) / kTK : 0;
-  load_bias_table<T>(sm, a, h, tid);
+  load_bias_table<T, LBL>(sm, a, h, tid);
   const bool want_bias = a.rel_bias != nullptr || a.rel_vec != nullptr;
+  bool flags = want_bias;  // as in the band workgroup
   GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
-  if (want_bias && n_tiles > 0) {
+  LabelRule lr = {};
+  if constexpr (LBL) {
+    // global rows: their label rows; segment ids mask g2g (global keys) and
+    // g2l (the others)
+    lr.lab = a.glabel ? a.glabel + ((size_t)(bh / a.H) * a.n_global + gq * kTQ) * N : nullptr;
+    lr.rows_global = 1;
+    lr.row_last = qcount - 1;  // rows past it belong to no global token
+    lr.stride = (uint32_t)N;
+    lr.V = a.n_labels;
+    lr.seg_g = (a.seg_pieces & 1) != 0;
+    lr.seg_l = (a.seg_pieces & 2) != 0;
+    flags = flags || a.glabel != nullptr || (a.seg && a.seg_pieces != 15);
+  }
+  if (flags && n_tiles > 0) {
     build_gmask<T>(sm, a.gidx, a.n_global, j0, 1, j1 - j0, tid);  // j1 - j0 <= chunk_len
     gi.mode = kGlobBitmap;
   }
@@ -409,7 +450,7 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   const T* kb = reinterpret_cast<const T*>(a.kg) + bh * head_elems;
   const T* vb = reinterpret_cast<const T*>(a.vg) + bh * head_elems;
   if (BIAS && a.rel_vec)
-    build_row_table<T>(rowtab, reinterpret_cast<float*>(&sm.v[0][0]), a, h, qb,
+    build_row_table<T, LBL>(rowtab, reinterpret_cast<float*>(&sm.v[0][0]), a, h, qb,
                        [&](int32_t r) { return qidx[min(r, qcount - 1)]; }, tid);
   // A tile of at most half the workgroup's rows (bf16: two key sub-tiles per
   // tile) keeps every wave busy: waves w and w + 2 take the same rows, wave w
@@ -419,7 +460,8 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
   const int32_t wrow = split ? (wave & 1) : wave;
   const int32_t qi = TT::qrow(wrow, lane, 0);
   const int32_t qpos = qidx[min(qi, qcount - 1)];
-  if (SEG) segment_rows(gi, a.seg + (size_t)(bh / a.H) * N, qpos);
+  // (the label kernel is built with SEG and may run without segment ids)
+  if (SEG && (!LBL || a.seg)) segment_rows(gi, a.seg + (size_t)(bh / a.H) * N, qpos);
   const bool dead = TT::kQW * wrow >= qcount;  // no valid row in this wave
   typename TT::Wave w;
   TT::load_q(w, qb, &qpos, lane);
@@ -431,9 +473,11 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
     const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= i_min);
     mr = {kRange, full ? 0 : 1, 1, -u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
   };
-  const BiasRule br = {!want_bias ? nullptr : a.rel_vec ? rowtab : sm.bias, a.rel_k, 1,
-                       a.rel_vec ? 2 * a.rel_k + 1 : 0};
-  run_tiles<T, false, BIAS, SEG>(sm, w, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead, a.scale_log2,
+  BiasRule br = {!want_bias ? nullptr : a.rel_vec ? rowtab : sm.bias, a.rel_k, 1,
+                 a.rel_vec ? 2 * a.rel_k + 1 : 0};
+  if constexpr (LBL) br.row_stride = a.rel_vec ? a.n_labels : 0;
+  run_tiles<T, false, BIAS, SEG, LBL>(sm, w, kb, vb, n_tiles, desc, br, gi, lr, qi, qpos, dead,
+                                      a.scale_log2,
                       split ? (wave >> 1) : -1);
   bool holds_rows = true;  // this wave holds a final running state
   if constexpr (TT::kSub == 2) {
@@ -482,13 +526,15 @@ __device__ __forceinline__ void global_workgroup(const AttnArgs& a,
                        gq * kTQ, qcount);
 }
 
-// At least kMinWavesPerEU waves per SIMD: that bounds each wave's registers.
+// At least kMinWavesPerEU waves per SIMD (the label kernel: at most 3, as it
+// needs more registers): that bounds each wave's registers.
 // BIAS: a relative-position bias (scalar table and/or key-side label vectors)
-// is given; SEG: segment masks are given. Each kernel carries only the code
-// its flags need.
-template <typename T, bool BIAS, bool SEG>
+// is given; SEG: segment masks are given; LBL: per-pair label matrices and/or
+// segment masks of some pieces only (instantiated with BIAS and SEG). Each
+// kernel carries only the code its flags need.
+template <typename T, bool BIAS, bool SEG, bool LBL>
 __global__ __launch_bounds__(TileTraits<T>::kThreads)
-__attribute__((amdgpu_waves_per_eu(TileTraits<T>::kMinWavesPerEU)))
+__attribute__((amdgpu_waves_per_eu(LBL && TileTraits<T>::kMinWavesPerEU > 3 ? 3 : TileTraits<T>::kMinWavesPerEU)))
 void attn_fwd_kernel(AttnArgs a) {
   __shared__ typename TileTraits<T>::Smem sm;
   // per-row label table (key-side label vectors only; sized at launch, else empty)
@@ -503,9 +549,9 @@ void attn_fwd_kernel(AttnArgs a) {
   const int32_t gcnt = min(gper, max(0, a.n_glob_wg - x * gper));
   const int32_t bcnt = min(bper, max(0, a.n_band_wg - x * bper));
   if (j < gcnt)
-    global_workgroup<T, BIAS, SEG>(a, sm, rowtab, x * gper + j);
+    global_workgroup<T, BIAS, SEG, LBL>(a, sm, rowtab, x * gper + j);
   else if (j - gcnt < bcnt)
-    band_workgroup<T, BIAS, SEG>(a, sm, rowtab, x * bper + (j - gcnt));
+    band_workgroup<T, BIAS, SEG, LBL>(a, sm, rowtab, x * bper + (j - gcnt));
 }
 
 hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
@@ -515,22 +561,25 @@ hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
                                          (a.n_band_wg + kXcds - 1) / kXcds);
   // dynamic LDS: the per-row label table of key-side label vectors
   const size_t rows = dtype == 1 ? TileTraits<bf16>::kTQ : TileTraits<float>::kTQ;
-  const uint32_t dyn = a.rel_vec ? (uint32_t)(rows * (2 * a.rel_k + 1) * sizeof(float)) : 0u;
+  const uint32_t dyn = a.rel_vec ? (uint32_t)(rows * a.n_labels * sizeof(float)) : 0u;
   const bool bias = a.rel_bias != nullptr || a.rel_vec != nullptr;
   const bool seg = a.seg != nullptr;
+  const bool lbl = a.glabel != nullptr || a.llabel != nullptr || (seg && a.seg_pieces != 15);
   const dim3 g((uint32_t)grid);
   if (dtype == 1) {
     const dim3 b(TileTraits<bf16>::kThreads);
-    if (bias && seg) hipLaunchKernelGGL((attn_fwd_kernel<bf16, true, true>), g, b, dyn, stream, a);
-    else if (bias) hipLaunchKernelGGL((attn_fwd_kernel<bf16, true, false>), g, b, dyn, stream, a);
-    else if (seg) hipLaunchKernelGGL((attn_fwd_kernel<bf16, false, true>), g, b, dyn, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<bf16, false, false>), g, b, dyn, stream, a);
+    if (lbl) hipLaunchKernelGGL((attn_fwd_kernel<bf16, true, true, true>), g, b, dyn, stream, a);
+    else if (bias && seg) hipLaunchKernelGGL((attn_fwd_kernel<bf16, true, true, false>), g, b, dyn, stream, a);
+    else if (bias) hipLaunchKernelGGL((attn_fwd_kernel<bf16, true, false, false>), g, b, dyn, stream, a);
+    else if (seg) hipLaunchKernelGGL((attn_fwd_kernel<bf16, false, true, false>), g, b, dyn, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<bf16, false, false, false>), g, b, dyn, stream, a);
   } else {
     const dim3 b(TileTraits<float>::kThreads);
-    if (bias && seg) hipLaunchKernelGGL((attn_fwd_kernel<float, true, true>), g, b, dyn, stream, a);
-    else if (bias) hipLaunchKernelGGL((attn_fwd_kernel<float, true, false>), g, b, dyn, stream, a);
-    else if (seg) hipLaunchKernelGGL((attn_fwd_kernel<float, false, true>), g, b, dyn, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<float, false, false>), g, b, dyn, stream, a);
+    if (lbl) hipLaunchKernelGGL((attn_fwd_kernel<float, true, true, true>), g, b, dyn, stream, a);
+    else if (bias && seg) hipLaunchKernelGGL((attn_fwd_kernel<float, true, true, false>), g, b, dyn, stream, a);
+    else if (bias) hipLaunchKernelGGL((attn_fwd_kernel<float, true, false, false>), g, b, dyn, stream, a);
+    else if (seg) hipLaunchKernelGGL((attn_fwd_kernel<float, false, true, false>), g, b, dyn, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<float, false, false, false>), g, b, dyn, stream, a);
   }
   return hipGetLastError();
 }

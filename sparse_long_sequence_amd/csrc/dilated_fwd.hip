@@ -52,6 +52,7 @@ __device__ __forceinline__ bool dilated_tile(const DilArgs& a, TileTraits<bf16>:
   TT::load_q(wv, qb, &qpos, lane);
   const BiasRule br = {nullptr, 0, 0, 0};
   const GlobInfo gi = {kGlobNone, nullptr, 0};
+  const LabelRule nolab = {};
   if (a.kind[k] == 1) {
     // Fixed pattern, strided part (LongNet page, §3.4 "Standard Self-Attention
     // and Sparse Attention (Preliminaries)"): the c summary positions at block
@@ -69,8 +70,8 @@ __device__ __forceinline__ bool dilated_tile(const DilArgs& a, TileTraits<bf16>:
       kt = {nullptr, blk * w + toff + (x0 - kb * c), 1, kTK, 0, kGlobNone};
       mr = {kRange, 0, 0, 0, -kFar, kFar, 0, 0, 1};
     };
-    run_tiles<bf16, false, false, false>(sm, wv, kb, vb, n_keys / kTK, desc_sum, br, gi, qi, qpos,
-                                         dead, a.scale_log2);
+    run_tiles<bf16, false, false, false, false>(sm, wv, kb, vb, n_keys / kTK, desc_sum, br, gi,
+                                                nolab, qi, qpos, dead, a.scale_log2);
   } else {
     const int32_t hi = a.causal ? t0 + qcount - 1 : n_rows - 1;
     const int32_t n_tiles = (hi + kTK) / kTK;
@@ -82,8 +83,8 @@ __device__ __forceinline__ bool dilated_tile(const DilArgs& a, TileTraits<bf16>:
       const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= t0);
       mr = {kRange, full ? 0 : 1, 0, t0 - u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
     };
-    run_tiles<bf16, false, false, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, qi, qpos, dead,
-                                         a.scale_log2);
+    run_tiles<bf16, false, false, false, false>(sm, wv, kb, vb, n_tiles, desc, br, gi, nolab, qi,
+                                                qpos, dead, a.scale_log2);
   }
   dt = {base, r, t0, qcount, qi, qpos};
   return true;

@@ -9,6 +9,8 @@ namespace la {
 constexpr int32_t kMaxHeadsDil = 64;  // per-head dilation table size
 constexpr int32_t kMaxPairs = 16;     // LongNet patterns per call
 constexpr int32_t kMaxRelK = 31;      // 2k+1 <= 63 bias entries per head
+constexpr int32_t kMaxLabels = 64;    // label vocabulary (distance + structural) per head
+constexpr int32_t kLabelDistance = 0xFE;  // per-pair label: the pair's usual clipped-distance label
 
 struct AttnArgs {
   const void *q, *k, *v;
@@ -21,6 +23,13 @@ struct AttnArgs {
   const float* rel_bias;
   const float* rel_vec;  // [H][2k+1][D] key-side label vectors, or null
   const int32_t* seg;    // [B][N] segment id per position (packed documents), or null
+  // Per-pair labels of the pieces with a global token: glabel [B][n_global][N]
+  // (global queries), llabel [B][N][n_global] (non-global queries, global
+  // keys); a vocabulary index < n_labels, kLabelDistance, or a masked pair.
+  const uint8_t* glabel;
+  const uint8_t* llabel;
+  int32_t n_labels;      // vocabulary size (2*rel_k+1 without structural labels)
+  int32_t seg_pieces;    // pieces segment ids mask: bits g2g 1, g2l 2, l2g 4, l2l 8
   int32_t rel_k;
   void* out;
   float* lse;

@@ -156,6 +156,18 @@ __device__ __forceinline__ bool sorted_contains(const int32_t* g, int32_t n, int
   return false;
 }
 
+// Index of p in the strictly increasing array g[0..n), or -1.
+__device__ __forceinline__ int32_t sorted_index(const int32_t* g, int32_t n, int32_t p) {
+  int32_t lo = 0, hi = n;
+  while (lo < hi) {
+    int32_t mid = (lo + hi) >> 1;
+    int32_t x = g[mid];
+    if (x == p) return mid;
+    if (x < p) lo = mid + 1; else hi = mid;
+  }
+  return -1;
+}
+
 // Key rows of one tile: positions base + stride*x (strided view) or idx[x]
 // (gather through the global index list), for x < count (count >= 1).
 struct KeyTile {
@@ -163,6 +175,9 @@ struct KeyTile {
   int32_t base, stride, count;  // count 0: nothing to load, every query block is empty
   int32_t gbit0;  // bit of row 0 in the workgroup's global bitmap (strided tiles)
   int32_t gmode;  // how the keys' "is global" flags are found (GlobMode)
+  // 1 + the global rank of key row 0 when the tile's keys are global tokens of
+  // consecutive ranks (per-pair label rows are then read contiguously), else 0
+  int32_t rank_run;
 };
 
 // Which (query, key) pairs of a tile are allowed.
@@ -220,6 +235,28 @@ struct BiasRule {
   int32_t row_stride;               // 0: one table; else query row qi's table at tab + qi * row_stride
 };
 
+// Structured inputs (only the kernels built for them read this). Per-pair
+// labels (ETC page, §3.4 "Relative Position Encoding", Step 1 and its
+// implementation note; a masked label is an entry M = 0 of "Per-instance
+// attention masks"), or lab = null. Global query rows (rows_global): row qi's
+// labels are lab[min(qi, row_last) * stride + key position] (the lanes past
+// the workgroup's last row read that row's); non-global rows: the labels of
+// their global keys are lab[qpos * stride + key's global rank] (want_rank:
+// the tiles stage each key's rank). seg_g / seg_l: the segment ids mask the
+// pairs whose key is global / non-global.
+struct LabelRule {
+  const uint8_t* lab;
+  int32_t rows_global;
+  int32_t row_last;  // rows_global: the workgroup's last query row
+  uint32_t stride;
+  int32_t V;  // vocabulary size: a label >= V other than kLabelDist masks the pair
+  int32_t want_rank;
+  int32_t seg_g, seg_l;
+};
+
+// A per-pair label value keeping the pair's usual clipped-distance label.
+constexpr int32_t kLabelDist = 0xFE;
+
 // Position of key row x of a tile (x clamped into [0, count) by the caller).
 template <bool GATHER>
 __device__ __forceinline__ int32_t key_pos(const KeyTile& kt, int32_t x) {
@@ -272,6 +309,7 @@ struct TileTraits<bf16> {
     alignas(16) uint32_t gmask[kGMaskWords];
     alignas(16) uint8_t kglob[2][kTK];
     alignas(16) int32_t kseg[2][kTK];  // segment ids of the staged keys (segment masks only)
+    alignas(16) int32_t kgrank[2][kTK];  // the keys' index in the global list, -1 if not global (labels only)
     int32_t segr[2][2];                // per staged tile: min and max of kseg
     int32_t gcls[2];  // per staged tile: bit 0 some key is global, bit 1 every key is
   };
@@ -582,6 +620,7 @@ struct TileTraits<float> {
     alignas(16) uint32_t gmask[kGMaskWords];
     alignas(16) uint8_t kglob[2][kTK];
     alignas(16) int32_t kseg[2][kTK];  // segment ids of the staged keys (segment masks only)
+    alignas(16) int32_t kgrank[2][kTK];  // the keys' index in the global list, -1 if not global (labels only)
     int32_t segr[2][2];                // per staged tile: min and max of kseg
     int32_t gcls[2];  // per staged tile: bit 0 some key is global, bit 1 every key is
   };
@@ -732,11 +771,12 @@ struct TileTraits<float> {
 };
 
 // Per-key position and global flag of a staged tile (tid < 64 write them);
-// SEG: also the keys' segment ids and their range, when gi has them.
-template <typename T, bool SEG>
+// SEG: also the keys' segment ids and their range, when gi has them; LBL: the
+// keys' global ranks, when gi asks for them.
+template <typename T, bool SEG, bool LBL>
 __device__ __forceinline__ void stage_meta(typename TileTraits<T>::Smem& sm, int32_t buf,
-                                           const KeyMeta& mt, const GlobInfo& gi, int32_t mode,
-                                           int32_t tid) {
+                                           const KeyMeta& mt, const GlobInfo& gi,
+                                           const LabelRule& lr, int32_t mode, int32_t tid) {
   if (tid < kTK) {
     sm.kpos[buf][tid] = mt.pos;
     uint8_t f = 0;
@@ -747,6 +787,9 @@ __device__ __forceinline__ void stage_meta(typename TileTraits<T>::Smem& sm, int
     else if (mode == kGlobAll)
       f = 1;
     sm.kglob[buf][tid] = f;
+    if constexpr (LBL) {
+      if (lr.want_rank) sm.kgrank[buf][tid] = f ? sorted_index(gi.gidx, gi.n_global, mt.pos) : -1;
+    }
     if (mode != kGlobNone) {
       // the rows past the tile's end repeat its last key, so the whole wave
       // (tid < 64) gives the tile's any / all
@@ -814,6 +857,89 @@ __device__ __forceinline__ void add_bias(float* s, const typename TileTraits<T>:
   }
 }
 
+// The labels of the lane's kNS pairs of sub-tile sb, four per word (element
+// r in byte r & 3 of word r >> 2; the lane's keys come in runs of four):
+// issued before the sub-tile's score MFMAs so that their latency overlaps
+// them. Global query rows read their label row at the keys' positions (the
+// tiles of the global-row pass are contiguous runs of positions); other rows
+// read theirs at the keys' global ranks, contiguous for a run of global keys
+// (kt.rank_run) and else looked up per key (kgrank, -1: not global, no label).
+template <typename T>
+__device__ __forceinline__ void load_labels(uint32_t lw[TileTraits<T>::kNS / 4],
+                                            const typename TileTraits<T>::Smem& sm, int32_t buf,
+                                            const LabelRule& lr, const KeyTile& kt, int sb,
+                                            int32_t qi, int32_t qpos, int32_t lane) {
+  using TT = TileTraits<T>;
+  static_assert(TT::kNS % 4 == 0, "runs of four keys per lane");
+  const int32_t kl = TT::key_lane(lane);
+  const int32_t row = lr.rows_global ? min(qi, lr.row_last) : qpos;
+  const uint8_t* lrow = lr.lab + (size_t)(uint32_t)row * lr.stride;
+  const int32_t last = kt.count - 1;
+  const bool run = lr.rows_global ? kt.stride == 1 : kt.rank_run > 0;
+  if (run) {
+    const uint8_t* lt = lrow + (lr.rows_global ? kt.base : kt.rank_run - 1);
+    if (kt.count == kTK && ((uintptr_t)lt & 3) == 0) {
+#pragma unroll
+      for (int g = 0; g < TT::kNS / 4; ++g)
+        lw[g] = *reinterpret_cast<const uint32_t*>(lt + TT::key_const(sb, 4 * g) + kl);
+    } else {  // a ragged or unaligned run: byte loads, clamped into the tile
+#pragma unroll
+      for (int g = 0; g < TT::kNS / 4; ++g) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x |= (uint32_t)lt[min(TT::key_const(sb, 4 * g + e) + kl, last)] << (8 * e);
+        lw[g] = x;
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int g = 0; g < TT::kNS / 4; ++g) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int32_t kj = TT::key_const(sb, 4 * g + e) + kl;
+      uint32_t b = (uint32_t)kLabelDist;
+      if (lr.rows_global) {
+        b = lrow[(uint32_t)sm.kpos[buf][kj]];
+      } else {
+        const int32_t gr = sm.kgrank[buf][kj];
+        if (gr >= 0) b = lrow[(uint32_t)gr];
+      }
+      x |= b << (8 * e);
+    }
+    lw[g] = x;
+  }
+}
+
+// Bias and masks from per-pair labels: a pair with an explicit label l < V
+// takes table entry l (whatever its piece), kLabelDist keeps the usual
+// distance label for same-kind pairs (none for mixed ones), and any other
+// value masks the pair (-inf).
+template <typename T>
+__device__ __forceinline__ void add_bias_labels(float* s, const uint32_t* lw,
+                                                const typename TileTraits<T>::Smem& sm,
+                                                int32_t buf, const BiasRule& br,
+                                                const LabelRule& lr, int sb, int32_t qi,
+                                                int32_t qpos, int32_t lane) {
+  using TT = TileTraits<T>;
+  int32_t kl = TT::key_lane(lane);
+  asm("" : "+v"(kl));  // opaque per call, as in add_bias
+  const float* tab = br.tab ? br.tab + qi * br.row_stride : nullptr;
+#pragma unroll
+  for (int r = 0; r < TT::kNS; ++r) {
+    const int32_t kj = TT::key_const(sb, r) + kl;
+    const int32_t lbl = (int32_t)((lw[r >> 2] >> (8 * (r & 3))) & 0xFFu);
+    const bool same = (sm.kglob[buf][kj] != 0) == (br.key_global_is_same_kind != 0);
+    const int32_t dl = min(max(sm.kpos[buf][kj] - qpos, -br.k), br.k);
+    const int32_t idx = lbl == kLabelDist ? (same ? dl + br.k : -1) : lbl;
+    const bool masked = lbl != kLabelDist && lbl >= lr.V;
+    const float b = (tab && idx >= 0 && !masked) ? tab[idx] : 0.f;
+    s[r] = masked ? kNegInf : s[r] + b;
+  }
+}
+
 // Set excluded (query, key) pairs of a partial tile to -inf. One uniform
 // branch per tile; the per-element tests are a few integer ops.
 template <typename T>
@@ -865,16 +991,21 @@ __device__ __forceinline__ void mask_tile(float* s, const typename TileTraits<T>
 
 // Exclude the pairs of sub-tile sb whose key lies in another segment than
 // this lane's query row (segment masks).
-template <typename T>
+// LBL: only the pieces gi names are checked (pairs with a global key: seg_g,
+// with a non-global key: seg_l); otherwise every pair.
+template <typename T, bool LBL>
 __device__ __forceinline__ void mask_segments(float* s, const typename TileTraits<T>::Smem& sm,
-                                              int32_t buf, int sb, int32_t sq, int32_t lane) {
+                                              int32_t buf, int sb, const GlobInfo& gi,
+                                              const LabelRule& lr, int32_t lane) {
   using TT = TileTraits<T>;
   int32_t kl = TT::key_lane(lane);
   asm("" : "+v"(kl));  // opaque per call, as in mask_tile
 #pragma unroll
   for (int r = 0; r < TT::kNS; ++r) {
     const int32_t kj = TT::key_const(sb, r) + kl;
-    s[r] = sm.kseg[buf][kj] == sq ? s[r] : kNegInf;
+    bool check = true;
+    if constexpr (LBL) check = sm.kglob[buf][kj] != 0 ? lr.seg_g != 0 : lr.seg_l != 0;
+    s[r] = (!check || sm.kseg[buf][kj] == gi.sq) ? s[r] : kNegInf;
   }
 }
 
@@ -945,11 +1076,12 @@ __device__ __forceinline__ void sub_update(const typename TileTraits<T>::Smem& s
 // range. When every sub-tile is full and no bias applies, the fast path runs
 // the sub-tiles one after the other with no mask or bias code. Otherwise each
 // sub-tile is skipped (no allowed pair), or biased and masked as needed.
-template <typename T, bool BIAS, bool SEG>
+template <typename T, bool BIAS, bool SEG, bool LBL>
 __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem& sm, int32_t buf,
                                              typename TileTraits<T>::Wave& w, int32_t lane,
                                              const MaskRule& mr, const BiasRule& br,
-                                             const GlobInfo& gi, const KeyTile& kt, bool strided,
+                                             const GlobInfo& gi, const LabelRule& lr,
+                                             const KeyTile& kt, bool strided,
                                              int32_t qi, int32_t qpos, bool dead,
                                              float scale_log2, int32_t only_sb) {
   using TT = TileTraits<T>;
@@ -964,12 +1096,19 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
   // Bias (ETC page, §3.4 "Relative Position Encoding": same-kind pairs only).
   // From the staged tile's global flags: no key of the query's kind means no
   // bias at all; every key of its kind means no per-key kind test.
-  bool bias_on = false, all_same = false;
+  bool bias_on = false, all_same = false, lab_on = false;
+  bool any_g = false, all_g = false;
   if constexpr (BIAS) {
     // (kGlobNone: no key is global, and the class word was not written)
     const int32_t gc = kt.gmode == kGlobNone ? 0 : __builtin_amdgcn_readfirstlane(sm.gcls[buf]);
-    const bool any_g = (gc & 1) != 0, all_g = (gc & 2) != 0;
+    any_g = (gc & 1) != 0;
+    all_g = (gc & 2) != 0;
     bias_on = br.tab != nullptr && (br.key_global_is_same_kind ? any_g : !all_g);
+    if constexpr (LBL) {
+      // per-pair labels: every pair of a global row, the global keys of others
+      lab_on = lr.lab != nullptr && (lr.rows_global || any_g);
+      bias_on = bias_on || lab_on;
+    }
     all_same = br.key_global_is_same_kind ? all_g : !any_g;
   }
   // A tile every pair of which is allowed for all of the workgroup's rows
@@ -993,7 +1132,22 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
   // sub-tile is masked per element.
   bool seg_check = false;
   if constexpr (SEG) {
-    if (gi.segb && kcount > 0) {
+    // LBL: the segment ids mask the pieces lr names only. A tile whose keys
+    // are all of masked pieces is checked as usual, one with none of them not
+    // at all, and one with keys of both per element.
+    bool seg_some = true, seg_mixed = false;
+    if constexpr (LBL) {
+      const bool chk_g = lr.seg_g && any_g, chk_l = lr.seg_l && !all_g;
+      const bool unchk = (!lr.seg_g && any_g) || (!lr.seg_l && !all_g);
+      seg_some = chk_g || chk_l;
+      seg_mixed = seg_some && unchk;
+    }
+    if (LBL && gi.segb && kcount > 0 && seg_mixed) {
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) cls[sb] = cls[sb] == kFull ? kPartial : cls[sb];
+      fast = false;
+      seg_check = true;
+    } else if (gi.segb && kcount > 0 && seg_some) {
       const int32_t kmn = __builtin_amdgcn_readfirstlane(sm.segr[buf][0]);
       const int32_t kmx = __builtin_amdgcn_readfirstlane(sm.segr[buf][1]);
       if (kmx < gi.sq_min || kmn > gi.sq_max) {
@@ -1022,6 +1176,8 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
   for (int sb = 0; sb < SB; ++sb) {
     if (cls[sb] == kEmpty) continue;  // no allowed pair: no scores, no softmax, no PV
     float s[TT::kNS];
+    uint32_t lw[TT::kNS / 4];
+    if (LBL && lab_on) load_labels<T>(lw, sm, buf, lr, kt, sb, qi, qpos, lane);
     TT::scores(sm, buf, w, lane, sb, s);
     float badd = 0.f;  // a bias shared by every pair of the sub-tile
     if (BIAS && bias_on) {
@@ -1029,7 +1185,7 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
       // the block's rows takes one table entry for every pair.
       bool uniform = false;
       int32_t ue = 0;
-      if (strided && all_same) {
+      if (strided && all_same && !lab_on) {
         constexpr int32_t SK = TT::kSubKeys;
         const int32_t q0 = __builtin_amdgcn_readlane(qpos, 0);
         const int32_t q1 = __builtin_amdgcn_readlane(qpos, TT::kRowsPerBlock - 1);
@@ -1038,11 +1194,12 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
         if (k0 - q1 >= br.k) { uniform = true; ue = 2 * br.k; }
         else if (k1 - q0 <= -br.k) { uniform = true; ue = 0; }
       }
-      if (uniform) badd = br.tab[qi * br.row_stride + ue];  // per query row with label vectors
+      if (LBL && lab_on) add_bias_labels<T>(s, lw, sm, buf, br, lr, sb, qi, qpos, lane);
+      else if (uniform) badd = br.tab[qi * br.row_stride + ue];  // per query row with label vectors
       else add_bias<T>(s, sm, buf, br, sb, qi, qpos, lane, all_same);
     }
     if (cls[sb] == kPartial) mask_tile<T>(s, sm, buf, mr, sb, kcount, qi, qpos, lane);
-    if (SEG && seg_check) mask_segments<T>(s, sm, buf, sb, gi.sq, lane);
+    if (SEG && seg_check) mask_segments<T, LBL>(s, sm, buf, sb, gi, lr, lane);
     sub_update<T, BIAS>(sm, buf, w, lane, sb, s, scale_log2, badd);
   }
 }
@@ -1056,16 +1213,17 @@ struct BufTag {
 // The key-tile loop: tiles 0..n_tiles-1 described by desc(n, KeyTile&, MaskRule&),
 // all strided with one stride or all gathered (GATHER); BIAS: br holds a bias
 // table (compiled out otherwise); SEG: gi holds segment ids (compiled out
-// otherwise). only_sb >= 0: this
+// otherwise); LBL: br may hold per-pair labels and gi may restrict the segment
+// mask to some pieces (compiled out otherwise). only_sb >= 0: this
 // wave computes only that key sub-tile of every tile (the others are left to
 // other waves holding the same rows).
-template <typename T, bool GATHER, bool BIAS, bool SEG, typename Desc>
+template <typename T, bool GATHER, bool BIAS, bool SEG, bool LBL, typename Desc>
 __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
                                           typename TileTraits<T>::Wave& w, const T* kb,
                                           const T* vb, int32_t n_tiles, Desc desc,
-                                          const BiasRule& br, const GlobInfo& gi, int32_t qi,
-                                          int32_t qpos, bool dead, float scale_log2,
-                                          int32_t only_sb = -1) {
+                                          const BiasRule& br, const GlobInfo& gi,
+                                          const LabelRule& lr, int32_t qi, int32_t qpos,
+                                          bool dead, float scale_log2, int32_t only_sb = -1) {
   using TT = TileTraits<T>;
   const int32_t tid = threadIdx.x, lane = tid & 63;
   if (n_tiles <= 0) return;
@@ -1076,7 +1234,7 @@ __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
   const FetchPlan fp = TT::plan(kt.stride, tid);
   TT::template fetch<GATHER>(pf, sm, 0, kb, vb, kt, fp, tid);
   TT::stage(sm, 0, pf, tid);
-  stage_meta<T, SEG>(sm, 0, pf.meta, gi, kt.gmode, tid);
+  stage_meta<T, SEG, LBL>(sm, 0, pf.meta, gi, lr, kt.gmode, tid);
   __syncthreads();
   // Tile n computes from LDS buffer n & 1 while tile n + 1 loads into the
   // other. The loop is unrolled by two so that the buffer of each step is a
@@ -1090,11 +1248,11 @@ __device__ __forceinline__ void run_tiles(typename TileTraits<T>::Smem& sm,
       desc(n + 1, kt_next, mr_next);
       TT::template fetch<GATHER>(pf, sm, buf ^ 1, kb, vb, kt_next, fp, tid);
     }
-    process_tile<T, BIAS, SEG>(sm, buf, w, lane, mr, br, gi, kt, !GATHER, qi, qpos, dead, scale_log2,
+    process_tile<T, BIAS, SEG, LBL>(sm, buf, w, lane, mr, br, gi, lr, kt, !GATHER, qi, qpos, dead, scale_log2,
                           only_sb);
     if (more) {
       TT::stage(sm, buf ^ 1, pf, tid);
-      stage_meta<T, SEG>(sm, buf ^ 1, pf.meta, gi, kt_next.gmode, tid);
+      stage_meta<T, SEG, LBL>(sm, buf ^ 1, pf.meta, gi, lr, kt_next.gmode, tid);
       kt = kt_next;
       mr = mr_next;
     }

@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .workloads import Workload
+from .workloads import LABEL_DISTANCE, Workload, etc_structure
 
 
 def band_global_pairs(w: Workload) -> int:
@@ -51,6 +51,25 @@ def band_global_pairs(w: Workload) -> int:
     return total * w.B
 
 
+def structured_pairs(w: Workload) -> int:
+    """Allowed pairs of an ETC structured workload (globals first, non-causal,
+    no dilation): a global row sees every key its label row does not mask; a
+    long row sees the long keys of its band inside its own context (l2l
+    segment mask) and every global its label row does not mask."""
+    st = etc_structure(w)
+    V = st["n_labels"]
+    ng, N, R = len(w.global_idx), w.N, w.radius
+    masked = lambda lab: (lab != LABEL_DISTANCE) & (lab >= V)
+    g_rows = int((~masked(st["glabel"][0])).sum())
+    l2g = int((~masked(st["llabel"][0][ng:])).sum())
+    seg = st["seg"][0].astype(np.int64)
+    l2l = 0
+    for i in range(ng, N):
+        lo, hi = max(ng, i - R), min(N - 1, i + R)
+        l2l += int((seg[lo:hi + 1] == seg[i]).sum())
+    return w.B * w.H * (g_rows + l2g + l2l)
+
+
 def dilated_pairs_head(w: Workload, h: int) -> int:
     """Pairs attended by all (w, r) patterns in head h of one batch row (a pair
     counted once per pattern): per segment, the kept rows of the head's offset
@@ -87,6 +106,8 @@ def useful_pairs(w: Workload) -> int:
         return dilated_pairs(w)
     if w.kind == "fixed":
         return fixed_pairs(w)
+    if w.structure:
+        return structured_pairs(w)
     return band_global_pairs(w)
 
 
@@ -101,6 +122,10 @@ def algorithmic_bytes(w: Workload) -> int:
     if w.separate_global:
         b += 2 * t + w.B * w.H * len(w.global_idx) * w.D * el
     if w.rel_k:
-        b += w.H * (2 * w.rel_k + 1) * 4
+        nv = w.H * (2 * w.rel_k + 1 + (4 if w.structure else 0))
+        b += nv * 4 * {"scalar": 1, "vector": w.D, "both": w.D + 1}[w.rel_kind]
+    if w.structure:  # the two label matrices and the segment ids
+        ng = len(w.global_idx)
+        b += w.B * (2 * ng * w.N + 4 * w.N)
     b += len(w.global_idx) * 4
     return b

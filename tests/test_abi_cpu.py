@@ -38,7 +38,7 @@ def test_header_declares_the_binding_exports():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_symbols():
         assert hasattr(L, name), name
-    assert la.la_version() == 1
+    assert la.la_version() == 2
 
 
 def _attn(L, dims, q=FAKE, k=FAKE, v=FAKE, gidx=None, n_global=0, radius=0, dil=None,
@@ -74,6 +74,16 @@ def test_attn_argument_errors(L):
     assert _attn(L, d, ext=LaAttnExt(2, None, None, None, None, 0, FAKE + 4)) == la.LA_EINVAL
     # segment ids must be 4-byte aligned
     assert _attn(L, d, ext=LaAttnExt(0, None, None, None, None, 0, None, FAKE + 2)) == la.LA_EINVAL
+    # structural labels: vocabulary size, label matrices and piece selection
+    E = lambda rk, nl=0, gl=None, ll=None, sp=0: LaAttnExt(rk, None, None, None, None, 0, None,
+                                                          None, gl, ll, nl, sp)
+    assert _attn(L, d, rel_bias=FAKE, ext=E(2, nl=4)) == la.LA_EINVAL     # below 2k+1
+    assert _attn(L, d, rel_bias=FAKE, ext=E(2, nl=65)) == la.LA_EUNSUPPORTED
+    assert _attn(L, d, ext=E(0, nl=8)) == la.LA_EINVAL                     # labels, no table
+    assert _attn(L, d, ext=E(0, gl=FAKE)) == la.LA_EINVAL                  # no global tokens
+    assert _attn(L, d, ext=E(0, ll=FAKE)) == la.LA_EINVAL
+    assert _attn(L, d, ext=E(0, sp=16)) == la.LA_EINVAL
+    assert _attn(L, d, ext=E(0, sp=-1)) == la.LA_EINVAL
     # globals need a large enough workspace
     assert _attn(L, d, gidx=FAKE, n_global=4) == la.LA_EINVAL
     need = la.la_attn_workspace_size(d, 4)

@@ -4,7 +4,7 @@
 TFLOP/s figure the bench reports. Here it is checked against the number of
 allowed (query, key) pairs the fp64 oracle's mask predicates give, read as
 exp(lse) with Q = K = V = 0 (every logit 0, so each row's softmax denominator
-is its key count, or multiplicity sum for LongNet), for all eight workloads.
+is its key count, or multiplicity sum for LongNet), for all nine workloads.
 Band workloads are counted over every row (heads with the same pattern are
 counted once and multiplied). The two 32K-token workloads are counted over
 every row of three heads with distinct offsets; their totals over all heads
@@ -32,7 +32,15 @@ def _band_count(w: W.Workload) -> int:
         seg = W.make_inputs(w.with_(B=1, H=1, N=w.N)).seg.numpy()
         B = 1
     z = np.zeros((B, len(distinct), w.N, DZ))
-    _, lse = oracle.attn_rows(z, z, z, w.global_idx, w.radius, distinct, w.causal, seg=seg)
+    kw = {}
+    if w.structure:  # label matrices and the piece-selected segment ids
+        st = W.etc_structure(w.with_(B=1))
+        B, seg = 1, st["seg"]
+        z = np.zeros((B, len(distinct), w.N, DZ))
+        # a zero table of the full vocabulary: structural labels count as allowed
+        kw = dict(glabel=st["glabel"], llabel=st["llabel"], seg_pieces=st["seg_pieces"],
+                  rel_bias=np.zeros((len(distinct), st["n_labels"])), rel_k=w.rel_k)
+    _, lse = oracle.attn_rows(z, z, z, w.global_idx, w.radius, distinct, w.causal, seg=seg, **kw)
     per = {d: int(np.rint(np.exp(lse[:, x])).sum()) for x, d in enumerate(distinct)}
     rows_b = w.B // B
     return rows_b * sum(per[d] for d in dils)

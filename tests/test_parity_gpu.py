@@ -47,9 +47,20 @@ def to64(t):
     return None if t is None else t.detach().to("cpu", torch.float64).numpy()
 
 
+def label_kw(inp: W.Inputs, dev=None):
+    """Structural labels and piece-selected segment masks of the inputs, if any."""
+    if inp.glabel is None and inp.llabel is None and not inp.seg_pieces:
+        return {}
+    cv = (lambda t: None if t is None else t.to(dev)) if dev is not None else \
+        (lambda t: None if t is None else t.numpy())
+    return dict(glabel=cv(inp.glabel), llabel=cv(inp.llabel), seg_pieces=inp.seg_pieces,
+                rel_k=inp.rel_k)
+
+
 def gpu_attn(w: W.Workload, inp: W.Inputs, dev, **kw):
     g = torch.tensor(w.global_idx, dtype=torch.int32, device=dev) if w.global_idx else None
     d = lambda t: None if t is None else t.to(dev)
+    kw = {**label_kw(inp, dev), **kw}
     out, lse = la.la_attn_forward(d(inp.q), d(inp.k), d(inp.v), g, w.radius, w.dilation, w.causal,
                                   d(inp.rel_bias), qg=d(inp.qg), kg=d(inp.kg), vg=d(inp.vg),
                                   rel_vec=d(inp.rel_vec), seg_ids=d(inp.seg), **kw)
@@ -68,7 +79,7 @@ def oracle_attn(w: W.Workload, inp: W.Inputs, sel=None):
     return oracle.attn_rows(to64(inp.q), to64(inp.k), to64(inp.v), w.global_idx, w.radius,
                             w.dilation, w.causal, to64(inp.rel_bias), to64(inp.qg), to64(inp.kg),
                             to64(inp.vg), sel=sel, rel_vec=to64(inp.rel_vec),
-                            seg=None if inp.seg is None else inp.seg.numpy())
+                            seg=None if inp.seg is None else inp.seg.numpy(), **label_kw(inp))
 
 
 def gpu_fixed(w: W.Workload, inp: W.Inputs, dev):
