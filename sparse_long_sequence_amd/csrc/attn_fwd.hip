@@ -564,7 +564,9 @@ hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream) {
   const uint32_t dyn = a.rel_vec ? (uint32_t)(rows * a.n_labels * sizeof(float)) : 0u;
   const bool bias = a.rel_bias != nullptr || a.rel_vec != nullptr;
   const bool seg = a.seg != nullptr;
-  const bool lbl = a.glabel != nullptr || a.llabel != nullptr || (seg && a.seg_pieces != 15);
+  // the label kernel also reads tables wider than the 2k+1 distance labels
+  const bool lbl = a.glabel != nullptr || a.llabel != nullptr || (seg && a.seg_pieces != 15) ||
+                   (bias && a.n_labels != 2 * a.rel_k + 1);
   const dim3 g((uint32_t)grid);
   if (dtype == 1) {
     const dim3 b(TileTraits<bf16>::kThreads);

@@ -159,6 +159,21 @@ def test_labels_without_tables(dev):
         compare(f"labels-masks-only/{which}", w.dtype, out, lse, o_ref, l_ref)
 
 
+def test_wide_table_without_matrices(dev):
+    # a vocabulary wider than the 2k+1 distance labels but no label matrix:
+    # only the distance labels are reached, from tables of V entries per head
+    G = (0, 1, 2, 100, 250)
+    w = W.Workload("wide-table", B=1, H=3, N=400, radius=30, global_idx=G, seed=159)
+    inp = W.make_inputs(w)
+    gen = torch.Generator().manual_seed(161)
+    inp.rel_k, V = 4, 13
+    inp.rel_bias = 0.3 * torch.randn(3, V, generator=gen)
+    inp.rel_vec = 0.3 * torch.randn(3, V, w.D, generator=gen)
+    say("case wide-table")
+    out, lse, o_ref, l_ref = run_both(w, inp, dev)
+    compare("wide-table", w.dtype, out, lse, o_ref, l_ref)
+
+
 # --------------------------------------------------------------------------
 # segment masks on some pieces only
 # --------------------------------------------------------------------------
@@ -215,6 +230,9 @@ def test_label_masks_exact(dev):
     rng = np.random.default_rng(157)
     gl = rng.choice([DIST, MASK], p=[0.7, 0.3], size=(B, len(G), N)).astype(np.uint8)
     ll = rng.choice([DIST, MASK, 0], p=[0.5, 0.3, 0.2], size=(B, N, len(G))).astype(np.uint8)
+    gl[0, 5, :] = MASK        # a global row with no allowed key: zeros, lse = -inf
+    gl[1, 7, :] = MASK
+    gl[1, 7, 900] = DIST      # ... and one with a single key
     inp.glabel, inp.llabel = torch.from_numpy(gl), torch.from_numpy(ll)
     inp.seg = torch.tensor(np.stack([np.repeat([0, 1], [600, 400])] * B), dtype=torch.int32)
     inp.seg_pieces = 8
@@ -223,6 +241,7 @@ def test_label_masks_exact(dev):
     o, l = to64(out), to64(lse)
     fin = np.isfinite(l_ref)
     assert np.array_equal(np.isfinite(l), fin)
+    assert not fin[0, :, 5].any() and np.all(o[0, :, 5] == 0)
     # lse = log(count) exactly up to the bf16 rounding of nothing (all logits 0)
     cnt_ref = np.rint(np.exp(l_ref[fin]))
     cnt = np.rint(np.exp(l[fin]))
