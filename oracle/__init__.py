@@ -102,7 +102,7 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.lo_attn_backward.restype = ctypes.c_int32
     lib.lo_attn_backward.argtypes = [ctypes.c_int32] * 4 + [_f64p] * 6 + [
         _i32p, ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p] + [_f64p] * 7 + [
-        ctypes.c_int32]
+        ctypes.c_int32, _f64p, _f64p, ctypes.c_int32, _u8p, _u8p, ctypes.c_int32, ctypes.c_int32]
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -165,6 +165,43 @@ LABEL_DISTANCE = 0xFE  # a pair's usual clipped-distance label
 LABEL_MASKED = 0xFF    # any value >= the vocabulary size (but LABEL_DISTANCE) masks the pair
 
 
+def _labels(rel_bias, rel_vec, rel_k, glabel, llabel, B, H, N, D, n_global):
+    """Checked bias tables and label matrices: (rel_bias, rel_vec, rel_k,
+    n_labels, glabel, llabel) in the library's types (n_labels 0: no table)."""
+    rb = None if rel_bias is None else _f64(rel_bias)
+    rv = None if rel_vec is None else _f64(rel_vec)
+    V = None
+    if rb is not None:
+        if rb.ndim != 2 or rb.shape[0] != H:
+            raise ValueError("rel_bias must be [H, V]")
+        V = rb.shape[1]
+    if rv is not None:
+        if rv.ndim != 3 or rv.shape[0] != H or rv.shape[2] != D:
+            raise ValueError("rel_vec must be [H, V, D]")
+        if V is not None and rv.shape[1] != V:
+            raise ValueError("rel_bias and rel_vec need the same vocabulary")
+        V = rv.shape[1]
+    rk = 0
+    if V is not None:
+        if rel_k is None:
+            if V % 2 != 1:
+                raise ValueError("give rel_k with a vocabulary of structural labels")
+            rel_k = (V - 1) // 2
+        rk = int(rel_k)
+        if V < 2 * rk + 1:
+            raise ValueError("the vocabulary holds fewer than 2k+1 labels")
+    gl = ll = None
+    if glabel is not None:
+        gl = np.ascontiguousarray(np.asarray(glabel, dtype=np.uint8))
+        if gl.shape != (B, n_global, N):
+            raise ValueError("glabel must be [B, n_global, N]")
+    if llabel is not None:
+        ll = np.ascontiguousarray(np.asarray(llabel, dtype=np.uint8))
+        if ll.shape != (B, N, n_global):
+            raise ValueError("llabel must be [B, N, n_global]")
+    return rb, rv, rk, 0 if V is None else V, gl, ll
+
+
 def attn_rows(q, k, v, global_idx=(), radius: int = 0, dilation=None, causal: bool = False,
               rel_bias=None, qg=None, kg=None, vg=None, sel=None, n_threads: int = 0, lib=None,
               rel_vec=None, seg=None, rel_k=None, glabel=None, llabel=None, seg_pieces: int = 0):
@@ -201,43 +238,13 @@ def attn_rows(q, k, v, global_idx=(), radius: int = 0, dilation=None, causal: bo
     dil = None if dilation is None else _i32(dilation)
     if dil is not None and dil.shape != (H,):
         raise ValueError("dilation must have one entry per head")
-    rb = None if rel_bias is None else _f64(rel_bias)
-    rv = None if rel_vec is None else _f64(rel_vec)
-    V = None
-    if rb is not None:
-        if rb.ndim != 2 or rb.shape[0] != H:
-            raise ValueError("rel_bias must be [H, V]")
-        V = rb.shape[1]
-    if rv is not None:
-        if rv.ndim != 3 or rv.shape[0] != H or rv.shape[2] != D:
-            raise ValueError("rel_vec must be [H, V, D]")
-        if V is not None and rv.shape[1] != V:
-            raise ValueError("rel_bias and rel_vec need the same vocabulary")
-        V = rv.shape[1]
-    rk = 0
-    if V is not None:
-        if rel_k is None:
-            if V % 2 != 1:
-                raise ValueError("give rel_k with a vocabulary of structural labels")
-            rel_k = (V - 1) // 2
-        rk = int(rel_k)
-        if V < 2 * rk + 1:
-            raise ValueError("the vocabulary holds fewer than 2k+1 labels")
-    nlab = 0 if V is None else V
+    rb, rv, rk, nlab, gl, ll = _labels(rel_bias, rel_vec, rel_k, glabel, llabel, B, H, N, D,
+                                       g.shape[0])
     sg = None
     if seg is not None:
         sg = _i32(seg)
         if sg.shape != (B, N):
             raise ValueError("seg must be [B, N]")
-    gl = ll = None
-    if glabel is not None:
-        gl = np.ascontiguousarray(np.asarray(glabel, dtype=np.uint8))
-        if gl.shape != (B, g.shape[0], N):
-            raise ValueError("glabel must be [B, n_global, N]")
-    if llabel is not None:
-        ll = np.ascontiguousarray(np.asarray(llabel, dtype=np.uint8))
-        if ll.shape != (B, N, g.shape[0]):
-            raise ValueError("llabel must be [B, N, n_global]")
     s, n = _sel(sel, B, H, N)
     out = np.zeros((n, D), dtype=np.float64)
     lse = np.zeros((n,), dtype=np.float64)
@@ -256,12 +263,13 @@ def attn_rows(q, k, v, global_idx=(), radius: int = 0, dilation=None, causal: bo
 
 def attn_backward(q, k, v, dout, global_idx=(), radius: int = 0, dilation=None,
                   causal: bool = False, qg=None, kg=None, vg=None, seg=None, n_threads: int = 0,
-                  lib=None):
+                  lib=None, rel_bias=None, rel_vec=None, rel_k=None, glabel=None, llabel=None,
+                  seg_pieces: int = 0):
     """Gradients of band + global attention in fp64 for upstream gradient ``dout``.
 
-    Arguments as in :func:`attn_rows` (no bias). Returns ``(dq, dk, dv)``, or
-    ``(dq, dk, dv, dqg, dkg, dvg)`` with separate global projections, each
-    ``[B,H,N,D]`` float64.
+    Arguments as in :func:`attn_rows` (the bias tables are inputs, not
+    differentiated). Returns ``(dq, dk, dv)``, or ``(dq, dk, dv, dqg, dkg,
+    dvg)`` with separate global projections, each ``[B,H,N,D]`` float64.
     """
     lib = lib or load()
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
@@ -279,12 +287,15 @@ def attn_backward(q, k, v, dout, global_idx=(), radius: int = 0, dilation=None,
     sg = None if seg is None else _i32(seg)
     if sg is not None and sg.shape != (B, N):
         raise ValueError("seg must be [B, N]")
+    rb, rv, rk, nlab, gl, ll = _labels(rel_bias, rel_vec, rel_k, glabel, llabel, B, H, N, D,
+                                       g.shape[0])
     grads = [np.zeros_like(q) for _ in range(6 if all(sep) else 3)]
     ptr = [_p(x, _f64p) for x in grads] + [None] * (6 - len(grads))
     rc = lib.lo_attn_backward(B, H, N, D, _p(q, _f64p), _p(k, _f64p), _p(v, _f64p),
                               _p(qg, _f64p), _p(kg, _f64p), _p(vg, _f64p), _p(g, _i32p),
                               g.shape[0], radius, _p(dil, _i32p), int(causal), _p(sg, _i32p),
-                              _p(do, _f64p), *ptr, n_threads)
+                              _p(do, _f64p), *ptr, n_threads, _p(rb, _f64p), _p(rv, _f64p), rk,
+                              _p(gl, _u8p), _p(ll, _u8p), nlab, int(seg_pieces))
     if rc != 0:
         raise ValueError("lo_attn_backward rejected its arguments")
     return tuple(grads)

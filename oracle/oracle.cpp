@@ -235,6 +235,51 @@ int32_t lo_longnet_mult_rows(int32_t N, int32_t head, const int32_t* w, const in
   return 0;
 }
 
+// The pairs of one row of the band + global pattern with its per-instance
+// inputs (segment ids, the pieces they mask, per-pair label matrices; see
+// lo_attn_rows): for query i of batch row b and head h, weight[j] is the mask
+// entry c_ij (0 or 1) and lab[j] the pair's label in the vocabulary of V
+// entries, -1 when the pair takes no label (a mixed pair keeping its usual
+// label, or no bias tables at all).
+struct RowRule {
+  int32_t N, radius, causal, rel_k, V, pieces, n_global;
+  const int32_t* dilation;
+  const int32_t* seg;
+  const uint8_t* glabel;
+  const uint8_t* llabel;
+  const uint8_t* is_glob;
+  const int32_t* grank;
+  bool has_tables;
+
+  void fill(int32_t b, int32_t h, int32_t i, double* weight, int32_t* lab) const {
+    const int32_t dil = dilation ? dilation[h] : 1;
+    const bool ig = is_glob[i] != 0;
+    const int32_t* sb = seg ? seg + (size_t)b * N : nullptr;
+    for (int32_t j = 0; j < N; ++j) {
+      const bool jg = is_glob[j] != 0;
+      weight[j] = mask_entry(i, j, ig, jg, radius, dil, causal);
+      const int32_t piece = ig ? (jg ? 1 : 2) : (jg ? 4 : 8);  // g2g, g2l, l2g, l2l
+      if (sb && (pieces & piece) && sb[j] != sb[i]) weight[j] = 0.0;  // another segment
+      int32_t l = kLabelDistance;
+      if (ig && glabel)
+        l = glabel[((size_t)b * n_global + grank[i]) * N + j];
+      else if (!ig && jg && llabel)
+        l = llabel[((size_t)b * N + i) * n_global + grank[j]];
+      if (l != kLabelDistance && l >= V) weight[j] = 0.0;  // M = 0
+      if (l == kLabelDistance) {
+        if (jg != ig) {
+          l = -1;  // mixed global/non-global pair: no label
+        } else {
+          int64_t dlt = (int64_t)j - i;
+          dlt = std::max<int64_t>(-rel_k, std::min<int64_t>(rel_k, dlt));
+          l = (int32_t)(dlt + rel_k);
+        }
+      }
+      lab[j] = (has_tables && weight[j] != 0.0) ? l : -1;
+    }
+  }
+};
+
 // Band + global attention (Longformer / ETC), fp64. seg: [B][N] segment ids
 // or null; with it, c_ij also needs seg[b][i] == seg[b][j] (ETC page, §3.4
 // "Per-instance attention masks": documents packed into one input are masked
@@ -292,10 +337,11 @@ int32_t lo_attn_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q
       is_glob[gidx[g]] = 1;
       grank[gidx[g]] = g;
     }
+  const RowRule rule = {N, radius, causal, rel_k, V, pieces, n_global, dilation, seg, glabel,
+                        llabel, is_glob.data(), grank.data(), rel_bias || rel_vec};
   parallel_rows(rows, n_threads, [&](int64_t x) {
     int32_t b, h, i;
     decode_row(sel, x, H, N, b, h, i);
-    const int32_t dil = dilation ? dilation[h] : 1;
     const bool ig = is_glob[i] != 0;
     const size_t head_off = ((size_t)b * H + h) * (size_t)N * D;
     // Global rows with separate projections use qg_i, kg_j, vg_j.
@@ -303,32 +349,15 @@ int32_t lo_attn_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q
     const double* qi = (sep ? qg : q) + head_off + (size_t)i * D;
     const double* kb = (sep ? kg : k) + head_off;
     const double* vb = (sep ? vg : v) + head_off;
-    std::vector<double> weight(N);
-    std::vector<int32_t> label(N, kLabelDistance);  // each pair's label
-    const int32_t* sb = seg ? seg + (size_t)b * N : nullptr;
-    for (int32_t j = 0; j < N; ++j) {  // the explicit mask row c_i,:
-      const bool jg = is_glob[j] != 0;
-      weight[j] = mask_entry(i, j, ig, jg, radius, dil, causal);
-      const int32_t piece = ig ? (jg ? 1 : 2) : (jg ? 4 : 8);  // g2g, g2l, l2g, l2l
-      if (sb && (pieces & piece) && sb[j] != sb[i]) weight[j] = 0.0;  // another segment
-      if (ig && glabel)
-        label[j] = glabel[((size_t)b * n_global + grank[i]) * N + j];
-      else if (!ig && jg && llabel)
-        label[j] = llabel[((size_t)b * N + i) * n_global + grank[j]];
-      if (label[j] != kLabelDistance && label[j] >= V) weight[j] = 0.0;  // M = 0
-    }
+    std::vector<double> weight(N);  // the explicit mask row c_i,:
+    std::vector<int32_t> label(N);  // each pair's label (-1: none)
+    rule.fill(b, h, i, weight.data(), label.data());
     const double* tab = rel_bias ? rel_bias + (size_t)h * V : nullptr;
     const double* vec = rel_vec ? rel_vec + (size_t)h * V * D : nullptr;
     const double scale = 1.0 / std::sqrt((double)D);
     auto bias = [&](int32_t j) -> double {
-      if (!tab && !vec) return 0.0;
-      int32_t l = label[j];
-      if (l == kLabelDistance) {
-        if ((is_glob[j] != 0) != ig) return 0.0;  // mixed global/non-global pair
-        int64_t dlt = (int64_t)j - i;
-        dlt = std::max<int64_t>(-rel_k, std::min<int64_t>(rel_k, dlt));
-        l = (int32_t)(dlt + rel_k);
-      }
+      const int32_t l = label[j];
+      if (l < 0) return 0.0;
       double b = tab ? tab[l] : 0.0;
       if (vec) {  // q_i . a_l / sqrt(D): the key-side vector's share of the logit
         const double* al = vec + (size_t)l * D;
@@ -351,38 +380,56 @@ int32_t lo_attn_rows(int32_t B, int32_t H, int32_t N, int32_t D, const double* q
 //   dV_j  = sum_i P_ij dO_i           dP_ij = dO_i . v_j
 //   D_i   = sum_j P_ij dP_ij          dS_ij = P_ij (dP_ij - D_i)
 //   dQ_i  = sum_j dS_ij k_j / sqrt(D)  dK_j = sum_i dS_ij q_i / sqrt(D)
-// The mask is lo_attn_rows's (pattern, causal, segments); no bias. A global
-// row with separate projections differentiates through qg_i, kg_j, vg_j, so its
-// terms go to dqg, dkg, dvg (given iff qg, kg, vg are). Heads are split over
-// threads; rows are visited in order within a head, so sums are deterministic.
+// The mask and the logits are lo_attn_rows's (pattern, causal, segment ids and
+// their pieces, per-pair labels, the scalar bias b_l and the key-side vectors
+// a_l of the pair's label l): z_ij = q_i . (k_j + a_l) / sqrt(D) + b_l. The
+// tables are inputs, not differentiated; a_l adds dS_ij a_l / sqrt(D) to dQ_i.
+// A global row with separate projections differentiates through qg_i, kg_j,
+// vg_j, so its terms go to dqg, dkg, dvg (given iff qg, kg, vg are). Heads are
+// split over threads; rows are visited in order within a head, so sums are
+// deterministic.
 int32_t lo_attn_backward(int32_t B, int32_t H, int32_t N, int32_t D, const double* q,
                          const double* k, const double* v, const double* qg, const double* kg,
                          const double* vg, const int32_t* gidx, int32_t n_global, int32_t radius,
                          const int32_t* dilation, int32_t causal, const int32_t* seg,
                          const double* dout, double* dq, double* dk, double* dv, double* dqg,
-                         double* dkg, double* dvg, int32_t n_threads) {
+                         double* dkg, double* dvg, int32_t n_threads, const double* rel_bias,
+                         const double* rel_vec, int32_t rel_k, const uint8_t* glabel,
+                         const uint8_t* llabel, int32_t n_labels, int32_t seg_pieces) {
   if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || radius < 0 || n_global < 0) return -1;
   if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
   const bool sep_all = qg && kg && vg && dqg && dkg && dvg;
   if ((qg || kg || vg || dqg || dkg || dvg) && !sep_all) return -1;
   if (n_global > 0 && !gidx) return -1;
+  if ((rel_bias || rel_vec) && rel_k < 0) return -1;
+  const int32_t V = n_labels > 0 ? n_labels : 2 * rel_k + 1;  // vocabulary size
+  if (n_labels > 0 && n_labels < 2 * rel_k + 1) return -1;
+  if ((glabel || llabel) && n_global == 0) return -1;
   if (dilation)
     for (int32_t h = 0; h < H; ++h)
       if (dilation[h] < 1) return -1;
   std::vector<uint8_t> is_glob(N, 0);
+  std::vector<int32_t> grank(N, -1);
   for (int32_t g = 0; g < n_global; ++g)
-    if (gidx[g] >= 0 && gidx[g] < N) is_glob[gidx[g]] = 1;
+    if (gidx[g] >= 0 && gidx[g] < N) {
+      is_glob[gidx[g]] = 1;
+      grank[gidx[g]] = g;
+    }
+  const RowRule rule = {N, radius, causal, rel_k, V, seg_pieces ? seg_pieces : 15, n_global,
+                        dilation, seg, glabel, llabel, is_glob.data(), grank.data(),
+                        rel_bias || rel_vec};
   const double scale = 1.0 / std::sqrt((double)D);
   const size_t head_elems = (size_t)N * D;
   parallel_rows((int64_t)B * H, n_threads, [&](int64_t bh) {
     const int32_t b = (int32_t)(bh / H), h = (int32_t)(bh % H);
-    const int32_t dil = dilation ? dilation[h] : 1;
     const size_t off = (size_t)bh * head_elems;
     double* outs[6] = {dq, dk, dv, dqg, dkg, dvg};
     for (double* o : outs)
       if (o) std::fill(o + off, o + off + head_elems, 0.0);
-    const int32_t* segb = seg ? seg + (size_t)b * N : nullptr;
-    std::vector<double> P(N), dP(N);
+    const double* tab = rel_bias ? rel_bias + (size_t)h * V : nullptr;
+    const double* vec = rel_vec ? rel_vec + (size_t)h * V * D : nullptr;
+    std::vector<double> P(N), dP(N), weight(N);
+    std::vector<int32_t> lab(N);
     for (int32_t i = 0; i < N; ++i) {
       const bool ig = is_glob[i] != 0;
       const bool sep = ig && sep_all;
@@ -394,17 +441,18 @@ int32_t lo_attn_backward(int32_t B, int32_t H, int32_t N, int32_t D, const doubl
       double* dvb = (sep ? dvg : dv) + off;
       const double* doi = dout + off + (size_t)i * D;
       // forward of row i: the allowed keys' probabilities
+      rule.fill(b, h, i, weight.data(), lab.data());
       double M = -std::numeric_limits<double>::infinity();
       for (int32_t j = 0; j < N; ++j) {
-        bool c = mask_entry(i, j, ig, is_glob[j] != 0, radius, dil, causal) != 0;
-        if (segb && segb[j] != segb[i]) c = false;
-        if (!c) {
+        if (weight[j] == 0.0) {
           P[j] = -std::numeric_limits<double>::infinity();
           continue;
         }
         double dot = 0.0;
         for (int32_t d = 0; d < D; ++d) dot += qi[d] * kb[(size_t)j * D + d];
-        P[j] = dot * scale;  // the logit for now
+        if (lab[j] >= 0 && vec)
+          for (int32_t d = 0; d < D; ++d) dot += qi[d] * vec[(size_t)lab[j] * D + d];
+        P[j] = dot * scale + (lab[j] >= 0 && tab ? tab[lab[j]] : 0.0);  // the logit for now
         M = std::max(M, P[j]);
       }
       if (M == -std::numeric_limits<double>::infinity()) continue;  // no key: O = 0, no gradient
@@ -428,9 +476,10 @@ int32_t lo_attn_backward(int32_t B, int32_t H, int32_t N, int32_t D, const doubl
       for (int32_t j = 0; j < N; ++j) {
         if (P[j] == 0.0) continue;
         const double dS = P[j] * (dP[j] - Di);
+        const double* al = lab[j] >= 0 && vec ? vec + (size_t)lab[j] * D : nullptr;
         for (int32_t d = 0; d < D; ++d) {
           dvb[(size_t)j * D + d] += P[j] * doi[d];
-          dqi[d] += dS * kb[(size_t)j * D + d] * scale;
+          dqi[d] += dS * (kb[(size_t)j * D + d] + (al ? al[d] : 0.0)) * scale;
           dkb[(size_t)j * D + d] += dS * qi[d] * scale;
         }
       }

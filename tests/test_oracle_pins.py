@@ -655,6 +655,49 @@ def pin_backward_finite_differences(lib):
                 assert abs(fd - g[x]) <= 1e-6 * (1 + abs(fd)), (c, x, fd, g[x])
 
 
+def pin_backward_labels_finite_differences(lib):
+    """The backward with a scalar bias table, key-side label vectors, per-pair
+    label matrices (masked pairs among them) and segment masks on some pieces,
+    against central differences of the forward's loss sum(dO * O) (fp64, eps
+    1e-6); the tables are inputs, not differentiated."""
+    rng = np.random.default_rng(29)
+    cases = [
+        dict(N=17, glob=(0, 6, 7), R=2, dil=[1, 2], causal=False, sep=True, pieces=9, kk=2, ns=3),
+        dict(N=15, glob=(2, 9), R=3, dil=[1, 1], causal=True, sep=False, pieces=6, kk=1, ns=2),
+    ]
+    for c in cases:
+        B, H, N, D = 2, 2, c["N"], 4
+        G = c["glob"]
+        V = 2 * c["kk"] + 1 + c["ns"]
+        q, k, v = rand_qkv(rng, B, H, N, D)
+        qg, kg, vg = rand_qkv(rng, B, H, N, D) if c["sep"] else (None, None, None)
+        tab = 0.5 * rng.standard_normal((H, V))
+        vec = 0.5 * rng.standard_normal((H, V, D))
+        vals = [0, 1, V - 1, DIST, DIST, DIST, MASK]
+        glabel = rng.choice(vals, size=(B, len(G), N)).astype(np.uint8)
+        llabel = rng.choice(vals, size=(B, N, len(G))).astype(np.uint8)
+        seg = (np.arange(N)[None] * 3 // N).repeat(B, 0)
+        dout = rng.standard_normal((B, H, N, D))
+        kw = dict(global_idx=G, radius=c["R"], dilation=c["dil"], causal=c["causal"], qg=qg,
+                  kg=kg, vg=vg, seg=seg, rel_bias=tab, rel_vec=vec, rel_k=c["kk"],
+                  glabel=glabel, llabel=llabel, seg_pieces=c["pieces"])
+        grads = oracle.attn_backward(q, k, v, dout, lib=lib, **kw)
+        tensors = [q, k, v] + ([qg, kg, vg] if c["sep"] else [])
+        eps = 1e-6
+        for t, g in zip(tensors, grads):
+            coords = [tuple(rng.integers(0, n) for n in t.shape) for _ in range(8)]
+            coords += [(0, 1, G[0], 2), (1, 0, G[1], 0)]  # global rows / keys
+            for x in coords:
+                old = t[x]
+                t[x] = old + eps
+                lp = _fd_loss(lib, (q, k, v), kw, dout)
+                t[x] = old - eps
+                lm = _fd_loss(lib, (q, k, v), kw, dout)
+                t[x] = old
+                fd = (lp - lm) / (2 * eps)
+                assert abs(fd - g[x]) <= 1e-6 * (1 + abs(fd)), (c, x, fd, g[x])
+
+
 def pin_backward_dense_autograd(lib):
     """A window covering every key, no global token: the gradients of dense
     softmax attention, from torch autograd in float64."""
@@ -974,7 +1017,8 @@ PINS = [pin_mask_matches_enumeration, pin_counts_closed_form, pin_counts_full_wo
         pin_fixed_pattern, pin_brute_force_longnet,
         pin_longnet_paths_agree,
         pin_rows_sum_to_one, pin_uncovered_rows, pin_sampled_rows_match_full,
-        pin_backward_finite_differences, pin_backward_dense_autograd,
+        pin_backward_finite_differences, pin_backward_labels_finite_differences,
+        pin_backward_dense_autograd,
         pin_backward_shift_invariants, pin_longnet_backward, pin_longnet_per_pattern_outputs,
         pin_longnet_backward_selected, pin_etc_structured_pieces, pin_labels_scattered_globals]
 
@@ -1006,7 +1050,7 @@ MUTANTS = [
     ("relvec-unscaled", "b += dot * scale;", "b += dot;"),
     ("relvec-against-key", "for (int32_t d = 0; d < D; ++d) dot += qi[d] * al[d];",
      "for (int32_t d = 0; d < D; ++d) dot += kb[(size_t)j * D + d] * al[d];"),
-    ("bias-on-mixed-pairs", "if ((is_glob[j] != 0) != ig) return 0.0;", ""),
+    ("bias-on-mixed-pairs", "if (jg != ig) {", "if (false) {"),
     ("shared-keys-for-global-rows", "const double* kb = (sep ? kg : k) + head_off;",
      "const double* kb = (sep ? k : k) + head_off;"),
     ("keys-as-values", "const double* vj = vbase + (size_t)j * D;",
@@ -1038,15 +1082,20 @@ MUTANTS = [
      "row.Di += row.c[j] * std::exp(row.logit[j] - row.lse) * dp;",
      "row.Di += std::exp(row.logit[j] - row.lse) * dp;"),
     ("selected-dv-from-dS", "dvj[d] += P * doi[d];", "dvj[d] += g * doi[d];"),
-    ("l2g-labels-transposed", "label[j] = llabel[((size_t)b * N + i) * n_global + grank[j]];",
-     "label[j] = llabel[((size_t)b * n_global + grank[j]) * N + i];"),
-    ("global-labels-by-position", "label[j] = glabel[((size_t)b * n_global + grank[i]) * N + j];",
-     "label[j] = glabel[((size_t)b * n_global + i) * N + j];"),
-    ("masked-label-ignored", "if (label[j] != kLabelDistance && label[j] >= V) weight[j] = 0.0;  // M = 0", ""),
+    ("l2g-labels-transposed", "l = llabel[((size_t)b * N + i) * n_global + grank[j]];",
+     "l = llabel[((size_t)b * n_global + grank[j]) * N + i];"),
+    ("global-labels-by-position", "l = glabel[((size_t)b * n_global + grank[i]) * N + j];",
+     "l = glabel[((size_t)b * n_global + i) * N + j];"),
+    ("masked-label-ignored", "if (l != kLabelDistance && l >= V) weight[j] = 0.0;  // M = 0", ""),
     ("segments-mask-every-piece", "const int32_t pieces = seg_pieces ? seg_pieces : 15;",
      "const int32_t pieces = 15;"),
-    ("explicit-labels-same-kind-only", "      if (!tab && !vec) return 0.0;\n      int32_t l = label[j];",
-     "      if (!tab && !vec) return 0.0;\n      if ((is_glob[j] != 0) != ig) return 0.0;\n      int32_t l = label[j];"),
+    ("explicit-labels-same-kind-only", "lab[j] = (has_tables && weight[j] != 0.0) ? l : -1;",
+     "lab[j] = (has_tables && weight[j] != 0.0 && jg == ig) ? l : -1;"),
+    ("backward-ignores-bias", "P[j] = dot * scale + (lab[j] >= 0 && tab ? tab[lab[j]] : 0.0);",
+     "P[j] = dot * scale;"),
+    ("backward-dq-without-label-vector",
+     "dqi[d] += dS * (kb[(size_t)j * D + d] + (al ? al[d] : 0.0)) * scale;",
+     "dqi[d] += dS * kb[(size_t)j * D + d] * scale;"),
     ("selected-dq-unscaled", "for (int32_t d = 0; d < D; ++d) dqi[d] += g * k[off + (size_t)j * D + d] * scale;",
      "for (int32_t d = 0; d < D; ++d) dqi[d] += g * k[off + (size_t)j * D + d];"),
 ]
