@@ -225,6 +225,16 @@ typedef struct {
   const int32_t *seg_ids;   /* device int32 [B][N] segment ids as given to the forward, or NULL */
   void *workspace;          /* la_attn_backward_workspace_size() bytes, 256-byte aligned */
   size_t workspace_bytes;
+  /* The forward's bias tables and structured-input arguments, as given to it
+   * (la_attn_ext; the scalar table here instead of la_attn_forward's rel_bias
+   * argument): read, not differentiated. Zero / NULL: none. */
+  int32_t rel_k;
+  const float *rel_bias;    /* device fp32 [H][V], or NULL */
+  const float *rel_vec;     /* device fp32 [H][V][D], 16-byte aligned, or NULL */
+  const uint8_t *glabel;    /* device uint8 [B][n_global][N], or NULL */
+  const uint8_t *llabel;    /* device uint8 [B][N][n_global], or NULL */
+  int32_t n_labels;         /* V: 0 (2*rel_k+1) or the vocabulary size, <= 64 */
+  int32_t seg_pieces;       /* pieces seg_ids masks (bits g2g 1, g2l 2, l2g 4, l2l 8; 0 = all) */
 } la_attn_bwd_ext;
 
 /* Backward of la_attn_forward for the band + global pattern (the training step
@@ -237,8 +247,13 @@ typedef struct {
  * With separate global projections a global row's terms go to ext->dqg,
  * ext->dkg, ext->dvg (through qg_i, kg_j, vg_j), every other row's to dq, dk, dv;
  * each of the six is fully written (rows that receive nothing get 0).
+ * With the forward's bias tables the logit is q_i . (k_j + a_l) / sqrt(D) + b_l
+ * for the pair's label l (ETC page, §3.4 "Relative Position Encoding"), so P
+ * is recomputed with it and dq_i gains sum_j dS_ij a_l / sqrt(D); the tables
+ * get no gradient. Label matrices and segment pieces mask pairs as in the
+ * forward.
  *  q, k, v, global_idx, n_global, radius, dilation, causal: as given to the
- *               forward; rel_bias / rel_vec are not supported here.
+ *               forward (its bias tables, labels and segment ids through ext).
  *  out, lse     the forward's output (dims/dtype as q) and its lse (fp32 [B,H,N],
  *               required).
  *  dout         device [B,H,N,D] in q's dtype: the loss gradient w.r.t. out.
@@ -252,7 +267,8 @@ la_status la_attn_backward(const la_dims *dims, const void *q, const void *k, co
                            hipStream_t stream, const la_attn_bwd_ext *ext);
 
 /* Bytes of workspace la_attn_backward needs (0 for invalid dims): fp32 D_i per
- * row and one global-flag byte per position, each part padded to 256 bytes. */
+ * row and each position's int32 rank in global_idx, each part padded to 256
+ * bytes. */
 size_t la_attn_backward_workspace_size(const la_dims *dims);
 
 /* Backward of la_dilated_forward (bf16 only). The mixture is one softmax over

@@ -74,7 +74,10 @@ class LaAttnBwdExt(ctypes.Structure):
     _fields_ = [("qg", ctypes.c_void_p), ("kg", ctypes.c_void_p), ("vg", ctypes.c_void_p),
                 ("dqg", ctypes.c_void_p), ("dkg", ctypes.c_void_p), ("dvg", ctypes.c_void_p),
                 ("seg_ids", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("rel_k", ctypes.c_int32),
+                ("rel_bias", ctypes.c_void_p), ("rel_vec", ctypes.c_void_p),
+                ("glabel", ctypes.c_void_p), ("llabel", ctypes.c_void_p),
+                ("n_labels", ctypes.c_int32), ("seg_pieces", ctypes.c_int32)]
 
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -243,6 +246,53 @@ class BoundBackward(BoundCall):
         return self.grads
 
 
+class _Labels:
+    """Checked bias tables and label matrices of one call (contiguous tensors
+    and what the C structs take)."""
+
+    def __init__(self, rb, rv, rk, n_labels, gl, ll):
+        self.rb, self.rv, self.rk, self.n_labels, self.gl, self.ll = rb, rv, rk, n_labels, gl, ll
+
+    @staticmethod
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+
+
+def _labels(dims: LaDims, n_global: int, rel_bias, rel_vec, rel_k, glabel, llabel) -> _Labels:
+    V = None
+    if rel_bias is not None:
+        if rel_bias.dtype != torch.float32 or not rel_bias.is_cuda or rel_bias.dim() != 2 \
+                or rel_bias.shape[0] != dims.H:
+            raise LaError(LA_EINVAL, "rel_bias must be a device fp32 [H, V] tensor")
+        V = rel_bias.shape[1]
+        rel_bias = rel_bias.contiguous()
+    if rel_vec is not None:
+        if rel_vec.dtype != torch.float32 or not rel_vec.is_cuda or rel_vec.dim() != 3 \
+                or rel_vec.shape[0] != dims.H or rel_vec.shape[2] != dims.D:
+            raise LaError(LA_EINVAL, "rel_vec must be a device fp32 [H, V, D] tensor")
+        if V is not None and rel_vec.shape[1] != V:
+            raise LaError(LA_EINVAL, "rel_bias and rel_vec need the same vocabulary")
+        V = rel_vec.shape[1]
+        rel_vec = rel_vec.contiguous()
+    rk, n_labels = 0, 0
+    if V is not None:
+        if rel_k is None:
+            if V % 2 != 1:
+                raise LaError(LA_EINVAL, "give rel_k with a vocabulary of structural labels")
+            rel_k = (V - 1) // 2
+        rk = int(rel_k)
+        n_labels = 0 if V == 2 * rk + 1 else V
+    mats = []
+    for name, t, shape in (("glabel", glabel, (dims.B, n_global, dims.N)),
+                           ("llabel", llabel, (dims.B, dims.N, n_global))):
+        if t is not None:
+            if t.dtype != torch.uint8 or not t.is_cuda or tuple(t.shape) != shape:
+                raise LaError(LA_EINVAL, f"{name} must be a device uint8 {list(shape)} tensor")
+            t = t.contiguous()
+        mats.append(t)
+    return _Labels(rel_bias, rel_vec, rk, n_labels, mats[0], mats[1])
+
+
 def bind_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
               global_idx: Optional[torch.Tensor] = None, radius: int = 0,
               dilation: Optional[Sequence[int]] = None, causal: bool = False,
@@ -291,44 +341,7 @@ def bind_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     dil = None if dilation is None else _host_i32(dilation)
     if dilation is not None and len(dilation) != dims.H:
         raise LaError(LA_EINVAL, "dilation needs one entry per head")
-    V = None
-    rptr = 0
-    if rel_bias is not None:
-        if rel_bias.dtype != torch.float32 or not rel_bias.is_cuda or rel_bias.dim() != 2 \
-                or rel_bias.shape[0] != dims.H:
-            raise LaError(LA_EINVAL, "rel_bias must be a device fp32 [H, V] tensor")
-        V = rel_bias.shape[1]
-        rel_bias = rel_bias.contiguous()
-        rptr = rel_bias.data_ptr()
-    vptr = 0
-    if rel_vec is not None:
-        if rel_vec.dtype != torch.float32 or not rel_vec.is_cuda or rel_vec.dim() != 3 \
-                or rel_vec.shape[0] != dims.H or rel_vec.shape[2] != dims.D:
-            raise LaError(LA_EINVAL, "rel_vec must be a device fp32 [H, V, D] tensor")
-        if V is not None and rel_vec.shape[1] != V:
-            raise LaError(LA_EINVAL, "rel_bias and rel_vec need the same vocabulary")
-        V = rel_vec.shape[1]
-        rel_vec = rel_vec.contiguous()
-        vptr = rel_vec.data_ptr()
-    rk, n_labels = 0, 0
-    if V is not None:
-        if rel_k is None:
-            if V % 2 != 1:
-                raise LaError(LA_EINVAL, "give rel_k with a vocabulary of structural labels")
-            rel_k = (V - 1) // 2
-        rk = int(rel_k)
-        n_labels = 0 if V == 2 * rk + 1 else V
-    lptr = []
-    for name, t, shape in (("glabel", glabel, (dims.B, n_global, dims.N)),
-                           ("llabel", llabel, (dims.B, dims.N, n_global))):
-        if t is None:
-            lptr.append(None)
-            continue
-        if t.dtype != torch.uint8 or not t.is_cuda or tuple(t.shape) != shape:
-            raise LaError(LA_EINVAL, f"{name} must be a device uint8 {list(shape)} tensor")
-        lptr.append(t.contiguous().data_ptr())
-    glabel = None if glabel is None else glabel.contiguous()
-    llabel = None if llabel is None else llabel.contiguous()
+    lab = _labels(dims, n_global, rel_bias, rel_vec, rel_k, glabel, llabel)
     sptr = 0
     if seg_ids is not None:
         if seg_ids.dtype != torch.int32 or not seg_ids.is_cuda \
@@ -343,15 +356,14 @@ def bind_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         ws = None
     else:
         ws = _workspace(la_attn_workspace_size(dims, n_global, sep), q.device, workspace)
-    ext = LaAttnExt(rk, _dev(qg, q, "qg") or None, _dev(kg, q, "kg") or None,
+    ext = LaAttnExt(lab.rk, _dev(qg, q, "qg") or None, _dev(kg, q, "kg") or None,
                     _dev(vg, q, "vg") or None, ws.data_ptr() if ws is not None else None,
-                    ws.numel() if ws is not None else 0, vptr or None, sptr or None,
-                    lptr[0], lptr[1], n_labels, int(seg_pieces))
+                    ws.numel() if ws is not None else 0, lab.ptr(lab.rv), sptr or None,
+                    lab.ptr(lab.gl), lab.ptr(lab.ll), lab.n_labels, int(seg_pieces))
     args = (ctypes.byref(dims), qptr, k.data_ptr(), v.data_ptr(), gptr or None, n_global,
-            int(radius), dil, int(bool(causal)), rptr or None, out.data_ptr(),
+            int(radius), dil, int(bool(causal)), lab.ptr(lab.rb), out.data_ptr(),
             lse.data_ptr() if lse is not None else None, _stream(q, stream), ctypes.byref(ext))
-    keep = (dims, ext, dil, q, k, v, global_idx, rel_bias, rel_vec, seg_ids, qg, kg, vg, ws,
-            glabel, llabel)
+    keep = (dims, ext, dil, q, k, v, global_idx, lab, seg_ids, qg, kg, vg, ws)
     fn = lib().la_attn_forward_noalloc if noalloc else lib().la_attn_forward
     return BoundCall(fn, args, keep, out, lse)
 
@@ -488,13 +500,20 @@ def bind_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
                        dilation: Optional[Sequence[int]] = None, causal: bool = False,
                        qg: Optional[torch.Tensor] = None, kg: Optional[torch.Tensor] = None,
                        vg: Optional[torch.Tensor] = None, seg_ids: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None, stream=None) -> BoundBackward:
+                       workspace: Optional[torch.Tensor] = None, stream=None,
+                       rel_bias: Optional[torch.Tensor] = None,
+                       rel_vec: Optional[torch.Tensor] = None, rel_k: Optional[int] = None,
+                       glabel: Optional[torch.Tensor] = None,
+                       llabel: Optional[torch.Tensor] = None,
+                       seg_pieces: int = 0) -> BoundBackward:
     """Validate and marshal a :func:`la_attn_backward` call without issuing it.
 
     ``out`` and ``lse`` are the forward's outputs for the same arguments and
     ``dout`` the loss gradient w.r.t. ``out`` (dtype of ``q``). The call's
     results are fp32 ``(dq, dk, dv)``, plus ``(dqg, dkg, dvg)`` with separate
-    global projections."""
+    global projections. The bias tables, label matrices and segment pieces are
+    those given to the forward (see :func:`bind_attn`); the tables are not
+    differentiated."""
     dims = _dims(q)
     ptrs = [_dev(t, q, name) for name, t in (("q", q), ("k", k), ("v", v), ("out", out),
                                              ("dout", dout))]
@@ -510,6 +529,7 @@ def bind_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
     if dilation is not None and len(dilation) != dims.H:
         raise LaError(LA_EINVAL, "dilation needs one entry per head")
     dil = None if dilation is None else _host_i32(dilation)
+    lab = _labels(dims, n_global, rel_bias, rel_vec, rel_k, glabel, llabel)
     sptr = 0
     if seg_ids is not None:
         if seg_ids.dtype != torch.int32 or not seg_ids.is_cuda \
@@ -526,22 +546,26 @@ def bind_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
              [t.data_ptr() for t in grads[3:]]
     ws = _workspace(la_attn_backward_workspace_size(dims), q.device, workspace)
     ext = LaAttnBwdExt(*gp, sptr or None, ws.data_ptr() if ws is not None else None,
-                       ws.numel() if ws is not None else 0)
+                       ws.numel() if ws is not None else 0, lab.rk, lab.ptr(lab.rb),
+                       lab.ptr(lab.rv), lab.ptr(lab.gl), lab.ptr(lab.ll), lab.n_labels,
+                       int(seg_pieces))
     args = (ctypes.byref(dims), ptrs[0], ptrs[1], ptrs[2], gptr or None, n_global, int(radius),
             dil, int(bool(causal)), ptrs[3], lse.data_ptr(), ptrs[4],
             grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(), _stream(q, stream),
             ctypes.byref(ext))
-    keep = (dims, ext, dil, q, k, v, out, lse, dout, global_idx, seg_ids, qg, kg, vg, ws)
+    keep = (dims, ext, dil, q, k, v, out, lse, dout, global_idx, seg_ids, qg, kg, vg, ws, lab)
     return BoundBackward(lib().la_attn_backward, args, keep, tuple(grads))
 
 
 def la_attn_backward(q, k, v, out, lse, dout, global_idx=None, radius: int = 0, dilation=None,
                      causal: bool = False, qg=None, kg=None, vg=None, seg_ids=None,
-                     workspace=None, stream=None):
+                     workspace=None, stream=None, rel_bias=None, rel_vec=None, rel_k=None,
+                     glabel=None, llabel=None, seg_pieces: int = 0):
     """One backward call; returns fp32 ``(dq, dk, dv)`` or, with separate global
     projections, ``(dq, dk, dv, dqg, dkg, dvg)``."""
     return bind_attn_backward(q, k, v, out, lse, dout, global_idx, radius, dilation, causal,
-                              qg, kg, vg, seg_ids, workspace, stream)()
+                              qg, kg, vg, seg_ids, workspace, stream, rel_bias, rel_vec, rel_k,
+                              glabel, llabel, seg_pieces)()
 
 
 def la_dilated_backward_workspace_size(dims: LaDims) -> int:

@@ -437,8 +437,9 @@ la_status la_fixed_forward(const la_dims* dims, const void* q, const void* k, co
 
 size_t la_attn_backward_workspace_size(const la_dims* dims) {
   if (check_dims(dims, false) != LA_OK) return 0;
-  // D_i per row, then one global flag byte per position
-  return align_up((size_t)dims->B * dims->H * dims->N * sizeof(float)) + align_up((size_t)dims->N);
+  // D_i per row, then each position's global rank
+  return align_up((size_t)dims->B * dims->H * dims->N * sizeof(float)) +
+         align_up((size_t)dims->N * sizeof(int32_t));
 }
 
 la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, const void* v,
@@ -481,6 +482,33 @@ la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, co
   }
   if (ext->seg_ids && ((uintptr_t)ext->seg_ids & 3u) != 0)
     return fail(LA_EINVAL, "ext->seg_ids must be 4-byte aligned");
+  // the forward's tables and structured inputs (the forward's checks)
+  const int32_t rel_k = ext->rel_k;
+  if ((ext->rel_bias || ext->rel_vec) && rel_k < 1)
+    return fail(LA_EINVAL, "ext->rel_bias / ext->rel_vec need ext->rel_k >= 1");
+  if (!ext->rel_bias && !ext->rel_vec && rel_k != 0)
+    return fail(LA_EINVAL, "ext->rel_k set without ext->rel_bias or ext->rel_vec");
+  if (ext->rel_vec && !aligned16(ext->rel_vec))
+    return fail(LA_EINVAL, "ext->rel_vec must be 16-byte aligned");
+  if (rel_k > la::kMaxRelK) return fail(LA_EUNSUPPORTED, "rel_k above 31");
+  if (ext->n_labels < 0 || (ext->n_labels > 0 && ext->n_labels < 2 * rel_k + 1))
+    return fail(LA_EINVAL, "ext->n_labels must be 0 or at least 2*rel_k+1");
+  if (ext->n_labels > la::kMaxLabels) return fail(LA_EUNSUPPORTED, "more than 64 labels");
+  if (ext->n_labels > 0 && !ext->rel_bias && !ext->rel_vec)
+    return fail(LA_EINVAL, "ext->n_labels set without ext->rel_bias or ext->rel_vec");
+  if ((ext->glabel || ext->llabel) && n_global == 0)
+    return fail(LA_EINVAL, "label matrices need global tokens");
+  if (ext->seg_pieces < 0 || ext->seg_pieces > 15)
+    return fail(LA_EINVAL, "ext->seg_pieces must be in [0, 15]");
+  if ((ext->glabel || ext->llabel) && (int64_t)n_global * dims->N > ((int64_t)1 << 31))
+    return fail(LA_EUNSUPPORTED, "label matrices above 2^31 entries per batch row");
+  a.rel_bias = ext->rel_bias;
+  a.rel_vec = ext->rel_vec;
+  a.glabel = ext->glabel;
+  a.llabel = ext->llabel;
+  a.rel_k = rel_k;
+  a.n_labels = ext->n_labels > 0 ? ext->n_labels : 2 * rel_k + 1;
+  a.seg_pieces = ext->seg_pieces == 0 ? 15 : ext->seg_pieces;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -499,8 +527,8 @@ la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, co
   a.dkg = ext->dkg;
   a.dvg = ext->dvg;
   a.delta = reinterpret_cast<float*>(ext->workspace);
-  a.gflag = reinterpret_cast<uint8_t*>(ext->workspace) +
-            align_up((size_t)dims->B * dims->H * dims->N * sizeof(float));
+  a.grank = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ext->workspace) +
+                                       align_up((size_t)dims->B * dims->H * dims->N * sizeof(float)));
   a.n_global = n_global;
   a.B = dims->B;
   a.H = dims->H;

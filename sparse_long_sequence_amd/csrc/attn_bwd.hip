@@ -65,11 +65,44 @@ __device__ __forceinline__ bool in_band(int32_t i, int32_t j, int32_t R, int32_t
   return t >= -R && t <= R;
 }
 
-// Global flags of the N positions (one byte each, in the workspace), so the
-// loops below test membership with one load instead of a search.
+// Global ranks of the N positions (index in global_idx, -1: not global; in
+// the workspace), so the loops below test membership with one load instead of
+// a search, and find a global token's label row.
 __global__ __launch_bounds__(256) void bwd_flags_kernel(BwdArgs a) {
   const int32_t p = (int32_t)(blockIdx.x * 256 + threadIdx.x);
-  if (p < a.N) a.gflag[p] = (a.n_global > 0 && sorted_contains(a.gidx, a.n_global, p)) ? 1 : 0;
+  if (p < a.N) a.grank[p] = a.n_global > 0 ? sorted_index(a.gidx, a.n_global, p) : -1;
+}
+
+// Pair (i, j) of batch row b under the forward's per-instance inputs, given
+// the two global ranks (ETC page, §3.4 "Per-instance attention masks" and
+// "Relative Position Encoding", Step 1): -2 when a segment mask of its piece
+// or a masking label excludes it, -1 when it is kept without a label (a mixed
+// pair keeping its usual label, or no bias tables), else its label.
+__device__ __forceinline__ int32_t bwd_pair(const BwdArgs& a, int32_t b, int32_t i, int32_t j,
+                                            int32_t gi, int32_t gj, const int32_t* segb) {
+  const bool ig = gi >= 0, jg = gj >= 0;
+  if (segb) {
+    const int32_t piece = ig ? (jg ? 1 : 2) : (jg ? 4 : 8);  // g2g, g2l, l2g, l2l
+    if ((a.seg_pieces & piece) && segb[i] != segb[j]) return -2;
+  }
+  int32_t l = kLabelDistance;
+  if (ig && a.glabel)
+    l = a.glabel[((size_t)b * a.n_global + gi) * a.N + j];
+  else if (!ig && jg && a.llabel)
+    l = a.llabel[((size_t)b * a.N + i) * a.n_global + gj];
+  if (l != kLabelDistance && l >= a.n_labels) return -2;
+  if (!a.rel_bias && !a.rel_vec) return -1;
+  if (l == kLabelDistance) {
+    if (ig != jg) return -1;
+    l = min(max(j - i, -a.rel_k), a.rel_k) + a.rel_k;
+  }
+  return l;
+}
+
+// The logit's bias for label lab (>= 0) of head h, given qa = q_i . a_lab
+// (unscaled; 0 without label vectors).
+__device__ __forceinline__ float label_bias(const BwdArgs& a, int32_t h, int32_t lab, float qa) {
+  return (a.rel_bias ? a.rel_bias[h * a.n_labels + lab] : 0.f) + qa * a.scale;
 }
 
 constexpr int kBatch = 8;  // pairs whose loads and reductions are issued together
@@ -77,7 +110,8 @@ constexpr int kBatch = 8;  // pairs whose loads and reductions are issued togeth
 // Row i's gradient dQ_i (query-centric), and D_i into the workspace.
 template <typename T>
 __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_kernel(BwdArgs a) {
-  const int32_t lane = threadIdx.x & 63;
+  __shared__ float qa_s[kWavesBwd][kMaxLabels];  // q_i . a_l of this wave's row
+  const int32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * kWavesBwd + (threadIdx.x >> 6);
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   if (row >= rows) return;
@@ -86,7 +120,8 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_kernel(BwdArgs a) {
   const int64_t bh = row / N;
   const int32_t h = (int32_t)(bh % a.H), b = (int32_t)(bh / a.H);
   const size_t hoff = (size_t)bh * N * kD;
-  const bool ig = a.gflag[i] != 0;
+  const int32_t gi = a.grank[i];
+  const bool ig = gi >= 0;
   const bool sep = ig && a.sep;
   const T* Q = static_cast<const T*>(sep ? a.qg : a.q) + hoff;
   const T* K = static_cast<const T*>(sep ? a.kg : a.k) + hoff;
@@ -98,18 +133,24 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_kernel(BwdArgs a) {
   const float qv = load_el(Q + (size_t)i * kD + lane);
   const float lse = a.lse[row];
   const int32_t* segb = a.seg ? a.seg + (size_t)b * N : nullptr;
-  const int32_t si = segb ? segb[i] : 0;
+  const float* avec = a.rel_vec ? a.rel_vec + (size_t)h * a.n_labels * kD : nullptr;
+  if (avec)
+    for (int32_t l = 0; l < a.n_labels; ++l) {
+      const float t = wave_sum(qv * avec[(size_t)l * kD + lane]);
+      if (lane == 0) qa_s[wv][l] = t;
+    }
   float acc = 0.f;
   // keys key_of(x), x in [0, n) (-1: skip), kBatch at a time; a skipped slot
   // reads row i (always valid) and gets weight 0
   auto sweep = [&](int32_t n, auto key_of) {
     for (int32_t x0 = 0; x0 < n; x0 += kBatch) {
-      int32_t j[kBatch];
+      int32_t j[kBatch], lb[kBatch];
       float kv[kBatch], vv[kBatch], s[kBatch], dp[kBatch];
 #pragma unroll
       for (int e = 0; e < kBatch; ++e) {
         j[e] = x0 + e < n ? key_of(x0 + e) : -1;
-        if (j[e] >= 0 && segb && segb[j[e]] != si) j[e] = -1;
+        lb[e] = j[e] >= 0 ? bwd_pair(a, b, i, j[e], gi, a.grank[j[e]], segb) : -1;
+        if (lb[e] == -2) j[e] = -1;
         const int32_t r = j[e] >= 0 ? j[e] : i;
         kv[e] = load_el(K + (size_t)r * kD + lane);
         vv[e] = load_el(V + (size_t)r * kD + lane);
@@ -121,8 +162,12 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < kBatch; ++e) {
-        const float p = j[e] >= 0 ? __expf(s[e] * a.scale - lse) : 0.f;
-        acc += p * (dp[e] - Di) * kv[e];
+        const bool lab = j[e] >= 0 && lb[e] >= 0;
+        const float bias = lab ? label_bias(a, h, lb[e], avec ? qa_s[wv][lb[e]] : 0.f) : 0.f;
+        const float p = j[e] >= 0 ? __expf(s[e] * a.scale + bias - lse) : 0.f;
+        // a label vector's share q_i . a_l of the logit adds a_l to dq
+        const float av = (lab && avec) ? avec[(size_t)lb[e] * kD + lane] : 0.f;
+        acc += p * (dp[e] - Di) * (kv[e] + av);
       }
     }
   };
@@ -168,9 +213,10 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_kernel(BwdArgs a) {
   const float* delta = a.delta + (size_t)bh * N;
   const T* dO = static_cast<const T*>(a.dout) + hoff;
   const int32_t* segb = a.seg ? a.seg + (size_t)b * N : nullptr;
-  const int32_t sj = segb ? segb[j] : 0;
   const int32_t d = a.dil[h], R = a.radius;
-  const bool jg = a.gflag[j] != 0;
+  const int32_t gj = a.grank[j];
+  const bool jg = gj >= 0;
+  const float* avec = a.rel_vec ? a.rel_vec + (size_t)h * a.n_labels * kD : nullptr;
 
   // rows row_of(x), x in [0, n) (-1: skip), through projections Q with this
   // key's (kv, vv), into (dk, dv); kBatch rows at a time, a skipped slot reads
@@ -178,12 +224,13 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_kernel(BwdArgs a) {
   auto sweep = [&](int32_t n, const T* Q, float kv, float vv, float& dk, float& dv,
                    auto row_of) {
     for (int32_t x0 = 0; x0 < n; x0 += kBatch) {
-      int32_t i[kBatch];
+      int32_t i[kBatch], lb[kBatch];
       float qv[kBatch], dov[kBatch], li[kBatch], di[kBatch], s[kBatch], dp[kBatch];
 #pragma unroll
       for (int e = 0; e < kBatch; ++e) {
         i[e] = x0 + e < n ? row_of(x0 + e) : -1;
-        if (i[e] >= 0 && segb && segb[i[e]] != sj) i[e] = -1;
+        lb[e] = i[e] >= 0 ? bwd_pair(a, b, i[e], j, a.grank[i[e]], gj, segb) : -1;
+        if (lb[e] == -2) i[e] = -1;
         const int32_t r = i[e] >= 0 ? i[e] : j;
         qv[e] = load_el(Q + (size_t)r * kD + lane);
         dov[e] = load_el(dO + (size_t)r * kD + lane);
@@ -198,7 +245,11 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < kBatch; ++e) {
         const bool on = i[e] >= 0 && li[e] != kNegInf;
-        const float p = on ? __expf(s[e] * a.scale - li[e]) : 0.f;
+        const bool lab = on && lb[e] >= 0;
+        float qa = 0.f;  // q_i . a_l (uniform branch: one pair per wave)
+        if (lab && avec) qa = wave_sum(qv[e] * avec[(size_t)lb[e] * kD + lane]);
+        const float bias = lab ? label_bias(a, h, lb[e], qa) : 0.f;
+        const float p = on ? __expf(s[e] * a.scale + bias - li[e]) : 0.f;
         dv += p * dov[e];
         dk += p * (dp[e] - di[e]) * qv[e];
       }
@@ -215,7 +266,7 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_kernel(BwdArgs a) {
     const int32_t u1 = min(R, (N - 1 - j) / d);
     sweep(u1 - u0 + 1, Qs, kv, vv, dk, dv, [&](int32_t x) {
       const int32_t i = j + (u0 + x) * d;
-      return a.gflag[i] ? -1 : i;
+      return a.grank[i] >= 0 ? -1 : i;
     });
   }
   // a global key: every other non-global row (causal: from j on)
@@ -223,7 +274,7 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_kernel(BwdArgs a) {
     const int32_t i0 = a.causal ? j : 0;
     sweep(N - i0, Qs, kv, vv, dk, dv, [&](int32_t x) {
       const int32_t i = i0 + x;
-      return (in_band(i, j, R, d, a.causal) || a.gflag[i]) ? -1 : i;
+      return (in_band(i, j, R, d, a.causal) || a.grank[i] >= 0) ? -1 : i;
     });
   }
   // global rows attend to every key (causal: rows from j on)
@@ -314,6 +365,7 @@ __device__ __forceinline__ float lane_totals(const float (&acc)[kD], int32_t lan
 
 __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_rows_kernel(BwdArgs a) {
   __shared__ float vq[kWavesBwd][kD], vdo[kWavesBwd][kD];
+  __shared__ float qa_s[kWavesBwd][kMaxLabels];  // q_i . a_l of this wave's row
   const int32_t lane = threadIdx.x & 63;
   const int32_t wv = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
   const int64_t rows = (int64_t)a.B * a.H * a.N;
@@ -325,7 +377,8 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_rows_kernel(BwdArgs a) 
   const int64_t bh = row / N;
   const int32_t h = (int32_t)(bh % a.H), b = (int32_t)(bh / a.H);
   const size_t hoff = (size_t)bh * N * kD;
-  const bool ig = a.gflag[i] != 0;
+  const int32_t gi = a.grank[i];
+  const bool ig = gi >= 0;
   const bool sep = ig && a.sep;
   const bf16* Q = static_cast<const bf16*>(sep ? a.qg : a.q) + hoff;
   const bf16* K = static_cast<const bf16*>(sep ? a.kg : a.k) + hoff;
@@ -333,14 +386,20 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_rows_kernel(BwdArgs a) 
   const float dov = load_el(static_cast<const bf16*>(a.dout) + hoff + (size_t)i * kD + lane);
   const float ov = load_el(static_cast<const bf16*>(a.out) + hoff + (size_t)i * kD + lane);
   const float Di = wave_sum(dov * ov);
-  vq[wv][lane] = load_el(Q + (size_t)i * kD + lane);
+  const float qv = load_el(Q + (size_t)i * kD + lane);
+  vq[wv][lane] = qv;
   vdo[wv][lane] = dov;
+  const float* avec = a.rel_vec ? a.rel_vec + (size_t)h * a.n_labels * kD : nullptr;
+  if (avec)
+    for (int32_t l = 0; l < a.n_labels; ++l) {
+      const float t = wave_sum(qv * avec[(size_t)l * kD + lane]);
+      if (lane == 0) qa_s[wv][l] = t;
+    }
   __syncthreads();  // the only barrier: every wave reaches it
   if (!valid) return;
   if (lane == 0) a.delta[row] = Di;
   const float lse = a.lse[row];
   const int32_t* segb = a.seg ? a.seg + (size_t)b * N : nullptr;
-  const int32_t si = segb ? segb[i] : 0;
   float acc[kD];
 #pragma unroll
   for (int d = 0; d < kD; ++d) acc[d] = 0.f;
@@ -350,15 +409,30 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_rows_kernel(BwdArgs a) 
     for (int32_t x0 = 0; x0 < n; x0 += 64) {
       const int32_t x = x0 + lane;
       int32_t j = x < n ? key_of(x) : -1;
-      if (j >= 0 && segb && segb[j] != si) j = -1;
+      const int32_t lb = j >= 0 ? bwd_pair(a, b, i, j, gi, a.grank[j], segb) : -1;
+      if (lb == -2) j = -1;
       const int32_t r = j >= 0 ? j : i;
       uint4 kc[8], vc[8];
       load_row(K + (size_t)r * kD, kc);
       load_row(V + (size_t)r * kD, vc);
       const float s = dot_row(kc, vq[wv]);
       const float dp = dot_row(vc, vdo[wv]);
-      const float p = j >= 0 ? __expf(s * a.scale - lse) : 0.f;
-      axpy_row(acc, p * (dp - Di), kc);
+      const bool lab = j >= 0 && lb >= 0;
+      const float bias = lab ? label_bias(a, h, lb, avec ? qa_s[wv][lb] : 0.f) : 0.f;
+      const float p = j >= 0 ? __expf(s * a.scale + bias - lse) : 0.f;
+      const float w = p * (dp - Di);
+      axpy_row(acc, w, kc);
+      if (lab && avec) {  // a label vector's share q_i . a_l of the logit adds a_l to dq
+        const float4* al = reinterpret_cast<const float4*>(avec + (size_t)lb * kD);
+#pragma unroll
+        for (int c = 0; c < kD / 4; ++c) {
+          const float4 x4 = al[c];
+          acc[4 * c] += w * x4.x;
+          acc[4 * c + 1] += w * x4.y;
+          acc[4 * c + 2] += w * x4.z;
+          acc[4 * c + 3] += w * x4.w;
+        }
+      }
     }
   };
   if (lse != kNegInf) {
@@ -412,9 +486,10 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_rows_kernel(BwdArgs a)
   const float* delta = a.delta + (size_t)bh * N;
   const bf16* dO = static_cast<const bf16*>(a.dout) + hoff;
   const int32_t* segb = a.seg ? a.seg + (size_t)b * N : nullptr;
-  const int32_t sj = segb ? segb[j] : 0;
   const int32_t d = a.dil[h], R = a.radius;
-  const bool jg = a.gflag[j] != 0;
+  const int32_t gj = a.grank[j];
+  const bool jg = gj >= 0;
+  const float* avec = a.rel_vec ? a.rel_vec + (size_t)h * a.n_labels * kD : nullptr;
   // Two passes over the same rows, one accumulator live at a time: dV (needs
   // s only) and then dK (needs s and dP).
   float acc[kD];
@@ -425,7 +500,8 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_rows_kernel(BwdArgs a)
     for (int32_t x0 = 0; x0 < n; x0 += 64) {
       const int32_t x = x0 + lane;
       int32_t i = x < n ? row_of(x) : -1;
-      if (i >= 0 && segb && segb[i] != sj) i = -1;
+      const int32_t lb = i >= 0 ? bwd_pair(a, b, i, j, a.grank[i], gj, segb) : -1;
+      if (lb == -2) i = -1;
       const int32_t r = i >= 0 ? i : j;
       uint4 qc[8], oc[8];
       load_row(Q + (size_t)r * kD, qc);
@@ -433,7 +509,9 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_rows_kernel(BwdArgs a)
       const float li = lse[r];
       const float sc = dot_row(qc, kvec);
       const bool on = i >= 0 && li != kNegInf;
-      const float p = on ? __expf(sc * a.scale - li) : 0.f;
+      float bias = 0.f;
+      if (on && lb >= 0) bias = label_bias(a, h, lb, avec ? dot_row(qc, avec + (size_t)lb * kD) : 0.f);
+      const float p = on ? __expf(sc * a.scale + bias - li) : 0.f;
       if (dk_pass) {
         const float dp = dot_row(oc, vvec);
         axpy_row(acc, p * (dp - delta[r]), qc);
@@ -455,13 +533,13 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_rows_kernel(BwdArgs a)
     const int32_t u1 = min(R, (N - 1 - j) / d);
     sweep(dk_pass, u1 - u0 + 1, Qs, vk[wv], vv[wv], [&](int32_t x) {
       const int32_t i = j + (u0 + x) * d;
-      return a.gflag[i] ? -1 : i;
+      return a.grank[i] >= 0 ? -1 : i;
     });
     if (jg) {
       const int32_t i0 = a.causal ? j : 0;
       sweep(dk_pass, N - i0, Qs, vk[wv], vv[wv], [&](int32_t x) {
         const int32_t i = i0 + x;
-        return (in_band(i, j, R, d, a.causal) || a.gflag[i]) ? -1 : i;
+        return (in_band(i, j, R, d, a.causal) || a.grank[i] >= 0) ? -1 : i;
       });
     }
     if (!a.sep) sweep(dk_pass, a.n_global, Qs, vk[wv], vv[wv], grow);

@@ -94,7 +94,14 @@ struct BwdArgs {
   const int32_t* seg;
   float *dq, *dk, *dv, *dqg, *dkg, *dvg;
   float* delta;  // workspace: D_i = dO_i . O_i per row
-  uint8_t* gflag;  // workspace: 1 at the N positions in global_idx
+  int32_t* grank;  // workspace: each position's index in global_idx, -1 if not global
+  // the forward's bias tables and per-instance inputs (as in AttnArgs; tables
+  // not differentiated): rel_bias [H][n_labels], rel_vec [H][n_labels][D]
+  const float* rel_bias;
+  const float* rel_vec;
+  const uint8_t* glabel;
+  const uint8_t* llabel;
+  int32_t rel_k, n_labels, seg_pieces;  // seg_pieces: bits g2g 1, g2l 2, l2g 4, l2l 8
   int32_t n_global, B, H, N, radius, causal, sep;
   int32_t dil[kMaxHeadsDil];
   float scale;

@@ -162,7 +162,7 @@ def test_fixed_argument_errors(L):
 def test_backward_argument_errors(L):
     d = LaDims(1, 2, 128, 64, la.LA_BF16)
     need = la.la_attn_backward_workspace_size(d)
-    assert need == 1 * 2 * 128 * 4 + 256  # D_i per row (1 KiB), one flag byte per position
+    assert need == 1 * 2 * 128 * 4 + 512  # D_i per row (1 KiB), an int32 rank per position
     ext = la.LaAttnBwdExt(None, None, None, None, None, None, None, FAKE, need)
 
     def call(dims=d, q=FAKE, lse=FAKE, dq=FAKE, gidx=None, n_global=0, radius=4, causal=0,
@@ -184,6 +184,15 @@ def test_backward_argument_errors(L):
         == la.LA_EINVAL                                        # qg.. without dqg..
     assert call(e=la.LaAttnBwdExt(None, None, None, None, None, None, FAKE + 2, FAKE, need)) \
         == la.LA_EINVAL                                        # misaligned seg_ids
+    # the forward's tables and structured inputs, checked as the forward does
+    E = lambda **kw: la.LaAttnBwdExt(None, None, None, None, None, None, None, FAKE, need, **kw)
+    assert call(e=E(rel_bias=FAKE)) == la.LA_EINVAL                       # no rel_k
+    assert call(e=E(rel_k=2)) == la.LA_EINVAL                             # rel_k, no table
+    assert call(e=E(rel_k=2, rel_vec=FAKE + 4)) == la.LA_EINVAL           # misaligned
+    assert call(e=E(rel_k=2, rel_bias=FAKE, n_labels=4)) == la.LA_EINVAL  # below 2k+1
+    assert call(e=E(rel_k=2, rel_bias=FAKE, n_labels=65)) == la.LA_EUNSUPPORTED
+    assert call(e=E(glabel=FAKE)) == la.LA_EINVAL                         # no global tokens
+    assert call(e=E(seg_pieces=16)) == la.LA_EINVAL
     assert call(dims=LaDims(1, 2, 128, 32, la.LA_BF16)) == la.LA_EUNSUPPORTED
     assert "D == 64" in la.la_last_error()
     assert call(dims=LaDims(0, 2, 128, 64, la.LA_BF16), e=None) == la.LA_OK  # empty: no-op

@@ -133,6 +133,78 @@ def test_backward_longformer_base(dev):
              inputs=(inp.q, inp.k, inp.v, inp.qg, inp.kg, inp.vg))
 
 
+def run_label_case(dev, tag, dtype, w: W.Workload, inp: W.Inputs, seed):
+    """Forward then backward with the inputs' bias tables, label matrices and
+    segment pieces; every gradient entry against the oracle's backward."""
+    say(f"backward {tag}: {dtype} B={w.B} H={w.H} N={w.N} |G|={len(w.global_idx)} "
+        f"R={w.radius} V={None if inp.rel_vec is None else inp.rel_vec.shape[1]} "
+        f"pieces={inp.seg_pieces}")
+    gen = torch.Generator().manual_seed(seed)
+    dout = rand(gen, (w.B, w.H, w.N, 64), dtype)
+    d = lambda t: None if t is None else t.to(dev).contiguous()
+    gidx = torch.tensor(sorted(w.global_idx), dtype=torch.int32, device=dev)
+    kw = dict(seg_ids=d(inp.seg), rel_vec=d(inp.rel_vec), rel_k=inp.rel_k,
+              glabel=d(inp.glabel), llabel=d(inp.llabel), seg_pieces=inp.seg_pieces)
+    sepkw = dict(qg=d(inp.qg), kg=d(inp.kg), vg=d(inp.vg))
+    out, lse = la.la_attn_forward(d(inp.q), d(inp.k), d(inp.v), gidx, w.radius, w.dilation,
+                                  w.causal, d(inp.rel_bias), **sepkw, **kw)
+    grads = la.la_attn_backward(d(inp.q), d(inp.k), d(inp.v), out, lse, d(dout), gidx, w.radius,
+                                w.dilation, w.causal, rel_bias=d(inp.rel_bias), **sepkw, **kw)
+    torch.cuda.synchronize()
+    f64 = lambda t: None if t is None else to64(t)
+    np_ = lambda t: None if t is None else t.numpy()
+    ref = oracle.attn_backward(f64(inp.q), f64(inp.k), f64(inp.v), f64(dout), w.global_idx,
+                               w.radius, w.dilation, w.causal, f64(inp.qg), f64(inp.kg),
+                               f64(inp.vg), seg=np_(inp.seg), rel_bias=f64(inp.rel_bias),
+                               rel_vec=f64(inp.rel_vec), rel_k=inp.rel_k,
+                               glabel=np_(inp.glabel), llabel=np_(inp.llabel),
+                               seg_pieces=inp.seg_pieces)
+    check(tag, dtype, grads, ref)
+
+
+LABEL_CASES = [
+    # tag, dtype, B, H, N, globals, R, dilation, causal, separate, rel_k, structural, kind, pieces
+    ("bias-scalar", "bf16", 1, 2, 300, (0, 1, 150), 20, None, False, False, 5, 0, "scalar", 0),
+    ("bias-both-sep", "bf16", 2, 2, 260, (3, 64, 200), 16, [1, 2], False, True, 3, 3, "both", 9),
+    ("labels-f32-causal", "f32", 1, 2, 200, (5, 70, 71), 12, None, True, False, 2, 2, "vector", 6),
+    ("labels-masks-only", "bf16", 1, 2, 230, (0, 100), 10, None, False, False, 0, 0, None, 4),
+]
+
+
+@pytest.mark.parametrize("case", LABEL_CASES, ids=[c[0] for c in LABEL_CASES])
+def test_backward_labels(dev, case):
+    tag, dtype, B, H, N, G, R, dil, causal, sep, rk, ns, kind, pieces = case
+    w = W.Workload(tag, B=B, H=H, N=N, dtype=dtype, radius=R, global_idx=G,
+                   dilation=None if dil is None else tuple(dil), causal=causal,
+                   separate_global=sep, seed=400 + LABEL_CASES.index(case))
+    inp = W.make_inputs(w)
+    V = 2 * rk + 1 + ns
+    gen = torch.Generator().manual_seed(401)
+    if kind in ("scalar", "both"):
+        inp.rel_bias = 0.3 * torch.randn(H, V, generator=gen)
+    if kind in ("vector", "both"):
+        inp.rel_vec = 0.3 * torch.randn(H, V, 64, generator=gen)
+    inp.rel_k = rk if kind else None
+    rng = np.random.default_rng(403)
+    vals = [0, V - 1, W.LABEL_DISTANCE, W.LABEL_DISTANCE, W.LABEL_MASKED] if kind else \
+        [0, W.LABEL_DISTANCE, W.LABEL_MASKED]
+    inp.glabel = torch.from_numpy(rng.choice(vals, size=(B, len(G), N)).astype(np.uint8))
+    inp.llabel = torch.from_numpy(rng.choice(vals, size=(B, N, len(G))).astype(np.uint8))
+    if pieces:
+        inp.seg = torch.tensor((np.arange(N) * 3 // N)[None].repeat(B, 0), dtype=torch.int32)
+        inp.seg_pieces = pieces
+    run_label_case(dev, tag, dtype, w, inp, seed=405)
+
+
+def test_backward_etc_structured(dev):
+    """The ETC structured layout (hard g2l, no cross-context g2g or l2l, four
+    structural labels, key-side label vectors) at a reduced size."""
+    w = W.Workload("etc-structured-bwd", B=1, H=2, N=64 + 900, radius=40,
+                   global_idx=tuple(range(64)), rel_k=6, rel_kind="both", structure=(4, 3),
+                   seed=407)
+    run_label_case(dev, "etc-structured", "bf16", w, W.make_inputs(w), seed=409)
+
+
 def test_backward_graph_replay(dev):
     """The backward call captured in a HIP graph (it writes its whole workspace
     with kernels, no memset) and replayed, with eager work between replays:
