@@ -264,16 +264,17 @@ COPY_PROBE_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_longformer_base_traffic.txt")
 
 
-def kernel_sources_digest() -> str:
-    """sha256 over the sources the forward kernels and their launches are built from
-    (and the build flags); the backward's own source, attn_bwd.hip, is left out."""
-    import glob
+# The sources the band + global forward kernel and its launch geometry are
+# built from, and the build flags: the measured traffic stands while they do.
+TRAFFIC_SOURCES = ("csrc/attn_fwd.hip", "csrc/tile_core.h", "csrc/kernels.h", "csrc/api.hip",
+                   "build.py")
 
+
+def kernel_sources_digest() -> str:
+    """sha256 over TRAFFIC_SOURCES (paths and contents)."""
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "sparse_long_sequence_amd")
-    files = sorted(f for f in glob.glob(os.path.join(pkg, "csrc", "*"))
-                   if os.path.basename(f) != "attn_bwd.hip") + \
-        sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))) + [os.path.join(pkg, "build.py")]
+    files = [os.path.join(pkg, f) for f in TRAFFIC_SOURCES]
     for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
         with open(f, "rb") as fh:
