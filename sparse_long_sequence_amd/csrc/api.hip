@@ -537,6 +537,18 @@ la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, co
   a.causal = causal;
   a.sep = sep_in ? 1 : 0;
   a.scale = (float)(1.0 / sqrt((double)kDHead));
+  a.scale_log2 = (float)(1.0 / sqrt((double)kDHead) * 1.4426950408889634);
+  // the MFMA dQ path: bf16 without bias tables, labels or segment ids
+  if (dims->dtype == LA_BF16 && !a.rel_bias && !a.rel_vec && !a.glabel && !a.llabel && !a.seg) {
+    const int32_t tq = la::host_query_tile(dims->dtype);
+    int32_t tiles = 0;
+    for (int32_t h = 0; h < dims->H; ++h)
+      tiles = std::max(tiles, la::host_band_tiles_of_head(dims->N, a.dil[h], tq));
+    a.band_tiles_per_head = tiles;
+    const int64_t band_wg = (int64_t)dims->B * dims->H * tiles;
+    if (band_wg > 0x7fffffffLL) return fail(LA_EUNSUPPORTED, "launch grid too large");
+    a.n_band_wg = (int32_t)band_wg;
+  }
   hipError_t e = la::launch_attn_bwd(a, dims->dtype, stream);
   if (e != hipSuccess) return fail(LA_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(e));
   return LA_OK;

@@ -1,0 +1,661 @@
+// attn_bwd_mfma.hip — dQ of band + global attention on the bf16 MFMA tile
+// engine (the chain rule through the masked softmax: LongNet page, §3.4
+// "Standard Self-Attention and Sparse Attention (Preliminaries)", Eq. 2,
+// differentiated; the pattern as in attn_fwd.hip).
+//
+// For the forward's own lse (natural log) and D_i = dO_i . O_i,
+//   P_ij  = exp(q_i . k_j / sqrt(D) - lse_i),   dP_ij = dO_i . v_j,
+//   dS_ij = P_ij (dP_ij - D_i),                 dQ_i  = sum_j dS_ij k_j / sqrt(D).
+// A workgroup owns a query tile of the non-global rows of one residue class
+// (as the forward's band workgroups) and streams the same key tiles through
+// LDS: the window, then the global keys outside it. Per 32-key sub-tile a
+// wave forms S^T = K Q^T and dP^T = V dO^T on MFMA (its rows' Q and dO in
+// registers), P from lse with no running max (lse is final), dS in bf16, and
+// dQ^T += K^T dS^T on MFMA with K read transposed from LDS (the forward's PV
+// step with K in place of V and dS in place of P). No atomics: each dQ row is
+// written once.
+//
+// dK, dV run the same engine with the roles swapped: a workgroup owns a tile
+// of non-global keys (their K and V fragments in registers) and streams the
+// query rows that reach them through LDS (Q in the K slot, dO in the V slot,
+// each row's lse and D_i next to them):
+//   S'^T = Q K^T and dP'^T = dO V^T per 32-row sub-tile, P and dS as above,
+//   dV^T += dO^T P^T and dK^T += Q^T dS^T (transposed LDS reads of dO and Q),
+// first over the window's non-global rows, then over the global rows (which
+// reach every key; with separate projections through qg_i, kg_j, vg_j into
+// dKg, dVg).
+#include "tile_core.h"
+#include "kernels.h"
+
+namespace la {
+namespace {
+
+using TT = TileTraits<bf16>;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// One wave's rows: Q and dO fragments (B operands), lse in log2 units (+inf
+// for a row without keys, so its P are 0), D_i, and dQ^T (as the forward's O).
+struct DqWave {
+  bf16x8 qf[4];
+  bf16x8 df[4];
+  f32x16 acc[2];
+  float lse2;
+  float di;
+};
+
+__device__ __forceinline__ void load_frag(bf16x8 (&f)[4], const bf16* base, int32_t pos,
+                                          int32_t lane) {
+  const bf16* src = base + (size_t)pos * kD + 8 * (lane >> 5);
+#pragma unroll
+  for (int st = 0; st < 4; ++st) f[st] = __builtin_bit_cast(bf16x8, ldg16(src + 16 * st));
+}
+
+// s[e] = X[key_const(sb, e) + key_lane] . f for the staged tile X (K or V,
+// [key][d] rows in the engine's swizzled layout): S^T or dP^T of sub-tile sb.
+__device__ __forceinline__ void tile_dots(const bf16* tile, const bf16x8 (&f)[4], int32_t lane,
+                                          int sb, float s[TT::kNS]) {
+  const int32_t r = lane & 31, h = lane >> 5;
+  const int32_t y = h ^ TT::swz(r);
+  const bf16* row = tile + (32 * sb + r) * kD;
+  f32x16 acc = {};
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(row + 8 * ((2 * st) ^ y));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, f[st], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int e = 0; e < TT::kNS; ++e) s[e] = acc[e];
+}
+
+// acc (X^T Y^T over sub-tile sb) += X^T . G^T, X the staged tile of buffer
+// `buf` read transposed (as the forward's V in its PV step) and G the
+// sub-tile's bf16 weights in the forward's P layout.
+template <int32_t BUF>
+__device__ __forceinline__ void acc_transposed(const bf16* tile0, f32x16 (&acc)[2], int32_t lane,
+                                               int sb, const TT::PTile& G) {
+  typedef short __attribute__((__vector_size__(4 * sizeof(short)))) s16x4;
+  const int32_t L = lane & 15, g = (lane >> 4) & 1, h = lane >> 5;
+  const int32_t kr = 4 * h + (L >> 2);
+  const int32_t u = (2 * g + ((L & 3) >> 1)) ^ TT::swz(kr);
+  const bf16* base = tile0 + kr * kD + 4 * (L & 1);
+  const uint32_t a00 = TT::lds_addr(base + 8 * (0 ^ u));
+  const uint32_t a01 = TT::lds_addr(base + 8 * kD + 8 * (0 ^ u ^ 2));
+  const uint32_t a10 = TT::lds_addr(base + 8 * (4 ^ u));
+  const uint32_t a11 = TT::lds_addr(base + 8 * kD + 8 * (4 ^ u ^ 2));
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int32_t off = (BUF * kTK * kD + (32 * sb + 16 * t) * kD) * 2;  // bytes
+    s16x4 lo0, hi0, lo1, hi1;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo0), "=&v"(hi0), "=&v"(lo1), "=&v"(hi1)
+        : "v"(a00), "v"(a01), "v"(a10), "v"(a11), "i"(off));
+    const bf16x8 x0 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo0, hi0, 0, 1, 2, 3, 4, 5, 6, 7));
+    const bf16x8 x1 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo1, hi1, 0, 1, 2, 3, 4, 5, 6, 7));
+    const bf16x8 y = __builtin_bit_cast(bf16x8, G.p[t]);
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, y, acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1, y, acc[1], 0, 0, 0);
+  }
+}
+
+// One staged key tile into dQ^T. The forward's block classes decide which
+// sub-tiles run and which need the per-element mask.
+template <int32_t BUF>
+__device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t lane,
+                                        const MaskRule& mr, const KeyTile& kt, int32_t qi,
+                                        int32_t qpos, bool dead, float c) {
+  const int32_t r0 = (mr.use_qpos ? __builtin_amdgcn_readlane(qpos, 0)
+                                  : __builtin_amdgcn_readlane(qi, 0)) + mr.ref_off;
+  const int32_t r1 = (mr.use_qpos ? __builtin_amdgcn_readlane(qpos, TT::kRowsPerBlock - 1)
+                                  : __builtin_amdgcn_readlane(qi, TT::kRowsPerBlock - 1)) + mr.ref_off;
+#pragma unroll
+  for (int sb = 0; sb < TT::kSub; ++sb) {
+    const int32_t cls = dead ? kEmpty : classify<bf16>(mr, kt.count, sb, r0, r1);
+    if (cls == kEmpty) continue;
+    float s[TT::kNS], dp[TT::kNS];
+    tile_dots(&sm.k[BUF][0], w.qf, lane, sb, s);
+    tile_dots(&sm.v[BUF][0], w.df, lane, sb, dp);
+    if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, qi, qpos, lane);
+    TT::PTile G;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 8 * t + 2 * i;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -w.lse2));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], c, -w.lse2));
+        G.p[t][i] = pack_bf16x2(p0 * (dp[e] - w.di), p1 * (dp[e + 1] - w.di));
+      }
+    }
+    acc_transposed<BUF>(&sm.k[0][0], w.acc, lane, sb, G);
+  }
+}
+
+// The forward's tile loop (fetch next, compute current, stage, barrier) with
+// `proc(buf_tag, kt, mr)` as the per-tile work; no bias, segment or label
+// state.
+template <bool GATHER, typename Desc, typename Proc>
+__device__ __forceinline__ void stream_tiles(TT::Smem& sm, const bf16* kb, const bf16* vb,
+                                             int32_t n_tiles, Desc desc, const GlobInfo& gi,
+                                             Proc proc) {
+  const int32_t tid = threadIdx.x;
+  if (n_tiles <= 0) return;
+  const LabelRule nolab = {};
+  TT::Prefetch pf;
+  KeyTile kt;
+  MaskRule mr;
+  desc(0, kt, mr);
+  const FetchPlan fp = TT::plan(kt.stride, tid);
+  TT::template fetch<GATHER>(pf, sm, 0, kb, vb, kt, fp, tid);
+  TT::stage(sm, 0, pf, tid);
+  stage_meta<bf16, false, false>(sm, 0, pf.meta, gi, nolab, kt.gmode, tid);
+  __syncthreads();
+  auto step = [&](auto buf_tag, int32_t n) {
+    constexpr int32_t buf = decltype(buf_tag)::value;
+    KeyTile kt_next;
+    MaskRule mr_next;
+    const bool more = n + 1 < n_tiles;
+    if (more) {
+      desc(n + 1, kt_next, mr_next);
+      TT::template fetch<GATHER>(pf, sm, buf ^ 1, kb, vb, kt_next, fp, tid);
+    }
+    proc(buf_tag, kt, mr);
+    if (more) {
+      TT::stage(sm, buf ^ 1, pf, tid);
+      stage_meta<bf16, false, false>(sm, buf ^ 1, pf.meta, gi, nolab, kt_next.gmode, tid);
+      kt = kt_next;
+      mr = mr_next;
+    }
+    __syncthreads();
+  };
+  for (int32_t n = 0; n < n_tiles; n += 2) {
+    step(BufTag<0>{}, n);
+    if (n + 1 < n_tiles) step(BufTag<1>{}, n + 1);
+  }
+}
+
+// Number of residue-class query tiles (of tq rows) of a head of dilation d
+// (the forward's enumeration).
+__device__ __forceinline__ int32_t tiles_of_class(int32_t N, int32_t d, int32_t c, int32_t tq) {
+  return ((N - c + d - 1) / d + tq - 1) / tq;
+}
+
+// Whether this lane's row (or key) of a tile is a global position.
+__device__ __forceinline__ bool qi_is_global(const BwdArgs& a, int32_t qi, int32_t qcount,
+                                             int32_t pos, int32_t g_first, int32_t g_last,
+                                             int32_t lo, int32_t hi) {
+  return qi < qcount && g_first <= hi && g_last >= lo && sorted_contains(a.gidx, a.n_global, pos);
+}
+
+// dQ of the non-global rows of one query tile (the forward's band workgroup:
+// window tiles, then the global keys outside the window).
+__device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t bw) {
+  constexpr int32_t kTQ = TT::kTQ;
+  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t N = a.N;
+  const size_t head_elems = (size_t)N * kD;
+  const int32_t bh = bw / a.band_tiles_per_head;
+  int32_t tile = bw % a.band_tiles_per_head;
+  const int32_t h = bh % a.H;
+  const int32_t d = a.dil[h];
+  int32_t c = 0, n_c = 0;
+  for (; c < d && c < N; ++c) {
+    n_c = (N - c + d - 1) / d;
+    const int32_t tc = tiles_of_class(N, d, c, kTQ);
+    if (tile < tc) break;
+    tile -= tc;
+  }
+  if (c >= d || c >= N) return;  // padding workgroup of a less-dilated head
+  const int32_t t0 = tile * kTQ;
+  const int32_t qcount = min(kTQ, n_c - t0);
+  const int32_t qbase = c + d * t0;
+  const int32_t i_lo = qbase, i_hi = qbase + d * (qcount - 1);
+  const int32_t ng = a.n_global;
+  const int32_t g_first = ng > 0 ? a.gidx[0] : 0;
+  const int32_t g_last = ng > 0 ? a.gidx[ng - 1] : -1;
+  // a tile made only of global rows has nothing here (the global rows' dQ
+  // comes from the global-row pass)
+  if (d == 1 && g_last - g_first == ng - 1 && g_first <= i_lo && g_last >= i_hi) return;
+
+  const bf16* qb = static_cast<const bf16*>(a.q) + bh * head_elems;
+  const bf16* kb = static_cast<const bf16*>(a.k) + bh * head_elems;
+  const bf16* vb = static_cast<const bf16*>(a.v) + bh * head_elems;
+  const bf16* dob = static_cast<const bf16*>(a.dout) + bh * head_elems;
+  const int32_t qi = TT::qrow(wave, lane, 0);
+  const int32_t qpos = qbase + d * min(qi, qcount - 1);
+  const bool dead = TT::kQW * wave >= qcount;
+  DqWave w;
+  load_frag(w.qf, qb, qpos, lane);
+  load_frag(w.df, dob, qpos, lane);
+  const float lse = a.lse[(size_t)bh * N + qpos];
+  w.lse2 = lse == kNegInf ? -kNegInf : lse * kLog2e;
+  w.di = a.delta[(size_t)bh * N + qpos];
+  w.acc[0] = f32x16{};
+  w.acc[1] = f32x16{};
+
+  const int32_t R = a.radius;
+  const int32_t lo = max(0, t0 - R);
+  const int32_t hi = a.causal ? (t0 + qcount - 1) : min(n_c - 1, t0 + qcount - 1 + R);
+  const int32_t n_band = (hi - lo + 1 + kTK - 1) / kTK;
+  const GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
+  auto proc = [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+    constexpr int32_t buf = decltype(buf_tag)::value;
+    dq_tile<buf>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2);
+  };
+  auto band_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+    const int32_t u0 = lo + n * kTK;
+    const int32_t kcount = min(kTK, hi - u0 + 1);
+    kt = {nullptr, c + d * u0, d, kcount, u0 - lo, kGlobNone};
+    const int32_t dmin = u0 - t0 - (qcount - 1);
+    const int32_t dmax = u0 + kcount - 1 - t0;
+    const int32_t hib = a.causal ? 0 : R;
+    const bool full = kcount == kTK && dmin >= -R && dmax <= hib;
+    mr = {kRange, full ? 0 : 1, 0, t0 - u0, -R, hib, 0, 0, 1};
+  };
+  const bool g_run = ng > 0 && d == 1 && g_last - g_first == ng - 1;
+  if (g_run) {
+    const int32_t n_gt = (ng + kTK - 1) / kTK;
+    auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+      if (n >= n_gt) {
+        band_desc(n - n_gt, kt, mr);
+        return;
+      }
+      const int32_t gt = n;
+      const int32_t cnt = min(kTK, ng - gt * kTK);
+      const int32_t gl = g_first + gt * kTK, gh = gl + cnt - 1;
+      const bool all_in_band =
+          a.causal ? (gl >= i_hi - R && gh <= i_lo) : (gl >= i_hi - R && gh <= i_lo + R);
+      const bool none_causal = a.causal && gl > i_hi;
+      const bool keep = !all_in_band && !none_causal;
+      kt = {nullptr, gl, 1, keep ? cnt : 0, 0, kGlobNone};
+      const bool all_out = cnt == kTK && (gh < i_lo - R || (!a.causal && gl > i_hi + R)) &&
+                           (!a.causal || gh <= i_lo);
+      mr = {kOutside, all_out ? 0 : 1, 1, -gl, -R, a.causal ? kFar : R, 0, 0, 1};
+    };
+    stream_tiles<false>(sm, kb, vb, n_band + n_gt, desc, gi, proc);
+  } else {
+    stream_tiles<false>(sm, kb, vb, n_band, band_desc, gi, proc);
+  }
+  if (ng > 0 && !g_run) {
+    const int32_t n_gt = (ng + kTK - 1) / kTK;
+    uint64_t keep = ~0ull;
+    if (n_gt <= 64) {
+      keep = 0;
+      for (int32_t gt = 0; gt < n_gt; ++gt) {
+        const int32_t cnt = min(kTK, ng - gt * kTK);
+        const int32_t gl = a.gidx[gt * kTK], gh = a.gidx[gt * kTK + cnt - 1];
+        bool all_in_band = false;
+        if (d == 1)
+          all_in_band = a.causal ? (gl >= i_hi - R && gh <= i_lo) : (gl >= i_hi - R && gh <= i_lo + R);
+        const bool none_causal = a.causal && gl > i_hi;
+        if (!all_in_band && !none_causal) keep |= (1ull << gt);
+      }
+    }
+    const int32_t n_glob = n_gt <= 64 ? __builtin_popcountll(keep) : n_gt;
+    auto glob_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+      int32_t gt = n;
+      if (n_gt <= 64) {
+        uint64_t m = keep;
+        for (int32_t s = 0; s < n; ++s) m &= m - 1;
+        gt = __builtin_ctzll(m);
+      }
+      const int32_t kcount = min(kTK, ng - gt * kTK);
+      kt = {a.gidx + gt * kTK, 0, 1, kcount, 0, kGlobNone};
+      const int32_t gl = a.gidx[gt * kTK], gh = a.gidx[gt * kTK + kcount - 1];
+      const bool outside = (gh < i_lo - d * R) || (gl > i_hi + d * R);
+      const bool causal_ok = !a.causal || gh <= i_lo;
+      const bool full = kcount == kTK && outside && causal_ok;
+      mr = {kGlobCol, full ? 0 : 1, 0, 0, 0, 0, a.causal, R, d};
+    };
+    stream_tiles<true>(sm, kb, vb, n_glob, glob_desc, gi, proc);
+  }
+
+  // non-global rows: dQ (and, with separate projections, a zero dQ_g row)
+  if (qi < qcount) {
+    const bool is_g = g_first <= i_hi && g_last >= i_lo && sorted_contains(a.gidx, ng, qpos);
+    if (!is_g) {
+      const int32_t hh = lane >> 5;
+      float* dst = a.dq + ((size_t)bh * N + qpos) * kD;
+      float* dsg = a.sep ? a.dqg + ((size_t)bh * N + qpos) * kD : nullptr;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = w.acc[db][4 * j + i] * a.scale;
+          *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * j + 4 * hh) = x;
+          if (dsg) *reinterpret_cast<f32x4*>(dsg + 32 * db + 8 * j + 4 * hh) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV of the non-global keys
+// ---------------------------------------------------------------------------
+
+// One wave's keys: K and V fragments, dK^T and dV^T.
+struct DkvWave {
+  bf16x8 kf[4];
+  bf16x8 vf[4];
+  f32x16 dk[2];
+  f32x16 dv[2];
+};
+
+// A streamed tile's per-row lse (log2 units, +inf for a row without keys) and
+// D_i sit in LDS next to its Q and dO rows (in the key-id and rank arrays,
+// which this pass does not use otherwise).
+__device__ __forceinline__ float* row_lse2(TT::Smem& sm, int32_t buf) {
+  return reinterpret_cast<float*>(&sm.kseg[buf][0]);
+}
+__device__ __forceinline__ float* row_di(TT::Smem& sm, int32_t buf) {
+  return reinterpret_cast<float*>(&sm.kgrank[buf][0]);
+}
+__device__ __forceinline__ const float* row_lse2(const TT::Smem& sm, int32_t buf) {
+  return reinterpret_cast<const float*>(&sm.kseg[buf][0]);
+}
+__device__ __forceinline__ const float* row_di(const TT::Smem& sm, int32_t buf) {
+  return reinterpret_cast<const float*>(&sm.kgrank[buf][0]);
+}
+
+// One streamed tile of query rows into dK^T, dV^T. EXCL_G: rows that are
+// global are excluded (they are taken in the global-row sweep); ROWS_AFTER:
+// (gathered global rows, causal) only rows at or after the lane's key.
+template <int32_t BUF, bool EXCL_G, bool ROWS_AFTER>
+__device__ __forceinline__ void dkv_tile(const TT::Smem& sm, DkvWave& w, int32_t lane,
+                                         const MaskRule& mr, const KeyTile& kt, int32_t ki,
+                                         int32_t kpos, bool dead, float c, bool causal) {
+  const int32_t r0 = __builtin_amdgcn_readlane(ki, 0) + mr.ref_off;
+  const int32_t r1 = __builtin_amdgcn_readlane(ki, TT::kRowsPerBlock - 1) + mr.ref_off;
+  bool any_g = false;
+  if constexpr (EXCL_G)
+    any_g = kt.gmode != kGlobNone && (__builtin_amdgcn_readfirstlane(sm.gcls[BUF]) & 1) != 0;
+  int32_t kl = TT::key_lane(lane);
+  asm("" : "+v"(kl));  // opaque per call, as in mask_tile
+#pragma unroll
+  for (int sb = 0; sb < TT::kSub; ++sb) {
+    const int32_t cls = dead ? kEmpty : classify<bf16>(mr, kt.count, sb, r0, r1);
+    if (cls == kEmpty) continue;
+    float s[TT::kNS], dp[TT::kNS];
+    tile_dots(&sm.k[BUF][0], w.kf, lane, sb, s);
+    tile_dots(&sm.v[BUF][0], w.vf, lane, sb, dp);
+    if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, ki, kpos, lane);
+    if (EXCL_G && any_g) {
+#pragma unroll
+      for (int r = 0; r < TT::kNS; ++r)
+        s[r] = sm.kglob[BUF][TT::key_const(sb, r) + kl] != 0 ? kNegInf : s[r];
+    }
+    if constexpr (ROWS_AFTER) {
+      if (causal) {
+#pragma unroll
+        for (int r = 0; r < TT::kNS; ++r)
+          s[r] = sm.kpos[BUF][TT::key_const(sb, r) + kl] >= kpos ? s[r] : kNegInf;
+      }
+    }
+    const float* l2 = row_lse2(sm, BUF);
+    const float* dd = row_di(sm, BUF);
+    TT::PTile P, G;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 8 * t + 2 * i;
+        const int32_t i0 = TT::key_const(sb, e) + kl, i1 = TT::key_const(sb, e + 1) + kl;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -l2[i0]));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], c, -l2[i1]));
+        P.p[t][i] = pack_bf16x2(p0, p1);
+        G.p[t][i] = pack_bf16x2(p0 * (dp[e] - dd[i0]), p1 * (dp[e + 1] - dd[i1]));
+      }
+    }
+    acc_transposed<BUF>(&sm.v[0][0], w.dv, lane, sb, P);
+    acc_transposed<BUF>(&sm.k[0][0], w.dk, lane, sb, G);
+    // one sub-tile's values live at a time (the two interleaved spill)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// stream_tiles for query rows: as stream_tiles, and each staged tile's rows'
+// lse (log2 units) and D_i, read with the tile's loads, written to LDS with
+// its staging. GI_MODE: how the rows' global flags are found.
+template <bool GATHER, typename Desc, typename Proc>
+__device__ __forceinline__ void stream_rows(TT::Smem& sm, const bf16* qb, const bf16* dob,
+                                            const float* lse, const float* delta,
+                                            int32_t n_tiles, Desc desc, const GlobInfo& gi,
+                                            Proc proc) {
+  const int32_t tid = threadIdx.x;
+  if (n_tiles <= 0) return;
+  const LabelRule nolab = {};
+  TT::Prefetch pf;
+  KeyTile kt;
+  MaskRule mr;
+  float pl = 0.f, pd = 0.f;
+  auto row_vals = [&](const KeyTile& t) {
+    if (tid < kTK && t.count > 0) {
+      const int32_t p = key_pos<GATHER>(t, min(tid, t.count - 1));
+      const float l = lse[p];
+      pl = l == kNegInf ? -kNegInf : l * kLog2e;
+      pd = delta[p];
+    }
+  };
+  auto put_rows = [&](int32_t buf) {
+    if (tid < kTK) {
+      row_lse2(sm, buf)[tid] = pl;
+      row_di(sm, buf)[tid] = pd;
+    }
+  };
+  desc(0, kt, mr);
+  const FetchPlan fp = TT::plan(kt.stride, tid);
+  TT::template fetch<GATHER>(pf, sm, 0, qb, dob, kt, fp, tid);
+  row_vals(kt);
+  TT::stage(sm, 0, pf, tid);
+  stage_meta<bf16, false, false>(sm, 0, pf.meta, gi, nolab, kt.gmode, tid);
+  put_rows(0);
+  __syncthreads();
+  auto step = [&](auto buf_tag, int32_t n) {
+    constexpr int32_t buf = decltype(buf_tag)::value;
+    KeyTile kt_next;
+    MaskRule mr_next;
+    const bool more = n + 1 < n_tiles;
+    if (more) {
+      desc(n + 1, kt_next, mr_next);
+      TT::template fetch<GATHER>(pf, sm, buf ^ 1, qb, dob, kt_next, fp, tid);
+      row_vals(kt_next);
+    }
+    proc(buf_tag, kt, mr);
+    if (more) {
+      TT::stage(sm, buf ^ 1, pf, tid);
+      stage_meta<bf16, false, false>(sm, buf ^ 1, pf.meta, gi, nolab, kt_next.gmode, tid);
+      put_rows(buf ^ 1);
+      kt = kt_next;
+      mr = mr_next;
+    }
+    __syncthreads();
+  };
+  for (int32_t n = 0; n < n_tiles; n += 2) {
+    step(BufTag<0>{}, n);
+    if (n + 1 < n_tiles) step(BufTag<1>{}, n + 1);
+  }
+}
+
+// Lane row of dK^T / dV^T (d = 32db + 8j + 4h + i) to an fp32 row.
+__device__ __forceinline__ void store_rows_f32(float* dst, const f32x16 (&acc)[2], float sc,
+                                               int32_t lane) {
+  const int32_t hh = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = acc[db][4 * j + i] * sc;
+      *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * j + 4 * hh) = x;
+    }
+  }
+}
+
+// dK, dV of the non-global keys of one key tile (a residue class of the
+// head's dilation, like the forward's query tiles).
+__device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t bw) {
+  constexpr int32_t kTQ = TT::kTQ;
+  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t N = a.N;
+  const size_t head_elems = (size_t)N * kD;
+  const int32_t bh = bw / a.band_tiles_per_head;
+  int32_t tile = bw % a.band_tiles_per_head;
+  const int32_t h = bh % a.H;
+  const int32_t d = a.dil[h];
+  int32_t c = 0, n_c = 0;
+  for (; c < d && c < N; ++c) {
+    n_c = (N - c + d - 1) / d;
+    const int32_t tc = tiles_of_class(N, d, c, kTQ);
+    if (tile < tc) break;
+    tile -= tc;
+  }
+  if (c >= d || c >= N) return;
+  const int32_t t0 = tile * kTQ;
+  const int32_t kcount = min(kTQ, n_c - t0);
+  const int32_t kbase = c + d * t0;
+  const int32_t j_lo = kbase, j_hi = kbase + d * (kcount - 1);
+  const int32_t ng = a.n_global;
+  const int32_t g_first = ng > 0 ? a.gidx[0] : 0;
+  const int32_t g_last = ng > 0 ? a.gidx[ng - 1] : -1;
+  // a tile of global keys only: the global-key pass has them
+  if (d == 1 && g_last - g_first == ng - 1 && g_first <= j_lo && g_last >= j_hi) return;
+
+  const int32_t ki = TT::qrow(wave, lane, 0);
+  const int32_t kpos = kbase + d * min(ki, kcount - 1);
+  const bool dead = TT::kQW * wave >= kcount;
+  DkvWave w;
+  load_frag(w.kf, static_cast<const bf16*>(a.k) + bh * head_elems, kpos, lane);
+  load_frag(w.vf, static_cast<const bf16*>(a.v) + bh * head_elems, kpos, lane);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    w.dk[x] = f32x16{};
+    w.dv[x] = f32x16{};
+  }
+  const float* lse = a.lse + (size_t)bh * N;
+  const float* delta = a.delta + (size_t)bh * N;
+  const bf16* dob = static_cast<const bf16*>(a.dout) + bh * head_elems;
+
+  // window rows in strided index space [lo, hi]: rows i with
+  // -R <= i - j <= R (causal: 0 <= i - j <= R)
+  const int32_t R = a.radius;
+  const int32_t lo = a.causal ? t0 : max(0, t0 - R);
+  const int32_t hi = min(n_c - 1, t0 + kcount - 1 + R);
+  const int32_t n_band = (hi - lo + 1 + kTK - 1) / kTK;
+  const int32_t lob = a.causal ? 0 : -R;
+  GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
+  if (ng > 0) {  // the rows' global flags: global rows come in their own sweep
+    if (hi - lo + 1 <= 32 * kGMaskWords) {
+      build_gmask<bf16>(sm, a.gidx, ng, c + d * lo, d, hi - lo + 1, tid);
+      gi.mode = kGlobBitmap;
+    } else {
+      gi.mode = kGlobSearch;
+    }
+  }
+  auto band_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+    const int32_t u0 = lo + n * kTK;
+    const int32_t cnt = min(kTK, hi - u0 + 1);
+    kt = {nullptr, c + d * u0, d, cnt, u0 - lo, gi.mode};
+    // strided index difference row - key = kr - ki - (t0 - u0)
+    const int32_t dmin = u0 - t0 - (kcount - 1);
+    const int32_t dmax = u0 + cnt - 1 - t0;
+    const bool full = cnt == kTK && dmin >= lob && dmax <= R;
+    mr = {kRange, full ? 0 : 1, 0, t0 - u0, lob, R, 0, 0, 1};
+  };
+  const bf16* qs = static_cast<const bf16*>(a.q) + bh * head_elems;
+  stream_rows<false>(sm, qs, dob, lse, delta, n_band, band_desc, gi,
+                     [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                       constexpr int32_t buf = decltype(buf_tag)::value;
+                       dkv_tile<buf, true, false>(sm, w, lane, mr, kt, ki, kpos, dead,
+                                                  a.scale_log2, a.causal);
+                     });
+  // the global rows reach every key (causal: rows at or after it)
+  const int32_t n_gt = (ng + kTK - 1) / kTK;
+  const GlobInfo gall = {kGlobNone, a.gidx, ng, nullptr, 0, 0, 0};
+  auto glob_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+    const int32_t cnt = min(kTK, ng - n * kTK);
+    kt = {a.gidx + n * kTK, 0, 1, cnt, 0, kGlobNone};
+    // every row of the tile, unless it is past the tile's end
+    mr = {kRange, cnt == kTK ? 0 : 1, 0, 0, -kFar, kFar, 0, 0, 1};
+  };
+  auto glob_proc = [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+    constexpr int32_t buf = decltype(buf_tag)::value;
+    dkv_tile<buf, false, true>(sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal);
+  };
+  const bool mine = ki < kcount && !qi_is_global(a, ki, kcount, kpos, g_first, g_last, j_lo, j_hi);
+  if (a.sep) {
+    // the window's rows are done: their dK, dV; the global rows go through
+    // qg_i, kg_j, vg_j into dKg, dVg
+    if (mine) {
+      store_rows_f32(a.dk + ((size_t)bh * N + kpos) * kD, w.dk, a.scale, lane);
+      store_rows_f32(a.dv + ((size_t)bh * N + kpos) * kD, w.dv, 1.f, lane);
+    }
+    load_frag(w.kf, static_cast<const bf16*>(a.kg) + bh * head_elems, kpos, lane);
+    load_frag(w.vf, static_cast<const bf16*>(a.vg) + bh * head_elems, kpos, lane);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      w.dk[x] = f32x16{};
+      w.dv[x] = f32x16{};
+    }
+  }
+  if (ng > 0)
+    stream_rows<true>(sm, static_cast<const bf16*>(a.sep ? a.qg : a.q) + bh * head_elems, dob,
+                      lse, delta, n_gt, glob_desc, gall, glob_proc);
+  if (mine) {
+    float* const dk = a.sep ? a.dkg : a.dk;
+    float* const dv = a.sep ? a.dvg : a.dv;
+    store_rows_f32(dk + ((size_t)bh * N + kpos) * kD, w.dk, a.scale, lane);
+    store_rows_f32(dv + ((size_t)bh * N + kpos) * kD, w.dv, 1.f, lane);
+  }
+}
+
+__global__ __launch_bounds__(TT::kThreads)
+__attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkv_mfma_kernel(BwdArgs a) {
+  __shared__ TT::Smem sm;
+  const int32_t x = (int32_t)blockIdx.x % kXcds, j = (int32_t)blockIdx.x / kXcds;
+  const int32_t per = (a.n_band_wg + kXcds - 1) / kXcds;
+  const int32_t bw = x * per + j;
+  if (j >= per || bw >= a.n_band_wg) return;
+  dkv_band_workgroup(a, sm, bw);
+}
+
+// Block b runs on XCD b % 8; each XCD takes a contiguous share of the query
+// tiles (tiles of one head then share K/V in that XCD's L2).
+// Two fragments per row (Q and dO) and two dot products per pair need more
+// registers than the forward: 3 waves per SIMD.
+__global__ __launch_bounds__(TT::kThreads)
+__attribute__((amdgpu_waves_per_eu(3)))
+void bwd_dq_mfma_kernel(BwdArgs a) {
+  __shared__ TT::Smem sm;
+  const int32_t x = (int32_t)blockIdx.x % kXcds, j = (int32_t)blockIdx.x / kXcds;
+  const int32_t per = (a.n_band_wg + kXcds - 1) / kXcds;
+  const int32_t bw = x * per + j;
+  if (j >= per || bw >= a.n_band_wg) return;
+  dq_band_workgroup(a, sm, bw);
+}
+
+}  // namespace
+
+hipError_t launch_dq_mfma(const BwdArgs& a, hipStream_t stream) {
+  if (a.n_band_wg <= 0) return hipSuccess;
+  const int64_t grid = (int64_t)kXcds * ((a.n_band_wg + kXcds - 1) / kXcds);
+  hipLaunchKernelGGL(bwd_dq_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dkv_mfma(const BwdArgs& a, hipStream_t stream) {
+  if (a.n_band_wg <= 0) return hipSuccess;
+  const int64_t grid = (int64_t)kXcds * ((a.n_band_wg + kXcds - 1) / kXcds);
+  hipLaunchKernelGGL(bwd_dkv_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace la
