@@ -259,7 +259,10 @@ typedef struct {
  *  dout         device [B,H,N,D] in q's dtype: the loss gradient w.r.t. out.
  *  dq, dk, dv   device fp32 [B,H,N,D] outputs; must not alias any input.
  * Requires ext->workspace (fully overwritten). Pointers 16-byte aligned. Errors
- * as for la_attn_forward. Three launches on `stream`, no allocation. */
+ * as for la_attn_forward. Three to six launches on `stream` (bf16 without
+ * tables, labels or segment ids: global ranks, D_i, MFMA dQ and dK/dV of the
+ * non-global rows and keys, then the global rows' and keys' own kernels), no
+ * allocation. */
 la_status la_attn_backward(const la_dims *dims, const void *q, const void *k, const void *v,
                            const int32_t *global_idx, int32_t n_global, int32_t radius,
                            const int32_t *dilation, int32_t causal, const void *out,
@@ -281,7 +284,9 @@ size_t la_attn_backward_workspace_size(const la_dims *dims);
  *  dout         device bf16 [B,H,N,D]: the loss gradient w.r.t. out.
  *  dq, dk, dv   device fp32 [B,H,N,D] outputs (fully written; must not alias inputs).
  *  workspace    la_dilated_backward_workspace_size() bytes, 256-byte aligned.
- * Errors as for la_dilated_forward. Two launches on `stream`, no allocation. */
+ * Errors as for la_dilated_forward. 2 + 2 * n_pairs launches on `stream` (D_i,
+ * zeroed gradients, then each pattern's dQ and dK/dV terms added in pattern
+ * order: deterministic), no allocation. */
 la_status la_dilated_backward(const la_dims *dims, const void *q, const void *k, const void *v,
                               const int32_t *seg_lens, const int32_t *dil_rates, int32_t n_pairs,
                               int32_t causal, const void *out, const float *lse,

@@ -604,6 +604,7 @@ la_status la_dilated_backward(const la_dims* dims, const void* q, const void* k,
   a.causal = causal;
   a.n_pairs = n_pairs;
   a.scale = (float)(1.0 / sqrt((double)kDHead));
+  a.scale_log2 = (float)(1.0 / sqrt((double)kDHead) * 1.4426950408889634);
   hipError_t e = la::launch_dilated_bwd(a, stream);
   if (e != hipSuccess) return fail(LA_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(e));
   return LA_OK;

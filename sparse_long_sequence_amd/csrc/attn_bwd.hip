@@ -17,11 +17,12 @@
 // No atomics: after a pass that marks the global positions, a query-centric
 // pass (one wave per row) writes D_i and dQ_i, and a key-centric pass (one
 // wave per key) visits every row that attends to its key and writes dK_j and
-// dV_j in one store. Lane d of a wave
-// holds element d of the 64-wide vectors; dot products are wave reductions.
-// This is the plain first form of the backward: fp32 VALU work, no MFMA. The
-// fp32 path keeps one lane per vector element (dot products as wave sums); the
-// bf16 path (below) puts one key or row on each lane instead.
+// dV_j in one store. These are the scalar kernels: fp32 VALU work, no MFMA.
+// The fp32 path keeps one lane per vector element (dot products as wave
+// sums); the bf16 path (below) puts one key or row on each lane instead. They
+// serve fp32 calls, calls with bias tables, labels or segment ids, and (bf16)
+// the global rows' dQ and the global keys' dK, dV; everything else runs on
+// the MFMA tile engine (attn_bwd_mfma.hip), the LongNet mixture included.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -581,139 +582,6 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_rows_kernel(BwdArgs a)
   }
 }
 
-// ---------------------------------------------------------------------------
-// LongNet mixture (bf16). The mixture is one softmax over the multiset of the
-// patterns' keys (LongNet page, §3.4 "Mixture of Dilated Attentions"), so a
-// pair reached by several patterns is visited once per pattern: the sweeps
-// below run per pattern over the kept positions of the row's (or key's)
-// segment, which adds the multiplicity by itself.
-// ---------------------------------------------------------------------------
-
-// Pattern (w, r) for head h around position p: the segment's first kept
-// position, its kept count, and whether p itself is kept (LongNet page, §3.4
-// "Dilated Attention: Core Mechanism" and "Multi-Head Dilated Attention:
-// Offset Mechanism": offset h mod r; the last segment ends at N).
-struct KeptRun {
-  int32_t first, count;
-  bool kept;
-};
-__device__ __forceinline__ KeptRun kept_run(int32_t p, int32_t w, int32_t r, int32_t h, int32_t N) {
-  const int32_t s0 = (p / w) * w, off = h % r;
-  const int32_t first = s0 + off, end = min(s0 + w, N);
-  return {first, first < end ? (end - first + r - 1) / r : 0, (p - s0) % r == off};
-}
-
-__global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_dil_kernel(BwdArgs a) {
-  __shared__ float vq[kWavesBwd][kD], vdo[kWavesBwd][kD];
-  const int32_t lane = threadIdx.x & 63;
-  const int32_t wv = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
-  const int64_t rows = (int64_t)a.B * a.H * a.N;
-  const int64_t row0 = (int64_t)blockIdx.x * kWavesBwd + wv;
-  const bool valid = row0 < rows;
-  const int64_t row = valid ? row0 : rows - 1;
-  const int32_t N = a.N;
-  const int32_t i = (int32_t)(row % N);
-  const int64_t bh = row / N;
-  const int32_t h = (int32_t)(bh % a.H);
-  const size_t hoff = (size_t)bh * N * kD;
-  const bf16* K = static_cast<const bf16*>(a.k) + hoff;
-  const bf16* V = static_cast<const bf16*>(a.v) + hoff;
-  const float dov = load_el(static_cast<const bf16*>(a.dout) + hoff + (size_t)i * kD + lane);
-  const float ov = load_el(static_cast<const bf16*>(a.out) + hoff + (size_t)i * kD + lane);
-  const float Di = wave_sum(dov * ov);
-  vq[wv][lane] = load_el(static_cast<const bf16*>(a.q) + hoff + (size_t)i * kD + lane);
-  vdo[wv][lane] = dov;
-  __syncthreads();  // the only barrier: every wave reaches it
-  if (!valid) return;
-  if (lane == 0) a.delta[row] = Di;
-  const float lse = a.lse[row];
-  float acc[kD];
-#pragma unroll
-  for (int d = 0; d < kD; ++d) acc[d] = 0.f;
-  if (lse != kNegInf) {
-    for (int32_t p = 0; p < a.n_pairs; ++p) {
-      const int32_t r = a.pr[p];
-      const KeptRun kr = kept_run(i, a.pw[p], r, h, N);
-      if (!kr.kept) continue;
-      // keys first + x r, x < n (causal: up to i itself)
-      const int32_t n = a.causal ? (i - kr.first) / r + 1 : kr.count;
-      for (int32_t x0 = 0; x0 < n; x0 += 64) {
-        const int32_t x = x0 + lane;
-        const int32_t j = x < n ? kr.first + x * r : -1;
-        const int32_t rr = j >= 0 ? j : i;
-        uint4 kc[8], vc[8];
-        load_row(K + (size_t)rr * kD, kc);
-        load_row(V + (size_t)rr * kD, vc);
-        const float sc = dot_row(kc, vq[wv]);
-        const float dp = dot_row(vc, vdo[wv]);
-        const float pr = j >= 0 ? __expf(sc * a.scale - lse) : 0.f;
-        axpy_row(acc, pr * (dp - Di), kc);
-      }
-    }
-  }
-  a.dq[hoff + (size_t)i * kD + lane] = lane_totals(acc, lane) * a.scale;
-}
-
-__global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_dil_kernel(BwdArgs a) {
-  __shared__ float vk[kWavesBwd][kD], vv[kWavesBwd][kD];
-  const int32_t lane = threadIdx.x & 63;
-  const int32_t wv = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
-  const int64_t keys = (int64_t)a.B * a.H * a.N;
-  const int64_t key0 = (int64_t)blockIdx.x * kWavesBwd + wv;
-  const bool valid = key0 < keys;
-  const int64_t key = valid ? key0 : keys - 1;
-  const int32_t N = a.N;
-  const int32_t j = (int32_t)(key % N);
-  const int64_t bh = key / N;
-  const int32_t h = (int32_t)(bh % a.H);
-  const size_t hoff = (size_t)bh * N * kD;
-  vk[wv][lane] = load_el(static_cast<const bf16*>(a.k) + hoff + (size_t)j * kD + lane);
-  vv[wv][lane] = load_el(static_cast<const bf16*>(a.v) + hoff + (size_t)j * kD + lane);
-  __syncthreads();  // the only barrier: every wave reaches it
-  if (!valid) return;
-  const float* lse = a.lse + (size_t)bh * N;
-  const float* delta = a.delta + (size_t)bh * N;
-  const bf16* Q = static_cast<const bf16*>(a.q) + hoff;
-  const bf16* dO = static_cast<const bf16*>(a.dout) + hoff;
-  float acc[kD];
-  // dV (s only), then dK (s and dP), over the rows every pattern pairs with j
-  auto pass = [&](bool dk_pass) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < kD; ++e) acc[e] = 0.f;
-    for (int32_t p = 0; p < a.n_pairs; ++p) {
-      const int32_t r = a.pr[p];
-      const KeptRun kr = kept_run(j, a.pw[p], r, h, N);
-      if (!kr.kept) continue;
-      // rows i0 + x r, x < n (causal: from j itself on)
-      const int32_t mj = (j - kr.first) / r;
-      const int32_t i0 = a.causal ? j : kr.first;
-      const int32_t n = a.causal ? kr.count - mj : kr.count;
-      for (int32_t x0 = 0; x0 < n; x0 += 64) {
-        const int32_t x = x0 + lane;
-        const int32_t i = x < n ? i0 + x * r : -1;
-        const int32_t rr = i >= 0 ? i : j;
-        uint4 qc[8], oc[8];
-        load_row(Q + (size_t)rr * kD, qc);
-        load_row(dO + (size_t)rr * kD, oc);
-        const float li = lse[rr];
-        const float sc = dot_row(qc, vk[wv]);
-        const bool on = i >= 0 && li != kNegInf;
-        const float pr = on ? __expf(sc * a.scale - li) : 0.f;
-        if (dk_pass) {
-          const float dp = dot_row(oc, vv[wv]);
-          axpy_row(acc, pr * (dp - delta[rr]), qc);
-        } else {
-          axpy_row(acc, pr, oc);
-        }
-      }
-    }
-  };
-  pass(false);
-  a.dv[hoff + (size_t)j * kD + lane] = lane_totals(acc, lane);
-  pass(true);
-  a.dk[hoff + (size_t)j * kD + lane] = lane_totals(acc, lane) * a.scale;
-}
-
 }  // namespace
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) {
@@ -751,9 +619,9 @@ hipError_t launch_dilated_bwd(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   if (rows <= 0) return hipSuccess;
   const dim3 g((uint32_t)((rows + kWavesBwd - 1) / kWavesBwd)), blk(64 * kWavesBwd);
-  hipLaunchKernelGGL(bwd_dq_dil_kernel, g, blk, 0, stream, a);
-  hipLaunchKernelGGL(bwd_dkv_dil_kernel, g, blk, 0, stream, a);
-  return hipGetLastError();
+  // D_i per row, then each pattern's terms on the MFMA tile engine
+  hipLaunchKernelGGL(bwd_delta_kernel<bf16>, g, blk, 0, stream, a);
+  return launch_dilated_bwd_mfma(a, stream);
 }
 
 }  // namespace la

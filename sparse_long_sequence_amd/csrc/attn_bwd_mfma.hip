@@ -642,7 +642,180 @@ void bwd_dq_mfma_kernel(BwdArgs a) {
   dq_band_workgroup(a, sm, bw);
 }
 
+// ---------------------------------------------------------------------------
+// LongNet mixture (bf16). The mixture is one softmax over the multiset of the
+// patterns' keys (LongNet page, §3.4 "Mixture of Dilated Attentions"), so with
+// the mixture's lse each pattern contributes its own pairs' terms and a pair
+// kept by several patterns adds once per pattern. One launch per pattern and
+// gradient adds that pattern's terms into dQ (or dK, dV), in pattern order:
+// every kept row (or key) belongs to one workgroup of a launch, so the sums
+// are deterministic; rows no pattern keeps keep the zeros written first.
+// ---------------------------------------------------------------------------
+
+// The pattern's segment geometry for head h (as the forward's dilated_tile):
+// kept rows base + r * t, t in [0, n_rows).
+struct DilGeom {
+  int32_t base, r, n_rows;
+};
+__device__ __forceinline__ DilGeom dil_geom(const BwdArgs& a, int32_t k, int32_t seg, int32_t h) {
+  const int32_t w = a.pw[k], r = a.pr[k];
+  const int32_t sigma = seg * w;
+  const int32_t L = min(w, a.N - sigma);
+  const int32_t s = h % r;
+  return {sigma + s, r, L > s ? (L - s + r - 1) / r : 0};
+}
+
+// Workgroup wg of a pattern launch: query (or key) tiles of kept rows, the
+// heaviest (latest) tile index first.
+__device__ __forceinline__ void dil_decode(const BwdArgs& a, int32_t nseg, int32_t qtiles,
+                                           int64_t wg, int32_t& qt, int32_t& seg, int32_t& bh) {
+  const int64_t per = (int64_t)a.B * a.H * nseg;
+  qt = qtiles - 1 - (int32_t)(wg / per);
+  const int64_t rest = wg % per;
+  seg = (int32_t)(rest % nseg);
+  bh = (int32_t)(rest / nseg);
+}
+
+// this lane's row += acc * sc (an fp32 row owned by this workgroup)
+__device__ __forceinline__ void add_rows_f32(float* dst, const f32x16 (&acc)[2], float sc,
+                                             int32_t lane) {
+  const int32_t hh = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4* p = reinterpret_cast<f32x4*>(dst + 32 * db + 8 * j + 4 * hh);
+      f32x4 x = *p;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] += acc[db][4 * j + i] * sc;
+      *p = x;
+    }
+  }
+}
+
+__global__ __launch_bounds__(TT::kThreads)
+__attribute__((amdgpu_waves_per_eu(3)))
+void bwd_dq_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles) {
+  __shared__ TT::Smem sm;
+  constexpr int32_t kTQ = TT::kTQ;
+  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t qt, seg, bh;
+  dil_decode(a, nseg, qtiles, blockIdx.x, qt, seg, bh);
+  const DilGeom g = dil_geom(a, k, seg, bh % a.H);
+  const int32_t t0 = qt * kTQ;
+  if (t0 >= g.n_rows) return;
+  const int32_t qcount = min(kTQ, g.n_rows - t0);
+  const size_t head_elems = (size_t)a.N * kD;
+  const int32_t qi = TT::qrow(wave, lane, 0);
+  const int32_t qpos = g.base + g.r * (t0 + min(qi, qcount - 1));
+  const bool dead = TT::kQW * wave >= qcount;
+  DqWave w;
+  load_frag(w.qf, static_cast<const bf16*>(a.q) + bh * head_elems, qpos, lane);
+  load_frag(w.df, static_cast<const bf16*>(a.dout) + bh * head_elems, qpos, lane);
+  const float lse = a.lse[(size_t)bh * a.N + qpos];
+  w.lse2 = lse == kNegInf ? -kNegInf : lse * kLog2e;
+  w.di = a.delta[(size_t)bh * a.N + qpos];
+  w.acc[0] = f32x16{};
+  w.acc[1] = f32x16{};
+  const int32_t hi = a.causal ? t0 + qcount - 1 : g.n_rows - 1;
+  const int32_t n_tiles = (hi + kTK) / kTK;
+  auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+    const int32_t u0 = n * kTK;
+    const int32_t kcount = min(kTK, hi - u0 + 1);
+    kt = {nullptr, g.base + g.r * u0, g.r, kcount, 0, kGlobNone};
+    const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= t0);
+    mr = {kRange, full ? 0 : 1, 0, t0 - u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
+  };
+  const GlobInfo gi = {kGlobNone, nullptr, 0, nullptr, 0, 0, 0};
+  stream_tiles<false>(sm, static_cast<const bf16*>(a.k) + bh * head_elems,
+                      static_cast<const bf16*>(a.v) + bh * head_elems, n_tiles, desc, gi,
+                      [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                        constexpr int32_t buf = decltype(buf_tag)::value;
+                        dq_tile<buf>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2);
+                      });
+  if (qi < qcount) add_rows_f32(a.dq + ((size_t)bh * a.N + qpos) * kD, w.acc, a.scale, lane);
+}
+
+__global__ __launch_bounds__(TT::kThreads)
+__attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkv_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles) {
+  __shared__ TT::Smem sm;
+  constexpr int32_t kTQ = TT::kTQ;
+  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t qt, seg, bh;
+  dil_decode(a, nseg, qtiles, blockIdx.x, qt, seg, bh);
+  const DilGeom g = dil_geom(a, k, seg, bh % a.H);
+  const int32_t t0 = qt * kTQ;
+  if (t0 >= g.n_rows) return;
+  const int32_t kcount = min(kTQ, g.n_rows - t0);
+  const size_t head_elems = (size_t)a.N * kD;
+  const int32_t ki = TT::qrow(wave, lane, 0);
+  const int32_t kpos = g.base + g.r * (t0 + min(ki, kcount - 1));
+  const bool dead = TT::kQW * wave >= kcount;
+  DkvWave w;
+  load_frag(w.kf, static_cast<const bf16*>(a.k) + bh * head_elems, kpos, lane);
+  load_frag(w.vf, static_cast<const bf16*>(a.v) + bh * head_elems, kpos, lane);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    w.dk[x] = f32x16{};
+    w.dv[x] = f32x16{};
+  }
+  // rows at or after the keys (causal), else every kept row
+  const int32_t lo = a.causal ? t0 : 0, hi = g.n_rows - 1;
+  const int32_t n_tiles = (hi - lo + 1 + kTK - 1) / kTK;
+  const int32_t lob = a.causal ? 0 : -kFar;
+  auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+    const int32_t u0 = lo + n * kTK;
+    const int32_t cnt = min(kTK, hi - u0 + 1);
+    kt = {nullptr, g.base + g.r * u0, g.r, cnt, 0, kGlobNone};
+    const bool full = cnt == kTK && (!a.causal || u0 >= t0 + kcount - 1);
+    mr = {kRange, full ? 0 : 1, 0, t0 - u0, lob, kFar, 0, 0, 1};
+  };
+  const GlobInfo gi = {kGlobNone, nullptr, 0, nullptr, 0, 0, 0};
+  stream_rows<false>(sm, static_cast<const bf16*>(a.q) + bh * head_elems,
+                     static_cast<const bf16*>(a.dout) + bh * head_elems,
+                     a.lse + (size_t)bh * a.N, a.delta + (size_t)bh * a.N, n_tiles, desc, gi,
+                     [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                       constexpr int32_t buf = decltype(buf_tag)::value;
+                       dkv_tile<buf, false, false>(sm, w, lane, mr, kt, ki, kpos, dead,
+                                                   a.scale_log2, a.causal);
+                     });
+  if (ki < kcount) {
+    add_rows_f32(a.dk + ((size_t)bh * a.N + kpos) * kD, w.dk, a.scale, lane);
+    add_rows_f32(a.dv + ((size_t)bh * a.N + kpos) * kD, w.dv, 1.f, lane);
+  }
+}
+
+// zeros into three fp32 buffers of n4 float4 each (a kernel: no memset)
+__global__ __launch_bounds__(256) void bwd_zero3_kernel(float* x, float* y, float* z, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  reinterpret_cast<f32x4*>(x)[i] = zero;
+  reinterpret_cast<f32x4*>(y)[i] = zero;
+  reinterpret_cast<f32x4*>(z)[i] = zero;
+}
+
 }  // namespace
+
+hipError_t launch_dilated_bwd_mfma(const BwdArgs& a, hipStream_t stream) {
+  const int64_t n4 = (int64_t)a.B * a.H * a.N * kD / 4;
+  if (n4 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_zero3_kernel, dim3((uint32_t)((n4 + 255) / 256)), dim3(256), 0, stream,
+                     a.dq, a.dk, a.dv, n4);
+  for (int32_t k = 0; k < a.n_pairs; ++k) {
+    const int32_t nseg = (a.N + a.pw[k] - 1) / a.pw[k];
+    const int32_t rows = (a.pw[k] + a.pr[k] - 1) / a.pr[k];
+    const int32_t qtiles = (rows + TT::kTQ - 1) / TT::kTQ;
+    const int64_t grid = (int64_t)a.B * a.H * nseg * qtiles;
+    if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bwd_dq_dil_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0, stream,
+                       a, k, nseg, qtiles);
+    hipLaunchKernelGGL(bwd_dkv_dil_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
+                       stream, a, k, nseg, qtiles);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_dq_mfma(const BwdArgs& a, hipStream_t stream) {
   if (a.n_band_wg <= 0) return hipSuccess;

@@ -121,6 +121,7 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream);
 hipError_t launch_dq_mfma(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dkv_mfma(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dilated_bwd(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_dilated_bwd_mfma(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dilated(const DilArgs& a, hipStream_t stream);
 int32_t host_band_tiles_of_head(int32_t N, int32_t d, int32_t tq);
 int32_t host_query_tile(int32_t dtype);  // query rows per workgroup
