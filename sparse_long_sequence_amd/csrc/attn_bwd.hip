@@ -382,14 +382,10 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_rows_kernel(BwdArgs a) 
   const int32_t lane = threadIdx.x & 63;
   const int32_t wv = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
   const int32_t N = a.N;
-  // every row, or (dq_global_rows) the global rows only: (b, h, g) in order
-  const int64_t rows = a.dq_global_rows ? (int64_t)a.B * a.H * a.n_global : (int64_t)a.B * a.H * N;
+  const int64_t rows = (int64_t)a.B * a.H * N;
   const int64_t row0 = (int64_t)blockIdx.x * kWavesBwd + wv;
   const bool valid = row0 < rows;
-  const int64_t slot = valid ? row0 : rows - 1;  // a wave past the end stages a valid row
-  const int64_t row = a.dq_global_rows
-                          ? (slot / a.n_global) * N + a.gidx[slot % a.n_global]
-                          : slot;
+  const int64_t row = valid ? row0 : rows - 1;  // a wave past the end stages a valid row
   const int32_t i = (int32_t)(row % N);
   const int64_t bh = row / N;
   const int32_t h = (int32_t)(bh % a.H), b = (int32_t)(bh / a.H);
@@ -414,7 +410,7 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_rows_kernel(BwdArgs a) 
     }
   __syncthreads();  // the only barrier: every wave reaches it
   if (!valid) return;
-  if (lane == 0 && !a.dq_global_rows) a.delta[row] = Di;
+  if (lane == 0) a.delta[row] = Di;
   const float lse = a.lse[row];
   const int32_t* segb = a.seg ? a.seg + (size_t)b * N : nullptr;
   float acc[kD];
@@ -482,14 +478,10 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_rows_kernel(BwdArgs a)
   const int32_t lane = threadIdx.x & 63;
   const int32_t wv = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
   const int32_t N = a.N;
-  // every key, or (dkv_global_keys) the global keys only: (b, h, g) in order
-  const int64_t keys = a.dkv_global_keys ? (int64_t)a.B * a.H * a.n_global : (int64_t)a.B * a.H * N;
+  const int64_t keys = (int64_t)a.B * a.H * N;
   const int64_t key0 = (int64_t)blockIdx.x * kWavesBwd + wv;
   const bool valid = key0 < keys;
-  const int64_t slot = valid ? key0 : keys - 1;
-  const int64_t key = a.dkv_global_keys
-                          ? (slot / a.n_global) * N + a.gidx[slot % a.n_global]
-                          : slot;
+  const int64_t key = valid ? key0 : keys - 1;
   const int32_t j = (int32_t)(key % N);
   const int64_t bh = key / N;
   const int32_t h = (int32_t)(bh % a.H), b = (int32_t)(bh / a.H);
@@ -596,15 +588,8 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) 
     if (e != hipSuccess) return e;
     e = launch_dkv_mfma(a, stream);
     if (e != hipSuccess) return e;
-    if (a.n_global > 0) {  // the global rows' dQ and the global keys' dK, dV per row / key
-      BwdArgs ag = a;
-      ag.dq_global_rows = 1;
-      ag.dkv_global_keys = 1;
-      const int64_t grows = (int64_t)a.B * a.H * a.n_global;
-      const dim3 gg((uint32_t)((grows + kWavesBwd - 1) / kWavesBwd));
-      hipLaunchKernelGGL(bwd_dq_rows_kernel, gg, blk, 0, stream, ag);
-      hipLaunchKernelGGL(bwd_dkv_rows_kernel, gg, blk, 0, stream, ag);
-    }
+    e = launch_glob_mfma(a, stream);  // the global rows' dQ, the global keys' dK, dV
+    if (e != hipSuccess) return e;
   } else if (dtype == 1) {
     hipLaunchKernelGGL(bwd_dq_rows_kernel, g, blk, 0, stream, a);
     hipLaunchKernelGGL(bwd_dkv_rows_kernel, g, blk, 0, stream, a);

@@ -371,8 +371,10 @@ template <int32_t BUF, bool EXCL_G, bool ROWS_AFTER>
 __device__ __forceinline__ void dkv_tile(const TT::Smem& sm, DkvWave& w, int32_t lane,
                                          const MaskRule& mr, const KeyTile& kt, int32_t ki,
                                          int32_t kpos, bool dead, float c, bool causal) {
-  const int32_t r0 = __builtin_amdgcn_readlane(ki, 0) + mr.ref_off;
-  const int32_t r1 = __builtin_amdgcn_readlane(ki, TT::kRowsPerBlock - 1) + mr.ref_off;
+  const int32_t r0 = (mr.use_qpos ? __builtin_amdgcn_readlane(kpos, 0)
+                                  : __builtin_amdgcn_readlane(ki, 0)) + mr.ref_off;
+  const int32_t r1 = (mr.use_qpos ? __builtin_amdgcn_readlane(kpos, TT::kRowsPerBlock - 1)
+                                  : __builtin_amdgcn_readlane(ki, TT::kRowsPerBlock - 1)) + mr.ref_off;
   bool any_g = false;
   if constexpr (EXCL_G)
     any_g = kt.gmode != kGlobNone && (__builtin_amdgcn_readfirstlane(sm.gcls[BUF]) & 1) != 0;
@@ -643,6 +645,161 @@ void bwd_dq_mfma_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// The global rows' dQ and the global keys' dK, dV: a global row reaches every
+// key and a global key every row, so a workgroup owns a tile of global rows
+// (or keys) and streams every key (or row) position in order.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(TT::kThreads)
+__attribute__((amdgpu_waves_per_eu(3)))
+void bwd_dq_glob_mfma_kernel(BwdArgs a) {
+  __shared__ TT::Smem sm;
+  constexpr int32_t kTQ = TT::kTQ;
+  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t n_gq = (a.n_global + kTQ - 1) / kTQ;
+  const int32_t bh = (int32_t)blockIdx.x / n_gq, gq = (int32_t)blockIdx.x % n_gq;
+  const int32_t N = a.N;
+  const size_t head_elems = (size_t)N * kD;
+  const int32_t qcount = min(kTQ, a.n_global - gq * kTQ);
+  const int32_t* qidx = a.gidx + gq * kTQ;
+  const int32_t i_min = qidx[0], i_max = qidx[qcount - 1];
+  const int32_t qi = TT::qrow(wave, lane, 0);
+  const int32_t qpos = qidx[min(qi, qcount - 1)];
+  const bool dead = TT::kQW * wave >= qcount;
+  const bool sep = a.sep != 0;
+  DqWave w;
+  load_frag(w.qf, static_cast<const bf16*>(sep ? a.qg : a.q) + bh * head_elems, qpos, lane);
+  load_frag(w.df, static_cast<const bf16*>(a.dout) + bh * head_elems, qpos, lane);
+  const float lse = a.lse[(size_t)bh * N + qpos];
+  w.lse2 = lse == kNegInf ? -kNegInf : lse * kLog2e;
+  w.di = a.delta[(size_t)bh * N + qpos];
+  w.acc[0] = f32x16{};
+  w.acc[1] = f32x16{};
+  const int32_t j1 = a.causal ? i_max + 1 : N;
+  const int32_t n_tiles = (j1 + kTK - 1) / kTK;
+  auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+    const int32_t u0 = n * kTK;
+    const int32_t kcount = min(kTK, j1 - u0);
+    kt = {nullptr, u0, 1, kcount, 0, kGlobNone};
+    // key position u0 + kj <= qpos when causal
+    const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= i_min);
+    mr = {kRange, full ? 0 : 1, 1, -u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
+  };
+  const GlobInfo gi = {kGlobNone, nullptr, 0, nullptr, 0, 0, 0};
+  stream_tiles<false>(sm, static_cast<const bf16*>(sep ? a.kg : a.k) + bh * head_elems,
+                      static_cast<const bf16*>(sep ? a.vg : a.v) + bh * head_elems, n_tiles, desc,
+                      gi, [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                        constexpr int32_t buf = decltype(buf_tag)::value;
+                        dq_tile<buf>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2);
+                      });
+  if (qi < qcount) {
+    const size_t ro = ((size_t)bh * N + qpos) * kD;
+    store_rows_f32((sep ? a.dqg : a.dq) + ro, w.acc, a.scale, lane);
+    if (sep) {  // a global row's shared-projection gradient is 0
+      f32x16 z[2] = {f32x16{}, f32x16{}};
+      store_rows_f32(a.dq + ro, z, 0.f, lane);
+    }
+  }
+}
+
+__global__ __launch_bounds__(TT::kThreads)
+__attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkv_glob_mfma_kernel(BwdArgs a) {
+  __shared__ TT::Smem sm;
+  constexpr int32_t kTQ = TT::kTQ;
+  const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t n_gk = (a.n_global + kTQ - 1) / kTQ;
+  const int32_t bh = (int32_t)blockIdx.x / n_gk, gk = (int32_t)blockIdx.x % n_gk;
+  const int32_t N = a.N;
+  const size_t head_elems = (size_t)N * kD;
+  const int32_t kcount = min(kTQ, a.n_global - gk * kTQ);
+  const int32_t* kidx = a.gidx + gk * kTQ;
+  const int32_t j_min = kidx[0], j_max = kidx[kcount - 1];
+  const int32_t ki = TT::qrow(wave, lane, 0);
+  const int32_t kpos = kidx[min(ki, kcount - 1)];
+  const bool dead = TT::kQW * wave >= kcount;
+  const bool sep = a.sep != 0;
+  DkvWave w;
+  load_frag(w.kf, static_cast<const bf16*>(a.k) + bh * head_elems, kpos, lane);
+  load_frag(w.vf, static_cast<const bf16*>(a.v) + bh * head_elems, kpos, lane);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    w.dk[x] = f32x16{};
+    w.dv[x] = f32x16{};
+  }
+  const float* lse = a.lse + (size_t)bh * N;
+  const float* delta = a.delta + (size_t)bh * N;
+  const bf16* dob = static_cast<const bf16*>(a.dout) + bh * head_elems;
+  // every row position (causal: from the first key on); with separate
+  // projections the global rows are left to the second sweep
+  const int32_t r0 = a.causal ? j_min : 0;
+  const int32_t n_tiles = (N - r0 + kTK - 1) / kTK;
+  GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
+  if (sep) {
+    if (N - r0 <= 32 * kGMaskWords) {
+      build_gmask<bf16>(sm, a.gidx, a.n_global, r0, 1, N - r0, tid);
+      gi.mode = kGlobBitmap;
+    } else {
+      gi.mode = kGlobSearch;
+    }
+  }
+  auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+    const int32_t u0 = r0 + n * kTK;
+    const int32_t cnt = min(kTK, N - u0);
+    kt = {nullptr, u0, 1, cnt, u0 - r0, gi.mode};
+    // row position u0 + kr >= kpos when causal
+    const bool full = cnt == kTK && (!a.causal || u0 >= j_max);
+    mr = {kRange, full ? 0 : 1, 1, -u0, a.causal ? 0 : -kFar, kFar, 0, 0, 1};
+  };
+  const bf16* qs = static_cast<const bf16*>(a.q) + bh * head_elems;
+  if (sep)
+    stream_rows<false>(sm, qs, dob, lse, delta, n_tiles, desc, gi,
+                       [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                         constexpr int32_t buf = decltype(buf_tag)::value;
+                         dkv_tile<buf, true, false>(sm, w, lane, mr, kt, ki, kpos, dead,
+                                                    a.scale_log2, a.causal);
+                       });
+  else
+    stream_rows<false>(sm, qs, dob, lse, delta, n_tiles, desc, gi,
+                       [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                         constexpr int32_t buf = decltype(buf_tag)::value;
+                         dkv_tile<buf, false, false>(sm, w, lane, mr, kt, ki, kpos, dead,
+                                                     a.scale_log2, a.causal);
+                       });
+  const size_t ro = ((size_t)bh * N + kpos) * kD;
+  if (ki < kcount) {
+    store_rows_f32(a.dk + ro, w.dk, a.scale, lane);
+    store_rows_f32(a.dv + ro, w.dv, 1.f, lane);
+  }
+  if (!sep) return;
+  // separate projections: the global rows through qg_i, kg_j, vg_j
+  load_frag(w.kf, static_cast<const bf16*>(a.kg) + bh * head_elems, kpos, lane);
+  load_frag(w.vf, static_cast<const bf16*>(a.vg) + bh * head_elems, kpos, lane);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    w.dk[x] = f32x16{};
+    w.dv[x] = f32x16{};
+  }
+  const int32_t n_gt = (a.n_global + kTK - 1) / kTK;
+  auto glob_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
+    const int32_t cnt = min(kTK, a.n_global - n * kTK);
+    kt = {a.gidx + n * kTK, 0, 1, cnt, 0, kGlobNone};
+    mr = {kRange, cnt == kTK ? 0 : 1, 0, 0, -kFar, kFar, 0, 0, 1};
+  };
+  const GlobInfo gall = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
+  stream_rows<true>(sm, static_cast<const bf16*>(a.qg) + bh * head_elems, dob, lse, delta, n_gt,
+                    glob_desc, gall, [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                      constexpr int32_t buf = decltype(buf_tag)::value;
+                      dkv_tile<buf, false, true>(sm, w, lane, mr, kt, ki, kpos, dead,
+                                                 a.scale_log2, a.causal);
+                    });
+  if (ki < kcount) {
+    store_rows_f32(a.dkg + ro, w.dk, a.scale, lane);
+    store_rows_f32(a.dvg + ro, w.dv, 1.f, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // LongNet mixture (bf16). The mixture is one softmax over the multiset of the
 // patterns' keys (LongNet page, §3.4 "Mixture of Dilated Attentions"), so with
 // the mixture's lse each pattern contributes its own pairs' terms and a pair
@@ -828,6 +985,16 @@ hipError_t launch_dkv_mfma(const BwdArgs& a, hipStream_t stream) {
   if (a.n_band_wg <= 0) return hipSuccess;
   const int64_t grid = (int64_t)kXcds * ((a.n_band_wg + kXcds - 1) / kXcds);
   hipLaunchKernelGGL(bwd_dkv_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_glob_mfma(const BwdArgs& a, hipStream_t stream) {
+  if (a.n_global <= 0) return hipSuccess;
+  const int64_t grid = (int64_t)a.B * a.H * ((a.n_global + TT::kTQ - 1) / TT::kTQ);
+  hipLaunchKernelGGL(bwd_dq_glob_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0, stream,
+                     a);
+  hipLaunchKernelGGL(bwd_dkv_glob_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

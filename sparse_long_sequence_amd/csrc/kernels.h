@@ -105,12 +105,10 @@ struct BwdArgs {
   int32_t n_global, B, H, N, radius, causal, sep;
   int32_t dil[kMaxHeadsDil];
   float scale;
-  // MFMA dQ (bf16 without tables, labels or segment ids): the forward's band
-  // query tiles; the scalar dQ kernel then runs over the global rows only
+  // MFMA backward (bf16 without tables, labels or segment ids): the forward's
+  // residue-class tiles (of query rows for dQ, of keys for dK, dV)
   float scale_log2;
   int32_t band_tiles_per_head, n_band_wg;
-  int32_t dq_global_rows;   // the scalar dQ kernel over the global rows only
-  int32_t dkv_global_keys;  // the scalar dK/dV kernel over the global keys only
   // LongNet mixture (launch_dilated_bwd only): patterns (w, r)
   int32_t n_pairs;
   int32_t pw[kMaxPairs], pr[kMaxPairs];
@@ -120,6 +118,7 @@ hipError_t launch_attn(const AttnArgs& a, int32_t dtype, hipStream_t stream);
 hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream);
 hipError_t launch_dq_mfma(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dkv_mfma(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_glob_mfma(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dilated_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dilated_bwd_mfma(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dilated(const DilArgs& a, hipStream_t stream);
