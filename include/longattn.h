@@ -258,11 +258,13 @@ typedef struct {
  *               required).
  *  dout         device [B,H,N,D] in q's dtype: the loss gradient w.r.t. out.
  *  dq, dk, dv   device fp32 [B,H,N,D] outputs; must not alias any input.
- * Requires ext->workspace (fully overwritten). Pointers 16-byte aligned. Errors
- * as for la_attn_forward. Three to six launches on `stream` (bf16 without
- * tables, labels or segment ids: global ranks, D_i, MFMA dQ and dK/dV of the
- * non-global rows and keys, then the global rows' and keys' own kernels), no
- * allocation. */
+ * Requires ext->workspace (its contents on entry are ignored). Pointers 16-byte
+ * aligned. Errors as for la_attn_forward. Three to seven launches on `stream`
+ * (bf16 without tables, labels or segment ids: global ranks, D_i, MFMA dQ and
+ * dK/dV of the non-global rows and keys, then the global rows' and keys' own
+ * kernels over up to 16 key or row ranges each and, with several ranges, one
+ * launch adding the ranges' partial sums in a fixed order), no allocation;
+ * results are bitwise reproducible. */
 la_status la_attn_backward(const la_dims *dims, const void *q, const void *k, const void *v,
                            const int32_t *global_idx, int32_t n_global, int32_t radius,
                            const int32_t *dilation, int32_t causal, const void *out,
@@ -270,8 +272,9 @@ la_status la_attn_backward(const la_dims *dims, const void *q, const void *k, co
                            hipStream_t stream, const la_attn_bwd_ext *ext);
 
 /* Bytes of workspace la_attn_backward needs (0 for invalid dims): fp32 D_i per
- * row and each position's int32 rank in global_idx, each part padded to 256
- * bytes. */
+ * row, each position's int32 rank in global_idx and, for bf16, fp32 partial
+ * sums of dQ, dK and dV for min(N rounded up to 128, 2048) rows per head; each
+ * part padded to 256 bytes. */
 size_t la_attn_backward_workspace_size(const la_dims *dims);
 
 /* Backward of la_dilated_forward (bf16 only). The mixture is one softmax over

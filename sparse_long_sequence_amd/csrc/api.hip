@@ -435,11 +435,19 @@ la_status la_fixed_forward(const la_dims* dims, const void* q, const void* k, co
   return LA_OK;
 }
 
+// The partial sums of the split global-row and global-key passes (bf16):
+// dQ, dK and dV for host_glob_part_rows(N) rows per head.
+static size_t bwd_part_bytes(const la_dims* dims) {
+  if (dims->dtype != LA_BF16) return 0;
+  return align_up((size_t)3 * dims->B * dims->H * la::host_glob_part_rows(dims->N) * kDHead *
+                  sizeof(float));
+}
+
 size_t la_attn_backward_workspace_size(const la_dims* dims) {
   if (check_dims(dims, false) != LA_OK) return 0;
-  // D_i per row, then each position's global rank
+  // D_i per row, each position's global rank, then the partial sums
   return align_up((size_t)dims->B * dims->H * dims->N * sizeof(float)) +
-         align_up((size_t)dims->N * sizeof(int32_t));
+         align_up((size_t)dims->N * sizeof(int32_t)) + bwd_part_bytes(dims);
 }
 
 la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, const void* v,
@@ -538,6 +546,7 @@ la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, co
   a.sep = sep_in ? 1 : 0;
   a.scale = (float)(1.0 / sqrt((double)kDHead));
   a.scale_log2 = (float)(1.0 / sqrt((double)kDHead) * 1.4426950408889634);
+  a.glob_chunks = 1;
   // the MFMA dQ path: bf16 without bias tables, labels or segment ids
   if (dims->dtype == LA_BF16 && !a.rel_bias && !a.rel_vec && !a.glabel && !a.llabel && !a.seg) {
     const int32_t tq = la::host_query_tile(dims->dtype);
@@ -548,6 +557,9 @@ la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, co
     const int64_t band_wg = (int64_t)dims->B * dims->H * tiles;
     if (band_wg > 0x7fffffffLL) return fail(LA_EUNSUPPORTED, "launch grid too large");
     a.n_band_wg = (int32_t)band_wg;
+    a.glob_chunks = la::host_glob_chunks((int64_t)dims->B * dims->H, dims->N, n_global);
+    a.gpart = reinterpret_cast<float*>(reinterpret_cast<char*>(a.grank) +
+                                       align_up((size_t)dims->N * sizeof(int32_t)));
   }
   hipError_t e = la::launch_attn_bwd(a, dims->dtype, stream);
   if (e != hipSuccess) return fail(LA_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(e));

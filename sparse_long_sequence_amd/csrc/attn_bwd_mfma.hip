@@ -647,8 +647,26 @@ void bwd_dq_mfma_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // The global rows' dQ and the global keys' dK, dV: a global row reaches every
 // key and a global key every row, so a workgroup owns a tile of global rows
-// (or keys) and streams every key (or row) position in order.
+// (or keys) and streams one of glob_chunks consecutive ranges of the key (or
+// row) tiles. With several ranges each writes its unscaled sums to its own
+// partial rows and bwd_glob_reduce_kernel adds them in range order.
 // ---------------------------------------------------------------------------
+
+// This workgroup's range of n_all tiles: [t0, t0 + count).
+__device__ __forceinline__ void chunk_range(int32_t n_all, int32_t chunks, int32_t c,
+                                            int32_t& t0, int32_t& count) {
+  const int32_t per = (n_all + chunks - 1) / chunks;
+  t0 = min(n_all, c * per);
+  count = min(n_all, t0 + per) - t0;
+}
+
+// Partial-sum row g (global index) of range c for part 0 (dQ), 1 (dK), 2 (dV).
+__device__ __forceinline__ float* part_row(const BwdArgs& a, int32_t part, int32_t c, int32_t bh,
+                                           int32_t g) {
+  const int32_t n_gpad = (a.n_global + TT::kTQ - 1) / TT::kTQ * TT::kTQ;
+  const size_t bhs = (size_t)a.B * a.H;
+  return a.gpart + ((((size_t)part * a.glob_chunks + c) * bhs + bh) * n_gpad + g) * kD;
+}
 
 __global__ __launch_bounds__(TT::kThreads)
 __attribute__((amdgpu_waves_per_eu(3)))
@@ -657,7 +675,9 @@ void bwd_dq_glob_mfma_kernel(BwdArgs a) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t n_gq = (a.n_global + kTQ - 1) / kTQ;
-  const int32_t bh = (int32_t)blockIdx.x / n_gq, gq = (int32_t)blockIdx.x % n_gq;
+  const int32_t chunks = a.glob_chunks, c = (int32_t)blockIdx.x % chunks;
+  const int32_t unit = (int32_t)blockIdx.x / chunks;
+  const int32_t bh = unit / n_gq, gq = unit % n_gq;
   const int32_t N = a.N;
   const size_t head_elems = (size_t)N * kD;
   const int32_t qcount = min(kTQ, a.n_global - gq * kTQ);
@@ -676,9 +696,10 @@ void bwd_dq_glob_mfma_kernel(BwdArgs a) {
   w.acc[0] = f32x16{};
   w.acc[1] = f32x16{};
   const int32_t j1 = a.causal ? i_max + 1 : N;
-  const int32_t n_tiles = (j1 + kTK - 1) / kTK;
+  int32_t t0, n_tiles;
+  chunk_range((j1 + kTK - 1) / kTK, chunks, c, t0, n_tiles);
   auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
-    const int32_t u0 = n * kTK;
+    const int32_t u0 = (t0 + n) * kTK;
     const int32_t kcount = min(kTK, j1 - u0);
     kt = {nullptr, u0, 1, kcount, 0, kGlobNone};
     // key position u0 + kj <= qpos when causal
@@ -692,7 +713,9 @@ void bwd_dq_glob_mfma_kernel(BwdArgs a) {
                         constexpr int32_t buf = decltype(buf_tag)::value;
                         dq_tile<buf>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2);
                       });
-  if (qi < qcount) {
+  if (qi < qcount && chunks > 1) {
+    store_rows_f32(part_row(a, 0, c, bh, gq * kTQ + qi), w.acc, 1.f, lane);
+  } else if (qi < qcount) {
     const size_t ro = ((size_t)bh * N + qpos) * kD;
     store_rows_f32((sep ? a.dqg : a.dq) + ro, w.acc, a.scale, lane);
     if (sep) {  // a global row's shared-projection gradient is 0
@@ -709,7 +732,9 @@ void bwd_dkv_glob_mfma_kernel(BwdArgs a) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t n_gk = (a.n_global + kTQ - 1) / kTQ;
-  const int32_t bh = (int32_t)blockIdx.x / n_gk, gk = (int32_t)blockIdx.x % n_gk;
+  const int32_t chunks = a.glob_chunks, c = (int32_t)blockIdx.x % chunks;
+  const int32_t unit = (int32_t)blockIdx.x / chunks;
+  const int32_t bh = unit / n_gk, gk = unit % n_gk;
   const int32_t N = a.N;
   const size_t head_elems = (size_t)N * kD;
   const int32_t kcount = min(kTQ, a.n_global - gk * kTQ);
@@ -730,23 +755,25 @@ void bwd_dkv_glob_mfma_kernel(BwdArgs a) {
   const float* lse = a.lse + (size_t)bh * N;
   const float* delta = a.delta + (size_t)bh * N;
   const bf16* dob = static_cast<const bf16*>(a.dout) + bh * head_elems;
-  // every row position (causal: from the first key on); with separate
-  // projections the global rows are left to the second sweep
+  // this range of the row positions (causal: from the first key on); with
+  // separate projections the global rows are left to the second sweep
   const int32_t r0 = a.causal ? j_min : 0;
-  const int32_t n_tiles = (N - r0 + kTK - 1) / kTK;
+  int32_t t0, n_tiles;
+  chunk_range((N - r0 + kTK - 1) / kTK, chunks, c, t0, n_tiles);
+  const int32_t ub = r0 + t0 * kTK, ue = min(N, ub + n_tiles * kTK);
   GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
-  if (sep) {
-    if (N - r0 <= 32 * kGMaskWords) {
-      build_gmask<bf16>(sm, a.gidx, a.n_global, r0, 1, N - r0, tid);
+  if (sep && n_tiles > 0) {
+    if (ue - ub <= 32 * kGMaskWords) {
+      build_gmask<bf16>(sm, a.gidx, a.n_global, ub, 1, ue - ub, tid);
       gi.mode = kGlobBitmap;
     } else {
       gi.mode = kGlobSearch;
     }
   }
   auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
-    const int32_t u0 = r0 + n * kTK;
+    const int32_t u0 = ub + n * kTK;
     const int32_t cnt = min(kTK, N - u0);
-    kt = {nullptr, u0, 1, cnt, u0 - r0, gi.mode};
+    kt = {nullptr, u0, 1, cnt, u0 - ub, gi.mode};
     // row position u0 + kr >= kpos when causal
     const bool full = cnt == kTK && (!a.causal || u0 >= j_max);
     mr = {kRange, full ? 0 : 1, 1, -u0, a.causal ? 0 : -kFar, kFar, 0, 0, 1};
@@ -767,11 +794,15 @@ void bwd_dkv_glob_mfma_kernel(BwdArgs a) {
                                                      a.scale_log2, a.causal);
                        });
   const size_t ro = ((size_t)bh * N + kpos) * kD;
-  if (ki < kcount) {
+  if (ki < kcount && chunks > 1) {
+    store_rows_f32(part_row(a, 1, c, bh, gk * kTQ + ki), w.dk, 1.f, lane);
+    store_rows_f32(part_row(a, 2, c, bh, gk * kTQ + ki), w.dv, 1.f, lane);
+  } else if (ki < kcount) {
     store_rows_f32(a.dk + ro, w.dk, a.scale, lane);
     store_rows_f32(a.dv + ro, w.dv, 1.f, lane);
   }
-  if (!sep) return;
+  // separate projections: the last range also sweeps the global rows
+  if (!sep || c != chunks - 1) return;
   // separate projections: the global rows through qg_i, kg_j, vg_j
   load_frag(w.kf, static_cast<const bf16*>(a.kg) + bh * head_elems, kpos, lane);
   load_frag(w.vf, static_cast<const bf16*>(a.vg) + bh * head_elems, kpos, lane);
@@ -943,6 +974,31 @@ void bwd_dkv_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles)
   }
 }
 
+// The global rows' dQ and the global keys' dK, dV from the ranges' partial
+// sums, added in range order; with separate projections a global row's dq is 0.
+// One thread per 4 columns of a global row.
+__global__ __launch_bounds__(256) void bwd_glob_reduce_kernel(BwdArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t bhs = (int64_t)a.B * a.H;
+  if (t >= bhs * a.n_global * (kD / 4)) return;
+  const int32_t d4 = (int32_t)(t % (kD / 4));
+  const int64_t r = t / (kD / 4);
+  const int32_t g = (int32_t)(r % a.n_global), bh = (int32_t)(r / a.n_global);
+  f32x4 s[3];
+#pragma unroll
+  for (int x = 0; x < 3; ++x) s[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int32_t c = 0; c < a.glob_chunks; ++c) {
+#pragma unroll
+    for (int x = 0; x < 3; ++x) s[x] += reinterpret_cast<const f32x4*>(part_row(a, x, c, bh, g))[d4];
+  }
+  const size_t ro = ((size_t)bh * a.N + a.gidx[g]) * kD;
+  f32x4* dq = reinterpret_cast<f32x4*>((a.sep ? a.dqg : a.dq) + ro);
+  dq[d4] = s[0] * a.scale;
+  if (a.sep) reinterpret_cast<f32x4*>(a.dq + ro)[d4] = f32x4{0.f, 0.f, 0.f, 0.f};
+  reinterpret_cast<f32x4*>(a.dk + ro)[d4] = s[1] * a.scale;
+  reinterpret_cast<f32x4*>(a.dv + ro)[d4] = s[2];
+}
+
 // zeros into three fp32 buffers of n4 float4 each (a kernel: no memset)
 __global__ __launch_bounds__(256) void bwd_zero3_kernel(float* x, float* y, float* z, int64_t n4) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -990,12 +1046,43 @@ hipError_t launch_dkv_mfma(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_glob_mfma(const BwdArgs& a, hipStream_t stream) {
   if (a.n_global <= 0) return hipSuccess;
-  const int64_t grid = (int64_t)a.B * a.H * ((a.n_global + TT::kTQ - 1) / TT::kTQ);
+  if (a.glob_chunks < 1 || (a.glob_chunks > 1 && !a.gpart)) return hipErrorInvalidValue;
+  const int64_t grid =
+      (int64_t)a.B * a.H * ((a.n_global + TT::kTQ - 1) / TT::kTQ) * a.glob_chunks;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_dq_glob_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0, stream,
                      a);
   hipLaunchKernelGGL(bwd_dkv_glob_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
                      stream, a);
+  if (a.glob_chunks > 1) {
+    const int64_t threads = (int64_t)a.B * a.H * a.n_global * (kD / 4);
+    hipLaunchKernelGGL(bwd_glob_reduce_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256),
+                       0, stream, a);
+  }
   return hipGetLastError();
+}
+
+// Partial-sum rows per head that the workspace holds: the padded sequence up
+// to 2048 (the ranges share them: chunks * n_gpad <= this).
+int32_t host_glob_part_rows(int32_t N) {
+  const int32_t padded = (N + TT::kTQ - 1) / TT::kTQ * TT::kTQ;
+  return padded < 2048 ? padded : 2048;
+}
+
+// Ranges per global tile: enough workgroups to fill the chip twice over
+// (about 512), at most 16, at least 4 tiles of 64 per range, and within the
+// workspace's partial rows.
+int32_t host_glob_chunks(int64_t bh, int32_t N, int32_t n_global) {
+  if (n_global <= 0 || bh <= 0) return 1;
+  const int32_t n_gpad = (n_global + TT::kTQ - 1) / TT::kTQ * TT::kTQ;
+  const int64_t units = bh * (n_gpad / TT::kTQ);
+  int64_t c = (512 + units - 1) / units;
+  c = c < 16 ? c : 16;
+  const int64_t by_rows = host_glob_part_rows(N) / n_gpad;
+  c = c < by_rows ? c : by_rows;
+  const int64_t by_len = (N + 4 * kTK - 1) / (4 * kTK);
+  c = c < by_len ? c : by_len;
+  return c > 1 ? (int32_t)c : 1;
 }
 
 }  // namespace la

@@ -109,6 +109,12 @@ struct BwdArgs {
   // residue-class tiles (of query rows for dQ, of keys for dK, dV)
   float scale_log2;
   int32_t band_tiles_per_head, n_band_wg;
+  // the global rows' dQ and the global keys' dK, dV split over glob_chunks
+  // key (row) ranges: fp32 partial sums [3][glob_chunks][B*H][n_gpad][D] in
+  // the workspace (n_gpad: n_global rounded up to the query tile), added in
+  // chunk order by a reduce launch; glob_chunks == 1 writes directly
+  float* gpart;
+  int32_t glob_chunks;
   // LongNet mixture (launch_dilated_bwd only): patterns (w, r)
   int32_t n_pairs;
   int32_t pw[kMaxPairs], pr[kMaxPairs];
@@ -123,6 +129,8 @@ hipError_t launch_dilated_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dilated_bwd_mfma(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dilated(const DilArgs& a, hipStream_t stream);
 int32_t host_band_tiles_of_head(int32_t N, int32_t d, int32_t tq);
+int32_t host_glob_part_rows(int32_t N);  // partial-sum rows per head in the workspace
+int32_t host_glob_chunks(int64_t bh, int32_t N, int32_t n_global);
 int32_t host_query_tile(int32_t dtype);  // query rows per workgroup
 constexpr int32_t kDilatedQueryTile = 128;  // bf16 workgroup rows of the LongNet kernel
 

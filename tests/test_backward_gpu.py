@@ -105,6 +105,10 @@ CASES = [
     ("f32-separate", "f32", 1, 1, 130, (7, 64), 5, [2], False, True, None),
     ("dense-window", "bf16", 1, 2, 96, (), 96, None, False, False, None),
     ("no-window", "bf16", 1, 1, 128, (10, 11), 0, None, False, False, None),
+    # six key (row) ranges for the global tiles; causal with late globals leaves
+    # the last dK/dV range without rows (it still sweeps the global rows)
+    ("ranges-causal", "bf16", 1, 2, 1500, (900, 1000, 1400), 32, [1, 2], True, True, None),
+    ("ranges-shared", "bf16", 2, 1, 1100, tuple(range(0, 1100, 7)), 24, None, False, False, None),
 ]
 
 
@@ -119,6 +123,13 @@ def test_backward_deterministic(dev):
     """Two calls give bitwise equal gradients (no atomics, fixed order)."""
     a = run_case(dev, "det-1", "bf16", 1, 2, 200, (0, 50), 10, None, False, True, None, seed=7)
     b = run_case(dev, "det-2", "bf16", 1, 2, 200, (0, 50), 10, None, False, True, None, seed=7)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    # global tiles split over key (row) ranges whose partial sums are added
+    a = run_case(dev, "det-3", "bf16", 1, 2, 1300, (0, 50, 1299), 10, None, False, True, None,
+                 seed=8)
+    b = run_case(dev, "det-4", "bf16", 1, 2, 1300, (0, 50, 1299), 10, None, False, True, None,
+                 seed=8)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 
