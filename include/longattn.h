@@ -287,9 +287,11 @@ size_t la_attn_backward_workspace_size(const la_dims *dims);
  *  dout         device bf16 [B,H,N,D]: the loss gradient w.r.t. out.
  *  dq, dk, dv   device fp32 [B,H,N,D] outputs (fully written; must not alias inputs).
  *  workspace    la_dilated_backward_workspace_size() bytes, 256-byte aligned.
- * Errors as for la_dilated_forward. 2 + 2 * n_pairs launches on `stream` (D_i,
- * zeroed gradients, then each pattern's dQ and dK/dV terms added in pattern
- * order: deterministic), no allocation. */
+ * Errors as for la_dilated_forward. 1 + 2 * n_pairs launches on `stream` (D_i,
+ * then each pattern's dQ and dK/dV terms: a pattern of dilation 1, which keeps
+ * every row and key, stores its terms first and the others add theirs in
+ * pattern order; without one a zeroing launch comes first and every pattern
+ * adds: deterministic), no allocation. */
 la_status la_dilated_backward(const la_dims *dims, const void *q, const void *k, const void *v,
                               const int32_t *seg_lens, const int32_t *dil_rates, int32_t n_pairs,
                               int32_t causal, const void *out, const float *lse,

@@ -20,9 +20,10 @@
 // dV_j in one store. These are the scalar kernels: fp32 VALU work, no MFMA.
 // The fp32 path keeps one lane per vector element (dot products as wave
 // sums); the bf16 path (below) puts one key or row on each lane instead. They
-// serve fp32 calls, calls with bias tables, labels or segment ids, and (bf16)
-// the global rows' dQ and the global keys' dK, dV; everything else runs on
-// the MFMA tile engine (attn_bwd_mfma.hip), the LongNet mixture included.
+// serve fp32 calls and calls with bias tables, labels or segment ids; bf16
+// calls without them run on the MFMA tile engine (attn_bwd_mfma.hip) after
+// one launch here that writes D_i and the global ranks, the LongNet mixture
+// included.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -108,16 +109,31 @@ __device__ __forceinline__ float label_bias(const BwdArgs& a, int32_t h, int32_t
 
 constexpr int kBatch = 8;  // pairs whose loads and reductions are issued together
 
-// D_i = dO_i . O_i of every row (one wave per row), for the MFMA dQ path.
-template <typename T>
-__global__ __launch_bounds__(64 * kWavesBwd) void bwd_delta_kernel(BwdArgs a) {
-  const int32_t lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kWavesBwd + (threadIdx.x >> 6);
-  if (row >= (int64_t)a.B * a.H * a.N) return;
-  const size_t o = (size_t)row * kD + lane;
-  const float Di = wave_sum(load_el(static_cast<const T*>(a.dout) + o) *
-                            load_el(static_cast<const T*>(a.out) + o));
-  if (lane == 0) a.delta[row] = Di;
+// For the MFMA path (bf16): D_i = dO_i . O_i of every row, eight lanes per row
+// with one 16-byte load each from dO and O, in the first delta_blocks
+// workgroups (32 rows each); each position's global rank in the ones after.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int32_t delta_blocks) {
+  if ((int32_t)blockIdx.x >= delta_blocks) {
+    const int32_t p = ((int32_t)blockIdx.x - delta_blocks) * 256 + (int32_t)threadIdx.x;
+    if (p < a.N) a.grank[p] = a.n_global > 0 ? sorted_index(a.gidx, a.n_global, p) : -1;
+    return;
+  }
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int32_t part = threadIdx.x & 7;
+  const bool live = row < (int64_t)a.B * a.H * a.N;
+  float x = 0.f;
+  if (live) {
+    const size_t o = (size_t)row * kD + 8 * part;
+    const bf16x8 d = __builtin_bit_cast(bf16x8, ldg16(static_cast<const bf16*>(a.dout) + o));
+    const bf16x8 y = __builtin_bit_cast(bf16x8, ldg16(static_cast<const bf16*>(a.out) + o));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x += (float)d[e] * (float)y[e];
+  }
+  // sum over the row's eight lanes: partners l^1, l^2, then the other quad
+  x += dpp_partner<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_partner<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_partner<0x141>(x);  // row_half_mirror
+  if (live && part == 0) a.delta[row] = x;
 }
 
 // Row i's gradient dQ_i (query-centric), and D_i into the workspace.
@@ -580,17 +596,20 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) 
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   if (rows <= 0) return hipSuccess;
   const dim3 g((uint32_t)((rows + kWavesBwd - 1) / kWavesBwd)), blk(64 * kWavesBwd);
-  hipLaunchKernelGGL(bwd_flags_kernel, dim3((uint32_t)((a.N + 255) / 256)), dim3(256), 0, stream, a);
   if (dtype == 1 && a.n_band_wg > 0) {
-    // dQ of the non-global rows on MFMA, of the global rows per row
-    hipLaunchKernelGGL(bwd_delta_kernel<bf16>, g, blk, 0, stream, a);
+    // D_i and the global ranks, then dQ, dK, dV on MFMA
+    const int32_t db = (int32_t)((rows + 31) / 32), fb = (a.N + 255) / 256;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((uint32_t)(db + fb)), dim3(256), 0, stream, a, db);
     hipError_t e = launch_dq_mfma(a, stream);
     if (e != hipSuccess) return e;
     e = launch_dkv_mfma(a, stream);
     if (e != hipSuccess) return e;
     e = launch_glob_mfma(a, stream);  // the global rows' dQ, the global keys' dK, dV
     if (e != hipSuccess) return e;
-  } else if (dtype == 1) {
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(bwd_flags_kernel, dim3((uint32_t)((a.N + 255) / 256)), dim3(256), 0, stream, a);
+  if (dtype == 1) {
     hipLaunchKernelGGL(bwd_dq_rows_kernel, g, blk, 0, stream, a);
     hipLaunchKernelGGL(bwd_dkv_rows_kernel, g, blk, 0, stream, a);
   } else {
@@ -603,9 +622,9 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) 
 hipError_t launch_dilated_bwd(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   if (rows <= 0) return hipSuccess;
-  const dim3 g((uint32_t)((rows + kWavesBwd - 1) / kWavesBwd)), blk(64 * kWavesBwd);
   // D_i per row, then each pattern's terms on the MFMA tile engine
-  hipLaunchKernelGGL(bwd_delta_kernel<bf16>, g, blk, 0, stream, a);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((uint32_t)((rows + 31) / 32)), dim3(256), 0, stream, a,
+                     (int32_t)((rows + 31) / 32));
   return launch_dilated_bwd_mfma(a, stream);
 }
 

@@ -835,9 +835,11 @@ void bwd_dkv_glob_mfma_kernel(BwdArgs a) {
 // patterns' keys (LongNet page, §3.4 "Mixture of Dilated Attentions"), so with
 // the mixture's lse each pattern contributes its own pairs' terms and a pair
 // kept by several patterns adds once per pattern. One launch per pattern and
-// gradient adds that pattern's terms into dQ (or dK, dV), in pattern order:
-// every kept row (or key) belongs to one workgroup of a launch, so the sums
-// are deterministic; rows no pattern keeps keep the zeros written first.
+// gradient adds that pattern's terms into dQ (or dK, dV): every kept row (or
+// key) belongs to one workgroup of a launch, so the sums are deterministic. A
+// pattern of dilation 1 keeps every row and key: when there is one it goes
+// first and stores its terms; otherwise zeros are written first (rows no
+// pattern keeps keep them).
 // ---------------------------------------------------------------------------
 
 // The pattern's segment geometry for head h (as the forward's dilated_tile):
@@ -883,7 +885,8 @@ __device__ __forceinline__ void add_rows_f32(float* dst, const f32x16 (&acc)[2],
 
 __global__ __launch_bounds__(TT::kThreads)
 __attribute__((amdgpu_waves_per_eu(3)))
-void bwd_dq_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles) {
+void bwd_dq_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles,
+                            int32_t store) {
   __shared__ TT::Smem sm;
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -921,12 +924,19 @@ void bwd_dq_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles) 
                         constexpr int32_t buf = decltype(buf_tag)::value;
                         dq_tile<buf>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2);
                       });
-  if (qi < qcount) add_rows_f32(a.dq + ((size_t)bh * a.N + qpos) * kD, w.acc, a.scale, lane);
+  if (qi < qcount) {
+    float* dst = a.dq + ((size_t)bh * a.N + qpos) * kD;
+    if (store)
+      store_rows_f32(dst, w.acc, a.scale, lane);
+    else
+      add_rows_f32(dst, w.acc, a.scale, lane);
+  }
 }
 
 __global__ __launch_bounds__(TT::kThreads)
 __attribute__((amdgpu_waves_per_eu(2)))
-void bwd_dkv_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles) {
+void bwd_dkv_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles,
+                             int32_t store) {
   __shared__ TT::Smem sm;
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -969,8 +979,15 @@ void bwd_dkv_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles)
                                                    a.scale_log2, a.causal);
                      });
   if (ki < kcount) {
-    add_rows_f32(a.dk + ((size_t)bh * a.N + kpos) * kD, w.dk, a.scale, lane);
-    add_rows_f32(a.dv + ((size_t)bh * a.N + kpos) * kD, w.dv, 1.f, lane);
+    float* dk = a.dk + ((size_t)bh * a.N + kpos) * kD;
+    float* dv = a.dv + ((size_t)bh * a.N + kpos) * kD;
+    if (store) {
+      store_rows_f32(dk, w.dk, a.scale, lane);
+      store_rows_f32(dv, w.dv, 1.f, lane);
+    } else {
+      add_rows_f32(dk, w.dk, a.scale, lane);
+      add_rows_f32(dv, w.dv, 1.f, lane);
+    }
   }
 }
 
@@ -1014,18 +1031,25 @@ __global__ __launch_bounds__(256) void bwd_zero3_kernel(float* x, float* y, floa
 hipError_t launch_dilated_bwd_mfma(const BwdArgs& a, hipStream_t stream) {
   const int64_t n4 = (int64_t)a.B * a.H * a.N * kD / 4;
   if (n4 <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_zero3_kernel, dim3((uint32_t)((n4 + 255) / 256)), dim3(256), 0, stream,
-                     a.dq, a.dk, a.dv, n4);
-  for (int32_t k = 0; k < a.n_pairs; ++k) {
+  int32_t first = -1;  // a pattern of dilation 1, launched first and storing
+  for (int32_t k = 0; k < a.n_pairs && first < 0; ++k)
+    if (a.pr[k] == 1) first = k;
+  if (first < 0)
+    hipLaunchKernelGGL(bwd_zero3_kernel, dim3((uint32_t)((n4 + 255) / 256)), dim3(256), 0, stream,
+                       a.dq, a.dk, a.dv, n4);
+  for (int32_t x = 0; x < a.n_pairs; ++x) {
+    // first, then the others in pattern order
+    const int32_t k = first < 0 ? x : (x == 0 ? first : (x <= first ? x - 1 : x));
+    const int32_t store = x == 0 && first >= 0 ? 1 : 0;
     const int32_t nseg = (a.N + a.pw[k] - 1) / a.pw[k];
     const int32_t rows = (a.pw[k] + a.pr[k] - 1) / a.pr[k];
     const int32_t qtiles = (rows + TT::kTQ - 1) / TT::kTQ;
     const int64_t grid = (int64_t)a.B * a.H * nseg * qtiles;
     if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(bwd_dq_dil_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0, stream,
-                       a, k, nseg, qtiles);
+                       a, k, nseg, qtiles, store);
     hipLaunchKernelGGL(bwd_dkv_dil_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
-                       stream, a, k, nseg, qtiles);
+                       stream, a, k, nseg, qtiles, store);
   }
   return hipGetLastError();
 }

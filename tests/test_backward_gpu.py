@@ -264,6 +264,8 @@ LONGNET_CASES = [
     ("n4096", 1, 2, 4096, ((1024, 1), (2048, 2), (4096, 4)), True),
     # no dilation-1 pattern: rows that no pattern covers have lse = -inf and no gradient
     ("no-r1-uncovered", 1, 5, 333, ((64, 2), (128, 3), (333, 5)), True),
+    # the dilation-1 pattern (launched first, storing) is not the first given
+    ("r1-not-first", 1, 3, 700, ((256, 2), (128, 1), (700, 7)), False),
 ]
 
 
