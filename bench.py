@@ -267,7 +267,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_longformer_base_traffic.
 # The sources the band + global forward kernel and its launch geometry are
 # built from, and the build flags: the measured traffic stands while they do.
 TRAFFIC_SOURCES = ("csrc/attn_fwd.hip", "csrc/tile_core.h", "csrc/kernels.h", "csrc/api.hip",
-                   "build.py")
+                   "csrc/entry.h", "build.py")
 
 
 def kernel_sources_digest() -> str:

@@ -27,7 +27,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
-#include "kernels.h"
+#include "bwd_kernels.h"
 #include "tile_core.h"
 
 namespace la {

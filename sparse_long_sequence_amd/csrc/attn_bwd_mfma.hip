@@ -25,7 +25,7 @@
 // reach every key; with separate projections through qg_i, kg_j, vg_j into
 // dKg, dVg).
 #include "tile_core.h"
-#include "kernels.h"
+#include "bwd_kernels.h"
 
 namespace la {
 namespace {

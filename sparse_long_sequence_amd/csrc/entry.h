@@ -2,6 +2,7 @@
 #pragma once
 
 #include <stddef.h>
+#include <stdint.h>
 
 #include "longattn.h"
 
@@ -24,5 +25,15 @@ la_status attn_forward_ws(const la_dims* dims, const void* q, const void* k, con
 
 // Sets the thread's error message; returns s.
 la_status set_error(la_status s, const char* msg);
+
+// dims checks shared by every call (D == 64, dtype, size limits; bf16 only
+// when need_bf16), setting the thread's error message on failure.
+la_status check_dims(const la_dims* d, bool need_bf16);
+
+constexpr int32_t kDHead = 64;  // the one head size built
+constexpr size_t kAlign = 256;  // workspace alignment and part padding
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool is_empty(const la_dims* d) { return d->B == 0 || d->H == 0 || d->N == 0; }
 
 }  // namespace la
