@@ -451,8 +451,14 @@ struct TileTraits<bf16> {
   }
 
   // p = 2^(s * c + nm) rounded to bf16; the row sum adds exactly these values.
+  // The wave runs this exponential stretch at raised issue priority: with
+  // several waves on a SIMD, the one in its VALU phase then issues ahead of
+  // waves that are starting their next MFMAs, which keeps both pipes busier
+  // (the forward's headline shape runs about 4% faster, the unmasked
+  // R = 4096 band about 5%).
   static __device__ __forceinline__ void softmax_p(const float s[kNS], float nm, float c,
                                                    PTile& P, float& l) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -464,6 +470,7 @@ struct TileTraits<bf16> {
         l = add_bf16x2(pk, l);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // O^T += V^T . P^T over sub-tile sb. MFMA step t takes the keys
