@@ -50,14 +50,14 @@ __device__ __forceinline__ void load_frag(bf16x8 (&f)[4], const bf16* base, int3
   for (int st = 0; st < 4; ++st) f[st] = __builtin_bit_cast(bf16x8, ldg16(src + 16 * st));
 }
 
-// s[e] = X[key_const(sb, e) + key_lane] . f for the staged tile X (K or V,
-// [key][d] rows in the engine's swizzled layout): S^T or dP^T of sub-tile sb.
+// s[e] = acc[e] + X[key_const(sb, e) + key_lane] . f for the staged tile X
+// (K or V, [key][d] rows in the engine's swizzled layout): S^T or dP^T of
+// sub-tile sb, accumulated onto acc (zero, or a per-element offset).
 __device__ __forceinline__ void tile_dots(const bf16* tile, const bf16x8 (&f)[4], int32_t lane,
-                                          int sb, float s[TT::kNS]) {
+                                          int sb, float s[TT::kNS], f32x16 acc = {}) {
   const int32_t r = lane & 31, h = lane >> 5;
   const int32_t y = h ^ TT::swz(r);
   const bf16* row = tile + (32 * sb + r) * kD;
-  f32x16 acc = {};
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(row + 8 * ((2 * st) ^ y));
@@ -348,16 +348,17 @@ struct DkvWave {
   f32x16 dv[2];
 };
 
-// A streamed tile's per-row lse (log2 units, +inf for a row without keys) and
-// D_i sit in LDS next to its Q and dO rows (in the key-id and rank arrays,
-// which this pass does not use otherwise).
-__device__ __forceinline__ float* row_lse2(TT::Smem& sm, int32_t buf) {
+// A streamed tile's per-row lse (times lse_mul: 1 / scale gives score units,
+// the raw q.k at which P = 1; log2 e gives log2 units; +inf for a row without
+// keys) and D_i sit in LDS next to its Q and dO rows (in the key-id and rank
+// arrays, which this pass does not use otherwise).
+__device__ __forceinline__ float* row_lse(TT::Smem& sm, int32_t buf) {
   return reinterpret_cast<float*>(&sm.kseg[buf][0]);
 }
 __device__ __forceinline__ float* row_di(TT::Smem& sm, int32_t buf) {
   return reinterpret_cast<float*>(&sm.kgrank[buf][0]);
 }
-__device__ __forceinline__ const float* row_lse2(const TT::Smem& sm, int32_t buf) {
+__device__ __forceinline__ const float* row_lse(const TT::Smem& sm, int32_t buf) {
   return reinterpret_cast<const float*>(&sm.kseg[buf][0]);
 }
 __device__ __forceinline__ const float* row_di(const TT::Smem& sm, int32_t buf) {
@@ -367,7 +368,16 @@ __device__ __forceinline__ const float* row_di(const TT::Smem& sm, int32_t buf) 
 // One streamed tile of query rows into dK^T, dV^T. EXCL_G: rows that are
 // global are excluded (they are taken in the global-row sweep); ROWS_AFTER:
 // (gathered global rows, causal) only rows at or after the lane's key.
-template <int32_t BUF, bool EXCL_G, bool ROWS_AFTER>
+// INIT: the score and dP MFMAs start from the rows' offsets (-lse / scale and
+// -D_i, with the lse staged in score units), so those per-element values take
+// no registers of their own; this lets the band kernel run 3 waves per SIMD.
+// Otherwise (lse staged in log2 units) the offsets are applied after the
+// MFMAs, which keeps the LDS reads off their critical path: the LongNet
+// sweeps, not register-bound, are faster that way.
+// PRIO: the exponential stretch at raised wave issue priority (as in the
+// forward's softmax); it pays in the LongNet sweeps (the (2048, 1) pattern's
+// dK/dV launch runs about 11% faster) and costs about 1% in the band ones.
+template <int32_t BUF, bool EXCL_G, bool ROWS_AFTER, bool INIT, bool PRIO = false>
 __device__ __forceinline__ void dkv_tile(const TT::Smem& sm, DkvWave& w, int32_t lane,
                                          const MaskRule& mr, const KeyTile& kt, int32_t ki,
                                          int32_t kpos, bool dead, float c, bool causal) {
@@ -384,9 +394,23 @@ __device__ __forceinline__ void dkv_tile(const TT::Smem& sm, DkvWave& w, int32_t
   for (int sb = 0; sb < TT::kSub; ++sb) {
     const int32_t cls = dead ? kEmpty : classify<bf16>(mr, kt.count, sb, r0, r1);
     if (cls == kEmpty) continue;
+    const float* ls = row_lse(sm, BUF);
+    const float* dd = row_di(sm, BUF);
     float s[TT::kNS], dp[TT::kNS];
-    tile_dots(&sm.k[BUF][0], w.kf, lane, sb, s);
-    tile_dots(&sm.v[BUF][0], w.vf, lane, sb, dp);
+    if constexpr (INIT) {  // s = q.k - lse / scale, dp = dO.v - D_i
+      f32x16 s0, d0;
+#pragma unroll
+      for (int e = 0; e < TT::kNS; ++e) {
+        const int32_t i = TT::key_const(sb, e) + kl;
+        s0[e] = -ls[i];
+        d0[e] = -dd[i];
+      }
+      tile_dots(&sm.k[BUF][0], w.kf, lane, sb, s, s0);
+      tile_dots(&sm.v[BUF][0], w.vf, lane, sb, dp, d0);
+    } else {  // s = q.k, dp = dO.v
+      tile_dots(&sm.k[BUF][0], w.kf, lane, sb, s);
+      tile_dots(&sm.v[BUF][0], w.vf, lane, sb, dp);
+    }
     if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, ki, kpos, lane);
     if (EXCL_G && any_g) {
 #pragma unroll
@@ -400,21 +424,28 @@ __device__ __forceinline__ void dkv_tile(const TT::Smem& sm, DkvWave& w, int32_t
           s[r] = sm.kpos[BUF][TT::key_const(sb, r) + kl] >= kpos ? s[r] : kNegInf;
       }
     }
-    const float* l2 = row_lse2(sm, BUF);
-    const float* dd = row_di(sm, BUF);
     TT::PTile P, G;
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 8 * t + 2 * i;
-        const int32_t i0 = TT::key_const(sb, e) + kl, i1 = TT::key_const(sb, e + 1) + kl;
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -l2[i0]));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], c, -l2[i1]));
+        float p0, p1;
+        if constexpr (INIT) {
+          p0 = __builtin_amdgcn_exp2f(s[e] * c);
+          p1 = __builtin_amdgcn_exp2f(s[e + 1] * c);
+          G.p[t][i] = pack_bf16x2(p0 * dp[e], p1 * dp[e + 1]);
+        } else {
+          const int32_t i0 = TT::key_const(sb, e) + kl, i1 = TT::key_const(sb, e + 1) + kl;
+          p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -ls[i0]));
+          p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], c, -ls[i1]));
+          G.p[t][i] = pack_bf16x2(p0 * (dp[e] - dd[i0]), p1 * (dp[e + 1] - dd[i1]));
+        }
         P.p[t][i] = pack_bf16x2(p0, p1);
-        G.p[t][i] = pack_bf16x2(p0 * (dp[e] - dd[i0]), p1 * (dp[e + 1] - dd[i1]));
       }
     }
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     acc_transposed<BUF>(&sm.v[0][0], w.dv, lane, sb, P);
     acc_transposed<BUF>(&sm.k[0][0], w.dk, lane, sb, G);
     // one sub-tile's values live at a time (the two interleaved spill)
@@ -423,11 +454,11 @@ __device__ __forceinline__ void dkv_tile(const TT::Smem& sm, DkvWave& w, int32_t
 }
 
 // stream_tiles for query rows: as stream_tiles, and each staged tile's rows'
-// lse (log2 units) and D_i, read with the tile's loads, written to LDS with
-// its staging. GI_MODE: how the rows' global flags are found.
+// lse (times lse_mul) and D_i, read with the tile's loads, written to LDS
+// with its staging.
 template <bool GATHER, typename Desc, typename Proc>
 __device__ __forceinline__ void stream_rows(TT::Smem& sm, const bf16* qb, const bf16* dob,
-                                            const float* lse, const float* delta,
+                                            const float* lse, const float* delta, float lse_mul,
                                             int32_t n_tiles, Desc desc, const GlobInfo& gi,
                                             Proc proc) {
   const int32_t tid = threadIdx.x;
@@ -441,13 +472,13 @@ __device__ __forceinline__ void stream_rows(TT::Smem& sm, const bf16* qb, const 
     if (tid < kTK && t.count > 0) {
       const int32_t p = key_pos<GATHER>(t, min(tid, t.count - 1));
       const float l = lse[p];
-      pl = l == kNegInf ? -kNegInf : l * kLog2e;
+      pl = l == kNegInf ? -kNegInf : l * lse_mul;
       pd = delta[p];
     }
   };
   auto put_rows = [&](int32_t buf) {
     if (tid < kTK) {
-      row_lse2(sm, buf)[tid] = pl;
+      row_lse(sm, buf)[tid] = pl;
       row_di(sm, buf)[tid] = pd;
     }
   };
@@ -572,10 +603,10 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& s
     mr = {kRange, full ? 0 : 1, 0, t0 - u0, lob, R, 0, 0, 1};
   };
   const bf16* qs = static_cast<const bf16*>(a.q) + bh * head_elems;
-  stream_rows<false>(sm, qs, dob, lse, delta, n_band, band_desc, gi,
+  stream_rows<false>(sm, qs, dob, lse, delta, 1.f / a.scale, n_band, band_desc, gi,
                      [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                        constexpr int32_t buf = decltype(buf_tag)::value;
-                       dkv_tile<buf, true, false>(sm, w, lane, mr, kt, ki, kpos, dead,
+                       dkv_tile<buf, true, false, true>(sm, w, lane, mr, kt, ki, kpos, dead,
                                                   a.scale_log2, a.causal);
                      });
   // the global rows reach every key (causal: rows at or after it)
@@ -589,7 +620,7 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& s
   };
   auto glob_proc = [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
     constexpr int32_t buf = decltype(buf_tag)::value;
-    dkv_tile<buf, false, true>(sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal);
+    dkv_tile<buf, false, true, true>(sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal);
   };
   const bool mine = ki < kcount && !qi_is_global(a, ki, kcount, kpos, g_first, g_last, j_lo, j_hi);
   if (a.sep) {
@@ -609,7 +640,7 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& s
   }
   if (ng > 0)
     stream_rows<true>(sm, static_cast<const bf16*>(a.sep ? a.qg : a.q) + bh * head_elems, dob,
-                      lse, delta, n_gt, glob_desc, gall, glob_proc);
+                      lse, delta, 1.f / a.scale, n_gt, glob_desc, gall, glob_proc);
   if (mine) {
     float* const dk = a.sep ? a.dkg : a.dk;
     float* const dv = a.sep ? a.dvg : a.dv;
@@ -619,7 +650,7 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& s
 }
 
 __global__ __launch_bounds__(TT::kThreads)
-__attribute__((amdgpu_waves_per_eu(2)))
+__attribute__((amdgpu_waves_per_eu(3)))
 void bwd_dkv_mfma_kernel(BwdArgs a) {
   __shared__ TT::Smem sm;
   const int32_t x = (int32_t)blockIdx.x % kXcds, j = (int32_t)blockIdx.x / kXcds;
@@ -780,17 +811,17 @@ void bwd_dkv_glob_mfma_kernel(BwdArgs a) {
   };
   const bf16* qs = static_cast<const bf16*>(a.q) + bh * head_elems;
   if (sep)
-    stream_rows<false>(sm, qs, dob, lse, delta, n_tiles, desc, gi,
+    stream_rows<false>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
                        [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                          constexpr int32_t buf = decltype(buf_tag)::value;
-                         dkv_tile<buf, true, false>(sm, w, lane, mr, kt, ki, kpos, dead,
+                         dkv_tile<buf, true, false, true>(sm, w, lane, mr, kt, ki, kpos, dead,
                                                     a.scale_log2, a.causal);
                        });
   else
-    stream_rows<false>(sm, qs, dob, lse, delta, n_tiles, desc, gi,
+    stream_rows<false>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
                        [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                          constexpr int32_t buf = decltype(buf_tag)::value;
-                         dkv_tile<buf, false, false>(sm, w, lane, mr, kt, ki, kpos, dead,
+                         dkv_tile<buf, false, false, true>(sm, w, lane, mr, kt, ki, kpos, dead,
                                                      a.scale_log2, a.causal);
                        });
   const size_t ro = ((size_t)bh * N + kpos) * kD;
@@ -818,10 +849,11 @@ void bwd_dkv_glob_mfma_kernel(BwdArgs a) {
     mr = {kRange, cnt == kTK ? 0 : 1, 0, 0, -kFar, kFar, 0, 0, 1};
   };
   const GlobInfo gall = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
-  stream_rows<true>(sm, static_cast<const bf16*>(a.qg) + bh * head_elems, dob, lse, delta, n_gt,
+  stream_rows<true>(sm, static_cast<const bf16*>(a.qg) + bh * head_elems, dob, lse, delta,
+                    1.f / a.scale, n_gt,
                     glob_desc, gall, [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                       constexpr int32_t buf = decltype(buf_tag)::value;
-                      dkv_tile<buf, false, true>(sm, w, lane, mr, kt, ki, kpos, dead,
+                      dkv_tile<buf, false, true, true>(sm, w, lane, mr, kt, ki, kpos, dead,
                                                  a.scale_log2, a.causal);
                     });
   if (ki < kcount) {
@@ -972,11 +1004,12 @@ void bwd_dkv_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles,
   const GlobInfo gi = {kGlobNone, nullptr, 0, nullptr, 0, 0, 0};
   stream_rows<false>(sm, static_cast<const bf16*>(a.q) + bh * head_elems,
                      static_cast<const bf16*>(a.dout) + bh * head_elems,
-                     a.lse + (size_t)bh * a.N, a.delta + (size_t)bh * a.N, n_tiles, desc, gi,
+                     a.lse + (size_t)bh * a.N, a.delta + (size_t)bh * a.N, kLog2e, n_tiles,
+                     desc, gi,
                      [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                        constexpr int32_t buf = decltype(buf_tag)::value;
-                       dkv_tile<buf, false, false>(sm, w, lane, mr, kt, ki, kpos, dead,
-                                                   a.scale_log2, a.causal);
+                       dkv_tile<buf, false, false, false, true>(sm, w, lane, mr, kt, ki, kpos, dead,
+                                                          a.scale_log2, a.causal);
                      });
   if (ki < kcount) {
     float* dk = a.dk + ((size_t)bh * a.N + kpos) * kD;
