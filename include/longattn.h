@@ -259,11 +259,11 @@ typedef struct {
  *  dout         device [B,H,N,D] in q's dtype: the loss gradient w.r.t. out.
  *  dq, dk, dv   device fp32 [B,H,N,D] outputs; must not alias any input.
  * Requires ext->workspace (its contents on entry are ignored). Pointers 16-byte
- * aligned. Errors as for la_attn_forward. Three to seven launches on `stream`
- * (bf16 without tables, labels or segment ids: global ranks, D_i, MFMA dQ and
- * dK/dV of the non-global rows and keys, then the global rows' and keys' own
- * kernels over up to 16 key or row ranges each and, with several ranges, one
- * launch adding the ranges' partial sums in a fixed order), no allocation;
+ * aligned. Errors as for la_attn_forward. Two or three launches on `stream`
+ * (bf16 without tables, labels or segment ids: one MFMA launch for dQ and D_i,
+ * one for dK and dV, the global rows and keys split over up to 16 key or row
+ * ranges, and with several ranges one launch adding their partial sums in a
+ * fixed order; otherwise global ranks, dQ and D_i, dK and dV), no allocation;
  * results are bitwise reproducible. */
 la_status la_attn_backward(const la_dims *dims, const void *q, const void *k, const void *v,
                            const int32_t *global_idx, int32_t n_global, int32_t radius,
@@ -287,11 +287,11 @@ size_t la_attn_backward_workspace_size(const la_dims *dims);
  *  dout         device bf16 [B,H,N,D]: the loss gradient w.r.t. out.
  *  dq, dk, dv   device fp32 [B,H,N,D] outputs (fully written; must not alias inputs).
  *  workspace    la_dilated_backward_workspace_size() bytes, 256-byte aligned.
- * Errors as for la_dilated_forward. 1 + 2 * n_pairs launches on `stream` (D_i,
- * then each pattern's dQ and dK/dV terms: a pattern of dilation 1, which keeps
- * every row and key, stores its terms first and the others add theirs in
- * pattern order; without one a zeroing launch comes first and every pattern
- * adds: deterministic), no allocation. */
+ * Errors as for la_dilated_forward. 2 * n_pairs launches on `stream` (each
+ * pattern's dQ and dK/dV terms: a pattern of dilation 1, which keeps every row
+ * and key, goes first, computes D_i and stores its terms, and the others add
+ * theirs in pattern order; without one, a D_i and a zeroing launch come first
+ * and every pattern adds: deterministic), no allocation. */
 la_status la_dilated_backward(const la_dims *dims, const void *q, const void *k, const void *v,
                               const int32_t *seg_lens, const int32_t *dil_rates, int32_t n_pairs,
                               int32_t causal, const void *out, const float *lse,

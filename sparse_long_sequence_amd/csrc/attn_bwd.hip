@@ -21,9 +21,9 @@
 // The fp32 path keeps one lane per vector element (dot products as wave
 // sums); the bf16 path (below) puts one key or row on each lane instead. They
 // serve fp32 calls and calls with bias tables, labels or segment ids; bf16
-// calls without them run on the MFMA tile engine (attn_bwd_mfma.hip) after
-// one launch here that writes D_i and the global ranks, the LongNet mixture
-// included.
+// calls without them, and the LongNet mixture, run on the MFMA tile engine
+// (attn_bwd_mfma.hip), whose dQ launches compute D_i (a LongNet call without
+// a pattern of dilation 1 takes it from the launch here first).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -109,15 +109,10 @@ __device__ __forceinline__ float label_bias(const BwdArgs& a, int32_t h, int32_t
 
 constexpr int kBatch = 8;  // pairs whose loads and reductions are issued together
 
-// For the MFMA path (bf16): D_i = dO_i . O_i of every row, eight lanes per row
-// with one 16-byte load each from dO and O, in the first delta_blocks
-// workgroups (32 rows each); each position's global rank in the ones after.
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int32_t delta_blocks) {
-  if ((int32_t)blockIdx.x >= delta_blocks) {
-    const int32_t p = ((int32_t)blockIdx.x - delta_blocks) * 256 + (int32_t)threadIdx.x;
-    if (p < a.N) a.grank[p] = a.n_global > 0 ? sorted_index(a.gidx, a.n_global, p) : -1;
-    return;
-  }
+// D_i = dO_i . O_i of every row for a LongNet call without a pattern of
+// dilation 1 (bf16): eight lanes per row with one 16-byte load each from dO and
+// O (32 rows per workgroup).
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int32_t part = threadIdx.x & 7;
   const bool live = row < (int64_t)a.B * a.H * a.N;
@@ -597,14 +592,13 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) 
   if (rows <= 0) return hipSuccess;
   const dim3 g((uint32_t)((rows + kWavesBwd - 1) / kWavesBwd)), blk(64 * kWavesBwd);
   if (dtype == 1 && a.n_band_wg > 0) {
-    // D_i and the global ranks, then dQ, dK, dV on MFMA
-    const int32_t db = (int32_t)((rows + 31) / 32), fb = (a.N + 255) / 256;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((uint32_t)(db + fb)), dim3(256), 0, stream, a, db);
+    // dQ (its workgroups write D_i of their rows), then dK, dV on MFMA (which
+    // need no global ranks)
     hipError_t e = launch_dq_mfma(a, stream);
     if (e != hipSuccess) return e;
     e = launch_dkv_mfma(a, stream);
     if (e != hipSuccess) return e;
-    e = launch_glob_mfma(a, stream);  // the global rows' dQ, the global keys' dK, dV
+    e = launch_glob_reduce(a, stream);  // the global tiles' partial sums
     if (e != hipSuccess) return e;
     return hipGetLastError();
   }
@@ -622,9 +616,12 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) 
 hipError_t launch_dilated_bwd(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   if (rows <= 0) return hipSuccess;
-  // D_i per row, then each pattern's terms on the MFMA tile engine
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((uint32_t)((rows + 31) / 32)), dim3(256), 0, stream, a,
-                     (int32_t)((rows + 31) / 32));
+  // each pattern's terms on the MFMA tile engine; a pattern of dilation 1
+  // goes first and its dQ launch writes D_i, else D_i comes first here
+  bool r1 = false;
+  for (int32_t k = 0; k < a.n_pairs; ++k) r1 = r1 || a.pr[k] == 1;
+  if (!r1)
+    hipLaunchKernelGGL(bwd_delta_kernel, dim3((uint32_t)((rows + 31) / 32)), dim3(256), 0, stream, a);
   return launch_dilated_bwd_mfma(a, stream);
 }
 

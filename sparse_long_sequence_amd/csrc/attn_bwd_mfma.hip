@@ -50,6 +50,21 @@ __device__ __forceinline__ void load_frag(bf16x8 (&f)[4], const bf16* base, int3
   for (int st = 0; st < 4; ++st) f[st] = __builtin_bit_cast(bf16x8, ldg16(src + 16 * st));
 }
 
+// D_i = dO_i . O_i of this lane's row, given its dO fragment (the row's two
+// lanes hold one half each).
+__device__ __forceinline__ float row_delta(const bf16x8 (&df)[4], const bf16* ob, int32_t pos,
+                                           int32_t lane) {
+  bf16x8 of[4];
+  load_frag(of, ob, pos, lane);
+  float x = 0.f;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x = __builtin_fmaf((float)df[st][e], (float)of[st][e], x);
+  }
+  return xor32_sum(x);
+}
+
 // s[e] = acc[e] + X[key_const(sb, e) + key_lane] . f for the staged tile X
 // (K or V, [key][d] rows in the engine's swizzled layout): S^T or dP^T of
 // sub-tile sb, accumulated onto acc (zero, or a per-element offset).
@@ -233,7 +248,7 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
   load_frag(w.df, dob, qpos, lane);
   const float lse = a.lse[(size_t)bh * N + qpos];
   w.lse2 = lse == kNegInf ? -kNegInf : lse * kLog2e;
-  w.di = a.delta[(size_t)bh * N + qpos];
+  w.di = row_delta(w.df, static_cast<const bf16*>(a.out) + bh * head_elems, qpos, lane);
   w.acc[0] = f32x16{};
   w.acc[1] = f32x16{};
 
@@ -314,11 +329,13 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
     stream_tiles<true>(sm, kb, vb, n_glob, glob_desc, gi, proc);
   }
 
-  // non-global rows: dQ (and, with separate projections, a zero dQ_g row)
+  // non-global rows: dQ (and, with separate projections, a zero dQ_g row),
+  // and D_i for the dK/dV pass
   if (qi < qcount) {
     const bool is_g = g_first <= i_hi && g_last >= i_lo && sorted_contains(a.gidx, ng, qpos);
     if (!is_g) {
       const int32_t hh = lane >> 5;
+      if (hh == 0) a.delta[(size_t)bh * N + qpos] = w.di;
       float* dst = a.dq + ((size_t)bh * N + qpos) * kD;
       float* dsg = a.sep ? a.dqg + ((size_t)bh * N + qpos) * kD : nullptr;
 #pragma unroll
@@ -649,32 +666,6 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& s
   }
 }
 
-__global__ __launch_bounds__(TT::kThreads)
-__attribute__((amdgpu_waves_per_eu(3)))
-void bwd_dkv_mfma_kernel(BwdArgs a) {
-  __shared__ TT::Smem sm;
-  const int32_t x = (int32_t)blockIdx.x % kXcds, j = (int32_t)blockIdx.x / kXcds;
-  const int32_t per = (a.n_band_wg + kXcds - 1) / kXcds;
-  const int32_t bw = x * per + j;
-  if (j >= per || bw >= a.n_band_wg) return;
-  dkv_band_workgroup(a, sm, bw);
-}
-
-// Block b runs on XCD b % 8; each XCD takes a contiguous share of the query
-// tiles (tiles of one head then share K/V in that XCD's L2).
-// Two fragments per row (Q and dO) and two dot products per pair need more
-// registers than the forward: 3 waves per SIMD.
-__global__ __launch_bounds__(TT::kThreads)
-__attribute__((amdgpu_waves_per_eu(3)))
-void bwd_dq_mfma_kernel(BwdArgs a) {
-  __shared__ TT::Smem sm;
-  const int32_t x = (int32_t)blockIdx.x % kXcds, j = (int32_t)blockIdx.x / kXcds;
-  const int32_t per = (a.n_band_wg + kXcds - 1) / kXcds;
-  const int32_t bw = x * per + j;
-  if (j >= per || bw >= a.n_band_wg) return;
-  dq_band_workgroup(a, sm, bw);
-}
-
 // ---------------------------------------------------------------------------
 // The global rows' dQ and the global keys' dK, dV: a global row reaches every
 // key and a global key every row, so a workgroup owns a tile of global rows
@@ -699,15 +690,13 @@ __device__ __forceinline__ float* part_row(const BwdArgs& a, int32_t part, int32
   return a.gpart + ((((size_t)part * a.glob_chunks + c) * bhs + bh) * n_gpad + g) * kD;
 }
 
-__global__ __launch_bounds__(TT::kThreads)
-__attribute__((amdgpu_waves_per_eu(3)))
-void bwd_dq_glob_mfma_kernel(BwdArgs a) {
-  __shared__ TT::Smem sm;
+// Workgroup wg of the B*H*ceil(n_global/128)*glob_chunks global-row ones.
+__device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t wg) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t n_gq = (a.n_global + kTQ - 1) / kTQ;
-  const int32_t chunks = a.glob_chunks, c = (int32_t)blockIdx.x % chunks;
-  const int32_t unit = (int32_t)blockIdx.x / chunks;
+  const int32_t chunks = a.glob_chunks, c = wg % chunks;
+  const int32_t unit = wg / chunks;
   const int32_t bh = unit / n_gq, gq = unit % n_gq;
   const int32_t N = a.N;
   const size_t head_elems = (size_t)N * kD;
@@ -723,7 +712,8 @@ void bwd_dq_glob_mfma_kernel(BwdArgs a) {
   load_frag(w.df, static_cast<const bf16*>(a.dout) + bh * head_elems, qpos, lane);
   const float lse = a.lse[(size_t)bh * N + qpos];
   w.lse2 = lse == kNegInf ? -kNegInf : lse * kLog2e;
-  w.di = a.delta[(size_t)bh * N + qpos];
+  w.di = row_delta(w.df, static_cast<const bf16*>(a.out) + bh * head_elems, qpos, lane);
+  if (c == 0 && qi < qcount && lane < 32) a.delta[(size_t)bh * N + qpos] = w.di;  // for dK/dV
   w.acc[0] = f32x16{};
   w.acc[1] = f32x16{};
   const int32_t j1 = a.causal ? i_max + 1 : N;
@@ -756,15 +746,13 @@ void bwd_dq_glob_mfma_kernel(BwdArgs a) {
   }
 }
 
-__global__ __launch_bounds__(TT::kThreads)
-__attribute__((amdgpu_waves_per_eu(2)))
-void bwd_dkv_glob_mfma_kernel(BwdArgs a) {
-  __shared__ TT::Smem sm;
+// Workgroup wg of the B*H*ceil(n_global/128)*glob_chunks global-key ones.
+__device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t wg) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t n_gk = (a.n_global + kTQ - 1) / kTQ;
-  const int32_t chunks = a.glob_chunks, c = (int32_t)blockIdx.x % chunks;
-  const int32_t unit = (int32_t)blockIdx.x / chunks;
+  const int32_t chunks = a.glob_chunks, c = wg % chunks;
+  const int32_t unit = wg / chunks;
   const int32_t bh = unit / n_gk, gk = unit % n_gk;
   const int32_t N = a.N;
   const size_t head_elems = (size_t)N * kD;
@@ -937,7 +925,12 @@ void bwd_dq_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles,
   load_frag(w.df, static_cast<const bf16*>(a.dout) + bh * head_elems, qpos, lane);
   const float lse = a.lse[(size_t)bh * a.N + qpos];
   w.lse2 = lse == kNegInf ? -kNegInf : lse * kLog2e;
-  w.di = a.delta[(size_t)bh * a.N + qpos];
+  if (store) {  // the first pattern keeps every row: D_i here, for the later launches
+    w.di = row_delta(w.df, static_cast<const bf16*>(a.out) + bh * head_elems, qpos, lane);
+    if (qi < qcount && lane < 32) a.delta[(size_t)bh * a.N + qpos] = w.di;
+  } else {
+    w.di = a.delta[(size_t)bh * a.N + qpos];
+  }
   w.acc[0] = f32x16{};
   w.acc[1] = f32x16{};
   const int32_t hi = a.causal ? t0 + qcount - 1 : g.n_rows - 1;
@@ -1024,29 +1017,83 @@ void bwd_dkv_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles,
   }
 }
 
+// The launches: the global-tile workgroups first (their count rounded up to a
+// multiple of 8), then the band workgroups. Block b runs on XCD b % 8; each
+// XCD takes a contiguous share of the band tiles (tiles of one head then
+// share K/V in that XCD's L2). The global tiles' work thus fills the chip
+// while the band tiles finish, instead of running alone in a launch of its
+// own.
+__device__ __forceinline__ int32_t glob_wg(const BwdArgs& a) {
+  return a.n_global > 0 ? a.B * a.H * ((a.n_global + TT::kTQ - 1) / TT::kTQ) * a.glob_chunks : 0;
+}
+__device__ __forceinline__ int32_t glob_wg_padded(const BwdArgs& a) {
+  return (glob_wg(a) + kXcds - 1) / kXcds * kXcds;
+}
+// The band tile of block b (after the global ones), or -1.
+__device__ __forceinline__ int32_t band_tile_of(const BwdArgs& a, int32_t b) {
+  const int32_t x = b % kXcds, j = b / kXcds;
+  const int32_t per = (a.n_band_wg + kXcds - 1) / kXcds;
+  const int32_t bw = x * per + j;
+  return j >= per || bw >= a.n_band_wg ? -1 : bw;
+}
+
+// Two fragments per row (Q and dO) and two dot products per pair need more
+// registers than the forward: 3 waves per SIMD.
+__global__ __launch_bounds__(TT::kThreads)
+__attribute__((amdgpu_waves_per_eu(3)))
+void bwd_dq_mfma_kernel(BwdArgs a) {
+  __shared__ TT::Smem sm;
+  const int32_t b = (int32_t)blockIdx.x, gw = glob_wg_padded(a);
+  if (b < gw) {
+    if (b < glob_wg(a)) dq_glob_workgroup(a, sm, b);
+    return;
+  }
+  const int32_t bw = band_tile_of(a, b - gw);
+  if (bw >= 0) dq_band_workgroup(a, sm, bw);
+}
+
+__global__ __launch_bounds__(TT::kThreads)
+__attribute__((amdgpu_waves_per_eu(3)))
+void bwd_dkv_mfma_kernel(BwdArgs a) {
+  __shared__ TT::Smem sm;
+  const int32_t b = (int32_t)blockIdx.x, gw = glob_wg_padded(a);
+  if (b < gw) {
+    if (b < glob_wg(a)) dkv_glob_workgroup(a, sm, b);
+    return;
+  }
+  const int32_t bw = band_tile_of(a, b - gw);
+  if (bw >= 0) dkv_band_workgroup(a, sm, bw);
+}
+
 // The global rows' dQ and the global keys' dK, dV from the ranges' partial
 // sums, added in range order; with separate projections a global row's dq is 0.
-// One thread per 4 columns of a global row.
+// One thread per 4 columns of a global row of one of the three parts.
 __global__ __launch_bounds__(256) void bwd_glob_reduce_kernel(BwdArgs a) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t bhs = (int64_t)a.B * a.H;
-  if (t >= bhs * a.n_global * (kD / 4)) return;
-  const int32_t d4 = (int32_t)(t % (kD / 4));
-  const int64_t r = t / (kD / 4);
+  const int64_t per_part = (int64_t)a.B * a.H * a.n_global * (kD / 4);
+  if (t >= 3 * per_part) return;
+  const int32_t x = (int32_t)(t / per_part);  // 0 dQ, 1 dK, 2 dV
+  const int64_t rest = t % per_part;
+  const int32_t d4 = (int32_t)(rest % (kD / 4));
+  const int64_t r = rest / (kD / 4);
   const int32_t g = (int32_t)(r % a.n_global), bh = (int32_t)(r / a.n_global);
-  f32x4 s[3];
+  // four loads in flight at a time, added in range order
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  for (int32_t c0 = 0; c0 < a.glob_chunks; c0 += 4) {
+    f32x4 v[4];
 #pragma unroll
-  for (int x = 0; x < 3; ++x) s[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int32_t c = 0; c < a.glob_chunks; ++c) {
+    for (int u = 0; u < 4; ++u)
+      v[u] = c0 + u < a.glob_chunks
+                 ? reinterpret_cast<const f32x4*>(part_row(a, x, c0 + u, bh, g))[d4]
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int x = 0; x < 3; ++x) s[x] += reinterpret_cast<const f32x4*>(part_row(a, x, c, bh, g))[d4];
+    for (int u = 0; u < 4; ++u)
+      if (c0 + u < a.glob_chunks) sum += v[u];
   }
   const size_t ro = ((size_t)bh * a.N + a.gidx[g]) * kD;
-  f32x4* dq = reinterpret_cast<f32x4*>((a.sep ? a.dqg : a.dq) + ro);
-  dq[d4] = s[0] * a.scale;
-  if (a.sep) reinterpret_cast<f32x4*>(a.dq + ro)[d4] = f32x4{0.f, 0.f, 0.f, 0.f};
-  reinterpret_cast<f32x4*>(a.dk + ro)[d4] = s[1] * a.scale;
-  reinterpret_cast<f32x4*>(a.dv + ro)[d4] = s[2];
+  float* dst = x == 0 ? (a.sep ? a.dqg : a.dq) : (x == 1 ? a.dk : a.dv);
+  reinterpret_cast<f32x4*>(dst + ro)[d4] = sum * (x == 2 ? 1.f : a.scale);
+  if (x == 0 && a.sep) reinterpret_cast<f32x4*>(a.dq + ro)[d4] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // zeros into three fp32 buffers of n4 float4 each (a kernel: no memset)
@@ -1067,7 +1114,7 @@ hipError_t launch_dilated_bwd_mfma(const BwdArgs& a, hipStream_t stream) {
   int32_t first = -1;  // a pattern of dilation 1, launched first and storing
   for (int32_t k = 0; k < a.n_pairs && first < 0; ++k)
     if (a.pr[k] == 1) first = k;
-  if (first < 0)
+  if (first < 0)  // zeros, then every pattern adds (D_i came from a launch before)
     hipLaunchKernelGGL(bwd_zero3_kernel, dim3((uint32_t)((n4 + 255) / 256)), dim3(256), 0, stream,
                        a.dq, a.dk, a.dv, n4);
   for (int32_t x = 0; x < a.n_pairs; ++x) {
@@ -1087,35 +1134,38 @@ hipError_t launch_dilated_bwd_mfma(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Blocks of a dQ or dK/dV launch: the padded global-tile ones and 8 times the
+// band tiles per XCD.
+static int64_t mfma_grid(const BwdArgs& a) {
+  const int64_t g = a.n_global > 0 ? (int64_t)a.B * a.H * ((a.n_global + TT::kTQ - 1) / TT::kTQ) *
+                                         a.glob_chunks
+                                   : 0;
+  return (g + kXcds - 1) / kXcds * kXcds + (int64_t)kXcds * ((a.n_band_wg + kXcds - 1) / kXcds);
+}
+
 hipError_t launch_dq_mfma(const BwdArgs& a, hipStream_t stream) {
   if (a.n_band_wg <= 0) return hipSuccess;
-  const int64_t grid = (int64_t)kXcds * ((a.n_band_wg + kXcds - 1) / kXcds);
+  if (a.glob_chunks < 1 || (a.glob_chunks > 1 && !a.gpart)) return hipErrorInvalidValue;
+  const int64_t grid = mfma_grid(a);
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_dq_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dkv_mfma(const BwdArgs& a, hipStream_t stream) {
   if (a.n_band_wg <= 0) return hipSuccess;
-  const int64_t grid = (int64_t)kXcds * ((a.n_band_wg + kXcds - 1) / kXcds);
+  if (a.glob_chunks < 1 || (a.glob_chunks > 1 && !a.gpart)) return hipErrorInvalidValue;
+  const int64_t grid = mfma_grid(a);
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_dkv_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_glob_mfma(const BwdArgs& a, hipStream_t stream) {
-  if (a.n_global <= 0) return hipSuccess;
-  if (a.glob_chunks < 1 || (a.glob_chunks > 1 && !a.gpart)) return hipErrorInvalidValue;
-  const int64_t grid =
-      (int64_t)a.B * a.H * ((a.n_global + TT::kTQ - 1) / TT::kTQ) * a.glob_chunks;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dq_glob_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0, stream,
-                     a);
-  hipLaunchKernelGGL(bwd_dkv_glob_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
+hipError_t launch_glob_reduce(const BwdArgs& a, hipStream_t stream) {
+  if (a.n_global <= 0 || a.glob_chunks <= 1) return hipSuccess;
+  const int64_t threads = (int64_t)3 * a.B * a.H * a.n_global * (kD / 4);
+  hipLaunchKernelGGL(bwd_glob_reduce_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0,
                      stream, a);
-  if (a.glob_chunks > 1) {
-    const int64_t threads = (int64_t)a.B * a.H * a.n_global * (kD / 4);
-    hipLaunchKernelGGL(bwd_glob_reduce_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256),
-                       0, stream, a);
-  }
   return hipGetLastError();
 }
 
