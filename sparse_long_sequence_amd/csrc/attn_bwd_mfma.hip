@@ -117,16 +117,49 @@ __device__ __forceinline__ void acc_transposed(const bf16* tile0, f32x16 (&acc)[
   }
 }
 
+// The forward's scalar bias table on a staged tile (ETC page, §3.4 "Relative
+// Position Encoding": same-kind pairs only; br.tab null: none). From the
+// tile's global flags: whether any pair takes the bias (on) and whether every
+// one does (same), as the forward decides them. A tile staged without flags
+// has no global position in it.
+struct TileBias {
+  bool on, same;
+};
+template <int32_t BUF>
+__device__ __forceinline__ TileBias tile_bias(const TT::Smem& sm, const BiasRule& br,
+                                              const KeyTile& kt) {
+  if (!br.tab) return {false, false};
+  const int32_t gc = kt.gmode == kGlobNone ? 0 : __builtin_amdgcn_readfirstlane(sm.gcls[BUF]);
+  const bool any_g = (gc & 1) != 0, all_g = (gc & 2) != 0;
+  return {br.key_global_is_same_kind ? any_g : !all_g,
+          br.key_global_is_same_kind ? all_g : !any_g};
+}
+
+// The head's scalar bias table, in q.k units (times sqrt(D)), into sm.bias
+// for br (visible after the next barrier). flip: entry l holds entry 2k - l,
+// for the dK/dV pass, whose lanes hold the keys and whose tiles hold the rows
+// (the bias of a pair depends on key - row).
+__device__ __forceinline__ BiasRule bias_rule(const BwdArgs& a, TT::Smem& sm, int32_t h,
+                                              bool flip, int32_t lane_is_global_kind) {
+  const int32_t nb = 2 * a.rel_k + 1;
+  if (!a.rel_bias) return {nullptr, 0, 0, 0};
+  const int32_t tid = threadIdx.x;
+  if (tid < nb) sm.bias[tid] = a.rel_bias[h * nb + (flip ? nb - 1 - tid : tid)] / a.scale;
+  return {sm.bias, a.rel_k, lane_is_global_kind, 0};
+}
+
 // One staged key tile into dQ^T. The forward's block classes decide which
 // sub-tiles run and which need the per-element mask.
-template <int32_t BUF>
+template <int32_t BUF, bool BIAS>
 __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t lane,
                                         const MaskRule& mr, const KeyTile& kt, int32_t qi,
-                                        int32_t qpos, bool dead, float c) {
+                                        int32_t qpos, bool dead, float c, const BiasRule& br) {
   const int32_t r0 = (mr.use_qpos ? __builtin_amdgcn_readlane(qpos, 0)
                                   : __builtin_amdgcn_readlane(qi, 0)) + mr.ref_off;
   const int32_t r1 = (mr.use_qpos ? __builtin_amdgcn_readlane(qpos, TT::kRowsPerBlock - 1)
                                   : __builtin_amdgcn_readlane(qi, TT::kRowsPerBlock - 1)) + mr.ref_off;
+  TileBias tb = {false, false};
+  if constexpr (BIAS) tb = tile_bias<BUF>(sm, br, kt);
 #pragma unroll
   for (int sb = 0; sb < TT::kSub; ++sb) {
     const int32_t cls = dead ? kEmpty : classify<bf16>(mr, kt.count, sb, r0, r1);
@@ -134,6 +167,9 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
     float s[TT::kNS], dp[TT::kNS];
     tile_dots(&sm.k[BUF][0], w.qf, lane, sb, s);
     tile_dots(&sm.v[BUF][0], w.df, lane, sb, dp);
+    if constexpr (BIAS) {
+      if (tb.on) add_bias<bf16>(s, sm, BUF, br, sb, qi, qpos, lane, tb.same);
+    }
     if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, qi, qpos, lane);
     TT::PTile G;
 #pragma unroll
@@ -208,6 +244,7 @@ __device__ __forceinline__ bool qi_is_global(const BwdArgs& a, int32_t qi, int32
 
 // dQ of the non-global rows of one query tile (the forward's band workgroup:
 // window tiles, then the global keys outside the window).
+template <bool BIAS>
 __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t bw) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -256,15 +293,29 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
   const int32_t lo = max(0, t0 - R);
   const int32_t hi = a.causal ? (t0 + qcount - 1) : min(n_c - 1, t0 + qcount - 1 + R);
   const int32_t n_band = (hi - lo + 1 + kTK - 1) / kTK;
-  const GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
+  GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
+  BiasRule br = {nullptr, 0, 0, 0};
+  if constexpr (BIAS) {
+    // the window keys' global flags decide which pairs are same-kind
+    br = bias_rule(a, sm, h, false, 0);
+    if (ng > 0) {
+      if (hi - lo + 1 <= 32 * kGMaskWords) {
+        build_gmask<bf16>(sm, a.gidx, ng, c + d * lo, d, hi - lo + 1, tid);
+        gi.mode = kGlobBitmap;
+      } else {
+        gi.mode = kGlobSearch;
+      }
+    }
+  }
+  const int32_t gkeys = BIAS ? kGlobAll : kGlobNone;  // mode of the global-key tiles
   auto proc = [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
     constexpr int32_t buf = decltype(buf_tag)::value;
-    dq_tile<buf>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2);
+    dq_tile<buf, BIAS>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2, br);
   };
   auto band_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = lo + n * kTK;
     const int32_t kcount = min(kTK, hi - u0 + 1);
-    kt = {nullptr, c + d * u0, d, kcount, u0 - lo, kGlobNone};
+    kt = {nullptr, c + d * u0, d, kcount, u0 - lo, gi.mode};
     const int32_t dmin = u0 - t0 - (qcount - 1);
     const int32_t dmax = u0 + kcount - 1 - t0;
     const int32_t hib = a.causal ? 0 : R;
@@ -286,7 +337,7 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
           a.causal ? (gl >= i_hi - R && gh <= i_lo) : (gl >= i_hi - R && gh <= i_lo + R);
       const bool none_causal = a.causal && gl > i_hi;
       const bool keep = !all_in_band && !none_causal;
-      kt = {nullptr, gl, 1, keep ? cnt : 0, 0, kGlobNone};
+      kt = {nullptr, gl, 1, keep ? cnt : 0, 0, gkeys};
       const bool all_out = cnt == kTK && (gh < i_lo - R || (!a.causal && gl > i_hi + R)) &&
                            (!a.causal || gh <= i_lo);
       mr = {kOutside, all_out ? 0 : 1, 1, -gl, -R, a.causal ? kFar : R, 0, 0, 1};
@@ -319,7 +370,7 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
         gt = __builtin_ctzll(m);
       }
       const int32_t kcount = min(kTK, ng - gt * kTK);
-      kt = {a.gidx + gt * kTK, 0, 1, kcount, 0, kGlobNone};
+      kt = {a.gidx + gt * kTK, 0, 1, kcount, 0, gkeys};
       const int32_t gl = a.gidx[gt * kTK], gh = a.gidx[gt * kTK + kcount - 1];
       const bool outside = (gh < i_lo - d * R) || (gl > i_hi + d * R);
       const bool causal_ok = !a.causal || gh <= i_lo;
@@ -394,10 +445,14 @@ __device__ __forceinline__ const float* row_di(const TT::Smem& sm, int32_t buf) 
 // PRIO: the exponential stretch at raised wave issue priority (as in the
 // forward's softmax); it pays in the LongNet sweeps (the (2048, 1) pattern's
 // dK/dV launch runs about 11% faster) and costs about 1% in the band ones.
-template <int32_t BUF, bool EXCL_G, bool ROWS_AFTER, bool INIT, bool PRIO = false>
+// BIAS: the scalar bias table (br: the flipped table, key_global_is_same_kind
+// = the lane's key is global).
+template <int32_t BUF, bool EXCL_G, bool ROWS_AFTER, bool INIT, bool PRIO = false,
+          bool BIAS = false>
 __device__ __forceinline__ void dkv_tile(const TT::Smem& sm, DkvWave& w, int32_t lane,
                                          const MaskRule& mr, const KeyTile& kt, int32_t ki,
-                                         int32_t kpos, bool dead, float c, bool causal) {
+                                         int32_t kpos, bool dead, float c, bool causal,
+                                         const BiasRule& br = {nullptr, 0, 0, 0}) {
   const int32_t r0 = (mr.use_qpos ? __builtin_amdgcn_readlane(kpos, 0)
                                   : __builtin_amdgcn_readlane(ki, 0)) + mr.ref_off;
   const int32_t r1 = (mr.use_qpos ? __builtin_amdgcn_readlane(kpos, TT::kRowsPerBlock - 1)
@@ -405,6 +460,8 @@ __device__ __forceinline__ void dkv_tile(const TT::Smem& sm, DkvWave& w, int32_t
   bool any_g = false;
   if constexpr (EXCL_G)
     any_g = kt.gmode != kGlobNone && (__builtin_amdgcn_readfirstlane(sm.gcls[BUF]) & 1) != 0;
+  TileBias tb = {false, false};
+  if constexpr (BIAS) tb = tile_bias<BUF>(sm, br, kt);
   int32_t kl = TT::key_lane(lane);
   asm("" : "+v"(kl));  // opaque per call, as in mask_tile
 #pragma unroll
@@ -427,6 +484,9 @@ __device__ __forceinline__ void dkv_tile(const TT::Smem& sm, DkvWave& w, int32_t
     } else {  // s = q.k, dp = dO.v
       tile_dots(&sm.k[BUF][0], w.kf, lane, sb, s);
       tile_dots(&sm.v[BUF][0], w.vf, lane, sb, dp);
+    }
+    if constexpr (BIAS) {
+      if (tb.on) add_bias<bf16>(s, sm, BUF, br, sb, ki, kpos, lane, tb.same);
     }
     if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, ki, kpos, lane);
     if (EXCL_G && any_g) {
@@ -551,6 +611,7 @@ __device__ __forceinline__ void store_rows_f32(float* dst, const f32x16 (&acc)[2
 
 // dK, dV of the non-global keys of one key tile (a residue class of the
 // head's dilation, like the forward's query tiles).
+template <bool BIAS>
 __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t bw) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -609,6 +670,8 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& s
       gi.mode = kGlobSearch;
     }
   }
+  BiasRule br = {nullptr, 0, 0, 0};
+  if constexpr (BIAS) br = bias_rule(a, sm, h, true, 0);  // lanes hold keys: flipped table
   auto band_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = lo + n * kTK;
     const int32_t cnt = min(kTK, hi - u0 + 1);
@@ -623,21 +686,23 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& s
   stream_rows<false>(sm, qs, dob, lse, delta, 1.f / a.scale, n_band, band_desc, gi,
                      [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                        constexpr int32_t buf = decltype(buf_tag)::value;
-                       dkv_tile<buf, true, false, true>(sm, w, lane, mr, kt, ki, kpos, dead,
-                                                  a.scale_log2, a.causal);
+                       dkv_tile<buf, true, false, true, false, BIAS>(
+                           sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br);
                      });
   // the global rows reach every key (causal: rows at or after it)
   const int32_t n_gt = (ng + kTK - 1) / kTK;
-  const GlobInfo gall = {kGlobNone, a.gidx, ng, nullptr, 0, 0, 0};
+  const int32_t grows = BIAS ? kGlobAll : kGlobNone;  // mode of the global-row tiles
+  const GlobInfo gall = {grows, a.gidx, ng, nullptr, 0, 0, 0};
   auto glob_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t cnt = min(kTK, ng - n * kTK);
-    kt = {a.gidx + n * kTK, 0, 1, cnt, 0, kGlobNone};
+    kt = {a.gidx + n * kTK, 0, 1, cnt, 0, grows};
     // every row of the tile, unless it is past the tile's end
     mr = {kRange, cnt == kTK ? 0 : 1, 0, 0, -kFar, kFar, 0, 0, 1};
   };
   auto glob_proc = [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
     constexpr int32_t buf = decltype(buf_tag)::value;
-    dkv_tile<buf, false, true, true>(sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal);
+    dkv_tile<buf, false, true, true, false, BIAS>(sm, w, lane, mr, kt, ki, kpos, dead,
+                                                  a.scale_log2, a.causal, br);
   };
   const bool mine = ki < kcount && !qi_is_global(a, ki, kcount, kpos, g_first, g_last, j_lo, j_hi);
   if (a.sep) {
@@ -691,6 +756,7 @@ __device__ __forceinline__ float* part_row(const BwdArgs& a, int32_t part, int32
 }
 
 // Workgroup wg of the B*H*ceil(n_global/128)*glob_chunks global-row ones.
+template <bool BIAS>
 __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t wg) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -719,20 +785,34 @@ __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm
   const int32_t j1 = a.causal ? i_max + 1 : N;
   int32_t t0, n_tiles;
   chunk_range((j1 + kTK - 1) / kTK, chunks, c, t0, n_tiles);
+  GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
+  BiasRule br = {nullptr, 0, 0, 0};
+  if constexpr (BIAS) {
+    // the keys' global flags decide which pairs are same-kind (global keys)
+    br = bias_rule(a, sm, bh % a.H, false, 1);
+    const int32_t ub = t0 * kTK, ue = min(j1, ub + n_tiles * kTK);
+    if (n_tiles > 0) {
+      if (ue - ub <= 32 * kGMaskWords) {
+        build_gmask<bf16>(sm, a.gidx, a.n_global, ub, 1, ue - ub, tid);
+        gi.mode = kGlobBitmap;
+      } else {
+        gi.mode = kGlobSearch;
+      }
+    }
+  }
   auto desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = (t0 + n) * kTK;
     const int32_t kcount = min(kTK, j1 - u0);
-    kt = {nullptr, u0, 1, kcount, 0, kGlobNone};
+    kt = {nullptr, u0, 1, kcount, n * kTK, gi.mode};
     // key position u0 + kj <= qpos when causal
     const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= i_min);
     mr = {kRange, full ? 0 : 1, 1, -u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
   };
-  const GlobInfo gi = {kGlobNone, nullptr, 0, nullptr, 0, 0, 0};
   stream_tiles<false>(sm, static_cast<const bf16*>(sep ? a.kg : a.k) + bh * head_elems,
                       static_cast<const bf16*>(sep ? a.vg : a.v) + bh * head_elems, n_tiles, desc,
                       gi, [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                         constexpr int32_t buf = decltype(buf_tag)::value;
-                        dq_tile<buf>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2);
+                        dq_tile<buf, BIAS>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2, br);
                       });
   if (qi < qcount && chunks > 1) {
     store_rows_f32(part_row(a, 0, c, bh, gq * kTQ + qi), w.acc, 1.f, lane);
@@ -747,6 +827,7 @@ __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm
 }
 
 // Workgroup wg of the B*H*ceil(n_global/128)*glob_chunks global-key ones.
+template <bool BIAS>
 __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t wg) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -781,7 +862,11 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, TT::Smem& s
   chunk_range((N - r0 + kTK - 1) / kTK, chunks, c, t0, n_tiles);
   const int32_t ub = r0 + t0 * kTK, ue = min(N, ub + n_tiles * kTK);
   GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
-  if (sep && n_tiles > 0) {
+  BiasRule br = {nullptr, 0, 0, 0};
+  if constexpr (BIAS) br = bias_rule(a, sm, bh % a.H, true, 1);  // lanes hold global keys
+  // the rows' global flags: excluded with separate projections; with a bias
+  // table, the same-kind pairs
+  if ((sep || BIAS) && n_tiles > 0) {
     if (ue - ub <= 32 * kGMaskWords) {
       build_gmask<bf16>(sm, a.gidx, a.n_global, ub, 1, ue - ub, tid);
       gi.mode = kGlobBitmap;
@@ -802,15 +887,15 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, TT::Smem& s
     stream_rows<false>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
                        [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                          constexpr int32_t buf = decltype(buf_tag)::value;
-                         dkv_tile<buf, true, false, true>(sm, w, lane, mr, kt, ki, kpos, dead,
-                                                    a.scale_log2, a.causal);
+                         dkv_tile<buf, true, false, true, false, BIAS>(
+                             sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br);
                        });
   else
     stream_rows<false>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
                        [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                          constexpr int32_t buf = decltype(buf_tag)::value;
-                         dkv_tile<buf, false, false, true>(sm, w, lane, mr, kt, ki, kpos, dead,
-                                                     a.scale_log2, a.causal);
+                         dkv_tile<buf, false, false, true, false, BIAS>(
+                             sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br);
                        });
   const size_t ro = ((size_t)bh * N + kpos) * kD;
   if (ki < kcount && chunks > 1) {
@@ -831,18 +916,19 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, TT::Smem& s
     w.dv[x] = f32x16{};
   }
   const int32_t n_gt = (a.n_global + kTK - 1) / kTK;
+  const int32_t grows = BIAS ? kGlobAll : kGlobNone;  // mode of the global-row tiles
   auto glob_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t cnt = min(kTK, a.n_global - n * kTK);
-    kt = {a.gidx + n * kTK, 0, 1, cnt, 0, kGlobNone};
+    kt = {a.gidx + n * kTK, 0, 1, cnt, 0, grows};
     mr = {kRange, cnt == kTK ? 0 : 1, 0, 0, -kFar, kFar, 0, 0, 1};
   };
-  const GlobInfo gall = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
+  const GlobInfo gall = {grows, a.gidx, a.n_global, nullptr, 0, 0, 0};
   stream_rows<true>(sm, static_cast<const bf16*>(a.qg) + bh * head_elems, dob, lse, delta,
                     1.f / a.scale, n_gt,
                     glob_desc, gall, [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                       constexpr int32_t buf = decltype(buf_tag)::value;
-                      dkv_tile<buf, false, true, true>(sm, w, lane, mr, kt, ki, kpos, dead,
-                                                 a.scale_log2, a.causal);
+                      dkv_tile<buf, false, true, true, false, BIAS>(
+                          sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br);
                     });
   if (ki < kcount) {
     store_rows_f32(a.dkg + ro, w.dk, a.scale, lane);
@@ -947,7 +1033,8 @@ void bwd_dq_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles,
                       static_cast<const bf16*>(a.v) + bh * head_elems, n_tiles, desc, gi,
                       [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                         constexpr int32_t buf = decltype(buf_tag)::value;
-                        dq_tile<buf>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2);
+                        dq_tile<buf, false>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2,
+                                            BiasRule{nullptr, 0, 0, 0});
                       });
   if (qi < qcount) {
     float* dst = a.dq + ((size_t)bh * a.N + qpos) * kD;
@@ -1039,30 +1126,35 @@ __device__ __forceinline__ int32_t band_tile_of(const BwdArgs& a, int32_t b) {
 
 // Two fragments per row (Q and dO) and two dot products per pair need more
 // registers than the forward: 3 waves per SIMD.
+// BIAS: with the forward's scalar bias table (a separate instantiation, so
+// that the kernels without one are built as before).
+template <bool BIAS>
 __global__ __launch_bounds__(TT::kThreads)
 __attribute__((amdgpu_waves_per_eu(3)))
 void bwd_dq_mfma_kernel(BwdArgs a) {
   __shared__ TT::Smem sm;
   const int32_t b = (int32_t)blockIdx.x, gw = glob_wg_padded(a);
   if (b < gw) {
-    if (b < glob_wg(a)) dq_glob_workgroup(a, sm, b);
+    if (b < glob_wg(a)) dq_glob_workgroup<BIAS>(a, sm, b);
     return;
   }
   const int32_t bw = band_tile_of(a, b - gw);
-  if (bw >= 0) dq_band_workgroup(a, sm, bw);
+  if (bw >= 0) dq_band_workgroup<BIAS>(a, sm, bw);
 }
 
+// (the table's per-element work needs the registers of 2 waves per SIMD)
+template <bool BIAS>
 __global__ __launch_bounds__(TT::kThreads)
-__attribute__((amdgpu_waves_per_eu(3)))
+__attribute__((amdgpu_waves_per_eu(BIAS ? 2 : 3)))
 void bwd_dkv_mfma_kernel(BwdArgs a) {
   __shared__ TT::Smem sm;
   const int32_t b = (int32_t)blockIdx.x, gw = glob_wg_padded(a);
   if (b < gw) {
-    if (b < glob_wg(a)) dkv_glob_workgroup(a, sm, b);
+    if (b < glob_wg(a)) dkv_glob_workgroup<BIAS>(a, sm, b);
     return;
   }
   const int32_t bw = band_tile_of(a, b - gw);
-  if (bw >= 0) dkv_band_workgroup(a, sm, bw);
+  if (bw >= 0) dkv_band_workgroup<BIAS>(a, sm, bw);
 }
 
 // The global rows' dQ and the global keys' dK, dV from the ranges' partial
@@ -1148,7 +1240,12 @@ hipError_t launch_dq_mfma(const BwdArgs& a, hipStream_t stream) {
   if (a.glob_chunks < 1 || (a.glob_chunks > 1 && !a.gpart)) return hipErrorInvalidValue;
   const int64_t grid = mfma_grid(a);
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dq_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0, stream, a);
+  if (a.rel_bias)
+    hipLaunchKernelGGL(bwd_dq_mfma_kernel<true>, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(bwd_dq_mfma_kernel<false>, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
@@ -1157,7 +1254,12 @@ hipError_t launch_dkv_mfma(const BwdArgs& a, hipStream_t stream) {
   if (a.glob_chunks < 1 || (a.glob_chunks > 1 && !a.gpart)) return hipErrorInvalidValue;
   const int64_t grid = mfma_grid(a);
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dkv_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0, stream, a);
+  if (a.rel_bias)
+    hipLaunchKernelGGL(bwd_dkv_mfma_kernel<true>, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(bwd_dkv_mfma_kernel<false>, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

@@ -483,7 +483,8 @@ struct TileTraits<bf16> {
   // The reads are issued through inline asm that also waits for them: for the
   // builtin, the compiler cannot tell that the read does not touch the LDS
   // buffer the next tile is being loaded into, and waits for those loads
-  // first, which leaves the prefetch only part of a tile to land.
+  // first, which leaves the prefetch only part of a tile to land. Both key
+  // steps' reads go out together, so the sub-tile waits for LDS once.
   static __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
   }
@@ -500,21 +501,32 @@ struct TileTraits<bf16> {
     const uint32_t a01 = lds_addr(base + 8 * kD + 8 * (0 ^ u ^ 2));
     const uint32_t a10 = lds_addr(base + 8 * (4 ^ u));
     const uint32_t a11 = lds_addr(base + 8 * kD + 8 * (4 ^ u ^ 2));
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int32_t off = (buf * kTK * kD + (32 * sb + 16 * t) * kD) * 2;  // bytes
-      s16x4 lo0, hi0, lo1, hi1;
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
-          "ds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
-          "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
-          "ds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(lo0), "=&v"(hi0), "=&v"(lo1), "=&v"(hi1)
-          : "v"(a00), "v"(a01), "v"(a10), "v"(a11), "i"(off));
+    const int32_t off = (buf * kTK * kD + (32 * sb) * kD) * 2;  // bytes
+    constexpr int32_t o16 = 16 * kD * 2;  // the second key step
+    s16x4 lo0, hi0, lo1, hi1, lo2, hi2, lo3, hi3;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo0), "=&v"(hi0), "=&v"(lo1), "=&v"(hi1), "=&v"(lo2), "=&v"(hi2), "=&v"(lo3), "=&v"(hi3)
+        : "v"(a00), "v"(a01), "v"(a10), "v"(a11), "i"(off), "i"(off + o16));
+    {
       const bf16x8 a0 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo0, hi0, 0, 1, 2, 3, 4, 5, 6, 7));
       const bf16x8 a1 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo1, hi1, 0, 1, 2, 3, 4, 5, 6, 7));
-      const bf16x8 b = __builtin_bit_cast(bf16x8, P.p[t]);
+      const bf16x8 b = __builtin_bit_cast(bf16x8, P.p[0]);
+      w.o[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, w.o[0], 0, 0, 0);
+      w.o[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, w.o[1], 0, 0, 0);
+    }
+    {
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo3, hi3, 0, 1, 2, 3, 4, 5, 6, 7));
+      const bf16x8 b = __builtin_bit_cast(bf16x8, P.p[1]);
       w.o[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, w.o[0], 0, 0, 0);
       w.o[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, w.o[1], 0, 0, 0);
     }

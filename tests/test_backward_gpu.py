@@ -207,6 +207,39 @@ def test_backward_labels(dev, case):
     run_label_case(dev, tag, dtype, w, inp, seed=405)
 
 
+BIAS_CASES = [
+    # the forward's scalar bias table alone (MFMA path): tag, B, H, N, globals,
+    # R, dilation, causal, separate, rel_k
+    ("bias-etc-like", 1, 3, 640, tuple(range(48)), 24, None, False, False, 6),
+    ("bias-scattered-sep-causal", 1, 2, 700, (3, 64, 65, 300, 699), 20, (1, 2), True, True, 4),
+    ("bias-no-window", 1, 1, 256, (10, 11), 0, None, False, False, 3),
+    ("bias-windows-hold-globals", 2, 2, 1300, (100, 101, 640, 641, 642, 1299), 40, (1, 3), False,
+     False, 12),
+]
+
+
+@pytest.mark.parametrize("case", BIAS_CASES, ids=[c[0] for c in BIAS_CASES])
+def test_backward_bias_table(dev, case):
+    """Same-kind pairs take the table's entry for their clipped distance (ETC
+    page, §3.4 "Relative Position Encoding"); global tokens inside windows,
+    dilated heads, separate projections and causal rows."""
+    tag, B, H, N, G, R, dil, causal, sep, rk = case
+    w = W.Workload(tag, B=B, H=H, N=N, radius=R, global_idx=G, dilation=dil, causal=causal,
+                   separate_global=sep, rel_k=rk, rel_kind="scalar",
+                   seed=500 + BIAS_CASES.index(case))
+    inp = W.make_inputs(w)
+    assert inp.rel_bias is not None and inp.rel_vec is None
+    run_label_case(dev, tag, "bf16", w, inp, seed=501)
+
+
+def test_backward_etc_shape(dev):
+    """The ETC global-local shape (B=1, H=12, n_g=256 global tokens then
+    n_l=4096 long tokens, R=84, per-head scalar table for distances in
+    [-12, 12]), every element against the oracle."""
+    w = W.WORKLOADS["etc-ng256-nl4096-r84-relk12"]
+    run_label_case(dev, "etc-shape", "bf16", w, W.make_inputs(w), seed=w.seed)
+
+
 def test_backward_etc_structured(dev):
     """The ETC structured layout (hard g2l, no cross-context g2g or l2l, four
     structural labels, key-side label vectors) at a reduced size."""
