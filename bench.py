@@ -25,9 +25,10 @@ timed as one region between two events, then K calls with an event pair each,
 then K cold calls: before each, a 512 MiB buffer is written (more than the
 L2 caches and the 256 MiB MALL hold), and an event pair times the call alone.
 
---backward times la_attn_backward on the Longformer-base workload and
-la_dilated_backward on the LongNet workload instead (same method; the
-forward's out and lse are computed once, untimed) and prints their JSON line.
+--backward times la_attn_backward on the Longformer-base and ETC (scalar bias
+table) workloads and la_dilated_backward on the LongNet workload instead (same
+method; the forward's out and lse are computed once, untimed) and prints their
+JSON line.
 
 --copy-probe also runs a plain device copy of 256 MiB (torch.neg, fp32) a few
 times: under rocprofv3 --pmc its FETCH_SIZE and WRITE_SIZE give the factor that
@@ -317,8 +318,8 @@ def copy_probe(dev, reps=3):
 
 def bench_backward(dev, args):
     """Backward calls, timed like the forward: the Longformer-base band + global
-    backward (dq, dk, dv and the separate global projections' gradients) and
-    the LongNet mixture's backward. Useful work: 10*D FLOPs per allowed pair
+    backward (dq, dk, dv and the separate global projections' gradients), the
+    LongNet mixture's backward and the ETC shape's (with its bias table). Useful work: 10*D FLOPs per allowed pair
     (q.k and dO.v recomputed, then dV, dQ and dK, 2*D each)."""
     import torch
 
@@ -327,7 +328,7 @@ def bench_backward(dev, args):
     from sparse_long_sequence_amd import workloads as W
 
     res = {}
-    for w in (W.LONGFORMER_BASE, W.LONGNET_SHARE):
+    for w in (W.LONGFORMER_BASE, W.LONGNET_SHARE, W.WORKLOADS["etc-ng256-nl4096-r84-relk12"]):
         log(f"bench backward: {w.name}")
         c = Call(w, dev)
         c()
@@ -339,7 +340,8 @@ def bench_backward(dev, args):
                                             w.causal)
         else:
             call = la.bind_attn_backward(c.q, c.k, c.v, c.out, c.lse, dout, c.g, w.radius,
-                                         w.dilation, w.causal, qg=c.qg, kg=c.kg, vg=c.vg)
+                                         w.dilation, w.causal, qg=c.qg, kg=c.kg, vg=c.vg,
+                                         rel_bias=c.rb, rel_vec=c.rv)
         steps = max(3, min(args.steps, 20))
         region_ms, mean_ms, med_ms, _ = time_calls(call, steps, min(args.warmup, 3), args.settle,
                                                    cold=False)
