@@ -287,11 +287,12 @@ size_t la_attn_backward_workspace_size(const la_dims *dims);
  *  dout         device bf16 [B,H,N,D]: the loss gradient w.r.t. out.
  *  dq, dk, dv   device fp32 [B,H,N,D] outputs (fully written; must not alias inputs).
  *  workspace    la_dilated_backward_workspace_size() bytes, 256-byte aligned.
- * Errors as for la_dilated_forward. 2 * n_pairs launches on `stream` (each
- * pattern's dQ and dK/dV terms: a pattern of dilation 1, which keeps every row
- * and key, goes first, computes D_i and stores its terms, and the others add
- * theirs in pattern order; without one, a D_i and a zeroing launch come first
- * and every pattern adds: deterministic), no allocation. */
+ * Errors as for la_dilated_forward. n_pairs + 1 launches on `stream`: each
+ * pattern's dQ terms, then its dK/dV terms in the next launch beside the next
+ * pattern's dQ terms. A pattern of dilation 1, which keeps every row and key,
+ * goes first, computes D_i and stores its terms; the others add theirs in a
+ * fixed order (deterministic). Without one, a D_i and a zeroing launch come
+ * first and every pattern adds. No allocation. */
 la_status la_dilated_backward(const la_dims *dims, const void *q, const void *k, const void *v,
                               const int32_t *seg_lens, const int32_t *dil_rates, int32_t n_pairs,
                               int32_t causal, const void *out, const float *lse,

@@ -989,15 +989,18 @@ __device__ __forceinline__ void add_rows_f32(float* dst, const f32x16 (&acc)[2],
   }
 }
 
-__global__ __launch_bounds__(TT::kThreads)
-__attribute__((amdgpu_waves_per_eu(3)))
-void bwd_dq_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles,
-                            int32_t store) {
-  __shared__ TT::Smem sm;
+// One launch's share of pattern k: its workgroups, decoded by dil_decode.
+struct DilPart {
+  int32_t k, nseg, qtiles, store;
+};
+
+__device__ __forceinline__ void dq_dil_workgroup(const BwdArgs& a, TT::Smem& sm, const DilPart& p,
+                                                 int64_t wg) {
+  const int32_t k = p.k, nseg = p.nseg, qtiles = p.qtiles, store = p.store;
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t qt, seg, bh;
-  dil_decode(a, nseg, qtiles, blockIdx.x, qt, seg, bh);
+  dil_decode(a, nseg, qtiles, wg, qt, seg, bh);
   const DilGeom g = dil_geom(a, k, seg, bh % a.H);
   const int32_t t0 = qt * kTQ;
   if (t0 >= g.n_rows) return;
@@ -1045,15 +1048,13 @@ void bwd_dq_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles,
   }
 }
 
-__global__ __launch_bounds__(TT::kThreads)
-__attribute__((amdgpu_waves_per_eu(2)))
-void bwd_dkv_dil_mfma_kernel(BwdArgs a, int32_t k, int32_t nseg, int32_t qtiles,
-                             int32_t store) {
-  __shared__ TT::Smem sm;
+__device__ __forceinline__ void dkv_dil_workgroup(const BwdArgs& a, TT::Smem& sm,
+                                                  const DilPart& p, int64_t wg) {
+  const int32_t k = p.k, nseg = p.nseg, qtiles = p.qtiles, store = p.store;
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t qt, seg, bh;
-  dil_decode(a, nseg, qtiles, blockIdx.x, qt, seg, bh);
+  dil_decode(a, nseg, qtiles, wg, qt, seg, bh);
   const DilGeom g = dil_geom(a, k, seg, bh % a.H);
   const int32_t t0 = qt * kTQ;
   if (t0 >= g.n_rows) return;
@@ -1188,6 +1189,21 @@ __global__ __launch_bounds__(256) void bwd_glob_reduce_kernel(BwdArgs a) {
   if (x == 0 && a.sep) reinterpret_cast<f32x4*>(a.dq + ro)[d4] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// One LongNet launch: the dK/dV workgroups of pattern kv.k (grid_kv of them,
+// the longer work, first), then the dQ ones of pattern q.k (k < 0: none). The
+// two parts add into different gradients, so they run side by side; each
+// gradient still takes its patterns in launch order.
+__global__ __launch_bounds__(TT::kThreads)
+__attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dil_mfma_kernel(BwdArgs a, DilPart kv, int64_t grid_kv, DilPart q) {
+  __shared__ TT::Smem sm;
+  const int64_t b = blockIdx.x;
+  if (b < grid_kv)
+    dkv_dil_workgroup(a, sm, kv, b);
+  else if (q.k >= 0)
+    dq_dil_workgroup(a, sm, q, b - grid_kv);
+}
+
 // zeros into three fp32 buffers of n4 float4 each (a kernel: no memset)
 __global__ __launch_bounds__(256) void bwd_zero3_kernel(float* x, float* y, float* z, int64_t n4) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1209,19 +1225,37 @@ hipError_t launch_dilated_bwd_mfma(const BwdArgs& a, hipStream_t stream) {
   if (first < 0)  // zeros, then every pattern adds (D_i came from a launch before)
     hipLaunchKernelGGL(bwd_zero3_kernel, dim3((uint32_t)((n4 + 255) / 256)), dim3(256), 0, stream,
                        a.dq, a.dk, a.dv, n4);
-  for (int32_t x = 0; x < a.n_pairs; ++x) {
-    // first, then the others in pattern order
-    const int32_t k = first < 0 ? x : (x == 0 ? first : (x <= first ? x - 1 : x));
-    const int32_t store = x == 0 && first >= 0 ? 1 : 0;
+  auto part_of = [&](int32_t k, bool store) {
     const int32_t nseg = (a.N + a.pw[k] - 1) / a.pw[k];
     const int32_t rows = (a.pw[k] + a.pr[k] - 1) / a.pr[k];
-    const int32_t qtiles = (rows + TT::kTQ - 1) / TT::kTQ;
-    const int64_t grid = (int64_t)a.B * a.H * nseg * qtiles;
-    if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(bwd_dq_dil_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0, stream,
-                       a, k, nseg, qtiles, store);
-    hipLaunchKernelGGL(bwd_dkv_dil_mfma_kernel, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
-                       stream, a, k, nseg, qtiles, store);
+    return DilPart{k, nseg, (rows + TT::kTQ - 1) / TT::kTQ, store ? 1 : 0};
+  };
+  auto grid_of = [&](const DilPart& p) { return (int64_t)a.B * a.H * p.nseg * p.qtiles; };
+  // order: the storing pattern, then the others by launch size, smallest
+  // first, so that the dK/dV launch left alone at the end is the largest
+  DilPart ord[kMaxPairs];
+  int32_t n = 0;
+  if (first >= 0) ord[n++] = part_of(first, true);
+  for (int32_t k = 0; k < a.n_pairs; ++k) {
+    if (k == first) continue;
+    const DilPart p = part_of(k, false);
+    int32_t x = n++;
+    while (x > (first >= 0 ? 1 : 0) && grid_of(ord[x - 1]) > grid_of(p)) {
+      ord[x] = ord[x - 1];
+      --x;
+    }
+    ord[x] = p;
+  }
+  for (int32_t x = 0; x < n; ++x)
+    if (grid_of(ord[x]) <= 0 || 2 * grid_of(ord[x]) > 0x7fffffffLL) return hipErrorInvalidValue;
+  // launch x: dK/dV of pattern x - 1 beside dQ of pattern x
+  const DilPart none = {-1, 0, 0, 0};
+  for (int32_t x = 0; x <= n; ++x) {
+    const DilPart kv = x > 0 ? ord[x - 1] : none;
+    const DilPart q = x < n ? ord[x] : none;
+    const int64_t gkv = x > 0 ? grid_of(kv) : 0, gq = x < n ? grid_of(q) : 0;
+    hipLaunchKernelGGL(bwd_dil_mfma_kernel, dim3((uint32_t)(gkv + gq)), dim3(TT::kThreads), 0,
+                       stream, a, kv, gkv, q);
   }
   return hipGetLastError();
 }
