@@ -940,12 +940,12 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, TT::Smem& s
 // LongNet mixture (bf16). The mixture is one softmax over the multiset of the
 // patterns' keys (LongNet page, §3.4 "Mixture of Dilated Attentions"), so with
 // the mixture's lse each pattern contributes its own pairs' terms and a pair
-// kept by several patterns adds once per pattern. One launch per pattern and
-// gradient adds that pattern's terms into dQ (or dK, dV): every kept row (or
-// key) belongs to one workgroup of a launch, so the sums are deterministic. A
-// pattern of dilation 1 keeps every row and key: when there is one it goes
-// first and stores its terms; otherwise zeros are written first (rows no
-// pattern keeps keep them).
+// kept by several patterns adds once per pattern. A pattern's dQ workgroups
+// (or dK/dV workgroups) add its terms into dQ (or dK, dV), every kept row (or
+// key) in one workgroup, and each gradient takes the patterns one launch after
+// another, so the sums are deterministic. A pattern of dilation 1 keeps every
+// row and key: when there is one it goes first and stores its terms;
+// otherwise zeros are written first (rows no pattern keeps keep them).
 // ---------------------------------------------------------------------------
 
 // The pattern's segment geometry for head h (as the forward's dilated_tile):
