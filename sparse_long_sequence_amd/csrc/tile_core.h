@@ -46,6 +46,10 @@ constexpr int kTK = 64;       // keys per key tile
 constexpr int kD = 64;        // head dimension
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// The running max of a row before any allowed key: far below any real
+// score (log2 units), so that the first allowed key always moves it and keys
+// masked to -inf give p = 0 against it, without tests for -inf.
+constexpr float kMFloor = -1e30f;
 constexpr float kInvScale = 8.0f;  // sqrt(kD): the bias table is stored in q.k units
 constexpr int kGMaskWords = 256;   // LDS bitmap of global positions: 8192 key rows
 constexpr int32_t kFar = 0x3fffffff;
@@ -430,7 +434,7 @@ struct TileTraits<bf16> {
     const f32x16 zf = {};
     w.o[0] = zf;
     w.o[1] = zf;
-    w.m[0] = kNegInf;
+    w.m[0] = kMFloor;
     w.l[0] = 0.f;
   }
 
@@ -559,8 +563,8 @@ struct TileTraits<bf16> {
       const float mb = xs[(wave * 2 + 0) * 64 + lane], lb = xs[(wave * 2 + 1) * 64 + lane];
       const float ma = w.m[0];
       const float m = fmaxf(ma, mb);
-      const float sa = ma == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ma - m);
-      const float sb = mb == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mb - m);
+      const float sa = __builtin_amdgcn_exp2f(ma - m);  // 0 for a side at the floor
+      const float sb = __builtin_amdgcn_exp2f(mb - m);
 #pragma unroll
       for (int e = 0; e < 32; ++e)
         w.o[e >> 4][e & 15] = w.o[e >> 4][e & 15] * sa + xo[(wave * 32 + e) * 64 + lane] * sb;
@@ -718,7 +722,7 @@ struct TileTraits<float> {
     for (int x = 0; x < 16; ++x) w.qf[x] = src[x];
     const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < 4; ++i) w.o[i] = zf;
-    w.m[0] = kNegInf;
+    w.m[0] = kMFloor;
     w.l[0] = 0.f;
   }
 
@@ -1069,18 +1073,20 @@ __device__ __forceinline__ void sub_update(const typename TileTraits<T>::Smem& s
 #pragma unroll
   for (int r = 1; r < TT::kNS; ++r) mx = fmaxf(mx, s[r]);
   if constexpr (ADD) mx += badd;
-  const float mt = TT::row_max(mx) * scale_log2;  // sub-tile max, log2 units (-inf if all masked)
+  const float mxr = TT::row_max(mx);  // sub-tile max, q.k units (-inf if all masked)
   const float m_old = w.m[0];
-  const bool up = mt > m_old + kRescaleSlack;
+  // the running max moves when the sub-tile's exceeds it by the slack
+  const bool up = __builtin_fmaf(mxr, scale_log2, -m_old) > kRescaleSlack;
   if (__ballot(up) != 0ull) {
-    const float alpha = !up ? 1.f : (m_old == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_old - mt));
+    const float mt = mxr * scale_log2;  // log2 units
+    const float alpha = !up ? 1.f : __builtin_amdgcn_exp2f(m_old - mt);  // 0 from the floor
     w.m[0] = up ? mt : m_old;
     w.l[0] *= alpha;
     TT::scale_acc(w, alpha);
   }
-  // A row with every key masked so far keeps m = -inf; shift by 0 then.
-  const float m_cur = w.m[0];
-  float nm = (m_cur == kNegInf) ? 0.f : -m_cur;
+  // A row with no allowed key so far keeps the floor: its keys here are all
+  // masked (-inf), and p = 2^-inf = 0.
+  float nm = -w.m[0];
   if constexpr (ADD) nm += badd * scale_log2;
   typename TT::PTile P;
   TT::softmax_p(s, nm, scale_log2, P, w.l[0]);
