@@ -319,8 +319,9 @@ def copy_probe(dev, reps=3):
 def bench_backward(dev, args):
     """Backward calls, timed like the forward: the Longformer-base band + global
     backward (dq, dk, dv and the separate global projections' gradients), the
-    LongNet mixture's backward and the ETC shape's (with its bias table). Useful work: 10*D FLOPs per allowed pair
-    (q.k and dO.v recomputed, then dV, dQ and dK, 2*D each)."""
+    LongNet mixture's backward, the ETC shape's (with its bias table) and the
+    packed-documents one (segment masks). Useful work: 10*D FLOPs per allowed
+    pair (q.k and dO.v recomputed, then dV, dQ and dK, 2*D each)."""
     import torch
 
     import sparse_long_sequence_amd as la
@@ -328,7 +329,8 @@ def bench_backward(dev, args):
     from sparse_long_sequence_amd import workloads as W
 
     res = {}
-    for w in (W.LONGFORMER_BASE, W.LONGNET_SHARE, W.WORKLOADS["etc-ng256-nl4096-r84-relk12"]):
+    for w in (W.LONGFORMER_BASE, W.LONGNET_SHARE, W.WORKLOADS["etc-ng256-nl4096-r84-relk12"],
+              W.PACKED):
         log(f"bench backward: {w.name}")
         c = Call(w, dev)
         c()
@@ -341,7 +343,7 @@ def bench_backward(dev, args):
         else:
             call = la.bind_attn_backward(c.q, c.k, c.v, c.out, c.lse, dout, c.g, w.radius,
                                          w.dilation, w.causal, qg=c.qg, kg=c.kg, vg=c.vg,
-                                         rel_bias=c.rb, rel_vec=c.rv)
+                                         rel_bias=c.rb, rel_vec=c.rv, seg_ids=c.seg)
         steps = max(3, min(args.steps, 20))
         region_ms, mean_ms, med_ms, _ = time_calls(call, steps, min(args.warmup, 3), args.settle,
                                                    cold=False)
@@ -374,7 +376,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 256 MiB device copy (counter scaling under rocprofv3)")
     ap.add_argument("--backward", action="store_true",
-                    help="time the two backward calls instead of the forward workloads")
+                    help="time the backward calls instead of the forward workloads")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

@@ -139,8 +139,9 @@ la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, co
   a.scale_log2 = (float)(1.0 / sqrt((double)kDHead) * 1.4426950408889634);
   a.glob_chunks = 1;
   // the MFMA path: bf16 with at most the scalar bias table of 2k+1 distance
-  // labels (no key vectors, labels or segment ids)
-  if (dims->dtype == LA_BF16 && !a.rel_vec && !a.glabel && !a.llabel && !a.seg &&
+  // labels and segment ids that mask every pair (no key vectors or labels)
+  if (dims->dtype == LA_BF16 && !a.rel_vec && !a.glabel && !a.llabel &&
+      (!a.seg || a.seg_pieces == 15) &&
       (!a.rel_bias || a.n_labels == 2 * rel_k + 1)) {
     const int32_t tq = la::host_query_tile(dims->dtype);
     int32_t tiles = 0;

@@ -148,12 +148,60 @@ __device__ __forceinline__ BiasRule bias_rule(const BwdArgs& a, TT::Smem& sm, in
   return {sm.bias, a.rel_k, lane_is_global_kind, 0};
 }
 
+// Per-instance segment masks (packed documents; ETC page, §3.4 "Per-instance
+// attention masks"): a pair is kept only when its row and key lie in the same
+// segment. gi takes the batch row's segment ids, this lane's row (or key) id
+// and the min / max over the wave (every lane of the wave takes part).
+template <bool SEG>
+__device__ __forceinline__ void seg_info(GlobInfo& gi, const BwdArgs& a, int32_t bh, int32_t pos) {
+  if constexpr (SEG) {
+    if (a.seg) {
+      gi.segb = a.seg + (size_t)(bh / a.H) * a.N;
+      gi.sq = gi.segb[pos];
+      gi.sq_min = wave_min(gi.sq);
+      gi.sq_max = wave_max(gi.sq);
+    }
+  }
+}
+
+// A staged tile against the wave's segments: 0 no pair kept, 1 every pair
+// kept as far as segments go, 2 a per-element check.
+template <int32_t BUF>
+__device__ __forceinline__ int32_t seg_tile(const TT::Smem& sm, const GlobInfo& gi,
+                                            const KeyTile& kt) {
+  if (!gi.segb || kt.count <= 0) return 1;
+  const int32_t kmn = __builtin_amdgcn_readfirstlane(sm.segr[BUF][0]);
+  const int32_t kmx = __builtin_amdgcn_readfirstlane(sm.segr[BUF][1]);
+  if (kmx < gi.sq_min || kmn > gi.sq_max) return 0;
+  return (kmn == kmx && gi.sq_min == gi.sq_max && kmn == gi.sq_min) ? 1 : 2;
+}
+
+// The pairs of sub-tile sb whose staged entry lies in another segment than
+// sq (this lane's row or key) are excluded.
+template <int32_t BUF>
+__device__ __forceinline__ void seg_mask(float* s, const TT::Smem& sm, int32_t sq, int sb,
+                                         int32_t lane) {
+  int32_t kl = TT::key_lane(lane);
+  asm("" : "+v"(kl));  // opaque per call, as in mask_tile
+#pragma unroll
+  for (int r = 0; r < TT::kNS; ++r)
+    s[r] = sm.kseg[BUF][TT::key_const(sb, r) + kl] == sq ? s[r] : kNegInf;
+}
+
 // One staged key tile into dQ^T. The forward's block classes decide which
-// sub-tiles run and which need the per-element mask.
-template <int32_t BUF, bool BIAS>
+// sub-tiles run and which need the per-element mask. SEG: segment masks from
+// gs (a tile of other segments only is skipped).
+template <int32_t BUF, bool BIAS, bool SEG = false>
 __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t lane,
                                         const MaskRule& mr, const KeyTile& kt, int32_t qi,
-                                        int32_t qpos, bool dead, float c, const BiasRule& br) {
+                                        int32_t qpos, bool dead, float c, const BiasRule& br,
+                                        const GlobInfo& gs) {
+  bool seg_check = false;
+  if constexpr (SEG) {
+    const int32_t st = seg_tile<BUF>(sm, gs, kt);
+    if (st == 0) return;
+    seg_check = st == 2;
+  }
   const int32_t r0 = (mr.use_qpos ? __builtin_amdgcn_readlane(qpos, 0)
                                   : __builtin_amdgcn_readlane(qi, 0)) + mr.ref_off;
   const int32_t r1 = (mr.use_qpos ? __builtin_amdgcn_readlane(qpos, TT::kRowsPerBlock - 1)
@@ -171,6 +219,7 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
       if (tb.on) add_bias<bf16>(s, sm, BUF, br, sb, qi, qpos, lane, tb.same);
     }
     if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, qi, qpos, lane);
+    if (SEG && seg_check) seg_mask<BUF>(s, sm, gs.sq, sb, lane);
     TT::PTile G;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -187,9 +236,9 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
 }
 
 // The forward's tile loop (fetch next, compute current, stage, barrier) with
-// `proc(buf_tag, kt, mr)` as the per-tile work; no bias, segment or label
-// state.
-template <bool GATHER, typename Desc, typename Proc>
+// `proc(buf_tag, kt, mr)` as the per-tile work; no bias or label state. SEG:
+// the staged keys' segment ids and their range, when gi has them.
+template <bool GATHER, bool SEG = false, typename Desc, typename Proc>
 __device__ __forceinline__ void stream_tiles(TT::Smem& sm, const bf16* kb, const bf16* vb,
                                              int32_t n_tiles, Desc desc, const GlobInfo& gi,
                                              Proc proc) {
@@ -203,7 +252,7 @@ __device__ __forceinline__ void stream_tiles(TT::Smem& sm, const bf16* kb, const
   const FetchPlan fp = TT::plan(kt.stride, tid);
   TT::template fetch<GATHER>(pf, sm, 0, kb, vb, kt, fp, tid);
   TT::stage(sm, 0, pf, tid);
-  stage_meta<bf16, false, false>(sm, 0, pf.meta, gi, nolab, kt.gmode, tid);
+  stage_meta<bf16, SEG, false>(sm, 0, pf.meta, gi, nolab, kt.gmode, tid);
   __syncthreads();
   auto step = [&](auto buf_tag, int32_t n) {
     constexpr int32_t buf = decltype(buf_tag)::value;
@@ -217,7 +266,7 @@ __device__ __forceinline__ void stream_tiles(TT::Smem& sm, const bf16* kb, const
     proc(buf_tag, kt, mr);
     if (more) {
       TT::stage(sm, buf ^ 1, pf, tid);
-      stage_meta<bf16, false, false>(sm, buf ^ 1, pf.meta, gi, nolab, kt_next.gmode, tid);
+      stage_meta<bf16, SEG, false>(sm, buf ^ 1, pf.meta, gi, nolab, kt_next.gmode, tid);
       kt = kt_next;
       mr = mr_next;
     }
@@ -244,7 +293,7 @@ __device__ __forceinline__ bool qi_is_global(const BwdArgs& a, int32_t qi, int32
 
 // dQ of the non-global rows of one query tile (the forward's band workgroup:
 // window tiles, then the global keys outside the window).
-template <bool BIAS>
+template <bool BIAS, bool SEG>
 __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t bw) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -294,6 +343,7 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
   const int32_t hi = a.causal ? (t0 + qcount - 1) : min(n_c - 1, t0 + qcount - 1 + R);
   const int32_t n_band = (hi - lo + 1 + kTK - 1) / kTK;
   GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
+  seg_info<SEG>(gi, a, bh, qpos);
   BiasRule br = {nullptr, 0, 0, 0};
   if constexpr (BIAS) {
     // the window keys' global flags decide which pairs are same-kind
@@ -310,7 +360,7 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
   const int32_t gkeys = BIAS ? kGlobAll : kGlobNone;  // mode of the global-key tiles
   auto proc = [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
     constexpr int32_t buf = decltype(buf_tag)::value;
-    dq_tile<buf, BIAS>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2, br);
+    dq_tile<buf, BIAS, SEG>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2, br, gi);
   };
   auto band_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = lo + n * kTK;
@@ -342,9 +392,9 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
                            (!a.causal || gh <= i_lo);
       mr = {kOutside, all_out ? 0 : 1, 1, -gl, -R, a.causal ? kFar : R, 0, 0, 1};
     };
-    stream_tiles<false>(sm, kb, vb, n_band + n_gt, desc, gi, proc);
+    stream_tiles<false, SEG>(sm, kb, vb, n_band + n_gt, desc, gi, proc);
   } else {
-    stream_tiles<false>(sm, kb, vb, n_band, band_desc, gi, proc);
+    stream_tiles<false, SEG>(sm, kb, vb, n_band, band_desc, gi, proc);
   }
   if (ng > 0 && !g_run) {
     const int32_t n_gt = (ng + kTK - 1) / kTK;
@@ -377,7 +427,7 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
       const bool full = kcount == kTK && outside && causal_ok;
       mr = {kGlobCol, full ? 0 : 1, 0, 0, 0, 0, a.causal, R, d};
     };
-    stream_tiles<true>(sm, kb, vb, n_glob, glob_desc, gi, proc);
+    stream_tiles<true, SEG>(sm, kb, vb, n_glob, glob_desc, gi, proc);
   }
 
   // non-global rows: dQ (and, with separate projections, a zero dQ_g row),
@@ -416,21 +466,21 @@ struct DkvWave {
   f32x16 dv[2];
 };
 
-// A streamed tile's per-row lse (times lse_mul: 1 / scale gives score units,
-// the raw q.k at which P = 1; log2 e gives log2 units; +inf for a row without
-// keys) and D_i sit in LDS next to its Q and dO rows (in the key-id and rank
-// arrays, which this pass does not use otherwise).
-__device__ __forceinline__ float* row_lse(TT::Smem& sm, int32_t buf) {
-  return reinterpret_cast<float*>(&sm.kseg[buf][0]);
+// The backward's LDS: the engine's tile buffers and, for the dK/dV pass, each
+// staged row tile's lse (times lse_mul: 1 / scale gives score units, the raw
+// q.k at which P = 1; log2 e gives log2 units; +inf for a row without keys)
+// and D_i.
+struct BwdSmem : TT::Smem {
+  alignas(16) float rlse[2][kTK];
+  alignas(16) float rdi[2][kTK];
+};
+__device__ __forceinline__ float* row_lse(BwdSmem& sm, int32_t buf) { return &sm.rlse[buf][0]; }
+__device__ __forceinline__ float* row_di(BwdSmem& sm, int32_t buf) { return &sm.rdi[buf][0]; }
+__device__ __forceinline__ const float* row_lse(const BwdSmem& sm, int32_t buf) {
+  return &sm.rlse[buf][0];
 }
-__device__ __forceinline__ float* row_di(TT::Smem& sm, int32_t buf) {
-  return reinterpret_cast<float*>(&sm.kgrank[buf][0]);
-}
-__device__ __forceinline__ const float* row_lse(const TT::Smem& sm, int32_t buf) {
-  return reinterpret_cast<const float*>(&sm.kseg[buf][0]);
-}
-__device__ __forceinline__ const float* row_di(const TT::Smem& sm, int32_t buf) {
-  return reinterpret_cast<const float*>(&sm.kgrank[buf][0]);
+__device__ __forceinline__ const float* row_di(const BwdSmem& sm, int32_t buf) {
+  return &sm.rdi[buf][0];
 }
 
 // One streamed tile of query rows into dK^T, dV^T. EXCL_G: rows that are
@@ -446,13 +496,21 @@ __device__ __forceinline__ const float* row_di(const TT::Smem& sm, int32_t buf) 
 // forward's softmax); it pays in the LongNet sweeps (the (2048, 1) pattern's
 // dK/dV launch runs about 11% faster) and costs about 1% in the band ones.
 // BIAS: the scalar bias table (br: the flipped table, key_global_is_same_kind
-// = the lane's key is global).
+// = the lane's key is global). SEG: segment masks from gs (the lane's key's
+// segment against the staged rows').
 template <int32_t BUF, bool EXCL_G, bool ROWS_AFTER, bool INIT, bool PRIO = false,
-          bool BIAS = false>
-__device__ __forceinline__ void dkv_tile(const TT::Smem& sm, DkvWave& w, int32_t lane,
+          bool BIAS = false, bool SEG = false>
+__device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t lane,
                                          const MaskRule& mr, const KeyTile& kt, int32_t ki,
                                          int32_t kpos, bool dead, float c, bool causal,
-                                         const BiasRule& br = {nullptr, 0, 0, 0}) {
+                                         const BiasRule& br = {nullptr, 0, 0, 0},
+                                         const GlobInfo& gs = {}) {
+  bool seg_check = false;
+  if constexpr (SEG) {
+    const int32_t st = seg_tile<BUF>(sm, gs, kt);
+    if (st == 0) return;
+    seg_check = st == 2;
+  }
   const int32_t r0 = (mr.use_qpos ? __builtin_amdgcn_readlane(kpos, 0)
                                   : __builtin_amdgcn_readlane(ki, 0)) + mr.ref_off;
   const int32_t r1 = (mr.use_qpos ? __builtin_amdgcn_readlane(kpos, TT::kRowsPerBlock - 1)
@@ -489,6 +547,7 @@ __device__ __forceinline__ void dkv_tile(const TT::Smem& sm, DkvWave& w, int32_t
       if (tb.on) add_bias<bf16>(s, sm, BUF, br, sb, ki, kpos, lane, tb.same);
     }
     if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, ki, kpos, lane);
+    if (SEG && seg_check) seg_mask<BUF>(s, sm, gs.sq, sb, lane);
     if (EXCL_G && any_g) {
 #pragma unroll
       for (int r = 0; r < TT::kNS; ++r)
@@ -532,9 +591,9 @@ __device__ __forceinline__ void dkv_tile(const TT::Smem& sm, DkvWave& w, int32_t
 
 // stream_tiles for query rows: as stream_tiles, and each staged tile's rows'
 // lse (times lse_mul) and D_i, read with the tile's loads, written to LDS
-// with its staging.
-template <bool GATHER, typename Desc, typename Proc>
-__device__ __forceinline__ void stream_rows(TT::Smem& sm, const bf16* qb, const bf16* dob,
+// with its staging (SEG: the rows' segment ids are staged as the keys' are).
+template <bool GATHER, bool SEG = false, typename Desc, typename Proc>
+__device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const bf16* dob,
                                             const float* lse, const float* delta, float lse_mul,
                                             int32_t n_tiles, Desc desc, const GlobInfo& gi,
                                             Proc proc) {
@@ -564,7 +623,7 @@ __device__ __forceinline__ void stream_rows(TT::Smem& sm, const bf16* qb, const 
   TT::template fetch<GATHER>(pf, sm, 0, qb, dob, kt, fp, tid);
   row_vals(kt);
   TT::stage(sm, 0, pf, tid);
-  stage_meta<bf16, false, false>(sm, 0, pf.meta, gi, nolab, kt.gmode, tid);
+  stage_meta<bf16, SEG, false>(sm, 0, pf.meta, gi, nolab, kt.gmode, tid);
   put_rows(0);
   __syncthreads();
   auto step = [&](auto buf_tag, int32_t n) {
@@ -580,7 +639,7 @@ __device__ __forceinline__ void stream_rows(TT::Smem& sm, const bf16* qb, const 
     proc(buf_tag, kt, mr);
     if (more) {
       TT::stage(sm, buf ^ 1, pf, tid);
-      stage_meta<bf16, false, false>(sm, buf ^ 1, pf.meta, gi, nolab, kt_next.gmode, tid);
+      stage_meta<bf16, SEG, false>(sm, buf ^ 1, pf.meta, gi, nolab, kt_next.gmode, tid);
       put_rows(buf ^ 1);
       kt = kt_next;
       mr = mr_next;
@@ -611,8 +670,8 @@ __device__ __forceinline__ void store_rows_f32(float* dst, const f32x16 (&acc)[2
 
 // dK, dV of the non-global keys of one key tile (a residue class of the
 // head's dilation, like the forward's query tiles).
-template <bool BIAS>
-__device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t bw) {
+template <bool BIAS, bool SEG>
+__device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm, int32_t bw) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t N = a.N;
@@ -662,6 +721,7 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& s
   const int32_t n_band = (hi - lo + 1 + kTK - 1) / kTK;
   const int32_t lob = a.causal ? 0 : -R;
   GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
+  seg_info<SEG>(gi, a, bh, kpos);
   if (ng > 0) {  // the rows' global flags: global rows come in their own sweep
     if (hi - lo + 1 <= 32 * kGMaskWords) {
       build_gmask<bf16>(sm, a.gidx, ng, c + d * lo, d, hi - lo + 1, tid);
@@ -683,16 +743,17 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& s
     mr = {kRange, full ? 0 : 1, 0, t0 - u0, lob, R, 0, 0, 1};
   };
   const bf16* qs = static_cast<const bf16*>(a.q) + bh * head_elems;
-  stream_rows<false>(sm, qs, dob, lse, delta, 1.f / a.scale, n_band, band_desc, gi,
-                     [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                       constexpr int32_t buf = decltype(buf_tag)::value;
-                       dkv_tile<buf, true, false, true, false, BIAS>(
-                           sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br);
-                     });
+  stream_rows<false, SEG>(sm, qs, dob, lse, delta, 1.f / a.scale, n_band, band_desc, gi,
+                          [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                            constexpr int32_t buf = decltype(buf_tag)::value;
+                            dkv_tile<buf, true, false, true, false, BIAS, SEG>(
+                                sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br,
+                                gi);
+                          });
   // the global rows reach every key (causal: rows at or after it)
   const int32_t n_gt = (ng + kTK - 1) / kTK;
   const int32_t grows = BIAS ? kGlobAll : kGlobNone;  // mode of the global-row tiles
-  const GlobInfo gall = {grows, a.gidx, ng, nullptr, 0, 0, 0};
+  const GlobInfo gall = {grows, a.gidx, ng, gi.segb, gi.sq, gi.sq_min, gi.sq_max};
   auto glob_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t cnt = min(kTK, ng - n * kTK);
     kt = {a.gidx + n * kTK, 0, 1, cnt, 0, grows};
@@ -701,8 +762,8 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& s
   };
   auto glob_proc = [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
     constexpr int32_t buf = decltype(buf_tag)::value;
-    dkv_tile<buf, false, true, true, false, BIAS>(sm, w, lane, mr, kt, ki, kpos, dead,
-                                                  a.scale_log2, a.causal, br);
+    dkv_tile<buf, false, true, true, false, BIAS, SEG>(sm, w, lane, mr, kt, ki, kpos, dead,
+                                                       a.scale_log2, a.causal, br, gall);
   };
   const bool mine = ki < kcount && !qi_is_global(a, ki, kcount, kpos, g_first, g_last, j_lo, j_hi);
   if (a.sep) {
@@ -721,8 +782,8 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, TT::Smem& s
     }
   }
   if (ng > 0)
-    stream_rows<true>(sm, static_cast<const bf16*>(a.sep ? a.qg : a.q) + bh * head_elems, dob,
-                      lse, delta, 1.f / a.scale, n_gt, glob_desc, gall, glob_proc);
+    stream_rows<true, SEG>(sm, static_cast<const bf16*>(a.sep ? a.qg : a.q) + bh * head_elems,
+                           dob, lse, delta, 1.f / a.scale, n_gt, glob_desc, gall, glob_proc);
   if (mine) {
     float* const dk = a.sep ? a.dkg : a.dk;
     float* const dv = a.sep ? a.dvg : a.dv;
@@ -756,7 +817,7 @@ __device__ __forceinline__ float* part_row(const BwdArgs& a, int32_t part, int32
 }
 
 // Workgroup wg of the B*H*ceil(n_global/128)*glob_chunks global-row ones.
-template <bool BIAS>
+template <bool BIAS, bool SEG>
 __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t wg) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -786,6 +847,7 @@ __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm
   int32_t t0, n_tiles;
   chunk_range((j1 + kTK - 1) / kTK, chunks, c, t0, n_tiles);
   GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
+  seg_info<SEG>(gi, a, bh, qpos);
   BiasRule br = {nullptr, 0, 0, 0};
   if constexpr (BIAS) {
     // the keys' global flags decide which pairs are same-kind (global keys)
@@ -808,12 +870,13 @@ __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm
     const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= i_min);
     mr = {kRange, full ? 0 : 1, 1, -u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
   };
-  stream_tiles<false>(sm, static_cast<const bf16*>(sep ? a.kg : a.k) + bh * head_elems,
-                      static_cast<const bf16*>(sep ? a.vg : a.v) + bh * head_elems, n_tiles, desc,
-                      gi, [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                        constexpr int32_t buf = decltype(buf_tag)::value;
-                        dq_tile<buf, BIAS>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2, br);
-                      });
+  stream_tiles<false, SEG>(sm, static_cast<const bf16*>(sep ? a.kg : a.k) + bh * head_elems,
+                           static_cast<const bf16*>(sep ? a.vg : a.v) + bh * head_elems, n_tiles,
+                           desc, gi, [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                             constexpr int32_t buf = decltype(buf_tag)::value;
+                             dq_tile<buf, BIAS, SEG>(sm, w, lane, mr, kt, qi, qpos, dead,
+                                                     a.scale_log2, br, gi);
+                           });
   if (qi < qcount && chunks > 1) {
     store_rows_f32(part_row(a, 0, c, bh, gq * kTQ + qi), w.acc, 1.f, lane);
   } else if (qi < qcount) {
@@ -827,8 +890,8 @@ __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm
 }
 
 // Workgroup wg of the B*H*ceil(n_global/128)*glob_chunks global-key ones.
-template <bool BIAS>
-__device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t wg) {
+template <bool BIAS, bool SEG>
+__device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, BwdSmem& sm, int32_t wg) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t n_gk = (a.n_global + kTQ - 1) / kTQ;
@@ -862,6 +925,7 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, TT::Smem& s
   chunk_range((N - r0 + kTK - 1) / kTK, chunks, c, t0, n_tiles);
   const int32_t ub = r0 + t0 * kTK, ue = min(N, ub + n_tiles * kTK);
   GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
+  seg_info<SEG>(gi, a, bh, kpos);
   BiasRule br = {nullptr, 0, 0, 0};
   if constexpr (BIAS) br = bias_rule(a, sm, bh % a.H, true, 1);  // lanes hold global keys
   // the rows' global flags: excluded with separate projections; with a bias
@@ -884,19 +948,21 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, TT::Smem& s
   };
   const bf16* qs = static_cast<const bf16*>(a.q) + bh * head_elems;
   if (sep)
-    stream_rows<false>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
-                       [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                         constexpr int32_t buf = decltype(buf_tag)::value;
-                         dkv_tile<buf, true, false, true, false, BIAS>(
-                             sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br);
-                       });
+    stream_rows<false, SEG>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
+                            [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                              constexpr int32_t buf = decltype(buf_tag)::value;
+                              dkv_tile<buf, true, false, true, false, BIAS, SEG>(
+                                  sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal,
+                                  br, gi);
+                            });
   else
-    stream_rows<false>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
-                       [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                         constexpr int32_t buf = decltype(buf_tag)::value;
-                         dkv_tile<buf, false, false, true, false, BIAS>(
-                             sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br);
-                       });
+    stream_rows<false, SEG>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
+                            [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                              constexpr int32_t buf = decltype(buf_tag)::value;
+                              dkv_tile<buf, false, false, true, false, BIAS, SEG>(
+                                  sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal,
+                                  br, gi);
+                            });
   const size_t ro = ((size_t)bh * N + kpos) * kD;
   if (ki < kcount && chunks > 1) {
     store_rows_f32(part_row(a, 1, c, bh, gk * kTQ + ki), w.dk, 1.f, lane);
@@ -922,14 +988,15 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, TT::Smem& s
     kt = {a.gidx + n * kTK, 0, 1, cnt, 0, grows};
     mr = {kRange, cnt == kTK ? 0 : 1, 0, 0, -kFar, kFar, 0, 0, 1};
   };
-  const GlobInfo gall = {grows, a.gidx, a.n_global, nullptr, 0, 0, 0};
-  stream_rows<true>(sm, static_cast<const bf16*>(a.qg) + bh * head_elems, dob, lse, delta,
-                    1.f / a.scale, n_gt,
-                    glob_desc, gall, [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                      constexpr int32_t buf = decltype(buf_tag)::value;
-                      dkv_tile<buf, false, true, true, false, BIAS>(
-                          sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br);
-                    });
+  const GlobInfo gall = {grows, a.gidx, a.n_global, gi.segb, gi.sq, gi.sq_min, gi.sq_max};
+  stream_rows<true, SEG>(sm, static_cast<const bf16*>(a.qg) + bh * head_elems, dob, lse, delta,
+                         1.f / a.scale, n_gt, glob_desc, gall,
+                         [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                           constexpr int32_t buf = decltype(buf_tag)::value;
+                           dkv_tile<buf, false, true, true, false, BIAS, SEG>(
+                               sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br,
+                               gall);
+                         });
   if (ki < kcount) {
     store_rows_f32(a.dkg + ro, w.dk, a.scale, lane);
     store_rows_f32(a.dvg + ro, w.dv, 1.f, lane);
@@ -1037,7 +1104,7 @@ __device__ __forceinline__ void dq_dil_workgroup(const BwdArgs& a, TT::Smem& sm,
                       [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                         constexpr int32_t buf = decltype(buf_tag)::value;
                         dq_tile<buf, false>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2,
-                                            BiasRule{nullptr, 0, 0, 0});
+                                            BiasRule{nullptr, 0, 0, 0}, gi);
                       });
   if (qi < qcount) {
     float* dst = a.dq + ((size_t)bh * a.N + qpos) * kD;
@@ -1048,7 +1115,7 @@ __device__ __forceinline__ void dq_dil_workgroup(const BwdArgs& a, TT::Smem& sm,
   }
 }
 
-__device__ __forceinline__ void dkv_dil_workgroup(const BwdArgs& a, TT::Smem& sm,
+__device__ __forceinline__ void dkv_dil_workgroup(const BwdArgs& a, BwdSmem& sm,
                                                   const DilPart& p, int64_t wg) {
   const int32_t k = p.k, nseg = p.nseg, qtiles = p.qtiles, store = p.store;
   constexpr int32_t kTQ = TT::kTQ;
@@ -1127,35 +1194,36 @@ __device__ __forceinline__ int32_t band_tile_of(const BwdArgs& a, int32_t b) {
 
 // Two fragments per row (Q and dO) and two dot products per pair need more
 // registers than the forward: 3 waves per SIMD.
-// BIAS: with the forward's scalar bias table (a separate instantiation, so
-// that the kernels without one are built as before).
-template <bool BIAS>
+// BIAS: with the forward's scalar bias table, SEG: with segment masks
+// (separate instantiations, so that the kernels without them are built as
+// before).
+template <bool BIAS, bool SEG>
 __global__ __launch_bounds__(TT::kThreads)
 __attribute__((amdgpu_waves_per_eu(3)))
 void bwd_dq_mfma_kernel(BwdArgs a) {
   __shared__ TT::Smem sm;
   const int32_t b = (int32_t)blockIdx.x, gw = glob_wg_padded(a);
   if (b < gw) {
-    if (b < glob_wg(a)) dq_glob_workgroup<BIAS>(a, sm, b);
+    if (b < glob_wg(a)) dq_glob_workgroup<BIAS, SEG>(a, sm, b);
     return;
   }
   const int32_t bw = band_tile_of(a, b - gw);
-  if (bw >= 0) dq_band_workgroup<BIAS>(a, sm, bw);
+  if (bw >= 0) dq_band_workgroup<BIAS, SEG>(a, sm, bw);
 }
 
 // (the table's per-element work needs the registers of 2 waves per SIMD)
-template <bool BIAS>
+template <bool BIAS, bool SEG>
 __global__ __launch_bounds__(TT::kThreads)
 __attribute__((amdgpu_waves_per_eu(BIAS ? 2 : 3)))
 void bwd_dkv_mfma_kernel(BwdArgs a) {
-  __shared__ TT::Smem sm;
+  __shared__ BwdSmem sm;
   const int32_t b = (int32_t)blockIdx.x, gw = glob_wg_padded(a);
   if (b < gw) {
-    if (b < glob_wg(a)) dkv_glob_workgroup<BIAS>(a, sm, b);
+    if (b < glob_wg(a)) dkv_glob_workgroup<BIAS, SEG>(a, sm, b);
     return;
   }
   const int32_t bw = band_tile_of(a, b - gw);
-  if (bw >= 0) dkv_band_workgroup<BIAS>(a, sm, bw);
+  if (bw >= 0) dkv_band_workgroup<BIAS, SEG>(a, sm, bw);
 }
 
 // The global rows' dQ and the global keys' dK, dV from the ranges' partial
@@ -1196,7 +1264,7 @@ __global__ __launch_bounds__(256) void bwd_glob_reduce_kernel(BwdArgs a) {
 __global__ __launch_bounds__(TT::kThreads)
 __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dil_mfma_kernel(BwdArgs a, DilPart kv, int64_t grid_kv, DilPart q) {
-  __shared__ TT::Smem sm;
+  __shared__ BwdSmem sm;
   const int64_t b = blockIdx.x;
   if (b < grid_kv)
     dkv_dil_workgroup(a, sm, kv, b);
@@ -1274,12 +1342,15 @@ hipError_t launch_dq_mfma(const BwdArgs& a, hipStream_t stream) {
   if (a.glob_chunks < 1 || (a.glob_chunks > 1 && !a.gpart)) return hipErrorInvalidValue;
   const int64_t grid = mfma_grid(a);
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (a.rel_bias)
-    hipLaunchKernelGGL(bwd_dq_mfma_kernel<true>, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
-                       stream, a);
+  const dim3 g((uint32_t)grid), t(TT::kThreads);
+  if (a.rel_bias && a.seg)
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<true, true>), g, t, 0, stream, a);
+  else if (a.rel_bias)
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<true, false>), g, t, 0, stream, a);
+  else if (a.seg)
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<false, true>), g, t, 0, stream, a);
   else
-    hipLaunchKernelGGL(bwd_dq_mfma_kernel<false>, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<false, false>), g, t, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1288,12 +1359,15 @@ hipError_t launch_dkv_mfma(const BwdArgs& a, hipStream_t stream) {
   if (a.glob_chunks < 1 || (a.glob_chunks > 1 && !a.gpart)) return hipErrorInvalidValue;
   const int64_t grid = mfma_grid(a);
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (a.rel_bias)
-    hipLaunchKernelGGL(bwd_dkv_mfma_kernel<true>, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
-                       stream, a);
+  const dim3 g((uint32_t)grid), t(TT::kThreads);
+  if (a.rel_bias && a.seg)
+    hipLaunchKernelGGL((bwd_dkv_mfma_kernel<true, true>), g, t, 0, stream, a);
+  else if (a.rel_bias)
+    hipLaunchKernelGGL((bwd_dkv_mfma_kernel<true, false>), g, t, 0, stream, a);
+  else if (a.seg)
+    hipLaunchKernelGGL((bwd_dkv_mfma_kernel<false, true>), g, t, 0, stream, a);
   else
-    hipLaunchKernelGGL(bwd_dkv_mfma_kernel<false>, dim3((uint32_t)grid), dim3(TT::kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((bwd_dkv_mfma_kernel<false, false>), g, t, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -52,11 +52,13 @@ def to64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def check(tag, dtype, got, ref, names=("dq", "dk", "dv", "dqg", "dkg", "dvg")):
+def check(tag, dtype, got, ref, names=("dq", "dk", "dv", "dqg", "dkg", "dvg"), floor=1e-30):
+    """floor: the least scale a tensor is held to (for tensors that are zero in
+    exact arithmetic, whose computed values are rounding noise)."""
     assert len(got) == len(ref)
     for name, g, r in zip(names, got, ref):
         g = g if isinstance(g, np.ndarray) else to64(g)
-        scale = max(np.abs(r).max(), 1e-30)
+        scale = max(np.abs(r).max(), floor)
         err = np.abs(g - r)
         bound = TOL_ABS[dtype] * scale + TOL_REL[dtype] * np.abs(r)
         assert np.isfinite(g).all(), f"{tag} {name}: non-finite"
@@ -66,7 +68,7 @@ def check(tag, dtype, got, ref, names=("dq", "dk", "dv", "dqg", "dkg", "dvg")):
 
 
 def run_case(dev, tag, dtype, B, H, N, glob, R, dil, causal, sep, seg_rows, seed,
-             inputs=None):
+             inputs=None, floor=1e-30):
     say(f"backward {tag}: {dtype} B={B} H={H} N={N} |G|={len(glob)} R={R} dil={dil} "
         f"causal={causal} sep={sep} seg={seg_rows}")
     gen = torch.Generator().manual_seed(seed)
@@ -78,9 +80,12 @@ def run_case(dev, tag, dtype, B, H, N, glob, R, dil, causal, sep, seg_rows, seed
     dout = rand(gen, (B, H, N, 64), dtype)
     seg = None
     if seg_rows:
-        # documents of the given lengths, one id each, per batch row
-        seg = torch.tensor(np.concatenate([np.full(n, x, np.int32) for x, n in enumerate(seg_rows)])
-                           )[None].repeat(B, 1)
+        # documents of the given lengths, one id each: the same for every batch
+        # row, or (a tuple of tuples) one layout per batch row
+        per_row = seg_rows if isinstance(seg_rows[0], tuple) else (seg_rows,) * B
+        seg = torch.tensor(np.stack([
+            np.concatenate([np.full(n, x, np.int32) for x, n in enumerate(lens)])
+            for lens in per_row]))
     d = lambda t: None if t is None else t.to(dev).contiguous()
     gidx = torch.tensor(sorted(glob), dtype=torch.int32, device=dev) if glob else None
     out, lse = la.la_attn_forward(d(q), d(k), d(v), gidx, R, dil, causal, qg=d(qg), kg=d(kg),
@@ -92,7 +97,7 @@ def run_case(dev, tag, dtype, B, H, N, glob, R, dil, causal, sep, seg_rows, seed
     ref = oracle.attn_backward(f64(q), f64(k), f64(v), f64(dout), tuple(glob), R, dil, causal,
                                f64(qg), f64(kg), f64(vg),
                                seg=None if seg is None else seg.numpy())
-    check(tag, dtype, grads, ref)
+    check(tag, dtype, grads, ref, floor=floor)
     return grads
 
 
@@ -117,6 +122,57 @@ def test_backward_small(dev, case):
     tag, dtype, B, H, N, glob, R, dil, causal, sep, seg = case
     run_case(dev, tag, dtype, B, H, N, glob, R, dil, causal, sep, seg,
              seed=300 + CASES.index(case))
+
+
+SEG_CASES = [
+    # per-instance segment masks (packed documents, every pair masked): tag, B,
+    # H, N, globals, R, dilation, causal, separate, documents (per row or shared)
+    ("seg-globals-in-documents-sep", 2, 2, 700, (0, 1, 300, 301, 650), 40, (1, 2), False, True,
+     ((300, 350, 50), (650, 50))),
+    ("seg-causal-dilated", 1, 3, 513, (0, 200, 512), 33, (1, 2, 3), True, False,
+     (1, 199, 250, 63)),
+    # a tile-aligned layout (every tile of one document) and one of single
+    # tokens: each row's only key is itself, so dS = 0 and dq = dk = 0 exactly
+    # (held to the bar at unit scale, the inputs' and dv's magnitude)
+    ("seg-aligned", 1, 2, 512, (0, 128, 256), 64, None, False, True, (128, 128, 256)),
+    ("seg-singletons", 1, 1, 200, (5,), 8, None, False, False, tuple([1] * 200)),
+    # the global tiles split over key (row) ranges
+    ("seg-ranges", 1, 2, 1500, (0, 700, 701, 1499), 32, None, False, True, (700, 800)),
+    ("seg-ranges-causal", 2, 2, 1300, tuple(range(0, 1300, 9)), 24, (1, 2), True, False,
+     ((640, 660), (100, 1100, 100))),
+]
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=[c[0] for c in SEG_CASES])
+def test_backward_segments(dev, case):
+    """Pairs whose row and key lie in different segments are masked (ETC page,
+    §3.4 "Per-instance attention masks"), for band, global-row and global-key
+    pairs alike."""
+    tag, B, H, N, G, R, dil, causal, sep, docs = case
+    run_case(dev, tag, "bf16", B, H, N, G, R, None if dil is None else list(dil), causal, sep,
+             docs, seed=600 + SEG_CASES.index(case),
+             floor=1.0 if tag == "seg-singletons" else 1e-30)
+
+
+def test_backward_segments_bias(dev):
+    """Segment masks together with the scalar bias table."""
+    w = W.Workload("seg-bias", B=2, H=2, N=900, radius=30, global_idx=(0, 1, 2, 450, 451),
+                   dilation=(1, 2), separate_global=True, rel_k=5, rel_kind="scalar", seed=611)
+    inp = W.make_inputs(w)
+    inp.seg = torch.tensor(np.stack([np.repeat(np.arange(3), (450, 300, 150)),
+                                     np.repeat(np.arange(2), (200, 700))]).astype(np.int32))
+    run_label_case(dev, "seg-bias", "bf16", w, inp, seed=613)
+
+
+def test_backward_packed(dev):
+    """The packed-documents shape (B=2, H=12, N=4096 holding four documents of
+    1024 tokens, R=256, the first 16 tokens of each document global with
+    separate projections), every element against the oracle."""
+    w = W.PACKED
+    inp = W.make_inputs(w)
+    run_case(dev, "packed", "bf16", w.B, w.H, w.N, w.global_idx, w.radius, None, w.causal, True,
+             tuple(w.documents), seed=w.seed,
+             inputs=(inp.q, inp.k, inp.v, inp.qg, inp.kg, inp.vg))
 
 
 def test_backward_deterministic(dev):
