@@ -261,11 +261,11 @@ typedef struct {
  * Requires ext->workspace (its contents on entry are ignored). Pointers 16-byte
  * aligned. Errors as for la_attn_forward. Two or three launches on `stream`
  * (bf16 with no label vectors or label matrices, at most the scalar table of
- * 2k+1 distance entries, and segment ids, if given, masking every piece: one
- * MFMA launch for dQ and D_i, one for dK and dV, the global rows and keys split
- * over up to 16 key or row ranges, and with several ranges one launch adding
- * their partial sums in a fixed order; otherwise global ranks, dQ and D_i, dK
- * and dV), no allocation; results are bitwise reproducible. */
+ * 2k+1 distance entries, and segment ids, if given, masking every piece: D_i,
+ * then one MFMA launch for dQ, dK and dV, the global rows and keys split over
+ * up to 16 key or row ranges, and with several ranges one launch adding their
+ * partial sums in a fixed order; otherwise global ranks, dQ and D_i, dK and
+ * dV), no allocation; results are bitwise reproducible. */
 la_status la_attn_backward(const la_dims *dims, const void *q, const void *k, const void *v,
                            const int32_t *global_idx, int32_t n_global, int32_t radius,
                            const int32_t *dilation, int32_t causal, const void *out,

@@ -592,11 +592,9 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) 
   if (rows <= 0) return hipSuccess;
   const dim3 g((uint32_t)((rows + kWavesBwd - 1) / kWavesBwd)), blk(64 * kWavesBwd);
   if (dtype == 1 && a.n_band_wg > 0) {
-    // dQ (its workgroups write D_i of their rows), then dK, dV on MFMA (which
-    // need no global ranks)
-    hipError_t e = launch_dq_mfma(a, stream);
-    if (e != hipSuccess) return e;
-    e = launch_dkv_mfma(a, stream);
+    // D_i, then dK/dV and dQ on MFMA in one launch (no global ranks needed)
+    hipLaunchKernelGGL(bwd_delta_kernel, dim3((uint32_t)((rows + 31) / 32)), dim3(256), 0, stream, a);
+    hipError_t e = launch_bwd_mfma(a, stream);
     if (e != hipSuccess) return e;
     e = launch_glob_reduce(a, stream);  // the global tiles' partial sums
     if (e != hipSuccess) return e;

@@ -334,7 +334,7 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
   load_frag(w.df, dob, qpos, lane);
   const float lse = a.lse[(size_t)bh * N + qpos];
   w.lse2 = lse == kNegInf ? -kNegInf : lse * kLog2e;
-  w.di = row_delta(w.df, static_cast<const bf16*>(a.out) + bh * head_elems, qpos, lane);
+  w.di = a.delta[(size_t)bh * N + qpos];  // D_i from the launch before
   w.acc[0] = f32x16{};
   w.acc[1] = f32x16{};
 
@@ -436,7 +436,6 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
     const bool is_g = g_first <= i_hi && g_last >= i_lo && sorted_contains(a.gidx, ng, qpos);
     if (!is_g) {
       const int32_t hh = lane >> 5;
-      if (hh == 0) a.delta[(size_t)bh * N + qpos] = w.di;
       float* dst = a.dq + ((size_t)bh * N + qpos) * kD;
       float* dsg = a.sep ? a.dqg + ((size_t)bh * N + qpos) * kD : nullptr;
 #pragma unroll
@@ -839,8 +838,7 @@ __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm
   load_frag(w.df, static_cast<const bf16*>(a.dout) + bh * head_elems, qpos, lane);
   const float lse = a.lse[(size_t)bh * N + qpos];
   w.lse2 = lse == kNegInf ? -kNegInf : lse * kLog2e;
-  w.di = row_delta(w.df, static_cast<const bf16*>(a.out) + bh * head_elems, qpos, lane);
-  if (c == 0 && qi < qcount && lane < 32) a.delta[(size_t)bh * N + qpos] = w.di;  // for dK/dV
+  w.di = a.delta[(size_t)bh * N + qpos];  // D_i from the launch before
   w.acc[0] = f32x16{};
   w.acc[1] = f32x16{};
   const int32_t j1 = a.causal ? i_max + 1 : N;
@@ -1192,38 +1190,35 @@ __device__ __forceinline__ int32_t band_tile_of(const BwdArgs& a, int32_t b) {
   return j >= per || bw >= a.n_band_wg ? -1 : bw;
 }
 
-// Two fragments per row (Q and dO) and two dot products per pair need more
-// registers than the forward: 3 waves per SIMD.
-// BIAS: with the forward's scalar bias table, SEG: with segment masks
-// (separate instantiations, so that the kernels without them are built as
-// before).
-template <bool BIAS, bool SEG>
-__global__ __launch_bounds__(TT::kThreads)
-__attribute__((amdgpu_waves_per_eu(3)))
-void bwd_dq_mfma_kernel(BwdArgs a) {
-  __shared__ TT::Smem sm;
-  const int32_t b = (int32_t)blockIdx.x, gw = glob_wg_padded(a);
-  if (b < gw) {
-    if (b < glob_wg(a)) dq_glob_workgroup<BIAS, SEG>(a, sm, b);
-    return;
-  }
-  const int32_t bw = band_tile_of(a, b - gw);
-  if (bw >= 0) dq_band_workgroup<BIAS, SEG>(a, sm, bw);
-}
-
-// (the table's per-element work needs the registers of 2 waves per SIMD)
+// dK/dV and dQ workgroups in one launch, the dK/dV ones (the longer work)
+// first: the two add into different gradients, and D_i came from a launch
+// before, so they run side by side and fill each other's tails.
 template <bool BIAS, bool SEG>
 __global__ __launch_bounds__(TT::kThreads)
 __attribute__((amdgpu_waves_per_eu(BIAS ? 2 : 3)))
-void bwd_dkv_mfma_kernel(BwdArgs a) {
+void bwd_mfma_kernel(BwdArgs a, int32_t grid_kv) {
   __shared__ BwdSmem sm;
-  const int32_t b = (int32_t)blockIdx.x, gw = glob_wg_padded(a);
-  if (b < gw) {
-    if (b < glob_wg(a)) dkv_glob_workgroup<BIAS, SEG>(a, sm, b);
+  const int32_t gw = glob_wg_padded(a);
+  const int32_t nb = grid_kv - gw;  // band slots per pass
+  int32_t b = (int32_t)blockIdx.x;
+  if (b < 2 * nb) {  // band: dK/dV, then dQ
+    const bool kv = b < nb;
+    const int32_t bw = band_tile_of(a, kv ? b : b - nb);
+    if (bw < 0) return;
+    if (kv)
+      dkv_band_workgroup<BIAS, SEG>(a, sm, bw);
+    else
+      dq_band_workgroup<BIAS, SEG>(a, sm, bw);
     return;
   }
-  const int32_t bw = band_tile_of(a, b - gw);
-  if (bw >= 0) dkv_band_workgroup<BIAS, SEG>(a, sm, bw);
+  b -= 2 * nb;  // global ranges: dK/dV, then dQ
+  const bool kv = b < gw;
+  if (!kv) b -= gw;
+  if (b >= glob_wg(a)) return;
+  if (kv)
+    dkv_glob_workgroup<BIAS, SEG>(a, sm, b);
+  else
+    dq_glob_workgroup<BIAS, SEG>(a, sm, b);
 }
 
 // The global rows' dQ and the global keys' dK, dV from the ranges' partial
@@ -1337,37 +1332,21 @@ static int64_t mfma_grid(const BwdArgs& a) {
   return (g + kXcds - 1) / kXcds * kXcds + (int64_t)kXcds * ((a.n_band_wg + kXcds - 1) / kXcds);
 }
 
-hipError_t launch_dq_mfma(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream) {
   if (a.n_band_wg <= 0) return hipSuccess;
   if (a.glob_chunks < 1 || (a.glob_chunks > 1 && !a.gpart)) return hipErrorInvalidValue;
   const int64_t grid = mfma_grid(a);
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 g((uint32_t)grid), t(TT::kThreads);
+  if (2 * grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 g((uint32_t)(2 * grid)), t(TT::kThreads);
+  const int32_t gkv = (int32_t)grid;
   if (a.rel_bias && a.seg)
-    hipLaunchKernelGGL((bwd_dq_mfma_kernel<true, true>), g, t, 0, stream, a);
+    hipLaunchKernelGGL((bwd_mfma_kernel<true, true>), g, t, 0, stream, a, gkv);
   else if (a.rel_bias)
-    hipLaunchKernelGGL((bwd_dq_mfma_kernel<true, false>), g, t, 0, stream, a);
+    hipLaunchKernelGGL((bwd_mfma_kernel<true, false>), g, t, 0, stream, a, gkv);
   else if (a.seg)
-    hipLaunchKernelGGL((bwd_dq_mfma_kernel<false, true>), g, t, 0, stream, a);
+    hipLaunchKernelGGL((bwd_mfma_kernel<false, true>), g, t, 0, stream, a, gkv);
   else
-    hipLaunchKernelGGL((bwd_dq_mfma_kernel<false, false>), g, t, 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_dkv_mfma(const BwdArgs& a, hipStream_t stream) {
-  if (a.n_band_wg <= 0) return hipSuccess;
-  if (a.glob_chunks < 1 || (a.glob_chunks > 1 && !a.gpart)) return hipErrorInvalidValue;
-  const int64_t grid = mfma_grid(a);
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 g((uint32_t)grid), t(TT::kThreads);
-  if (a.rel_bias && a.seg)
-    hipLaunchKernelGGL((bwd_dkv_mfma_kernel<true, true>), g, t, 0, stream, a);
-  else if (a.rel_bias)
-    hipLaunchKernelGGL((bwd_dkv_mfma_kernel<true, false>), g, t, 0, stream, a);
-  else if (a.seg)
-    hipLaunchKernelGGL((bwd_dkv_mfma_kernel<false, true>), g, t, 0, stream, a);
-  else
-    hipLaunchKernelGGL((bwd_dkv_mfma_kernel<false, false>), g, t, 0, stream, a);
+    hipLaunchKernelGGL((bwd_mfma_kernel<false, false>), g, t, 0, stream, a, gkv);
   return hipGetLastError();
 }
 

@@ -42,9 +42,8 @@ struct BwdArgs {
 };
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream);
-hipError_t launch_dq_mfma(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_dkv_mfma(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_glob_reduce(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream);  // dK/dV and dQ, D_i given
 hipError_t launch_dilated_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dilated_bwd_mfma(const BwdArgs& a, hipStream_t stream);
 int32_t host_glob_part_rows(int32_t N);  // partial-sum rows per head in the workspace
