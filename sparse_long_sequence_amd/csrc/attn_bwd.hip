@@ -109,26 +109,42 @@ __device__ __forceinline__ float label_bias(const BwdArgs& a, int32_t h, int32_t
 
 constexpr int kBatch = 8;  // pairs whose loads and reductions are issued together
 
-// D_i = dO_i . O_i of every row for a LongNet call without a pattern of
-// dilation 1 (bf16): eight lanes per row with one 16-byte load each from dO and
-// O (32 rows per workgroup).
+// D_i = dO_i . O_i of every row (bf16; for the band + global MFMA path, and a
+// LongNet call without a pattern of dilation 1): eight lanes per row with one
+// 16-byte load each from dO and O, kDeltaPasses rows per group of eight lanes
+// with all their loads in flight at once (32 * kDeltaPasses rows per
+// workgroup).
+constexpr int kDeltaPasses = 4;
+static int64_t delta_blocks(int64_t rows) { return (rows + 32 * kDeltaPasses - 1) / (32 * kDeltaPasses); }
+
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
   const int32_t part = threadIdx.x & 7;
-  const bool live = row < (int64_t)a.B * a.H * a.N;
-  float x = 0.f;
-  if (live) {
-    const size_t o = (size_t)row * kD + 8 * part;
-    const bf16x8 d = __builtin_bit_cast(bf16x8, ldg16(static_cast<const bf16*>(a.dout) + o));
-    const bf16x8 y = __builtin_bit_cast(bf16x8, ldg16(static_cast<const bf16*>(a.out) + o));
+  bf16x8 d[kDeltaPasses], y[kDeltaPasses];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x += (float)d[e] * (float)y[e];
+  for (int p = 0; p < kDeltaPasses; ++p) {
+    const int64_t row = ((int64_t)blockIdx.x * kDeltaPasses + p) * 32 + (threadIdx.x >> 3);
+    if (row < rows) {
+      const size_t o = (size_t)row * kD + 8 * part;
+      d[p] = __builtin_bit_cast(bf16x8, ldg16(static_cast<const bf16*>(a.dout) + o));
+      y[p] = __builtin_bit_cast(bf16x8, ldg16(static_cast<const bf16*>(a.out) + o));
+    }
   }
-  // sum over the row's eight lanes: partners l^1, l^2, then the other quad
-  x += dpp_partner<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp_partner<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp_partner<0x141>(x);  // row_half_mirror
-  if (live && part == 0) a.delta[row] = x;
+#pragma unroll
+  for (int p = 0; p < kDeltaPasses; ++p) {
+    const int64_t row = ((int64_t)blockIdx.x * kDeltaPasses + p) * 32 + (threadIdx.x >> 3);
+    const bool live = row < rows;
+    float x = 0.f;
+    if (live) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x += (float)d[p][e] * (float)y[p][e];
+    }
+    // sum over the row's eight lanes: partners l^1, l^2, then the other quad
+    x += dpp_partner<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_partner<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_partner<0x141>(x);  // row_half_mirror
+    if (live && part == 0) a.delta[row] = x;
+  }
 }
 
 // Row i's gradient dQ_i (query-centric), and D_i into the workspace.
@@ -593,7 +609,7 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) 
   const dim3 g((uint32_t)((rows + kWavesBwd - 1) / kWavesBwd)), blk(64 * kWavesBwd);
   if (dtype == 1 && a.n_band_wg > 0) {
     // D_i, then dK/dV and dQ on MFMA in one launch (no global ranks needed)
-    hipLaunchKernelGGL(bwd_delta_kernel, dim3((uint32_t)((rows + 31) / 32)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_delta_kernel, dim3((uint32_t)delta_blocks(rows)), dim3(256), 0, stream, a);
     hipError_t e = launch_bwd_mfma(a, stream);
     if (e != hipSuccess) return e;
     e = launch_glob_reduce(a, stream);  // the global tiles' partial sums
@@ -619,7 +635,7 @@ hipError_t launch_dilated_bwd(const BwdArgs& a, hipStream_t stream) {
   bool r1 = false;
   for (int32_t k = 0; k < a.n_pairs; ++k) r1 = r1 || a.pr[k] == 1;
   if (!r1)
-    hipLaunchKernelGGL(bwd_delta_kernel, dim3((uint32_t)((rows + 31) / 32)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_delta_kernel, dim3((uint32_t)delta_blocks(rows)), dim3(256), 0, stream, a);
   return launch_dilated_bwd_mfma(a, stream);
 }
 

@@ -1233,19 +1233,17 @@ __global__ __launch_bounds__(256) void bwd_glob_reduce_kernel(BwdArgs a) {
   const int32_t d4 = (int32_t)(rest % (kD / 4));
   const int64_t r = rest / (kD / 4);
   const int32_t g = (int32_t)(r % a.n_global), bh = (int32_t)(r / a.n_global);
-  // four loads in flight at a time, added in range order
+  // every range's load in flight at once (at most kMaxGlobChunks), then
+  // added in range order
+  f32x4 v[kMaxGlobChunks];
+#pragma unroll
+  for (int u = 0; u < kMaxGlobChunks; ++u)
+    v[u] = u < a.glob_chunks ? reinterpret_cast<const f32x4*>(part_row(a, x, u, bh, g))[d4]
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-  for (int32_t c0 = 0; c0 < a.glob_chunks; c0 += 4) {
-    f32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      v[u] = c0 + u < a.glob_chunks
-                 ? reinterpret_cast<const f32x4*>(part_row(a, x, c0 + u, bh, g))[d4]
-                 : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (c0 + u < a.glob_chunks) sum += v[u];
-  }
+  for (int u = 0; u < kMaxGlobChunks; ++u)
+    if (u < a.glob_chunks) sum += v[u];
   const size_t ro = ((size_t)bh * a.N + a.gidx[g]) * kD;
   float* dst = x == 0 ? (a.sep ? a.dqg : a.dq) : (x == 1 ? a.dk : a.dv);
   reinterpret_cast<f32x4*>(dst + ro)[d4] = sum * (x == 2 ? 1.f : a.scale);
@@ -1352,6 +1350,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_glob_reduce(const BwdArgs& a, hipStream_t stream) {
   if (a.n_global <= 0 || a.glob_chunks <= 1) return hipSuccess;
+  if (a.glob_chunks > kMaxGlobChunks) return hipErrorInvalidValue;
   const int64_t threads = (int64_t)3 * a.B * a.H * a.n_global * (kD / 4);
   hipLaunchKernelGGL(bwd_glob_reduce_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0,
                      stream, a);
@@ -1373,7 +1372,7 @@ int32_t host_glob_chunks(int64_t bh, int32_t N, int32_t n_global) {
   const int32_t n_gpad = (n_global + TT::kTQ - 1) / TT::kTQ * TT::kTQ;
   const int64_t units = bh * (n_gpad / TT::kTQ);
   int64_t c = (512 + units - 1) / units;
-  c = c < 16 ? c : 16;
+  c = c < kMaxGlobChunks ? c : kMaxGlobChunks;
   const int64_t by_rows = host_glob_part_rows(N) / n_gpad;
   c = c < by_rows ? c : by_rows;
   const int64_t by_len = (N + 4 * kTK - 1) / (4 * kTK);

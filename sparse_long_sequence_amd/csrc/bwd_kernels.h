@@ -41,6 +41,8 @@ struct BwdArgs {
   int32_t pw[kMaxPairs], pr[kMaxPairs];
 };
 
+constexpr int32_t kMaxGlobChunks = 16;  // key (row) ranges per global tile
+
 hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream);
 hipError_t launch_glob_reduce(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream);  // dK/dV and dQ, D_i given
