@@ -466,9 +466,9 @@ struct DkvWave {
 };
 
 // The backward's LDS: the engine's tile buffers and, for the dK/dV pass, each
-// staged row tile's lse (times lse_mul: 1 / scale gives score units, the raw
-// q.k at which P = 1; log2 e gives log2 units; +inf for a row without keys)
-// and D_i.
+// staged row tile's offsets, negated: -lse times lse_mul (1 / scale gives
+// score units, the raw q.k at which P = 1; log2 e gives log2 units; -inf for
+// a row without keys) and -D_i.
 struct BwdSmem : TT::Smem {
   alignas(16) float rlse[2][kTK];
   alignas(16) float rdi[2][kTK];
@@ -525,16 +525,21 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
   for (int sb = 0; sb < TT::kSub; ++sb) {
     const int32_t cls = dead ? kEmpty : classify<bf16>(mr, kt.count, sb, r0, r1);
     if (cls == kEmpty) continue;
-    const float* ls = row_lse(sm, BUF);
-    const float* dd = row_di(sm, BUF);
+    // the lane's 16 rows are 4 runs of 4 (key_const): one 16-byte read per run
+    const f32x4* ls = reinterpret_cast<const f32x4*>(row_lse(sm, BUF) + kl);
+    const f32x4* dd = reinterpret_cast<const f32x4*>(row_di(sm, BUF) + kl);
     float s[TT::kNS], dp[TT::kNS];
     if constexpr (INIT) {  // s = q.k - lse / scale, dp = dO.v - D_i
       f32x16 s0, d0;
 #pragma unroll
-      for (int e = 0; e < TT::kNS; ++e) {
-        const int32_t i = TT::key_const(sb, e) + kl;
-        s0[e] = -ls[i];
-        d0[e] = -dd[i];
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 x = ls[(TT::key_const(sb, 4 * j)) / 4];
+        const f32x4 y = dd[(TT::key_const(sb, 4 * j)) / 4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s0[4 * j + i] = x[i];
+          d0[4 * j + i] = y[i];
+        }
       }
       tile_dots(&sm.k[BUF][0], w.kf, lane, sb, s, s0);
       tile_dots(&sm.v[BUF][0], w.vf, lane, sb, dp, d0);
@@ -572,10 +577,11 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
           p1 = __builtin_amdgcn_exp2f(s[e + 1] * c);
           G.p[t][i] = pack_bf16x2(p0 * dp[e], p1 * dp[e + 1]);
         } else {
-          const int32_t i0 = TT::key_const(sb, e) + kl, i1 = TT::key_const(sb, e + 1) + kl;
-          p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -ls[i0]));
-          p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], c, -ls[i1]));
-          G.p[t][i] = pack_bf16x2(p0 * (dp[e] - dd[i0]), p1 * (dp[e + 1] - dd[i1]));
+          const f32x4 x = ls[TT::key_const(sb, e) / 4], y = dd[TT::key_const(sb, e) / 4];
+          const int u = e & 3;
+          p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, x[u]));
+          p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], c, x[u + 1]));
+          G.p[t][i] = pack_bf16x2(p0 * (dp[e] + y[u]), p1 * (dp[e + 1] + y[u + 1]));
         }
         P.p[t][i] = pack_bf16x2(p0, p1);
       }
@@ -607,8 +613,8 @@ __device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const b
     if (tid < kTK && t.count > 0) {
       const int32_t p = key_pos<GATHER>(t, min(tid, t.count - 1));
       const float l = lse[p];
-      pl = l == kNegInf ? -kNegInf : l * lse_mul;
-      pd = delta[p];
+      pl = l == kNegInf ? kNegInf : -(l * lse_mul);
+      pd = -delta[p];
     }
   };
   auto put_rows = [&](int32_t buf) {
