@@ -467,8 +467,8 @@ struct DkvWave {
 
 // The backward's LDS: the engine's tile buffers and, for the dK/dV pass, each
 // staged row tile's offsets, negated: -lse times lse_mul (1 / scale gives
-// score units, the raw q.k at which P = 1; log2 e gives log2 units; -inf for
-// a row without keys) and -D_i.
+// score units, the raw q.k at which P = 1; -inf for a row without keys) and
+// -D_i.
 struct BwdSmem : TT::Smem {
   alignas(16) float rlse[2][kTK];
   alignas(16) float rdi[2][kTK];
@@ -485,20 +485,18 @@ __device__ __forceinline__ const float* row_di(const BwdSmem& sm, int32_t buf) {
 // One streamed tile of query rows into dK^T, dV^T. EXCL_G: rows that are
 // global are excluded (they are taken in the global-row sweep); ROWS_AFTER:
 // (gathered global rows, causal) only rows at or after the lane's key.
-// INIT: the score and dP MFMAs start from the rows' offsets (-lse / scale and
-// -D_i, with the lse staged in score units), so those per-element values take
-// no registers of their own; this lets the band kernel run 3 waves per SIMD.
-// Otherwise (lse staged in log2 units) the offsets are applied after the
-// MFMAs, which keeps the LDS reads off their critical path: the LongNet
-// sweeps, not register-bound, are faster that way.
+// The score and dP MFMAs start from the rows' offsets (-lse / scale and -D_i,
+// staged with the lse in score units), so those per-element values take no
+// registers of their own (this lets the band kernel run 3 waves per SIMD) and
+// no VALU work after the MFMAs.
 // PRIO: the exponential stretch at raised wave issue priority (as in the
 // forward's softmax); it pays in the LongNet sweeps (the (2048, 1) pattern's
 // dK/dV launch runs about 11% faster) and costs about 1% in the band ones.
 // BIAS: the scalar bias table (br: the flipped table, key_global_is_same_kind
 // = the lane's key is global). SEG: segment masks from gs (the lane's key's
 // segment against the staged rows').
-template <int32_t BUF, bool EXCL_G, bool ROWS_AFTER, bool INIT, bool PRIO = false,
-          bool BIAS = false, bool SEG = false>
+template <int32_t BUF, bool EXCL_G, bool ROWS_AFTER, bool PRIO = false, bool BIAS = false,
+          bool SEG = false>
 __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t lane,
                                          const MaskRule& mr, const KeyTile& kt, int32_t ki,
                                          int32_t kpos, bool dead, float c, bool causal,
@@ -529,7 +527,7 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
     const f32x4* ls = reinterpret_cast<const f32x4*>(row_lse(sm, BUF) + kl);
     const f32x4* dd = reinterpret_cast<const f32x4*>(row_di(sm, BUF) + kl);
     float s[TT::kNS], dp[TT::kNS];
-    if constexpr (INIT) {  // s = q.k - lse / scale, dp = dO.v - D_i
+    {  // s = q.k - lse / scale, dp = dO.v - D_i
       f32x16 s0, d0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -543,9 +541,6 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
       }
       tile_dots(&sm.k[BUF][0], w.kf, lane, sb, s, s0);
       tile_dots(&sm.v[BUF][0], w.vf, lane, sb, dp, d0);
-    } else {  // s = q.k, dp = dO.v
-      tile_dots(&sm.k[BUF][0], w.kf, lane, sb, s);
-      tile_dots(&sm.v[BUF][0], w.vf, lane, sb, dp);
     }
     if constexpr (BIAS) {
       if (tb.on) add_bias<bf16>(s, sm, BUF, br, sb, ki, kpos, lane, tb.same);
@@ -571,18 +566,9 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 8 * t + 2 * i;
-        float p0, p1;
-        if constexpr (INIT) {
-          p0 = __builtin_amdgcn_exp2f(s[e] * c);
-          p1 = __builtin_amdgcn_exp2f(s[e + 1] * c);
-          G.p[t][i] = pack_bf16x2(p0 * dp[e], p1 * dp[e + 1]);
-        } else {
-          const f32x4 x = ls[TT::key_const(sb, e) / 4], y = dd[TT::key_const(sb, e) / 4];
-          const int u = e & 3;
-          p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, x[u]));
-          p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], c, x[u + 1]));
-          G.p[t][i] = pack_bf16x2(p0 * (dp[e] + y[u]), p1 * (dp[e + 1] + y[u + 1]));
-        }
+        const float p0 = __builtin_amdgcn_exp2f(s[e] * c);
+        const float p1 = __builtin_amdgcn_exp2f(s[e + 1] * c);
+        G.p[t][i] = pack_bf16x2(p0 * dp[e], p1 * dp[e + 1]);
         P.p[t][i] = pack_bf16x2(p0, p1);
       }
     }
@@ -751,7 +737,7 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm
   stream_rows<false, SEG>(sm, qs, dob, lse, delta, 1.f / a.scale, n_band, band_desc, gi,
                           [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                             constexpr int32_t buf = decltype(buf_tag)::value;
-                            dkv_tile<buf, true, false, true, false, BIAS, SEG>(
+                            dkv_tile<buf, true, false, false, BIAS, SEG>(
                                 sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br,
                                 gi);
                           });
@@ -767,7 +753,7 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm
   };
   auto glob_proc = [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
     constexpr int32_t buf = decltype(buf_tag)::value;
-    dkv_tile<buf, false, true, true, false, BIAS, SEG>(sm, w, lane, mr, kt, ki, kpos, dead,
+    dkv_tile<buf, false, true, false, BIAS, SEG>(sm, w, lane, mr, kt, ki, kpos, dead,
                                                        a.scale_log2, a.causal, br, gall);
   };
   const bool mine = ki < kcount && !qi_is_global(a, ki, kcount, kpos, g_first, g_last, j_lo, j_hi);
@@ -955,7 +941,7 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, BwdSmem& sm
     stream_rows<false, SEG>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
                             [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                               constexpr int32_t buf = decltype(buf_tag)::value;
-                              dkv_tile<buf, true, false, true, false, BIAS, SEG>(
+                              dkv_tile<buf, true, false, false, BIAS, SEG>(
                                   sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal,
                                   br, gi);
                             });
@@ -963,7 +949,7 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, BwdSmem& sm
     stream_rows<false, SEG>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
                             [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                               constexpr int32_t buf = decltype(buf_tag)::value;
-                              dkv_tile<buf, false, false, true, false, BIAS, SEG>(
+                              dkv_tile<buf, false, false, false, BIAS, SEG>(
                                   sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal,
                                   br, gi);
                             });
@@ -997,7 +983,7 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, BwdSmem& sm
                          1.f / a.scale, n_gt, glob_desc, gall,
                          [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                            constexpr int32_t buf = decltype(buf_tag)::value;
-                           dkv_tile<buf, false, true, true, false, BIAS, SEG>(
+                           dkv_tile<buf, false, true, false, BIAS, SEG>(
                                sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br,
                                gall);
                          });
@@ -1156,12 +1142,12 @@ __device__ __forceinline__ void dkv_dil_workgroup(const BwdArgs& a, BwdSmem& sm,
   const GlobInfo gi = {kGlobNone, nullptr, 0, nullptr, 0, 0, 0};
   stream_rows<false>(sm, static_cast<const bf16*>(a.q) + bh * head_elems,
                      static_cast<const bf16*>(a.dout) + bh * head_elems,
-                     a.lse + (size_t)bh * a.N, a.delta + (size_t)bh * a.N, kLog2e, n_tiles,
-                     desc, gi,
+                     a.lse + (size_t)bh * a.N, a.delta + (size_t)bh * a.N, 1.f / a.scale,
+                     n_tiles, desc, gi,
                      [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                        constexpr int32_t buf = decltype(buf_tag)::value;
-                       dkv_tile<buf, false, false, false, true>(sm, w, lane, mr, kt, ki, kpos, dead,
-                                                          a.scale_log2, a.causal);
+                       dkv_tile<buf, false, false, true>(sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2,
+                                                   a.causal);
                      });
   if (ki < kcount) {
     float* dk = a.dk + ((size_t)bh * a.N + kpos) * kD;
