@@ -259,13 +259,14 @@ typedef struct {
  *  dout         device [B,H,N,D] in q's dtype: the loss gradient w.r.t. out.
  *  dq, dk, dv   device fp32 [B,H,N,D] outputs; must not alias any input.
  * Requires ext->workspace (its contents on entry are ignored). Pointers 16-byte
- * aligned. Errors as for la_attn_forward. Two or three launches on `stream`
- * (bf16 with no label vectors or label matrices, at most the scalar table of
- * 2k+1 distance entries, and segment ids, if given, masking every piece: D_i,
- * then one MFMA launch for dQ, dK and dV, the global rows and keys split over
- * up to 16 key or row ranges, and with several ranges one launch adding their
- * partial sums in a fixed order; otherwise global ranks, dQ and D_i, dK and
- * dV), no allocation; results are bitwise reproducible. */
+ * aligned. Errors as for la_attn_forward. Two to four launches on `stream`
+ * (bf16 with the 2k+1 distance labels alone, if any (a scalar table, label
+ * vectors or both; no label matrices), and segment ids, if given, masking
+ * every piece: D_i, with label vectors each row's label table, then one MFMA
+ * launch for dQ, dK and dV, the global rows and keys split over up to 16 key
+ * or row ranges, and with several ranges one launch adding their partial sums
+ * in a fixed order; otherwise global ranks, dQ and D_i, dK and dV), no
+ * allocation; results are bitwise reproducible. */
 la_status la_attn_backward(const la_dims *dims, const void *q, const void *k, const void *v,
                            const int32_t *global_idx, int32_t n_global, int32_t radius,
                            const int32_t *dilation, int32_t causal, const void *out,
@@ -274,7 +275,8 @@ la_status la_attn_backward(const la_dims *dims, const void *q, const void *k, co
 
 /* Bytes of workspace la_attn_backward needs (0 for invalid dims): fp32 D_i per
  * row, each position's int32 rank in global_idx and, for bf16, fp32 partial
- * sums of dQ, dK and dV for min(N rounded up to 128, 2048) rows per head; each
+ * sums of dQ, dK and dV for min(N rounded up to 128, 2048) rows per head and
+ * a label table of 64 fp32 entries per row (used with label vectors); each
  * part padded to 256 bytes. */
 size_t la_attn_backward_workspace_size(const la_dims *dims);
 

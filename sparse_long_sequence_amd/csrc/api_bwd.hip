@@ -30,15 +30,23 @@ size_t bwd_part_bytes(const la_dims* dims) {
                   sizeof(float));
 }
 
+// Each row's label table for key-side label vectors (bf16): up to
+// kMaxLabels fp32 entries per row.
+size_t bwd_rowtab_bytes(const la_dims* dims) {
+  if (dims->dtype != LA_BF16) return 0;
+  return align_up((size_t)dims->B * dims->H * dims->N * la::kMaxLabels * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t la_attn_backward_workspace_size(const la_dims* dims) {
   if (check_dims(dims, false) != LA_OK) return 0;
-  // D_i per row, each position's global rank, then the partial sums
+  // D_i per row, each position's global rank, the partial sums, the row tables
   return align_up((size_t)dims->B * dims->H * dims->N * sizeof(float)) +
-         align_up((size_t)dims->N * sizeof(int32_t)) + bwd_part_bytes(dims);
+         align_up((size_t)dims->N * sizeof(int32_t)) + bwd_part_bytes(dims) +
+         bwd_rowtab_bytes(dims);
 }
 
 la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, const void* v,
@@ -138,11 +146,11 @@ la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, co
   a.scale = (float)(1.0 / sqrt((double)kDHead));
   a.scale_log2 = (float)(1.0 / sqrt((double)kDHead) * 1.4426950408889634);
   a.glob_chunks = 1;
-  // the MFMA path: bf16 with at most the scalar bias table of 2k+1 distance
-  // labels and segment ids that mask every pair (no key vectors or labels)
-  if (dims->dtype == LA_BF16 && !a.rel_vec && !a.glabel && !a.llabel &&
-      (!a.seg || a.seg_pieces == 15) &&
-      (!a.rel_bias || a.n_labels == 2 * rel_k + 1)) {
+  // the MFMA path: bf16 with the 2k+1 distance labels alone (a scalar table,
+  // key-side label vectors or both; no label matrices) and segment ids that
+  // mask every pair
+  if (dims->dtype == LA_BF16 && !a.glabel && !a.llabel && (!a.seg || a.seg_pieces == 15) &&
+      (!(a.rel_bias || a.rel_vec) || a.n_labels == 2 * rel_k + 1)) {
     const int32_t tq = la::host_query_tile(dims->dtype);
     int32_t tiles = 0;
     for (int32_t h = 0; h < dims->H; ++h)
@@ -154,6 +162,8 @@ la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, co
     a.glob_chunks = la::host_glob_chunks((int64_t)dims->B * dims->H, dims->N, n_global);
     a.gpart = reinterpret_cast<float*>(reinterpret_cast<char*>(a.grank) +
                                        align_up((size_t)dims->N * sizeof(int32_t)));
+    if (a.rel_vec)
+      a.rowtab = reinterpret_cast<float*>(reinterpret_cast<char*>(a.gpart) + bwd_part_bytes(dims));
   }
   hipError_t e = la::launch_attn_bwd(a, dims->dtype, stream);
   if (e != hipSuccess) return fail(LA_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(e));

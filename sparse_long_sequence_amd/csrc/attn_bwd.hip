@@ -610,7 +610,9 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) 
   if (dtype == 1 && a.n_band_wg > 0) {
     // D_i, then dK/dV and dQ on MFMA in one launch (no global ranks needed)
     hipLaunchKernelGGL(bwd_delta_kernel, dim3((uint32_t)delta_blocks(rows)), dim3(256), 0, stream, a);
-    hipError_t e = launch_bwd_mfma(a, stream);
+    hipError_t e = launch_rowtab(a, stream);  // key-side label vectors: the rows' tables
+    if (e != hipSuccess) return e;
+    e = launch_bwd_mfma(a, stream);
     if (e != hipSuccess) return e;
     e = launch_glob_reduce(a, stream);  // the global tiles' partial sums
     if (e != hipSuccess) return e;

@@ -41,6 +41,7 @@ struct DqWave {
   f32x16 acc[2];
   float lse2;
   float di;
+  float c_lo, c_hi;  // key vectors: this lane's dS sums over the two clipped labels
 };
 
 __device__ __forceinline__ void load_frag(bf16x8 (&f)[4], const bf16* base, int32_t pos,
@@ -188,10 +189,90 @@ __device__ __forceinline__ void seg_mask(float* s, const TT::Smem& sm, int32_t s
     s[r] = sm.kseg[BUF][TT::key_const(sb, r) + kl] == sq ? s[r] : kNegInf;
 }
 
+// Key-side label vectors, dQ pass: the same-kind pairs' dS of sub-tile sb by
+// label (clipped distance key - row): the two clipped labels into the lane's
+// registers, the others into C[qi][l] in LDS (each such (row, label) pair has
+// one key, so the lanes of one add never share an address).
+template <int32_t BUF>
+__device__ __forceinline__ void vec_label_sums(DqWave& w, const float* ds, const TT::Smem& sm,
+                                               const BiasRule& br, int sb, int32_t qi,
+                                               int32_t qpos, int32_t lane, bool all_same) {
+  int32_t kl = TT::key_lane(lane);
+  asm("" : "+v"(kl));  // opaque per call, as in mask_tile
+  const int32_t k = br.k, top = 2 * br.k;
+  float* C = const_cast<float*>(br.tab) + TT::kTQ * br.row_stride + qi * br.row_stride;
+#pragma unroll
+  for (int r = 0; r < TT::kNS; ++r) {
+    const int32_t kj = TT::key_const(sb, r) + kl;
+    const bool same =
+        all_same || ((sm.kglob[BUF][kj] != 0) == (br.key_global_is_same_kind != 0));
+    const int32_t l = min(max(sm.kpos[BUF][kj] - qpos, -k), k) + k;
+    const float x = same ? ds[r] : 0.f;
+    w.c_lo += l == 0 ? x : 0.f;
+    w.c_hi += l == top ? x : 0.f;
+    if (same && l > 0 && l < top) atomicAdd(C + l, ds[r]);
+  }
+}
+
+// Key-side label vectors, dQ workgroup set-up: the rows' tables (row r at
+// position pos(r); rows past the tile repeat its last), the label sums
+// zeroed and the head's vectors a_l (fp32 [V][D]) into the dynamic LDS; visible
+// after the tile loop's first barrier.
+template <typename Pos>
+__device__ __forceinline__ BiasRule vec_rule_dq(const BwdArgs& a, float* dyn, int32_t bh,
+                                                int32_t h, int32_t lane_is_global_kind,
+                                                Pos pos) {
+  const int32_t V = a.n_labels, tid = threadIdx.x;
+  const float* tb = a.rowtab + (size_t)bh * a.N * V;
+  float* rt = dyn;
+  float* C = dyn + TT::kTQ * V;
+  float* A = dyn + 2 * TT::kTQ * V;
+  const int32_t r = tid >> 1, l0 = tid & 1;  // two threads per row
+  const float* src = tb + (size_t)pos(r) * V;
+  for (int32_t l = l0; l < V; l += 2) {
+    rt[r * V + l] = src[l];
+    C[r * V + l] = 0.f;
+  }
+  const float* av = a.rel_vec + (size_t)h * V * kD;
+  for (int32_t x = tid; x < V * kD; x += TT::kThreads) A[x] = av[x];
+  return {dyn, a.rel_k, lane_is_global_kind, V};
+}
+
+// Key-side label vectors, dQ workgroup end: dQ_i^T += sum_l C_il a_l for the
+// lane's row (the clipped labels' sums combined over the row's two lanes, in
+// lane order).
+__device__ __forceinline__ void vec_dq_epilogue(DqWave& w, const BiasRule& br, const float* dyn,
+                                                int32_t qi, int32_t lane) {
+  const int32_t V = br.row_stride, top = 2 * br.k, hh = lane >> 5;
+  const float* C = dyn + TT::kTQ * V + qi * V;
+  const float* A = dyn + 2 * TT::kTQ * V;
+  const float olo = __shfl_xor(w.c_lo, 32), ohi = __shfl_xor(w.c_hi, 32);
+  const float lo = hh == 0 ? w.c_lo + olo : olo + w.c_lo;
+  const float hi = hh == 0 ? w.c_hi + ohi : ohi + w.c_hi;
+  for (int32_t l = 0; l < V; ++l) {
+    const float cl = l == 0 ? lo : (l == top ? hi : C[l]);
+    const float* al = A + l * kD + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(al + 32 * db + 8 * j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w.acc[db][4 * j + i] = __builtin_fmaf(cl, x[i], w.acc[db][4 * j + i]);
+      }
+    }
+  }
+}
+
 // One staged key tile into dQ^T. The forward's block classes decide which
 // sub-tiles run and which need the per-element mask. SEG: segment masks from
-// gs (a tile of other segments only is skipped).
-template <int32_t BUF, bool BIAS, bool SEG = false>
+// gs (a tile of other segments only is skipped). VEC: key-side label vectors
+// (ETC page, §3.4 "Relative Position Encoding": the logit is q_i . (k_j + a_l)
+// / sqrt(D) for a same-kind pair of label l), br.tab holding the workgroup's
+// rows' tables (row stride V) followed by the label sums C [rows][V]: the
+// same-kind pairs' dS add to C[row][l] (the clipped labels 0 and 2k in the
+// lane's registers), for dQ_i's term sum_l C_il a_l.
+template <int32_t BUF, bool BIAS, bool SEG = false, bool VEC = false>
 __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t lane,
                                         const MaskRule& mr, const KeyTile& kt, int32_t qi,
                                         int32_t qpos, bool dead, float c, const BiasRule& br,
@@ -207,7 +288,7 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
   const int32_t r1 = (mr.use_qpos ? __builtin_amdgcn_readlane(qpos, TT::kRowsPerBlock - 1)
                                   : __builtin_amdgcn_readlane(qi, TT::kRowsPerBlock - 1)) + mr.ref_off;
   TileBias tb = {false, false};
-  if constexpr (BIAS) tb = tile_bias<BUF>(sm, br, kt);
+  if constexpr (BIAS || VEC) tb = tile_bias<BUF>(sm, br, kt);
 #pragma unroll
   for (int sb = 0; sb < TT::kSub; ++sb) {
     const int32_t cls = dead ? kEmpty : classify<bf16>(mr, kt.count, sb, r0, r1);
@@ -215,12 +296,13 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
     float s[TT::kNS], dp[TT::kNS];
     tile_dots(&sm.k[BUF][0], w.qf, lane, sb, s);
     tile_dots(&sm.v[BUF][0], w.df, lane, sb, dp);
-    if constexpr (BIAS) {
+    if constexpr (BIAS || VEC) {
       if (tb.on) add_bias<bf16>(s, sm, BUF, br, sb, qi, qpos, lane, tb.same);
     }
     if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, qi, qpos, lane);
     if (SEG && seg_check) seg_mask<BUF>(s, sm, gs.sq, sb, lane);
     TT::PTile G;
+    float ds[TT::kNS];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -228,8 +310,13 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
         const int e = 8 * t + 2 * i;
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -w.lse2));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], c, -w.lse2));
-        G.p[t][i] = pack_bf16x2(p0 * (dp[e] - w.di), p1 * (dp[e + 1] - w.di));
+        ds[e] = p0 * (dp[e] - w.di);
+        ds[e + 1] = p1 * (dp[e + 1] - w.di);
+        G.p[t][i] = pack_bf16x2(ds[e], ds[e + 1]);
       }
+    }
+    if constexpr (VEC) {
+      if (tb.on) vec_label_sums<BUF>(w, ds, sm, br, sb, qi, qpos, lane, tb.same);
     }
     acc_transposed<BUF>(&sm.k[0][0], w.acc, lane, sb, G);
   }
@@ -293,8 +380,9 @@ __device__ __forceinline__ bool qi_is_global(const BwdArgs& a, int32_t qi, int32
 
 // dQ of the non-global rows of one query tile (the forward's band workgroup:
 // window tiles, then the global keys outside the window).
-template <bool BIAS, bool SEG>
-__device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t bw) {
+template <bool BIAS, bool SEG, bool VEC>
+__device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm, float* dyn,
+                                                  int32_t bw) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t N = a.N;
@@ -337,6 +425,8 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
   w.di = a.delta[(size_t)bh * N + qpos];  // D_i from the launch before
   w.acc[0] = f32x16{};
   w.acc[1] = f32x16{};
+  w.c_lo = 0.f;
+  w.c_hi = 0.f;
 
   const int32_t R = a.radius;
   const int32_t lo = max(0, t0 - R);
@@ -345,9 +435,13 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
   GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
   seg_info<SEG>(gi, a, bh, qpos);
   BiasRule br = {nullptr, 0, 0, 0};
-  if constexpr (BIAS) {
+  if constexpr (BIAS || VEC) {
     // the window keys' global flags decide which pairs are same-kind
-    br = bias_rule(a, sm, h, false, 0);
+    if constexpr (VEC)
+      br = vec_rule_dq(a, dyn, bh, h, 0,
+                       [&](int32_t r) { return qbase + d * min(r, qcount - 1); });
+    else
+      br = bias_rule(a, sm, h, false, 0);
     if (ng > 0) {
       if (hi - lo + 1 <= 32 * kGMaskWords) {
         build_gmask<bf16>(sm, a.gidx, ng, c + d * lo, d, hi - lo + 1, tid);
@@ -357,10 +451,10 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
       }
     }
   }
-  const int32_t gkeys = BIAS ? kGlobAll : kGlobNone;  // mode of the global-key tiles
+  const int32_t gkeys = (BIAS || VEC) ? kGlobAll : kGlobNone;  // mode of the global-key tiles
   auto proc = [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
     constexpr int32_t buf = decltype(buf_tag)::value;
-    dq_tile<buf, BIAS, SEG>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2, br, gi);
+    dq_tile<buf, BIAS, SEG, VEC>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2, br, gi);
   };
   auto band_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = lo + n * kTK;
@@ -430,8 +524,8 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
     stream_tiles<true, SEG>(sm, kb, vb, n_glob, glob_desc, gi, proc);
   }
 
-  // non-global rows: dQ (and, with separate projections, a zero dQ_g row),
-  // and D_i for the dK/dV pass
+  if constexpr (VEC) vec_dq_epilogue(w, br, dyn, qi, lane);
+  // non-global rows: dQ (and, with separate projections, a zero dQ_g row)
   if (qi < qcount) {
     const bool is_g = g_first <= i_hi && g_last >= i_lo && sorted_contains(a.gidx, ng, qpos);
     if (!is_g) {
@@ -482,6 +576,25 @@ __device__ __forceinline__ const float* row_di(const BwdSmem& sm, int32_t buf) {
   return &sm.rdi[buf][0];
 }
 
+// Key-side label vectors, dK/dV pass: each same-kind pair of sub-tile sb adds
+// its row's table entry for label clip(key - row) + k (the lane holds the key,
+// the elements the staged rows).
+template <int32_t BUF>
+__device__ __forceinline__ void vec_add_rows(float* s, const BwdSmem& sm, const BiasRule& br,
+                                             int sb, int32_t kpos, int32_t kl, bool all_same) {
+  const int32_t V = br.row_stride, k = br.k;
+  const float* vt = br.tab + BUF * kTK * V;
+#pragma unroll
+  for (int r = 0; r < TT::kNS; ++r) {
+    const int32_t kj = TT::key_const(sb, r) + kl;
+    const bool same =
+        all_same || ((sm.kglob[BUF][kj] != 0) == (br.key_global_is_same_kind != 0));
+    const int32_t l = min(max(kpos - sm.kpos[BUF][kj], -k), k) + k;
+    const float b = vt[kj * V + l];  // always read: keeps the loop branch-free
+    s[r] += same ? b : 0.f;
+  }
+}
+
 // One streamed tile of query rows into dK^T, dV^T. EXCL_G: rows that are
 // global are excluded (they are taken in the global-row sweep); ROWS_AFTER:
 // (gathered global rows, causal) only rows at or after the lane's key.
@@ -494,9 +607,10 @@ __device__ __forceinline__ const float* row_di(const BwdSmem& sm, int32_t buf) {
 // dK/dV launch runs about 11% faster) and costs about 1% in the band ones.
 // BIAS: the scalar bias table (br: the flipped table, key_global_is_same_kind
 // = the lane's key is global). SEG: segment masks from gs (the lane's key's
-// segment against the staged rows').
+// segment against the staged rows'). VEC: key-side label vectors, br.tab the
+// staged rows' tables (kTK rows of br.row_stride labels per buffer).
 template <int32_t BUF, bool EXCL_G, bool ROWS_AFTER, bool PRIO = false, bool BIAS = false,
-          bool SEG = false>
+          bool SEG = false, bool VEC = false>
 __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t lane,
                                          const MaskRule& mr, const KeyTile& kt, int32_t ki,
                                          int32_t kpos, bool dead, float c, bool causal,
@@ -516,7 +630,7 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
   if constexpr (EXCL_G)
     any_g = kt.gmode != kGlobNone && (__builtin_amdgcn_readfirstlane(sm.gcls[BUF]) & 1) != 0;
   TileBias tb = {false, false};
-  if constexpr (BIAS) tb = tile_bias<BUF>(sm, br, kt);
+  if constexpr (BIAS || VEC) tb = tile_bias<BUF>(sm, br, kt);
   int32_t kl = TT::key_lane(lane);
   asm("" : "+v"(kl));  // opaque per call, as in mask_tile
 #pragma unroll
@@ -544,6 +658,9 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
     }
     if constexpr (BIAS) {
       if (tb.on) add_bias<bf16>(s, sm, BUF, br, sb, ki, kpos, lane, tb.same);
+    }
+    if constexpr (VEC) {
+      if (tb.on) vec_add_rows<BUF>(s, sm, br, sb, kpos, kl, tb.same);
     }
     if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, ki, kpos, lane);
     if (SEG && seg_check) seg_mask<BUF>(s, sm, gs.sq, sb, lane);
@@ -583,11 +700,14 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
 // stream_tiles for query rows: as stream_tiles, and each staged tile's rows'
 // lse (times lse_mul) and D_i, read with the tile's loads, written to LDS
 // with its staging (SEG: the rows' segment ids are staged as the keys' are).
-template <bool GATHER, bool SEG = false, typename Desc, typename Proc>
+// VEC: also the rows' label tables (tab: the head's [N][V] tables) into
+// vt + buf * kTK * V.
+template <bool GATHER, bool SEG = false, bool VEC = false, typename Desc, typename Proc>
 __device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const bf16* dob,
                                             const float* lse, const float* delta, float lse_mul,
                                             int32_t n_tiles, Desc desc, const GlobInfo& gi,
-                                            Proc proc) {
+                                            Proc proc, const float* tab = nullptr,
+                                            float* vt = nullptr, int32_t V = 0) {
   const int32_t tid = threadIdx.x;
   if (n_tiles <= 0) return;
   const LabelRule nolab = {};
@@ -595,6 +715,9 @@ __device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const b
   KeyTile kt;
   MaskRule mr;
   float pl = 0.f, pd = 0.f;
+  // VEC: four threads per row, labels tid % 4 + 4u
+  constexpr int32_t kVecPer = VEC ? kMaxLabels / 4 : 1;
+  float pv[kVecPer];
   auto row_vals = [&](const KeyTile& t) {
     if (tid < kTK && t.count > 0) {
       const int32_t p = key_pos<GATHER>(t, min(tid, t.count - 1));
@@ -602,11 +725,29 @@ __device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const b
       pl = l == kNegInf ? kNegInf : -(l * lse_mul);
       pd = -delta[p];
     }
+    if constexpr (VEC) {
+      if (t.count > 0) {
+        const float* src = tab + (size_t)key_pos<GATHER>(t, min(tid >> 2, t.count - 1)) * V;
+#pragma unroll
+        for (int u = 0; u < kVecPer; ++u) {
+          const int32_t l = (tid & 3) + 4 * u;
+          if (l < V) pv[u] = src[l];
+        }
+      }
+    }
   };
   auto put_rows = [&](int32_t buf) {
     if (tid < kTK) {
       row_lse(sm, buf)[tid] = pl;
       row_di(sm, buf)[tid] = pd;
+    }
+    if constexpr (VEC) {
+      float* dst = vt + buf * kTK * V + (tid >> 2) * V;
+#pragma unroll
+      for (int u = 0; u < kVecPer; ++u) {
+        const int32_t l = (tid & 3) + 4 * u;
+        if (l < V) dst[l] = pv[u];
+      }
     }
   };
   desc(0, kt, mr);
@@ -661,8 +802,9 @@ __device__ __forceinline__ void store_rows_f32(float* dst, const f32x16 (&acc)[2
 
 // dK, dV of the non-global keys of one key tile (a residue class of the
 // head's dilation, like the forward's query tiles).
-template <bool BIAS, bool SEG>
-__device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm, int32_t bw) {
+template <bool BIAS, bool SEG, bool VEC>
+__device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm, float* dyn,
+                                                   int32_t bw) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t N = a.N;
@@ -723,6 +865,8 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm
   }
   BiasRule br = {nullptr, 0, 0, 0};
   if constexpr (BIAS) br = bias_rule(a, sm, h, true, 0);  // lanes hold keys: flipped table
+  if constexpr (VEC) br = {dyn, a.rel_k, 0, a.n_labels};  // the staged rows' tables
+  const float* vtab = VEC ? a.rowtab + (size_t)bh * N * a.n_labels : nullptr;
   auto band_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = lo + n * kTK;
     const int32_t cnt = min(kTK, hi - u0 + 1);
@@ -734,16 +878,17 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm
     mr = {kRange, full ? 0 : 1, 0, t0 - u0, lob, R, 0, 0, 1};
   };
   const bf16* qs = static_cast<const bf16*>(a.q) + bh * head_elems;
-  stream_rows<false, SEG>(sm, qs, dob, lse, delta, 1.f / a.scale, n_band, band_desc, gi,
-                          [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                            constexpr int32_t buf = decltype(buf_tag)::value;
-                            dkv_tile<buf, true, false, false, BIAS, SEG>(
-                                sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br,
-                                gi);
-                          });
+  stream_rows<false, SEG, VEC>(sm, qs, dob, lse, delta, 1.f / a.scale, n_band, band_desc, gi,
+                               [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                                 constexpr int32_t buf = decltype(buf_tag)::value;
+                                 dkv_tile<buf, true, false, false, BIAS, SEG, VEC>(
+                                     sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal,
+                                     br, gi);
+                               },
+                               vtab, dyn, a.n_labels);
   // the global rows reach every key (causal: rows at or after it)
   const int32_t n_gt = (ng + kTK - 1) / kTK;
-  const int32_t grows = BIAS ? kGlobAll : kGlobNone;  // mode of the global-row tiles
+  const int32_t grows = (BIAS || VEC) ? kGlobAll : kGlobNone;  // mode of the global-row tiles
   const GlobInfo gall = {grows, a.gidx, ng, gi.segb, gi.sq, gi.sq_min, gi.sq_max};
   auto glob_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t cnt = min(kTK, ng - n * kTK);
@@ -753,8 +898,8 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm
   };
   auto glob_proc = [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
     constexpr int32_t buf = decltype(buf_tag)::value;
-    dkv_tile<buf, false, true, false, BIAS, SEG>(sm, w, lane, mr, kt, ki, kpos, dead,
-                                                       a.scale_log2, a.causal, br, gall);
+    dkv_tile<buf, false, true, false, BIAS, SEG, VEC>(sm, w, lane, mr, kt, ki, kpos, dead,
+                                                        a.scale_log2, a.causal, br, gall);
   };
   const bool mine = ki < kcount && !qi_is_global(a, ki, kcount, kpos, g_first, g_last, j_lo, j_hi);
   if (a.sep) {
@@ -773,8 +918,10 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm
     }
   }
   if (ng > 0)
-    stream_rows<true, SEG>(sm, static_cast<const bf16*>(a.sep ? a.qg : a.q) + bh * head_elems,
-                           dob, lse, delta, 1.f / a.scale, n_gt, glob_desc, gall, glob_proc);
+    stream_rows<true, SEG, VEC>(sm,
+                                static_cast<const bf16*>(a.sep ? a.qg : a.q) + bh * head_elems,
+                                dob, lse, delta, 1.f / a.scale, n_gt, glob_desc, gall, glob_proc,
+                                vtab, dyn, a.n_labels);
   if (mine) {
     float* const dk = a.sep ? a.dkg : a.dk;
     float* const dv = a.sep ? a.dvg : a.dv;
@@ -808,8 +955,9 @@ __device__ __forceinline__ float* part_row(const BwdArgs& a, int32_t part, int32
 }
 
 // Workgroup wg of the B*H*ceil(n_global/128)*glob_chunks global-row ones.
-template <bool BIAS, bool SEG>
-__device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm, int32_t wg) {
+template <bool BIAS, bool SEG, bool VEC>
+__device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm, float* dyn,
+                                                  int32_t wg) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t n_gq = (a.n_global + kTQ - 1) / kTQ;
@@ -833,15 +981,21 @@ __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm
   w.di = a.delta[(size_t)bh * N + qpos];  // D_i from the launch before
   w.acc[0] = f32x16{};
   w.acc[1] = f32x16{};
+  w.c_lo = 0.f;
+  w.c_hi = 0.f;
   const int32_t j1 = a.causal ? i_max + 1 : N;
   int32_t t0, n_tiles;
   chunk_range((j1 + kTK - 1) / kTK, chunks, c, t0, n_tiles);
   GlobInfo gi = {kGlobNone, a.gidx, a.n_global, nullptr, 0, 0, 0};
   seg_info<SEG>(gi, a, bh, qpos);
   BiasRule br = {nullptr, 0, 0, 0};
-  if constexpr (BIAS) {
+  if constexpr (BIAS || VEC) {
     // the keys' global flags decide which pairs are same-kind (global keys)
-    br = bias_rule(a, sm, bh % a.H, false, 1);
+    if constexpr (VEC)
+      br = vec_rule_dq(a, dyn, bh, bh % a.H, 1,
+                       [&](int32_t r) { return qidx[min(r, qcount - 1)]; });
+    else
+      br = bias_rule(a, sm, bh % a.H, false, 1);
     const int32_t ub = t0 * kTK, ue = min(j1, ub + n_tiles * kTK);
     if (n_tiles > 0) {
       if (ue - ub <= 32 * kGMaskWords) {
@@ -864,9 +1018,10 @@ __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm
                            static_cast<const bf16*>(sep ? a.vg : a.v) + bh * head_elems, n_tiles,
                            desc, gi, [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
                              constexpr int32_t buf = decltype(buf_tag)::value;
-                             dq_tile<buf, BIAS, SEG>(sm, w, lane, mr, kt, qi, qpos, dead,
-                                                     a.scale_log2, br, gi);
+                             dq_tile<buf, BIAS, SEG, VEC>(sm, w, lane, mr, kt, qi, qpos, dead,
+                                                          a.scale_log2, br, gi);
                            });
+  if constexpr (VEC) vec_dq_epilogue(w, br, dyn, qi, lane);
   if (qi < qcount && chunks > 1) {
     store_rows_f32(part_row(a, 0, c, bh, gq * kTQ + qi), w.acc, 1.f, lane);
   } else if (qi < qcount) {
@@ -880,8 +1035,9 @@ __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm
 }
 
 // Workgroup wg of the B*H*ceil(n_global/128)*glob_chunks global-key ones.
-template <bool BIAS, bool SEG>
-__device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, BwdSmem& sm, int32_t wg) {
+template <bool BIAS, bool SEG, bool VEC>
+__device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, BwdSmem& sm, float* dyn,
+                                                   int32_t wg) {
   constexpr int32_t kTQ = TT::kTQ;
   const int32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t n_gk = (a.n_global + kTQ - 1) / kTQ;
@@ -918,9 +1074,11 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, BwdSmem& sm
   seg_info<SEG>(gi, a, bh, kpos);
   BiasRule br = {nullptr, 0, 0, 0};
   if constexpr (BIAS) br = bias_rule(a, sm, bh % a.H, true, 1);  // lanes hold global keys
+  if constexpr (VEC) br = {dyn, a.rel_k, 1, a.n_labels};  // the staged rows' tables
+  const float* vtab = VEC ? a.rowtab + (size_t)bh * N * a.n_labels : nullptr;
   // the rows' global flags: excluded with separate projections; with a bias
-  // table, the same-kind pairs
-  if ((sep || BIAS) && n_tiles > 0) {
+  // table or label vectors, the same-kind pairs
+  if ((sep || BIAS || VEC) && n_tiles > 0) {
     if (ue - ub <= 32 * kGMaskWords) {
       build_gmask<bf16>(sm, a.gidx, a.n_global, ub, 1, ue - ub, tid);
       gi.mode = kGlobBitmap;
@@ -938,21 +1096,23 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, BwdSmem& sm
   };
   const bf16* qs = static_cast<const bf16*>(a.q) + bh * head_elems;
   if (sep)
-    stream_rows<false, SEG>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
-                            [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                              constexpr int32_t buf = decltype(buf_tag)::value;
-                              dkv_tile<buf, true, false, false, BIAS, SEG>(
-                                  sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal,
-                                  br, gi);
-                            });
+    stream_rows<false, SEG, VEC>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
+                                 [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                                   constexpr int32_t buf = decltype(buf_tag)::value;
+                                   dkv_tile<buf, true, false, false, BIAS, SEG, VEC>(
+                                       sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2,
+                                       a.causal, br, gi);
+                                 },
+                                 vtab, dyn, a.n_labels);
   else
-    stream_rows<false, SEG>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
-                            [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                              constexpr int32_t buf = decltype(buf_tag)::value;
-                              dkv_tile<buf, false, false, false, BIAS, SEG>(
-                                  sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal,
-                                  br, gi);
-                            });
+    stream_rows<false, SEG, VEC>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
+                                 [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                                   constexpr int32_t buf = decltype(buf_tag)::value;
+                                   dkv_tile<buf, false, false, false, BIAS, SEG, VEC>(
+                                       sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2,
+                                       a.causal, br, gi);
+                                 },
+                                 vtab, dyn, a.n_labels);
   const size_t ro = ((size_t)bh * N + kpos) * kD;
   if (ki < kcount && chunks > 1) {
     store_rows_f32(part_row(a, 1, c, bh, gk * kTQ + ki), w.dk, 1.f, lane);
@@ -972,21 +1132,22 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, BwdSmem& sm
     w.dv[x] = f32x16{};
   }
   const int32_t n_gt = (a.n_global + kTK - 1) / kTK;
-  const int32_t grows = BIAS ? kGlobAll : kGlobNone;  // mode of the global-row tiles
+  const int32_t grows = (BIAS || VEC) ? kGlobAll : kGlobNone;  // mode of the global-row tiles
   auto glob_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t cnt = min(kTK, a.n_global - n * kTK);
     kt = {a.gidx + n * kTK, 0, 1, cnt, 0, grows};
     mr = {kRange, cnt == kTK ? 0 : 1, 0, 0, -kFar, kFar, 0, 0, 1};
   };
   const GlobInfo gall = {grows, a.gidx, a.n_global, gi.segb, gi.sq, gi.sq_min, gi.sq_max};
-  stream_rows<true, SEG>(sm, static_cast<const bf16*>(a.qg) + bh * head_elems, dob, lse, delta,
-                         1.f / a.scale, n_gt, glob_desc, gall,
-                         [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                           constexpr int32_t buf = decltype(buf_tag)::value;
-                           dkv_tile<buf, false, true, false, BIAS, SEG>(
-                               sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal, br,
-                               gall);
-                         });
+  stream_rows<true, SEG, VEC>(sm, static_cast<const bf16*>(a.qg) + bh * head_elems, dob, lse,
+                              delta, 1.f / a.scale, n_gt, glob_desc, gall,
+                              [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                                constexpr int32_t buf = decltype(buf_tag)::value;
+                                dkv_tile<buf, false, true, false, BIAS, SEG, VEC>(
+                                    sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal,
+                                    br, gall);
+                              },
+                              vtab, dyn, a.n_labels);
   if (ki < kcount) {
     store_rows_f32(a.dkg + ro, w.dk, a.scale, lane);
     store_rows_f32(a.dvg + ro, w.dv, 1.f, lane);
@@ -1185,11 +1346,13 @@ __device__ __forceinline__ int32_t band_tile_of(const BwdArgs& a, int32_t b) {
 // dK/dV and dQ workgroups in one launch, the dK/dV ones (the longer work)
 // first: the two add into different gradients, and D_i came from a launch
 // before, so they run side by side and fill each other's tails.
-template <bool BIAS, bool SEG>
+// VEC: key-side label vectors (their tables in the dynamic LDS).
+template <bool BIAS, bool SEG, bool VEC>
 __global__ __launch_bounds__(TT::kThreads)
-__attribute__((amdgpu_waves_per_eu(BIAS ? 2 : 3)))
+__attribute__((amdgpu_waves_per_eu((BIAS || VEC) ? 2 : 3)))
 void bwd_mfma_kernel(BwdArgs a, int32_t grid_kv) {
   __shared__ BwdSmem sm;
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
   const int32_t gw = glob_wg_padded(a);
   const int32_t nb = grid_kv - gw;  // band slots per pass
   int32_t b = (int32_t)blockIdx.x;
@@ -1198,9 +1361,9 @@ void bwd_mfma_kernel(BwdArgs a, int32_t grid_kv) {
     const int32_t bw = band_tile_of(a, kv ? b : b - nb);
     if (bw < 0) return;
     if (kv)
-      dkv_band_workgroup<BIAS, SEG>(a, sm, bw);
+      dkv_band_workgroup<BIAS, SEG, VEC>(a, sm, dyn, bw);
     else
-      dq_band_workgroup<BIAS, SEG>(a, sm, bw);
+      dq_band_workgroup<BIAS, SEG, VEC>(a, sm, dyn, bw);
     return;
   }
   b -= 2 * nb;  // global ranges: dK/dV, then dQ
@@ -1208,9 +1371,9 @@ void bwd_mfma_kernel(BwdArgs a, int32_t grid_kv) {
   if (!kv) b -= gw;
   if (b >= glob_wg(a)) return;
   if (kv)
-    dkv_glob_workgroup<BIAS, SEG>(a, sm, b);
+    dkv_glob_workgroup<BIAS, SEG, VEC>(a, sm, dyn, b);
   else
-    dq_glob_workgroup<BIAS, SEG>(a, sm, b);
+    dq_glob_workgroup<BIAS, SEG, VEC>(a, sm, dyn, b);
 }
 
 // The global rows' dQ and the global keys' dK, dV from the ranges' partial
@@ -1255,6 +1418,40 @@ void bwd_dil_mfma_kernel(BwdArgs a, DilPart kv, int64_t grid_kv, DilPart q) {
     dkv_dil_workgroup(a, sm, kv, b);
   else if (q.k >= 0)
     dq_dil_workgroup(a, sm, q, b - grid_kv);
+}
+
+// Key-side label vectors (ETC page, §3.4 "Relative Position Encoding"): each
+// row's table T[row][l] = q'_row . a_l + b_l / scale (b the scalar table, if
+// any), in q.k units, q' the row's query (qg for a global row with separate
+// projections). 64 rows of one head per workgroup, one thread per row, the
+// head's vectors in LDS.
+__global__ __launch_bounds__(64) void bwd_rowtab_kernel(BwdArgs a) {
+  __shared__ float av[kMaxLabels * kD];
+  const int32_t V = a.n_labels;
+  const int32_t per = (a.N + 63) / 64;
+  const int32_t bh = (int32_t)(blockIdx.x / per), t = (int32_t)(blockIdx.x % per);
+  const int32_t h = bh % a.H;
+  for (int32_t x = threadIdx.x; x < V * kD; x += 64) av[x] = a.rel_vec[(size_t)h * V * kD + x];
+  __syncthreads();
+  const int32_t i = t * 64 + (int32_t)threadIdx.x;
+  if (i >= a.N) return;
+  const bool g = a.sep && a.n_global > 0 && sorted_contains(a.gidx, a.n_global, i);
+  const bf16* qr = static_cast<const bf16*>(g ? a.qg : a.q) + ((size_t)bh * a.N + i) * kD;
+  float qv[kD];
+#pragma unroll
+  for (int c = 0; c < kD / 8; ++c) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(qr + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[8 * c + e] = (float)x[e];
+  }
+  float* dst = a.rowtab + ((size_t)bh * a.N + i) * V;
+  const float* sb = a.rel_bias ? a.rel_bias + (size_t)h * V : nullptr;
+  for (int32_t l = 0; l < V; ++l) {
+    float acc = sb ? sb[l] / a.scale : 0.f;
+#pragma unroll
+    for (int d = 0; d < kD; ++d) acc = __builtin_fmaf(qv[d], av[l * kD + d], acc);
+    dst[l] = acc;
+  }
 }
 
 // zeros into three fp32 buffers of n4 float4 each (a kernel: no memset)
@@ -1329,14 +1526,32 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream) {
   if (2 * grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 g((uint32_t)(2 * grid)), t(TT::kThreads);
   const int32_t gkv = (int32_t)grid;
-  if (a.rel_bias && a.seg)
-    hipLaunchKernelGGL((bwd_mfma_kernel<true, true>), g, t, 0, stream, a, gkv);
-  else if (a.rel_bias)
-    hipLaunchKernelGGL((bwd_mfma_kernel<true, false>), g, t, 0, stream, a, gkv);
-  else if (a.seg)
-    hipLaunchKernelGGL((bwd_mfma_kernel<false, true>), g, t, 0, stream, a, gkv);
-  else
-    hipLaunchKernelGGL((bwd_mfma_kernel<false, false>), g, t, 0, stream, a, gkv);
+  if (a.rel_vec) {  // the tables (scalar bias folded in), the label sums, the vectors
+    if (!a.rowtab || a.n_labels != 2 * a.rel_k + 1 || a.n_labels > kMaxLabels)
+      return hipErrorInvalidValue;
+    const uint32_t dyn = (uint32_t)((2 * TT::kTQ + kD) * a.n_labels * sizeof(float));
+    if (a.seg)
+      hipLaunchKernelGGL((bwd_mfma_kernel<false, true, true>), g, t, dyn, stream, a, gkv);
+    else
+      hipLaunchKernelGGL((bwd_mfma_kernel<false, false, true>), g, t, dyn, stream, a, gkv);
+  } else if (a.rel_bias && a.seg) {
+    hipLaunchKernelGGL((bwd_mfma_kernel<true, true, false>), g, t, 0, stream, a, gkv);
+  } else if (a.rel_bias) {
+    hipLaunchKernelGGL((bwd_mfma_kernel<true, false, false>), g, t, 0, stream, a, gkv);
+  } else if (a.seg) {
+    hipLaunchKernelGGL((bwd_mfma_kernel<false, true, false>), g, t, 0, stream, a, gkv);
+  } else {
+    hipLaunchKernelGGL((bwd_mfma_kernel<false, false, false>), g, t, 0, stream, a, gkv);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rowtab(const BwdArgs& a, hipStream_t stream) {
+  if (!a.rel_vec || a.n_band_wg <= 0) return hipSuccess;
+  if (!a.rowtab || a.n_labels < 1 || a.n_labels > kMaxLabels) return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)a.B * a.H * ((a.N + 63) / 64);
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_rowtab_kernel, dim3((uint32_t)blocks), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

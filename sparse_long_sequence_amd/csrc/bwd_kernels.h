@@ -36,6 +36,10 @@ struct BwdArgs {
   // chunk order by a reduce launch; glob_chunks == 1 writes directly
   float* gpart;
   int32_t glob_chunks;
+  // key-side label vectors on the MFMA path: each row's label table
+  // [B*H*N][n_labels] (q . a_l plus the scalar bias over scale, in q.k units),
+  // written by a launch before the MFMA one
+  float* rowtab;
   // LongNet mixture (launch_dilated_bwd only): patterns (w, r)
   int32_t n_pairs;
   int32_t pw[kMaxPairs], pr[kMaxPairs];
@@ -46,6 +50,7 @@ constexpr int32_t kMaxGlobChunks = 16;  // key (row) ranges per global tile
 hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream);
 hipError_t launch_glob_reduce(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream);  // dK/dV and dQ, D_i given
+hipError_t launch_rowtab(const BwdArgs& a, hipStream_t stream);    // a.rowtab from q, qg, rel_vec
 hipError_t launch_dilated_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_dilated_bwd_mfma(const BwdArgs& a, hipStream_t stream);
 int32_t host_glob_part_rows(int32_t N);  // partial-sum rows per head in the workspace

@@ -162,11 +162,12 @@ def test_fixed_argument_errors(L):
 def test_backward_argument_errors(L):
     d = LaDims(1, 2, 128, 64, la.LA_BF16)
     need = la.la_attn_backward_workspace_size(d)
-    # D_i per row (1 KiB), an int32 rank per position, partial dQ, dK, dV of 128 rows per head
-    assert need == 1 * 2 * 128 * 4 + 512 + 3 * 1 * 2 * 128 * 64 * 4
+    # D_i per row (1 KiB), an int32 rank per position, partial dQ, dK, dV of 128 rows per head,
+    # then (bf16) a label table of up to 64 fp32 entries per row
+    assert need == 1 * 2 * 128 * 4 + 512 + 3 * 1 * 2 * 128 * 64 * 4 + 1 * 2 * 128 * 64 * 4
     assert la.la_attn_backward_workspace_size(LaDims(1, 2, 128, 64, la.LA_F32)) == 1024 + 512
     assert la.la_attn_backward_workspace_size(LaDims(2, 3, 8192, 64, la.LA_BF16)) == (
-        2 * 3 * 8192 * 4 + 8192 * 4 + 3 * 2 * 3 * 2048 * 64 * 4)
+        2 * 3 * 8192 * 4 + 8192 * 4 + 3 * 2 * 3 * 2048 * 64 * 4 + 2 * 3 * 8192 * 64 * 4)
     ext = la.LaAttnBwdExt(None, None, None, None, None, None, None, FAKE, need)
 
     def call(dims=d, q=FAKE, lse=FAKE, dq=FAKE, gidx=None, n_global=0, radius=4, causal=0,

