@@ -189,6 +189,17 @@ __device__ __forceinline__ void seg_mask(float* s, const TT::Smem& sm, int32_t s
     s[r] = sm.kseg[BUF][TT::key_const(sb, r) + kl] == sq ? s[r] : kNegInf;
 }
 
+// Which clipped-distance label every pair of a sub-tile takes, from its keys'
+// and rows' first and last positions (both non-decreasing): 1 every pair at
+// key - row <= -k (label 0), 2 every pair at key - row >= k (label 2k), 0
+// mixed. Wave-uniform.
+__device__ __forceinline__ int32_t label_side(int32_t kfirst, int32_t klast, int32_t rfirst,
+                                              int32_t rlast, int32_t k) {
+  if (klast - rfirst <= -k) return 1;
+  if (kfirst - rlast >= k) return 2;
+  return 0;
+}
+
 // Key-side label vectors, dQ pass: the same-kind pairs' dS of sub-tile sb by
 // label (clipped distance key - row): the two clipped labels into the lane's
 // registers, the others into C[qi][l] in LDS (each such (row, label) pair has
@@ -288,16 +299,32 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
   const int32_t r1 = (mr.use_qpos ? __builtin_amdgcn_readlane(qpos, TT::kRowsPerBlock - 1)
                                   : __builtin_amdgcn_readlane(qi, TT::kRowsPerBlock - 1)) + mr.ref_off;
   TileBias tb = {false, false};
-  if constexpr (BIAS || VEC) tb = tile_bias<BUF>(sm, br, kt);
+  int32_t q0 = 0, q1 = 0;  // the wave's first and last row positions
+  if constexpr (BIAS || VEC) {
+    tb = tile_bias<BUF>(sm, br, kt);
+    q0 = __builtin_amdgcn_readlane(qpos, 0);
+    q1 = __builtin_amdgcn_readlane(qpos, TT::kRowsPerBlock - 1);
+  }
 #pragma unroll
   for (int sb = 0; sb < TT::kSub; ++sb) {
     const int32_t cls = dead ? kEmpty : classify<bf16>(mr, kt.count, sb, r0, r1);
     if (cls == kEmpty) continue;
+    // one clipped label for the whole sub-tile: its table entry joins the
+    // exponent's offset (per lane), no per-element lookup
+    int32_t side = 0;
+    if constexpr (BIAS || VEC) {
+      if (tb.on && tb.same)
+        side = label_side(__builtin_amdgcn_readfirstlane(sm.kpos[BUF][32 * sb]),
+                          __builtin_amdgcn_readfirstlane(sm.kpos[BUF][32 * sb + 31]), q0, q1, br.k);
+    }
     float s[TT::kNS], dp[TT::kNS];
     tile_dots(&sm.k[BUF][0], w.qf, lane, sb, s);
     tile_dots(&sm.v[BUF][0], w.df, lane, sb, dp);
+    float off = -w.lse2;
     if constexpr (BIAS || VEC) {
-      if (tb.on) add_bias<bf16>(s, sm, BUF, br, sb, qi, qpos, lane, tb.same);
+      if (tb.on && side == 0) add_bias<bf16>(s, sm, BUF, br, sb, qi, qpos, lane, tb.same);
+      if (side != 0)
+        off = __builtin_fmaf(br.tab[qi * br.row_stride + (side == 1 ? 0 : 2 * br.k)], c, off);
     }
     if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, qi, qpos, lane);
     if (SEG && seg_check) seg_mask<BUF>(s, sm, gs.sq, sb, lane);
@@ -308,15 +335,25 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 8 * t + 2 * i;
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -w.lse2));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], c, -w.lse2));
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, off));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], c, off));
         ds[e] = p0 * (dp[e] - w.di);
         ds[e + 1] = p1 * (dp[e + 1] - w.di);
         G.p[t][i] = pack_bf16x2(ds[e], ds[e + 1]);
       }
     }
     if constexpr (VEC) {
-      if (tb.on) vec_label_sums<BUF>(w, ds, sm, br, sb, qi, qpos, lane, tb.same);
+      if (tb.on && side == 0) {
+        vec_label_sums<BUF>(w, ds, sm, br, sb, qi, qpos, lane, tb.same);
+      } else if (side != 0) {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < TT::kNS; ++e) t += ds[e];
+        if (side == 1)
+          w.c_lo += t;
+        else
+          w.c_hi += t;
+      }
     }
     acc_transposed<BUF>(&sm.k[0][0], w.acc, lane, sb, G);
   }
@@ -630,15 +667,38 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
   if constexpr (EXCL_G)
     any_g = kt.gmode != kGlobNone && (__builtin_amdgcn_readfirstlane(sm.gcls[BUF]) & 1) != 0;
   TileBias tb = {false, false};
-  if constexpr (BIAS || VEC) tb = tile_bias<BUF>(sm, br, kt);
+  int32_t kq0 = 0, kq1 = 0;  // the wave's first and last key positions
+  if constexpr (BIAS || VEC) {
+    tb = tile_bias<BUF>(sm, br, kt);
+    kq0 = __builtin_amdgcn_readlane(kpos, 0);
+    kq1 = __builtin_amdgcn_readlane(kpos, TT::kRowsPerBlock - 1);
+  }
   int32_t kl = TT::key_lane(lane);
   asm("" : "+v"(kl));  // opaque per call, as in mask_tile
 #pragma unroll
   for (int sb = 0; sb < TT::kSub; ++sb) {
     const int32_t cls = dead ? kEmpty : classify<bf16>(mr, kt.count, sb, r0, r1);
     if (cls == kEmpty) continue;
+    // one clipped label for the whole sub-tile: VEC starts the score MFMAs
+    // from the offsets with the rows' entries added; the scalar table's entry
+    // joins the exponent
+    int32_t side = 0;
+    if constexpr (BIAS || VEC) {
+      if (tb.on && tb.same)
+        side = label_side(kq0, kq1, __builtin_amdgcn_readfirstlane(sm.kpos[BUF][32 * sb]),
+                          __builtin_amdgcn_readfirstlane(sm.kpos[BUF][32 * sb + 31]), br.k);
+    }
+    const float* lsrc = row_lse(sm, BUF);
+    if constexpr (VEC) {
+      if (side != 0)
+        lsrc = br.tab + 2 * kTK * br.row_stride + (side == 1 ? 0 : 2 * kTK) + BUF * kTK;
+    }
+    float coff = 0.f;
+    if constexpr (BIAS) {
+      if (side != 0) coff = br.tab[side == 1 ? 2 * br.k : 0] * c;  // the flipped table
+    }
     // the lane's 16 rows are 4 runs of 4 (key_const): one 16-byte read per run
-    const f32x4* ls = reinterpret_cast<const f32x4*>(row_lse(sm, BUF) + kl);
+    const f32x4* ls = reinterpret_cast<const f32x4*>(lsrc + kl);
     const f32x4* dd = reinterpret_cast<const f32x4*>(row_di(sm, BUF) + kl);
     float s[TT::kNS], dp[TT::kNS];
     {  // s = q.k - lse / scale, dp = dO.v - D_i
@@ -657,10 +717,10 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
       tile_dots(&sm.v[BUF][0], w.vf, lane, sb, dp, d0);
     }
     if constexpr (BIAS) {
-      if (tb.on) add_bias<bf16>(s, sm, BUF, br, sb, ki, kpos, lane, tb.same);
+      if (tb.on && side == 0) add_bias<bf16>(s, sm, BUF, br, sb, ki, kpos, lane, tb.same);
     }
     if constexpr (VEC) {
-      if (tb.on) vec_add_rows<BUF>(s, sm, br, sb, kpos, kl, tb.same);
+      if (tb.on && side == 0) vec_add_rows<BUF>(s, sm, br, sb, kpos, kl, tb.same);
     }
     if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, ki, kpos, lane);
     if (SEG && seg_check) seg_mask<BUF>(s, sm, gs.sq, sb, lane);
@@ -683,8 +743,8 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 8 * t + 2 * i;
-        const float p0 = __builtin_amdgcn_exp2f(s[e] * c);
-        const float p1 = __builtin_amdgcn_exp2f(s[e + 1] * c);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, coff));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], c, coff));
         G.p[t][i] = pack_bf16x2(p0 * dp[e], p1 * dp[e + 1]);
         P.p[t][i] = pack_bf16x2(p0, p1);
       }
@@ -701,7 +761,9 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
 // lse (times lse_mul) and D_i, read with the tile's loads, written to LDS
 // with its staging (SEG: the rows' segment ids are staged as the keys' are).
 // VEC: also the rows' label tables (tab: the head's [N][V] tables) into
-// vt + buf * kTK * V.
+// vt + buf * kTK * V, and after the two buffers' tables the rows' offsets with
+// the clipped labels' entries added, -lse * lse_mul + T[row][0] ([2][kTK])
+// then + T[row][V - 1] ([2][kTK]).
 template <bool GATHER, bool SEG = false, bool VEC = false, typename Desc, typename Proc>
 __device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const bf16* dob,
                                             const float* lse, const float* delta, float lse_mul,
@@ -714,7 +776,7 @@ __device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const b
   TT::Prefetch pf;
   KeyTile kt;
   MaskRule mr;
-  float pl = 0.f, pd = 0.f;
+  float pl = 0.f, pd = 0.f, plo = 0.f, phi = 0.f;
   // VEC: four threads per row, labels tid % 4 + 4u
   constexpr int32_t kVecPer = VEC ? kMaxLabels / 4 : 1;
   float pv[kVecPer];
@@ -724,6 +786,10 @@ __device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const b
       const float l = lse[p];
       pl = l == kNegInf ? kNegInf : -(l * lse_mul);
       pd = -delta[p];
+      if constexpr (VEC) {
+        plo = pl + tab[(size_t)p * V];
+        phi = pl + tab[(size_t)p * V + V - 1];
+      }
     }
     if constexpr (VEC) {
       if (t.count > 0) {
@@ -742,6 +808,10 @@ __device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const b
       row_di(sm, buf)[tid] = pd;
     }
     if constexpr (VEC) {
+      if (tid < kTK) {
+        vt[2 * kTK * V + buf * kTK + tid] = plo;
+        vt[2 * kTK * V + 2 * kTK + buf * kTK + tid] = phi;
+      }
       float* dst = vt + buf * kTK * V + (tid >> 2) * V;
 #pragma unroll
       for (int u = 0; u < kVecPer; ++u) {
@@ -1529,6 +1599,8 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream) {
   if (a.rel_vec) {  // the tables (scalar bias folded in), the label sums, the vectors
     if (!a.rowtab || a.n_labels != 2 * a.rel_k + 1 || a.n_labels > kMaxLabels)
       return hipErrorInvalidValue;
+    // dQ: rows' tables, label sums, vectors; dK/dV: two tiles' tables and
+    // four offset rows (2 * kTQ * V >= 2 * kTK * V + 4 * kTK for V >= 3)
     const uint32_t dyn = (uint32_t)((2 * TT::kTQ + kD) * a.n_labels * sizeof(float));
     if (a.seg)
       hipLaunchKernelGGL((bwd_mfma_kernel<false, true, true>), g, t, dyn, stream, a, gkv);
