@@ -1493,33 +1493,48 @@ void bwd_dil_mfma_kernel(BwdArgs a, DilPart kv, int64_t grid_kv, DilPart q) {
 // Key-side label vectors (ETC page, §3.4 "Relative Position Encoding"): each
 // row's table T[row][l] = q'_row . a_l + b_l / scale (b the scalar table, if
 // any), in q.k units, q' the row's query (qg for a global row with separate
-// projections). 64 rows of one head per workgroup, one thread per row, the
-// head's vectors in LDS.
-__global__ __launch_bounds__(64) void bwd_rowtab_kernel(BwdArgs a) {
-  __shared__ float av[kMaxLabels * kD];
+// projections). 64 rows of one head per workgroup, four threads per row
+// (labels l = part + 4u), the head's vectors in LDS (rows padded to D + 4
+// floats: the four labels a wave reads at once, 16 bytes each, fall on
+// different banks).
+__global__ __launch_bounds__(256) void bwd_rowtab_kernel(BwdArgs a) {
+  constexpr int32_t kRow = kD + 4;
+  __shared__ __attribute__((aligned(16))) float av[kMaxLabels * kRow];
   const int32_t V = a.n_labels;
   const int32_t per = (a.N + 63) / 64;
   const int32_t bh = (int32_t)(blockIdx.x / per), t = (int32_t)(blockIdx.x % per);
   const int32_t h = bh % a.H;
-  for (int32_t x = threadIdx.x; x < V * kD; x += 64) av[x] = a.rel_vec[(size_t)h * V * kD + x];
+  const int32_t i = t * 64 + (int32_t)(threadIdx.x >> 2), part = (int32_t)(threadIdx.x & 3);
+  const bool live = i < a.N;
+  // the row's query loads go out before the vectors' staging
+  bf16x8 qx[kD / 8];
+  if (live) {
+    const bool g = a.sep && a.n_global > 0 && sorted_contains(a.gidx, a.n_global, i);
+    const bf16* qr = static_cast<const bf16*>(g ? a.qg : a.q) + ((size_t)bh * a.N + i) * kD;
+#pragma unroll
+    for (int c = 0; c < kD / 8; ++c) qx[c] = *reinterpret_cast<const bf16x8*>(qr + 8 * c);
+  }
+  for (int32_t x = threadIdx.x; x < V * kD; x += 256)
+    av[(x / kD) * kRow + x % kD] = a.rel_vec[(size_t)h * V * kD + x];
   __syncthreads();
-  const int32_t i = t * 64 + (int32_t)threadIdx.x;
-  if (i >= a.N) return;
-  const bool g = a.sep && a.n_global > 0 && sorted_contains(a.gidx, a.n_global, i);
-  const bf16* qr = static_cast<const bf16*>(g ? a.qg : a.q) + ((size_t)bh * a.N + i) * kD;
+  if (!live) return;
   float qv[kD];
 #pragma unroll
   for (int c = 0; c < kD / 8; ++c) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(qr + 8 * c);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[8 * c + e] = (float)x[e];
+    for (int e = 0; e < 8; ++e) qv[8 * c + e] = (float)qx[c][e];
   }
   float* dst = a.rowtab + ((size_t)bh * a.N + i) * V;
   const float* sb = a.rel_bias ? a.rel_bias + (size_t)h * V : nullptr;
-  for (int32_t l = 0; l < V; ++l) {
+  for (int32_t l = part; l < V; l += 4) {
     float acc = sb ? sb[l] / a.scale : 0.f;
+    const f32x4* al = reinterpret_cast<const f32x4*>(av + l * kRow);
 #pragma unroll
-    for (int d = 0; d < kD; ++d) acc = __builtin_fmaf(qv[d], av[l * kD + d], acc);
+    for (int c = 0; c < kD / 4; ++c) {
+      const f32x4 x = al[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(qv[4 * c + e], x[e], acc);
+    }
     dst[l] = acc;
   }
 }
@@ -1623,7 +1638,7 @@ hipError_t launch_rowtab(const BwdArgs& a, hipStream_t stream) {
   if (!a.rowtab || a.n_labels < 1 || a.n_labels > kMaxLabels) return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)a.B * a.H * ((a.N + 63) / 64);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_rowtab_kernel, dim3((uint32_t)blocks), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(bwd_rowtab_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
