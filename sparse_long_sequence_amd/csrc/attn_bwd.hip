@@ -451,6 +451,7 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_rows_kernel(BwdArgs a) 
       int32_t j = x < n ? key_of(x) : -1;
       const int32_t lb = j >= 0 ? bwd_pair(a, b, i, j, gi, a.grank[j], segb) : -1;
       if (lb == -2) j = -1;
+      if (__ballot(j >= 0) == 0ull) continue;  // no lane has a pair (masks, labels)
       const int32_t r = j >= 0 ? j : i;
       uint4 kc[8], vc[8];
       load_row(K + (size_t)r * kD, kc);
@@ -542,6 +543,7 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_rows_kernel(BwdArgs a)
       int32_t i = x < n ? row_of(x) : -1;
       const int32_t lb = i >= 0 ? bwd_pair(a, b, i, j, a.grank[i], gj, segb) : -1;
       if (lb == -2) i = -1;
+      if (__ballot(i >= 0) == 0ull) continue;  // no lane has a pair (masks, labels)
       const int32_t r = i >= 0 ? i : j;
       uint4 qc[8], oc[8];
       load_row(Q + (size_t)r * kD, qc);
