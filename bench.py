@@ -319,8 +319,9 @@ def copy_probe(dev, reps=3):
 def bench_backward(dev, args):
     """Backward calls, timed like the forward: the Longformer-base band + global
     backward (dq, dk, dv and the separate global projections' gradients), the
-    LongNet mixture's backward, the ETC shape's (with its bias table, and with
-    key-side label vectors) and the packed-documents one (segment masks). Useful work: 10*D FLOPs per allowed
+    LongNet mixture's backward, the ETC shape's (with its bias table, with
+    key-side label vectors, and with the structured inputs' label matrices and
+    piece masks) and the packed-documents one (segment masks). Useful work: 10*D FLOPs per allowed
     pair (q.k and dO.v recomputed, then dV, dQ and dK, 2*D each)."""
     import torch
 
@@ -330,7 +331,7 @@ def bench_backward(dev, args):
 
     res = {}
     for w in (W.LONGFORMER_BASE, W.LONGNET_SHARE, W.WORKLOADS["etc-ng256-nl4096-r84-relk12"],
-              W.PACKED, W.ETC_VECTORS):
+              W.PACKED, W.ETC_VECTORS, W.ETC_STRUCTURED):
         log(f"bench backward: {w.name}")
         c = Call(w, dev)
         c()
@@ -343,8 +344,8 @@ def bench_backward(dev, args):
         else:
             call = la.bind_attn_backward(c.q, c.k, c.v, c.out, c.lse, dout, c.g, w.radius,
                                          w.dilation, w.causal, qg=c.qg, kg=c.kg, vg=c.vg,
-                                         rel_bias=c.rb, rel_vec=c.rv, rel_k=w.rel_k or None,
-                                         seg_ids=c.seg)
+                                         rel_bias=c.rb, rel_vec=c.rv, seg_ids=c.seg,
+                                         **{"rel_k": w.rel_k or None, **c.lab})
         steps = max(3, min(args.steps, 20))
         region_ms, mean_ms, med_ms, _ = time_calls(call, steps, min(args.warmup, 3), args.settle,
                                                    cold=False)

@@ -260,12 +260,11 @@ typedef struct {
  *  dq, dk, dv   device fp32 [B,H,N,D] outputs; must not alias any input.
  * Requires ext->workspace (its contents on entry are ignored). Pointers 16-byte
  * aligned. Errors as for la_attn_forward. Two to four launches on `stream`
- * (bf16 with the 2k+1 distance labels alone, if any (a scalar table, label
- * vectors or both; no label matrices), and segment ids, if given, masking
- * every piece: D_i, with label vectors each row's label table, then one MFMA
+ * (bf16: D_i, with label vectors, or a scalar table under label matrices,
+ * piece masks or a wider vocabulary, each row's label table, then one MFMA
  * launch for dQ, dK and dV, the global rows and keys split over up to 16 key
  * or row ranges, and with several ranges one launch adding their partial sums
- * in a fixed order; otherwise global ranks, dQ and D_i, dK and dV), no
+ * in a fixed order; fp32: global ranks, dQ and D_i, dK and dV), no
  * allocation; results are bitwise reproducible. */
 la_status la_attn_backward(const la_dims *dims, const void *q, const void *k, const void *v,
                            const int32_t *global_idx, int32_t n_global, int32_t radius,

@@ -146,11 +146,8 @@ la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, co
   a.scale = (float)(1.0 / sqrt((double)kDHead));
   a.scale_log2 = (float)(1.0 / sqrt((double)kDHead) * 1.4426950408889634);
   a.glob_chunks = 1;
-  // the MFMA path: bf16 with the 2k+1 distance labels alone (a scalar table,
-  // key-side label vectors or both; no label matrices) and segment ids that
-  // mask every pair
-  if (dims->dtype == LA_BF16 && !a.glabel && !a.llabel && (!a.seg || a.seg_pieces == 15) &&
-      (!(a.rel_bias || a.rel_vec) || a.n_labels == 2 * rel_k + 1)) {
+  // the MFMA path: every bf16 call
+  if (dims->dtype == LA_BF16) {
     const int32_t tq = la::host_query_tile(dims->dtype);
     int32_t tiles = 0;
     for (int32_t h = 0; h < dims->H; ++h)
@@ -162,7 +159,11 @@ la_status la_attn_backward(const la_dims* dims, const void* q, const void* k, co
     a.glob_chunks = la::host_glob_chunks((int64_t)dims->B * dims->H, dims->N, n_global);
     a.gpart = reinterpret_cast<float*>(reinterpret_cast<char*>(a.grank) +
                                        align_up((size_t)dims->N * sizeof(int32_t)));
-    if (a.rel_vec)
+    // row tables: with label vectors, and with a scalar table under label
+    // matrices, piece masks or a wider vocabulary
+    const bool lbl = a.glabel || a.llabel || (a.seg && a.seg_pieces != 15) ||
+                     ((a.rel_bias || a.rel_vec) && a.n_labels != 2 * rel_k + 1);
+    if (a.rel_vec || (lbl && a.rel_bias))
       a.rowtab = reinterpret_cast<float*>(reinterpret_cast<char*>(a.gpart) + bwd_part_bytes(dims));
   }
   hipError_t e = la::launch_attn_bwd(a, dims->dtype, stream);

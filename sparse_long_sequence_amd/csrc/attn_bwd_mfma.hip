@@ -189,6 +189,90 @@ __device__ __forceinline__ void seg_mask(float* s, const TT::Smem& sm, int32_t s
     s[r] = sm.kseg[BUF][TT::key_const(sb, r) + kl] == sq ? s[r] : kNegInf;
 }
 
+// Per-pair label matrices and per-piece segment masks (ETC page, §3.4
+// "Per-instance attention masks" and "Relative Position Encoding", Step 1 and
+// its implementation note), for the tiles that hold a global token: the
+// batch row's label matrices (glabel [n_global][N], llabel [N][n_global]) and
+// segment ids, the vocabulary size and clip k, the pieces the segment ids
+// mask (bits g2g 1, g2l 2, l2g 4, l2l 8), the lane's own global rank (its
+// row in the dQ pass, its key in the dK/dV pass; -1 not global) and whether
+// row tables exist.
+struct LblCtx {
+  const uint8_t* glabel;
+  const uint8_t* llabel;
+  const int32_t* segb;
+  int32_t N, n_global, V, k, pieces, rank, tabs, avec;
+};
+
+__device__ __forceinline__ LblCtx lbl_ctx(const BwdArgs& a, int32_t bh, int32_t rank) {
+  const int32_t b = bh / a.H;
+  return {a.glabel ? a.glabel + (size_t)b * a.n_global * a.N : nullptr,
+          a.llabel ? a.llabel + (size_t)b * a.N * a.n_global : nullptr,
+          a.seg ? a.seg + (size_t)b * a.N : nullptr,
+          a.N,  a.n_global,    a.n_labels, a.rel_k, a.seg_pieces, rank, a.rowtab != nullptr,
+          a.rel_vec != nullptr};
+}
+
+// Pair (row i, key j) with global ranks gi, gj: -2 masked (a segment mask of
+// its piece or a masking label), -1 kept without a label (a mixed pair keeping
+// its usual label, or no tables), else its label (explicit, or the clipped
+// distance of a same-kind pair).
+__device__ __forceinline__ int32_t lbl_pair(const LblCtx& L, int32_t i, int32_t gi, int32_t j,
+                                            int32_t gj) {
+  const bool ig = gi >= 0, jg = gj >= 0;
+  if (L.segb) {
+    const int32_t piece = ig ? (jg ? 1 : 2) : (jg ? 4 : 8);
+    if ((L.pieces & piece) && L.segb[i] != L.segb[j]) return -2;
+  }
+  int32_t l = kLabelDist;
+  if (ig && L.glabel)
+    l = L.glabel[(size_t)gi * L.N + j];
+  else if (!ig && jg && L.llabel)
+    l = L.llabel[(size_t)i * L.n_global + gj];
+  if (l != kLabelDist && l >= L.V) return -2;
+  if (!L.tabs) return -1;
+  if (l == kLabelDist) {
+    if (ig != jg) return -1;
+    l = min(max(j - i, -L.k), L.k) + L.k;
+  }
+  return l;
+}
+
+// dQ pass, a tile holding a global token: each pair's label by lbl_pair (the
+// lane's row against the staged keys), its table entry (trow: the lane's row
+// table, or null) added and masked pairs excluded; lab keeps the labels.
+template <int32_t BUF>
+__device__ __forceinline__ void lbl_scores_dq(float* s, int32_t* lab, const TT::Smem& sm,
+                                              const LblCtx& L, int sb, int32_t qpos,
+                                              int32_t lane, const float* trow) {
+  int32_t kl = TT::key_lane(lane);
+  asm("" : "+v"(kl));  // opaque per call, as in mask_tile
+#pragma unroll
+  for (int r = 0; r < TT::kNS; ++r) {
+    const int32_t kj = TT::key_const(sb, r) + kl;
+    const int32_t l = lbl_pair(L, qpos, L.rank, sm.kpos[BUF][kj], sm.kgrank[BUF][kj]);
+    lab[r] = l;
+    if (l == -2) s[r] = kNegInf;
+    else if (l >= 0 && trow) s[r] += trow[l];
+  }
+}
+
+// dQ pass with label vectors, a tile holding a global token: the labelled
+// pairs' dS into the row's label sums, one half-wave at a time (the two lanes
+// of a row may share a label; lanes of one half hold different rows).
+__device__ __forceinline__ void lbl_sums_dq(const float* ds, const int32_t* lab, float* crow,
+                                            int32_t lane) {
+  const int32_t hh = lane >> 5;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (hh == half) {
+#pragma unroll
+      for (int r = 0; r < TT::kNS; ++r)
+        if (lab[r] >= 0) atomicAdd(crow + lab[r], ds[r]);
+    }
+  }
+}
+
 // Which clipped-distance label every pair of a sub-tile takes, from its keys'
 // and rows' first and last positions (both non-decreasing): 1 every pair at
 // key - row <= -k (label 0), 2 every pair at key - row >= k (label 2k), 0
@@ -229,24 +313,30 @@ __device__ __forceinline__ void vec_label_sums(DqWave& w, const float* ds, const
 // position pos(r); rows past the tile repeat its last), the label sums
 // zeroed and the head's vectors a_l (fp32 [V][D]) into the dynamic LDS; visible
 // after the tile loop's first barrier.
-template <typename Pos>
+template <bool LBL, typename Pos>
 __device__ __forceinline__ BiasRule vec_rule_dq(const BwdArgs& a, float* dyn, int32_t bh,
                                                 int32_t h, int32_t lane_is_global_kind,
                                                 Pos pos) {
+  // (without LBL the tables and vectors are always there)
+  const bool tabs = !LBL || a.rowtab != nullptr, avec = !LBL || a.rel_vec != nullptr;
   const int32_t V = a.n_labels, tid = threadIdx.x;
-  const float* tb = a.rowtab + (size_t)bh * a.N * V;
+  const float* tb = tabs ? a.rowtab + (size_t)bh * a.N * V : nullptr;
   float* rt = dyn;
   float* C = dyn + TT::kTQ * V;
   float* A = dyn + 2 * TT::kTQ * V;
   const int32_t r = tid >> 1, l0 = tid & 1;  // two threads per row
-  const float* src = tb + (size_t)pos(r) * V;
-  for (int32_t l = l0; l < V; l += 2) {
-    rt[r * V + l] = src[l];
-    C[r * V + l] = 0.f;
+  if (tabs) {
+    const float* src = tb + (size_t)pos(r) * V;
+    for (int32_t l = l0; l < V; l += 2) {
+      rt[r * V + l] = src[l];
+      C[r * V + l] = 0.f;
+    }
   }
-  const float* av = a.rel_vec + (size_t)h * V * kD;
-  for (int32_t x = tid; x < V * kD; x += TT::kThreads) A[x] = av[x];
-  return {dyn, a.rel_k, lane_is_global_kind, V};
+  if (avec) {
+    const float* av = a.rel_vec + (size_t)h * V * kD;
+    for (int32_t x = tid; x < V * kD; x += TT::kThreads) A[x] = av[x];
+  }
+  return {tabs ? dyn : nullptr, a.rel_k, lane_is_global_kind, V};
 }
 
 // Key-side label vectors, dQ workgroup end: dQ_i^T += sum_l C_il a_l for the
@@ -261,7 +351,7 @@ __device__ __forceinline__ void vec_dq_epilogue(DqWave& w, const BiasRule& br, c
   const float lo = hh == 0 ? w.c_lo + olo : olo + w.c_lo;
   const float hi = hh == 0 ? w.c_hi + ohi : ohi + w.c_hi;
   for (int32_t l = 0; l < V; ++l) {
-    const float cl = l == 0 ? lo : (l == top ? hi : C[l]);
+    const float cl = C[l] + (l == 0 ? lo : 0.f) + (l == top ? hi : 0.f);
     const float* al = A + l * kD + 4 * hh;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
@@ -283,16 +373,27 @@ __device__ __forceinline__ void vec_dq_epilogue(DqWave& w, const BiasRule& br, c
 // rows' tables (row stride V) followed by the label sums C [rows][V]: the
 // same-kind pairs' dS add to C[row][l] (the clipped labels 0 and 2k in the
 // lane's registers), for dQ_i's term sum_l C_il a_l.
-template <int32_t BUF, bool BIAS, bool SEG = false, bool VEC = false>
+template <int32_t BUF, bool BIAS, bool SEG = false, bool VEC = false, bool LBL = false>
 __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t lane,
                                         const MaskRule& mr, const KeyTile& kt, int32_t qi,
                                         int32_t qpos, bool dead, float c, const BiasRule& br,
-                                        const GlobInfo& gs) {
+                                        const GlobInfo& gs, const LblCtx* lc = nullptr) {
+  // LBL: a tile whose rows or keys hold a global token decides each pair by
+  // lbl_pair; the others (l2l pairs only) take the paths below, with segment
+  // masks only if the l2l piece has them
+  bool per_pair = false, seg_on = SEG;
+  if constexpr (LBL) {
+    const int32_t gc = kt.gmode == kGlobNone ? 0 : __builtin_amdgcn_readfirstlane(sm.gcls[BUF]);
+    per_pair = lc->rank >= 0 || (gc & 1) != 0;
+    seg_on = !per_pair && (lc->pieces & 8) != 0;
+  }
   bool seg_check = false;
   if constexpr (SEG) {
-    const int32_t st = seg_tile<BUF>(sm, gs, kt);
-    if (st == 0) return;
-    seg_check = st == 2;
+    if (seg_on) {
+      const int32_t st = seg_tile<BUF>(sm, gs, kt);
+      if (st == 0) return;
+      seg_check = st == 2;
+    }
   }
   const int32_t r0 = (mr.use_qpos ? __builtin_amdgcn_readlane(qpos, 0)
                                   : __builtin_amdgcn_readlane(qi, 0)) + mr.ref_off;
@@ -301,7 +402,7 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
   TileBias tb = {false, false};
   int32_t q0 = 0, q1 = 0;  // the wave's first and last row positions
   if constexpr (BIAS || VEC) {
-    tb = tile_bias<BUF>(sm, br, kt);
+    if (!per_pair) tb = tile_bias<BUF>(sm, br, kt);
     q0 = __builtin_amdgcn_readlane(qpos, 0);
     q1 = __builtin_amdgcn_readlane(qpos, TT::kRowsPerBlock - 1);
   }
@@ -326,6 +427,12 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
       if (side != 0)
         off = __builtin_fmaf(br.tab[qi * br.row_stride + (side == 1 ? 0 : 2 * br.k)], c, off);
     }
+    int32_t lab[TT::kNS];
+    if constexpr (LBL) {
+      if (per_pair)
+        lbl_scores_dq<BUF>(s, lab, sm, *lc, sb, qpos, lane,
+                           br.tab ? br.tab + qi * br.row_stride : nullptr);
+    }
     if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, qi, qpos, lane);
     if (SEG && seg_check) seg_mask<BUF>(s, sm, gs.sq, sb, lane);
     TT::PTile G;
@@ -343,8 +450,12 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
       }
     }
     if constexpr (VEC) {
-      if (tb.on && side == 0) {
-        vec_label_sums<BUF>(w, ds, sm, br, sb, qi, qpos, lane, tb.same);
+      const bool sums = !LBL || lc->avec;
+      if (LBL && per_pair) {
+        if (sums) lbl_sums_dq(ds, lab, const_cast<float*>(br.tab) + TT::kTQ * br.row_stride +
+                                           qi * br.row_stride, lane);
+      } else if (tb.on && side == 0) {
+        if (sums) vec_label_sums<BUF>(w, ds, sm, br, sb, qi, qpos, lane, tb.same);
       } else if (side != 0) {
         float t = 0.f;
 #pragma unroll
@@ -362,13 +473,14 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
 // The forward's tile loop (fetch next, compute current, stage, barrier) with
 // `proc(buf_tag, kt, mr)` as the per-tile work; no bias or label state. SEG:
 // the staged keys' segment ids and their range, when gi has them.
-template <bool GATHER, bool SEG = false, typename Desc, typename Proc>
+template <bool GATHER, bool SEG = false, bool LBL = false, typename Desc, typename Proc>
 __device__ __forceinline__ void stream_tiles(TT::Smem& sm, const bf16* kb, const bf16* vb,
                                              int32_t n_tiles, Desc desc, const GlobInfo& gi,
                                              Proc proc) {
   const int32_t tid = threadIdx.x;
   if (n_tiles <= 0) return;
-  const LabelRule nolab = {};
+  LabelRule nolab = {};
+  nolab.want_rank = LBL ? 1 : 0;  // LBL: the keys' global ranks
   TT::Prefetch pf;
   KeyTile kt;
   MaskRule mr;
@@ -376,7 +488,7 @@ __device__ __forceinline__ void stream_tiles(TT::Smem& sm, const bf16* kb, const
   const FetchPlan fp = TT::plan(kt.stride, tid);
   TT::template fetch<GATHER>(pf, sm, 0, kb, vb, kt, fp, tid);
   TT::stage(sm, 0, pf, tid);
-  stage_meta<bf16, SEG, false>(sm, 0, pf.meta, gi, nolab, kt.gmode, tid);
+  stage_meta<bf16, SEG, LBL>(sm, 0, pf.meta, gi, nolab, kt.gmode, tid);
   __syncthreads();
   auto step = [&](auto buf_tag, int32_t n) {
     constexpr int32_t buf = decltype(buf_tag)::value;
@@ -390,7 +502,7 @@ __device__ __forceinline__ void stream_tiles(TT::Smem& sm, const bf16* kb, const
     proc(buf_tag, kt, mr);
     if (more) {
       TT::stage(sm, buf ^ 1, pf, tid);
-      stage_meta<bf16, SEG, false>(sm, buf ^ 1, pf.meta, gi, nolab, kt_next.gmode, tid);
+      stage_meta<bf16, SEG, LBL>(sm, buf ^ 1, pf.meta, gi, nolab, kt_next.gmode, tid);
       kt = kt_next;
       mr = mr_next;
     }
@@ -417,7 +529,7 @@ __device__ __forceinline__ bool qi_is_global(const BwdArgs& a, int32_t qi, int32
 
 // dQ of the non-global rows of one query tile (the forward's band workgroup:
 // window tiles, then the global keys outside the window).
-template <bool BIAS, bool SEG, bool VEC>
+template <bool BIAS, bool SEG, bool VEC, bool LBL>
 __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm, float* dyn,
                                                   int32_t bw) {
   constexpr int32_t kTQ = TT::kTQ;
@@ -475,7 +587,7 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
   if constexpr (BIAS || VEC) {
     // the window keys' global flags decide which pairs are same-kind
     if constexpr (VEC)
-      br = vec_rule_dq(a, dyn, bh, h, 0,
+      br = vec_rule_dq<LBL>(a, dyn, bh, h, 0,
                        [&](int32_t r) { return qbase + d * min(r, qcount - 1); });
     else
       br = bias_rule(a, sm, h, false, 0);
@@ -489,9 +601,11 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
     }
   }
   const int32_t gkeys = (BIAS || VEC) ? kGlobAll : kGlobNone;  // mode of the global-key tiles
+  const LblCtx lc = lbl_ctx(a, bh, -1);  // (LBL) the rows here count as non-global
   auto proc = [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
     constexpr int32_t buf = decltype(buf_tag)::value;
-    dq_tile<buf, BIAS, SEG, VEC>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2, br, gi);
+    dq_tile<buf, BIAS, SEG, VEC, LBL>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2, br, gi,
+                                      &lc);
   };
   auto band_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = lo + n * kTK;
@@ -523,9 +637,9 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
                            (!a.causal || gh <= i_lo);
       mr = {kOutside, all_out ? 0 : 1, 1, -gl, -R, a.causal ? kFar : R, 0, 0, 1};
     };
-    stream_tiles<false, SEG>(sm, kb, vb, n_band + n_gt, desc, gi, proc);
+    stream_tiles<false, SEG, LBL>(sm, kb, vb, n_band + n_gt, desc, gi, proc);
   } else {
-    stream_tiles<false, SEG>(sm, kb, vb, n_band, band_desc, gi, proc);
+    stream_tiles<false, SEG, LBL>(sm, kb, vb, n_band, band_desc, gi, proc);
   }
   if (ng > 0 && !g_run) {
     const int32_t n_gt = (ng + kTK - 1) / kTK;
@@ -558,10 +672,12 @@ __device__ __forceinline__ void dq_band_workgroup(const BwdArgs& a, TT::Smem& sm
       const bool full = kcount == kTK && outside && causal_ok;
       mr = {kGlobCol, full ? 0 : 1, 0, 0, 0, 0, a.causal, R, d};
     };
-    stream_tiles<true, SEG>(sm, kb, vb, n_glob, glob_desc, gi, proc);
+    stream_tiles<true, SEG, LBL>(sm, kb, vb, n_glob, glob_desc, gi, proc);
   }
 
-  if constexpr (VEC) vec_dq_epilogue(w, br, dyn, qi, lane);
+  if constexpr (VEC) {
+    if (!LBL || a.rel_vec) vec_dq_epilogue(w, br, dyn, qi, lane);
+  }
   // non-global rows: dQ (and, with separate projections, a zero dQ_g row)
   if (qi < qcount) {
     const bool is_g = g_first <= i_hi && g_last >= i_lo && sorted_contains(a.gidx, ng, qpos);
@@ -632,6 +748,21 @@ __device__ __forceinline__ void vec_add_rows(float* s, const BwdSmem& sm, const 
   }
 }
 
+// dK/dV pass, a tile holding a global token: each pair's label by lbl_pair
+// (the staged rows against the lane's key), its row's table entry (vt: the
+// staged tables of this buffer, or null) added and masked pairs excluded.
+template <int32_t BUF>
+__device__ __forceinline__ void lbl_scores_dkv(float* s, const BwdSmem& sm, const LblCtx& L,
+                                               int sb, int32_t kpos, int32_t kl, const float* vt) {
+#pragma unroll
+  for (int r = 0; r < TT::kNS; ++r) {
+    const int32_t kj = TT::key_const(sb, r) + kl;
+    const int32_t l = lbl_pair(L, sm.kpos[BUF][kj], sm.kgrank[BUF][kj], kpos, L.rank);
+    if (l == -2) s[r] = kNegInf;
+    else if (l >= 0 && vt) s[r] += vt[kj * L.V + l];
+  }
+}
+
 // One streamed tile of query rows into dK^T, dV^T. EXCL_G: rows that are
 // global are excluded (they are taken in the global-row sweep); ROWS_AFTER:
 // (gathered global rows, causal) only rows at or after the lane's key.
@@ -647,17 +778,26 @@ __device__ __forceinline__ void vec_add_rows(float* s, const BwdSmem& sm, const 
 // segment against the staged rows'). VEC: key-side label vectors, br.tab the
 // staged rows' tables (kTK rows of br.row_stride labels per buffer).
 template <int32_t BUF, bool EXCL_G, bool ROWS_AFTER, bool PRIO = false, bool BIAS = false,
-          bool SEG = false, bool VEC = false>
+          bool SEG = false, bool VEC = false, bool LBL = false>
 __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t lane,
                                          const MaskRule& mr, const KeyTile& kt, int32_t ki,
                                          int32_t kpos, bool dead, float c, bool causal,
                                          const BiasRule& br = {nullptr, 0, 0, 0},
-                                         const GlobInfo& gs = {}) {
+                                         const GlobInfo& gs = {}, const LblCtx* lc = nullptr) {
+  // LBL: as in dq_tile (rows excluded as global do not count: they are masked)
+  bool per_pair = false, seg_on = SEG;
+  if constexpr (LBL) {
+    const int32_t gc = kt.gmode == kGlobNone ? 0 : __builtin_amdgcn_readfirstlane(sm.gcls[BUF]);
+    per_pair = lc->rank >= 0 || (!EXCL_G && (gc & 1) != 0);
+    seg_on = !per_pair && (lc->pieces & 8) != 0;
+  }
   bool seg_check = false;
   if constexpr (SEG) {
-    const int32_t st = seg_tile<BUF>(sm, gs, kt);
-    if (st == 0) return;
-    seg_check = st == 2;
+    if (seg_on) {
+      const int32_t st = seg_tile<BUF>(sm, gs, kt);
+      if (st == 0) return;
+      seg_check = st == 2;
+    }
   }
   const int32_t r0 = (mr.use_qpos ? __builtin_amdgcn_readlane(kpos, 0)
                                   : __builtin_amdgcn_readlane(ki, 0)) + mr.ref_off;
@@ -669,7 +809,7 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
   TileBias tb = {false, false};
   int32_t kq0 = 0, kq1 = 0;  // the wave's first and last key positions
   if constexpr (BIAS || VEC) {
-    tb = tile_bias<BUF>(sm, br, kt);
+    if (!per_pair) tb = tile_bias<BUF>(sm, br, kt);
     kq0 = __builtin_amdgcn_readlane(kpos, 0);
     kq1 = __builtin_amdgcn_readlane(kpos, TT::kRowsPerBlock - 1);
   }
@@ -722,6 +862,11 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
     if constexpr (VEC) {
       if (tb.on && side == 0) vec_add_rows<BUF>(s, sm, br, sb, kpos, kl, tb.same);
     }
+    if constexpr (LBL) {
+      if (per_pair)
+        lbl_scores_dkv<BUF>(s, sm, *lc, sb, kpos, kl,
+                            br.tab ? br.tab + BUF * kTK * br.row_stride : nullptr);
+    }
     if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, ki, kpos, lane);
     if (SEG && seg_check) seg_mask<BUF>(s, sm, gs.sq, sb, lane);
     if (EXCL_G && any_g) {
@@ -763,16 +908,19 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
 // VEC: also the rows' label tables (tab: the head's [N][V] tables) into
 // vt + buf * kTK * V, and after the two buffers' tables the rows' offsets with
 // the clipped labels' entries added, -lse * lse_mul + T[row][0] ([2][kTK])
-// then + T[row][V - 1] ([2][kTK]).
-template <bool GATHER, bool SEG = false, bool VEC = false, typename Desc, typename Proc>
+// then + T[row][vtop] ([2][kTK]; vtop = 2k).
+template <bool GATHER, bool SEG = false, bool VEC = false, bool LBL = false, typename Desc,
+          typename Proc>
 __device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const bf16* dob,
                                             const float* lse, const float* delta, float lse_mul,
                                             int32_t n_tiles, Desc desc, const GlobInfo& gi,
                                             Proc proc, const float* tab = nullptr,
-                                            float* vt = nullptr, int32_t V = 0) {
+                                            float* vt = nullptr, int32_t V = 0,
+                                            int32_t vtop = 0) {
   const int32_t tid = threadIdx.x;
   if (n_tiles <= 0) return;
-  const LabelRule nolab = {};
+  LabelRule nolab = {};
+  nolab.want_rank = LBL ? 1 : 0;  // LBL: the rows' global ranks
   TT::Prefetch pf;
   KeyTile kt;
   MaskRule mr;
@@ -787,12 +935,14 @@ __device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const b
       pl = l == kNegInf ? kNegInf : -(l * lse_mul);
       pd = -delta[p];
       if constexpr (VEC) {
-        plo = pl + tab[(size_t)p * V];
-        phi = pl + tab[(size_t)p * V + V - 1];
+        if (!LBL || tab) {
+          plo = pl + tab[(size_t)p * V];
+          phi = pl + tab[(size_t)p * V + vtop];
+        }
       }
     }
     if constexpr (VEC) {
-      if (t.count > 0) {
+      if (t.count > 0 && (!LBL || tab)) {
         const float* src = tab + (size_t)key_pos<GATHER>(t, min(tid >> 2, t.count - 1)) * V;
 #pragma unroll
         for (int u = 0; u < kVecPer; ++u) {
@@ -808,6 +958,7 @@ __device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const b
       row_di(sm, buf)[tid] = pd;
     }
     if constexpr (VEC) {
+      if (LBL && !tab) return;
       if (tid < kTK) {
         vt[2 * kTK * V + buf * kTK + tid] = plo;
         vt[2 * kTK * V + 2 * kTK + buf * kTK + tid] = phi;
@@ -825,7 +976,7 @@ __device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const b
   TT::template fetch<GATHER>(pf, sm, 0, qb, dob, kt, fp, tid);
   row_vals(kt);
   TT::stage(sm, 0, pf, tid);
-  stage_meta<bf16, SEG, false>(sm, 0, pf.meta, gi, nolab, kt.gmode, tid);
+  stage_meta<bf16, SEG, LBL>(sm, 0, pf.meta, gi, nolab, kt.gmode, tid);
   put_rows(0);
   __syncthreads();
   auto step = [&](auto buf_tag, int32_t n) {
@@ -841,7 +992,7 @@ __device__ __forceinline__ void stream_rows(BwdSmem& sm, const bf16* qb, const b
     proc(buf_tag, kt, mr);
     if (more) {
       TT::stage(sm, buf ^ 1, pf, tid);
-      stage_meta<bf16, SEG, false>(sm, buf ^ 1, pf.meta, gi, nolab, kt_next.gmode, tid);
+      stage_meta<bf16, SEG, LBL>(sm, buf ^ 1, pf.meta, gi, nolab, kt_next.gmode, tid);
       put_rows(buf ^ 1);
       kt = kt_next;
       mr = mr_next;
@@ -872,7 +1023,7 @@ __device__ __forceinline__ void store_rows_f32(float* dst, const f32x16 (&acc)[2
 
 // dK, dV of the non-global keys of one key tile (a residue class of the
 // head's dilation, like the forward's query tiles).
-template <bool BIAS, bool SEG, bool VEC>
+template <bool BIAS, bool SEG, bool VEC, bool LBL>
 __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm, float* dyn,
                                                    int32_t bw) {
   constexpr int32_t kTQ = TT::kTQ;
@@ -935,8 +1086,10 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm
   }
   BiasRule br = {nullptr, 0, 0, 0};
   if constexpr (BIAS) br = bias_rule(a, sm, h, true, 0);  // lanes hold keys: flipped table
-  if constexpr (VEC) br = {dyn, a.rel_k, 0, a.n_labels};  // the staged rows' tables
-  const float* vtab = VEC ? a.rowtab + (size_t)bh * N * a.n_labels : nullptr;
+  const bool tabs = !LBL || a.rowtab != nullptr;  // (without LBL always there)
+  if constexpr (VEC) br = {tabs ? dyn : nullptr, a.rel_k, 0, a.n_labels};  // staged tables
+  const float* vtab = VEC && tabs ? a.rowtab + (size_t)bh * N * a.n_labels : nullptr;
+  const LblCtx lc = lbl_ctx(a, bh, -1);  // (LBL) the keys here count as non-global
   auto band_desc = [&](int32_t n, KeyTile& kt, MaskRule& mr) {
     const int32_t u0 = lo + n * kTK;
     const int32_t cnt = min(kTK, hi - u0 + 1);
@@ -948,14 +1101,15 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm
     mr = {kRange, full ? 0 : 1, 0, t0 - u0, lob, R, 0, 0, 1};
   };
   const bf16* qs = static_cast<const bf16*>(a.q) + bh * head_elems;
-  stream_rows<false, SEG, VEC>(sm, qs, dob, lse, delta, 1.f / a.scale, n_band, band_desc, gi,
-                               [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                                 constexpr int32_t buf = decltype(buf_tag)::value;
-                                 dkv_tile<buf, true, false, false, BIAS, SEG, VEC>(
-                                     sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal,
-                                     br, gi);
-                               },
-                               vtab, dyn, a.n_labels);
+  stream_rows<false, SEG, VEC, LBL>(sm, qs, dob, lse, delta, 1.f / a.scale, n_band, band_desc,
+                                    gi,
+                                    [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                                      constexpr int32_t buf = decltype(buf_tag)::value;
+                                      dkv_tile<buf, true, false, false, BIAS, SEG, VEC, LBL>(
+                                          sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2,
+                                          a.causal, br, gi, &lc);
+                                    },
+                                    vtab, dyn, a.n_labels, 2 * a.rel_k);
   // the global rows reach every key (causal: rows at or after it)
   const int32_t n_gt = (ng + kTK - 1) / kTK;
   const int32_t grows = (BIAS || VEC) ? kGlobAll : kGlobNone;  // mode of the global-row tiles
@@ -968,8 +1122,8 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm
   };
   auto glob_proc = [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
     constexpr int32_t buf = decltype(buf_tag)::value;
-    dkv_tile<buf, false, true, false, BIAS, SEG, VEC>(sm, w, lane, mr, kt, ki, kpos, dead,
-                                                        a.scale_log2, a.causal, br, gall);
+    dkv_tile<buf, false, true, false, BIAS, SEG, VEC, LBL>(sm, w, lane, mr, kt, ki, kpos, dead,
+                                                             a.scale_log2, a.causal, br, gall, &lc);
   };
   const bool mine = ki < kcount && !qi_is_global(a, ki, kcount, kpos, g_first, g_last, j_lo, j_hi);
   if (a.sep) {
@@ -988,10 +1142,9 @@ __device__ __forceinline__ void dkv_band_workgroup(const BwdArgs& a, BwdSmem& sm
     }
   }
   if (ng > 0)
-    stream_rows<true, SEG, VEC>(sm,
-                                static_cast<const bf16*>(a.sep ? a.qg : a.q) + bh * head_elems,
-                                dob, lse, delta, 1.f / a.scale, n_gt, glob_desc, gall, glob_proc,
-                                vtab, dyn, a.n_labels);
+    stream_rows<true, SEG, VEC, LBL>(
+        sm, static_cast<const bf16*>(a.sep ? a.qg : a.q) + bh * head_elems, dob, lse, delta,
+        1.f / a.scale, n_gt, glob_desc, gall, glob_proc, vtab, dyn, a.n_labels, 2 * a.rel_k);
   if (mine) {
     float* const dk = a.sep ? a.dkg : a.dk;
     float* const dv = a.sep ? a.dvg : a.dv;
@@ -1025,7 +1178,7 @@ __device__ __forceinline__ float* part_row(const BwdArgs& a, int32_t part, int32
 }
 
 // Workgroup wg of the B*H*ceil(n_global/128)*glob_chunks global-row ones.
-template <bool BIAS, bool SEG, bool VEC>
+template <bool BIAS, bool SEG, bool VEC, bool LBL>
 __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm, float* dyn,
                                                   int32_t wg) {
   constexpr int32_t kTQ = TT::kTQ;
@@ -1062,7 +1215,7 @@ __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm
   if constexpr (BIAS || VEC) {
     // the keys' global flags decide which pairs are same-kind (global keys)
     if constexpr (VEC)
-      br = vec_rule_dq(a, dyn, bh, bh % a.H, 1,
+      br = vec_rule_dq<LBL>(a, dyn, bh, bh % a.H, 1,
                        [&](int32_t r) { return qidx[min(r, qcount - 1)]; });
     else
       br = bias_rule(a, sm, bh % a.H, false, 1);
@@ -1084,14 +1237,18 @@ __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm
     const bool full = kcount == kTK && (!a.causal || u0 + kTK - 1 <= i_min);
     mr = {kRange, full ? 0 : 1, 1, -u0, -kFar, a.causal ? 0 : kFar, 0, 0, 1};
   };
-  stream_tiles<false, SEG>(sm, static_cast<const bf16*>(sep ? a.kg : a.k) + bh * head_elems,
-                           static_cast<const bf16*>(sep ? a.vg : a.v) + bh * head_elems, n_tiles,
-                           desc, gi, [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                             constexpr int32_t buf = decltype(buf_tag)::value;
-                             dq_tile<buf, BIAS, SEG, VEC>(sm, w, lane, mr, kt, qi, qpos, dead,
-                                                          a.scale_log2, br, gi);
-                           });
-  if constexpr (VEC) vec_dq_epilogue(w, br, dyn, qi, lane);
+  const LblCtx lc = lbl_ctx(a, bh, gq * kTQ + min(qi, qcount - 1));  // (LBL) the lane's row rank
+  stream_tiles<false, SEG, LBL>(
+      sm, static_cast<const bf16*>(sep ? a.kg : a.k) + bh * head_elems,
+      static_cast<const bf16*>(sep ? a.vg : a.v) + bh * head_elems, n_tiles, desc, gi,
+      [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+        constexpr int32_t buf = decltype(buf_tag)::value;
+        dq_tile<buf, BIAS, SEG, VEC, LBL>(sm, w, lane, mr, kt, qi, qpos, dead, a.scale_log2, br,
+                                          gi, &lc);
+      });
+  if constexpr (VEC) {
+    if (!LBL || a.rel_vec) vec_dq_epilogue(w, br, dyn, qi, lane);
+  }
   if (qi < qcount && chunks > 1) {
     store_rows_f32(part_row(a, 0, c, bh, gq * kTQ + qi), w.acc, 1.f, lane);
   } else if (qi < qcount) {
@@ -1105,7 +1262,7 @@ __device__ __forceinline__ void dq_glob_workgroup(const BwdArgs& a, TT::Smem& sm
 }
 
 // Workgroup wg of the B*H*ceil(n_global/128)*glob_chunks global-key ones.
-template <bool BIAS, bool SEG, bool VEC>
+template <bool BIAS, bool SEG, bool VEC, bool LBL>
 __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, BwdSmem& sm, float* dyn,
                                                    int32_t wg) {
   constexpr int32_t kTQ = TT::kTQ;
@@ -1144,8 +1301,10 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, BwdSmem& sm
   seg_info<SEG>(gi, a, bh, kpos);
   BiasRule br = {nullptr, 0, 0, 0};
   if constexpr (BIAS) br = bias_rule(a, sm, bh % a.H, true, 1);  // lanes hold global keys
-  if constexpr (VEC) br = {dyn, a.rel_k, 1, a.n_labels};  // the staged rows' tables
-  const float* vtab = VEC ? a.rowtab + (size_t)bh * N * a.n_labels : nullptr;
+  const bool tabs = !LBL || a.rowtab != nullptr;  // (without LBL always there)
+  if constexpr (VEC) br = {tabs ? dyn : nullptr, a.rel_k, 1, a.n_labels};  // staged tables
+  const float* vtab = VEC && tabs ? a.rowtab + (size_t)bh * N * a.n_labels : nullptr;
+  const LblCtx lc = lbl_ctx(a, bh, gk * kTQ + min(ki, kcount - 1));  // (LBL) the lane's key rank
   // the rows' global flags: excluded with separate projections; with a bias
   // table or label vectors, the same-kind pairs
   if ((sep || BIAS || VEC) && n_tiles > 0) {
@@ -1166,23 +1325,23 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, BwdSmem& sm
   };
   const bf16* qs = static_cast<const bf16*>(a.q) + bh * head_elems;
   if (sep)
-    stream_rows<false, SEG, VEC>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
-                                 [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                                   constexpr int32_t buf = decltype(buf_tag)::value;
-                                   dkv_tile<buf, true, false, false, BIAS, SEG, VEC>(
-                                       sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2,
-                                       a.causal, br, gi);
-                                 },
-                                 vtab, dyn, a.n_labels);
+    stream_rows<false, SEG, VEC, LBL>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
+                                      [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                                        constexpr int32_t buf = decltype(buf_tag)::value;
+                                        dkv_tile<buf, true, false, false, BIAS, SEG, VEC, LBL>(
+                                            sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2,
+                                            a.causal, br, gi, &lc);
+                                      },
+                                      vtab, dyn, a.n_labels, 2 * a.rel_k);
   else
-    stream_rows<false, SEG, VEC>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
-                                 [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                                   constexpr int32_t buf = decltype(buf_tag)::value;
-                                   dkv_tile<buf, false, false, false, BIAS, SEG, VEC>(
-                                       sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2,
-                                       a.causal, br, gi);
-                                 },
-                                 vtab, dyn, a.n_labels);
+    stream_rows<false, SEG, VEC, LBL>(sm, qs, dob, lse, delta, 1.f / a.scale, n_tiles, desc, gi,
+                                      [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                                        constexpr int32_t buf = decltype(buf_tag)::value;
+                                        dkv_tile<buf, false, false, false, BIAS, SEG, VEC, LBL>(
+                                            sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2,
+                                            a.causal, br, gi, &lc);
+                                      },
+                                      vtab, dyn, a.n_labels, 2 * a.rel_k);
   const size_t ro = ((size_t)bh * N + kpos) * kD;
   if (ki < kcount && chunks > 1) {
     store_rows_f32(part_row(a, 1, c, bh, gk * kTQ + ki), w.dk, 1.f, lane);
@@ -1209,15 +1368,15 @@ __device__ __forceinline__ void dkv_glob_workgroup(const BwdArgs& a, BwdSmem& sm
     mr = {kRange, cnt == kTK ? 0 : 1, 0, 0, -kFar, kFar, 0, 0, 1};
   };
   const GlobInfo gall = {grows, a.gidx, a.n_global, gi.segb, gi.sq, gi.sq_min, gi.sq_max};
-  stream_rows<true, SEG, VEC>(sm, static_cast<const bf16*>(a.qg) + bh * head_elems, dob, lse,
-                              delta, 1.f / a.scale, n_gt, glob_desc, gall,
-                              [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
-                                constexpr int32_t buf = decltype(buf_tag)::value;
-                                dkv_tile<buf, false, true, false, BIAS, SEG, VEC>(
-                                    sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2, a.causal,
-                                    br, gall);
-                              },
-                              vtab, dyn, a.n_labels);
+  stream_rows<true, SEG, VEC, LBL>(sm, static_cast<const bf16*>(a.qg) + bh * head_elems, dob,
+                                   lse, delta, 1.f / a.scale, n_gt, glob_desc, gall,
+                                   [&](auto buf_tag, const KeyTile& kt, const MaskRule& mr) {
+                                     constexpr int32_t buf = decltype(buf_tag)::value;
+                                     dkv_tile<buf, false, true, false, BIAS, SEG, VEC, LBL>(
+                                         sm, w, lane, mr, kt, ki, kpos, dead, a.scale_log2,
+                                         a.causal, br, gall, &lc);
+                                   },
+                                   vtab, dyn, a.n_labels, 2 * a.rel_k);
   if (ki < kcount) {
     store_rows_f32(a.dkg + ro, w.dk, a.scale, lane);
     store_rows_f32(a.dvg + ro, w.dv, 1.f, lane);
@@ -1416,8 +1575,9 @@ __device__ __forceinline__ int32_t band_tile_of(const BwdArgs& a, int32_t b) {
 // dK/dV and dQ workgroups in one launch, the dK/dV ones (the longer work)
 // first: the two add into different gradients, and D_i came from a launch
 // before, so they run side by side and fill each other's tails.
-// VEC: key-side label vectors (their tables in the dynamic LDS).
-template <bool BIAS, bool SEG, bool VEC>
+// VEC: key-side label vectors (their tables in the dynamic LDS). LBL: label
+// matrices and per-piece segment masks (with VEC and SEG; tables optional).
+template <bool BIAS, bool SEG, bool VEC, bool LBL = false>
 __global__ __launch_bounds__(TT::kThreads)
 __attribute__((amdgpu_waves_per_eu((BIAS || VEC) ? 2 : 3)))
 void bwd_mfma_kernel(BwdArgs a, int32_t grid_kv) {
@@ -1431,9 +1591,9 @@ void bwd_mfma_kernel(BwdArgs a, int32_t grid_kv) {
     const int32_t bw = band_tile_of(a, kv ? b : b - nb);
     if (bw < 0) return;
     if (kv)
-      dkv_band_workgroup<BIAS, SEG, VEC>(a, sm, dyn, bw);
+      dkv_band_workgroup<BIAS, SEG, VEC, LBL>(a, sm, dyn, bw);
     else
-      dq_band_workgroup<BIAS, SEG, VEC>(a, sm, dyn, bw);
+      dq_band_workgroup<BIAS, SEG, VEC, LBL>(a, sm, dyn, bw);
     return;
   }
   b -= 2 * nb;  // global ranges: dK/dV, then dQ
@@ -1441,9 +1601,9 @@ void bwd_mfma_kernel(BwdArgs a, int32_t grid_kv) {
   if (!kv) b -= gw;
   if (b >= glob_wg(a)) return;
   if (kv)
-    dkv_glob_workgroup<BIAS, SEG, VEC>(a, sm, dyn, b);
+    dkv_glob_workgroup<BIAS, SEG, VEC, LBL>(a, sm, dyn, b);
   else
-    dq_glob_workgroup<BIAS, SEG, VEC>(a, sm, dyn, b);
+    dq_glob_workgroup<BIAS, SEG, VEC, LBL>(a, sm, dyn, b);
 }
 
 // The global rows' dQ and the global keys' dK, dV from the ranges' partial
@@ -1514,8 +1674,9 @@ __global__ __launch_bounds__(256) void bwd_rowtab_kernel(BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < kD / 8; ++c) qx[c] = *reinterpret_cast<const bf16x8*>(qr + 8 * c);
   }
-  for (int32_t x = threadIdx.x; x < V * kD; x += 256)
-    av[(x / kD) * kRow + x % kD] = a.rel_vec[(size_t)h * V * kD + x];
+  if (a.rel_vec)
+    for (int32_t x = threadIdx.x; x < V * kD; x += 256)
+      av[(x / kD) * kRow + x % kD] = a.rel_vec[(size_t)h * V * kD + x];
   __syncthreads();
   if (!live) return;
   float qv[kD];
@@ -1528,12 +1689,14 @@ __global__ __launch_bounds__(256) void bwd_rowtab_kernel(BwdArgs a) {
   const float* sb = a.rel_bias ? a.rel_bias + (size_t)h * V : nullptr;
   for (int32_t l = part; l < V; l += 4) {
     float acc = sb ? sb[l] / a.scale : 0.f;
-    const f32x4* al = reinterpret_cast<const f32x4*>(av + l * kRow);
+    if (a.rel_vec) {
+      const f32x4* al = reinterpret_cast<const f32x4*>(av + l * kRow);
 #pragma unroll
-    for (int c = 0; c < kD / 4; ++c) {
-      const f32x4 x = al[c];
+      for (int c = 0; c < kD / 4; ++c) {
+        const f32x4 x = al[c];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(qv[4 * c + e], x[e], acc);
+        for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(qv[4 * c + e], x[e], acc);
+      }
     }
     dst[l] = acc;
   }
@@ -1611,7 +1774,16 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream) {
   if (2 * grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 g((uint32_t)(2 * grid)), t(TT::kThreads);
   const int32_t gkv = (int32_t)grid;
-  if (a.rel_vec) {  // the tables (scalar bias folded in), the label sums, the vectors
+  const bool lbl = a.glabel || a.llabel || (a.seg && a.seg_pieces != 15) ||
+                   ((a.rel_bias || a.rel_vec) && a.n_labels != 2 * a.rel_k + 1);
+  if (lbl) {  // row tables when there is a table, label sums with vectors
+    if ((a.rel_bias || a.rel_vec) != (a.rowtab != nullptr) || a.n_labels < 1 ||
+        a.n_labels > kMaxLabels)
+      return hipErrorInvalidValue;
+    const int32_t V = a.n_labels < 3 ? 3 : a.n_labels;  // room for the dK/dV offset rows
+    const uint32_t dyn = (uint32_t)((2 * TT::kTQ + kD) * V * sizeof(float));
+    hipLaunchKernelGGL((bwd_mfma_kernel<false, true, true, true>), g, t, dyn, stream, a, gkv);
+  } else if (a.rel_vec) {  // the tables (scalar bias folded in), the label sums, the vectors
     if (!a.rowtab || a.n_labels != 2 * a.rel_k + 1 || a.n_labels > kMaxLabels)
       return hipErrorInvalidValue;
     // dQ: rows' tables, label sums, vectors; dK/dV: two tiles' tables and
@@ -1634,7 +1806,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_rowtab(const BwdArgs& a, hipStream_t stream) {
-  if (!a.rel_vec || a.n_band_wg <= 0) return hipSuccess;
+  if (!a.rowtab || a.n_band_wg <= 0) return hipSuccess;
   if (!a.rowtab || a.n_labels < 1 || a.n_labels > kMaxLabels) return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)a.B * a.H * ((a.N + 63) / 64);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;

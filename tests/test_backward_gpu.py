@@ -374,6 +374,15 @@ def test_backward_etc_structured(dev):
     run_label_case(dev, "etc-structured", "bf16", w, W.make_inputs(w), seed=409)
 
 
+def test_backward_etc_structured_full(dev):
+    """The full ETC structured workload (B=1, H=12, 256 global tokens then 4096
+    long tokens, R=84, 16 contexts and 7 answer candidates: label matrices, hard
+    g2l and g2g masks, l2l segment ids, 29 labels with key-side vectors), every
+    element against the oracle."""
+    w = W.WORKLOADS["etc-structured-ng256-nl4096-r84-relvec12-v29"]
+    run_label_case(dev, "etc-structured-full", "bf16", w, W.make_inputs(w), seed=w.seed)
+
+
 def test_backward_graph_replay(dev):
     """The backward call captured in a HIP graph (it writes its whole workspace
     with kernels, no memset) and replayed, with eager work between replays:
