@@ -235,6 +235,12 @@ LABEL_CASES = [
     ("bias-both-sep", "bf16", 2, 2, 260, (3, 64, 200), 16, [1, 2], False, True, 3, 3, "both", 9),
     ("labels-f32-causal", "f32", 1, 2, 200, (5, 70, 71), 12, None, True, False, 2, 2, "vector", 6),
     ("labels-masks-only", "bf16", 1, 2, 230, (0, 100), 10, None, False, False, 0, 0, None, 4),
+    # label matrices on the bf16 MFMA path: causal with separate projections and
+    # the g2l and l2g pieces masked; dilated heads with vectors and every piece
+    ("labels-bf16-causal-sep", "bf16", 1, 2, 300, (5, 70, 71, 200), 12, None, True, True, 3, 2,
+     "both", 6),
+    ("labels-vector-dilated", "bf16", 2, 3, 500, (0, 10, 250), 20, [1, 2, 3], False, False, 4, 3,
+     "vector", 15),
 ]
 
 
