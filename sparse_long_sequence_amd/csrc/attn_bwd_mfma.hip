@@ -238,37 +238,62 @@ __device__ __forceinline__ int32_t lbl_pair(const LblCtx& L, int32_t i, int32_t 
   return l;
 }
 
-// dQ pass, a tile holding a global token: each pair's label by lbl_pair (the
-// lane's row against the staged keys), its table entry (trow: the lane's row
-// table, or null) added and masked pairs excluded; lab keeps the labels.
-template <int32_t BUF>
-__device__ __forceinline__ void lbl_scores_dq(float* s, int32_t* lab, const TT::Smem& sm,
-                                              const LblCtx& L, int sb, int32_t qpos,
-                                              int32_t lane, const float* trow) {
-  int32_t kl = TT::key_lane(lane);
-  asm("" : "+v"(kl));  // opaque per call, as in mask_tile
+// A tile holding a global token, sub-tile sb: each pair's label by lbl_pair
+// (row against key), packed four to a word as label + 2 (byte r & 3 of word
+// r >> 2). ROWS_IN_LANES: the lane holds the row (dQ pass; the staged entries
+// are keys), else the key (dK/dV pass; the staged entries are rows). Returns
+// whether any pair of the wave's sub-tile is kept.
+template <int32_t BUF, bool ROWS_IN_LANES>
+__device__ __forceinline__ bool lbl_labels(uint32_t (&lw)[TT::kNS / 4], const TT::Smem& sm,
+                                           const LblCtx& L, int sb, int32_t pos, int32_t kl) {
+  bool any = false;
+#pragma unroll
+  for (int g = 0; g < TT::kNS / 4; ++g) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int32_t kj = TT::key_const(sb, 4 * g + e) + kl;
+      const int32_t l = ROWS_IN_LANES
+                            ? lbl_pair(L, pos, L.rank, sm.kpos[BUF][kj], sm.kgrank[BUF][kj])
+                            : lbl_pair(L, sm.kpos[BUF][kj], sm.kgrank[BUF][kj], pos, L.rank);
+      any = any || l != -2;
+      x |= (uint32_t)(l + 2) << (8 * e);
+    }
+    lw[g] = x;
+  }
+  return __ballot(any) != 0ull;
+}
+__device__ __forceinline__ int32_t lbl_at(const uint32_t (&lw)[TT::kNS / 4], int r) {
+  return (int32_t)((lw[r >> 2] >> (8 * (r & 3))) & 0xffu) - 2;
+}
+
+// The labels applied to the scores: masked pairs excluded, labelled ones add
+// the table entry (tab(kj, l): the row's table, or null without tables).
+template <typename Tab>
+__device__ __forceinline__ void lbl_apply(float* s, const uint32_t (&lw)[TT::kNS / 4], int sb,
+                                          int32_t kl, bool tabs, Tab tab) {
 #pragma unroll
   for (int r = 0; r < TT::kNS; ++r) {
-    const int32_t kj = TT::key_const(sb, r) + kl;
-    const int32_t l = lbl_pair(L, qpos, L.rank, sm.kpos[BUF][kj], sm.kgrank[BUF][kj]);
-    lab[r] = l;
+    const int32_t l = lbl_at(lw, r);
     if (l == -2) s[r] = kNegInf;
-    else if (l >= 0 && trow) s[r] += trow[l];
+    else if (l >= 0 && tabs) s[r] += tab(TT::key_const(sb, r) + kl, l);
   }
 }
 
 // dQ pass with label vectors, a tile holding a global token: the labelled
 // pairs' dS into the row's label sums, one half-wave at a time (the two lanes
 // of a row may share a label; lanes of one half hold different rows).
-__device__ __forceinline__ void lbl_sums_dq(const float* ds, const int32_t* lab, float* crow,
-                                            int32_t lane) {
+__device__ __forceinline__ void lbl_sums_dq(const float* ds, const uint32_t (&lw)[TT::kNS / 4],
+                                            float* crow, int32_t lane) {
   const int32_t hh = lane >> 5;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if (hh == half) {
 #pragma unroll
-      for (int r = 0; r < TT::kNS; ++r)
-        if (lab[r] >= 0) atomicAdd(crow + lab[r], ds[r]);
+      for (int r = 0; r < TT::kNS; ++r) {
+        const int32_t l = lbl_at(lw, r);
+        if (l >= 0) atomicAdd(crow + l, ds[r]);
+      }
     }
   }
 }
@@ -418,6 +443,11 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
         side = label_side(__builtin_amdgcn_readfirstlane(sm.kpos[BUF][32 * sb]),
                           __builtin_amdgcn_readfirstlane(sm.kpos[BUF][32 * sb + 31]), q0, q1, br.k);
     }
+    uint32_t lw[TT::kNS / 4];
+    if constexpr (LBL) {
+      // a sub-tile whose pairs are all masked is skipped before its MFMAs
+      if (per_pair && !lbl_labels<BUF, true>(lw, sm, *lc, sb, qpos, TT::key_lane(lane))) continue;
+    }
     float s[TT::kNS], dp[TT::kNS];
     tile_dots(&sm.k[BUF][0], w.qf, lane, sb, s);
     tile_dots(&sm.v[BUF][0], w.df, lane, sb, dp);
@@ -427,11 +457,12 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
       if (side != 0)
         off = __builtin_fmaf(br.tab[qi * br.row_stride + (side == 1 ? 0 : 2 * br.k)], c, off);
     }
-    int32_t lab[TT::kNS];
     if constexpr (LBL) {
-      if (per_pair)
-        lbl_scores_dq<BUF>(s, lab, sm, *lc, sb, qpos, lane,
-                           br.tab ? br.tab + qi * br.row_stride : nullptr);
+      if (per_pair) {
+        const float* trow = br.tab ? br.tab + qi * br.row_stride : nullptr;
+        lbl_apply(s, lw, sb, TT::key_lane(lane), trow != nullptr,
+                  [&](int32_t, int32_t l) { return trow[l]; });
+      }
     }
     if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, qi, qpos, lane);
     if (SEG && seg_check) seg_mask<BUF>(s, sm, gs.sq, sb, lane);
@@ -452,8 +483,8 @@ __device__ __forceinline__ void dq_tile(const TT::Smem& sm, DqWave& w, int32_t l
     if constexpr (VEC) {
       const bool sums = !LBL || lc->avec;
       if (LBL && per_pair) {
-        if (sums) lbl_sums_dq(ds, lab, const_cast<float*>(br.tab) + TT::kTQ * br.row_stride +
-                                           qi * br.row_stride, lane);
+        if (sums) lbl_sums_dq(ds, lw, const_cast<float*>(br.tab) + TT::kTQ * br.row_stride +
+                                          qi * br.row_stride, lane);
       } else if (tb.on && side == 0) {
         if (sums) vec_label_sums<BUF>(w, ds, sm, br, sb, qi, qpos, lane, tb.same);
       } else if (side != 0) {
@@ -748,21 +779,6 @@ __device__ __forceinline__ void vec_add_rows(float* s, const BwdSmem& sm, const 
   }
 }
 
-// dK/dV pass, a tile holding a global token: each pair's label by lbl_pair
-// (the staged rows against the lane's key), its row's table entry (vt: the
-// staged tables of this buffer, or null) added and masked pairs excluded.
-template <int32_t BUF>
-__device__ __forceinline__ void lbl_scores_dkv(float* s, const BwdSmem& sm, const LblCtx& L,
-                                               int sb, int32_t kpos, int32_t kl, const float* vt) {
-#pragma unroll
-  for (int r = 0; r < TT::kNS; ++r) {
-    const int32_t kj = TT::key_const(sb, r) + kl;
-    const int32_t l = lbl_pair(L, sm.kpos[BUF][kj], sm.kgrank[BUF][kj], kpos, L.rank);
-    if (l == -2) s[r] = kNegInf;
-    else if (l >= 0 && vt) s[r] += vt[kj * L.V + l];
-  }
-}
-
 // One streamed tile of query rows into dK^T, dV^T. EXCL_G: rows that are
 // global are excluded (they are taken in the global-row sweep); ROWS_AFTER:
 // (gathered global rows, causal) only rows at or after the lane's key.
@@ -819,6 +835,11 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
   for (int sb = 0; sb < TT::kSub; ++sb) {
     const int32_t cls = dead ? kEmpty : classify<bf16>(mr, kt.count, sb, r0, r1);
     if (cls == kEmpty) continue;
+    uint32_t lw[TT::kNS / 4];
+    if constexpr (LBL) {
+      // a sub-tile whose pairs are all masked is skipped before its MFMAs
+      if (per_pair && !lbl_labels<BUF, false>(lw, sm, *lc, sb, kpos, kl)) continue;
+    }
     // one clipped label for the whole sub-tile: VEC starts the score MFMAs
     // from the offsets with the rows' entries added; the scalar table's entry
     // joins the exponent
@@ -863,9 +884,12 @@ __device__ __forceinline__ void dkv_tile(const BwdSmem& sm, DkvWave& w, int32_t 
       if (tb.on && side == 0) vec_add_rows<BUF>(s, sm, br, sb, kpos, kl, tb.same);
     }
     if constexpr (LBL) {
-      if (per_pair)
-        lbl_scores_dkv<BUF>(s, sm, *lc, sb, kpos, kl,
-                            br.tab ? br.tab + BUF * kTK * br.row_stride : nullptr);
+      if (per_pair) {
+        const float* vt = br.tab ? br.tab + BUF * kTK * br.row_stride : nullptr;
+        const int32_t V = br.row_stride;
+        lbl_apply(s, lw, sb, kl, vt != nullptr,
+                  [&](int32_t kj, int32_t l) { return vt[kj * V + l]; });
+      }
     }
     if (cls == kPartial) mask_tile<bf16>(s, sm, BUF, mr, sb, kt.count, ki, kpos, lane);
     if (SEG && seg_check) seg_mask<BUF>(s, sm, gs.sq, sb, lane);
