@@ -14,16 +14,13 @@
 // Linear Projections for Local vs. Global Attention") differentiate through
 // qg_i, kg_j, vg_j, so their terms land in dqg, dkg, dvg.
 //
-// No atomics: after a pass that marks the global positions, a query-centric
-// pass (one wave per row) writes D_i and dQ_i, and a key-centric pass (one
+// bf16 calls and the LongNet mixture run on the MFMA tile engine
+// (attn_bwd_mfma.hip); this file holds their D_i launch and the fp32 path.
+// The fp32 path has no atomics: after a pass that marks the global positions,
+// a query-centric pass (one wave per row, one lane per vector element, dot
+// products as wave sums) writes D_i and dQ_i, and a key-centric pass (one
 // wave per key) visits every row that attends to its key and writes dK_j and
-// dV_j in one store. These are the scalar kernels: fp32 VALU work, no MFMA.
-// The fp32 path keeps one lane per vector element (dot products as wave
-// sums); the bf16 path (below) puts one key or row on each lane instead. They
-// serve fp32 calls and calls with bias tables, labels or segment ids; bf16
-// calls without them, and the LongNet mixture, run on the MFMA tile engine
-// (attn_bwd_mfma.hip), whose dQ launches compute D_i (a LongNet call without
-// a pattern of dilation 1 takes it from the launch here first).
+// dV_j in one store.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -36,7 +33,6 @@ namespace {
 constexpr int kWavesBwd = 4;  // rows (or keys) per workgroup
 
 __device__ __forceinline__ float load_el(const float* p) { return *p; }
-__device__ __forceinline__ float load_el(const bf16* p) { return (float)*p; }
 
 // Sum over the 64 lanes, in registers; every lane gets the same value (each
 // step adds a lane's value and its partner's, a commutative pair). DPP moves
@@ -337,280 +333,15 @@ __global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_kernel(BwdArgs a) {
   a.dv[hoff + (size_t)j * kD + lane] = dv;
 }
 
-// ---------------------------------------------------------------------------
-// bf16 form: one lane per key (dQ) or per row (dK, dV). Each lane loads whole
-// 128-byte rows and forms its own dot products against the wave's query or key
-// vectors, which sit in LDS (read as broadcasts), so a pair costs no cross-lane
-// work; each lane keeps a 64-wide partial gradient, summed across the lanes once
-// per row (or key) at the end.
-// ---------------------------------------------------------------------------
-
-// Eight bf16 (one 16-byte chunk, element 2e in the low half of word e) to fp32.
-__device__ __forceinline__ void unpack8(const uint4& u, float (&f)[8]) {
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f[2 * e] = __builtin_bit_cast(float, w[e] << 16);
-    f[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xffff0000u);
-  }
-}
-
-// A 64-element bf16 row as eight 16-byte chunks.
-__device__ __forceinline__ void load_row(const bf16* row, uint4 (&c)[8]) {
-  const uint4* p = reinterpret_cast<const uint4*>(row);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) c[k] = p[k];
-}
-
-// x . y over 64 elements: x packed in chunks, y a wave vector in LDS.
-__device__ __forceinline__ float dot_row(const uint4 (&c)[8], const float* y) {
-  float s = 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    float f[8];
-    unpack8(c[k], f);
-    const float4 y0 = *reinterpret_cast<const float4*>(y + 8 * k);
-    const float4 y1 = *reinterpret_cast<const float4*>(y + 8 * k + 4);
-    s += f[0] * y0.x + f[1] * y0.y + f[2] * y0.z + f[3] * y0.w;
-    s += f[4] * y1.x + f[5] * y1.y + f[6] * y1.z + f[7] * y1.w;
-  }
-  return s;
-}
-
-// acc += w * row (row packed in chunks). The chunk is unpacked again here
-// (an opaque copy of its words) rather than kept unpacked from the dot
-// product, which would hold 64 more registers per row.
-__device__ __forceinline__ void axpy_row(float (&acc)[kD], float w, const uint4 (&c)[8]) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    uint4 u = c[k];
-    asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
-    float f[8];
-    unpack8(u, f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[8 * k + e] += w * f[e];
-  }
-}
-
-// Lane d receives the sum over the lanes of acc[d].
-__device__ __forceinline__ float lane_totals(const float (&acc)[kD], int32_t lane) {
-  float res = 0.f;
-#pragma unroll
-  for (int d = 0; d < kD; ++d) {
-    const float t = wave_sum(acc[d]);
-    res = lane == d ? t : res;
-  }
-  return res;
-}
-
-__global__ __launch_bounds__(64 * kWavesBwd) void bwd_dq_rows_kernel(BwdArgs a) {
-  __shared__ float vq[kWavesBwd][kD], vdo[kWavesBwd][kD];
-  __shared__ float qa_s[kWavesBwd][kMaxLabels];  // q_i . a_l of this wave's row
-  const int32_t lane = threadIdx.x & 63;
-  const int32_t wv = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
-  const int32_t N = a.N;
-  const int64_t rows = (int64_t)a.B * a.H * N;
-  const int64_t row0 = (int64_t)blockIdx.x * kWavesBwd + wv;
-  const bool valid = row0 < rows;
-  const int64_t row = valid ? row0 : rows - 1;  // a wave past the end stages a valid row
-  const int32_t i = (int32_t)(row % N);
-  const int64_t bh = row / N;
-  const int32_t h = (int32_t)(bh % a.H), b = (int32_t)(bh / a.H);
-  const size_t hoff = (size_t)bh * N * kD;
-  const int32_t gi = a.grank[i];
-  const bool ig = gi >= 0;
-  const bool sep = ig && a.sep;
-  const bf16* Q = static_cast<const bf16*>(sep ? a.qg : a.q) + hoff;
-  const bf16* K = static_cast<const bf16*>(sep ? a.kg : a.k) + hoff;
-  const bf16* V = static_cast<const bf16*>(sep ? a.vg : a.v) + hoff;
-  const float dov = load_el(static_cast<const bf16*>(a.dout) + hoff + (size_t)i * kD + lane);
-  const float ov = load_el(static_cast<const bf16*>(a.out) + hoff + (size_t)i * kD + lane);
-  const float Di = wave_sum(dov * ov);
-  const float qv = load_el(Q + (size_t)i * kD + lane);
-  vq[wv][lane] = qv;
-  vdo[wv][lane] = dov;
-  const float* avec = a.rel_vec ? a.rel_vec + (size_t)h * a.n_labels * kD : nullptr;
-  if (avec)
-    for (int32_t l = 0; l < a.n_labels; ++l) {
-      const float t = wave_sum(qv * avec[(size_t)l * kD + lane]);
-      if (lane == 0) qa_s[wv][l] = t;
-    }
-  __syncthreads();  // the only barrier: every wave reaches it
-  if (!valid) return;
-  if (lane == 0) a.delta[row] = Di;
-  const float lse = a.lse[row];
-  const int32_t* segb = a.seg ? a.seg + (size_t)b * N : nullptr;
-  float acc[kD];
-#pragma unroll
-  for (int d = 0; d < kD; ++d) acc[d] = 0.f;
-  // keys key_of(x), x in [0, n) (-1: skip), one per lane; a skipped lane
-  // reads row i (always valid) and gets weight 0
-  auto sweep = [&](int32_t n, auto key_of) {
-    for (int32_t x0 = 0; x0 < n; x0 += 64) {
-      const int32_t x = x0 + lane;
-      int32_t j = x < n ? key_of(x) : -1;
-      const int32_t lb = j >= 0 ? bwd_pair(a, b, i, j, gi, a.grank[j], segb) : -1;
-      if (lb == -2) j = -1;
-      if (__ballot(j >= 0) == 0ull) continue;  // no lane has a pair (masks, labels)
-      const int32_t r = j >= 0 ? j : i;
-      uint4 kc[8], vc[8];
-      load_row(K + (size_t)r * kD, kc);
-      load_row(V + (size_t)r * kD, vc);
-      const float s = dot_row(kc, vq[wv]);
-      const float dp = dot_row(vc, vdo[wv]);
-      const bool lab = j >= 0 && lb >= 0;
-      const float bias = lab ? label_bias(a, h, lb, avec ? qa_s[wv][lb] : 0.f) : 0.f;
-      const float p = j >= 0 ? __expf(s * a.scale + bias - lse) : 0.f;
-      const float w = p * (dp - Di);
-      axpy_row(acc, w, kc);
-      if (lab && avec) {  // a label vector's share q_i . a_l of the logit adds a_l to dq
-        const float4* al = reinterpret_cast<const float4*>(avec + (size_t)lb * kD);
-#pragma unroll
-        for (int c = 0; c < kD / 4; ++c) {
-          const float4 x4 = al[c];
-          acc[4 * c] += w * x4.x;
-          acc[4 * c + 1] += w * x4.y;
-          acc[4 * c + 2] += w * x4.z;
-          acc[4 * c + 3] += w * x4.w;
-        }
-      }
-    }
-  };
-  if (lse != kNegInf) {
-    if (ig) {
-      sweep(a.causal ? i + 1 : N, [&](int32_t x) { return x; });
-    } else {
-      const int32_t d = a.dil[h], R = a.radius;
-      const int32_t t0 = -min(R, i / d);
-      const int32_t t1 = a.causal ? 0 : min(R, (N - 1 - i) / d);
-      sweep(t1 - t0 + 1, [&](int32_t x) { return i + (t0 + x) * d; });
-      sweep(a.n_global, [&](int32_t x) {
-        const int32_t j = a.gidx[x];
-        const bool skip = j < 0 || j >= N || (a.causal && j > i) || in_band(i, j, R, d, a.causal);
-        return skip ? -1 : j;
-      });
-    }
-  }
-  const float g = lane_totals(acc, lane) * a.scale;
-  if (a.sep) {
-    a.dq[hoff + (size_t)i * kD + lane] = ig ? 0.f : g;
-    a.dqg[hoff + (size_t)i * kD + lane] = ig ? g : 0.f;
-  } else {
-    a.dq[hoff + (size_t)i * kD + lane] = g;
-  }
-}
-
-__global__ __launch_bounds__(64 * kWavesBwd) void bwd_dkv_rows_kernel(BwdArgs a) {
-  // this wave's key and value vectors, shared and (separate projections) global
-  __shared__ float vk[kWavesBwd][kD], vv[kWavesBwd][kD], vkg[kWavesBwd][kD], vvg[kWavesBwd][kD];
-  const int32_t lane = threadIdx.x & 63;
-  const int32_t wv = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
-  const int32_t N = a.N;
-  const int64_t keys = (int64_t)a.B * a.H * N;
-  const int64_t key0 = (int64_t)blockIdx.x * kWavesBwd + wv;
-  const bool valid = key0 < keys;
-  const int64_t key = valid ? key0 : keys - 1;
-  const int32_t j = (int32_t)(key % N);
-  const int64_t bh = key / N;
-  const int32_t h = (int32_t)(bh % a.H), b = (int32_t)(bh / a.H);
-  const size_t hoff = (size_t)bh * N * kD;
-  const size_t jo = hoff + (size_t)j * kD + lane;
-  vk[wv][lane] = load_el(static_cast<const bf16*>(a.k) + jo);
-  vv[wv][lane] = load_el(static_cast<const bf16*>(a.v) + jo);
-  if (a.sep) {
-    vkg[wv][lane] = load_el(static_cast<const bf16*>(a.kg) + jo);
-    vvg[wv][lane] = load_el(static_cast<const bf16*>(a.vg) + jo);
-  }
-  __syncthreads();  // the only barrier: every wave reaches it
-  if (!valid) return;
-  const float* lse = a.lse + (size_t)bh * N;
-  const float* delta = a.delta + (size_t)bh * N;
-  const bf16* dO = static_cast<const bf16*>(a.dout) + hoff;
-  const int32_t* segb = a.seg ? a.seg + (size_t)b * N : nullptr;
-  const int32_t d = a.dil[h], R = a.radius;
-  const int32_t gj = a.grank[j];
-  const bool jg = gj >= 0;
-  const float* avec = a.rel_vec ? a.rel_vec + (size_t)h * a.n_labels * kD : nullptr;
-  // Two passes over the same rows, one accumulator live at a time: dV (needs
-  // s only) and then dK (needs s and dP).
-  float acc[kD];
-  // rows row_of(x), x in [0, n) (-1: skip), one per lane, through projection Q
-  // against key vectors (kvec, vvec); a skipped lane reads row j and gets weight 0
-  auto sweep = [&](bool dk_pass, int32_t n, const bf16* Q, const float* kvec, const float* vvec,
-                   auto row_of) __attribute__((always_inline)) {
-    for (int32_t x0 = 0; x0 < n; x0 += 64) {
-      const int32_t x = x0 + lane;
-      int32_t i = x < n ? row_of(x) : -1;
-      const int32_t lb = i >= 0 ? bwd_pair(a, b, i, j, a.grank[i], gj, segb) : -1;
-      if (lb == -2) i = -1;
-      if (__ballot(i >= 0) == 0ull) continue;  // no lane has a pair (masks, labels)
-      const int32_t r = i >= 0 ? i : j;
-      uint4 qc[8], oc[8];
-      load_row(Q + (size_t)r * kD, qc);
-      load_row(dO + (size_t)r * kD, oc);
-      const float li = lse[r];
-      const float sc = dot_row(qc, kvec);
-      const bool on = i >= 0 && li != kNegInf;
-      float bias = 0.f;
-      if (on && lb >= 0) bias = label_bias(a, h, lb, avec ? dot_row(qc, avec + (size_t)lb * kD) : 0.f);
-      const float p = on ? __expf(sc * a.scale + bias - li) : 0.f;
-      if (dk_pass) {
-        const float dp = dot_row(oc, vvec);
-        axpy_row(acc, p * (dp - delta[r]), qc);
-      } else {
-        axpy_row(acc, p, oc);
-      }
-    }
-  };
-  const bf16* Qs = static_cast<const bf16*>(a.q) + hoff;
-  auto grow = [&](int32_t x) {
-    const int32_t i = a.gidx[x];
-    return (i < 0 || i >= N || (a.causal && i < j)) ? -1 : i;
-  };
-  // every row that reaches key j through the shared projections
-  auto shared_rows = [&](bool dk_pass) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < kD; ++e) acc[e] = 0.f;
-    const int32_t u0 = a.causal ? 0 : -min(R, j / d);
-    const int32_t u1 = min(R, (N - 1 - j) / d);
-    sweep(dk_pass, u1 - u0 + 1, Qs, vk[wv], vv[wv], [&](int32_t x) {
-      const int32_t i = j + (u0 + x) * d;
-      return a.grank[i] >= 0 ? -1 : i;
-    });
-    if (jg) {
-      const int32_t i0 = a.causal ? j : 0;
-      sweep(dk_pass, N - i0, Qs, vk[wv], vv[wv], [&](int32_t x) {
-        const int32_t i = i0 + x;
-        return (in_band(i, j, R, d, a.causal) || a.grank[i] >= 0) ? -1 : i;
-      });
-    }
-    if (!a.sep) sweep(dk_pass, a.n_global, Qs, vk[wv], vv[wv], grow);
-  };
-  shared_rows(false);
-  a.dv[hoff + (size_t)j * kD + lane] = lane_totals(acc, lane);
-  shared_rows(true);
-  a.dk[hoff + (size_t)j * kD + lane] = lane_totals(acc, lane) * a.scale;
-  if (a.sep) {  // the global rows, through qg_i, kg_j, vg_j
-    const bf16* Qg = static_cast<const bf16*>(a.qg) + hoff;
-#pragma unroll
-    for (int e = 0; e < kD; ++e) acc[e] = 0.f;
-    sweep(false, a.n_global, Qg, vkg[wv], vvg[wv], grow);
-    a.dvg[hoff + (size_t)j * kD + lane] = lane_totals(acc, lane);
-#pragma unroll
-    for (int e = 0; e < kD; ++e) acc[e] = 0.f;
-    sweep(true, a.n_global, Qg, vkg[wv], vvg[wv], grow);
-    a.dkg[hoff + (size_t)j * kD + lane] = lane_totals(acc, lane) * a.scale;
-  }
-}
-
 }  // namespace
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   if (rows <= 0) return hipSuccess;
   const dim3 g((uint32_t)((rows + kWavesBwd - 1) / kWavesBwd)), blk(64 * kWavesBwd);
-  if (dtype == 1 && a.n_band_wg > 0) {
+  if (dtype == 1) {
     // D_i, then dK/dV and dQ on MFMA in one launch (no global ranks needed)
+    if (a.n_band_wg <= 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(bwd_delta_kernel, dim3((uint32_t)delta_blocks(rows)), dim3(256), 0, stream, a);
     hipError_t e = launch_rowtab(a, stream);  // key-side label vectors: the rows' tables
     if (e != hipSuccess) return e;
@@ -620,14 +351,10 @@ hipError_t launch_attn_bwd(const BwdArgs& a, int32_t dtype, hipStream_t stream) 
     if (e != hipSuccess) return e;
     return hipGetLastError();
   }
+  // fp32: global ranks, then dQ and D_i, then dK and dV on the VALU
   hipLaunchKernelGGL(bwd_flags_kernel, dim3((uint32_t)((a.N + 255) / 256)), dim3(256), 0, stream, a);
-  if (dtype == 1) {
-    hipLaunchKernelGGL(bwd_dq_rows_kernel, g, blk, 0, stream, a);
-    hipLaunchKernelGGL(bwd_dkv_rows_kernel, g, blk, 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(bwd_dq_kernel<float>, g, blk, 0, stream, a);
-    hipLaunchKernelGGL(bwd_dkv_kernel<float>, g, blk, 0, stream, a);
-  }
+  hipLaunchKernelGGL(bwd_dq_kernel<float>, g, blk, 0, stream, a);
+  hipLaunchKernelGGL(bwd_dkv_kernel<float>, g, blk, 0, stream, a);
   return hipGetLastError();
 }
 
