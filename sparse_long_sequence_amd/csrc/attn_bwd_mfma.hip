@@ -1,7 +1,13 @@
-// attn_bwd_mfma.hip — dQ of band + global attention on the bf16 MFMA tile
-// engine (the chain rule through the masked softmax: LongNet page, §3.4
-// "Standard Self-Attention and Sparse Attention (Preliminaries)", Eq. 2,
-// differentiated; the pattern as in attn_fwd.hip).
+// attn_bwd_mfma.hip — the bf16 backward of band + global attention and of the
+// LongNet mixture on the MFMA tile engine (the chain rule through the masked
+// softmax: LongNet page, §3.4 "Standard Self-Attention and Sparse Attention
+// (Preliminaries)", Eq. 2, differentiated; the pattern as in attn_fwd.hip).
+// Band + global: one launch holds the dK/dV and the dQ workgroups (D_i comes
+// from a launch before, each row's label table too when labels carry vectors
+// or a table), and the split global tiles' partial sums are added by a launch
+// after. The forward's per-instance inputs (bias tables, key-side label
+// vectors, segment ids, label matrices and piece masks) select instantiations
+// of the same workgroups.
 //
 // For the forward's own lse (natural log) and D_i = dO_i . O_i,
 //   P_ij  = exp(q_i . k_j / sqrt(D) - lse_i),   dP_ij = dO_i . v_j,
@@ -13,12 +19,13 @@
 // registers), P from lse with no running max (lse is final), dS in bf16, and
 // dQ^T += K^T dS^T on MFMA with K read transposed from LDS (the forward's PV
 // step with K in place of V and dS in place of P). No atomics: each dQ row is
-// written once.
+// written once (the global rows' ranges into partial sums).
 //
 // dK, dV run the same engine with the roles swapped: a workgroup owns a tile
 // of non-global keys (their K and V fragments in registers) and streams the
 // query rows that reach them through LDS (Q in the K slot, dO in the V slot,
-// each row's lse and D_i next to them):
+// each row's negated offsets -lse / scale and -D_i next to them, where the
+// score and dP MFMAs start):
 //   S'^T = Q K^T and dP'^T = dO V^T per 32-row sub-tile, P and dS as above,
 //   dV^T += dO^T P^T and dK^T += Q^T dS^T (transposed LDS reads of dO and Q),
 // first over the window's non-global rows, then over the global rows (which
