@@ -314,6 +314,8 @@ VEC_CASES = [
     ("vec-k-above-radius", 1, 2, 300, (0, 150), 5, None, False, True, 9, "both", None),
     ("vec-segments", 2, 2, 900, (0, 1, 2, 450, 451), 30, (1, 2), False, True, 5, "vector",
      (450, 300, 150)),
+    # no global token at all (no tile carries global flags), causal, ragged tail
+    ("vec-no-globals-causal", 1, 2, 500, (), 30, None, True, False, 7, "vector", None),
 ]
 
 
