@@ -1760,8 +1760,11 @@ hipError_t launch_dilated_bwd_mfma(const BwdArgs& a, hipStream_t stream) {
     return DilPart{k, nseg, (rows + TT::kTQ - 1) / TT::kTQ, store ? 1 : 0};
   };
   auto grid_of = [&](const DilPart& p) { return (int64_t)a.B * a.H * p.nseg * p.qtiles; };
-  // order: the storing pattern, then the others by launch size, smallest
-  // first, so that the dK/dV launch left alone at the end is the largest
+  // order: the storing pattern, then the others taken alternately from the
+  // small and the large end of their launch sizes. A pattern with few
+  // workgroups (long segments at a high dilation) has the longest chains of
+  // tiles per workgroup; paired with a pattern of many short workgroups, the
+  // latter fill the chip around those chains.
   DilPart ord[kMaxPairs];
   int32_t n = 0;
   if (first >= 0) ord[n++] = part_of(first, true);
@@ -1774,6 +1777,16 @@ hipError_t launch_dilated_bwd_mfma(const BwdArgs& a, hipStream_t stream) {
       --x;
     }
     ord[x] = p;
+  }
+  {
+    const int32_t s0 = first >= 0 ? 1 : 0;
+    DilPart alt[kMaxPairs];
+    int32_t lo = s0, hi = n - 1, m = s0;
+    while (lo <= hi) {
+      alt[m++] = ord[lo++];
+      if (lo <= hi) alt[m++] = ord[hi--];
+    }
+    for (int32_t x = s0; x < n; ++x) ord[x] = alt[x];
   }
   for (int32_t x = 0; x < n; ++x)
     if (grid_of(ord[x]) <= 0 || 2 * grid_of(ord[x]) > 0x7fffffffLL) return hipErrorInvalidValue;
