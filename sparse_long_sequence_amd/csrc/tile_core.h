@@ -880,6 +880,23 @@ __device__ __forceinline__ void add_bias(float* s, const typename TileTraits<T>:
   }
 }
 
+// add_bias for a tile of consecutive positions whose keys are all of the
+// query's kind: key kj sits at base + kj, so a pair's distance is
+// (base - qpos) + kj with kj a compile-time constant plus the lane's part,
+// and no key position is read from LDS.
+template <typename T>
+__device__ __forceinline__ void add_bias_run(float* s, const BiasRule& br, int sb, int32_t qi,
+                                             int32_t off, int32_t lane) {
+  using TT = TileTraits<T>;
+  const int32_t c = off + TT::key_lane(lane);
+  const float* tab = br.tab + qi * br.row_stride + br.k;
+#pragma unroll
+  for (int r = 0; r < TT::kNS; ++r) {
+    const int32_t dl = min(max(c + TT::key_const(sb, r), -br.k), br.k);
+    s[r] += tab[dl];
+  }
+}
+
 // The labels of the lane's kNS pairs of sub-tile sb, four per word (element
 // r in byte r & 3 of word r >> 2; the lane's keys come in runs of four):
 // issued before the sub-tile's score MFMAs so that their latency overlaps
@@ -1221,6 +1238,8 @@ __device__ __forceinline__ void process_tile(const typename TileTraits<T>::Smem&
       }
       if (LBL && lab_on) add_bias_labels<T>(s, lw, sm, buf, br, lr, sb, qi, qpos, lane);
       else if (uniform) badd = br.tab[qi * br.row_stride + ue];  // per query row with label vectors
+      else if (strided && all_same && kt.stride == 1)
+        add_bias_run<T>(s, br, sb, qi, kt.base - qpos, lane);
       else add_bias<T>(s, sm, buf, br, sb, qi, qpos, lane, all_same);
     }
     if (cls[sb] == kPartial) mask_tile<T>(s, sm, buf, mr, sb, kcount, qi, qpos, lane);
